@@ -1,0 +1,154 @@
+"""NumPy-facing wrappers around the C oracle (oracle/qmv_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, the smoke check and the CPU
+baseline of the benchmark; never by the product library.  Each wrapper only
+marshals arrays; all arithmetic is in the C file, which cites the passages of
+the source pages it follows.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from .build_oracle import build as _build
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_ptr = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(_build())
+        lib.oracle_quantize_rows.argtypes = [_ptr, _i64, _i64, _ptr, _ptr]
+        lib.oracle_quantize_tensor.argtypes = [_ptr, _i64, _i64, _ptr, _ptr]
+        lib.oracle_trit5_row_bytes.argtypes = [_i64]
+        lib.oracle_trit5_row_bytes.restype = _i64
+        lib.oracle_trit5_row_stride.argtypes = [_i64]
+        lib.oracle_trit5_row_stride.restype = _i64
+        lib.oracle_int8_row_stride.argtypes = [_i64]
+        lib.oracle_int8_row_stride.restype = _i64
+        lib.oracle_pack_trit5.argtypes = [_ptr, _i64, _i64, _ptr, _ptr]
+        lib.oracle_unpack_trit5.argtypes = [_ptr, _i64, _i64, _ptr]
+        lib.oracle_unpack_trit5.restype = _i64
+        lib.oracle_layout_int8.argtypes = [_ptr, _i64, _i64, _ptr]
+        lib.oracle_matmul_int.argtypes = [_ptr, _ptr, _i64, _i64, _i64, _ptr, ctypes.c_int]
+        lib.oracle_matmul_int.restype = ctypes.c_int
+        lib.oracle_dequant.argtypes = [_ptr, _i64, _i64, _ptr, ctypes.c_float, _ptr]
+        lib.oracle_lmhead.argtypes = [_ptr, _ptr, _i64, _i64, _ptr, _ptr, ctypes.c_int]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def quantize_rows(x):
+    """Per-row int8 quantisation of a 2-D fp32 array -> (int8 [m][k], fp32 [m])."""
+    x, px = _c(np.atleast_2d(x), np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), np.int8)
+    s = np.empty(m, np.float32)
+    _load().oracle_quantize_rows(px, m, k, q.ctypes.data, s.ctypes.data)
+    return q, s
+
+
+def quantize_tensor(w):
+    """Per-tensor int8 quantisation of a 2-D fp32 array -> (int8 [n][k], fp32 scale)."""
+    w, pw = _c(np.atleast_2d(w), np.float32)
+    n, k = w.shape
+    q = np.empty((n, k), np.int8)
+    s = np.empty(1, np.float32)
+    _load().oracle_quantize_tensor(pw, n, k, q.ctypes.data, s.ctypes.data)
+    return q, np.float32(s[0])
+
+
+def trit5_row_bytes(k: int) -> int:
+    return int(_load().oracle_trit5_row_bytes(k))
+
+
+def trit5_row_stride(k: int) -> int:
+    return int(_load().oracle_trit5_row_stride(k))
+
+
+def int8_row_stride(k: int) -> int:
+    return int(_load().oracle_int8_row_stride(k))
+
+
+def pack_trit5(t):
+    """Trits [n][k] -> (packed bytes in the device layout, count of invalid trits)."""
+    t, pt = _c(np.atleast_2d(t), np.int8)
+    n, k = t.shape
+    out = np.empty(n * trit5_row_stride(k), np.uint8)
+    bad = np.zeros(1, np.int64)
+    _load().oracle_pack_trit5(pt, n, k, out.ctypes.data, bad.ctypes.data)
+    return out, int(bad[0])
+
+
+def unpack_trit5(packed, n: int, k: int):
+    """Packed device bytes -> (trits [n][k], count of bytes >= 243)."""
+    p, pp = _c(packed, np.uint8)
+    assert p.size == n * trit5_row_stride(k)
+    t = np.empty((n, k), np.int8)
+    invalid = _load().oracle_unpack_trit5(pp, n, k, t.ctypes.data)
+    return t, int(invalid)
+
+
+def layout_int8(q):
+    """int8 codes [n][k] -> bytes in the device layout."""
+    q, pq = _c(np.atleast_2d(q), np.int8)
+    n, k = q.shape
+    out = np.empty(n * int8_row_stride(k), np.int8)
+    _load().oracle_layout_int8(pq, n, k, out.ctypes.data)
+    return out
+
+
+def matmul_int(x8, w, threads: int = 0):
+    """Exact acc[m][n] = sum_k x8[m][k] * w[n][k] (int32; raises on overflow)."""
+    x8, px = _c(np.atleast_2d(x8), np.int8)
+    w, pw = _c(np.atleast_2d(w), np.int8)
+    m, k = x8.shape
+    n, k2 = w.shape
+    assert k == k2
+    acc = np.empty((m, n), np.int32)
+    ovf = _load().oracle_matmul_int(px, pw, m, n, k, acc.ctypes.data, threads or max_threads())
+    if ovf:
+        raise OverflowError("integer dot product does not fit int32")
+    return acc
+
+
+def dequant(acc, sx, sw):
+    """y[m][n] = fl32(acc * sx[m] * sw) formed in fp64."""
+    acc, pa = _c(np.atleast_2d(acc), np.int32)
+    sx, ps = _c(np.atleast_1d(sx), np.float32)
+    m, n = acc.shape
+    assert sx.size == m
+    y = np.empty((m, n), np.float32)
+    _load().oracle_dequant(pa, m, n, ps, ctypes.c_float(float(sw)), y.ctypes.data)
+    return y
+
+
+def lmhead(w_bf16, x, threads: int = 0):
+    """Logits (fp64 [v]) and the first-max index of their fp32 roundings."""
+    w, pw = _c(np.atleast_2d(w_bf16), np.uint16)
+    x, px = _c(x, np.float32)
+    v, k = w.shape
+    assert x.size == k
+    logits = np.empty(v, np.float64)
+    idx = np.zeros(1, np.int32)
+    _load().oracle_lmhead(pw, px, v, k, logits.ctypes.data, idx.ctypes.data, threads or max_threads())
+    return logits, int(idx[0])
+
+
+__all__ = ["max_threads", "quantize_rows", "quantize_tensor", "trit5_row_bytes", "trit5_row_stride",
+           "int8_row_stride", "pack_trit5", "unpack_trit5", "layout_int8", "matmul_int", "dequant",
+           "lmhead"]

@@ -1,0 +1,148 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the smoke check.
+
+This module holds no arithmetic of the method (no quantisation, packing or
+dot products): it only draws numbers.  Both the HIP path and the CPU oracle
+receive its outputs as plain arrays.
+
+Generator: splitmix64 used as a counter-based stream (output i of a stream
+with seed s is mix(s + (i + 1) * 0x9E3779B97F4A7C15)), the RNG the cpp20gemma
+README uses for reproducible tests, with base seed 42.  Draws:
+
+* uniform u in [0, 1): the top 53 bits of an output times 2^-53;
+* normal: Box-Muller on two uniforms, cos branch, then cast to fp32;
+* trit: r = (z >> 32) % 10; -1 if r < 3, 0 if r < 7, +1 otherwise, so
+  P(-1, 0, +1) = (0.3, 0.4, 0.3);
+* bf16: fp32 rounded to nearest even (NaN-free inputs only).
+"""
+import numpy as np
+
+GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+BASE_SEED = 42
+
+# Stream tags: one per kind of tensor, so independent streams never overlap.
+TAG_WEIGHT = 1
+TAG_ACT = 2
+TAG_SCALE = 3
+TAG_HEAD = 4
+TAG_MISC = 5
+
+
+def _mix_inplace(z, tmp):
+    np.right_shift(z, np.uint64(30), out=tmp)
+    z ^= tmp
+    z *= _M1
+    np.right_shift(z, np.uint64(27), out=tmp)
+    z ^= tmp
+    z *= _M2
+    np.right_shift(z, np.uint64(31), out=tmp)
+    z ^= tmp
+    return z
+
+
+def splitmix64_scalar(x: int) -> int:
+    """One splitmix64 step on a Python int (used to derive stream seeds)."""
+    m = (1 << 64) - 1
+    z = (x + 0x9E3779B97F4A7C15) & m
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & m
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & m
+    return z ^ (z >> 31)
+
+
+def stream_seed(config_id: int, layer: int, matrix_id: int, tag: int, base: int = BASE_SEED) -> int:
+    m = (1 << 64) - 1
+    return splitmix64_scalar((base ^ (config_id << 48) ^ (layer << 16) ^ matrix_id ^ (tag << 40)) & m)
+
+
+def raw(seed: int, count: int, start: int = 0):
+    """Outputs start .. start+count-1 of the stream with this seed (uint64)."""
+    out = np.empty(count, dtype=np.uint64)
+    block = 1 << 16
+    tmp = np.empty(block, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        for b0 in range(0, count, block):
+            b1 = min(count, b0 + block)
+            z = out[b0:b1]
+            z[:] = np.arange(start + b0 + 1, start + b1 + 1, dtype=np.uint64)
+            z *= GOLDEN
+            z += np.uint64(seed)
+            _mix_inplace(z, tmp[: b1 - b0])
+    return out
+
+
+def uniform(seed: int, count: int, start: int = 0):
+    return (raw(seed, count, start) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+
+
+def normal(seed: int, shape, std: float = 1.0):
+    count = int(np.prod(shape))
+    u = uniform(seed, 2 * count).reshape(count, 2)
+    r = np.sqrt(-2.0 * np.log1p(-u[:, 0]))
+    z = r * np.cos(2.0 * np.pi * u[:, 1])
+    return (z * std).astype(np.float32).reshape(shape)
+
+
+_TRIT_OF_DECILE = np.array([-1, -1, -1, 0, 0, 0, 0, 1, 1, 1], dtype=np.int8)
+
+
+def trits(seed: int, shape, start: int = 0):
+    """Trits for outputs start .. start+count-1 of the stream (row-major shape)."""
+    count = int(np.prod(shape))
+    r = (raw(seed, count, start) >> np.uint64(32)) % np.uint64(10)
+    return _TRIT_OF_DECILE[r.astype(np.intp)].reshape(shape)
+
+
+def ternary_scale(seed: int) -> float:
+    """One per-matrix scale, uniform in [0.01, 0.03)."""
+    return float(np.float32(0.01 + 0.02 * uniform(seed, 1)[0]))
+
+
+def to_bf16_bits(x):
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    b = b + np.uint64(0x7FFF) + lsb
+    return (b >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(h):
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# The workloads named on the pages, as shapes.
+# --------------------------------------------------------------------------
+
+# Gemma-3-1B decoder block (d=1152, 4 query heads x 256, 1 kv head x 256,
+# ffn 6912): (name, N=out rows, K=in columns).  o_proj is listed apart.
+GEMMA_MATS = [("q", 1024, 1152), ("k", 256, 1152), ("v", 256, 1152),
+              ("gate", 6912, 1152), ("up", 6912, 1152), ("down", 1152, 6912)]
+GEMMA_O = ("o", 1152, 1024)
+GEMMA_LAYERS = 26
+
+# BitNet-b1.58-large block (d=1536, ffn 4096), 24 blocks.
+BITNET_MATS = [("q", 1536, 1536), ("k", 1536, 1536), ("v", 1536, 1536), ("o", 1536, 1536),
+               ("gate", 4096, 1536), ("up", 4096, 1536), ("down", 1536, 4096)]
+BITNET_LAYERS = 24
+
+# Output layer: 262144 vocabulary rows x 1152.
+HEAD_V, HEAD_K = 262144, 1152
+
+# int8 per-tensor matvec: W 768x288.
+INT8_N, INT8_K = 768, 288
+
+CONFIG_INT8, CONFIG_GEMMA_DECODE, CONFIG_GEMMA_PREFILL, CONFIG_HEAD, CONFIG_BITNET = 0, 1, 2, 3, 4
+
+
+def decode_stack(mats, layers, config_id, m=1, act_seed_config=None):
+    """Yield (layer, index, name, N, K, trits, scale, x) for every matrix of a stack.
+
+    trits are int8 [N][K]; x is fp32 [m][K] ~ N(0,1)."""
+    acfg = config_id if act_seed_config is None else act_seed_config
+    for layer in range(layers):
+        for mid, (name, n, k) in enumerate(mats):
+            t = trits(stream_seed(config_id, layer, mid, TAG_WEIGHT), (n, k))
+            s = ternary_scale(stream_seed(config_id, layer, mid, TAG_SCALE))
+            x = normal(stream_seed(acfg, layer, mid, TAG_ACT), (m, k))
+            yield layer, mid, name, n, k, t, s, x
