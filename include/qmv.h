@@ -1,0 +1,203 @@
+/*
+ * qmv.h -- C ABI of libqmv, the MI355X (gfx950) quantized matrix-vector library.
+ *
+ * What it computes (the pages' statement of the problem):
+ *   - Weights are ternary, five trits per byte with one fp32 scale per matrix
+ *     ("Gemma 3 1B at 114 tokens per second on a laptop CPU", sections
+ *     "Step 1: a kernel for 1.6-bit weights" and "Step 2: making a ternary
+ *     Gemma"), or int8 with one symmetric per-tensor scale (cpp20gemma README,
+ *     "Architecture & implementation").
+ *   - Activations are rounded to int8 with one scale per token ("Step 2";
+ *     llama2.c tour, "Key ideas & tradeoffs": activations quantised at run
+ *     time).
+ *   - Dot products are exact int32 sums; the two scales are applied once,
+ *     after the sum (cpp20gemma, "Architecture & implementation").
+ *   - Many tokens ("lanes") can share one pass over the weights ("Many users
+ *     at once"; "Step 1": prompt tokens go through each matrix in one pass).
+ *   - The output layer is a bf16 matrix-vector product followed by a greedy
+ *     choice of the first maximum ("Step 3: the output layer became the
+ *     bottleneck"; llama2.c tour, "Sampling").
+ *
+ * Conventions (apply to every call):
+ *   - Pointers are DEVICE pointers unless marked "host".  Every buffer is owned
+ *     by the caller; the library never allocates or frees device memory.
+ *     Scratch memory is passed in as `workspace`.
+ *   - Calls are asynchronous: host-side arguments are validated synchronously;
+ *     on a validation failure the call returns a negative status and enqueues
+ *     nothing.  Otherwise the work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the null stream) and the call returns QMV_OK, or QMV_EHIP if the
+ *     HIP runtime reported an error when enqueuing.
+ *   - There are no device-side error reports apart from the optional invalid
+ *     trit counter of qmv_pack_ternary; read it after synchronising.
+ *   - Non-finite fp32 inputs are outside the contract.
+ *   - The library keeps no global mutable state: calls on different streams
+ *     with different buffers may run concurrently.
+ *
+ * Device weight layout (both weight types): a row's bytes are cut into
+ * 16-byte chunks and chunk c of every row is stored before chunk c+1 of any
+ * row, i.e. byte j of row r lives at ((j / 16) * n + r) * 16 + (j % 16).
+ * Row byte counts are padded to a multiple of 16.
+ *   - ternary: row bytes = ceil(k/5); byte j holds columns 5j..5j+4 as the
+ *     base-3 number sum_i (t[5j+i] + 1) * 3^i (0..242); columns >= k and the
+ *     padding bytes hold trit 0 (a padding byte is 121).
+ *   - int8: row bytes = k int8 codes, zero padded.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every call (0 = success). */
+enum {
+    QMV_OK = 0,
+    QMV_EINVAL = -1,        /* null pointer, negative size or bad flag */
+    QMV_ESHAPE = -2,        /* sizes inconsistent or beyond the supported range */
+    QMV_EVALUE = -3,        /* a host-side value is out of range (e.g. a non-finite scale) */
+    QMV_EHIP = -4,          /* the HIP runtime reported an error */
+    QMV_EUNSUPPORTED = -5,  /* unknown weight type */
+    QMV_EWORKSPACE = -6     /* workspace missing or too small */
+};
+
+/* Weight types. */
+enum {
+    QMV_W_TERNARY5 = 1,     /* five trits per byte, one fp32 scale per matrix */
+    QMV_W_INT8 = 2          /* int8 codes, one fp32 scale per tensor */
+};
+
+/* Flags of qmv_gemv / qmv_gemm_prefill. */
+enum {
+    /* The workspace already holds the problem table written by the previous
+     * call with this workspace and an identical problem list; skip the
+     * host-to-device upload of the table. */
+    QMV_F_TABLE_READY = 1
+};
+
+/* Limits. */
+#define QMV_MAX_GEMV_M 16            /* tokens per qmv_gemv problem */
+#define QMV_MAX_K (1 << 20)          /* input columns */
+#define QMV_MAX_N (1 << 24)          /* output rows */
+
+/* A packed weight matrix (host struct describing device memory). */
+typedef struct qmv_weight {
+    int32_t wtype;          /* QMV_W_TERNARY5 or QMV_W_INT8 */
+    int32_t reserved;       /* must be 0 */
+    int64_t n;              /* output rows */
+    int64_t k;              /* input columns */
+    const void* data;       /* device, qmv_packed_bytes(wtype, n, k) bytes, 16-byte aligned */
+    const float* scale;     /* device, 1 fp32 */
+} qmv_weight;
+
+/* One matrix-times-activations problem: y[m][n] = (x8[m][:] . W[n][:]) * sx[m] * scale. */
+typedef struct qmv_problem {
+    qmv_weight w;
+    const int8_t* x8;       /* device, [m][k] int8, row-major, natural column order */
+    const float* sx;        /* device, [m] fp32 per-token scales */
+    int64_t m;              /* tokens (lanes) */
+    float* y;               /* device, [m][n] fp32, row-major */
+    int32_t* acc;           /* device, [m][n] int32 exact dot products; NULL = not wanted */
+} qmv_problem;
+
+/* Library version string and status names (static strings). */
+const char* qmv_version(void);
+const char* qmv_status_str(int32_t status);
+
+/* Bytes of a packed matrix in the device layout: n * roundup(ceil(k/5), 16)
+ * for QMV_W_TERNARY5, n * roundup(k, 16) for QMV_W_INT8; -1 on bad input. */
+int64_t qmv_packed_bytes(int32_t wtype, int64_t n, int64_t k);
+
+/*
+ * qmv_pack_ternary -- trits -> five trits per byte ("Step 1": 3^5 = 243 codes
+ * fit in a byte; "Step 2": one scale per matrix).
+ *   trits     [n][k] int8 in {-1, 0, +1}, row-major.  A value outside the set
+ *             is packed as 0 and counted in *bad_count.
+ *   scale     the matrix scale (host value, finite) -> written to *scale_out.
+ *   packed    qmv_packed_bytes(QMV_W_TERNARY5, n, k) bytes, 16-byte aligned.
+ *   scale_out 1 fp32.
+ *   bad_count nullable; 1 int32, zeroed and then incremented in-stream.
+ *   desc_out  nullable host struct, filled in on success.
+ * One-time preparation, not part of the per-token path.
+ */
+int32_t qmv_pack_ternary(const int8_t* trits, int64_t n, int64_t k, float scale, void* packed,
+                         float* scale_out, int32_t* bad_count, qmv_weight* desc_out, void* stream);
+
+/*
+ * qmv_pack_int8 -- fp32 weights -> int8 codes with one per-tensor scale
+ * (cpp20gemma, "Architecture & implementation"):
+ *   scale = max(max|w|, 1e-9) / 127 (fp32, correctly rounded),
+ *   code  = clip(round_half_even(w / scale), -128, 127) (IEEE fp32 division).
+ *   w         [n][k] fp32, row-major, finite.
+ *   packed    qmv_packed_bytes(QMV_W_INT8, n, k) bytes, 16-byte aligned.
+ *   scale_out 1 fp32 (also used as the in-stream max cell while packing).
+ *   desc_out  nullable host struct.
+ */
+int32_t qmv_pack_int8(const float* w, int64_t n, int64_t k, void* packed, float* scale_out,
+                      qmv_weight* desc_out, void* stream);
+
+/*
+ * qmv_quantize_act -- per-token int8 activation quantisation ("Step 2": the
+ * inputs of every layer are rounded to int8; same formula as qmv_pack_int8,
+ * one scale per row).
+ *   x   [m][k] fp32 row-major, finite.   x8 [m][k] int8.   sx [m] fp32.
+ *   A row of zeros gets sx = 1e-9/127 and all-zero codes.
+ */
+int32_t qmv_quantize_act(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, void* stream);
+
+/* Workspace bytes qmv_gemv / qmv_gemm_prefill need for this problem list
+ * (-1 on bad input).  The workspace must be 256-byte aligned. */
+int64_t qmv_gemv_workspace_bytes(const qmv_problem* probs /* host */, int32_t count);
+int64_t qmv_prefill_workspace_bytes(const qmv_problem* probs /* host */, int32_t count);
+
+/*
+ * qmv_gemv -- grouped weight-streaming matrix-vector products for 1..16 tokens
+ * ("On a CPU, speed is bytes": every weight byte is read once per step;
+ * "Many users at once": one read of each byte serves every lane).
+ *   probs     host array of `count` problems (1 <= count); each problem has
+ *             1 <= m <= QMV_MAX_GEMV_M, its own weights, activations and
+ *             outputs.  All problems run in one kernel launch.
+ *   workspace device, >= qmv_gemv_workspace_bytes(probs, count) bytes; holds
+ *             the problem table uploaded in-stream (see QMV_F_TABLE_READY).
+ *   flags     0 or QMV_F_TABLE_READY.
+ * y (and acc when non-NULL) are written for every problem.  x8/acc must not
+ * alias y.  Results are exact in acc and do not depend on the grouping.
+ */
+int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes,
+                 uint32_t flags, void* stream);
+
+/*
+ * qmv_gemm_prefill -- the same products for any number of tokens, computed
+ * with int8 matrix cores ("Step 1": all prompt tokens go through each weight
+ * matrix in one pass).  Ternary weights only.  Same arguments and results as
+ * qmv_gemv, with 1 <= m <= 65536 per problem.
+ */
+int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes,
+                         uint32_t flags, void* stream);
+
+/* Workspace bytes of qmv_lmhead_argmax for a v x k head. */
+int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k);
+
+/*
+ * qmv_lmhead_argmax -- output layer and greedy choice ("Step 3": score every
+ * vocabulary row against the final hidden state; llama2.c "Sampling": greedy
+ * keeps the first maximum).
+ *   w_bf16    [v][k] bf16 bit patterns, row-major, 16-byte aligned.
+ *   x         [k] fp32 hidden state.
+ *   logit[r]  = sum_c float(w[r][c]) * x[c], accumulated in fp32.
+ *   idx       1 int32: smallest r with the largest logit.
+ *   max_logit nullable, 1 fp32: that logit.
+ *   logits    nullable, [v] fp32: every logit.
+ *   workspace >= qmv_lmhead_workspace_bytes(v, k) bytes, 256-byte aligned.
+ */
+int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int64_t k, int32_t* idx,
+                          float* max_logit, float* logits, void* workspace, int64_t ws_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

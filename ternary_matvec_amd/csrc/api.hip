@@ -1,0 +1,268 @@
+// api.hip -- the C ABI of libqmv: host-side validation, problem tables and
+// kernel launches.  Declarations and the contract of every call are in
+// include/qmv.h.
+#include <qmv.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "qmv_internal.hpp"
+
+using namespace qmv;
+
+namespace {
+
+constexpr int64_t kMaxProblems = (int64_t)1 << kTileProbBits;
+constexpr int64_t kMaxInt8K = 65536;  // keeps every int8 x int8 dot inside int32
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+int64_t row_stride(int32_t wtype, int64_t k)
+{
+    if (wtype == QMV_W_TERNARY5) return round_up((k + 4) / 5, 16);
+    if (wtype == QMV_W_INT8) return round_up(k, 16);
+    return -1;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? QMV_OK : QMV_EHIP; }
+
+int32_t check_weight(const qmv_weight& w)
+{
+    if (w.wtype != QMV_W_TERNARY5 && w.wtype != QMV_W_INT8) return QMV_EUNSUPPORTED;
+    if (w.reserved != 0) return QMV_EINVAL;
+    if (!w.data || !w.scale) return QMV_EINVAL;
+    if (!aligned(w.data, 16)) return QMV_EINVAL;
+    if (w.n < 1 || w.k < 1 || w.n > QMV_MAX_N || w.k > QMV_MAX_K) return QMV_ESHAPE;
+    if (w.wtype == QMV_W_INT8 && w.k > kMaxInt8K) return QMV_ESHAPE;
+    return QMV_OK;
+}
+
+int32_t check_problems(const qmv_problem* probs, int32_t count, int64_t max_m)
+{
+    if (!probs) return QMV_EINVAL;
+    if (count < 1 || count > kMaxProblems) return QMV_ESHAPE;
+    for (int32_t i = 0; i < count; ++i) {
+        const qmv_problem& p = probs[i];
+        int32_t st = check_weight(p.w);
+        if (st != QMV_OK) return st;
+        if (!p.x8 || !p.sx || !p.y) return QMV_EINVAL;
+        if (p.m < 1 || p.m > max_m) return QMV_ESHAPE;
+        if ((p.w.n + kRowsPerTile - 1) / kRowsPerTile > ((int64_t)1 << kTileRowBits)) return QMV_ESHAPE;
+    }
+    return QMV_OK;
+}
+
+// Workspace image of a problem list: [DevProblem x count][tile entries],
+// problems ordered by decreasing row length so the longest tiles start first.
+struct Table {
+    std::vector<uint8_t> bytes;
+    int64_t tiles_offset = 0;
+    int32_t total_tiles = 0;
+    // per weight type: first tile, tile count, max m, max chunks
+    int32_t first[3] = {0, 0, 0}, count[3] = {0, 0, 0}, max_m[3] = {0, 0, 0}, max_chunks[3] = {0, 0, 0};
+};
+
+int64_t table_bytes(const qmv_problem* probs, int32_t count)
+{
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < count; ++i) tiles += (probs[i].w.n + kRowsPerTile - 1) / kRowsPerTile;
+    return round_up((int64_t)sizeof(DevProblem) * count, 256) + round_up(tiles * 4, 256);
+}
+
+void build_table(const qmv_problem* probs, int32_t count, Table& t)
+{
+    std::vector<int32_t> order(count);
+    for (int32_t i = 0; i < count; ++i) order[i] = i;
+    // group by weight type, then longest rows first (stable for equal keys)
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+        if (probs[a].w.wtype != probs[b].w.wtype) return probs[a].w.wtype < probs[b].w.wtype;
+        return row_stride(probs[a].w.wtype, probs[a].w.k) > row_stride(probs[b].w.wtype, probs[b].w.k);
+    });
+    const int64_t pbytes = round_up((int64_t)sizeof(DevProblem) * count, 256);
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < count; ++i) tiles += (probs[i].w.n + kRowsPerTile - 1) / kRowsPerTile;
+    t.bytes.assign(pbytes + round_up(tiles * 4, 256), 0);
+    t.tiles_offset = pbytes;
+    t.total_tiles = (int32_t)tiles;
+    DevProblem* dp = reinterpret_cast<DevProblem*>(t.bytes.data());
+    uint32_t* te = reinterpret_cast<uint32_t*>(t.bytes.data() + pbytes);
+    int32_t tile = 0;
+    for (int32_t slot = 0; slot < count; ++slot) {
+        const qmv_problem& p = probs[order[slot]];
+        const int32_t wt = p.w.wtype;
+        const int64_t stride = row_stride(wt, p.w.k);
+        DevProblem& d = dp[slot];
+        d.w = static_cast<const uint8_t*>(p.w.data);
+        d.sw = p.w.scale;
+        d.x8 = p.x8;
+        d.sx = p.sx;
+        d.y = p.y;
+        d.acc = p.acc;
+        d.n = (int32_t)p.w.n;
+        d.k = (int32_t)p.w.k;
+        d.m = (int32_t)p.m;
+        d.chunks = (int32_t)(stride / 16);
+        d.tile_begin = tile;
+        d.wtype = wt;
+        if (t.count[wt] == 0) t.first[wt] = tile;
+        const int32_t ntiles = (int32_t)((p.w.n + kRowsPerTile - 1) / kRowsPerTile);
+        for (int32_t r = 0; r < ntiles; ++r) te[tile + r] = ((uint32_t)slot << kTileRowBits) | (uint32_t)r;
+        tile += ntiles;
+        t.count[wt] += ntiles;
+        t.max_m[wt] = std::max<int32_t>(t.max_m[wt], (int32_t)p.m);
+        t.max_chunks[wt] = std::max<int32_t>(t.max_chunks[wt], d.chunks);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qmv_version(void) { return "qmv 0.1 (gfx950)"; }
+
+const char* qmv_status_str(int32_t status)
+{
+    switch (status) {
+        case QMV_OK: return "ok";
+        case QMV_EINVAL: return "invalid argument";
+        case QMV_ESHAPE: return "bad or unsupported shape";
+        case QMV_EVALUE: return "value out of range";
+        case QMV_EHIP: return "HIP runtime error";
+        case QMV_EUNSUPPORTED: return "unsupported weight type";
+        case QMV_EWORKSPACE: return "workspace missing or too small";
+        default: return "unknown status";
+    }
+}
+
+int64_t qmv_packed_bytes(int32_t wtype, int64_t n, int64_t k)
+{
+    if (n < 1 || k < 1 || n > QMV_MAX_N || k > QMV_MAX_K) return -1;
+    const int64_t s = row_stride(wtype, k);
+    return s < 0 ? -1 : n * s;
+}
+
+int32_t qmv_pack_ternary(const int8_t* trits, int64_t n, int64_t k, float scale, void* packed, float* scale_out,
+                         int32_t* bad_count, qmv_weight* desc_out, void* stream)
+{
+    if (!trits || !packed || !scale_out) return QMV_EINVAL;
+    if (n < 1 || k < 1 || n > QMV_MAX_N || k > QMV_MAX_K) return QMV_ESHAPE;
+    if (!aligned(packed, 16)) return QMV_EINVAL;
+    if (!std::isfinite(scale)) return QMV_EVALUE;
+    const hipStream_t s = as_stream(stream);
+    const int64_t chunks = row_stride(QMV_W_TERNARY5, k) / 16;
+    hipError_t e = launch_fill_pack_header(scale_out, scale, bad_count, s);
+    if (e == hipSuccess) e = launch_pack_ternary(trits, n, k, chunks, static_cast<uint8_t*>(packed), bad_count, s);
+    if (e != hipSuccess) return QMV_EHIP;
+    if (desc_out) {
+        desc_out->wtype = QMV_W_TERNARY5;
+        desc_out->reserved = 0;
+        desc_out->n = n;
+        desc_out->k = k;
+        desc_out->data = packed;
+        desc_out->scale = scale_out;
+    }
+    return QMV_OK;
+}
+
+int32_t qmv_pack_int8(const float* w, int64_t n, int64_t k, void* packed, float* scale_out, qmv_weight* desc_out,
+                      void* stream)
+{
+    if (!w || !packed || !scale_out) return QMV_EINVAL;
+    if (n < 1 || k < 1 || n > QMV_MAX_N || k > kMaxInt8K) return QMV_ESHAPE;
+    if (!aligned(packed, 16)) return QMV_EINVAL;
+    const int64_t chunks = row_stride(QMV_W_INT8, k) / 16;
+    hipError_t e = launch_pack_int8(w, n, k, chunks, static_cast<int8_t*>(packed), scale_out, as_stream(stream));
+    if (e != hipSuccess) return QMV_EHIP;
+    if (desc_out) {
+        desc_out->wtype = QMV_W_INT8;
+        desc_out->reserved = 0;
+        desc_out->n = n;
+        desc_out->k = k;
+        desc_out->data = packed;
+        desc_out->scale = scale_out;
+    }
+    return QMV_OK;
+}
+
+int32_t qmv_quantize_act(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, void* stream)
+{
+    if (!x || !x8 || !sx) return QMV_EINVAL;
+    if (m < 1 || k < 1 || k > QMV_MAX_K || m > ((int64_t)1 << 31) - 1) return QMV_ESHAPE;
+    return hip_status(launch_quantize_rows(x, m, k, x8, sx, as_stream(stream)));
+}
+
+int64_t qmv_gemv_workspace_bytes(const qmv_problem* probs, int32_t count)
+{
+    if (check_problems(probs, count, QMV_MAX_GEMV_M) != QMV_OK) return -1;
+    return table_bytes(probs, count);
+}
+
+int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, uint32_t flags,
+                 void* stream)
+{
+    int32_t st = check_problems(probs, count, QMV_MAX_GEMV_M);
+    if (st != QMV_OK) return st;
+    if (flags & ~(uint32_t)QMV_F_TABLE_READY) return QMV_EINVAL;
+    const int64_t need = table_bytes(probs, count);
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return QMV_EWORKSPACE;
+    Table t;
+    build_table(probs, count, t);
+    for (int wt = 1; wt <= 2; ++wt)
+        if (t.count[wt] && gemv_lds_bytes(wt, t.max_m[wt], t.max_chunks[wt]) > kMaxLds) return QMV_ESHAPE;
+    const hipStream_t s = as_stream(stream);
+    if (!(flags & QMV_F_TABLE_READY)) {
+        hipError_t e = hipMemcpyAsync(workspace, t.bytes.data(), t.bytes.size(), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return QMV_EHIP;
+    }
+    const DevProblem* dp = static_cast<const DevProblem*>(workspace);
+    const uint32_t* tiles = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(workspace) + t.tiles_offset);
+    for (int wt = 1; wt <= 2; ++wt) {
+        if (t.count[wt] == 0) continue;
+        hipError_t e = launch_gemv(dp, tiles, t.first[wt], t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
+        if (e != hipSuccess) return QMV_EHIP;
+    }
+    return QMV_OK;
+}
+
+int64_t qmv_prefill_workspace_bytes(const qmv_problem* probs, int32_t count)
+{
+    (void)probs;
+    (void)count;
+    return -1;
+}
+
+int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, uint32_t flags,
+                         void* stream)
+{
+    (void)probs;
+    (void)count;
+    (void)workspace;
+    (void)ws_bytes;
+    (void)flags;
+    (void)stream;
+    return QMV_EUNSUPPORTED;
+}
+
+int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k)
+{
+    if (v < 1 || k < 1 || v > QMV_MAX_N || k > QMV_MAX_K) return -1;
+    return round_up(lmhead_partials(v) * 8, 256);
+}
+
+int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int64_t k, int32_t* idx,
+                          float* max_logit, float* logits, void* workspace, int64_t ws_bytes, void* stream)
+{
+    if (!w_bf16 || !x || !idx) return QMV_EINVAL;
+    if (v < 1 || k < 1 || v > QMV_MAX_N || k > QMV_MAX_K) return QMV_ESHAPE;
+    const int64_t need = qmv_lmhead_workspace_bytes(v, k);
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return QMV_EWORKSPACE;
+    return hip_status(launch_lmhead(w_bf16, x, v, k, idx, max_logit, logits, workspace, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,319 @@
+// k_gemv.hip -- grouped weight-streaming GEMV for 1..16 tokens (gfx950).
+//
+// What is computed: for each problem, acc[m][r] = sum_c x8[m][c] * w[r][c]
+// exactly in int32 and y = acc * sx[m] * sw ("Gemma 3 1B at 114 tokens per
+// second on a laptop CPU", "Step 1": the weights are unpacked back to int8
+// and multiplied with a 4-way int8 dot product, exact integer arithmetic;
+// cpp20gemma README, "Architecture & implementation": the scales are applied
+// once, after the dot).
+//
+// How (MI355X):
+//  * Weights sit in the chunk-interleaved layout (chunk c of every row before
+//    chunk c+1), so lane l of a wave owns row r0+l and a wave's 16-byte load of
+//    one chunk is 1 KiB of contiguous HBM.  Each lane accumulates its own row:
+//    no cross-lane reduction is needed; the 4 waves of a workgroup split the
+//    row's chunks and meet in LDS at the end.
+//  * The activation vector is staged once per workgroup in LDS, reordered into
+//    trit-plane order (the page's "trit number i of 4 neighbouring bytes"
+//    grouping, "Step 1"): inside each 80-column chunk,
+//        xq[80c + 16i + 4w + b] = x8[80c + 20w + 5b + i],
+//    so digit plane i of packed dword w meets the 4-byte x group it multiplies.
+//    Every lane reads the same LDS address (a broadcast).
+//  * Unpacking a packed dword (4 bytes, 20 trits) uses prefix quotients
+//    P_j = floor(b / 3^(5-j)), j = 1..5 (P_5 = b).  Digit d_(5-j) = P_j - 3 P_(j-1),
+//    so  sum_i d_i X_i = sum_j P_j . X_(5-j) - 3 sum_(j<5) P_j . X_(4-j):
+//    two int32 accumulators, no digit subtraction.  floor(v/3) is one packed
+//    fp16 FMA on two bytes held as fp16 values 1024 + v: the product-sum
+//    (1024+v)*0.332763671875 + 683 rounds (round-to-nearest-even, exact
+//    fused FMA) to 1024 + floor(v/3) for every v in 0..242, checked
+//    exhaustively.  Four chained FMAs give P_4, P_3, P_2, P_1; v_perm_b32 gathers
+//    the bytes into dot4 operands.  P_5 = b may exceed 127, so it enters as
+//    b ^ 0x80 = b - 128 and 128 * sum(X_0) is added back.  Trits are
+//    t = d - 1, so sum(x) is subtracted.  All sums are modulo 2^32; the final
+//    value is exact whenever the true dot fits int32.
+#include "qmv_internal.hpp"
+
+namespace qmv {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c)
+{
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// Two fp16 lanes holding 1024 + v (v <= 242) -> 1024 + floor(v / 3).
+__device__ __forceinline__ uint32_t third2(uint32_t h)
+{
+    const half2_t mul = __builtin_bit_cast(half2_t, 0x35533553u);  // 0.332763671875
+    const half2_t add = __builtin_bit_cast(half2_t, 0x61566156u);  // 683.0
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, h), mul, add));
+}
+
+struct Planes {
+    uint32_t p1, p2, p3, p4, b5;
+};
+
+// One packed dword [b0 b1 b2 b3] -> prefix-quotient planes, byte k of each
+// plane belonging to packed byte k.
+__device__ __forceinline__ Planes unpack(uint32_t w)
+{
+    const uint32_t mag = 0x64646464u;                          // fp16 high byte of 1024
+    const uint32_t lo = __builtin_amdgcn_perm(mag, w, 0x04020400u);  // [b0 64 b2 64]
+    const uint32_t hi = __builtin_amdgcn_perm(mag, w, 0x04030401u);  // [b1 64 b3 64]
+    const uint32_t lo4 = third2(lo), hi4 = third2(hi);
+    const uint32_t lo3 = third2(lo4), hi3 = third2(hi4);
+    const uint32_t lo2 = third2(lo3), hi2 = third2(hi3);
+    const uint32_t lo1 = third2(lo2), hi1 = third2(hi2);
+    Planes p;
+    p.p4 = __builtin_amdgcn_perm(hi4, lo4, 0x06020400u);
+    p.p3 = __builtin_amdgcn_perm(hi3, lo3, 0x06020400u);
+    p.p2 = __builtin_amdgcn_perm(hi2, lo2, 0x06020400u);
+    p.p1 = __builtin_amdgcn_perm(hi1, lo1, 0x06020400u);
+    p.b5 = w ^ 0x80808080u;
+    return p;
+}
+
+__device__ __forceinline__ uint32_t sel(const uint4& v, int i)
+{
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+constexpr int kBatch = 4;  // chunks in flight per lane
+
+template <int MT, int WT>
+__global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ probs,
+                                                const uint32_t* __restrict__ tiles, int32_t tile_base)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    __shared__ int s_sum[MT];
+    __shared__ int s_sum0[MT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+
+    const uint32_t te = tiles[tile_base + blockIdx.x];
+    const DevProblem* P = probs + (te >> kTileRowBits);
+    const int rb = (int)(te & ((1u << kTileRowBits) - 1));
+    const int n = P->n, k = P->k, m = P->m, C = P->chunks;
+    const int row = rb * kRowsPerTile + lane;
+    const bool live = row < n;
+
+    const int per = (C + 3) >> 2;
+    const int c_lo = min(C, wave * per);
+    const int c_hi = min(C, c_lo + per);
+
+    const uint4* wp = reinterpret_cast<const uint4*>(P->w) + row;
+    const size_t cstride = (size_t)n;
+
+    // Issue the first weight loads before staging the activations.
+    uint4 buf[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int c = c_lo + u;
+        buf[u] = (live && c < c_hi) ? wp[(size_t)c * cstride] : make_uint4(0u, 0u, 0u, 0u);
+    }
+
+    // ---- stage activations in LDS ------------------------------------------
+    constexpr int kXBytesPerChunk = (WT == 1) ? 80 : 16;
+    const int dw_per_tok = (kXBytesPerChunk / 4) * C;
+    uint32_t* xs = reinterpret_cast<uint32_t*>(smem);
+    if (WT == 1) {
+        if (tid < MT) {
+            s_sum[tid] = 0;
+            s_sum0[tid] = 0;
+        }
+        __syncthreads();
+    }
+    for (int q = tid; q < m * dw_per_tok; q += kBlock) {
+        const int mi = q / dw_per_tok;
+        const int d = q - mi * dw_per_tok;
+        const int8_t* xr = P->x8 + (size_t)mi * k;
+        uint32_t v = 0;
+        if (WT == 1) {
+            const int c = d / 20;
+            const int r = d - c * 20;
+            const int i = r >> 2, wd = r & 3;
+            const int col0 = 80 * c + 20 * wd + i;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int col = col0 + 5 * b;
+                const uint32_t byte = (col < k) ? (uint32_t)(uint8_t)xr[col] : 0u;
+                v |= byte << (8 * b);
+            }
+            const int s = dot4(v, 0x01010101u, 0);
+            if (s) {
+                atomicAdd(&s_sum[mi], s);
+                if (i == 0) atomicAdd(&s_sum0[mi], s);
+            }
+        } else {
+            const int col0 = 4 * d;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int col = col0 + b;
+                const uint32_t byte = (col < k) ? (uint32_t)(uint8_t)xr[col] : 0u;
+                v |= byte << (8 * b);
+            }
+        }
+        xs[q] = v;
+    }
+    __syncthreads();
+
+    // ---- stream the wave's chunks --------------------------------------------
+    int acc_a[MT], acc_b[MT];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+        acc_a[mi] = 0;
+        acc_b[mi] = 0;
+    }
+    const uint4* xs4 = reinterpret_cast<const uint4*>(smem);
+    const int x4_per_tok = dw_per_tok / 4;
+
+    for (int c0 = c_lo; c0 < c_hi; c0 += kBatch) {
+        uint4 nxt[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = c0 + kBatch + u;
+            nxt[u] = (live && c < c_hi) ? wp[(size_t)c * cstride] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = c0 + u;
+            if (c < c_hi) {
+                if (WT == 1) {
+                    Planes pl[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) pl[j] = unpack(sel(buf[u], j));
+#pragma unroll
+                    for (int mi = 0; mi < MT; ++mi) {
+                        if (mi < m) {
+                            const uint4* xq = xs4 + mi * x4_per_tok + 5 * c;
+                            const uint4 X0 = xq[0], X1 = xq[1], X2 = xq[2], X3 = xq[3], X4 = xq[4];
+                            int a = acc_a[mi], b = acc_b[mi];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                                const uint32_t x0 = sel(X0, j), x1 = sel(X1, j), x2 = sel(X2, j);
+                                const uint32_t x3 = sel(X3, j), x4 = sel(X4, j);
+                                a = dot4(pl[j].p1, x4, a);
+                                a = dot4(pl[j].p2, x3, a);
+                                a = dot4(pl[j].p3, x2, a);
+                                a = dot4(pl[j].p4, x1, a);
+                                a = dot4(pl[j].b5, x0, a);
+                                b = dot4(pl[j].p1, x3, b);
+                                b = dot4(pl[j].p2, x2, b);
+                                b = dot4(pl[j].p3, x1, b);
+                                b = dot4(pl[j].p4, x0, b);
+                            }
+                            acc_a[mi] = a;
+                            acc_b[mi] = b;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int mi = 0; mi < MT; ++mi) {
+                        if (mi < m) {
+                            const uint4 X = xs4[mi * x4_per_tok + c];
+                            int a = acc_a[mi];
+                            a = dot4(buf[u].x, X.x, a);
+                            a = dot4(buf[u].y, X.y, a);
+                            a = dot4(buf[u].z, X.z, a);
+                            a = dot4(buf[u].w, X.w, a);
+                            acc_a[mi] = a;
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) buf[u] = nxt[u];
+    }
+
+    // ---- combine the four waves and write ------------------------------------
+    int* red = reinterpret_cast<int*>(smem + (size_t)MT * dw_per_tok * 4);
+    if (wave > 0) {
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            red[((wave - 1) * MT + mi) * 2 * kWave + lane] = acc_a[mi];
+            red[((wave - 1) * MT + mi) * 2 * kWave + kWave + lane] = acc_b[mi];
+        }
+    }
+    __syncthreads();
+    if (wave == 0 && live) {
+        const float sw = *P->sw;
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) {
+            if (mi < m) {
+                int a = acc_a[mi], b = acc_b[mi];
+#pragma unroll
+                for (int w = 0; w < 3; ++w) {
+                    a += red[(w * MT + mi) * 2 * kWave + lane];
+                    b += red[(w * MT + mi) * 2 * kWave + kWave + lane];
+                }
+                int total;
+                if (WT == 1) {
+                    total = (int)((uint32_t)a + 128u * (uint32_t)s_sum0[mi] - 3u * (uint32_t)b -
+                                  (uint32_t)s_sum[mi]);
+                } else {
+                    total = a;
+                }
+                const size_t o = (size_t)mi * n + row;
+                P->y[o] = (float)total * P->sx[mi] * sw;
+                if (P->acc) P->acc[o] = total;
+            }
+        }
+    }
+}
+
+int mt_for(int max_m)
+{
+    return max_m <= 1 ? 1 : max_m <= 2 ? 2 : max_m <= 4 ? 4 : max_m <= 8 ? 8 : 16;
+}
+
+size_t lds_bytes(int mt, int wt, int max_chunks)
+{
+    return (size_t)(wt == 1 ? 80 : 16) * max_chunks * mt + (size_t)3 * mt * 2 * kWave * 4;
+}
+
+template <int MT, int WT>
+hipError_t launch_one(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
+                      int max_chunks, hipStream_t s)
+{
+    const size_t lds = lds_bytes(MT, WT, max_chunks);
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<MT, WT>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((k_gemv<MT, WT>), dim3((unsigned)tile_count), dim3(kBlock), lds, s, probs, tiles,
+                       tile_begin);
+    return hipGetLastError();
+}
+
+template <int WT>
+hipError_t launch_wt(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
+                     int max_m, int max_chunks, hipStream_t s)
+{
+    if (max_m <= 1) return launch_one<1, WT>(probs, tiles, tile_begin, tile_count, max_chunks, s);
+    if (max_m <= 2) return launch_one<2, WT>(probs, tiles, tile_begin, tile_count, max_chunks, s);
+    if (max_m <= 4) return launch_one<4, WT>(probs, tiles, tile_begin, tile_count, max_chunks, s);
+    if (max_m <= 8) return launch_one<8, WT>(probs, tiles, tile_begin, tile_count, max_chunks, s);
+    return launch_one<16, WT>(probs, tiles, tile_begin, tile_count, max_chunks, s);
+}
+
+}  // namespace
+
+int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks)
+{
+    return (int64_t)lds_bytes(mt_for(max_m), wtype, max_chunks);
+}
+
+hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
+                       int wtype, int max_m, int max_chunks, hipStream_t s)
+{
+    if (wtype == 1) return launch_wt<1>(probs, tiles, tile_begin, tile_count, max_m, max_chunks, s);
+    return launch_wt<2>(probs, tiles, tile_begin, tile_count, max_m, max_chunks, s);
+}
+
+}  // namespace qmv

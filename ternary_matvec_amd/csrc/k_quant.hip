@@ -1,0 +1,211 @@
+// k_quant.hip -- activation quantisation and one-time weight packing.
+//
+// Quantisation formula (cpp20gemma README, "Architecture & implementation"):
+// scale = max(max|v|, 1e-9) / 127, code = clip(round(v / scale), -128, 127),
+// with one scale per token for activations ("Gemma 3 1B at 114 tokens per
+// second on a laptop CPU", "Step 2": every layer's inputs are rounded to int8)
+// and one per tensor for int8 weights.  Division is IEEE fp32 (the library is
+// built with correctly rounded division) and rounding is half-to-even
+// (v_rndne_f32), the IEEE default.
+//
+// Five trits per byte ("Step 1": 3^5 = 243 codes fit in a byte): byte j of a
+// row is sum_i (t[5j+i] + 1) * 3^i; columns past k count as trit 0.
+#include "qmv_internal.hpp"
+
+namespace qmv {
+namespace {
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Max over a 256-thread block; every thread receives the result.
+__device__ __forceinline__ float block_max(float v, float* red)
+{
+    v = wave_max(v);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float scale_from_max(float m)
+{
+    return fmaxf(m, 1e-9f) / 127.0f;
+}
+
+__device__ __forceinline__ int8_t quantize_one(float v, float s)
+{
+    float q = __builtin_rintf(v / s);
+    q = fminf(fmaxf(q, -128.0f), 127.0f);
+    return (int8_t)(int)q;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row quantisation: one workgroup per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void k_quantize_rows(const float* __restrict__ x, int64_t k,
+                                                         int8_t* __restrict__ x8, float* __restrict__ sx)
+{
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * k;
+    int8_t* qr = x8 + row * k;
+    float m = 0.0f;
+    const bool vec = ((reinterpret_cast<uintptr_t>(xr) & 15) == 0);
+    int64_t head = vec ? (k & ~int64_t(3)) : 0;
+    if (vec) {
+        const float4* x4 = reinterpret_cast<const float4*>(xr);
+        for (int64_t i = threadIdx.x; i < head / 4; i += kBlock) {
+            float4 v = x4[i];
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        }
+    }
+    for (int64_t i = head + threadIdx.x; i < k; i += kBlock) m = fmaxf(m, fabsf(xr[i]));
+    m = block_max(m, red);
+    const float s = scale_from_max(m);
+    if (threadIdx.x == 0) sx[row] = s;
+    const bool vec_out = vec && ((reinterpret_cast<uintptr_t>(qr) & 3) == 0);
+    if (vec_out) {
+        const float4* x4 = reinterpret_cast<const float4*>(xr);
+        uint32_t* q4 = reinterpret_cast<uint32_t*>(qr);
+        for (int64_t i = threadIdx.x; i < head / 4; i += kBlock) {
+            float4 v = x4[i];
+            uint32_t b0 = (uint8_t)quantize_one(v.x, s), b1 = (uint8_t)quantize_one(v.y, s);
+            uint32_t b2 = (uint8_t)quantize_one(v.z, s), b3 = (uint8_t)quantize_one(v.w, s);
+            q4[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+        for (int64_t i = head + threadIdx.x; i < k; i += kBlock) qr[i] = quantize_one(xr[i], s);
+    } else {
+        for (int64_t i = threadIdx.x; i < k; i += kBlock) qr[i] = quantize_one(xr[i], s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Packing.
+// ---------------------------------------------------------------------------
+__global__ void k_fill_pack_header(float* scale_out, float scale, int32_t* bad)
+{
+    if (threadIdx.x == 0) {
+        *scale_out = scale;
+        if (bad) *bad = 0;
+    }
+}
+
+// One thread per output byte, in device order: o = (c * n + r) * 16 + jj.
+__global__ __launch_bounds__(kBlock) void k_pack_ternary(const int8_t* __restrict__ t, int64_t n, int64_t k,
+                                                        int64_t total, uint8_t* __restrict__ out,
+                                                        int32_t* __restrict__ bad)
+{
+    int nbad = 0;
+    for (int64_t o = (int64_t)blockIdx.x * kBlock + threadIdx.x; o < total; o += (int64_t)gridDim.x * kBlock) {
+        const int64_t slot = o >> 4;
+        const int64_t c = slot / n;
+        const int64_t r = slot - c * n;
+        const int64_t j = c * 16 + (o & 15);
+        const int8_t* tr = t + r * k;
+        int code = 0, place = 1;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int64_t col = 5 * j + i;
+            int trit = 0;
+            if (col < k) {
+                trit = tr[col];
+                if (trit < -1 || trit > 1) {
+                    ++nbad;
+                    trit = 0;
+                }
+            }
+            code += (trit + 1) * place;
+            place *= 3;
+        }
+        out[o] = (uint8_t)code;
+    }
+    if (bad && nbad) atomicAdd(bad, nbad);
+}
+
+__global__ void k_zero_u32(uint32_t* p)
+{
+    if (threadIdx.x == 0) *p = 0u;
+}
+
+// Max |w| over the tensor into *cell (fp32 bits; non-negative, so unsigned
+// order is float order).
+__global__ __launch_bounds__(kBlock) void k_absmax(const float* __restrict__ w, int64_t count, uint32_t* cell)
+{
+    __shared__ float red[4];
+    float m = 0.0f;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < count; i += (int64_t)gridDim.x * kBlock)
+        m = fmaxf(m, fabsf(w[i]));
+    m = block_max(m, red);
+    if (threadIdx.x == 0) atomicMax(cell, __float_as_uint(m));
+}
+
+__global__ __launch_bounds__(kBlock) void k_pack_int8(const float* __restrict__ w, int64_t n, int64_t k,
+                                                     int64_t total, int8_t* __restrict__ out,
+                                                     const uint32_t* __restrict__ cell)
+{
+    const float s = scale_from_max(__uint_as_float(*cell));
+    for (int64_t o = (int64_t)blockIdx.x * kBlock + threadIdx.x; o < total; o += (int64_t)gridDim.x * kBlock) {
+        const int64_t slot = o >> 4;
+        const int64_t c = slot / n;
+        const int64_t r = slot - c * n;
+        const int64_t j = c * 16 + (o & 15);
+        out[o] = (j < k) ? quantize_one(w[r * k + j], s) : (int8_t)0;
+    }
+}
+
+__global__ void k_finish_int8_scale(float* scale_out)
+{
+    if (threadIdx.x == 0) *scale_out = scale_from_max(*scale_out);
+}
+
+int grid_for(int64_t items)
+{
+    int64_t g = (items + kBlock - 1) / kBlock;
+    if (g > 65536) g = 65536;
+    if (g < 1) g = 1;
+    return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)m), dim3(kBlock), 0, s, x, k, x8, sx);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_pack_header(float* scale_out, float scale, int32_t* bad, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_fill_pack_header, dim3(1), dim3(kWave), 0, s, scale_out, scale, bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_ternary(const int8_t* trits, int64_t n, int64_t k, int64_t chunks, uint8_t* out,
+                               int32_t* bad, hipStream_t s)
+{
+    const int64_t total = n * chunks * 16;
+    hipLaunchKernelGGL(k_pack_ternary, dim3(grid_for(total)), dim3(kBlock), 0, s, trits, n, k, total, out, bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_int8(const float* w, int64_t n, int64_t k, int64_t chunks, int8_t* out, float* scale_out,
+                            hipStream_t s)
+{
+    uint32_t* cell = reinterpret_cast<uint32_t*>(scale_out);
+    const int64_t count = n * k;
+    const int64_t total = n * chunks * 16;
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(kWave), 0, s, cell);
+    hipLaunchKernelGGL(k_absmax, dim3(grid_for(count)), dim3(kBlock), 0, s, w, count, cell);
+    hipLaunchKernelGGL(k_pack_int8, dim3(grid_for(total)), dim3(kBlock), 0, s, w, n, k, total, out,
+                       (const uint32_t*)cell);
+    hipLaunchKernelGGL(k_finish_int8_scale, dim3(1), dim3(kWave), 0, s, scale_out);
+    return hipGetLastError();
+}
+
+}  // namespace qmv

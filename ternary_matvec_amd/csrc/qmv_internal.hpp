@@ -1,0 +1,48 @@
+// qmv_internal.hpp -- device-side descriptors and helpers shared by the HIP
+// kernels of libqmv (gfx950 only).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+constexpr int kWave = 64;         // CDNA wavefront width
+constexpr int kBlock = 256;       // threads per workgroup for the streaming kernels
+constexpr int kRowsPerTile = 64;  // one output row per lane of a wave
+constexpr int kTileProbBits = 14; // tile entry = problem << 18 | row block
+constexpr int kTileRowBits = 18;
+
+// One problem as the kernels see it (uploaded into the caller's workspace).
+struct DevProblem {
+    const uint8_t* w;    // packed weights in the chunk-interleaved layout
+    const float* sw;     // 1 fp32 weight scale
+    const int8_t* x8;    // [m][k] int8 activations, natural column order
+    const float* sx;     // [m] fp32 activation scales
+    float* y;            // [m][n] fp32 outputs
+    int32_t* acc;        // [m][n] int32 exact dots, or null
+    int32_t n;           // output rows
+    int32_t k;           // input columns
+    int32_t m;           // tokens
+    int32_t chunks;      // 16-byte chunks per row (row stride / 16)
+    int32_t tile_begin;  // first tile of this problem in the launch
+    int32_t wtype;       // 1 = five trits per byte, 2 = int8
+};
+static_assert(sizeof(DevProblem) == 72, "DevProblem layout");
+
+// Launchers implemented in the kernel translation units.
+hipError_t launch_fill_pack_header(float* scale_out, float scale, int32_t* bad, hipStream_t s);
+hipError_t launch_pack_ternary(const int8_t* trits, int64_t n, int64_t k, int64_t chunks, uint8_t* out,
+                               int32_t* bad, hipStream_t s);
+hipError_t launch_pack_int8(const float* w, int64_t n, int64_t k, int64_t chunks, int8_t* out,
+                            float* scale_out, hipStream_t s);
+hipError_t launch_quantize_rows(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, hipStream_t s);
+int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks);
+constexpr int64_t kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
+hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
+                       int wtype, int max_m, int max_chunks, hipStream_t s);
+hipError_t launch_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, int32_t* idx,
+                         float* max_logit, float* logits, void* workspace, hipStream_t s);
+int64_t lmhead_partials(int64_t v);
+
+}  // namespace qmv

@@ -1,0 +1,266 @@
+"""ctypes binding of libqmv (include/qmv.h) over PyTorch device tensors.
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch supplies device memory and the current stream.  If the library has
+not been built, `load()` raises -- there is no fallback of any kind.
+"""
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqmv.so")
+
+QMV_OK = 0
+QMV_EINVAL = -1
+QMV_ESHAPE = -2
+QMV_EVALUE = -3
+QMV_EHIP = -4
+QMV_EUNSUPPORTED = -5
+QMV_EWORKSPACE = -6
+
+QMV_W_TERNARY5 = 1
+QMV_W_INT8 = 2
+QMV_F_TABLE_READY = 1
+QMV_MAX_GEMV_M = 16
+
+_c_i32, _c_i64, _c_u32, _c_ptr, _c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
+
+
+class qmv_weight(ctypes.Structure):
+    _fields_ = [("wtype", _c_i32), ("reserved", _c_i32), ("n", _c_i64), ("k", _c_i64),
+                ("data", _c_ptr), ("scale", _c_ptr)]
+
+
+class qmv_problem(ctypes.Structure):
+    _fields_ = [("w", qmv_weight), ("x8", _c_ptr), ("sx", _c_ptr), ("m", _c_i64), ("y", _c_ptr),
+                ("acc", _c_ptr)]
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, status_str(status), status))
+
+
+_lib = None
+
+# name -> (restype, argtypes); mirrors include/qmv.h
+SIGNATURES = {
+    "qmv_version": (ctypes.c_char_p, []),
+    "qmv_status_str": (ctypes.c_char_p, [_c_i32]),
+    "qmv_packed_bytes": (_c_i64, [_c_i32, _c_i64, _c_i64]),
+    "qmv_pack_ternary": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_f32, _c_ptr, _c_ptr, _c_ptr,
+                                  ctypes.POINTER(qmv_weight), _c_ptr]),
+    "qmv_pack_int8": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.POINTER(qmv_weight), _c_ptr]),
+    "qmv_quantize_act": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "qmv_gemv_workspace_bytes": (_c_i64, [ctypes.POINTER(qmv_problem), _c_i32]),
+    "qmv_prefill_workspace_bytes": (_c_i64, [ctypes.POINTER(qmv_problem), _c_i32]),
+    "qmv_gemv": (_c_i32, [ctypes.POINTER(qmv_problem), _c_i32, _c_ptr, _c_i64, _c_u32, _c_ptr]),
+    "qmv_gemm_prefill": (_c_i32, [ctypes.POINTER(qmv_problem), _c_i32, _c_ptr, _c_i64, _c_u32, _c_ptr]),
+    "qmv_lmhead_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
+    "qmv_lmhead_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64,
+                                   _c_ptr]),
+}
+
+
+def load(path: str = LIB_PATH):
+    """Load libqmv.so (built by ternary_matvec_amd.build); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError("libqmv.so not found at %s: build it with "
+                               "`python -c 'import __graft_entry__; __graft_entry__.build()'`" % path)
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return load().qmv_status_str(status).decode()
+
+
+def version() -> str:
+    return load().qmv_version().decode()
+
+
+def _check(status, what):
+    if status != QMV_OK:
+        raise QmvError(status, what)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, dtype, what):
+    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
+        raise ValueError("%s must be a contiguous %s CUDA tensor" % (what, dtype))
+    return t
+
+
+def _alloc_aligned(nbytes, device, align=256):
+    """A uint8 tensor of nbytes whose data pointer is `align`-aligned (plumbing only)."""
+    raw = torch.empty(nbytes + align, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % align
+    return raw[off:off + nbytes]
+
+
+def qmv_packed_bytes(wtype: int, n: int, k: int) -> int:
+    return int(load().qmv_packed_bytes(wtype, n, k))
+
+
+class Weight:
+    """A packed matrix: device bytes, device scale and its host descriptor."""
+
+    def __init__(self, desc: qmv_weight, packed: torch.Tensor, scale: torch.Tensor):
+        self.desc = desc
+        self.packed = packed
+        self.scale = scale
+
+    @property
+    def n(self):
+        return int(self.desc.n)
+
+    @property
+    def k(self):
+        return int(self.desc.k)
+
+    @property
+    def wtype(self):
+        return int(self.desc.wtype)
+
+
+def qmv_pack_ternary(trits, scale: float, packed=None, scale_out=None, bad_count=None, stream=None) -> Weight:
+    _dev(trits, torch.int8, "trits")
+    n, k = trits.shape
+    nbytes = qmv_packed_bytes(QMV_W_TERNARY5, n, k)
+    if packed is None:
+        packed = _alloc_aligned(nbytes, trits.device, 16)
+    if scale_out is None:
+        scale_out = torch.empty(1, dtype=torch.float32, device=trits.device)
+    desc = qmv_weight()
+    _check(load().qmv_pack_ternary(_ptr(trits), n, k, float(scale), _ptr(packed), _ptr(scale_out),
+                                   _ptr(bad_count), ctypes.byref(desc), _stream(stream)), "qmv_pack_ternary")
+    return Weight(desc, packed, scale_out)
+
+
+def qmv_pack_int8(w, packed=None, scale_out=None, stream=None) -> Weight:
+    _dev(w, torch.float32, "w")
+    n, k = w.shape
+    nbytes = qmv_packed_bytes(QMV_W_INT8, n, k)
+    if packed is None:
+        packed = _alloc_aligned(nbytes, w.device, 16)
+    if scale_out is None:
+        scale_out = torch.empty(1, dtype=torch.float32, device=w.device)
+    desc = qmv_weight()
+    _check(load().qmv_pack_int8(_ptr(w), n, k, _ptr(packed), _ptr(scale_out), ctypes.byref(desc),
+                                _stream(stream)), "qmv_pack_int8")
+    return Weight(desc, packed, scale_out)
+
+
+def qmv_quantize_act(x, x8=None, sx=None, stream=None):
+    _dev(x, torch.float32, "x")
+    m, k = x.shape
+    if x8 is None:
+        x8 = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check(load().qmv_quantize_act(_ptr(x), m, k, _ptr(x8), _ptr(sx), _stream(stream)), "qmv_quantize_act")
+    return x8, sx
+
+
+class Problem:
+    """y[m][n] = (x8 . W) * sx * scale for one weight matrix and m tokens."""
+
+    def __init__(self, weight: Weight, x8, sx, y=None, acc=None):
+        _dev(x8, torch.int8, "x8")
+        _dev(sx, torch.float32, "sx")
+        m = x8.shape[0]
+        if y is None:
+            y = torch.empty((m, weight.n), dtype=torch.float32, device=x8.device)
+        self.weight, self.x8, self.sx, self.y, self.acc = weight, x8, sx, y, acc
+
+    def struct(self) -> qmv_problem:
+        p = qmv_problem()
+        p.w = self.weight.desc
+        p.x8 = self.x8.data_ptr()
+        p.sx = self.sx.data_ptr()
+        p.m = self.x8.shape[0]
+        p.y = self.y.data_ptr()
+        p.acc = None if self.acc is None else self.acc.data_ptr()
+        return p
+
+
+def problem_array(problems):
+    arr = (qmv_problem * len(problems))()
+    for i, p in enumerate(problems):
+        arr[i] = p.struct()
+    return arr
+
+
+def qmv_gemv_workspace_bytes(arr) -> int:
+    return int(load().qmv_gemv_workspace_bytes(arr, len(arr)))
+
+
+def qmv_prefill_workspace_bytes(arr) -> int:
+    return int(load().qmv_prefill_workspace_bytes(arr, len(arr)))
+
+
+def _grouped(fn_name, ws_fn, problems, workspace, flags, stream):
+    arr = problems if isinstance(problems, ctypes.Array) else problem_array(problems)
+    need = ws_fn(arr)
+    if need < 0:
+        raise QmvError(QMV_ESHAPE, fn_name)
+    if workspace is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+        workspace = _alloc_aligned(max(need, 256), dev)
+    _check(getattr(load(), fn_name)(arr, len(arr), _ptr(workspace), workspace.numel(), flags, _stream(stream)),
+           fn_name)
+    return workspace
+
+
+def qmv_gemv(problems, workspace=None, flags=0, stream=None):
+    """Grouped GEMV (1..16 tokens per problem) in one launch; returns the workspace used."""
+    return _grouped("qmv_gemv", qmv_gemv_workspace_bytes, problems, workspace, flags, stream)
+
+
+def qmv_gemm_prefill(problems, workspace=None, flags=0, stream=None):
+    """Grouped int8-MFMA GEMM for any number of tokens; returns the workspace used."""
+    return _grouped("qmv_gemm_prefill", qmv_prefill_workspace_bytes, problems, workspace, flags, stream)
+
+
+def qmv_lmhead_workspace_bytes(v: int, k: int) -> int:
+    return int(load().qmv_lmhead_workspace_bytes(v, k))
+
+
+def qmv_lmhead_argmax(w_bf16, x, logits=None, idx=None, max_logit=None, workspace=None, want_logits=False,
+                      stream=None):
+    """Returns (idx tensor [1] int32, max_logit tensor [1] fp32, logits or None)."""
+    if w_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("w_bf16 must hold bf16 bit patterns")
+    _dev(x, torch.float32, "x")
+    v, k = w_bf16.shape
+    dev = x.device
+    if idx is None:
+        idx = torch.empty(1, dtype=torch.int32, device=dev)
+    if max_logit is None:
+        max_logit = torch.empty(1, dtype=torch.float32, device=dev)
+    if logits is None and want_logits:
+        logits = torch.empty(v, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _alloc_aligned(max(qmv_lmhead_workspace_bytes(v, k), 256), dev)
+    _check(load().qmv_lmhead_argmax(_ptr(w_bf16), _ptr(x), v, k, _ptr(idx), _ptr(max_logit), _ptr(logits),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)), "qmv_lmhead_argmax")
+    return idx, max_logit, logits

@@ -146,3 +146,61 @@ def decode_stack(mats, layers, config_id, m=1, act_seed_config=None):
             s = ternary_scale(stream_seed(config_id, layer, mid, TAG_SCALE))
             x = normal(stream_seed(acfg, layer, mid, TAG_ACT), (m, k))
             yield layer, mid, name, n, k, t, s, x
+
+
+# --------------------------------------------------------------------------
+# The same counter-based streams drawn with torch (on any device), for inputs
+# too large to draw quickly on the host.  Integer draws (raw, trits) are
+# bit-identical to the NumPy ones above.  Normal draws use the device's own
+# log/cos, so their last bits may differ from the NumPy draw: code that hands
+# a torch-drawn tensor to the oracle copies that very tensor to the host.
+# --------------------------------------------------------------------------
+
+def _i64(u: int) -> int:
+    u &= (1 << 64) - 1
+    return u - (1 << 64) if u >= (1 << 63) else u
+
+
+def _lsr(z, s: int):
+    import torch
+    return torch.bitwise_and(torch.bitwise_right_shift(z, s), (1 << (64 - s)) - 1)
+
+
+def raw_torch(seed: int, count: int, start: int = 0, device="cpu"):
+    """int64 tensor holding the uint64 stream outputs (two's complement)."""
+    import torch
+    z = torch.arange(start + 1, start + count + 1, dtype=torch.int64, device=device)
+    z.mul_(_i64(0x9E3779B97F4A7C15)).add_(_i64(seed))
+    z.bitwise_xor_(_lsr(z, 30)).mul_(_i64(0xBF58476D1CE4E5B9))
+    z.bitwise_xor_(_lsr(z, 27)).mul_(_i64(0x94D049BB133111EB))
+    z.bitwise_xor_(_lsr(z, 31))
+    return z
+
+
+def trits_torch(seed: int, shape, device="cpu", start: int = 0, block: int = 1 << 24):
+    """Same trits as `trits` (bit-identical), drawn with torch."""
+    import torch
+    count = int(np.prod(shape))
+    lut = torch.tensor(_TRIT_OF_DECILE, dtype=torch.int8, device=device)
+    out = torch.empty(count, dtype=torch.int8, device=device)
+    for b0 in range(0, count, block):
+        b1 = min(count, b0 + block)
+        z = raw_torch(seed, b1 - b0, start + b0, device)
+        r = torch.remainder(_lsr(z, 32), 10)
+        out[b0:b1] = lut[r]
+    return out.reshape(shape)
+
+
+def normal_torch(seed: int, shape, std: float = 1.0, device="cpu", block: int = 1 << 23):
+    """N(0, std^2) fp32 draws from the same stream layout as `normal` (device math)."""
+    import torch
+    count = int(np.prod(shape))
+    out = torch.empty(count, dtype=torch.float32, device=device)
+    for b0 in range(0, count, block):
+        b1 = min(count, b0 + block)
+        z = raw_torch(seed, 2 * (b1 - b0), 2 * b0, device)
+        u = _lsr(z, 11).to(torch.float64) * (2.0 ** -53)
+        u = u.reshape(-1, 2)
+        r = torch.sqrt(-2.0 * torch.log1p(-u[:, 0]))
+        out[b0:b1] = (r * torch.cos(2.0 * np.pi * u[:, 1]) * std).to(torch.float32)
+    return out.reshape(shape)

@@ -1,0 +1,123 @@
+"""The C-ABI library loads and exports every symbol include/qmv.h declares.
+
+CPU only: these calls validate host-side arguments and return before any
+device work, so no GPU is needed.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from ternary_matvec_amd import qmv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "qmv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(qmv.LIB_PATH):
+        pytest.fail("libqmv.so is not built (run __graft_entry__.build())")
+    return qmv.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert "qmv_gemv" in names and "qmv_lmhead_argmax" in names
+    for name in names:
+        assert hasattr(lib, name), name
+    # the binding declares exactly the header's functions
+    assert sorted(qmv.SIGNATURES) == names
+
+
+def test_north_star_entry_points_present(lib):
+    for name in ("qmv_pack_ternary", "qmv_pack_int8", "qmv_quantize_act", "qmv_gemv", "qmv_gemm_prefill",
+                 "qmv_lmhead_argmax"):
+        assert hasattr(lib, name)
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in qmv.version()
+    assert qmv.status_str(0) == "ok"
+    assert qmv.status_str(qmv.QMV_EWORKSPACE) == "workspace missing or too small"
+    assert qmv.status_str(12345) == "unknown status"
+
+
+def test_packed_bytes(lib):
+    assert qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, 1024, 1152) == 1024 * 240
+    assert qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, 1152, 6912) == 1152 * 1392
+    assert qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, 3, 81) == 3 * 32
+    assert qmv.qmv_packed_bytes(qmv.QMV_W_INT8, 768, 288) == 768 * 288
+    assert qmv.qmv_packed_bytes(qmv.QMV_W_INT8, 2, 17) == 64
+    assert qmv.qmv_packed_bytes(7, 2, 17) == -1
+    assert qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, 0, 17) == -1
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_host_validation_errors(lib):
+    desc = qmv.qmv_weight()
+    s = None
+    # null pointers
+    assert lib.qmv_pack_ternary(None, 4, 4, 1.0, _fake(4096), _fake(8192), None, ctypes.byref(desc), s) == qmv.QMV_EINVAL
+    assert lib.qmv_quantize_act(None, 1, 4, _fake(4096), _fake(8192), s) == qmv.QMV_EINVAL
+    # bad shapes
+    assert lib.qmv_pack_ternary(_fake(64), 0, 4, 1.0, _fake(4096), _fake(8192), None, None, s) == qmv.QMV_ESHAPE
+    assert lib.qmv_quantize_act(_fake(64), 1, 0, _fake(4096), _fake(8192), s) == qmv.QMV_ESHAPE
+    # misaligned packed buffer, non-finite scale
+    assert lib.qmv_pack_ternary(_fake(64), 2, 4, 1.0, _fake(4097), _fake(8192), None, None, s) == qmv.QMV_EINVAL
+    assert lib.qmv_pack_ternary(_fake(64), 2, 4, float("inf"), _fake(4096), _fake(8192), None, None, s) == qmv.QMV_EVALUE
+    # int8 K limit keeps every dot inside int32
+    assert lib.qmv_pack_int8(_fake(64), 2, 70000, _fake(4096), _fake(8192), None, s) == qmv.QMV_ESHAPE
+    # lm_head
+    assert lib.qmv_lmhead_argmax(_fake(4096), _fake(64), 10, 8, None, None, None, _fake(256), 4096, s) == qmv.QMV_EINVAL
+    assert lib.qmv_lmhead_argmax(_fake(4096), _fake(64), 10, 8, _fake(64), None, None, None, 0, s) == qmv.QMV_EWORKSPACE
+    assert qmv.qmv_lmhead_workspace_bytes(262144, 1152) > 0
+
+
+def _problem(wtype=qmv.QMV_W_TERNARY5, n=64, k=80, m=1, data=4096):
+    p = qmv.qmv_problem()
+    p.w.wtype, p.w.reserved, p.w.n, p.w.k, p.w.data, p.w.scale = wtype, 0, n, k, data, 8192
+    p.x8, p.sx, p.m, p.y, p.acc = 12288, 16384, m, 20480, None
+    return p
+
+
+def test_gemv_validation(lib):
+    arr = (qmv.qmv_problem * 2)(_problem(), _problem(n=100, k=1152, m=3))
+    need = lib.qmv_gemv_workspace_bytes(arr, 2)
+    assert need > 0 and need % 256 == 0
+    # workspace missing / too small / misaligned
+    assert lib.qmv_gemv(arr, 2, None, 0, 0, None) == qmv.QMV_EWORKSPACE
+    assert lib.qmv_gemv(arr, 2, _fake(1 << 20), need - 1, 0, None) == qmv.QMV_EWORKSPACE
+    assert lib.qmv_gemv(arr, 2, _fake((1 << 20) + 64), need, 0, None) == qmv.QMV_EWORKSPACE
+    # bad flags
+    assert lib.qmv_gemv(arr, 2, _fake(1 << 20), need, 4, None) == qmv.QMV_EINVAL
+    # m out of range for the GEMV
+    bad = (qmv.qmv_problem * 1)(_problem(m=17))
+    assert lib.qmv_gemv(bad, 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_ESHAPE
+    assert lib.qmv_gemv_workspace_bytes(bad, 1) == -1
+    # unknown weight type, reserved field, misaligned weights, null y
+    bad = (qmv.qmv_problem * 1)(_problem(wtype=9))
+    assert lib.qmv_gemv(bad, 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EUNSUPPORTED
+    p = _problem()
+    p.w.reserved = 1
+    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EINVAL
+    p = _problem(data=4100)
+    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EINVAL
+    p = _problem()
+    p.y = None
+    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EINVAL
+    # activations too large to stage for 16 tokens
+    big = (qmv.qmv_problem * 1)(_problem(n=64, k=1 << 20, m=16))
+    assert lib.qmv_gemv(big, 1, _fake(1 << 20), 1 << 30, 0, None) == qmv.QMV_ESHAPE
+    # count
+    assert lib.qmv_gemv(arr, 0, _fake(1 << 20), need, 0, None) == qmv.QMV_ESHAPE
+    assert lib.qmv_gemv(None, 1, _fake(1 << 20), need, 0, None) == qmv.QMV_EINVAL

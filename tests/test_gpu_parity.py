@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact for packed bytes, int8 codes, scales and int32 accumulators; fp32
+outputs within 1e-6 relative of the oracle's correctly rounded value; bf16
+output-layer logits within max(2e-2 |r|, gamma_K * sum|w x|) and the chosen
+index equal to the oracle's unless the two logits are within that tolerance.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from ternary_matvec_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def _t(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+def _x_for(seed, m, k, std=1.0):
+    return synth.normal(seed, (m, k), std=std)
+
+
+# --------------------------------------------------------------------------
+# A1: activation quantisation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m,k", [(1, 1), (1, 7), (2, 5), (3, 288), (130, 1152), (2, 6912), (4, 1537), (1, 70001)])
+def test_quantize_act_bit_exact(qmv_gpu, m, k):
+    from ternary_matvec_amd import qmv
+    say("quantize_act", m, k)
+    x = _x_for(1000 + k, m, k, std=2.5)
+    if m > 1:
+        x[1, :] = 0.0                       # zero row -> floor scale
+    x[0, 0] = 127.0 if k > 1 else x[0, 0]   # keep one exact half case alive in row 0
+    if k > 3:
+        x[0, 1], x[0, 2], x[0, 3] = 0.5, 2.5, -2.5
+    q_ref, s_ref = oracle.quantize_rows(x)
+    x8, sx = qmv.qmv_quantize_act(_t(x))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(sx.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    np.testing.assert_array_equal(x8.cpu().numpy(), q_ref)
+
+
+def test_quantize_act_unaligned_rows(qmv_gpu):
+    from ternary_matvec_amd import qmv
+    say("quantize_act unaligned")
+    x = _x_for(77, 5, 33)
+    big = torch.zeros(5 * 33 + 1, dtype=torch.float32, device=DEV)
+    big[1:] = _t(x).reshape(-1)
+    xin = big[1:].view(5, 33)                      # 4-byte aligned, not 16-byte aligned
+    x8 = torch.empty(5 * 33 + 3, dtype=torch.int8, device=DEV)[3:].view(5, 33)
+    sx = torch.empty(5, dtype=torch.float32, device=DEV)
+    qmv.qmv_quantize_act(xin, x8=x8, sx=sx)
+    q_ref, s_ref = oracle.quantize_rows(x)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(x8.cpu().numpy(), q_ref)
+    np.testing.assert_array_equal(sx.cpu().numpy(), s_ref)
+
+
+# --------------------------------------------------------------------------
+# A10: packing
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,k", [(1, 1), (3, 7), (9, 23), (64, 81), (300, 1152), (17, 6912), (65, 160)])
+def test_pack_ternary_bit_exact(qmv_gpu, n, k):
+    from ternary_matvec_amd import qmv
+    say("pack_ternary", n, k)
+    t = synth.trits(2000 + k, (n, k))
+    ref, bad = oracle.pack_trit5(t)
+    bad_dev = torch.full((1,), 77, dtype=torch.int32, device=DEV)
+    w = qmv.qmv_pack_ternary(_t(t), 0.0173, bad_count=bad_dev)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(w.packed.cpu().numpy(), ref)
+    assert w.scale.item() == np.float32(0.0173)
+    assert bad_dev.item() == bad == 0
+    assert w.n == n and w.k == k and w.wtype == qmv.QMV_W_TERNARY5
+
+
+def test_pack_ternary_counts_bad_trits(qmv_gpu):
+    from ternary_matvec_amd import qmv
+    say("pack_ternary bad trits")
+    t = synth.trits(31, (40, 50))
+    t[3, 4], t[17, 0], t[39, 49] = 2, -5, 100
+    ref, bad = oracle.pack_trit5(t)
+    bad_dev = torch.zeros(1, dtype=torch.int32, device=DEV)
+    w = qmv.qmv_pack_ternary(_t(t), 1.0, bad_count=bad_dev)
+    torch.cuda.synchronize()
+    assert bad == 3 and bad_dev.item() == 3
+    np.testing.assert_array_equal(w.packed.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("n,k", [(768, 288), (5, 17), (1, 1), (33, 100)])
+def test_pack_int8_bit_exact(qmv_gpu, n, k):
+    from ternary_matvec_amd import qmv
+    say("pack_int8", n, k)
+    w = synth.normal(3000 + k, (n, k), std=0.02)
+    q_ref, s_ref = oracle.quantize_tensor(w)
+    ref = oracle.layout_int8(q_ref)
+    pw = qmv.qmv_pack_int8(_t(w))
+    torch.cuda.synchronize()
+    assert pw.scale.cpu().numpy().view(np.uint32)[0] == np.float32(s_ref).view(np.uint32)
+    np.testing.assert_array_equal(pw.packed.cpu().numpy().view(np.int8), ref)
+
+
+# --------------------------------------------------------------------------
+# A2-A7: GEMV
+# --------------------------------------------------------------------------
+
+def _check_y(y, acc_ref, sx, sw):
+    y_ref = oracle.dequant(acc_ref, sx, sw)
+    err = np.abs(y.astype(np.float64) - y_ref.astype(np.float64))
+    tol = 1e-6 * np.abs(y_ref.astype(np.float64))
+    assert np.all(err <= tol), float((err - tol).max())
+    assert np.all(y[acc_ref == 0] == 0.0)
+
+
+GEMV_CASES = [(1, 1, 1), (5, 7, 1), (64, 80, 1), (65, 81, 2), (3, 400, 1), (200, 1152, 1), (130, 1152, 3),
+              (1152, 6912, 1), (100, 1000, 16), (64, 5, 4), (257, 333, 8), (70, 1600, 5)]
+
+
+@pytest.mark.parametrize("n,k,m", GEMV_CASES)
+def test_gemv_ternary_parity(qmv_gpu, n, k, m):
+    from ternary_matvec_amd import qmv
+    say("gemv ternary", n, k, m)
+    t = synth.trits(4000 + n + k, (n, k))
+    x = _x_for(5000 + k + m, m, k)
+    q, sx = oracle.quantize_rows(x)
+    sw = synth.ternary_scale(6000 + n)
+    acc_ref = oracle.matmul_int(q, t)
+    w = qmv.qmv_pack_ternary(_t(t), sw)
+    acc = torch.full((m, n), -7, dtype=torch.int32, device=DEV)
+    p = qmv.Problem(w, _t(q), _t(sx), acc=acc)
+    qmv.qmv_gemv([p])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    _check_y(p.y.cpu().numpy(), acc_ref, sx, np.float32(sw))
+
+
+@pytest.mark.parametrize("n,k,m", [(768, 288, 1), (33, 17, 3), (64, 4096, 2), (5, 1, 16)])
+def test_gemv_int8_parity(qmv_gpu, n, k, m):
+    from ternary_matvec_amd import qmv
+    say("gemv int8", n, k, m)
+    wf = synth.normal(7000 + k, (n, k), std=0.02)
+    q_w, s_w = oracle.quantize_tensor(wf)
+    x = _x_for(7100 + k, m, k)
+    q, sx = oracle.quantize_rows(x)
+    acc_ref = oracle.matmul_int(q, q_w)
+    pw = qmv.qmv_pack_int8(_t(wf))
+    acc = torch.zeros((m, n), dtype=torch.int32, device=DEV)
+    p = qmv.Problem(pw, _t(q), _t(sx), acc=acc)
+    qmv.qmv_gemv([p])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    _check_y(p.y.cpu().numpy(), acc_ref, sx, s_w)
+
+
+def test_gemv_grouped_mixed_equals_single(qmv_gpu):
+    """One grouped launch over ternary and int8 problems of mixed shapes and
+    token counts gives the same bits as one launch per problem."""
+    from ternary_matvec_amd import qmv
+    say("gemv grouped mixed")
+    specs = [(1, 1024, 1152, 1), (1, 256, 1152, 2), (2, 100, 288, 1), (1, 1152, 6912, 1), (2, 64, 80, 3),
+             (1, 6912, 1152, 1), (1, 7, 9, 16)]
+    probs, refs = [], []
+    for i, (wt, n, k, m) in enumerate(specs):
+        x = _x_for(8000 + i, m, k)
+        q, sx = oracle.quantize_rows(x)
+        if wt == 1:
+            t = synth.trits(8100 + i, (n, k))
+            w = qmv.qmv_pack_ternary(_t(t), 0.02 + i * 1e-3)
+            refs.append(oracle.matmul_int(q, t))
+        else:
+            wf = synth.normal(8200 + i, (n, k), std=0.05)
+            w = qmv.qmv_pack_int8(_t(wf))
+            refs.append(oracle.matmul_int(q, oracle.quantize_tensor(wf)[0]))
+        probs.append(qmv.Problem(w, _t(q), _t(sx), acc=torch.zeros((m, n), dtype=torch.int32, device=DEV)))
+    ws = qmv.qmv_gemv(probs)
+    torch.cuda.synchronize()
+    grouped = [(p.acc.cpu().numpy().copy(), p.y.cpu().numpy().copy()) for p in probs]
+    for p, ref, (acc_g, y_g) in zip(probs, refs, grouped):
+        np.testing.assert_array_equal(acc_g, ref)
+        p.acc.zero_()
+        p.y.zero_()
+        qmv.qmv_gemv([p])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(p.acc.cpu().numpy(), acc_g)
+        np.testing.assert_array_equal(p.y.cpu().numpy(), y_g)
+    # a second launch that reuses the uploaded table gives the same bits
+    for p in probs:
+        p.y.zero_()
+    qmv.qmv_gemv(probs, workspace=ws, flags=qmv.QMV_F_TABLE_READY)
+    torch.cuda.synchronize()
+    for p, (_, y_g) in zip(probs, grouped):
+        np.testing.assert_array_equal(p.y.cpu().numpy(), y_g)
+
+
+def test_gemv_batch_columns_equal_single_token(qmv_gpu):
+    """Exact integers: token j of a 16-token problem equals the 1-token result."""
+    from ternary_matvec_amd import qmv
+    say("gemv batch invariance")
+    n, k, m = 300, 1536, 16
+    t = synth.trits(9000, (n, k))
+    q, sx = oracle.quantize_rows(_x_for(9001, m, k))
+    w = qmv.qmv_pack_ternary(_t(t), 0.02)
+    acc16 = torch.zeros((m, n), dtype=torch.int32, device=DEV)
+    qmv.qmv_gemv([qmv.Problem(w, _t(q), _t(sx), acc=acc16)])
+    for j in (0, 5, 15):
+        acc1 = torch.zeros((1, n), dtype=torch.int32, device=DEV)
+        qmv.qmv_gemv([qmv.Problem(w, _t(q[j:j + 1]), _t(sx[j:j + 1]), acc=acc1)])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(acc1.cpu().numpy()[0], acc16.cpu().numpy()[j])
+
+
+def test_gemv_extreme_values(qmv_gpu):
+    """All +1 / all -1 / one-hot rows against activations at the int8 extremes."""
+    from ternary_matvec_amd import qmv
+    say("gemv extremes")
+    k = 6912
+    t = np.zeros((64 + 3, k), np.int8)
+    t[0] = 1
+    t[1] = -1
+    for r in range(2, 67):
+        t[r, (r * 101) % k] = 1 if r % 2 else -1
+    q = np.full((2, k), -128, np.int8)
+    q[1] = 127
+    sx = np.array([0.5, 0.25], np.float32)
+    acc_ref = oracle.matmul_int(q, t)
+    w = qmv.qmv_pack_ternary(_t(t), 1.0)
+    acc = torch.zeros((2, t.shape[0]), dtype=torch.int32, device=DEV)
+    qmv.qmv_gemv([qmv.Problem(w, _t(q), _t(sx), acc=acc)])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    assert acc_ref[0, 0] == -128 * k and acc_ref[1, 1] == -127 * k
+
+
+# --------------------------------------------------------------------------
+# A9: output layer + greedy choice
+# --------------------------------------------------------------------------
+
+def _check_head(w_bits, x, idx, logits):
+    ref, ref_idx = oracle.lmhead(w_bits, x)
+    wf = synth.bf16_bits_to_f32(w_bits).astype(np.float64)
+    k = x.size
+    gamma = k * 2.0 ** -24 / (1 - k * 2.0 ** -24)
+    absdot = np.abs(wf) @ np.abs(x.astype(np.float64))
+    tol = np.maximum(2e-2 * np.abs(ref), gamma * absdot)
+    if logits is not None:
+        err = np.abs(logits.astype(np.float64) - ref)
+        assert np.all(err <= tol), float((err - tol).max())
+    if idx != ref_idx:
+        assert abs(ref[idx] - ref[ref_idx]) <= max(tol[idx], tol[ref_idx]), (idx, ref_idx)
+    return ref_idx
+
+
+@pytest.mark.parametrize("v,k", [(1, 8), (100, 64), (1000, 1152), (5000, 1000), (333, 2050), (64, 9)])
+def test_lmhead_parity(qmv_gpu, v, k):
+    from ternary_matvec_amd import qmv
+    say("lmhead", v, k)
+    w_bits = synth.to_bf16_bits(synth.normal(10000 + v, (v, k), std=0.02))
+    x = synth.normal(10001 + k, (k,))
+    idx, mx, logits = qmv.qmv_lmhead_argmax(_t(w_bits.view(np.int16)), _t(x), want_logits=True)
+    torch.cuda.synchronize()
+    _check_head(w_bits, x, int(idx.item()), logits.cpu().numpy())
+    assert mx.item() == logits.cpu().numpy()[int(idx.item())]
+
+
+def test_lmhead_planted_winner_and_tie(qmv_gpu):
+    from ternary_matvec_amd import qmv
+    say("lmhead planted")
+    v, k = 20000, 1152
+    w_bits = synth.to_bf16_bits(synth.normal(11000, (v, k), std=0.02))
+    x = synth.normal(11001, (k,))
+    w_bits[12345] = synth.to_bf16_bits(np.sign(x) * 0.5)
+    idx, _, _ = qmv.qmv_lmhead_argmax(_t(w_bits.view(np.int16)), _t(x))
+    torch.cuda.synchronize()
+    assert idx.item() == 12345
+    w_bits[777] = w_bits[12345]                       # an exact tie: the first index wins
+    w_bits[19999] = w_bits[12345]
+    idx, _, _ = qmv.qmv_lmhead_argmax(_t(w_bits.view(np.int16)), _t(x))
+    torch.cuda.synchronize()
+    assert idx.item() == 777
