@@ -1,0 +1,370 @@
+"""Benchmark of the quantized matvec hot path on one MI355X.
+
+Headline workload: batch-1 ternary decode over Gemma-3-1B-shaped weights,
+26 layers x {q, k, v, gate, up, down} = 156 matrices, trits iid with
+P(-1, 0, +1) = (0.3, 0.4, 0.3), one scale per matrix, x ~ N(0, 1).  One step:
+  qmv_quantize_act on the 130 activation rows of K = 1152 and the 26 rows of
+  K = 6912, then one grouped qmv_gemv over the 156 problems.
+Weights rotate over several full copies so the 256 MB Infinity Cache cannot
+hold the working set.  `value` = algorithmic bytes per step / step time.
+
+Also reported (not the headline): 512-token prefill through qmv_gemm_prefill
+(int8 TOPS), the 262144 x 1152 bf16 output layer with greedy argmax (GB/s),
+the 768 x 288 int8 GEMV (us/call), BitNet-b1.58-large-shaped decode at 1, 4 and
+16 tokens, and the CPU oracle timed on the host's cores on a bounded sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, datasheet
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, datasheet
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=8, help="weight copies rotated to defeat the MALL")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# Workload construction
+# ---------------------------------------------------------------------------
+
+class DecodeStack:
+    """A stack of ternary matrices packed on the GPU, with its activations."""
+
+    def __init__(self, mats, layers, config_id, m, copies, dev):
+        import torch
+        from ternary_matvec_amd import qmv, synth
+        self.mats, self.layers, self.m, self.copies = mats, layers, m, copies
+        self.config_id = config_id
+        self.weights = []          # per (layer, mid): Weight of copy 0
+        self.specs = []
+        ks = sorted(set(k for _, _, k in mats))
+        self.x = {}                # K -> fp32 [rows*m][K] on device (host copy kept for the oracle)
+        self.x_host = {}
+        rows_per_k = {k: 0 for k in ks}
+        for layer in range(layers):
+            for mid, (name, n, k) in enumerate(mats):
+                self.specs.append((layer, mid, name, n, k, rows_per_k[k]))
+                rows_per_k[k] += 1
+        for k in ks:
+            xs = [synth.normal(synth.stream_seed(config_id, layer, mid, synth.TAG_ACT), (m, kk))
+                  for (layer, mid, _, _, kk, _) in self.specs if kk == k]
+            self.x_host[k] = np.concatenate(xs, axis=0)
+            self.x[k] = torch.from_numpy(self.x_host[k]).to(dev)
+        self.x8, self.sx = {}, {}
+        for k in ks:
+            self.x8[k] = torch.empty(self.x[k].shape, dtype=torch.int8, device=dev)
+            self.sx[k] = torch.empty(self.x[k].shape[0], dtype=torch.float32, device=dev)
+        total_packed = sum(qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, n, k) for (_, _, _, n, k, _) in self.specs)
+        self.packed_bytes = total_packed
+        self.pool = [qmv._alloc_aligned(total_packed, dev, 256) for _ in range(copies)]
+        self.scales = torch.empty(len(self.specs), dtype=torch.float32, device=dev)
+        self.y = {}
+        off = 0
+        descs = []
+        for i, (layer, mid, name, n, k, slot) in enumerate(self.specs):
+            nb = qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, n, k)
+            t = synth.trits_torch(synth.stream_seed(config_id, layer, mid, synth.TAG_WEIGHT), (n, k), device=dev)
+            s = synth.ternary_scale(synth.stream_seed(config_id, layer, mid, synth.TAG_SCALE))
+            w = qmv.qmv_pack_ternary(t, s, packed=self.pool[0][off:off + nb], scale_out=self.scales[i:i + 1])
+            descs.append((off, nb, w))
+            self.y[i] = torch.empty((m, n), dtype=torch.float32, device=dev)
+            off += nb
+            del t
+        torch.cuda.synchronize()
+        for c in range(1, copies):
+            self.pool[c].copy_(self.pool[0])
+        torch.cuda.synchronize()
+        # one problem list (and one uploaded table) per copy
+        self.arrays, self.workspaces = [], []
+        for c in range(copies):
+            probs = []
+            for i, (off_i, nb, w) in enumerate(descs):
+                layer, mid, name, n, k, slot = self.specs[i]
+                wc = qmv.Weight(qmv.qmv_weight(w.desc.wtype, 0, n, k, self.pool[c][off_i:].data_ptr(),
+                                               self.scales[i:i + 1].data_ptr()),
+                                self.pool[c][off_i:off_i + nb], self.scales[i:i + 1])
+                probs.append(qmv.Problem(wc, self.x8[k][slot * m:(slot + 1) * m], self.sx[k][slot * m:(slot + 1) * m],
+                                         y=self.y[i]))
+            arr = qmv.problem_array(probs)
+            ws = qmv.qmv_gemv(arr) if m <= qmv.QMV_MAX_GEMV_M else None
+            self.arrays.append(arr)
+            self.workspaces.append(ws)
+        torch.cuda.synchronize()
+
+    # algorithmic bytes ---------------------------------------------------------
+    def weight_bytes(self):
+        return sum(n * ((k + 4) // 5) for (_, _, _, n, k, _) in self.specs)
+
+    def gemv_bytes(self):
+        """Bytes one grouped GEMV must move: packed weights at 5 trits/byte,
+        int8 activations in, fp32 outputs out, one scale per matrix and token."""
+        m = self.m
+        return sum(n * ((k + 4) // 5) + m * k + 4 * m * n + 4 + 4 * m for (_, _, _, n, k, _) in self.specs)
+
+    def quant_bytes(self):
+        return sum(5 * v.numel() + 4 * v.shape[0] for v in self.x.values())
+
+    def step_bytes(self):
+        return self.gemv_bytes() + self.quant_bytes()
+
+    def macs(self):
+        return sum(self.m * n * k for (_, _, _, n, k, _) in self.specs)
+
+
+def time_decode(stack, steps, warmup, stream):
+    """Whole steps (quantise + grouped GEMV) timed with events; the GEMV launch
+    of every timed step is bracketed by its own pair of events."""
+    import torch
+    from ternary_matvec_amd import qmv
+
+    def step(i, ev=None):
+        for k in stack.x:
+            qmv.qmv_quantize_act(stack.x[k], x8=stack.x8[k], sx=stack.sx[k], stream=stream)
+        c = i % stack.copies
+        if ev is not None:
+            ev[0].record(stream)
+        qmv.qmv_gemv(stack.arrays[c], workspace=stack.workspaces[c], flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(steps):
+        step(i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / steps
+    gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return step_ms, gemv_ms, wall
+
+
+def time_gemv_only(stack, steps, warmup, stream):
+    """Back-to-back grouped GEMV launches (no quantisation), events around the loop."""
+    import torch
+    from ternary_matvec_amd import qmv
+    for i in range(warmup):
+        qmv.qmv_gemv(stack.arrays[i % stack.copies], workspace=stack.workspaces[i % stack.copies],
+                     flags=qmv.QMV_F_TABLE_READY, stream=stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(steps):
+        qmv.qmv_gemv(stack.arrays[i % stack.copies], workspace=stack.workspaces[i % stack.copies],
+                     flags=qmv.QMV_F_TABLE_READY, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(stack, target_s, dev):
+    """The oracle (per-token quantise, exact integer matmul from trits,
+    dequantise) over whole steps of the same workload, repeated until about
+    `target_s` seconds of CPU work."""
+    import oracle
+    from ternary_matvec_amd import synth
+    threads = oracle.max_threads()
+    inputs = []
+    for (lay, mid, name, n, k, slot) in stack.specs:
+        t = synth.trits_torch(synth.stream_seed(stack.config_id, lay, mid, synth.TAG_WEIGHT), (n, k),
+                              device=dev).cpu().numpy()
+        s = synth.ternary_scale(synth.stream_seed(stack.config_id, lay, mid, synth.TAG_SCALE))
+        x = stack.x_host[k][slot * stack.m:(slot + 1) * stack.m]
+        inputs.append((t, x, np.float32(s)))
+    elapsed, passes = 0.0, 0
+    while passes == 0 or elapsed < target_s:
+        t0 = time.perf_counter()
+        for (t, x, s) in inputs:
+            q, sx = oracle.quantize_rows(x)
+            acc = oracle.matmul_int(q, t, threads=threads)
+            oracle.dequant(acc, sx, s)
+        elapsed += time.perf_counter() - t0
+        passes += 1
+    value = stack.step_bytes() * passes / elapsed / 1e9
+    return {"value": round(value, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d full step(s) of the same workload (%d matrices, batch %d): per-token quantise, exact "
+                      "int matmul from unpacked trits, dequantise; %.1f s on %d threads"
+                      % (passes, len(stack.specs), stack.m, elapsed, threads)}
+
+
+# ---------------------------------------------------------------------------
+# Extras
+# ---------------------------------------------------------------------------
+
+def bench_head(dev, stream, reps=50):
+    import torch
+    from ternary_matvec_amd import qmv, synth
+    v, k = synth.HEAD_V, synth.HEAD_K
+    w0 = synth.normal_torch(synth.stream_seed(3, 0, 0, synth.TAG_HEAD), (v, k), std=0.02, device=dev)
+    copies = [w0.to(torch.bfloat16)]
+    del w0
+    copies.append(copies[0].clone())
+    x = torch.from_numpy(synth.normal(synth.stream_seed(3, 0, 0, synth.TAG_ACT), (k,))).to(dev)
+    ws = qmv._alloc_aligned(qmv.qmv_lmhead_workspace_bytes(v, k), dev)
+    idx = torch.empty(1, dtype=torch.int32, device=dev)
+    mx = torch.empty(1, dtype=torch.float32, device=dev)
+    for i in range(5):
+        qmv.qmv_lmhead_argmax(copies[i % 2], x, idx=idx, max_logit=mx, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(reps):
+        qmv.qmv_lmhead_argmax(copies[i % 2], x, idx=idx, max_logit=mx, workspace=ws, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    nbytes = v * k * 2 + 4 * k + 8
+    return {"workload": "bf16 output layer 262144x1152 + first-max argmax", "us": round(ms * 1e3, 2),
+            "GB/s": round(nbytes / ms / 1e6, 1), "frac_hbm_peak": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+            "idx": int(idx.item())}
+
+
+def bench_int8(dev, stream, reps=2000):
+    import torch
+    from ternary_matvec_amd import qmv, synth
+    n, k = synth.INT8_N, synth.INT8_K
+    w = torch.from_numpy(synth.normal(synth.stream_seed(0, 0, 0, synth.TAG_WEIGHT), (n, k), std=0.02)).to(dev)
+    x = torch.from_numpy(synth.normal(synth.stream_seed(0, 0, 0, synth.TAG_ACT), (1, k))).to(dev)
+    pw = qmv.qmv_pack_int8(w)
+    x8, sx = qmv.qmv_quantize_act(x)
+    p = qmv.Problem(pw, x8, sx)
+    arr = qmv.problem_array([p])
+    ws = qmv.qmv_gemv(arr)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        qmv.qmv_quantize_act(x, x8=x8, sx=sx, stream=stream)
+        qmv.qmv_gemv(arr, workspace=ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / reps * 1e3
+    nbytes = n * k + 5 * k + 4 * n + 8
+    return {"workload": "int8 per-tensor GEMV 768x288, batch 1 (quantise + GEMV)", "us_per_call": round(us, 2),
+            "GB/s": round(nbytes / us / 1e3, 2)}
+
+
+def bench_bitnet(dev, stream, steps, warmup, copies):
+    import torch
+    from ternary_matvec_amd import synth
+    out = {}
+    for m in (1, 4, 16):
+        st = DecodeStack(synth.BITNET_MATS, synth.BITNET_LAYERS, synth.CONFIG_BITNET, m, copies, dev)
+        step_ms, gemv_ms, _ = time_decode(st, steps, warmup, stream)
+        out["m%d" % m] = {"gemv_us": round(gemv_ms * 1e3, 2), "step_us": round(step_ms * 1e3, 2),
+                          "gemv_GB/s": round(st.gemv_bytes() / gemv_ms / 1e6, 1),
+                          "weights_per_s": float("%.4g" % (sum(n * k for (_, _, _, n, k, _) in st.specs) / gemv_ms * 1e3)),
+                          "MAC/s": float("%.4g" % (st.macs() / gemv_ms * 1e3))}
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from ternary_matvec_amd import qmv, synth
+    qmv.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    log("building the Gemma-shaped decode stack (26 layers x 6 matrices, %d copies)" % args.copies)
+    t0 = time.perf_counter()
+    stack = DecodeStack(synth.GEMMA_MATS, synth.GEMMA_LAYERS, synth.CONFIG_GEMMA_DECODE, 1, args.copies, dev)
+    log("stack ready in %.1f s: %.1f MB packed per copy" % (time.perf_counter() - t0, stack.packed_bytes / 1e6))
+
+    step_ms, gemv_ms, wall = time_decode(stack, args.steps, args.warmup, stream)
+    gemv_only_ms = time_gemv_only(stack, args.steps, args.warmup, stream)
+    log("step %.2f us, gemv (events in step) %.2f us, gemv back-to-back %.2f us" %
+        (step_ms * 1e3, gemv_ms * 1e3, gemv_only_ms * 1e3))
+
+    step_bytes = stack.step_bytes()
+    gemv_bytes = stack.gemv_bytes()
+    value = step_bytes / step_ms / 1e6          # GB/s
+    achieved = gemv_bytes / gemv_ms / 1e6
+    result = {
+        "metric": "batch-1 ternary GEMV achieved HBM GB/s (% of peak) + prefill int8 TOPS",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 x trit -> int32, fp32 scales",
+        "data": "synthetic (splitmix64 seed 42: trits P(-1,0,1)=(.3,.4,.3), x ~ N(0,1))",
+        "config": {"workload": "ternary batch-1 decode, Gemma-3-1B shapes x26 layers (156 matrices: q 1024x1152, "
+                               "k/v 256x1152, gate/up 6912x1152, down 1152x6912), 5 trits/byte",
+                   "tokens": 1, "matrices": len(stack.specs), "weight_copies": args.copies,
+                   "step": "qmv_quantize_act x2 + one grouped qmv_gemv",
+                   "step_bytes": step_bytes, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "k_gemv<1,1> (grouped ternary GEMV)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": gemv_bytes, "launch_us": round(gemv_ms * 1e3, 3),
+                     "launch_us_back_to_back": round(gemv_only_ms * 1e3, 3)},
+    }
+    if not args.no_extras:
+        extras = {}
+        try:
+            log("output layer")
+            extras["lmhead"] = bench_head(dev, stream)
+            torch.cuda.empty_cache()
+            log("int8 GEMV")
+            extras["int8_gemv"] = bench_int8(dev, stream)
+            log("BitNet decode")
+            extras["bitnet_decode"] = bench_bitnet(dev, stream, max(20, args.steps // 4), 5, min(args.copies, 8))
+        except Exception as e:  # extras never hide the headline line
+            extras["error"] = repr(e)
+        result["extras"] = extras
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(stack, args.cpu_seconds, dev)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -53,50 +53,98 @@ int32_t check_problems(const qmv_problem* probs, int32_t count, int64_t max_m)
         if (st != QMV_OK) return st;
         if (!p.x8 || !p.sx || !p.y) return QMV_EINVAL;
         if (p.m < 1 || p.m > max_m) return QMV_ESHAPE;
-        if ((p.w.n + kRowsPerTile - 1) / kRowsPerTile > ((int64_t)1 << kTileRowBits)) return QMV_ESHAPE;
     }
     return QMV_OK;
 }
 
-// Workspace image of a problem list: [DevProblem x count][tile entries],
-// problems ordered by decreasing row length so the longest tiles start first.
+// Workspace image of a problem list: [DevProblem x count][tile entries].
+// Problems are grouped by weight type; inside a group the largest tiles come
+// first so they start first.  A tile is a block of rows of one problem:
+// 64 rows for the workgroup kernel, 64 / lanes_per_row rows for the streaming
+// kernel.
 struct Table {
     std::vector<uint8_t> bytes;
     int64_t tiles_offset = 0;
     int32_t total_tiles = 0;
-    // per weight type: first tile, tile count, max m, max chunks
+    // per weight type: streaming kernel?, first tile, tile count, max m, max chunks
+    bool stream[3] = {false, false, false};
     int32_t first[3] = {0, 0, 0}, count[3] = {0, 0, 0}, max_m[3] = {0, 0, 0}, max_chunks[3] = {0, 0, 0};
 };
 
-int64_t table_bytes(const qmv_problem* probs, int32_t count)
-{
+struct Plan {
+    std::vector<int32_t> order;    // problem index per table slot
+    std::vector<int32_t> rows;     // rows per tile, per problem
+    std::vector<int32_t> lanes;    // lanes per row, per problem
     int64_t tiles = 0;
-    for (int32_t i = 0; i < count; ++i) tiles += (probs[i].w.n + kRowsPerTile - 1) / kRowsPerTile;
-    return round_up((int64_t)sizeof(DevProblem) * count, 256) + round_up(tiles * 4, 256);
+    bool stream[3] = {false, false, false};
+    int32_t max_m[3] = {0, 0, 0}, max_chunks[3] = {0, 0, 0};
+};
+
+void make_plan(const qmv_problem* probs, int32_t count, Plan& pl)
+{
+    for (int32_t i = 0; i < count; ++i) {
+        const int32_t wt = probs[i].w.wtype;
+        pl.max_m[wt] = std::max<int32_t>(pl.max_m[wt], (int32_t)probs[i].m);
+        pl.max_chunks[wt] = std::max<int32_t>(pl.max_chunks[wt], (int32_t)(row_stride(wt, probs[i].w.k) / 16));
+    }
+    for (int wt = 1; wt <= 2; ++wt)
+        pl.stream[wt] = pl.max_m[wt] > 0 && gemv_stream_fits(wt, pl.max_m[wt], pl.max_chunks[wt]);
+    pl.rows.resize(count);
+    pl.lanes.resize(count);
+    pl.order.resize(count);
+    for (int32_t i = 0; i < count; ++i) {
+        const int32_t wt = probs[i].w.wtype;
+        const int32_t chunks = (int32_t)(row_stride(wt, probs[i].w.k) / 16);
+        pl.lanes[i] = pl.stream[wt] ? gemv_stream_lanes_per_row(chunks) : 1;
+        pl.rows[i] = kRowsPerTile / pl.lanes[i];
+        pl.tiles += (probs[i].w.n + pl.rows[i] - 1) / pl.rows[i];
+        pl.order[i] = i;
+    }
+    std::stable_sort(pl.order.begin(), pl.order.end(), [&](int32_t a, int32_t b) {
+        if (probs[a].w.wtype != probs[b].w.wtype) return probs[a].w.wtype < probs[b].w.wtype;
+        const int64_t ta = (int64_t)pl.rows[a] * row_stride(probs[a].w.wtype, probs[a].w.k);
+        const int64_t tb = (int64_t)pl.rows[b] * row_stride(probs[b].w.wtype, probs[b].w.k);
+        return ta > tb;
+    });
 }
 
-void build_table(const qmv_problem* probs, int32_t count, Table& t)
+int64_t plan_bytes(const Plan& pl, int32_t count)
 {
-    std::vector<int32_t> order(count);
-    for (int32_t i = 0; i < count; ++i) order[i] = i;
-    // group by weight type, then longest rows first (stable for equal keys)
-    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-        if (probs[a].w.wtype != probs[b].w.wtype) return probs[a].w.wtype < probs[b].w.wtype;
-        return row_stride(probs[a].w.wtype, probs[a].w.k) > row_stride(probs[b].w.wtype, probs[b].w.k);
-    });
+    return round_up((int64_t)sizeof(DevProblem) * count, 256) + round_up(pl.tiles * 4, 256);
+}
+
+bool plan_tiles_fit(const qmv_problem* probs, int32_t count, const Plan& pl)
+{
+    for (int32_t i = 0; i < count; ++i)
+        if ((probs[i].w.n + pl.rows[i] - 1) / pl.rows[i] > ((int64_t)1 << kTileRowBits)) return false;
+    return true;
+}
+
+int64_t table_bytes(const qmv_problem* probs, int32_t count)
+{
+    Plan pl;
+    make_plan(probs, count, pl);
+    return plan_bytes(pl, count);
+}
+
+void build_table(const qmv_problem* probs, int32_t count, const Plan& pl, Table& t)
+{
     const int64_t pbytes = round_up((int64_t)sizeof(DevProblem) * count, 256);
-    int64_t tiles = 0;
-    for (int32_t i = 0; i < count; ++i) tiles += (probs[i].w.n + kRowsPerTile - 1) / kRowsPerTile;
-    t.bytes.assign(pbytes + round_up(tiles * 4, 256), 0);
+    t.bytes.assign(plan_bytes(pl, count), 0);
     t.tiles_offset = pbytes;
-    t.total_tiles = (int32_t)tiles;
+    t.total_tiles = (int32_t)pl.tiles;
     DevProblem* dp = reinterpret_cast<DevProblem*>(t.bytes.data());
     uint32_t* te = reinterpret_cast<uint32_t*>(t.bytes.data() + pbytes);
     int32_t tile = 0;
+    for (int wt = 1; wt <= 2; ++wt) {
+        t.stream[wt] = pl.stream[wt];
+        t.max_m[wt] = pl.max_m[wt];
+        t.max_chunks[wt] = pl.max_chunks[wt];
+    }
     for (int32_t slot = 0; slot < count; ++slot) {
-        const qmv_problem& p = probs[order[slot]];
+        const int32_t pi = pl.order[slot];
+        const qmv_problem& p = probs[pi];
         const int32_t wt = p.w.wtype;
-        const int64_t stride = row_stride(wt, p.w.k);
         DevProblem& d = dp[slot];
         d.w = static_cast<const uint8_t*>(p.w.data);
         d.sw = p.w.scale;
@@ -107,16 +155,16 @@ void build_table(const qmv_problem* probs, int32_t count, Table& t)
         d.n = (int32_t)p.w.n;
         d.k = (int32_t)p.w.k;
         d.m = (int32_t)p.m;
-        d.chunks = (int32_t)(stride / 16);
+        d.chunks = (int32_t)(row_stride(wt, p.w.k) / 16);
         d.tile_begin = tile;
         d.wtype = wt;
+        d.lanes_per_row = pl.lanes[pi];
+        d.reserved = 0;
         if (t.count[wt] == 0) t.first[wt] = tile;
-        const int32_t ntiles = (int32_t)((p.w.n + kRowsPerTile - 1) / kRowsPerTile);
+        const int32_t ntiles = (int32_t)((p.w.n + pl.rows[pi] - 1) / pl.rows[pi]);
         for (int32_t r = 0; r < ntiles; ++r) te[tile + r] = ((uint32_t)slot << kTileRowBits) | (uint32_t)r;
         tile += ntiles;
         t.count[wt] += ntiles;
-        t.max_m[wt] = std::max<int32_t>(t.max_m[wt], (int32_t)p.m);
-        t.max_chunks[wt] = std::max<int32_t>(t.max_chunks[wt], d.chunks);
     }
 }
 
@@ -209,22 +257,30 @@ int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64
     int32_t st = check_problems(probs, count, QMV_MAX_GEMV_M);
     if (st != QMV_OK) return st;
     if (flags & ~(uint32_t)QMV_F_TABLE_READY) return QMV_EINVAL;
-    const int64_t need = table_bytes(probs, count);
-    if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return QMV_EWORKSPACE;
-    Table t;
-    build_table(probs, count, t);
+    Plan pl;
+    make_plan(probs, count, pl);
+    if (!plan_tiles_fit(probs, count, pl)) return QMV_ESHAPE;
     for (int wt = 1; wt <= 2; ++wt)
-        if (t.count[wt] && gemv_lds_bytes(wt, t.max_m[wt], t.max_chunks[wt]) > kMaxLds) return QMV_ESHAPE;
+        if (pl.max_m[wt] && !pl.stream[wt] && gemv_lds_bytes(wt, pl.max_m[wt], pl.max_chunks[wt]) > kMaxLds)
+            return QMV_ESHAPE;
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < plan_bytes(pl, count)) return QMV_EWORKSPACE;
+    Table t;
+    build_table(probs, count, pl, t);
     const hipStream_t s = as_stream(stream);
     if (!(flags & QMV_F_TABLE_READY)) {
         hipError_t e = hipMemcpyAsync(workspace, t.bytes.data(), t.bytes.size(), hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return QMV_EHIP;
     }
-    const DevProblem* dp = static_cast<const DevProblem*>(workspace);
-    const uint32_t* tiles = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(workspace) + t.tiles_offset);
+    const uint8_t* base = static_cast<const uint8_t*>(workspace);
+    const DevProblem* dp = reinterpret_cast<const DevProblem*>(base);
+    const uint32_t* tiles = reinterpret_cast<const uint32_t*>(base + t.tiles_offset);
     for (int wt = 1; wt <= 2; ++wt) {
         if (t.count[wt] == 0) continue;
-        hipError_t e = launch_gemv(dp, tiles, t.first[wt], t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
+        hipError_t e;
+        if (t.stream[wt])
+            e = launch_gemv_stream(dp, tiles, t.first[wt], t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
+        else
+            e = launch_gemv(dp, tiles, t.first[wt], t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
         if (e != hipSuccess) return QMV_EHIP;
     }
     return QMV_OK;

@@ -32,53 +32,10 @@
 //    t = d - 1, so sum(x) is subtracted.  All sums are modulo 2^32; the final
 //    value is exact whenever the true dot fits int32.
 #include "qmv_internal.hpp"
+#include "unpack.hpp"
 
 namespace qmv {
 namespace {
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c)
-{
-    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
-}
-
-// Two fp16 lanes holding 1024 + v (v <= 242) -> 1024 + floor(v / 3).
-__device__ __forceinline__ uint32_t third2(uint32_t h)
-{
-    const half2_t mul = __builtin_bit_cast(half2_t, 0x35533553u);  // 0.332763671875
-    const half2_t add = __builtin_bit_cast(half2_t, 0x61566156u);  // 683.0
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(__builtin_bit_cast(half2_t, h), mul, add));
-}
-
-struct Planes {
-    uint32_t p1, p2, p3, p4, b5;
-};
-
-// One packed dword [b0 b1 b2 b3] -> prefix-quotient planes, byte k of each
-// plane belonging to packed byte k.
-__device__ __forceinline__ Planes unpack(uint32_t w)
-{
-    const uint32_t mag = 0x64646464u;                          // fp16 high byte of 1024
-    const uint32_t lo = __builtin_amdgcn_perm(mag, w, 0x04020400u);  // [b0 64 b2 64]
-    const uint32_t hi = __builtin_amdgcn_perm(mag, w, 0x04030401u);  // [b1 64 b3 64]
-    const uint32_t lo4 = third2(lo), hi4 = third2(hi);
-    const uint32_t lo3 = third2(lo4), hi3 = third2(hi4);
-    const uint32_t lo2 = third2(lo3), hi2 = third2(hi3);
-    const uint32_t lo1 = third2(lo2), hi1 = third2(hi2);
-    Planes p;
-    p.p4 = __builtin_amdgcn_perm(hi4, lo4, 0x06020400u);
-    p.p3 = __builtin_amdgcn_perm(hi3, lo3, 0x06020400u);
-    p.p2 = __builtin_amdgcn_perm(hi2, lo2, 0x06020400u);
-    p.p1 = __builtin_amdgcn_perm(hi1, lo1, 0x06020400u);
-    p.b5 = w ^ 0x80808080u;
-    return p;
-}
-
-__device__ __forceinline__ uint32_t sel(const uint4& v, int i)
-{
-    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
 
 constexpr int kBatch = 4;  // chunks in flight per lane
 
@@ -105,15 +62,15 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
     const int c_lo = min(C, wave * per);
     const int c_hi = min(C, c_lo + per);
 
-    const uint4* wp = reinterpret_cast<const uint4*>(P->w) + row;
+    const QMV_GLOBAL v4u32* wp = gload_ptr(reinterpret_cast<const v4u32*>(P->w)) + row;
     const size_t cstride = (size_t)n;
 
     // Issue the first weight loads before staging the activations.
-    uint4 buf[kBatch];
+    v4u32 buf[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
         const int c = c_lo + u;
-        buf[u] = (live && c < c_hi) ? wp[(size_t)c * cstride] : make_uint4(0u, 0u, 0u, 0u);
+        buf[u] = (live && c < c_hi) ? wp[(size_t)c * cstride] : v4u32{0u, 0u, 0u, 0u};
     }
 
     // ---- stage activations in LDS ------------------------------------------
@@ -130,7 +87,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
     for (int q = tid; q < m * dw_per_tok; q += kBlock) {
         const int mi = q / dw_per_tok;
         const int d = q - mi * dw_per_tok;
-        const int8_t* xr = P->x8 + (size_t)mi * k;
+        const QMV_GLOBAL int8_t* xr = gload_ptr(P->x8) + (size_t)mi * k;
         uint32_t v = 0;
         if (WT == 1) {
             const int c = d / 20;
@@ -172,11 +129,11 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
     const int x4_per_tok = dw_per_tok / 4;
 
     for (int c0 = c_lo; c0 < c_hi; c0 += kBatch) {
-        uint4 nxt[kBatch];
+        v4u32 nxt[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int c = c0 + kBatch + u;
-            nxt[u] = (live && c < c_hi) ? wp[(size_t)c * cstride] : make_uint4(0u, 0u, 0u, 0u);
+            nxt[u] = (live && c < c_hi) ? wp[(size_t)c * cstride] : v4u32{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
@@ -216,10 +173,10 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
                         if (mi < m) {
                             const uint4 X = xs4[mi * x4_per_tok + c];
                             int a = acc_a[mi];
-                            a = dot4(buf[u].x, X.x, a);
-                            a = dot4(buf[u].y, X.y, a);
-                            a = dot4(buf[u].z, X.z, a);
-                            a = dot4(buf[u].w, X.w, a);
+                            a = dot4(buf[u][0], X.x, a);
+                            a = dot4(buf[u][1], X.y, a);
+                            a = dot4(buf[u][2], X.z, a);
+                            a = dot4(buf[u][3], X.w, a);
                             acc_a[mi] = a;
                         }
                     }
@@ -241,7 +198,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
     }
     __syncthreads();
     if (wave == 0 && live) {
-        const float sw = *P->sw;
+        const float sw = *gload_ptr(P->sw);
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
             if (mi < m) {
@@ -259,8 +216,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
                     total = a;
                 }
                 const size_t o = (size_t)mi * n + row;
-                P->y[o] = (float)total * P->sx[mi] * sw;
-                if (P->acc) P->acc[o] = total;
+                gstore_ptr(P->y)[o] = (float)total * gload_ptr(P->sx)[mi] * sw;
+                if (P->acc) gstore_ptr(P->acc)[o] = total;
             }
         }
     }

@@ -27,8 +27,25 @@ struct DevProblem {
     int32_t chunks;      // 16-byte chunks per row (row stride / 16)
     int32_t tile_begin;  // first tile of this problem in the launch
     int32_t wtype;       // 1 = five trits per byte, 2 = int8
+    int32_t lanes_per_row;  // streaming kernel: lanes sharing one row (1, 2 or 4)
+    int32_t reserved;
 };
-static_assert(sizeof(DevProblem) == 72, "DevProblem layout");
+static_assert(sizeof(DevProblem) == 80, "DevProblem layout");
+
+// Pointers read from a descriptor in memory are generic (FLAT) to the
+// compiler; FLAT loads also count against the LDS wait counter, which
+// serialises weight streaming with LDS traffic.  These casts make them global.
+#define QMV_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const QMV_GLOBAL T* gload_ptr(const T* p)
+{
+    return (const QMV_GLOBAL T*)p;
+}
+template <typename T>
+__device__ __forceinline__ QMV_GLOBAL T* gstore_ptr(T* p)
+{
+    return (QMV_GLOBAL T*)p;
+}
 
 // Launchers implemented in the kernel translation units.
 hipError_t launch_fill_pack_header(float* scale_out, float scale, int32_t* bad, hipStream_t s);
@@ -41,6 +58,12 @@ int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks);
 constexpr int64_t kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
 hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
                        int wtype, int max_m, int max_chunks, hipStream_t s);
+// Streaming (persistent) GEMV for 1..2 tokens: lanes per row for a row of
+// `chunks` 16-byte chunks, and whether a problem list fits the kernel.
+int gemv_stream_lanes_per_row(int chunks);
+bool gemv_stream_fits(int wtype, int max_m, int max_chunks);
+hipError_t launch_gemv_stream(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin,
+                              int32_t tile_count, int wtype, int max_m, int max_chunks, hipStream_t s);
 hipError_t launch_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, int32_t* idx,
                          float* max_logit, float* logits, void* workspace, hipStream_t s);
 int64_t lmhead_partials(int64_t v);

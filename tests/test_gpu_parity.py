@@ -128,8 +128,12 @@ def _check_y(y, acc_ref, sx, sw):
     assert np.all(y[acc_ref == 0] == 0.0)
 
 
+# (n, k, m): ragged rows and columns, every lanes-per-row split of the
+# streaming kernel (row chunks 1..32, 33..64, 65+; odd chunk counts leave
+# lanes with one chunk less), and the workgroup kernel for m > 2.
 GEMV_CASES = [(1, 1, 1), (5, 7, 1), (64, 80, 1), (65, 81, 2), (3, 400, 1), (200, 1152, 1), (130, 1152, 3),
-              (1152, 6912, 1), (100, 1000, 16), (64, 5, 4), (257, 333, 8), (70, 1600, 5)]
+              (1152, 6912, 1), (77, 6912, 2), (100, 2800, 1), (50, 5000, 2), (33, 4096, 1), (100, 1000, 16),
+              (64, 5, 4), (257, 333, 8), (70, 1600, 5), (17, 6912, 4)]
 
 
 @pytest.mark.parametrize("n,k,m", GEMV_CASES)
@@ -150,7 +154,7 @@ def test_gemv_ternary_parity(qmv_gpu, n, k, m):
     _check_y(p.y.cpu().numpy(), acc_ref, sx, np.float32(sw))
 
 
-@pytest.mark.parametrize("n,k,m", [(768, 288, 1), (33, 17, 3), (64, 4096, 2), (5, 1, 16)])
+@pytest.mark.parametrize("n,k,m", [(768, 288, 1), (33, 17, 3), (64, 4096, 2), (5, 1, 16), (40, 1040, 1), (9, 700, 2)])
 def test_gemv_int8_parity(qmv_gpu, n, k, m):
     from ternary_matvec_amd import qmv
     say("gemv int8", n, k, m)
