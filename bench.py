@@ -225,6 +225,91 @@ def cpu_baseline(stack, target_s, dev):
 # Extras
 # ---------------------------------------------------------------------------
 
+class PrefillStack:
+    """The decode stack's weights (copy 0) with 512-token activations per matrix."""
+
+    def __init__(self, stack, m, dev):
+        import torch
+        from ternary_matvec_amd import qmv, synth
+        self.stack, self.m = stack, m
+        ks = sorted(stack.x.keys())
+        self.x, self.x8, self.sx = {}, {}, {}
+        for k in ks:
+            rows = [s for s in stack.specs if s[4] == k]
+            xk = torch.empty((len(rows) * m, k), dtype=torch.float32, device=dev)
+            for (layer, mid, name, n, kk, slot) in rows:
+                xk[slot * m:(slot + 1) * m] = synth.normal_torch(
+                    synth.stream_seed(synth.CONFIG_GEMMA_PREFILL, layer, mid, synth.TAG_ACT), (m, k), device=dev)
+            self.x[k] = xk
+            self.x8[k] = torch.empty(xk.shape, dtype=torch.int8, device=dev)
+            self.sx[k] = torch.empty(xk.shape[0], dtype=torch.float32, device=dev)
+        self.y = {}
+        probs = []
+        pool = stack.pool[0]
+        off = 0
+        for i, (layer, mid, name, n, k, slot) in enumerate(stack.specs):
+            nb = qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, n, k)
+            w = qmv.Weight(qmv.qmv_weight(qmv.QMV_W_TERNARY5, 0, n, k, pool[off:].data_ptr(),
+                                          stack.scales[i:i + 1].data_ptr()), pool[off:off + nb], stack.scales[i:i + 1])
+            off += nb
+            self.y[i] = torch.empty((m, n), dtype=torch.float32, device=dev)
+            probs.append(qmv.Problem(w, self.x8[k][slot * m:(slot + 1) * m], self.sx[k][slot * m:(slot + 1) * m],
+                                     y=self.y[i]))
+        self.arr = qmv.problem_array(probs)
+        self.ws = qmv.qmv_gemm_prefill(self.arr)
+        torch.cuda.synchronize()
+
+    def ops(self):
+        return 2 * sum(self.m * n * k for (_, _, _, n, k, _) in self.stack.specs)
+
+    def bytes(self):
+        """Algorithmic bytes of one pass: packed weights, int8 activations in, fp32 outputs out."""
+        m = self.m
+        return sum(n * ((k + 4) // 5) + m * k + 4 * m * n + 4 + 4 * m for (_, _, _, n, k, _) in self.stack.specs)
+
+
+def time_prefill(ps, steps, warmup, stream):
+    import torch
+    from ternary_matvec_amd import qmv
+
+    def step(ev=None):
+        for k in ps.x:
+            qmv.qmv_quantize_act(ps.x[k], x8=ps.x8[k], sx=ps.sx[k], stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        qmv.qmv_gemm_prefill(ps.arr, workspace=ps.ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def bench_prefill(stack, dev, stream, steps=20, warmup=3):
+    import torch
+    ps = PrefillStack(stack, 512, dev)
+    step_ms, kern_ms = time_prefill(ps, steps, warmup, stream)
+    tops = ps.ops() / kern_ms / 1e9
+    out = {"workload": "ternary prefill, 512 tokens x Gemma-3-1B shapes x26 layers (156 matrices)",
+           "kernel": "k_prefill (v_mfma_i32_32x32x32_i8)", "prefill_us": round(kern_ms * 1e3, 1),
+           "step_us": round(step_ms * 1e3, 1), "TOPS": round(tops, 1),
+           "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
+           "GB/s": round(ps.bytes() / kern_ms / 1e6, 1), "ops_per_pass": ps.ops(), "bytes_per_pass": ps.bytes()}
+    del ps
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_head(dev, stream, reps=50):
     import torch
     from ternary_matvec_amd import qmv, synth
@@ -347,6 +432,9 @@ def main():
                      "bytes_per_launch": gemv_bytes, "launch_us": round(gemv_ms * 1e3, 3),
                      "launch_us_back_to_back": round(gemv_only_ms * 1e3, 3)},
     }
+    log("prefill (512 tokens)")
+    result["prefill"] = bench_prefill(stack, dev, stream)
+    log("prefill %.1f us, %.1f TOPS" % (result["prefill"]["prefill_us"], result["prefill"]["TOPS"]))
     if not args.no_extras:
         extras = {}
         try:

@@ -168,6 +168,30 @@ void build_table(const qmv_problem* probs, int32_t count, const Plan& pl, Table&
     }
 }
 
+constexpr int64_t kMaxPrefillM = 65536;
+
+int32_t check_prefill(const qmv_problem* probs, int32_t count)
+{
+    int32_t st = check_problems(probs, count, kMaxPrefillM);
+    if (st != QMV_OK) return st;
+    for (int32_t i = 0; i < count; ++i)
+        if (probs[i].w.wtype != QMV_W_TERNARY5) return QMV_EUNSUPPORTED;
+    return QMV_OK;
+}
+
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
+
+// Workspace of a prefill problem list: the problem table and the XCD-ordered
+// tile list (8 lists padded to the longest, bounded by 8 x all tiles).
+int64_t prefill_table_bytes(const qmv_problem* probs, int32_t count)
+{
+    int64_t tiles = 0;
+    for (int32_t i = 0; i < count; ++i) tiles += prefill_tiles(probs[i].m, probs[i].w.n);
+    // no XCD list can be longer than all tiles together
+    const int64_t bound = kXcds * tiles;
+    return round_up((int64_t)sizeof(DevProblem) * count, 256) + round_up(bound * 8, 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,21 +312,85 @@ int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64
 
 int64_t qmv_prefill_workspace_bytes(const qmv_problem* probs, int32_t count)
 {
-    (void)probs;
-    (void)count;
-    return -1;
+    if (check_prefill(probs, count) != QMV_OK) return -1;
+    return prefill_table_bytes(probs, count);
 }
 
 int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, uint32_t flags,
                          void* stream)
 {
-    (void)probs;
-    (void)count;
-    (void)workspace;
-    (void)ws_bytes;
-    (void)flags;
-    (void)stream;
-    return QMV_EUNSUPPORTED;
+    int32_t st = check_prefill(probs, count);
+    if (st != QMV_OK) return st;
+    if (flags & ~(uint32_t)QMV_F_TABLE_READY) return QMV_EINVAL;
+    const int64_t need = prefill_table_bytes(probs, count);
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return QMV_EWORKSPACE;
+    // Problem table: longest rows first.
+    std::vector<int32_t> order(count);
+    for (int32_t i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return probs[a].w.k > probs[b].w.k; });
+    const int64_t pbytes = round_up((int64_t)sizeof(DevProblem) * count, 256);
+    std::vector<uint8_t> img(need, 0);
+    DevProblem* dp = reinterpret_cast<DevProblem*>(img.data());
+    // Tile list, XCD-aware: workgroup b runs on XCD b % 8 (round-robin dispatch),
+    // so tiles that share an activation block (same problem and token block) go
+    // to one XCD's list and run back to back there, reusing that XCD's L2.  The
+    // token-block groups are spread over the XCDs longest first, to the least
+    // loaded one.
+    struct Group {
+        int32_t slot;
+        int64_t mt, ntiles, work;
+    };
+    std::vector<Group> groups;
+    for (int32_t slot = 0; slot < count; ++slot) {
+        const qmv_problem& p = probs[order[slot]];
+        DevProblem& d = dp[slot];
+        d.w = static_cast<const uint8_t*>(p.w.data);
+        d.sw = p.w.scale;
+        d.x8 = p.x8;
+        d.sx = p.sx;
+        d.y = p.y;
+        d.acc = p.acc;
+        d.n = (int32_t)p.w.n;
+        d.k = (int32_t)p.w.k;
+        d.m = (int32_t)p.m;
+        d.chunks = (int32_t)(row_stride(p.w.wtype, p.w.k) / 16);
+        d.tile_begin = 0;
+        d.wtype = p.w.wtype;
+        d.lanes_per_row = 1;
+        d.reserved = 0;
+        const int64_t mts = (p.m + kPrefillTileM - 1) / kPrefillTileM;
+        const int64_t nts = (p.w.n + kPrefillTileN - 1) / kPrefillTileN;
+        for (int64_t mt = 0; mt < mts; ++mt) groups.push_back({slot, mt, nts, nts * ((d.chunks + 1) / 2)});
+    }
+    std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.work > b.work; });
+    std::vector<std::vector<uint64_t>> lists(kXcds);
+    std::vector<int64_t> load(kXcds, 0);
+    for (const Group& gr : groups) {
+        int x = 0;
+        for (int i = 1; i < kXcds; ++i)
+            if (load[i] < load[x]) x = i;
+        load[x] += gr.work;
+        for (int64_t nt = 0; nt < gr.ntiles; ++nt)
+            lists[x].push_back(((uint64_t)gr.slot << 48) | ((uint64_t)gr.mt << 32) | (uint64_t)nt);
+    }
+    size_t longest = 0;
+    for (const auto& l : lists) longest = std::max(longest, l.size());
+    const int64_t grid = (int64_t)longest * kXcds;
+    if (pbytes + grid * 8 > need) return QMV_EWORKSPACE;  // cannot happen: need covers 8 x all tiles
+    uint64_t* te = reinterpret_cast<uint64_t*>(img.data() + pbytes);
+    for (int64_t b = 0; b < grid; ++b) {
+        const auto& l = lists[b % kXcds];
+        const size_t j = (size_t)(b / kXcds);
+        te[b] = j < l.size() ? l[j] : ~0ull;
+    }
+    const hipStream_t s = as_stream(stream);
+    if (!(flags & QMV_F_TABLE_READY)) {
+        hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return QMV_EHIP;
+    }
+    const uint8_t* base = static_cast<const uint8_t*>(workspace);
+    return hip_status(launch_prefill(reinterpret_cast<const DevProblem*>(base),
+                                     reinterpret_cast<const uint64_t*>(base + pbytes), grid, s));
 }
 
 int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k)

@@ -22,8 +22,17 @@
 namespace qmv {
 namespace {
 
-constexpr int kSBatch = 4;  // chunks per step batch; the next batch is in flight meanwhile
-constexpr int kStreamWavesPerCU = 16;
+#ifndef QMV_STREAM_BATCH
+#define QMV_STREAM_BATCH 2
+#endif
+#ifndef QMV_STREAM_WAVES_PER_CU
+#define QMV_STREAM_WAVES_PER_CU 16
+#endif
+#ifndef QMV_STREAM_MIN_WAVES_PER_EU
+#define QMV_STREAM_MIN_WAVES_PER_EU 1
+#endif
+constexpr int kSBatch = QMV_STREAM_BATCH;  // chunks per step batch; the next batch is in flight meanwhile
+constexpr int kStreamWavesPerCU = QMV_STREAM_WAVES_PER_CU;
 
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -63,7 +72,7 @@ __device__ __forceinline__ uint32_t x_dword_bytes(const QMV_GLOBAL int8_t* xr, i
 }
 
 template <int MT, int WT>
-__global__ __launch_bounds__(kBlock) void k_gemv_stream(const DevProblem* __restrict__ probs,
+__global__ __launch_bounds__(kBlock, QMV_STREAM_MIN_WAVES_PER_EU) void k_gemv_stream(const DevProblem* __restrict__ probs,
                                                        const uint32_t* __restrict__ tiles, int32_t tile_base,
                                                        int32_t tile_count, int32_t wave_lds_bytes)
 {

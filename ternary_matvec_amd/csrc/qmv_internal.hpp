@@ -64,6 +64,12 @@ int gemv_stream_lanes_per_row(int chunks);
 bool gemv_stream_fits(int wtype, int max_m, int max_chunks);
 hipError_t launch_gemv_stream(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin,
                               int32_t tile_count, int wtype, int max_m, int max_chunks, hipStream_t s);
+// Prefill (int8 matrix cores): tiles of 256 tokens x 256 rows.
+constexpr int64_t kPrefillTileM = 256;
+constexpr int64_t kPrefillTileN = 256;
+int64_t prefill_tiles(int64_t m, int64_t n);
+void prefill_tile_entries(int32_t slot, int64_t m, int64_t n, uint64_t* out);
+hipError_t launch_prefill(const DevProblem* probs, const uint64_t* tiles, int64_t tile_count, hipStream_t s);
 hipError_t launch_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, int32_t* idx,
                          float* max_logit, float* logits, void* workspace, hipStream_t s);
 int64_t lmhead_partials(int64_t v);

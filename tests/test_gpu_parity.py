@@ -297,3 +297,62 @@ def test_lmhead_planted_winner_and_tie(qmv_gpu):
     idx, _, _ = qmv.qmv_lmhead_argmax(_t(w_bits.view(np.int16)), _t(x))
     torch.cuda.synchronize()
     assert idx.item() == 777
+
+
+# --------------------------------------------------------------------------
+# A8: prefill GEMM on int8 matrix cores
+# --------------------------------------------------------------------------
+
+# (n, k, m): ragged tokens and rows around the 256 x 256 tile, odd chunk
+# counts (the last K step is half empty), K not a multiple of 4.
+PREFILL_CASES = [(1, 1, 1), (5, 7, 3), (64, 80, 32), (300, 1152, 256), (257, 1152, 300), (33, 6912, 512),
+                 (1024, 1152, 512), (100, 1600, 17), (513, 161, 257), (40, 1537, 5)]
+
+
+@pytest.mark.parametrize("n,k,m", PREFILL_CASES)
+def test_prefill_parity(qmv_gpu, n, k, m):
+    from ternary_matvec_amd import qmv
+    say("prefill", n, k, m)
+    t = synth.trits(12000 + n + k, (n, k))
+    x = _x_for(12001 + k + m, m, k)
+    q, sx = oracle.quantize_rows(x)
+    sw = synth.ternary_scale(12002 + n)
+    acc_ref = oracle.matmul_int(q, t)
+    w = qmv.qmv_pack_ternary(_t(t), sw)
+    acc = torch.full((m, n), -7, dtype=torch.int32, device=DEV)
+    p = qmv.Problem(w, _t(q), _t(sx), acc=acc)
+    qmv.qmv_gemm_prefill([p])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    _check_y(p.y.cpu().numpy(), acc_ref, sx, np.float32(sw))
+
+
+def test_prefill_grouped_equals_gemv(qmv_gpu):
+    """Grouped prefill over mixed shapes equals single launches, and each
+    token row equals the decode GEMV of that token (exact integers)."""
+    from ternary_matvec_amd import qmv
+    say("prefill grouped vs gemv")
+    specs = [(1024, 1152, 40), (256, 1152, 7), (1152, 6912, 3), (6912, 1152, 2)]
+    probs, refs, ins = [], [], []
+    for i, (n, k, m) in enumerate(specs):
+        t = synth.trits(13000 + i, (n, k))
+        q, sx = oracle.quantize_rows(_x_for(13100 + i, m, k))
+        w = qmv.qmv_pack_ternary(_t(t), 0.02)
+        refs.append(oracle.matmul_int(q, t))
+        ins.append((w, q, sx))
+        probs.append(qmv.Problem(w, _t(q), _t(sx), acc=torch.zeros((m, n), dtype=torch.int32, device=DEV)))
+    qmv.qmv_gemm_prefill(probs)
+    torch.cuda.synchronize()
+    for p, ref, (w, q, sx) in zip(probs, refs, ins):
+        got = p.acc.cpu().numpy()
+        np.testing.assert_array_equal(got, ref)
+        y_grouped = p.y.cpu().numpy().copy()
+        single = qmv.Problem(w, _t(q), _t(sx), acc=torch.zeros_like(p.acc))
+        qmv.qmv_gemm_prefill([single])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(single.y.cpu().numpy(), y_grouped)
+        for j in (0, q.shape[0] - 1):
+            one = qmv.Problem(w, _t(q[j:j + 1]), _t(sx[j:j + 1]), acc=torch.zeros((1, w.n), dtype=torch.int32, device=DEV))
+            qmv.qmv_gemv([one])
+            torch.cuda.synchronize()
+            np.testing.assert_array_equal(one.acc.cpu().numpy()[0], got[j])
