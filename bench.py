@@ -26,6 +26,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, datasheet
+GEMV_SOURCES = ("k_gemv_stream.hip", "unpack.hpp", "qmv_internal.hpp")
+GEMV_COUNTERS = os.path.join(ROOT, "profiles", "k_gemv_stream_counters.json")
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, datasheet
 
 
@@ -42,6 +44,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run a plain device-to-device copy of this many MiB five times: the "
+                         "known-size kernel that calibrates the FETCH_SIZE / WRITE_SIZE counters "
+                         "(1024 makes it the largest copy of the run)")
     return ap.parse_args()
 
 
@@ -381,6 +387,33 @@ def bench_bitnet(dev, stream, steps, warmup, copies):
     return out
 
 
+def gemv_source_hash():
+    """sha256 over the sources of the streaming GEMV kernel (counter records name the hash they
+    were taken with)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMV_SOURCES:
+        with open(os.path.join(ROOT, "ternary_matvec_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gemv_traffic():
+    """HBM bytes per launch of the streaming GEMV from the committed rocprofv3 counter record:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the dispatches of the headline launch),
+    each scaled by the factor the same counter gave for a plain copy of known size.  None when the
+    record is missing or was taken with different kernel sources."""
+    try:
+        with open(GEMV_COUNTERS) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != gemv_source_hash():
+        return None
+    kib = rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]
+    return int(round(kib * 1024))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -426,9 +459,9 @@ def main():
                    "tokens": 1, "matrices": len(stack.specs), "weight_copies": args.copies,
                    "step": "qmv_quantize_act x2 + one grouped qmv_gemv",
                    "step_bytes": step_bytes, "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "k_gemv<1,1> (grouped ternary GEMV)",
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_stream<1,1> (grouped ternary GEMV)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": gemv_traffic(),
                      "bytes_per_launch": gemv_bytes, "launch_us": round(gemv_ms * 1e3, 3),
                      "launch_us_back_to_back": round(gemv_only_ms * 1e3, 3)},
     }
@@ -448,6 +481,15 @@ def main():
         except Exception as e:  # extras never hide the headline line
             extras["error"] = repr(e)
         result["extras"] = extras
+    if args.copy_probe_mb:
+        nbytes = args.copy_probe_mb << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = nbytes
+        del src, dst
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(stack, args.cpu_seconds, dev)
