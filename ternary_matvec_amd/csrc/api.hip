@@ -6,6 +6,9 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <memory>
+#include <mutex>
+#include <queue>
 #include <vector>
 
 #include "qmv_internal.hpp"
@@ -57,94 +60,192 @@ int32_t check_problems(const qmv_problem* probs, int32_t count, int64_t max_m)
     return QMV_OK;
 }
 
-// Workspace image of a problem list: [DevProblem x count][tile entries].
-// Problems are grouped by weight type; inside a group the largest tiles come
-// first so they start first.  A tile is a block of rows of one problem:
-// 64 rows for the workgroup kernel, 64 / lanes_per_row rows for the streaming
-// kernel.
+// ---------------------------------------------------------------------------
+// GEMV problem tables.
+//
+// Workspace image: [DevProblem x count] then, per weight type present, either
+// a tile list for the workgroup kernel (64-row tiles) or a schedule for the
+// streaming kernel ([nb + 1 offsets][workgroup tile entries]).  Problems are
+// grouped by weight type in the table.
+//
+// Streaming schedule: every problem gets L lanes per row (1, 2 or 4), so a
+// workgroup tile is 4 * 64 / L rows.  Several L assignments are tried (each the
+// smallest L that brings a problem under a target number of chunk steps); each
+// is scheduled longest-processing-time-first onto the nb workgroups and the
+// one with the shortest modelled makespan is kept.
+// ---------------------------------------------------------------------------
+
+#ifndef QMV_STREAM_WG_PER_CU
+#define QMV_STREAM_WG_PER_CU 4
+#endif
+constexpr int kStreamWgPerCu = QMV_STREAM_WG_PER_CU;   // 16 waves per compute unit
+constexpr int kStreamMaxM = 2;
+
 struct Table {
     std::vector<uint8_t> bytes;
-    int64_t tiles_offset = 0;
-    int32_t total_tiles = 0;
-    // per weight type: streaming kernel?, first tile, tile count, max m, max chunks
     bool stream[3] = {false, false, false};
-    int32_t first[3] = {0, 0, 0}, count[3] = {0, 0, 0}, max_m[3] = {0, 0, 0}, max_chunks[3] = {0, 0, 0};
-};
-
-struct Plan {
-    std::vector<int32_t> order;    // problem index per table slot
-    std::vector<int32_t> rows;     // rows per tile, per problem
-    std::vector<int32_t> lanes;    // lanes per row, per problem
-    int64_t tiles = 0;
-    bool stream[3] = {false, false, false};
+    int64_t region[3] = {0, 0, 0};      // byte offset of the type's tile list or schedule
+    int32_t count[3] = {0, 0, 0};       // tiles (workgroup kernel) or workgroup tiles (streaming)
     int32_t max_m[3] = {0, 0, 0}, max_chunks[3] = {0, 0, 0};
+    int32_t nb[3] = {0, 0, 0}, slot_bytes[3] = {0, 0, 0};
 };
 
-void make_plan(const qmv_problem* probs, int32_t count, Plan& pl)
+int32_t chunks_of(const qmv_problem& p) { return (int32_t)(row_stride(p.w.wtype, p.w.k) / 16); }
+
+int64_t rows_tiles(int64_t n, int64_t rows) { return (n + rows - 1) / rows; }
+
+// Upper bound of the table bytes for any device with at most `cus` compute units.
+int64_t table_bound(const qmv_problem* probs, int32_t count, int cus)
 {
+    int64_t tiles64 = 0;
+    for (int32_t i = 0; i < count; ++i) tiles64 += rows_tiles(probs[i].w.n, kRowsPerTile);
+    int64_t b = round_up((int64_t)sizeof(DevProblem) * count, 256);
+    (void)cus;
+    for (int wt = 1; wt <= 2; ++wt) b += round_up((tiles64 + kStreamHdr + 2 * kStreamXcds) * 4, 256);
+    return b;
+}
+
+struct StreamChoice {
+    std::vector<int32_t> lanes;        // per table slot (0 for other types)
+    std::vector<uint32_t> words;       // offsets + entries
+    int nb = 0;
+    int64_t slot_bytes = 0;
+    double makespan = 0;
+};
+
+// Schedule the streaming problems `slots` (table slots of one weight type).
+bool schedule_stream(const std::vector<const qmv_problem*>& sp, const std::vector<int32_t>& slots, int wtype,
+                     int mt, int cus, StreamChoice& best)
+{
+    static const int kTargets[] = {4, 6, 8, 12, 16, 24, 32, 48, 64, 1 << 30};
+    for (const qmv_problem* p : sp)   // the kernel sizes its weight buffers in 32 bits
+        if ((int64_t)chunks_of(*p) * 16 * p->w.n >= ((int64_t)1 << 31)) return false;
+    std::vector<std::vector<int32_t>> tried;
+    bool found = false;
+    for (int target : kTargets) {
+#ifdef QMV_STREAM_TARGET
+        if (target != QMV_STREAM_TARGET) continue;
+#endif
+        std::vector<int32_t> lanes(sp.size());
+        for (size_t i = 0; i < sp.size(); ++i) {
+            const int c = chunks_of(*sp[i]);
+            int L = 1;
+            while (L < 4 && gemv_stream_steps(c, L) > target) L *= 2;
+            lanes[i] = L;
+        }
+        if (std::find(tried.begin(), tried.end(), lanes) != tried.end()) continue;
+        tried.push_back(lanes);
+        int64_t slot = 0;
+        for (size_t i = 0; i < sp.size(); ++i)
+            slot = std::max(slot, gemv_stream_slot_bytes(wtype, mt, chunks_of(*sp[i]), lanes[i]));
+        slot = round_up(slot, 16);
+        const size_t lds = gemv_stream_lds_bytes(mt, slot);
+        if ((int64_t)lds > kMaxLds) continue;
+        const int wg_per_cu = (int)std::min<int64_t>(kStreamWgPerCu, kMaxLds / (int64_t)lds);
+        // workgroup tiles, longest first
+        struct Item { double cost; uint32_t entry; };
+        std::vector<Item> items;
+        for (size_t i = 0; i < sp.size(); ++i) {
+            const qmv_problem& p = *sp[i];
+            const int c = chunks_of(p);
+            const int64_t rows = 4 * (kRowsPerTile / lanes[i]);
+            // chunk steps (an int8 step is a quarter of a ternary one) plus the
+            // tile boundary (barrier, epilogue, ring refill), which measures at
+            // about six ternary steps
+            const double cost = (double)gemv_stream_steps(c, lanes[i]) * (wtype == 1 ? p.m : 0.3 * p.m) + 6.0;
+            const int64_t nt = rows_tiles(p.w.n, rows);
+            for (int64_t r = 0; r < nt; ++r)
+                items.push_back({cost, ((uint32_t)slots[i] << kTileRowBits) | (uint32_t)r});
+        }
+        std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
+        const int nb = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * wg_per_cu, (int64_t)items.size()));
+        // Tiles after each workgroup's first are taken dynamically, so the
+        // finish is about the mean load plus one of the last (smallest) tiles.
+        double total = 0;
+        for (const Item& it : items) total += it.cost;
+        const double makespan = total / nb + items.back().cost;
+        if (found && makespan >= best.makespan) continue;
+        found = true;
+        best.lanes = lanes;
+        best.nb = nb;
+        best.slot_bytes = slot;
+        best.makespan = makespan;
+        // The kernel deals tiles per XCD: the same items, longest first, onto
+        // the 8 XCD lists (each list stays longest first).
+        std::vector<std::vector<uint32_t>> xl(kStreamXcds);
+        std::vector<double> load(kStreamXcds, 0.0);
+        std::vector<int> wgs(kStreamXcds);
+        for (int x = 0; x < kStreamXcds; ++x) wgs[x] = (nb - x + kStreamXcds - 1) / kStreamXcds;
+        for (const Item& it : items) {
+            int bx = -1;
+            for (int x = 0; x < kStreamXcds; ++x)   // least loaded per workgroup
+                if (wgs[x] > 0 && (bx < 0 || load[x] / wgs[x] < load[bx] / wgs[bx])) bx = x;
+            xl[bx].push_back(it.entry);
+            load[bx] += it.cost;
+        }
+        best.words.assign(kStreamHdr + 2 * kStreamXcds, 0u);
+        uint32_t off = 0;
+        for (int x = 0; x < kStreamXcds; ++x) {
+            best.words[kStreamHdr + 2 * x] = off;
+            best.words[kStreamHdr + 2 * x + 1] = (uint32_t)xl[x].size();
+            off += (uint32_t)xl[x].size();
+        }
+        for (int x = 0; x < kStreamXcds; ++x) best.words.insert(best.words.end(), xl[x].begin(), xl[x].end());
+    }
+    return found;
+}
+
+// Builds the table; returns QMV_OK or a status.
+int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
+{
+    std::vector<int32_t> order(count);
+    for (int32_t i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return probs[a].w.wtype < probs[b].w.wtype; });
     for (int32_t i = 0; i < count; ++i) {
         const int32_t wt = probs[i].w.wtype;
-        pl.max_m[wt] = std::max<int32_t>(pl.max_m[wt], (int32_t)probs[i].m);
-        pl.max_chunks[wt] = std::max<int32_t>(pl.max_chunks[wt], (int32_t)(row_stride(wt, probs[i].w.k) / 16));
+        t.max_m[wt] = std::max<int32_t>(t.max_m[wt], (int32_t)probs[i].m);
+        t.max_chunks[wt] = std::max<int32_t>(t.max_chunks[wt], chunks_of(probs[i]));
     }
-    for (int wt = 1; wt <= 2; ++wt)
-        pl.stream[wt] = pl.max_m[wt] > 0 && gemv_stream_fits(wt, pl.max_m[wt], pl.max_chunks[wt]);
-    pl.rows.resize(count);
-    pl.lanes.resize(count);
-    pl.order.resize(count);
-    for (int32_t i = 0; i < count; ++i) {
-        const int32_t wt = probs[i].w.wtype;
-        const int32_t chunks = (int32_t)(row_stride(wt, probs[i].w.k) / 16);
-        pl.lanes[i] = pl.stream[wt] ? gemv_stream_lanes_per_row(chunks) : 1;
-        pl.rows[i] = kRowsPerTile / pl.lanes[i];
-        pl.tiles += (probs[i].w.n + pl.rows[i] - 1) / pl.rows[i];
-        pl.order[i] = i;
-    }
-    std::stable_sort(pl.order.begin(), pl.order.end(), [&](int32_t a, int32_t b) {
-        if (probs[a].w.wtype != probs[b].w.wtype) return probs[a].w.wtype < probs[b].w.wtype;
-        const int64_t ta = (int64_t)pl.rows[a] * row_stride(probs[a].w.wtype, probs[a].w.k);
-        const int64_t tb = (int64_t)pl.rows[b] * row_stride(probs[b].w.wtype, probs[b].w.k);
-        return ta > tb;
-    });
-}
-
-int64_t plan_bytes(const Plan& pl, int32_t count)
-{
-    return round_up((int64_t)sizeof(DevProblem) * count, 256) + round_up(pl.tiles * 4, 256);
-}
-
-bool plan_tiles_fit(const qmv_problem* probs, int32_t count, const Plan& pl)
-{
-    for (int32_t i = 0; i < count; ++i)
-        if ((probs[i].w.n + pl.rows[i] - 1) / pl.rows[i] > ((int64_t)1 << kTileRowBits)) return false;
-    return true;
-}
-
-int64_t table_bytes(const qmv_problem* probs, int32_t count)
-{
-    Plan pl;
-    make_plan(probs, count, pl);
-    return plan_bytes(pl, count);
-}
-
-void build_table(const qmv_problem* probs, int32_t count, const Plan& pl, Table& t)
-{
     const int64_t pbytes = round_up((int64_t)sizeof(DevProblem) * count, 256);
-    t.bytes.assign(plan_bytes(pl, count), 0);
-    t.tiles_offset = pbytes;
-    t.total_tiles = (int32_t)pl.tiles;
-    DevProblem* dp = reinterpret_cast<DevProblem*>(t.bytes.data());
-    uint32_t* te = reinterpret_cast<uint32_t*>(t.bytes.data() + pbytes);
-    int32_t tile = 0;
+    std::vector<int32_t> lanes(count, 1);             // per table slot
+    std::vector<uint32_t> words[3];
     for (int wt = 1; wt <= 2; ++wt) {
-        t.stream[wt] = pl.stream[wt];
-        t.max_m[wt] = pl.max_m[wt];
-        t.max_chunks[wt] = pl.max_chunks[wt];
+        if (t.max_m[wt] == 0) continue;
+        std::vector<const qmv_problem*> sp;
+        std::vector<int32_t> slots;
+        for (int32_t slot = 0; slot < count; ++slot)
+            if (probs[order[slot]].w.wtype == wt) {
+                sp.push_back(&probs[order[slot]]);
+                slots.push_back(slot);
+            }
+        StreamChoice ch;
+        if (t.max_m[wt] <= kStreamMaxM &&
+            schedule_stream(sp, slots, wt, t.max_m[wt] <= 1 ? 1 : 2, cus, ch)) {
+            t.stream[wt] = true;
+            t.nb[wt] = ch.nb;
+            t.slot_bytes[wt] = (int32_t)ch.slot_bytes;
+            t.count[wt] = (int32_t)(ch.words.size() - kStreamHdr - 2 * kStreamXcds);
+            for (size_t i = 0; i < slots.size(); ++i) lanes[slots[i]] = ch.lanes[i];
+            words[wt] = std::move(ch.words);
+        } else {
+            if (gemv_lds_bytes(wt, t.max_m[wt], t.max_chunks[wt]) > kMaxLds) return QMV_ESHAPE;
+            for (size_t i = 0; i < sp.size(); ++i) {
+                const int64_t nt = rows_tiles(sp[i]->w.n, kRowsPerTile);
+                for (int64_t r = 0; r < nt; ++r) words[wt].push_back(((uint32_t)slots[i] << kTileRowBits) | (uint32_t)r);
+            }
+            t.count[wt] = (int32_t)words[wt].size();
+        }
     }
+    int64_t total = pbytes;
+    for (int wt = 1; wt <= 2; ++wt) {
+        t.region[wt] = total;
+        total += round_up((int64_t)words[wt].size() * 4, 256);
+    }
+    t.bytes.assign(total, 0);
+    DevProblem* dp = reinterpret_cast<DevProblem*>(t.bytes.data());
     for (int32_t slot = 0; slot < count; ++slot) {
-        const int32_t pi = pl.order[slot];
-        const qmv_problem& p = probs[pi];
-        const int32_t wt = p.w.wtype;
+        const qmv_problem& p = probs[order[slot]];
         DevProblem& d = dp[slot];
         d.w = static_cast<const uint8_t*>(p.w.data);
         d.sw = p.w.scale;
@@ -155,17 +256,79 @@ void build_table(const qmv_problem* probs, int32_t count, const Plan& pl, Table&
         d.n = (int32_t)p.w.n;
         d.k = (int32_t)p.w.k;
         d.m = (int32_t)p.m;
-        d.chunks = (int32_t)(row_stride(wt, p.w.k) / 16);
-        d.tile_begin = tile;
-        d.wtype = wt;
-        d.lanes_per_row = pl.lanes[pi];
+        d.chunks = chunks_of(p);
+        d.tile_begin = 0;
+        d.wtype = p.w.wtype;
+        d.lanes_per_row = lanes[slot];
         d.reserved = 0;
-        if (t.count[wt] == 0) t.first[wt] = tile;
-        const int32_t ntiles = (int32_t)((p.w.n + pl.rows[pi] - 1) / pl.rows[pi]);
-        for (int32_t r = 0; r < ntiles; ++r) te[tile + r] = ((uint32_t)slot << kTileRowBits) | (uint32_t)r;
-        tile += ntiles;
-        t.count[wt] += ntiles;
     }
+    for (int wt = 1; wt <= 2; ++wt)
+        if (!words[wt].empty())
+            std::memcpy(t.bytes.data() + t.region[wt], words[wt].data(), words[wt].size() * 4);
+    return QMV_OK;
+}
+
+// Compute units of the current device; with no usable device the plan is made
+// for a 256-CU part (host validation still works, launches then fail).
+int device_cus(int* cus_out)
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+        *cus_out = 256;
+        return -1;
+    }
+    *cus_out = cus;
+    return dev;
+}
+
+// A few recently built tables, keyed by device and the problem list's bytes,
+// so a decode loop that launches the same list again does not re-plan it.
+struct TableCache {
+    std::mutex mu;
+    struct Entry {
+        int dev, cus;
+        std::vector<uint8_t> key;
+        std::shared_ptr<const Table> table;
+    };
+    std::vector<Entry> entries;
+    size_t next = 0;
+};
+
+TableCache& table_cache()
+{
+    static TableCache c;
+    return c;
+}
+
+int32_t get_table(const qmv_problem* probs, int32_t count, std::shared_ptr<const Table>& out)
+{
+    int cus = 0;
+    const int dev = device_cus(&cus);
+    const uint8_t* kb = reinterpret_cast<const uint8_t*>(probs);
+    const size_t kn = sizeof(qmv_problem) * (size_t)count;
+    TableCache& c = table_cache();
+    {
+        std::lock_guard<std::mutex> g(c.mu);
+        for (const auto& e : c.entries)
+            if (e.dev == dev && e.cus == cus && e.key.size() == kn && std::memcmp(e.key.data(), kb, kn) == 0) {
+                out = e.table;
+                return QMV_OK;
+            }
+    }
+    auto t = std::make_shared<Table>();
+    const int32_t st = build_table(probs, count, cus, *t);
+    if (st != QMV_OK) return st;
+    std::lock_guard<std::mutex> g(c.mu);
+    TableCache::Entry e{dev, cus, std::vector<uint8_t>(kb, kb + kn), t};
+    if (c.entries.size() < 8) {
+        c.entries.push_back(std::move(e));
+    } else {
+        c.entries[c.next] = std::move(e);
+        c.next = (c.next + 1) % 8;
+    }
+    out = t;
+    return QMV_OK;
 }
 
 constexpr int64_t kMaxPrefillM = 65536;
@@ -272,7 +435,9 @@ int32_t qmv_quantize_act(const float* x, int64_t m, int64_t k, int8_t* x8, float
 int64_t qmv_gemv_workspace_bytes(const qmv_problem* probs, int32_t count)
 {
     if (check_problems(probs, count, QMV_MAX_GEMV_M) != QMV_OK) return -1;
-    return table_bytes(probs, count);
+    int cus = 0;
+    device_cus(&cus);
+    return table_bound(probs, count, cus);
 }
 
 int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, uint32_t flags,
@@ -281,30 +446,30 @@ int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64
     int32_t st = check_problems(probs, count, QMV_MAX_GEMV_M);
     if (st != QMV_OK) return st;
     if (flags & ~(uint32_t)QMV_F_TABLE_READY) return QMV_EINVAL;
-    Plan pl;
-    make_plan(probs, count, pl);
-    if (!plan_tiles_fit(probs, count, pl)) return QMV_ESHAPE;
-    for (int wt = 1; wt <= 2; ++wt)
-        if (pl.max_m[wt] && !pl.stream[wt] && gemv_lds_bytes(wt, pl.max_m[wt], pl.max_chunks[wt]) > kMaxLds)
-            return QMV_ESHAPE;
-    if (!workspace || !aligned(workspace, 256) || ws_bytes < plan_bytes(pl, count)) return QMV_EWORKSPACE;
-    Table t;
-    build_table(probs, count, pl, t);
+    std::shared_ptr<const Table> tp;
+    st = get_table(probs, count, tp);
+    if (st != QMV_OK) return st;
+    const Table& t = *tp;
+    int cus = 0;
+    device_cus(&cus);
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < table_bound(probs, count, cus) ||
+        ws_bytes < (int64_t)t.bytes.size())
+        return QMV_EWORKSPACE;
     const hipStream_t s = as_stream(stream);
     if (!(flags & QMV_F_TABLE_READY)) {
         hipError_t e = hipMemcpyAsync(workspace, t.bytes.data(), t.bytes.size(), hipMemcpyHostToDevice, s);
         if (e != hipSuccess) return QMV_EHIP;
     }
-    const uint8_t* base = static_cast<const uint8_t*>(workspace);
+    uint8_t* base = static_cast<uint8_t*>(workspace);
     const DevProblem* dp = reinterpret_cast<const DevProblem*>(base);
-    const uint32_t* tiles = reinterpret_cast<const uint32_t*>(base + t.tiles_offset);
     for (int wt = 1; wt <= 2; ++wt) {
         if (t.count[wt] == 0) continue;
+        uint32_t* words = reinterpret_cast<uint32_t*>(base + t.region[wt]);
         hipError_t e;
         if (t.stream[wt])
-            e = launch_gemv_stream(dp, tiles, t.first[wt], t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
+            e = launch_gemv_stream(dp, words, t.nb[wt], wt, t.max_m[wt], t.slot_bytes[wt], s);
         else
-            e = launch_gemv(dp, tiles, t.first[wt], t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
+            e = launch_gemv(dp, words, 0, t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
         if (e != hipSuccess) return QMV_EHIP;
     }
     return QMV_OK;

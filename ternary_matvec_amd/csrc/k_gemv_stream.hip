@@ -5,17 +5,40 @@
 // "Gemma 3 1B at 114 tokens per second on a laptop CPU", "Step 1"; cpp20gemma
 // README, "Architecture & implementation"), organised for streaming:
 //
-//  * Every wave is an independent worker with a static share of the tiles:
-//    wave g takes tiles g, g + G, g + 2G, ... of the launch (G waves), and the
-//    host lists tiles largest first.  No atomics, no workgroup barriers.
-//  * A tile is 64 / L rows of one problem, L = lanes per row (1, 2 or 4,
-//    larger for longer rows) so every tile moves a similar number of bytes.
-//    Lane s*R + r (R = 64 / L rows) streams chunks s, s + L, ... of row r; for
-//    a fixed s the R rows' chunk is one contiguous run of R * 16 bytes.  The L
-//    partial sums of a row meet through lane shuffles at the end of the tile.
-//  * A wave stages its tile's activations in its own LDS slice, already in
-//    trit-plane order (the page's once-per-token input reorder); a wave-local
-//    fence orders its LDS writes and reads.
+//  * Work unit = a workgroup tile: 4 * R rows of one problem, one R-row wave
+//    tile per compute wave.  R = 64 / L, L = lanes per row (1, 2 or 4, chosen
+//    by the host so tiles are of similar length).  Lane s*R + r of a wave
+//    streams chunks s, s + L, s + 2L, ... of row r; for a fixed s the R rows'
+//    chunk is one contiguous run of R * 16 bytes.  The L partial sums of a row
+//    meet through lane shuffles at the end of the tile.
+//  * Tiles are dealt to the 8 XCDs by the host (longest processing time
+//    first; workgroup b runs on XCD b mod 8).  Inside an XCD's list a
+//    workgroup's first tile is fixed (its rank among the XCD's workgroups) and
+//    every later one is taken from a per-XCD atomic counter, one tile ahead, by
+//    the staging wave: workgroups that run slower take fewer tiles and all
+//    finish within about one tile of each other.  The last workgroup of an XCD
+//    to finish resets its counters for the next launch.
+//  * A workgroup is four compute waves and one staging wave.  The staging
+//    wave prepares the next tile's activations in LDS (two slots) while the
+//    compute waves stream the current one, so activation loads never sit in
+//    the compute waves' in-order memory counters.  For ternary weights what is
+//    staged is not x itself but, per packed byte, the five int16 combinations
+//    Z_1..Z_5 described below, in the order the weight registers come out of
+//    the unpacker: the page's once-per-token input reorder.
+//  * Weight loads are raw buffer loads into a register ring (kRing - 1 chunk
+//    loads in flight while one is consumed): past the end of the matrix they
+//    return zeros instead of faulting, so no lane clamps or branches; loads past
+//    a tile's last chunk fetch the next tile's first chunks.
+//
+// Ternary arithmetic.  For a packed byte b with base-3 digits d_1..d_5 (d_1 the
+// most significant, digit d = trit + 1) meeting activations X_1..X_5, let
+// P_j = floor(b / 3^(5-j)), so d_j = P_j - 3 P_(j-1) and
+//     sum_j d_j X_j = sum_j P_j Z_j,   Z_j = X_j - 3 X_(j+1) (j < 5),  Z_5 = X_5.
+// The unpacker holds P_j of two bytes as the fp16 pair 1024 + P_j, whose int16
+// bit pattern is 25600 + P_j, so one v_dot2_i32_i16 with the int16 pair of Z
+// values adds P.Z plus 25600 * (Z sum); that constant and sum x (trit = d - 1)
+// are taken off once per row.  Sums are modulo 2^32, exact whenever the true
+// dot fits int32.
 #include "qmv_internal.hpp"
 #include "unpack.hpp"
 
@@ -23,305 +46,504 @@ namespace qmv {
 namespace {
 
 #ifndef QMV_STREAM_BATCH
-#define QMV_STREAM_BATCH 2
+#define QMV_STREAM_BATCH 1
 #endif
-#ifndef QMV_STREAM_WAVES_PER_CU
-#define QMV_STREAM_WAVES_PER_CU 16
+#ifndef QMV_STREAM_RING
+#define QMV_STREAM_RING 4
 #endif
-#ifndef QMV_STREAM_MIN_WAVES_PER_EU
-#define QMV_STREAM_MIN_WAVES_PER_EU 1
-#endif
-constexpr int kSBatch = QMV_STREAM_BATCH;  // chunks per step batch; the next batch is in flight meanwhile
-constexpr int kStreamWavesPerCU = QMV_STREAM_WAVES_PER_CU;
+constexpr int kSBatch = QMV_STREAM_BATCH;      // chunks per register batch
+constexpr int kRing = QMV_STREAM_RING;         // batches in the register ring: kRing - 1 in flight
+constexpr int kStepGrain = kSBatch * kRing;    // chunk steps of a tile are a multiple of this
+constexpr int kComputeWaves = 4;
+constexpr int kStreamThreads = (kComputeWaves + 1) * kWave;   // + the staging wave
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+constexpr int kZBytes = 192;                   // staged bytes per 16-byte ternary chunk per token (4 x 12 dwords)
+constexpr int kXBytes = 16;                    // staged bytes per 16-byte int8 chunk per token
+constexpr uint32_t kEnd = 0xffffffffu;         // no tile
 
-__device__ __forceinline__ void wave_lds_sync()
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int dot2(uint32_t a, uint32_t b, int c)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return __builtin_amdgcn_sdot2(__builtin_bit_cast(s16x2, a), __builtin_bit_cast(s16x2, b), c, false);
 }
 
-__device__ __forceinline__ int wave_sum(int v)
+// Sum over a wave, exact in int32 arithmetic: prefix sums inside each row of
+// 16 lanes by DPP row shifts (lanes shifted in from outside the row add 0),
+// then the four row totals through lane reads.
+__device__ __forceinline__ int wave_total(int v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) + __builtin_amdgcn_readlane(v, 47) +
+           __builtin_amdgcn_readlane(v, 63);
+}
+
+// Z values of one 20-column group (natural dwords nat[0..4]; packed byte q of
+// the group covers columns 5q .. 5q+4, column 5q+e meeting the digit of 3^e,
+// so X_j = x[5q + 5 - j]).  out[2i + r] is the int16 pair of Z_(i+1) for bytes
+// r (low half) and r + 2 (high half): the same byte pairs the unpacker puts
+// into one fp16 register.  Adds the group's Z sum and x sum to sum_z, sum_x.
+__device__ __forceinline__ void z_group(const uint32_t nat[5], uint32_t out[10], int& sum_z, int& sum_x)
 {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
-}
-
-// One natural-order activation dword (columns 4d .. 4d+3 of a row of k int8
-// values, k a multiple of 4, row 4-byte aligned): the load address is clamped
-// into the row and bytes past column k are zeroed, so no lane branches.
-__device__ __forceinline__ uint32_t x_dword(const QMV_GLOBAL uint32_t* xr4, int d, int k)
-{
-    const int last = (k >> 2) - 1;
-    const uint32_t v = xr4[d < last ? d : last];
-    const int valid = k - 4 * d;
-    return valid >= 4 ? v : valid <= 0 ? 0u : v & ((1u << (8 * valid)) - 1u);
-}
-
-// Byte-wise variant for rows that are not 4-byte aligned or k % 4 != 0.
-__device__ __forceinline__ uint32_t x_dword_bytes(const QMV_GLOBAL int8_t* xr, int d, int k)
-{
-    uint32_t v = 0;
+    for (int r = 0; r < 2; ++r) {
+        int za[5], zb[5];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int col = 4 * d + b;
-        v |= (col < k ? (uint32_t)(uint8_t)xr[col] : 0u) << (8 * b);
+        for (int h = 0; h < 2; ++h) {
+            const int q = r + 2 * h;
+            int x[5];
+#pragma unroll
+            for (int e = 0; e < 5; ++e) {
+                const int b = 5 * q + e;
+                x[e] = (int)(int8_t)(uint8_t)(nat[b >> 2] >> (8 * (b & 3)));
+                sum_x += x[e];
+            }
+            int* z = h ? zb : za;
+            z[0] = x[4] - 3 * x[3];
+            z[1] = x[3] - 3 * x[2];
+            z[2] = x[2] - 3 * x[1];
+            z[3] = x[1] - 3 * x[0];
+            z[4] = x[0];
+            // Z_1 + .. + Z_5 = x4 - 2 (x3 + x2 + x1 + x0)
+            sum_z += x[4] - 2 * (x[3] + x[2] + x[1] + x[0]);
+        }
+#pragma unroll
+        for (int i = 0; i < 5; ++i) out[2 * i + r] = __builtin_amdgcn_perm((uint32_t)zb[i], (uint32_t)za[i], 0x05040100u);
     }
-    return v;
 }
 
+// What a wave needs to know about one workgroup tile.
+struct Tile {
+    const DevProblem* P;
+    const int8_t* x8;
+    const uint8_t* w;
+    int n, k, m, C, lshift, wb, nsteps, cpad, tok_bytes;
+    uint32_t chunk_bytes;   // n * 16: one chunk of every row
+    int s_part, row;        // per lane (compute waves)
+    uint32_t voff;          // per lane: byte offset of its row's chunk s_part
+};
+
+// The part of a tile the compute waves use, as the staging wave leaves it in
+// LDS for them (so they never wait on descriptor loads from memory).
+struct TileDesc {
+    const uint8_t* w;
+    float* y;
+    int32_t* acc;
+    int32_t n, m, C, lshift, wb;
+    uint32_t te;            // tile entry, kEnd = no tile
+    float sw;
+    float sx[2];
+    int32_t pad;
+};
+static_assert(sizeof(TileDesc) == 64, "TileDesc layout");
+
+template <int CB>
+__device__ __forceinline__ void tile_derive(Tile& T, int wave, int lane)
+{
+    const int L = 1 << T.lshift;
+    const int rshift = 6 - T.lshift;                          // R = 64 / L rows per wave tile
+    T.nsteps = (((T.C + L - 1) >> T.lshift) + kStepGrain - 1) / kStepGrain * kStepGrain;
+    T.cpad = T.nsteps << T.lshift;                            // staged chunks: C real, the rest zeros
+    T.tok_bytes = T.cpad * CB;
+    T.chunk_bytes = (uint32_t)T.n * 16u;
+    T.s_part = lane >> rshift;
+    T.row = ((T.wb * kComputeWaves + wave) << rshift) + (lane & ((1 << rshift) - 1));
+    T.voff = (uint32_t)((T.s_part * T.n + T.row) * 16);
+}
+
+template <int CB>
+__device__ __forceinline__ Tile tile_at(const DevProblem* probs, uint32_t te, int wave, int lane)
+{
+    Tile T;
+    T.P = probs + (te >> kTileRowBits);
+    T.wb = (int)(te & ((1u << kTileRowBits) - 1));
+    T.x8 = T.P->x8;
+    T.w = T.P->w;
+    T.n = T.P->n;
+    T.k = T.P->k;
+    T.m = T.P->m;
+    T.C = T.P->chunks;
+    T.lshift = T.P->lanes_per_row == 1 ? 0 : T.P->lanes_per_row == 2 ? 1 : 2;
+    tile_derive<CB>(T, wave, lane);
+    return T;
+}
+
+__device__ __forceinline__ TileDesc desc_of(const Tile& T, uint32_t te)
+{
+    TileDesc d;
+    d.w = T.w;
+    d.y = T.P->y;
+    d.acc = T.P->acc;
+    d.n = T.n;
+    d.m = T.m;
+    d.C = T.C;
+    d.lshift = T.lshift;
+    d.wb = T.wb;
+    d.te = te;
+    d.sw = *cload_ptr(T.P->sw);
+    d.sx[0] = cload_ptr(T.P->sx)[0];
+    d.sx[1] = cload_ptr(T.P->sx)[T.m > 1 ? 1 : 0];
+    d.pad = 0;
+    return d;
+}
+
+// A descriptor read back from LDS, made wave-uniform.
+__device__ __forceinline__ TileDesc desc_load(const TileDesc* p)
+{
+    uint32_t v[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 q = reinterpret_cast<const uint4*>(p)[i];
+        v[4 * i + 0] = __builtin_amdgcn_readfirstlane(q.x);
+        v[4 * i + 1] = __builtin_amdgcn_readfirstlane(q.y);
+        v[4 * i + 2] = __builtin_amdgcn_readfirstlane(q.z);
+        v[4 * i + 3] = __builtin_amdgcn_readfirstlane(q.w);
+    }
+    return __builtin_bit_cast(TileDesc, v);
+}
+
+template <int CB>
+__device__ __forceinline__ Tile tile_of(const TileDesc& d, int wave, int lane)
+{
+    Tile T;
+    T.P = nullptr;
+    T.x8 = nullptr;
+    T.w = d.w;
+    T.n = d.n;
+    T.k = 0;
+    T.m = d.m;
+    T.C = d.C;
+    T.lshift = d.lshift;
+    T.wb = d.wb;
+    tile_derive<CB>(T, wave, lane);
+    return T;
+}
+
+// Step i of a tile reads chunks iL .. iL+L-1: a buffer based at chunk iL whose
+// size is what is left of the matrix, so reads past its end return zeros (the
+// host keeps every matrix of this kernel under 2^31 bytes).
+__device__ __forceinline__ v4u32 load_step(const Tile& T, int i, uint32_t voff)
+{
+    const int c0 = min(i << T.lshift, T.C);
+    const uint32_t nrec = (uint32_t)(T.C - c0) * T.chunk_bytes;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(T.w + (uint32_t)c0 * T.chunk_bytes), (short)0, (int)nrec, (int)kRsrcWord3);
+    return __builtin_bit_cast(v4u32, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+}
+
+// ---------------------------------------------------------------------------
+// Staging (one wave).  Activation unit u of token mi is a 20-column group (5
+// dwords, ternary) or one dword (int8) of the row, at any alignment and for
+// any k: the aligned dwords holding it are read through a buffer sized to the
+// row's aligned dwords (zeros past them), funnel-shifted into place, and bytes
+// past column k are zeroed.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uintptr_t row_addr(const Tile& T, int mi)
+{
+    return reinterpret_cast<uintptr_t>(T.x8) + (uintptr_t)mi * (uintptr_t)T.k;
+}
+
+template <int WT>
+__device__ __forceinline__ void unit_at(const Tile& T, int mi, int u, uint32_t* nat)
+{
+    constexpr int kD = WT == 1 ? 5 : 1;
+    const uintptr_t a = row_addr(T, mi);
+    const uint32_t sh = (uint32_t)(a & 3);
+    const uint32_t words = (sh + (uint32_t)T.k + 3u) >> 2;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a & ~(uintptr_t)3), (short)0, (int)(4 * words), (int)kRsrcWord3);
+    uint32_t raw[kD + 1];
+#pragma unroll
+    for (int j = 0; j <= kD; ++j) raw[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (kD * u + j), 0, 0);
+#pragma unroll
+    for (int j = 0; j < kD; ++j) {
+        const uint32_t v = __builtin_amdgcn_alignbyte(raw[j + 1], raw[j], sh);
+        const int valid = T.k - 4 * (kD * u + j);
+        nat[j] = valid >= 4 ? v : valid <= 0 ? 0u : v & ((1u << (8 * valid)) - 1u);
+    }
+}
+
+// The ten Z words of group g (chunk g / 4, dword g % 4) into their 48-byte
+// slot of the staged chunk.
+__device__ __forceinline__ void put_z(uint32_t* zo, int g, const uint32_t zz[10])
+{
+    uint32_t* d = zo + (g >> 2) * 48 + (g & 3) * 12;
+    reinterpret_cast<uint4*>(d)[0] = make_uint4(zz[0], zz[1], zz[2], zz[3]);
+    reinterpret_cast<uint4*>(d)[1] = make_uint4(zz[4], zz[5], zz[6], zz[7]);
+    reinterpret_cast<uint2*>(d)[4] = make_uint2(zz[8], zz[9]);
+}
+
+// Stage tile T into an LDS slot (the staging wave): Z values (ternary) or x
+// (int8) for chunks 0..C-1, zeros up to cpad, and the ternary correction
+// 25600 * sum Z + sum x of each token.
 template <int MT, int WT>
-__global__ __launch_bounds__(kBlock, QMV_STREAM_MIN_WAVES_PER_EU) void k_gemv_stream(const DevProblem* __restrict__ probs,
-                                                       const uint32_t* __restrict__ tiles, int32_t tile_base,
-                                                       int32_t tile_count, int32_t wave_lds_bytes)
+__device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, int* corr)
+{
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
+        if (mi > 0 && mi >= T.m) continue;
+        uint32_t* zo = reinterpret_cast<uint32_t*>(slot + (size_t)mi * T.tok_bytes);
+        const int units = 4 * T.C;
+        if (WT == 1) {
+            int s_z = 0, s_x = 0;
+            for (int g = lane; g < units; g += kWave) {
+                uint32_t nat[5], zz[10];
+                unit_at<1>(T, mi, g, nat);
+                z_group(nat, zz, s_z, s_x);
+                put_z(zo, g, zz);
+            }
+            for (int d = 48 * T.C + lane; d < 48 * T.cpad; d += kWave) zo[d] = 0u;
+            const int cw = wave_total((int)(25600u * (uint32_t)s_z + (uint32_t)s_x));
+            if (lane == 0) corr[mi] = cw;
+        } else {
+            for (int d = lane; d < units; d += kWave) unit_at<2>(T, mi, d, &zo[d]);
+            for (int d = units + lane; d < 4 * T.cpad; d += kWave) zo[d] = 0u;
+        }
+    }
+}
+
+// Schedule words: [counters: 8 tile counters + 8 done counters, 64 words
+// apart][8 x (list offset, list size)][tile entries of the 8 XCD lists].
+// LDS: [2 tile slots of slot_bytes][2 tile descriptors][corr: 2 x MT]
+template <int MT, int WT>
+__global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem* __restrict__ probs,
+                                                               uint32_t* __restrict__ sched, int32_t slot_bytes)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    uint32_t* xl = reinterpret_cast<uint32_t*>(smem + (size_t)wave * wave_lds_bytes);
-    const uint4* xl4 = reinterpret_cast<const uint4*>(xl);
-    constexpr int kXdwPerChunk = (WT == 1) ? 20 : 4;
+    constexpr int kCB = (WT == 1) ? kZBytes : kXBytes;   // staged bytes per chunk per token
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    TileDesc* const descs = reinterpret_cast<TileDesc*>(smem + 2 * (size_t)slot_bytes);
+    int* const corr_base = reinterpret_cast<int*>(descs + 2);
 
-    const int gw = blockIdx.x * (kBlock / kWave) + wave;
-    const int G = gridDim.x * (kBlock / kWave);
-    for (int t = gw; t < tile_count; t += G) {
-        const uint32_t te = tiles[tile_base + t];
-        const DevProblem* P = probs + (te >> kTileRowBits);
-        const int rb = (int)(te & ((1u << kTileRowBits) - 1));
-        const int n = P->n, k = P->k, m = P->m, C = P->chunks;
-        const int L = P->lanes_per_row;
-        const int R = kWave / L;
-        const int s_part = lane / R;            // which of the row's L chunk streams this lane takes
-        const int row = rb * R + (lane - s_part * R);
-        const bool live = row < n;
-        // Loads are never predicated: dead rows read row n-1 and chunk indices
-        // past the row read its last chunk; both are discarded (dead rows) or
-        // meet the all-zero activation chunk C (see below).
-        const QMV_GLOBAL v4u32* wp = gload_ptr(reinterpret_cast<const v4u32*>(P->w)) + (live ? row : n - 1);
-        const size_t cstride = (size_t)n;
-        const int nmax = (C + L - 1) / L;       // chunk steps of the row group (uniform)
-        const int nsteps = (nmax + kSBatch - 1) / kSBatch * kSBatch;
-        const int xdw_per_tok = kXdwPerChunk * (C + 1);
+    const int xcd = blockIdx.x % kStreamXcds;
+    const uint32_t rank = blockIdx.x / kStreamXcds;                       // among the XCD's workgroups
+    const uint32_t wgs = (gridDim.x - xcd + kStreamXcds - 1) / kStreamXcds;   // workgroups of this XCD
+    const QMV_CONST uint32_t* hdr = cload_ptr(sched + kStreamHdr);
+    const uint32_t list_off = hdr[2 * xcd], list_size = hdr[2 * xcd + 1];
+    const uint32_t* list = sched + kStreamHdr + 2 * kStreamXcds + list_off;
+    const uint32_t te0 = rank < list_size ? list[rank] : kEnd;
 
-        // ---- activation loads for the first staging pass go out first ----------
-        const bool fast_x = ((k & 3) == 0) && ((reinterpret_cast<uintptr_t>(P->x8) & 3) == 0);
-        const int ngroups = (WT == 1) ? 4 * C : 4 * C;   // 20-column groups (ternary) or dwords (int8)
-        uint32_t nat0[MT][5];
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-            const QMV_GLOBAL int8_t* xr = gload_ptr(P->x8) + (size_t)min(mi, m - 1) * k;
-            const QMV_GLOBAL uint32_t* xr4 = reinterpret_cast<const QMV_GLOBAL uint32_t*>(xr);
-#pragma unroll
-            for (int j = 0; j < (WT == 1 ? 5 : 1); ++j) {
-                const int d = (WT == 1) ? 5 * lane + j : lane;
-                nat0[mi][j] = fast_x ? x_dword(xr4, d, k) : x_dword_bytes(xr, d, k);
+    if (wave == kComputeWaves) {
+        // ---- staging wave: tile q into slot q & 1, the entry of tile q + 1, then
+        // barrier q ------------------------------------------------------------------
+        // The counter is read one tile ahead of its use (an atomic under
+        // contention takes microseconds): the ticket for tile q + 2 is taken
+        // while tile q + 1 is streamed.
+        uint32_t te = te0;
+        uint32_t ticket = 0;
+        if (te != kEnd && lane == 0) ticket = atomicAdd(&sched[64 * xcd], 1u);
+        Tile T;
+        if (te != kEnd) {
+            T = tile_at<kCB>(probs, te, 0, lane);
+            if (lane == 0) descs[0] = desc_of(T, te);
+        }
+        for (int par = 0; te != kEnd; par ^= 1) {
+            stage<MT, WT>(T, lane, smem + (size_t)par * slot_bytes, corr_base + par * MT);
+            uint32_t nx = kEnd;
+            if (lane == 0) {
+                const uint32_t i = wgs + ticket;
+                nx = i < list_size ? list[i] : kEnd;
+                if (nx != kEnd) ticket = atomicAdd(&sched[64 * xcd], 1u);
+            }
+            nx = __builtin_amdgcn_readfirstlane(nx);
+            if (nx != kEnd) {
+                T = tile_at<kCB>(probs, nx, 0, lane);
+                if (lane == 0) descs[par ^ 1] = desc_of(T, nx);
+            } else if (lane == 0) {
+                descs[par ^ 1].te = kEnd;
+            }
+            te = nx;
+            __syncthreads();
+        }
+        // Every workgroup of the XCD counts itself done once; the last one resets
+        // both counters.  Relaxed order suffices: a workgroup reaches this point
+        // only after the value of its last ticket came back (its loop exit
+        // depends on it), so every ticket of the launch has been taken before
+        // the last done count, and the resets reach the next launch through the
+        // end of this kernel.  (Acquire/release here would write back and
+        // invalidate the XCD's L2 per workgroup.)
+        if (lane == 0) {
+            uint32_t* done = &sched[64 * (kStreamXcds + xcd)];
+            if (__hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == wgs - 1) {
+                __hip_atomic_store(&sched[64 * xcd], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
+        return;
+    }
+    if (te0 == kEnd) return;
 
-        // ---- first batch of weights --------------------------------------------
-        v4u32 buf[kSBatch];
+    // ---- compute waves ----------------------------------------------------------------
+    Tile cur = tile_at<kCB>(probs, te0, wave, lane);
+    v4u32 ring[kRing][kSBatch];
 #pragma unroll
-        for (int u = 0; u < kSBatch; ++u) buf[u] = wp[(size_t)min(s_part + u * L, C - 1) * cstride];
+    for (int r = 0; r + 1 < kRing; ++r)
+#pragma unroll
+        for (int u = 0; u < kSBatch; ++u) ring[r][u] = load_step(cur, r * kSBatch + u, cur.voff);
 
-        // ---- stage this tile's activations in the wave's LDS slice --------------
-        // Chunk C of each token is all zeros: a lane whose row has no chunk left
-        // at some step reads it, so that step adds nothing.
-        int sum_all[MT], sum_d0[MT];
+    for (int par = 0;; par ^= 1) {
+        __syncthreads();   // this tile is staged and the next one named; every wave is done with the last
+        // The next tile (after the last one: the tile itself, with its batch loads
+        // past the matrix end, so every path is the same).
+        const TileDesc cd = desc_load(descs + par);
+        const TileDesc nd = desc_load(descs + (par ^ 1));
+        const bool has_next = nd.te != kEnd;
+        const Tile nxt = tile_of<kCB>(has_next ? nd : cd, wave, lane);
+        const uint8_t* zs = smem + (size_t)par * slot_bytes;
+        const int* corr = corr_base + par * MT;
+
+        int acc_lo[MT], acc_hi[MT];
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
-            sum_all[mi] = 0;
-            sum_d0[mi] = 0;
-            if (mi < m) {
-                const QMV_GLOBAL int8_t* xr = gload_ptr(P->x8) + (size_t)mi * k;
-                const QMV_GLOBAL uint32_t* xr4 = reinterpret_cast<const QMV_GLOBAL uint32_t*>(xr);
-                uint32_t* xo = xl + mi * xdw_per_tok;
-                if (lane < kXdwPerChunk) xo[kXdwPerChunk * C + lane] = 0u;
-                int s_all = 0, s_0 = 0;
-                for (int g = lane; g < ngroups; g += kWave) {
-                    if (WT == 1) {
-                        uint32_t nat[5];
-                        if (g == lane) {
-#pragma unroll
-                            for (int j = 0; j < 5; ++j) nat[j] = nat0[mi][j];
-                        } else {
-#pragma unroll
-                            for (int j = 0; j < 5; ++j)
-                                nat[j] = fast_x ? x_dword(xr4, 5 * g + j, k) : x_dword_bytes(xr, 5 * g + j, k);
-                        }
-                        uint32_t pl[5];
-                        reorder20(nat[0], nat[1], nat[2], nat[3], nat[4], pl);
-                        const int c = g >> 2, w = g & 3;
-#pragma unroll
-                        for (int i = 0; i < 5; ++i) {
-                            xo[20 * c + 4 * i + w] = pl[i];
-                            s_all = dot4(pl[i], 0x01010101u, s_all);
-                        }
-                        s_0 = dot4(pl[0], 0x01010101u, s_0);
-                    } else {
-                        xo[g] = (g == lane) ? nat0[mi][0] : (fast_x ? x_dword(xr4, g, k) : x_dword_bytes(xr, g, k));
-                    }
-                }
-                if (WT == 1) {
-                    sum_all[mi] = wave_sum(s_all);
-                    sum_d0[mi] = wave_sum(s_0);
-                }
-            }
+            acc_lo[mi] = 0;
+            acc_hi[mi] = 0;
         }
-        wave_lds_sync();
-
-        // ---- stream the tile ---------------------------------------------------
-        // Two register batches in ping-pong: batch b+1's loads are issued before
-        // batch b is consumed, so a batch is always in flight.  Loads past the
-        // last step re-read the row's last chunk (a cache hit) and are unused.
-        int acc_a[MT], acc_b[MT];
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-            acc_a[mi] = 0;
-            acc_b[mi] = 0;
-        }
-        const int x4_per_tok = xdw_per_tok / 4;
-        auto load_batch = [&](v4u32* dst, int i0) {
-#pragma unroll
-            for (int u = 0; u < kSBatch; ++u) dst[u] = wp[(size_t)min(s_part + (i0 + u) * L, C - 1) * cstride];
-        };
+        const uint8_t* zlane = zs + cur.s_part * kCB;
+        const int zstep = kCB << cur.lshift;
+        const int tok_bytes = cur.tok_bytes;
         auto run_batch = [&](const v4u32* src, int i0) {
 #pragma unroll
             for (int u = 0; u < kSBatch; ++u) {
-                const int c = min(s_part + (i0 + u) * L, C);   // C = the zero activation chunk
+                const uint8_t* zc = zlane + (i0 + u) * zstep;
                 if (WT == 1) {
-                    Planes pl[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) pl[j] = unpack(src[u][j]);
+                    for (int j = 0; j < 4; ++j) {
+                        uint4 Z[MT][3];   // the 10 Z pairs of dword j (and two pad words)
 #pragma unroll
-                    for (int mi = 0; mi < MT; ++mi) {
-                        if (mi < m) {
-                            const uint4* xq = xl4 + mi * x4_per_tok + 5 * c;
-                            const uint4 X0 = xq[0], X1 = xq[1], X2 = xq[2], X3 = xq[3], X4 = xq[4];
-                            int a = acc_a[mi], b = acc_b[mi];
+                        for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                const uint32_t x0 = sel(X0, j), x1 = sel(X1, j), x2 = sel(X2, j);
-                                const uint32_t x3 = sel(X3, j), x4 = sel(X4, j);
-                                a = dot4(pl[j].p1, x4, a);
-                                a = dot4(pl[j].p2, x3, a);
-                                a = dot4(pl[j].p3, x2, a);
-                                a = dot4(pl[j].p4, x1, a);
-                                a = dot4(pl[j].b5, x0, a);
-                                b = dot4(pl[j].p1, x3, b);
-                                b = dot4(pl[j].p2, x2, b);
-                                b = dot4(pl[j].p3, x1, b);
-                                b = dot4(pl[j].p4, x0, b);
+                            for (int q = 0; q < 3; ++q)
+                                Z[mi][q] = reinterpret_cast<const uint4*>(zc + (size_t)mi * tok_bytes + 48 * j)[q];
+                        constexpr uint32_t mag = 0x64646464u;
+                        uint32_t lo = __builtin_amdgcn_perm(mag, src[u][j], 0x04020400u);   // 1024 + b0 | b2
+                        uint32_t hi = __builtin_amdgcn_perm(mag, src[u][j], 0x04030401u);   // 1024 + b1 | b3
+#pragma unroll
+                        for (int i = 4; i >= 0; --i) {   // P_5 = b, then P_4 .. P_1
+#pragma unroll
+                            for (int mi = 0; mi < MT; ++mi) {
+                                acc_lo[mi] = dot2(lo, sel(Z[mi][i >> 1], (2 * i) & 3), acc_lo[mi]);
+                                acc_hi[mi] = dot2(hi, sel(Z[mi][i >> 1], (2 * i + 1) & 3), acc_hi[mi]);
                             }
-                            acc_a[mi] = a;
-                            acc_b[mi] = b;
+                            if (i > 0) {
+                                lo = third2(lo);
+                                hi = third2(hi);
+                            }
                         }
+                        // one dword at a time: other waves hide the latency, and
+                        // short live ranges leave room for the ring
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 } else {
 #pragma unroll
                     for (int mi = 0; mi < MT; ++mi) {
-                        if (mi < m) {
-                            const uint4 X = xl4[mi * x4_per_tok + c];
-                            int a = acc_a[mi];
-                            a = dot4(src[u][0], X.x, a);
-                            a = dot4(src[u][1], X.y, a);
-                            a = dot4(src[u][2], X.z, a);
-                            a = dot4(src[u][3], X.w, a);
-                            acc_a[mi] = a;
-                        }
+                        const uint4 X = *reinterpret_cast<const uint4*>(zc + (size_t)mi * tok_bytes);
+                        int a = acc_lo[mi];
+                        a = dot4(src[u][0], X.x, a);
+                        a = dot4(src[u][1], X.y, a);
+                        a = dot4(src[u][2], X.z, a);
+                        a = dot4(src[u][3], X.w, a);
+                        acc_lo[mi] = a;
                     }
                 }
             }
         };
-        v4u32 bufb[kSBatch];
-        for (int i0 = 0; i0 < nsteps; i0 += 2 * kSBatch) {
-            load_batch(bufb, i0 + kSBatch);
-            run_batch(buf, i0);
-            load_batch(buf, i0 + 2 * kSBatch);
-            if (i0 + kSBatch < nsteps) run_batch(bufb, i0 + kSBatch);
+        // Register ring: while batch b is consumed, batches b+1 .. b+kRing-1 are in
+        // flight; loads past this tile's last batch fetch the next tile's first
+        // batches (after the last tile: nothing, they lie past the matrix end).
+        const int nbatches = cur.nsteps / kSBatch;   // a multiple of kRing, at least kRing
+        for (int i0 = 0; i0 < nbatches; i0 += kRing) {
+#pragma unroll
+            for (int s = 0; s < kRing; ++s) {
+                const int b = i0 + s + kRing - 1;
+                const bool mine = b < nbatches;
+                const Tile& src_t = mine ? cur : nxt;
+                const uint32_t vo = mine ? cur.voff : nxt.voff;
+                const int bb = mine ? b : (has_next ? b - nbatches : nbatches + kRing);
+#pragma unroll
+                for (int u = 0; u < kSBatch; ++u)
+                    ring[(s + kRing - 1) % kRing][u] = load_step(src_t, bb * kSBatch + u, vo);
+                __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the batch they overlap
+                run_batch(ring[s], (i0 + s) * kSBatch);
+            }
         }
 
         // ---- combine the L lanes of each row and write the tile --------------------
-        for (int off = R; off < kWave; off <<= 1) {
+        int total[MT];
 #pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                acc_a[mi] += __shfl_xor(acc_a[mi], off, kWave);
-                acc_b[mi] += __shfl_xor(acc_b[mi], off, kWave);
-            }
+        for (int mi = 0; mi < MT; ++mi) total[mi] = acc_lo[mi] + acc_hi[mi];
+        for (int off = kWave >> cur.lshift; off < kWave; off <<= 1) {
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) total[mi] += __shfl_xor(total[mi], off, kWave);
         }
-        if (live && s_part == 0) {
-            const float sw = *gload_ptr(P->sw);
-            const QMV_GLOBAL float* sx = gload_ptr(P->sx);
-            QMV_GLOBAL float* y = gstore_ptr(P->y);
+        int cr[MT];
+#pragma unroll
+        for (int mi = 0; mi < MT; ++mi) cr[mi] = WT == 1 ? corr[mi] : 0;
+        if (cur.row < cur.n && cur.s_part == 0) {
+            QMV_GLOBAL float* y = gstore_ptr(cd.y);
+            int32_t* accp = cd.acc;
+            const float sw = cd.sw;
+            const float sx[2] = {cd.sx[0], cd.sx[1]};
 #pragma unroll
             for (int mi = 0; mi < MT; ++mi) {
-                if (mi < m) {
-                    int total;
-                    if (WT == 1)
-                        total = (int)((uint32_t)acc_a[mi] + 128u * (uint32_t)sum_d0[mi] -
-                                      3u * (uint32_t)acc_b[mi] - (uint32_t)sum_all[mi]);
-                    else
-                        total = acc_a[mi];
-                    const size_t o = (size_t)mi * n + row;
-                    y[o] = (float)total * sx[mi] * sw;
-                    if (P->acc) gstore_ptr(P->acc)[o] = total;
+                if (mi < cur.m) {
+                    const int tot = (int)((uint32_t)total[mi] - (uint32_t)cr[mi]);
+                    const size_t o = (size_t)mi * cur.n + cur.row;
+                    y[o] = (float)tot * sx[mi] * sw;
+                    if (accp) gstore_ptr(accp)[o] = tot;
                 }
             }
         }
-        // the next tile overwrites this wave's LDS slice
-        wave_lds_sync();
+        if (!has_next) break;
+        cur = nxt;
     }
 }
 
 template <int MT, int WT>
-hipError_t launch_stream_one(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
-                             int max_chunks, int cus, hipStream_t s)
+hipError_t launch_stream_one(const DevProblem* probs, uint32_t* sched, int nb, int32_t slot_bytes, hipStream_t s)
 {
-    const int wave_lds = (WT == 1 ? 80 : 16) * (max_chunks + 1) * MT;
-    int waves_per_cu = kStreamWavesPerCU;
-    const int lds_waves = (int)(kMaxLds / (wave_lds > 0 ? wave_lds : 1)) & ~3;
-    if (lds_waves < waves_per_cu) waves_per_cu = lds_waves < 4 ? 4 : lds_waves;
-    int blocks = cus * waves_per_cu / 4;
-    const int max_blocks = (tile_count + 3) / 4;
-    if (blocks > max_blocks) blocks = max_blocks;
-    if (blocks < 1) blocks = 1;
-    const size_t lds = (size_t)wave_lds * 4;
+    const size_t lds = gemv_stream_lds_bytes(MT, slot_bytes);
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((k_gemv_stream<MT, WT>), dim3((unsigned)blocks), dim3(kBlock), lds, s, probs, tiles,
-                       tile_begin, tile_count, wave_lds);
+    hipLaunchKernelGGL((k_gemv_stream<MT, WT>), dim3((unsigned)nb), dim3(kStreamThreads), lds, s, probs, sched,
+                       slot_bytes);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int gemv_stream_lanes_per_row(int chunks)
+int64_t gemv_stream_steps(int chunks, int lanes)
 {
-    return chunks <= 32 ? 1 : chunks <= 64 ? 2 : 4;
+    return ((chunks + lanes - 1) / lanes + kStepGrain - 1) / kStepGrain * kStepGrain;
 }
 
-bool gemv_stream_fits(int wtype, int max_m, int max_chunks)
+int64_t gemv_stream_slot_bytes(int wtype, int mt, int chunks, int lanes)
 {
-    const int mt = max_m <= 1 ? 1 : 2;
-    return max_m <= 2 && (int64_t)(wtype == 1 ? 80 : 16) * (max_chunks + 1) * mt * 4 <= 64 * 1024;
+    return (int64_t)mt * gemv_stream_steps(chunks, lanes) * lanes * (wtype == 1 ? kZBytes : kXBytes);
 }
 
-hipError_t launch_gemv_stream(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
-                              int wtype, int max_m, int max_chunks, hipStream_t s)
+size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes)
 {
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
+    return (size_t)(2 * slot_bytes + 2 * (int64_t)sizeof(TileDesc) + 2 * mt * (int64_t)sizeof(int));
+}
+
+hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,
+                              int32_t slot_bytes, hipStream_t s)
+{
     if (wtype == 1) {
-        if (max_m <= 1) return launch_stream_one<1, 1>(probs, tiles, tile_begin, tile_count, max_chunks, cus, s);
-        return launch_stream_one<2, 1>(probs, tiles, tile_begin, tile_count, max_chunks, cus, s);
+        if (max_m <= 1) return launch_stream_one<1, 1>(probs, sched, nb, slot_bytes, s);
+        return launch_stream_one<2, 1>(probs, sched, nb, slot_bytes, s);
     }
-    if (max_m <= 1) return launch_stream_one<1, 2>(probs, tiles, tile_begin, tile_count, max_chunks, cus, s);
-    return launch_stream_one<2, 2>(probs, tiles, tile_begin, tile_count, max_chunks, cus, s);
+    if (max_m <= 1) return launch_stream_one<1, 2>(probs, sched, nb, slot_bytes, s);
+    return launch_stream_one<2, 2>(probs, sched, nb, slot_bytes, s);
 }
 
 }  // namespace qmv

@@ -45,15 +45,6 @@ constexpr int kBOff = kANBuf * kABuf;     // B ring after the A ring
 constexpr int kEpiOff = kBOff + kANBuf * kBBuf;
 constexpr int kPrefillLds = kEpiOff + 2 * kPBM * 4;   // 161792 bytes of the 163840 per CU
 
-// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0 and vmcnt[5:4] in bits 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // (1024 + P_(j-1), 1024 + P_j) per 16-bit lane -> low byte = P_j - 3 P_(j-1).
 __device__ __forceinline__ uint32_t digit2(uint32_t prev, uint32_t cur)
 {

@@ -41,10 +41,29 @@ __device__ __forceinline__ const QMV_GLOBAL T* gload_ptr(const T* p)
 {
     return (const QMV_GLOBAL T*)p;
 }
+// Read-only for the whole kernel and wave-uniform: the constant address space
+// makes such reads scalar loads (they then never wait behind vector loads).
+#define QMV_CONST __attribute__((address_space(4)))
+template <typename T>
+__device__ __forceinline__ const QMV_CONST T* cload_ptr(const T* p)
+{
+    return (const QMV_CONST T*)p;
+}
 template <typename T>
 __device__ __forceinline__ QMV_GLOBAL T* gstore_ptr(T* p)
 {
     return (QMV_GLOBAL T*)p;
+}
+
+// Wait until at most N vector memory operations of this wave are outstanding
+// (they complete in order); the other counters are left alone.  gfx9
+// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in 6:4,
+// lgkmcnt in 11:8.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Launchers implemented in the kernel translation units.
@@ -58,12 +77,19 @@ int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks);
 constexpr int64_t kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
 hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
                        int wtype, int max_m, int max_chunks, hipStream_t s);
-// Streaming (persistent) GEMV for 1..2 tokens: lanes per row for a row of
-// `chunks` 16-byte chunks, and whether a problem list fits the kernel.
-int gemv_stream_lanes_per_row(int chunks);
-bool gemv_stream_fits(int wtype, int max_m, int max_chunks);
-hipError_t launch_gemv_stream(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin,
-                              int32_t tile_count, int wtype, int max_m, int max_chunks, hipStream_t s);
+// Streaming (persistent) GEMV for 1..2 tokens.  Workgroups are 4 compute
+// waves + 1 staging wave; a workgroup tile is 4 * 64 / lanes_per_row rows of
+// one problem, entry = problem slot << kTileRowBits | row block.  Schedule
+// words (in the workspace, writable): [kStreamHdr words of counters, zero
+// between launches][kStreamXcds x (offset, size)][the XCD tile lists].  LDS =
+// two staged tiles of slot_bytes + a few words.
+constexpr int kStreamXcds = 8;
+constexpr int kStreamHdr = 64 * 2 * kStreamXcds;
+int64_t gemv_stream_steps(int chunks, int lanes);
+int64_t gemv_stream_slot_bytes(int wtype, int mt, int chunks, int lanes);
+size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes);
+hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,
+                              int32_t slot_bytes, hipStream_t s);
 // Prefill (int8 matrix cores): tiles of 256 tokens x 256 rows.
 constexpr int64_t kPrefillTileM = 256;
 constexpr int64_t kPrefillTileN = 256;
