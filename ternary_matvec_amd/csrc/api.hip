@@ -78,7 +78,7 @@ int32_t check_problems(const qmv_problem* probs, int32_t count, int64_t max_m)
 #ifndef QMV_STREAM_WG_PER_CU
 #define QMV_STREAM_WG_PER_CU 4
 #endif
-constexpr int kStreamWgPerCu = QMV_STREAM_WG_PER_CU;   // 16 waves per compute unit
+constexpr int kStreamWgPerCu = QMV_STREAM_WG_PER_CU;   // at most 16 compute waves per compute unit
 constexpr int kStreamMaxM = 2;
 
 struct Table {
@@ -141,18 +141,23 @@ bool schedule_stream(const std::vector<const qmv_problem*>& sp, const std::vecto
         slot = round_up(slot, 16);
         const size_t lds = gemv_stream_lds_bytes(mt, slot);
         if ((int64_t)lds > kMaxLds) continue;
-        const int wg_per_cu = (int)std::min<int64_t>(kStreamWgPerCu, kMaxLds / (int64_t)lds);
+        // resident workgroups per compute unit: the runtime's answer for this
+        // kernel and LDS size, else (no usable device) the LDS bound
+        int wg_per_cu = gemv_stream_wg_per_cu(wtype, mt, slot);
+        if (wg_per_cu <= 0) wg_per_cu = (int)std::min<int64_t>(kStreamWgPerCu, kMaxLds / (int64_t)lds);
+        wg_per_cu = std::min(wg_per_cu, kStreamWgPerCu);
         // workgroup tiles, longest first
         struct Item { double cost; uint32_t entry; };
         std::vector<Item> items;
         for (size_t i = 0; i < sp.size(); ++i) {
             const qmv_problem& p = *sp[i];
             const int c = chunks_of(p);
-            const int64_t rows = 4 * (kRowsPerTile / lanes[i]);
+            const int64_t rows = 4 * (kRowsPerTile / lanes[i]) * kStreamRowsPerLane;
             // chunk steps (an int8 step is a quarter of a ternary one) plus the
             // tile boundary (barrier, epilogue, ring refill), which measures at
             // about six ternary steps
-            const double cost = (double)gemv_stream_steps(c, lanes[i]) * (wtype == 1 ? p.m : 0.3 * p.m) + 6.0;
+            const double cost =
+                ((double)gemv_stream_steps(c, lanes[i]) * (wtype == 1 ? p.m : 0.3 * p.m) + 6.0) * kStreamRowsPerLane;
             const int64_t nt = rows_tiles(p.w.n, rows);
             for (int64_t r = 0; r < nt; ++r)
                 items.push_back({cost, ((uint32_t)slots[i] << kTileRowBits) | (uint32_t)r});

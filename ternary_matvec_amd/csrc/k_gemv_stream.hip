@@ -5,12 +5,13 @@
 // "Gemma 3 1B at 114 tokens per second on a laptop CPU", "Step 1"; cpp20gemma
 // README, "Architecture & implementation"), organised for streaming:
 //
-//  * Work unit = a workgroup tile: 4 * R rows of one problem, one R-row wave
+//  * Work unit = a workgroup tile: 4 * 2R rows of one problem, one 2R-row wave
 //    tile per compute wave.  R = 64 / L, L = lanes per row (1, 2 or 4, chosen
 //    by the host so tiles are of similar length).  Lane s*R + r of a wave
-//    streams chunks s, s + L, s + 2L, ... of row r; for a fixed s the R rows'
-//    chunk is one contiguous run of R * 16 bytes.  The L partial sums of a row
-//    meet through lane shuffles at the end of the tile.
+//    streams chunks s, s + L, s + 2L, ... of rows r and R + r (the two rows
+//    share every activation read); for a fixed s the R rows' chunk is one
+//    contiguous run of R * 16 bytes.  The L partial sums of a row meet through
+//    lane shuffles at the end of the tile.
 //  * Tiles are dealt to the 8 XCDs by the host (longest processing time
 //    first; workgroup b runs on XCD b mod 8).  Inside an XCD's list a
 //    workgroup's first tile is fixed (its rank among the XCD's workgroups) and
@@ -45,15 +46,12 @@
 namespace qmv {
 namespace {
 
-#ifndef QMV_STREAM_BATCH
-#define QMV_STREAM_BATCH 1
-#endif
 #ifndef QMV_STREAM_RING
 #define QMV_STREAM_RING 4
 #endif
-constexpr int kSBatch = QMV_STREAM_BATCH;      // chunks per register batch
-constexpr int kRing = QMV_STREAM_RING;         // batches in the register ring: kRing - 1 in flight
-constexpr int kStepGrain = kSBatch * kRing;    // chunk steps of a tile are a multiple of this
+constexpr int kRPL = kStreamRowsPerLane;       // rows per lane: they share each staged activation read
+constexpr int kRing = QMV_STREAM_RING;         // chunk steps in the register ring: kRing - 1 in flight
+constexpr int kStepGrain = kRing;              // chunk steps of a tile are a multiple of this
 constexpr int kComputeWaves = 4;
 constexpr int kStreamThreads = (kComputeWaves + 1) * kWave;   // + the staging wave
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
@@ -122,8 +120,9 @@ struct Tile {
     const uint8_t* w;
     int n, k, m, C, lshift, wb, nsteps, cpad, tok_bytes;
     uint32_t chunk_bytes;   // n * 16: one chunk of every row
-    int s_part, row;        // per lane (compute waves)
-    uint32_t voff;          // per lane: byte offset of its row's chunk s_part
+    int s_part, row;        // per lane (compute waves): its first row (the second is row + R)
+    uint32_t voff;          // per lane: byte offset of its first row's chunk s_part
+    uint32_t voff_r;        // R rows of one chunk: the second row's offset is voff + voff_r
 };
 
 // The part of a tile the compute waves use, as the staging wave leaves it in
@@ -150,8 +149,9 @@ __device__ __forceinline__ void tile_derive(Tile& T, int wave, int lane)
     T.tok_bytes = T.cpad * CB;
     T.chunk_bytes = (uint32_t)T.n * 16u;
     T.s_part = lane >> rshift;
-    T.row = ((T.wb * kComputeWaves + wave) << rshift) + (lane & ((1 << rshift) - 1));
+    T.row = (((T.wb * kComputeWaves + wave) * kRPL) << rshift) + (lane & ((1 << rshift) - 1));
     T.voff = (uint32_t)((T.s_part * T.n + T.row) * 16);
+    T.voff_r = 16u << rshift;
 }
 
 template <int CB>
@@ -381,11 +381,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
 
     // ---- compute waves ----------------------------------------------------------------
     Tile cur = tile_at<kCB>(probs, te0, wave, lane);
-    v4u32 ring[kRing][kSBatch];
+    v4u32 ring[kRing][kRPL];
 #pragma unroll
     for (int r = 0; r + 1 < kRing; ++r)
 #pragma unroll
-        for (int u = 0; u < kSBatch; ++u) ring[r][u] = load_step(cur, r * kSBatch + u, cur.voff);
+        for (int h = 0; h < kRPL; ++h) ring[r][h] = load_step(cur, r, cur.voff + h * cur.voff_r);
 
     for (int par = 0;; par ^= 1) {
         __syncthreads();   // this tile is staged and the next one named; every wave is done with the last
@@ -398,104 +398,113 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
         const uint8_t* zs = smem + (size_t)par * slot_bytes;
         const int* corr = corr_base + par * MT;
 
-        int acc_lo[MT], acc_hi[MT];
+        int acc_lo[kRPL][MT], acc_hi[kRPL][MT];
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-            acc_lo[mi] = 0;
-            acc_hi[mi] = 0;
-        }
+        for (int h = 0; h < kRPL; ++h)
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) {
+                acc_lo[h][mi] = 0;
+                acc_hi[h][mi] = 0;
+            }
         const uint8_t* zlane = zs + cur.s_part * kCB;
         const int zstep = kCB << cur.lshift;
         const int tok_bytes = cur.tok_bytes;
-        auto run_batch = [&](const v4u32* src, int i0) {
+        // one chunk step: the weight chunk of each of the lane's rows against the
+        // staged activations of that chunk
+        auto run_step = [&](const v4u32* src, int i) {
+            const uint8_t* zc = zlane + i * zstep;
+            if (WT == 1) {
 #pragma unroll
-            for (int u = 0; u < kSBatch; ++u) {
-                const uint8_t* zc = zlane + (i0 + u) * zstep;
-                if (WT == 1) {
+                for (int j = 0; j < 4; ++j) {
+                    uint4 Z[MT][3];   // the 10 Z pairs of dword j (and two pad words)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        uint4 Z[MT][3];   // the 10 Z pairs of dword j (and two pad words)
+                    for (int mi = 0; mi < MT; ++mi)
 #pragma unroll
-                        for (int mi = 0; mi < MT; ++mi)
+                        for (int q = 0; q < 3; ++q)
+                            Z[mi][q] = reinterpret_cast<const uint4*>(zc + (size_t)mi * tok_bytes + 48 * j)[q];
 #pragma unroll
-                            for (int q = 0; q < 3; ++q)
-                                Z[mi][q] = reinterpret_cast<const uint4*>(zc + (size_t)mi * tok_bytes + 48 * j)[q];
+                    for (int h = 0; h < kRPL; ++h) {
                         constexpr uint32_t mag = 0x64646464u;
-                        uint32_t lo = __builtin_amdgcn_perm(mag, src[u][j], 0x04020400u);   // 1024 + b0 | b2
-                        uint32_t hi = __builtin_amdgcn_perm(mag, src[u][j], 0x04030401u);   // 1024 + b1 | b3
+                        uint32_t lo = __builtin_amdgcn_perm(mag, src[h][j], 0x04020400u);   // 1024 + b0 | b2
+                        uint32_t hi = __builtin_amdgcn_perm(mag, src[h][j], 0x04030401u);   // 1024 + b1 | b3
 #pragma unroll
-                        for (int i = 4; i >= 0; --i) {   // P_5 = b, then P_4 .. P_1
+                        for (int i5 = 4; i5 >= 0; --i5) {   // P_5 = b, then P_4 .. P_1
 #pragma unroll
                             for (int mi = 0; mi < MT; ++mi) {
-                                acc_lo[mi] = dot2(lo, sel(Z[mi][i >> 1], (2 * i) & 3), acc_lo[mi]);
-                                acc_hi[mi] = dot2(hi, sel(Z[mi][i >> 1], (2 * i + 1) & 3), acc_hi[mi]);
+                                acc_lo[h][mi] = dot2(lo, sel(Z[mi][i5 >> 1], (2 * i5) & 3), acc_lo[h][mi]);
+                                acc_hi[h][mi] = dot2(hi, sel(Z[mi][i5 >> 1], (2 * i5 + 1) & 3), acc_hi[h][mi]);
                             }
-                            if (i > 0) {
+                            if (i5 > 0) {
                                 lo = third2(lo);
                                 hi = third2(hi);
                             }
                         }
-                        // one dword at a time: other waves hide the latency, and
-                        // short live ranges leave room for the ring
-                        __builtin_amdgcn_sched_barrier(0);
                     }
-                } else {
+                    // one dword at a time: other waves hide the latency, and short
+                    // live ranges leave room for the ring
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
 #pragma unroll
-                    for (int mi = 0; mi < MT; ++mi) {
-                        const uint4 X = *reinterpret_cast<const uint4*>(zc + (size_t)mi * tok_bytes);
-                        int a = acc_lo[mi];
-                        a = dot4(src[u][0], X.x, a);
-                        a = dot4(src[u][1], X.y, a);
-                        a = dot4(src[u][2], X.z, a);
-                        a = dot4(src[u][3], X.w, a);
-                        acc_lo[mi] = a;
+                for (int mi = 0; mi < MT; ++mi) {
+                    const uint4 X = *reinterpret_cast<const uint4*>(zc + (size_t)mi * tok_bytes);
+#pragma unroll
+                    for (int h = 0; h < kRPL; ++h) {
+                        int a = acc_lo[h][mi];
+                        a = dot4(src[h][0], X.x, a);
+                        a = dot4(src[h][1], X.y, a);
+                        a = dot4(src[h][2], X.z, a);
+                        a = dot4(src[h][3], X.w, a);
+                        acc_lo[h][mi] = a;
                     }
                 }
             }
         };
-        // Register ring: while batch b is consumed, batches b+1 .. b+kRing-1 are in
-        // flight; loads past this tile's last batch fetch the next tile's first
-        // batches (after the last tile: nothing, they lie past the matrix end).
-        const int nbatches = cur.nsteps / kSBatch;   // a multiple of kRing, at least kRing
-        for (int i0 = 0; i0 < nbatches; i0 += kRing) {
+        // Register ring: while step i is consumed, steps i+1 .. i+kRing-1 are in
+        // flight; loads past this tile's last step fetch the next tile's first
+        // steps (after the last tile: nothing, they lie past the matrix end).
+        const int nsteps = cur.nsteps;   // a multiple of kRing, at least kRing
+        for (int i0 = 0; i0 < nsteps; i0 += kRing) {
 #pragma unroll
             for (int s = 0; s < kRing; ++s) {
                 const int b = i0 + s + kRing - 1;
-                const bool mine = b < nbatches;
+                const bool mine = b < nsteps;
                 const Tile& src_t = mine ? cur : nxt;
                 const uint32_t vo = mine ? cur.voff : nxt.voff;
-                const int bb = mine ? b : (has_next ? b - nbatches : nbatches + kRing);
+                const uint32_t vr = mine ? cur.voff_r : nxt.voff_r;
+                const int bb = mine ? b : (has_next ? b - nsteps : nsteps + kRing);
 #pragma unroll
-                for (int u = 0; u < kSBatch; ++u)
-                    ring[(s + kRing - 1) % kRing][u] = load_step(src_t, bb * kSBatch + u, vo);
-                __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the batch they overlap
-                run_batch(ring[s], (i0 + s) * kSBatch);
+                for (int h = 0; h < kRPL; ++h) ring[(s + kRing - 1) % kRing][h] = load_step(src_t, bb, vo + h * vr);
+                __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the step they overlap
+                run_step(ring[s], i0 + s);
             }
         }
 
         // ---- combine the L lanes of each row and write the tile --------------------
-        int total[MT];
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi) total[mi] = acc_lo[mi] + acc_hi[mi];
-        for (int off = kWave >> cur.lshift; off < kWave; off <<= 1) {
-#pragma unroll
-            for (int mi = 0; mi < MT; ++mi) total[mi] += __shfl_xor(total[mi], off, kWave);
-        }
         int cr[MT];
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) cr[mi] = WT == 1 ? corr[mi] : 0;
-        if (cur.row < cur.n && cur.s_part == 0) {
-            QMV_GLOBAL float* y = gstore_ptr(cd.y);
-            int32_t* accp = cd.acc;
-            const float sw = cd.sw;
-            const float sx[2] = {cd.sx[0], cd.sx[1]};
 #pragma unroll
-            for (int mi = 0; mi < MT; ++mi) {
-                if (mi < cur.m) {
-                    const int tot = (int)((uint32_t)total[mi] - (uint32_t)cr[mi]);
-                    const size_t o = (size_t)mi * cur.n + cur.row;
-                    y[o] = (float)tot * sx[mi] * sw;
-                    if (accp) gstore_ptr(accp)[o] = tot;
+        for (int h = 0; h < kRPL; ++h) {
+            int total[MT];
+#pragma unroll
+            for (int mi = 0; mi < MT; ++mi) total[mi] = acc_lo[h][mi] + acc_hi[h][mi];
+            for (int off = kWave >> cur.lshift; off < kWave; off <<= 1) {
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi) total[mi] += __shfl_xor(total[mi], off, kWave);
+            }
+            const int row = cur.row + (h << (6 - cur.lshift));
+            if (row < cur.n && cur.s_part == 0) {
+                QMV_GLOBAL float* y = gstore_ptr(cd.y);
+                int32_t* accp = cd.acc;
+#pragma unroll
+                for (int mi = 0; mi < MT; ++mi) {
+                    if (mi < cur.m) {
+                        const int tot = (int)((uint32_t)total[mi] - (uint32_t)cr[mi]);
+                        const size_t o = (size_t)mi * cur.n + row;
+                        y[o] = (float)tot * cd.sx[mi] * cd.sw;
+                        if (accp) gstore_ptr(accp)[o] = tot;
+                    }
                 }
             }
         }
@@ -533,6 +542,27 @@ int64_t gemv_stream_slot_bytes(int wtype, int mt, int chunks, int lanes)
 size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes)
 {
     return (size_t)(2 * slot_bytes + 2 * (int64_t)sizeof(TileDesc) + 2 * mt * (int64_t)sizeof(int));
+}
+
+template <int MT, int WT>
+int occupancy_one(int64_t slot_bytes)
+{
+    const size_t lds = gemv_stream_lds_bytes(MT, slot_bytes);
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
+                                                     kStreamThreads, lds) != hipSuccess)
+        return 0;
+    return n;
+}
+
+int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes)
+{
+    if (wtype == 1) return max_m <= 1 ? occupancy_one<1, 1>(slot_bytes) : occupancy_one<2, 1>(slot_bytes);
+    return max_m <= 1 ? occupancy_one<1, 2>(slot_bytes) : occupancy_one<2, 2>(slot_bytes);
 }
 
 hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,

@@ -78,16 +78,23 @@ constexpr int64_t kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
 hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
                        int wtype, int max_m, int max_chunks, hipStream_t s);
 // Streaming (persistent) GEMV for 1..2 tokens.  Workgroups are 4 compute
-// waves + 1 staging wave; a workgroup tile is 4 * 64 / lanes_per_row rows of
-// one problem, entry = problem slot << kTileRowBits | row block.  Schedule
+// waves + 1 staging wave; a workgroup tile is 4 * 64 / lanes_per_row *
+// kStreamRowsPerLane rows of one problem, entry = problem slot << kTileRowBits | row block.  Schedule
 // words (in the workspace, writable): [kStreamHdr words of counters, zero
 // between launches][kStreamXcds x (offset, size)][the XCD tile lists].  LDS =
 // two staged tiles of slot_bytes + a few words.
 constexpr int kStreamXcds = 8;
+#ifndef QMV_STREAM_RPL
+#define QMV_STREAM_RPL 2
+#endif
+constexpr int kStreamRowsPerLane = QMV_STREAM_RPL;   // a workgroup tile is 4 * 64 / lanes_per_row * this rows
 constexpr int kStreamHdr = 64 * 2 * kStreamXcds;
 int64_t gemv_stream_steps(int chunks, int lanes);
 int64_t gemv_stream_slot_bytes(int wtype, int mt, int chunks, int lanes);
 size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes);
+// Workgroups of the streaming kernel resident per compute unit (registers and
+// LDS), 0 if it cannot run or no device is usable.
+int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes);
 hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,
                               int32_t slot_bytes, hipStream_t s);
 // Prefill (int8 matrix cores): tiles of 256 tokens x 256 rows.
