@@ -44,6 +44,7 @@ constexpr int kBBuf = 4 * 2 * 64 * 16;    // one staged B buffer: wave x row blo
 constexpr int kBOff = kANBuf * kABuf;     // B ring after the A ring
 constexpr int kEpiOff = kBOff + kANBuf * kBBuf;
 constexpr int kPrefillLds = kEpiOff + 2 * kPBM * 4;   // 161792 bytes of the 163840 per CU
+constexpr int kParkPitch = kPBN + 4;      // parked row pitch (ints): 16-byte rows, token rows 4 banks apart
 
 // (1024 + P_(j-1), 1024 + P_j) per 16-bit lane -> low byte = P_j - 3 P_(j-1).
 __device__ __forceinline__ uint32_t digit2(uint32_t prev, uint32_t cur)
@@ -174,79 +175,132 @@ __global__ __launch_bounds__(kBlock, 1) void k_prefill(const DevProblem* __restr
             }
         }
     };
-    // Wait for the loads of step s+1.  Per step the issue order is A(s+2) (11)
-    // then B(s+2) (2), after A(s+1), B(s+1) of the previous step, so when the
-    // s+2 loads are out everything but the newest 13 has landed at vmcnt(13).
-    auto wait_next = [&](bool s2_issued) {
-        if (s2_issued) {
-            if (fast) wait_vmcnt<kSlots + 2>();
-            else wait_vmcnt<2>();   // the A path without DMA issues only the 2 B loads
-        } else {
-            wait_vmcnt<0>();
-        }
-    };
-
     v16i32 acc[8][2];
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = v16i32{};
 
-    // prologue: steps 0 and 1 in flight, wait for step 0
-    stage_a(0, 0);
+    // Digits of step s: this lane's 16 packed bytes of each row block (braw, read
+    // from the B ring) -> 5 B operands of 16 natural-order digits each.  Work is
+    // split in parts so it can ride along the MFMAs: part j (0..3) expands dword j
+    // of both row blocks, part 4 assembles the operands (zero past column k).
+    uint32_t nat[2][20];
+    auto read_b = [&](int buf, v4u32 (&braw)[2]) {
+        const uint8_t* bbuf = smem + kBOff + buf * kBBuf;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+            braw[nb] = *reinterpret_cast<const v4u32*>(bbuf + 1024 * (2 * wave + nb) + 16 * lane);
+    };
+    auto digits_part = [&](int s, const v4u32 (&braw)[2], int part, v4i32 (&bop)[2][5]) {
+        if (part < 4) {
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][part], nat[nb] + 5 * part);
+        } else {
+            const int cbase = 80 * (2 * s + g);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int i = 0; i < 5; ++i) {
+                    const bool on = cbase + 16 * i < k;   // columns past k (and chunks past the row) add 0
+                    bop[nb][i] = on ? v4i32{(int)nat[nb][4 * i], (int)nat[nb][4 * i + 1], (int)nat[nb][4 * i + 2],
+                                            (int)nat[nb][4 * i + 3]}
+                                    : v4i32{0, 0, 0, 0};
+                }
+        }
+    };
+
+    // Pipeline: at step s the MFMAs use A(s) (LDS) and the digits of B(s)
+    // (registers, expanded during step s-1, assembled into operands at its end),
+    // while the digits of B(s+1) are expanded and the loads of step s+2 fly.  Issue order per step is B then A,
+    // so "B(s+2) and everything older has landed" is vmcnt(A loads of one step).
     stage_b(0, 0);
-    const bool two = steps > 1;
-    if (two) {
-        stage_a(1, 1);
+    stage_a(0, 0);
+    if (steps > 1) {
         stage_b(1, 1);
+        stage_a(1, 1);
     }
-    wait_next(two);
+    wait_vmcnt<0>();
     __syncthreads();
     sum_a(0, 0);
+    v4i32 bop[2][5];
+    {
+        v4u32 braw[2];
+        read_b(0, braw);
+#pragma unroll
+        for (int part = 0; part < 5; ++part) digits_part(0, braw, part, bop);
+    }
 
     for (int s = 0; s < steps; ++s) {
         const int buf = s % kANBuf;
         const bool more = s + 1 < steps;
         const bool more2 = s + 2 < steps;
-        // this step's B chunk of each row block, expanded to natural-order digits
-        v4i32 bop[2][5];
-        {
-            const uint8_t* bbuf = smem + kBOff + buf * kBBuf;
-            const int cbase = 80 * (2 * s + g);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const v4u32 braw = *reinterpret_cast<const v4u32*>(bbuf + 1024 * (2 * wave + nb) + 16 * lane);
-                uint32_t nat[20];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) natural_digits(braw[j], nat + 5 * j);
-#pragma unroll
-                for (int i = 0; i < 5; ++i) {
-                    const bool on = cbase + 16 * i < k;   // columns past k (and chunks past the row) add 0
-                    bop[nb][i] = on ? v4i32{(int)nat[4 * i], (int)nat[4 * i + 1], (int)nat[4 * i + 2], (int)nat[4 * i + 3]}
-                                    : v4i32{0, 0, 0, 0};
-                }
-            }
-        }
         if (more2) {
-            stage_a(s + 2, (s + 2) % kANBuf);
             stage_b(s + 2, (s + 2) % kANBuf);
+            stage_a(s + 2, (s + 2) % kANBuf);
         }
         // Plane-outer order: each accumulator is touched once per plane, so 16
-        // independent MFMAs separate two that depend on each other.
+        // independent MFMAs separate two that depend on each other.  The A
+        // operands of plane i+1 are read from LDS and a fifth of the next step's
+        // digit expansion is done while plane i's MFMAs run (one wave per SIMD:
+        // nothing else would hide the LDS latency or fill the MFMA pipe).
+        // the next step's packed weights (stale data after the last step: expanded
+        // and never used, which keeps the MFMA block free of branches)
+        v4u32 bnext[2];
+        read_b((s + 1) % kANBuf, bnext);
         const uint8_t* arow = smem + buf * kABuf + l32 * kARow + 80 * g;
+        // A operands in half planes (4 token blocks): the next half's reads fly
+        // while the current half's 8 MFMAs run
+        v4i32 aop[2][4];
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            v4i32 aop[8];
+        for (int mb = 0; mb < 4; ++mb) aop[0][mb] = *reinterpret_cast<const v4i32*>(arow + 32 * mb * kARow);
+        auto plane = [&](int i) {
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) aop[mb] = *reinterpret_cast<const v4i32*>(arow + 32 * mb * kARow + 16 * i);
+            for (int h = 0; h < 2; ++h) {
+                const int hs = 2 * i + h;                 // half-plane index 0..9
+                if (hs + 1 < 10) {
+                    const int ni = (hs + 1) >> 1, nh = (hs + 1) & 1;
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) {
-                acc[mb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[mb], bop[0][i], acc[mb][0], 0, 0, 0);
-                acc[mb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[mb], bop[1][i], acc[mb][1], 0, 0, 0);
+                    for (int mb = 0; mb < 4; ++mb)
+                        aop[(hs + 1) & 1][mb] =
+                            *reinterpret_cast<const v4i32*>(arow + 32 * (4 * nh + mb) * kARow + 16 * ni);
+                }
+                if (h == 0 && i < 4) {
+                    digits_part(s + 1, bnext, i, bop);
+                    // keep this part's work here, among the MFMAs (the compiler
+                    // would otherwise sink it to the end of the step)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        asm volatile("" ::"v"(nat[nb][5 * i]), "v"(nat[nb][5 * i + 1]), "v"(nat[nb][5 * i + 2]),
+                                     "v"(nat[nb][5 * i + 3]), "v"(nat[nb][5 * i + 4]));
+                }
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    const int tb = 4 * h + mb;
+                    acc[tb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[hs & 1][mb], bop[0][i], acc[tb][0], 0, 0, 0);
+                    acc[tb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[hs & 1][mb], bop[1][i], acc[tb][1], 0, 0, 0);
+                }
+                // one MFMA (its operands were read a half plane ago), then the next
+                // half's LDS reads, then one MFMA per few VALU ops
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+#pragma unroll
+                for (int q = 1; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-        }
+        };
+#pragma unroll
+        for (int i = 0; i < 5; ++i) plane(i);
+        // the next step's operands replace this step's once its MFMAs are issued
+        digits_part(s + 1, bnext, 4, bop);
         if (more) {
-            wait_next(more2);
+            // A(s+1) and B(s+2) have landed once only A(s+2) may still fly
+            if (more2 && fast) wait_vmcnt<kSlots>();
+            else wait_vmcnt<0>();
             __syncthreads();
             sum_a(s + 1, (s + 1) % kANBuf);
         }
@@ -263,33 +317,63 @@ __global__ __launch_bounds__(kBlock, 1) void k_prefill(const DevProblem* __restr
         tscale[tid] = tok < mtok ? gload_ptr(P->sx)[tok] * sw : 0.0f;
     }
     __syncthreads();
+    // The tile leaves through LDS, 128 tokens at a time: the exact sums (acc
+    // minus the token's digit offset) are parked as [token][row] and written out
+    // as whole 1 KB token rows with 16-byte stores, y = sum * sx * sw (long
+    // contiguous writes instead of 128-byte pieces per accumulator register).
     QMV_GLOBAL float* y = gstore_ptr(P->y);
     QMV_GLOBAL int32_t* accout = P->acc ? gstore_ptr(P->acc) : nullptr;
+    const bool vec = ((reinterpret_cast<uintptr_t>(P->y) & 15) == 0) && ((n & 3) == 0) &&
+                     (!P->acc || (reinterpret_cast<uintptr_t>(P->acc) & 15) == 0);
+    int* park = reinterpret_cast<int*>(smem);   // [128][kParkPitch]
+    static_assert(128 * kParkPitch * 4 <= kEpiOff, "parking fits below the token sums");
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb) {
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            // rows ml .. ml+3 of this lane's accumulator registers 4*q4 .. 4*q4+3
-            const int ml = 32 * mb + 8 * q4 + 4 * g;
-            const int4 ts = *reinterpret_cast<const int4*>(tsum + ml);
-            const float4 sc = *reinterpret_cast<const float4*>(tscale + ml);
-            const int tsv[4] = {ts.x, ts.y, ts.z, ts.w};
-            const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+        for (int mh = 0; mh < 4; ++mh) {
+            const int mb = 4 * half + mh;
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int r = n0 + 64 * wave + 32 * nb + l32;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int ml = 32 * mb + 8 * q4 + 4 * g;   // tile token of register 4*q4 (+e)
+                const int4 ts = *reinterpret_cast<const int4*>(tsum + ml);
+                const int tsv[4] = {ts.x, ts.y, ts.z, ts.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tok = m0 + ml + e;
-                    if (r < n && tok < mtok) {
-                        const int total = acc[mb][nb][4 * q4 + e] - tsv[e];
-                        const size_t o = (size_t)tok * n + r;
-                        y[o] = (float)total * scv[e];
-                        if (accout) accout[o] = total;
+                for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        park[(ml + e - 128 * half) * kParkPitch + 64 * wave + 32 * nb + l32] =
+                            acc[mb][nb][4 * q4 + e] - tsv[e];
+            }
+        }
+        __syncthreads();
+        for (int it = 0; it < 128 / 4; ++it) {
+            const int tl = 4 * it + wave;                  // token within the half
+            const int tok = m0 + 128 * half + tl;
+            const int r = n0 + 4 * lane;
+            if (tok < mtok && r < n) {
+                const int4 v = *reinterpret_cast<const int4*>(park + tl * kParkPitch + 4 * lane);
+                const float sc = tscale[128 * half + tl];
+                const size_t o = (size_t)tok * n + r;
+                if (vec && r + 3 < n) {
+                    *reinterpret_cast<QMV_GLOBAL v4u32*>(y + o) =
+                        v4u32{__float_as_uint((float)v.x * sc), __float_as_uint((float)v.y * sc),
+                              __float_as_uint((float)v.z * sc), __float_as_uint((float)v.w * sc)};
+                    if (accout)
+                        *reinterpret_cast<QMV_GLOBAL v4u32*>(accout + o) =
+                            v4u32{(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+                } else {
+                    const int vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        if (r + e < n) {
+                            y[o + e] = (float)vv[e] * sc;
+                            if (accout) accout[o + e] = vv[e];
+                        }
                     }
                 }
             }
         }
+        __syncthreads();
     }
 }
 
