@@ -349,15 +349,16 @@ int32_t check_prefill(const qmv_problem* probs, int32_t count)
 
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
-// Workspace of a prefill problem list: the problem table and the XCD-ordered
-// tile list (8 lists padded to the longest, bounded by 8 x all tiles).
+// Workspace of a prefill problem list: the problem table, the XCD-ordered
+// tile list (8 lists padded to the longest, bounded by 8 x all tiles) and a
+// block of zeros the kernel copies for activation columns past k.
 int64_t prefill_table_bytes(const qmv_problem* probs, int32_t count)
 {
     int64_t tiles = 0;
     for (int32_t i = 0; i < count; ++i) tiles += prefill_tiles(probs[i].m, probs[i].w.n);
     // no XCD list can be longer than all tiles together
     const int64_t bound = kXcds * tiles;
-    return round_up((int64_t)sizeof(DevProblem) * count, 256) + round_up(bound * 8, 256);
+    return round_up((int64_t)sizeof(DevProblem) * count, 256) + round_up(bound * 8, 256) + kPrefillZeroBytes;
 }
 
 }  // namespace
@@ -546,7 +547,7 @@ int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspac
     size_t longest = 0;
     for (const auto& l : lists) longest = std::max(longest, l.size());
     const int64_t grid = (int64_t)longest * kXcds;
-    if (pbytes + grid * 8 > need) return QMV_EWORKSPACE;  // cannot happen: need covers 8 x all tiles
+    if (pbytes + grid * 8 > need - kPrefillZeroBytes) return QMV_EWORKSPACE;  // cannot happen: need covers 8 x all tiles
     uint64_t* te = reinterpret_cast<uint64_t*>(img.data() + pbytes);
     for (int64_t b = 0; b < grid; ++b) {
         const auto& l = lists[b % kXcds];
@@ -560,7 +561,8 @@ int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspac
     }
     const uint8_t* base = static_cast<const uint8_t*>(workspace);
     return hip_status(launch_prefill(reinterpret_cast<const DevProblem*>(base),
-                                     reinterpret_cast<const uint64_t*>(base + pbytes), grid, s));
+                                     reinterpret_cast<const uint64_t*>(base + pbytes), grid,
+                                     reinterpret_cast<const int8_t*>(base + need - kPrefillZeroBytes), s));
 }
 
 int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k)

@@ -6,21 +6,29 @@
 // prompt token through each weight matrix in one pass; cpp20gemma README,
 // "Architecture & implementation": scales applied once after the dot).
 //
-// Work: a workgroup (4 waves) owns a 256-token x 256-row tile of one problem;
-// wave w owns rows 64w..64w+63 (two 32-row blocks) for all 256 tokens (eight
-// 32-token blocks): 16 accumulators of v_mfma_i32_32x32x32_i8.  The K loop
-// advances two 16-byte chunks (160 columns) per step.
-//  * A (activations, natural column order): the step's 256 x 160 tile is
-//    copied HBM -> LDS with global_load_lds_dwordx4 (no registers), double
-//    buffered; operand i of lane (m, g) is columns 80g + 16i .. +15 of row m.
-//  * B (weights): lane (r = lane % 32, g = lane / 32) loads chunk 2s+g of its
-//    row and expands the 16 packed bytes into 80 digits d = t + 1 in natural
-//    column order, in registers: floor(b/3^j) by the packed-fp16 chain of
-//    unpack.hpp, digit j = P_(5-j) - 3 P_(4-j) by one packed 16-bit
-//    multiply-add per two bytes, then byte permutes into column order.
-//  * 5 MFMAs per (token block, row block) cover the 160 columns.  Because the
+// Work: a workgroup (4 waves) owns a 128-token x 256-row tile of one problem;
+// wave w owns rows 64w..64w+63 (two 32-row blocks) for all 128 tokens (four
+// 32-token blocks): 8 accumulators of v_mfma_i32_32x32x32_i8 in 128 registers.
+// Two workgroups share a compute unit (registers and LDS are sized for it), so
+// the output stores of one drain while the matrix cores run the other.  The K
+// loop advances two 16-byte chunks (160 columns) per step.
+//  * Weights are the MFMA B operand (rows): lane (r = lane % 32, g = lane / 32)
+//    takes chunk 2s+g of its row, HBM -> LDS (two-step ring) -> registers, and
+//    expands its 16 packed bytes into 80 digits d = t + 1 in natural column
+//    order, one packed dword per plane just ahead of the plane that uses it:
+//    floor(b/3^j) by the packed-fp16 chain of unpack.hpp, digit j = P_(5-j) -
+//    3 P_(4-j) by one packed 16-bit multiply-add per two bytes, then byte
+//    permutes into column order.
+//  * Activations are the A operand (tokens): the step's 128 x 160 tile goes
+//    HBM -> LDS (three-step ring) with global_load_lds_dwordx4, no registers.
+//    Columns at or past k are copied from a block of zeros, so whatever digits
+//    meet them (row padding, clamped chunks) add nothing.
+//  * 5 MFMAs per (row block, token block) cover the 160 columns.  Because the
 //    digits are t + 1, the epilogue subtracts sum_c x8[m][c], summed from the
-//    staged tile.  Columns at or past k meet zeroed B operands.
+//    staged tiles.
+//  * C = activations x digits^T: a register of the accumulators holds, per
+//    half-wave, 32 consecutive outputs of one token; the epilogue stores whole
+//    128-byte lines straight from the registers.
 // Operand layout of v_mfma_i32_32x32x32_i8 (checked on the hardware): A row =
 // B column = lane % 32, lanes 32..63 hold the second 16 K-bytes; accumulator
 // register i of lane l is row 8*(i/4) + 4*(l/32) + i%4, column l % 32.
@@ -34,17 +42,51 @@ typedef int v4i32 __attribute__((ext_vector_type(4)));
 typedef int v16i32 __attribute__((ext_vector_type(16)));
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kPBM = 256;                 // tokens per tile
-constexpr int kPBN = 256;                 // rows per tile (64 per wave)
-constexpr int kSlots = 11;                // 16-byte slots per staged token row (10 used)
-constexpr int kARow = 16 * kSlots;        // 176 bytes: odd number of 16-byte units
-constexpr int kABuf = kPBM * kARow;       // one staged A buffer (45056 bytes)
-constexpr int kANBuf = 3;                 // staged buffers (two steps in flight)
-constexpr int kBBuf = 4 * 2 * 64 * 16;    // one staged B buffer: wave x row block x lane x 16 bytes
-constexpr int kBOff = kANBuf * kABuf;     // B ring after the A ring
-constexpr int kEpiOff = kBOff + kANBuf * kBBuf;
-constexpr int kPrefillLds = kEpiOff + 2 * kPBM * 4;   // 161792 bytes of the 163840 per CU
-constexpr int kParkPitch = kPBN + 4;      // parked row pitch (ints): 16-byte rows, token rows 4 banks apart
+constexpr int kPBM = (int)kPrefillTileM;  // tokens per tile (128)
+constexpr int kPBN = (int)kPrefillTileN;  // rows per tile (256, 64 per wave)
+constexpr int kPieces = 10;               // 16-byte pieces per staged token row (160 columns)
+constexpr int kARow = 16 * kPieces;       // 160 bytes, rows 8..15 of each 16 rotated by one piece
+constexpr int kABuf = kPBM * kARow;       // one staged activation buffer (20480 bytes)
+constexpr int kANBuf = 3;                 // activation ring: the step in use + two in flight
+constexpr int kADma = kABuf / (16 * kBlock);   // activation copies per wave per step (5)
+constexpr int kBBuf = 4 * 2 * 64 * 16;    // one staged weight buffer: wave x row block x lane x 16 bytes
+constexpr int kBNBuf = 2;                 // weight ring: read into registers one step ahead
+constexpr int kBOff = kANBuf * kABuf;
+constexpr int kEpiOff = kBOff + kBNBuf * kBBuf;
+constexpr int kPrefillLds = kEpiOff + 3 * kPBM * 4;   // + token sums (two halves) and scales: 79360 bytes
+static_assert(kADma * 16 * kBlock == kABuf, "activation tile splits evenly over the copies");
+static_assert(2 * kPrefillLds <= 160 * 1024, "two workgroups per compute unit");
+
+// Byte offset of 16-byte piece p (0..9) of staged token row r.  Rows 8..15 of
+// every 16 are rotated by one piece, so 16 lanes reading one piece of 16
+// consecutive rows cover all 64 banks.
+__device__ __forceinline__ int apos(int r, int p)
+{
+    const int q = p + ((r >> 3) & 1);
+    return r * kARow + 16 * (q >= kPieces ? q - kPieces : q);
+}
+
+// Workgroup barrier for LDS hand-offs that leaves this wave's copies into LDS
+// in flight: it waits only for the wave's own LDS (and scalar) accesses; the
+// copies a hand-off depends on are waited for explicitly (wait_vmcnt) before
+// it.  The memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// HBM -> LDS copy of 16 bytes per lane: lane i's bytes land at lds + 16 i (lds
+// wave-uniform).  Issued as inline assembly so that the compiler's wait-count
+// pass does not track it: it would wait for every copy in flight before each
+// later LDS read, which allows no copy to overlap a step.  The kernel waits for
+// these copies itself (wait_vmcnt) before the barrier that hands them over.
+// M0 is written here; this kernel has no other use of it (LDS instructions do
+// not read it on gfx9 and later).
+__device__ __forceinline__ void copy16_to_lds(const void QMV_GLOBAL* src, const uint8_t* lds)
+{
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(a) : "memory");
+}
 
 // (1024 + P_(j-1), 1024 + P_j) per 16-bit lane -> low byte = P_j - 3 P_(j-1).
 __device__ __forceinline__ uint32_t digit2(uint32_t prev, uint32_t cur)
@@ -55,7 +97,7 @@ __device__ __forceinline__ uint32_t digit2(uint32_t prev, uint32_t cur)
 
 // One packed dword (20 trits, columns 0..19 relative) -> five dwords of
 // digits d = t + 1 in natural column order: nat[u] holds columns 4u .. 4u+3.
-__device__ __forceinline__ void natural_digits(uint32_t w, uint32_t nat[5])
+__device__ __forceinline__ void natural_digits(uint32_t w, uint32_t* nat)
 {
     const uint32_t mag = 0x64646464u;
     const uint32_t lo = __builtin_amdgcn_perm(mag, w, 0x04020400u);  // [b0 64 b2 64]
@@ -91,8 +133,9 @@ __device__ __forceinline__ uint32_t x_bytes(const QMV_GLOBAL int8_t* xr, int col
     return v;
 }
 
-__global__ __launch_bounds__(kBlock, 1) void k_prefill(const DevProblem* __restrict__ probs,
-                                                       const uint64_t* __restrict__ tiles)
+__global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restrict__ probs,
+                                                       const uint64_t* __restrict__ tiles,
+                                                       const int8_t* __restrict__ zeros)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int tid = threadIdx.x;
@@ -110,110 +153,103 @@ __global__ __launch_bounds__(kBlock, 1) void k_prefill(const DevProblem* __restr
     const int m0 = mt * kPBM, n0 = nt * kPBN;
     const int steps = (C + 1) >> 1;
 
-    // ---- B addressing: two 32-row blocks per wave ----------------------------------
+    // ---- weights: two 32-row blocks per wave, HBM -> LDS ------------------------------
+    // lane l of a row block -> 16 bytes at l * 16 of the wave's region; each
+    // lane reads its own chunk back.  Rows past n repeat row n - 1 (never stored).
     const QMV_GLOBAL v4u32* wbase = gload_ptr(reinterpret_cast<const v4u32*>(P->w));
-    static_assert(kPrefillLds <= 160 * 1024, "LDS budget of one CU");
     int brow[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const int r = n0 + 64 * wave + 32 * nb + l32;
         brow[nb] = r < n ? r : n - 1;
     }
-    // B goes HBM -> LDS too (lane l of a row block -> 16 bytes at lane * 16), so
-    // the two-step prefetch needs no registers; each lane reads its own chunk back.
-    auto stage_b = [&](int s, int buf) {
+    auto copy_b = [&](int s, int buf, int nb) {
         const int c = min(2 * s + g, C - 1);
-        uint8_t* bbuf = smem + kBOff + buf * kBBuf;
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-            __builtin_amdgcn_global_load_lds((const void QMV_GLOBAL*)(wbase + (size_t)c * n + brow[nb]),
-                                             (void __attribute__((address_space(3)))*)(bbuf + 1024 * (2 * wave + nb)),
-                                             16, 0, 0);
+        copy16_to_lds(wbase + (size_t)c * n + brow[nb], smem + kBOff + buf * kBBuf + 1024 * (2 * wave + nb));
     };
-
-    // ---- A staging ---------------------------------------------------------------
-    // Fast path: slot f of a buffer = row f / 11, 16-byte piece f % 11 (piece 10 is
-    // padding); wave w fills slots [64 (11 w + j), +64) for j = 0..10, one per lane.
-    const QMV_GLOBAL int8_t* xbase = gload_ptr(P->x8);
-    const bool fast = ((k & 15) == 0) && ((reinterpret_cast<uintptr_t>(P->x8) & 15) == 0);
-    const int f0 = 64 * kSlots * wave + lane;
-    auto stage_a = [&](int s, int buf) {
-        uint8_t* abuf = smem + buf * kABuf;
-        if (fast) {
-            const int colmax = k - 16;
+    auto stage_b = [&](int s, int buf) {
 #pragma unroll
-            for (int j = 0; j < kSlots; ++j) {
-                const int f = f0 + 64 * j;
-                const int r = f / kSlots;
-                const int p = f - r * kSlots;
-                const int tok = min(m0 + r, mtok - 1);
-                const int col = min(160 * s + 16 * min(p, 9), colmax);
-                __builtin_amdgcn_global_load_lds(
-                    (const void QMV_GLOBAL*)(xbase + (size_t)tok * k + col),
-                    (void __attribute__((address_space(3)))*)(abuf + 1024 * (kSlots * wave + j)), 16, 0, 0);
-            }
-        } else {
-            // thread t writes row t: 40 dwords, zero past column k or past the last token
-            const int tok = m0 + tid;
-            uint32_t* row = reinterpret_cast<uint32_t*>(abuf + tid * kARow);
-            const QMV_GLOBAL int8_t* xr = xbase + (size_t)min(tok, mtok - 1) * k;
-            for (int d = 0; d < 40; ++d) row[d] = tok < mtok ? x_bytes(xr, 160 * s + 4 * d, k) : 0u;
-        }
+        for (int nb = 0; nb < 2; ++nb) copy_b(s, buf, nb);
     };
-    // sum of row tid's staged columns below k
-    int rsum = 0;
-    auto sum_a = [&](int s, int buf) {
-        const uint4* row = reinterpret_cast<const uint4*>(smem + buf * kABuf + tid * kARow);
-#pragma unroll
-        for (int p = 0; p < 10; ++p) {
-            if (160 * s + 16 * p < k) {
-                const uint4 v = row[p];
-                rsum = dot4(v.x, 0x01010101u, rsum);
-                rsum = dot4(v.y, 0x01010101u, rsum);
-                rsum = dot4(v.z, 0x01010101u, rsum);
-                rsum = dot4(v.w, 0x01010101u, rsum);
-            }
-        }
-    };
-    v16i32 acc[8][2];
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = v16i32{};
-
-    // Digits of step s: this lane's 16 packed bytes of each row block (braw, read
-    // from the B ring) -> 5 B operands of 16 natural-order digits each.  Work is
-    // split in parts so it can ride along the MFMAs: part j (0..3) expands dword j
-    // of both row blocks, part 4 assembles the operands (zero past column k).
-    uint32_t nat[2][20];
     auto read_b = [&](int buf, v4u32 (&braw)[2]) {
         const uint8_t* bbuf = smem + kBOff + buf * kBBuf;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
             braw[nb] = *reinterpret_cast<const v4u32*>(bbuf + 1024 * (2 * wave + nb) + 16 * lane);
     };
-    auto digits_part = [&](int s, const v4u32 (&braw)[2], int part, v4i32 (&bop)[2][5]) {
-        if (part < 4) {
+
+    // ---- activations: 128 token rows x 10 pieces per step --------------------------------
+    // Fast path (k % 16 == 0, 16-byte aligned rows): copy j of wave w fills
+    // stored slots 64 (5w + j) + lane, slot f = row f / 10 at stored piece
+    // f % 10.  Tokens past m repeat token m - 1 (never stored).
+    const QMV_GLOBAL int8_t* xbase = gload_ptr(P->x8);
+    const QMV_GLOBAL int8_t* zsrc = gload_ptr(zeros);
+    const bool fast = ((k & 15) == 0) && ((reinterpret_cast<uintptr_t>(P->x8) & 15) == 0);
+    int a_tp[kADma];   // token << 4 | source piece of each copy
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][part], nat[nb] + 5 * part);
+    for (int j = 0; j < kADma; ++j) {
+        const int f = 64 * (kADma * wave + j) + lane;
+        const int r = f / kPieces;
+        const int q = f - r * kPieces;                     // stored piece
+        const int p = q - ((r >> 3) & 1);                  // source piece
+        a_tp[j] = (min(m0 + r, mtok - 1) << 4) | (p < 0 ? p + kPieces : p);
+    }
+    auto copy_a = [&](int s, int buf, int j) {
+        const int col = 160 * s + 16 * (a_tp[j] & 15);
+        const QMV_GLOBAL int8_t* src = col < k ? xbase + (size_t)(a_tp[j] >> 4) * k + col : zsrc;
+        copy16_to_lds(src, smem + buf * kABuf + 1024 * (kADma * wave + j));
+    };
+    auto stage_a = [&](int s, int buf) {
+        uint8_t* abuf = smem + buf * kABuf;
+        if (fast) {
+#pragma unroll
+            for (int j = 0; j < kADma; ++j) copy_a(s, buf, j);
         } else {
-            const int cbase = 80 * (2 * s + g);
+            // thread t writes pieces 5h .. 5h+4 of row r (h = t / 128), zero past column k
+            const int r = tid & (kPBM - 1), h = tid >> 7;
+            const int tok = m0 + r;
+            const QMV_GLOBAL int8_t* xr = xbase + (size_t)min(tok, mtok - 1) * k;
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int j = 0; j < 5; ++j) {
+                const int p = 5 * h + j;
+                uint32_t* dst = reinterpret_cast<uint32_t*>(abuf + apos(r, p));
 #pragma unroll
-                for (int i = 0; i < 5; ++i) {
-                    const bool on = cbase + 16 * i < k;   // columns past k (and chunks past the row) add 0
-                    bop[nb][i] = on ? v4i32{(int)nat[nb][4 * i], (int)nat[nb][4 * i + 1], (int)nat[nb][4 * i + 2],
-                                            (int)nat[nb][4 * i + 3]}
-                                    : v4i32{0, 0, 0, 0};
-                }
+                for (int d = 0; d < 4; ++d) dst[d] = tok < mtok ? x_bytes(xr, 160 * s + 16 * p + 4 * d, k) : 0u;
+            }
         }
     };
+    // Sum of row (tid % 128)'s staged columns, pieces 5h .. 5h+4 (h = tid / 128),
+    // one piece per plane; zero past k.
+    int rsum = 0;
+    // pieces 5h .. 5h+3 of a row are consecutive; only 5h+4 can wrap to piece 0
+    const int sbase = apos(tid & (kPBM - 1), 5 * (tid >> 7));
+    const int slast = apos(tid & (kPBM - 1), 5 * (tid >> 7) + 4);
+    auto sum_piece = [&](int buf, int j) {
+        const uint4 v = *reinterpret_cast<const uint4*>(smem + buf * kABuf + (j < 4 ? sbase + 16 * j : slast));
+        rsum = dot4(v.x, 0x01010101u, rsum);
+        rsum = dot4(v.y, 0x01010101u, rsum);
+        rsum = dot4(v.z, 0x01010101u, rsum);
+        rsum = dot4(v.w, 0x01010101u, rsum);
+    };
+    // This lane's activation operand of plane i is piece 5g + i of token row
+    // 32 tb + l32: a per-lane offset (rows of a lane share one rotation).
+    const int abase = apos(l32, 5 * g);       // pieces 5g .. 5g+3 are consecutive
+    const int alast = apos(l32, 5 * g + 4);   // piece 5g+4 can wrap to piece 0
+    auto aoff = [&](int i) { return i < 4 ? abase + 16 * i : alast; };
 
-    // Pipeline: at step s the MFMAs use A(s) (LDS) and the digits of B(s)
-    // (registers, expanded during step s-1, assembled into operands at its end),
-    // while the digits of B(s+1) are expanded and the loads of step s+2 fly.  Issue order per step is B then A,
-    // so "B(s+2) and everything older has landed" is vmcnt(A loads of one step).
+    v16i32 acc[4][2];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) acc[tb][nb] = v16i32{};
+
+    // Pipeline: at step s the MFMAs use the activations of step s (LDS ring slot
+    // s % 3) and the weights of step s (registers, read from the LDS ring during
+    // step s - 1, digits expanded one dword per plane).  Copies for step s + 2
+    // are issued during step s, weights first (plane 0), then the activations
+    // spread over planes 1..4 so that no wave stalls long on a burst of copies:
+    // "weights of s + 2 and everything older have landed" is vmcnt(activation
+    // copies of one step).
     stage_b(0, 0);
     stage_a(0, 0);
     if (steps > 1) {
@@ -221,159 +257,129 @@ __global__ __launch_bounds__(kBlock, 1) void k_prefill(const DevProblem* __restr
         stage_a(1, 1);
     }
     wait_vmcnt<0>();
-    __syncthreads();
-    sum_a(0, 0);
-    v4i32 bop[2][5];
-    {
-        v4u32 braw[2];
-        read_b(0, braw);
+    lds_barrier();
+    v4u32 braw[2];
+    read_b(0, braw);
+    uint32_t nat[2][20];   // the step's digits in natural column order, 4 per dword
 #pragma unroll
-        for (int part = 0; part < 5; ++part) digits_part(0, braw, part, bop);
-    }
+    for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][0], &nat[nb][0]);
 
     for (int s = 0; s < steps; ++s) {
         const int buf = s % kANBuf;
-        const bool more = s + 1 < steps;
         const bool more2 = s + 2 < steps;
-        if (more2) {
-            stage_b(s + 2, (s + 2) % kANBuf);
-            stage_a(s + 2, (s + 2) % kANBuf);
-        }
-        // Plane-outer order: each accumulator is touched once per plane, so 16
-        // independent MFMAs separate two that depend on each other.  The A
-        // operands of plane i+1 are read from LDS and a fifth of the next step's
-        // digit expansion is done while plane i's MFMAs run (one wave per SIMD:
-        // nothing else would hide the LDS latency or fill the MFMA pipe).
-        // the next step's packed weights (stale data after the last step: expanded
-        // and never used, which keeps the MFMA block free of branches)
+        const int abuf2 = (s + 2) % kANBuf;
+        if (more2 && !fast) stage_a(s + 2, abuf2);
+        // the next step's packed weights (after the last step: stale, expanded and
+        // never used, which keeps the MFMA block free of branches)
         v4u32 bnext[2];
-        read_b((s + 1) % kANBuf, bnext);
-        const uint8_t* arow = smem + buf * kABuf + l32 * kARow + 80 * g;
-        // A operands in half planes (4 token blocks): the next half's reads fly
-        // while the current half's 8 MFMAs run
+        read_b((s + 1) & 1, bnext);
+        uint32_t nxt[2][5];
+        const uint8_t* arow = smem + buf * kABuf;   // + aoff: this lane's token row and piece
         v4i32 aop[2][4];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) aop[0][mb] = *reinterpret_cast<const v4i32*>(arow + 32 * mb * kARow);
-        auto plane = [&](int i) {
+        for (int tb = 0; tb < 4; ++tb) aop[0][tb] = *reinterpret_cast<const v4i32*>(arow + 32 * tb * kARow + aoff(0));
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int hs = 2 * i + h;                 // half-plane index 0..9
-                if (hs + 1 < 10) {
-                    const int ni = (hs + 1) >> 1, nh = (hs + 1) & 1;
-#pragma unroll
-                    for (int mb = 0; mb < 4; ++mb)
-                        aop[(hs + 1) & 1][mb] =
-                            *reinterpret_cast<const v4i32*>(arow + 32 * (4 * nh + mb) * kARow + 16 * ni);
+        for (int i = 0; i < 5; ++i) {
+            // copies for step s + 2: weights (into the slot of step s's weights,
+            // already in registers), then activations
+            if (more2) {
+                if (i == 0) stage_b(s + 2, s & 1);
+                else if (fast) {
+                    if (i == 1) copy_a(s + 2, abuf2, 0);
+                    copy_a(s + 2, abuf2, i);
                 }
-                if (h == 0 && i < 4) {
-                    digits_part(s + 1, bnext, i, bop);
-                    // keep this part's work here, among the MFMAs (the compiler
-                    // would otherwise sink it to the end of the step)
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
-                        asm volatile("" ::"v"(nat[nb][5 * i]), "v"(nat[nb][5 * i + 1]), "v"(nat[nb][5 * i + 2]),
-                                     "v"(nat[nb][5 * i + 3]), "v"(nat[nb][5 * i + 4]));
-                }
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    const int tb = 4 * h + mb;
-                    acc[tb][0] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[hs & 1][mb], bop[0][i], acc[tb][0], 0, 0, 0);
-                    acc[tb][1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[hs & 1][mb], bop[1][i], acc[tb][1], 0, 0, 0);
-                }
-                // one MFMA (its operands were read a half plane ago), then the next
-                // half's LDS reads, then one MFMA per few VALU ops
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-#pragma unroll
-                for (int q = 1; q < 8; ++q) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
             }
-        };
+            sum_piece(buf, i);
+            // plane i covers columns 16i .. 16i+15 of each lane's chunk: digit
+            // dwords 4i .. 4i+3, from packed dwords i-1 and i (expanded a plane ahead)
+            if (i < 4) {
 #pragma unroll
-        for (int i = 0; i < 5; ++i) plane(i);
-        // the next step's operands replace this step's once its MFMAs are issued
-        digits_part(s + 1, bnext, 4, bop);
-        if (more) {
-            // A(s+1) and B(s+2) have landed once only A(s+2) may still fly
-            if (more2 && fast) wait_vmcnt<kSlots>();
+                for (int tb = 0; tb < 4; ++tb)
+                    aop[(i + 1) & 1][tb] = *reinterpret_cast<const v4i32*>(arow + 32 * tb * kARow + aoff(i + 1));
+            }
+            if (i < 3) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][i + 1], &nat[nb][5 * (i + 1)]);
+            } else if (i == 3) {
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) natural_digits(bnext[nb][0], nxt[nb]);
+            }
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    const v4i32 wop = {(int)nat[nb][4 * i], (int)nat[nb][4 * i + 1], (int)nat[nb][4 * i + 2],
+                                       (int)nat[nb][4 * i + 3]};
+                    acc[tb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[i & 1][tb], wop, acc[tb][nb], 0, 0, 0);
+                }
+            // one MFMA (its operands are ready), the next plane's LDS reads, then
+            // one MFMA per few VALU ops of the next dword's expansion
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+            for (int q = 1; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            braw[nb] = bnext[nb];
+#pragma unroll
+            for (int u = 0; u < 5; ++u) nat[nb][u] = nxt[nb][u];
+        }
+        if (s + 1 < steps) {
+            // activations of s + 1 and weights of s + 2 have landed once only the
+            // activation copies of s + 2 may still fly
+            if (more2 && fast) wait_vmcnt<kADma>();
             else wait_vmcnt<0>();
-            __syncthreads();
-            sum_a(s + 1, (s + 1) % kANBuf);
+            lds_barrier();
         }
     }
 
-    // ---- per-token sums and scales in LDS, then the epilogue -------------------------
-    int* tsum = reinterpret_cast<int*>(smem + kEpiOff);
-    float* tscale = reinterpret_cast<float*>(smem + kEpiOff + kPBM * 4);
-    __syncthreads();
-    {
-        const float sw = *gload_ptr(P->sw);
+    // ---- epilogue ---------------------------------------------------------------------
+    // Token sums and scales go to LDS.  Accumulator register 4q+e of lane l is
+    // token 8q + 4g + e of its 32-token block and row l % 32 of its 32-row block,
+    // so each register's half-wave holds 32 consecutive outputs of one token: a
+    // whole 128-byte line, stored straight from the registers.
+    int* tsum = reinterpret_cast<int*>(smem + kEpiOff);                 // [2][128]
+    float* tscale = reinterpret_cast<float*>(smem + kEpiOff + 2 * kPBM * 4);
+    tsum[tid] = rsum;   // half tid / 128 of row tid % 128
+    if (tid < kPBM) {
         const int tok = m0 + tid;
-        tsum[tid] = rsum;
-        tscale[tid] = tok < mtok ? gload_ptr(P->sx)[tok] * sw : 0.0f;
+        tscale[tid] = tok < mtok ? gload_ptr(P->sx)[tok] * *gload_ptr(P->sw) : 0.0f;
     }
     __syncthreads();
-    // The tile leaves through LDS, 128 tokens at a time: the exact sums (acc
-    // minus the token's digit offset) are parked as [token][row] and written out
-    // as whole 1 KB token rows with 16-byte stores, y = sum * sx * sw (long
-    // contiguous writes instead of 128-byte pieces per accumulator register).
     QMV_GLOBAL float* y = gstore_ptr(P->y);
     QMV_GLOBAL int32_t* accout = P->acc ? gstore_ptr(P->acc) : nullptr;
-    const bool vec = ((reinterpret_cast<uintptr_t>(P->y) & 15) == 0) && ((n & 3) == 0) &&
-                     (!P->acc || (reinterpret_cast<uintptr_t>(P->acc) & 15) == 0);
-    int* park = reinterpret_cast<int*>(smem);   // [128][kParkPitch]
-    static_assert(128 * kParkPitch * 4 <= kEpiOff, "parking fits below the token sums");
+    const bool full = m0 + kPBM <= mtok && n0 + kPBN <= n;
+    const int rl = n0 + 64 * wave + l32;   // this lane's row in row block 0 (+32 in block 1)
+    const int loff = 4 * g * n + rl;       // + (token block base + 8q + e) * n
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-        for (int mh = 0; mh < 4; ++mh) {
-            const int mb = 4 * half + mh;
+        for (int q = 0; q < 4; ++q) {
+            const int t0 = 32 * tb + 8 * q + 4 * g;   // tile token of register 4q (+e)
+            const int4 ta = *reinterpret_cast<const int4*>(tsum + t0);
+            const int4 tc = *reinterpret_cast<const int4*>(tsum + kPBM + t0);
+            const float4 sc4 = *reinterpret_cast<const float4*>(tscale + t0);
+            const int tsv[4] = {ta.x + tc.x, ta.y + tc.y, ta.z + tc.z, ta.w + tc.w};
+            const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int ml = 32 * mb + 8 * q4 + 4 * g;   // tile token of register 4*q4 (+e)
-                const int4 ts = *reinterpret_cast<const int4*>(tsum + ml);
-                const int tsv[4] = {ts.x, ts.y, ts.z, ts.w};
+            for (int e = 0; e < 4; ++e) {
+                const size_t urow = (size_t)(m0 + 32 * tb + 8 * q + e) * n;   // uniform part of the offset
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        park[(ml + e - 128 * half) * kParkPitch + 64 * wave + 32 * nb + l32] =
-                            acc[mb][nb][4 * q4 + e] - tsv[e];
-            }
-        }
-        __syncthreads();
-        for (int it = 0; it < 128 / 4; ++it) {
-            const int tl = 4 * it + wave;                  // token within the half
-            const int tok = m0 + 128 * half + tl;
-            const int r = n0 + 4 * lane;
-            if (tok < mtok && r < n) {
-                const int4 v = *reinterpret_cast<const int4*>(park + tl * kParkPitch + 4 * lane);
-                const float sc = tscale[128 * half + tl];
-                const size_t o = (size_t)tok * n + r;
-                if (vec && r + 3 < n) {
-                    *reinterpret_cast<QMV_GLOBAL v4u32*>(y + o) =
-                        v4u32{__float_as_uint((float)v.x * sc), __float_as_uint((float)v.y * sc),
-                              __float_as_uint((float)v.z * sc), __float_as_uint((float)v.w * sc)};
-                    if (accout)
-                        *reinterpret_cast<QMV_GLOBAL v4u32*>(accout + o) =
-                            v4u32{(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
-                } else {
-                    const int vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if (r + e < n) {
-                            y[o + e] = (float)vv[e] * sc;
-                            if (accout) accout[o + e] = vv[e];
-                        }
+                for (int nb = 0; nb < 2; ++nb) {
+                    const int v = acc[tb][nb][4 * q + e] - tsv[e];
+                    if (full || (m0 + t0 + e < mtok && rl + 32 * nb < n)) {
+                        y[urow + loff + 32 * nb] = (float)v * scv[e];
+                        if (accout) accout[urow + loff + 32 * nb] = v;
                     }
                 }
             }
         }
-        __syncthreads();
     }
 }
 
@@ -389,12 +395,13 @@ void prefill_tile_entries(int32_t slot, int64_t m, int64_t n, uint64_t* out)
         for (int64_t nt = 0; nt < nts; ++nt) out[i++] = ((uint64_t)slot << 48) | ((uint64_t)mt << 32) | (uint64_t)nt;
 }
 
-hipError_t launch_prefill(const DevProblem* probs, const uint64_t* tiles, int64_t tile_count, hipStream_t s)
+hipError_t launch_prefill(const DevProblem* probs, const uint64_t* tiles, int64_t tile_count, const int8_t* zeros,
+                          hipStream_t s)
 {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_prefill, dim3((unsigned)tile_count), dim3(kBlock), kPrefillLds, s, probs, tiles);
+    hipLaunchKernelGGL(k_prefill, dim3((unsigned)tile_count), dim3(kBlock), kPrefillLds, s, probs, tiles, zeros);
     return hipGetLastError();
 }
 

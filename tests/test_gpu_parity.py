@@ -303,10 +303,12 @@ def test_lmhead_planted_winner_and_tie(qmv_gpu):
 # A8: prefill GEMM on int8 matrix cores
 # --------------------------------------------------------------------------
 
-# (n, k, m): ragged tokens and rows around the 256 x 256 tile, odd chunk
-# counts (the last K step is half empty), K not a multiple of 4.
+# (n, k, m): ragged tokens and rows around the 128-token x 256-row tile, odd
+# chunk counts (the last K step is half empty), K not a multiple of 4 or 16
+# (activation rows staged byte-wise), a single K step.
 PREFILL_CASES = [(1, 1, 1), (5, 7, 3), (64, 80, 32), (300, 1152, 256), (257, 1152, 300), (33, 6912, 512),
-                 (1024, 1152, 512), (100, 1600, 17), (513, 161, 257), (40, 1537, 5)]
+                 (1024, 1152, 512), (100, 1600, 17), (513, 161, 257), (40, 1537, 5), (256, 1152, 128),
+                 (255, 1152, 129), (260, 1160, 127), (768, 2304, 384)]
 
 
 @pytest.mark.parametrize("n,k,m", PREFILL_CASES)
