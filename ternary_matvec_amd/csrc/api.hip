@@ -101,7 +101,10 @@ int64_t table_bound(const qmv_problem* probs, int32_t count, int cus)
     for (int32_t i = 0; i < count; ++i) tiles64 += rows_tiles(probs[i].w.n, kRowsPerTile);
     int64_t b = round_up((int64_t)sizeof(DevProblem) * count, 256);
     (void)cus;
-    for (int wt = 1; wt <= 2; ++wt) b += round_up((tiles64 + kStreamHdr + 2 * kStreamXcds) * 4, 256);
+    // per weight type: counters, list offsets, tile entries (at most one per 64
+    // rows) and the first two entries of each workgroup (no more workgroups
+    // than tiles)
+    for (int wt = 1; wt <= 2; ++wt) b += round_up((3 * tiles64 + kStreamHdr + 2 * kStreamXcds) * 4, 256);
     return b;
 }
 
@@ -188,11 +191,26 @@ bool schedule_stream(const std::vector<const qmv_problem*>& sp, const std::vecto
             xl[bx].push_back(it.entry);
             load[bx] += it.cost;
         }
-        best.words.assign(kStreamHdr + 2 * kStreamXcds, 0u);
+        // [counters][first two entries of each workgroup][list offsets and
+        // sizes][lists]; workgroup b runs on XCD b % 8, as the XCD's workgroup
+        // r = b / 8 of w: its tiles are entries w + r and r (the shorter first:
+        // the lists are longest first, and the longer one is then staged while
+        // the shorter one streams), then the entries from 2w on as its tickets
+        // name them
+        best.words.assign(kStreamHdr + 2 * nb + 2 * kStreamXcds, 0u);
+        for (int b = 0; b < nb; ++b) {
+            const int x = b % kStreamXcds;
+            const auto& l = xl[x];
+            const size_t r = (size_t)(b / kStreamXcds), w = (size_t)wgs[x];
+            const uint32_t e0 = r < l.size() ? l[r] : 0xffffffffu;
+            const uint32_t e1 = w + r < l.size() ? l[w + r] : 0xffffffffu;
+            best.words[kStreamHdr + 2 * b] = e1 != 0xffffffffu ? e1 : e0;
+            best.words[kStreamHdr + 2 * b + 1] = e1 != 0xffffffffu ? e0 : e1;
+        }
         uint32_t off = 0;
         for (int x = 0; x < kStreamXcds; ++x) {
-            best.words[kStreamHdr + 2 * x] = off;
-            best.words[kStreamHdr + 2 * x + 1] = (uint32_t)xl[x].size();
+            best.words[kStreamHdr + 2 * nb + 2 * x] = off;
+            best.words[kStreamHdr + 2 * nb + 2 * x + 1] = (uint32_t)xl[x].size();
             off += (uint32_t)xl[x].size();
         }
         for (int x = 0; x < kStreamXcds; ++x) best.words.insert(best.words.end(), xl[x].begin(), xl[x].end());
@@ -230,7 +248,7 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
             t.stream[wt] = true;
             t.nb[wt] = ch.nb;
             t.slot_bytes[wt] = (int32_t)ch.slot_bytes;
-            t.count[wt] = (int32_t)(ch.words.size() - kStreamHdr - 2 * kStreamXcds);
+            t.count[wt] = (int32_t)(ch.words.size() - kStreamHdr - 2 * ch.nb - 2 * kStreamXcds);
             for (size_t i = 0; i < slots.size(); ++i) lanes[slots[i]] = ch.lanes[i];
             words[wt] = std::move(ch.words);
         } else {

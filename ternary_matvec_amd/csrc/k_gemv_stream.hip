@@ -247,18 +247,29 @@ __device__ __forceinline__ uintptr_t row_addr(const Tile& T, int mi)
     return reinterpret_cast<uintptr_t>(T.x8) + (uintptr_t)mi * (uintptr_t)T.k;
 }
 
+// The aligned dwords of token mi's row, as a buffer: reads past them return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const Tile& T, int mi, uint32_t& sh)
+{
+    const uintptr_t a = row_addr(T, mi);
+    sh = (uint32_t)(a & 3);
+    const uint32_t words = (sh + (uint32_t)T.k + 3u) >> 2;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(a & ~(uintptr_t)3), (short)0, (int)(4 * words), (int)kRsrcWord3);
+}
+
+// Unit u: its kD + 1 aligned dwords are loaded (unit_load), then shifted into
+// place with bytes past column k cleared (unit_of).
 template <int WT>
-__device__ __forceinline__ void unit_at(const Tile& T, int mi, int u, uint32_t* nat)
+__device__ __forceinline__ void unit_load(__amdgpu_buffer_rsrc_t rs, int u, uint32_t* raw)
 {
     constexpr int kD = WT == 1 ? 5 : 1;
-    const uintptr_t a = row_addr(T, mi);
-    const uint32_t sh = (uint32_t)(a & 3);
-    const uint32_t words = (sh + (uint32_t)T.k + 3u) >> 2;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(a & ~(uintptr_t)3), (short)0, (int)(4 * words), (int)kRsrcWord3);
-    uint32_t raw[kD + 1];
 #pragma unroll
     for (int j = 0; j <= kD; ++j) raw[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (kD * u + j), 0, 0);
+}
+
+template <int WT>
+__device__ __forceinline__ void unit_of(const Tile& T, uint32_t sh, int u, const uint32_t* raw, uint32_t* nat)
+{
+    constexpr int kD = WT == 1 ? 5 : 1;
 #pragma unroll
     for (int j = 0; j < kD; ++j) {
         const uint32_t v = __builtin_amdgcn_alignbyte(raw[j + 1], raw[j], sh);
@@ -279,35 +290,56 @@ __device__ __forceinline__ void put_z(uint32_t* zo, int g, const uint32_t zz[10]
 
 // Stage tile T into an LDS slot (the staging wave): Z values (ternary) or x
 // (int8) for chunks 0..C-1, zeros up to cpad, and the ternary correction
-// 25600 * sum Z + sum x of each token.
-template <int MT, int WT>
-__device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, int* corr)
+// 25600 * sum Z + sum x of each token.  `after_loads` runs once, in uniform
+// control flow, right after the first activation loads of every lane are
+// issued: work placed there overlaps their latency instead of delaying them.
+template <int MT, int WT, class F>
+__device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, int* corr, F after_loads)
 {
+    constexpr int kD = WT == 1 ? 5 : 1;
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
         if (mi > 0 && mi >= T.m) continue;
         uint32_t* zo = reinterpret_cast<uint32_t*>(slot + (size_t)mi * T.tok_bytes);
         const int units = 4 * T.C;
-        if (WT == 1) {
-            int s_z = 0, s_x = 0;
-            for (int g = lane; g < units; g += kWave) {
+        uint32_t sh;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(T, mi, sh);
+        // every lane's first unit, loaded unconditionally (reads past the row
+        // return zeros)
+        uint32_t raw0[kD + 1];
+        unit_load<WT>(rs, lane, raw0);
+        if (mi == 0) after_loads();
+        int s_z = 0, s_x = 0;
+        for (int g = lane; g < units; g += kWave) {
+            uint32_t raw[kD + 1];
+            if (g == lane) {
+#pragma unroll
+                for (int j = 0; j <= kD; ++j) raw[j] = raw0[j];
+            } else {
+                unit_load<WT>(rs, g, raw);
+            }
+            if (WT == 1) {
                 uint32_t nat[5], zz[10];
-                unit_at<1>(T, mi, g, nat);
+                unit_of<1>(T, sh, g, raw, nat);
                 z_group(nat, zz, s_z, s_x);
                 put_z(zo, g, zz);
+            } else {
+                unit_of<2>(T, sh, g, raw, &zo[g]);
             }
+        }
+        if (WT == 1) {
             for (int d = 48 * T.C + lane; d < 48 * T.cpad; d += kWave) zo[d] = 0u;
             const int cw = wave_total((int)(25600u * (uint32_t)s_z + (uint32_t)s_x));
             if (lane == 0) corr[mi] = cw;
         } else {
-            for (int d = lane; d < units; d += kWave) unit_at<2>(T, mi, d, &zo[d]);
             for (int d = units + lane; d < 4 * T.cpad; d += kWave) zo[d] = 0u;
         }
     }
 }
 
 // Schedule words: [counters: 8 tile counters + 8 done counters, 64 words
-// apart][8 x (list offset, list size)][tile entries of the 8 XCD lists].
+// apart][first tile entry of each workgroup][8 x (list offset, list size)]
+// [tile entries of the 8 XCD lists].
 // LDS: [2 tile slots of slot_bytes][2 tile descriptors][corr: 2 x MT]
 template <int MT, int WT>
 __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem* __restrict__ probs,
@@ -322,37 +354,71 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
     int* const corr_base = reinterpret_cast<int*>(descs + 2);
 
     const int xcd = blockIdx.x % kStreamXcds;
-    const uint32_t rank = blockIdx.x / kStreamXcds;                       // among the XCD's workgroups
     const uint32_t wgs = (gridDim.x - xcd + kStreamXcds - 1) / kStreamXcds;   // workgroups of this XCD
-    const QMV_CONST uint32_t* hdr = cload_ptr(sched + kStreamHdr);
-    const uint32_t list_off = hdr[2 * xcd], list_size = hdr[2 * xcd + 1];
-    const uint32_t* list = sched + kStreamHdr + 2 * kStreamXcds + list_off;
-    const uint32_t te0 = rank < list_size ? list[rank] : kEnd;
+    // A workgroup's first two tiles are one load away; the rest of its XCD's
+    // list is dealt by the ticket counter, from entry 2 * wgs on.
+    const uint32_t te0 = cload_ptr(sched + kStreamHdr)[2 * blockIdx.x];
+    const uint32_t* const hdr = sched + kStreamHdr + 2 * gridDim.x;
 
     if (wave == kComputeWaves) {
         // ---- staging wave: tile q into slot q & 1, the entry of tile q + 1, then
         // barrier q ------------------------------------------------------------------
         // The counter is read one tile ahead of its use (an atomic under
         // contention takes microseconds): the ticket for tile q + 2 is taken
-        // while tile q + 1 is streamed.
+        // while tile q + 1 is streamed.  Tile 1 is the static second entry, so
+        // nothing on the way to the first barrier waits for an atomic.
+        const uint32_t te1 = cload_ptr(sched + kStreamHdr)[2 * blockIdx.x + 1];
         uint32_t te = te0;
         uint32_t ticket = 0;
-        if (te != kEnd && lane == 0) ticket = atomicAdd(&sched[64 * xcd], 1u);
-        Tile T;
-        if (te != kEnd) {
-            T = tile_at<kCB>(probs, te, 0, lane);
-            if (lane == 0) descs[0] = desc_of(T, te);
+        Tile T, T1;
+        TileDesc d1;
+        if (te != kEnd) T = tile_at<kCB>(probs, te, 0, lane);
+        if (te1 != kEnd) {   // tile 1's descriptor, fetched with tile 0's (scalar loads)
+            T1 = tile_at<kCB>(probs, te1, 0, lane);
+            d1 = desc_of(T1, te1);
         }
+        uint32_t list_size = 0;
+        const uint32_t* list = nullptr;
+        bool first = true;
         for (int par = 0; te != kEnd; par ^= 1) {
-            stage<MT, WT>(T, lane, smem + (size_t)par * slot_bytes, corr_base + par * MT);
-            uint32_t nx = kEnd;
-            if (lane == 0) {
-                const uint32_t i = wgs + ticket;
-                nx = i < list_size ? list[i] : kEnd;
-                if (nx != kEnd) ticket = atomicAdd(&sched[64 * xcd], 1u);
+            stage<MT, WT>(T, lane, smem + (size_t)par * slot_bytes, corr_base + par * MT, [&] {
+                if (first) {
+                    // Tile 0: release the compute waves' weight prefetch only once
+                    // these loads (and the tile's scales) are back: they gate every
+                    // wave of the workgroup, and behind the prefetch of the whole
+                    // chip (tens of MB) they would wait microseconds.  Then the
+                    // tile's descriptor and the first ticket.
+                    const TileDesc d0 = desc_of(T, te);   // wave-uniform: scalar loads
+                    wait_vmcnt<0>();
+                    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the scalar loads
+                    __builtin_amdgcn_s_barrier();
+                    if (lane == 0) {
+                        descs[0] = d0;
+                        if (te1 != kEnd) ticket = atomicAdd(&sched[64 * xcd], 1u);
+                    }
+                }
+            });
+            if (list == nullptr) {
+                const uint32_t list_off = cload_ptr(hdr)[2 * xcd];
+                list_size = cload_ptr(hdr)[2 * xcd + 1];
+                list = hdr + 2 * kStreamXcds + list_off;
             }
-            nx = __builtin_amdgcn_readfirstlane(nx);
-            if (nx != kEnd) {
+            uint32_t nx = kEnd;
+            if (first) {
+                nx = te1;
+                first = false;
+            } else {
+                if (lane == 0) {
+                    const uint32_t i = 2 * wgs + ticket;
+                    nx = i < list_size ? list[i] : kEnd;
+                    if (nx != kEnd) ticket = atomicAdd(&sched[64 * xcd], 1u);
+                }
+                nx = __builtin_amdgcn_readfirstlane(nx);
+            }
+            if (nx != kEnd && par == 0 && nx == te1) {
+                T = T1;
+                if (lane == 0) descs[1] = d1;
+            } else if (nx != kEnd) {
                 T = tile_at<kCB>(probs, nx, 0, lane);
                 if (lane == 0) descs[par ^ 1] = desc_of(T, nx);
             } else if (lane == 0) {
@@ -381,6 +447,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
 
     // ---- compute waves ----------------------------------------------------------------
     Tile cur = tile_at<kCB>(probs, te0, wave, lane);
+    __builtin_amdgcn_s_barrier();   // the staging wave has issued tile 0's activation loads
     v4u32 ring[kRing][kRPL];
 #pragma unroll
     for (int r = 0; r + 1 < kRing; ++r)

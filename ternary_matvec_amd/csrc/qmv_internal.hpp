@@ -81,7 +81,8 @@ hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t t
 // waves + 1 staging wave; a workgroup tile is 4 * 64 / lanes_per_row *
 // kStreamRowsPerLane rows of one problem, entry = problem slot << kTileRowBits | row block.  Schedule
 // words (in the workspace, writable): [kStreamHdr words of counters, zero
-// between launches][kStreamXcds x (offset, size)][the XCD tile lists].  LDS =
+// between launches][the first two tile entries of each workgroup][kStreamXcds x
+// (offset, size)][the XCD tile lists].  LDS =
 // two staged tiles of slot_bytes + a few words.
 constexpr int kStreamXcds = 8;
 #ifndef QMV_STREAM_RPL
