@@ -193,6 +193,117 @@ def time_gemv_only(stack, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps
 
 
+def time_read_ceiling(stack, reps, stream):
+    """The plain-read yardstick (qmv_read_probe) over the same weight copies, rotated
+    like the GEMV's: the HBM read rate this machine reaches on these buffers."""
+    import torch
+    from ternary_matvec_amd import qmv
+    out = torch.zeros(1, dtype=torch.int32, device=stack.pool[0].device)
+    for c in range(stack.copies):
+        qmv.qmv_read_probe(stack.pool[c], out, stream=stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(reps):
+        qmv.qmv_read_probe(stack.pool[i % stack.copies], out, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    return stack.pool[0].numel() / ms / 1e6, ms
+
+
+def copies_sweep(stack, steps, stream):
+    """GEMV GB/s with the weights rotated over C = 1, 2, 4, 8 copies: the rate must be
+    flat once the rotating set (C x 137.5 MB) is well past the 256 MB Infinity Cache."""
+    import torch
+    from ternary_matvec_amd import qmv
+    out = {}
+    for c_count in (1, 2, 4, 8):
+        if c_count > stack.copies:
+            break
+        for i in range(10):
+            qmv.qmv_gemv(stack.arrays[i % c_count], workspace=stack.workspaces[i % c_count],
+                         flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(steps):
+            qmv.qmv_gemv(stack.arrays[i % c_count], workspace=stack.workspaces[i % c_count],
+                         flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        out["C%d" % c_count] = {"gemv_us": round(ms * 1e3, 2), "GB/s": round(stack.gemv_bytes() / ms / 1e6, 1)}
+    return out
+
+
+def chained(stack, steps, stream, copies=4):
+    """The step as stream-ordered launches instead of one grouped launch: 156 (one per
+    matrix) or 78 (q/k/v and gate/up grouped per layer, down alone)."""
+    import ctypes
+    import torch
+    from ternary_matvec_amd import qmv
+    copies = min(copies, stack.copies)
+    per_layer = len(stack.mats)
+    groups = {"156": [], "78": []}
+    for c in range(copies):
+        arr = stack.arrays[c]
+        base = ctypes.addressof(arr)
+        size = ctypes.sizeof(qmv.qmv_problem)
+        one, grouped = [], []
+        for i in range(len(arr)):
+            sub = (qmv.qmv_problem * 1).from_address(base + i * size)
+            one.append((sub, qmv.qmv_gemv(sub, stream=stream)))
+        for lay in range(len(arr) // per_layer):
+            for lo, hi in ((0, 3), (3, 5), (5, 6)):
+                sub = (qmv.qmv_problem * (hi - lo)).from_address(base + (lay * per_layer + lo) * size)
+                grouped.append((sub, qmv.qmv_gemv(sub, stream=stream)))
+        groups["156"].append(one)
+        groups["78"].append(grouped)
+    torch.cuda.synchronize()
+    out = {}
+    for name, per_copy in groups.items():
+        def step(i):
+            for sub, ws in per_copy[i % copies]:
+                qmv.qmv_gemv(sub, workspace=ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        for i in range(3):
+            step(i)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(steps):
+            step(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / steps
+        out["launches_%s" % name] = {"step_us": round(ms * 1e3, 1),
+                                     "GB/s": round(stack.gemv_bytes() / ms / 1e6, 1)}
+    return out
+
+
+def time_quantize(stack, steps, stream):
+    """The step's two qmv_quantize_act calls (one per K) alone."""
+    import torch
+    from ternary_matvec_amd import qmv
+    for _ in range(5):
+        for k in stack.x:
+            qmv.qmv_quantize_act(stack.x[k], x8=stack.x8[k], sx=stack.sx[k], stream=stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(steps):
+        for k in stack.x:
+            qmv.qmv_quantize_act(stack.x[k], x8=stack.x8[k], sx=stack.sx[k], stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / steps
+    return {"us": round(ms * 1e3, 2), "GB/s": round(stack.quant_bytes() / ms / 1e6, 1)}
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
@@ -225,6 +336,34 @@ def cpu_baseline(stack, target_s, dev):
             "sample": "%d full step(s) of the same workload (%d matrices, batch %d): per-token quantise, exact "
                       "int matmul from unpacked trits, dequantise; %.1f s on %d threads"
                       % (passes, len(stack.specs), stack.m, elapsed, threads)}
+
+
+def cpu_single_thread(stack, target_s, dev):
+    """The oracle on one thread over one layer's 6 matrices (repeated to about
+    `target_s` seconds), in GB/s of that layer's step bytes."""
+    import oracle
+    from ternary_matvec_amd import synth
+    per_layer = len(stack.mats)
+    inputs, nbytes = [], 0
+    for (lay, mid, name, n, k, slot) in stack.specs[:per_layer]:
+        t = synth.trits_torch(synth.stream_seed(stack.config_id, lay, mid, synth.TAG_WEIGHT), (n, k),
+                              device=dev).cpu().numpy()
+        s = synth.ternary_scale(synth.stream_seed(stack.config_id, lay, mid, synth.TAG_SCALE))
+        x = stack.x_host[k][slot * stack.m:(slot + 1) * stack.m]
+        inputs.append((t, x, np.float32(s)))
+        m = stack.m
+        nbytes += n * ((k + 4) // 5) + m * k + 4 * m * n + 4 + 4 * m + 5 * m * k + 4 * m
+    elapsed, passes = 0.0, 0
+    while passes == 0 or elapsed < target_s:
+        t0 = time.perf_counter()
+        for (t, x, s) in inputs:
+            q, sx = oracle.quantize_rows(x)
+            acc = oracle.matmul_int(q, t, threads=1)
+            oracle.dequant(acc, sx, s)
+        elapsed += time.perf_counter() - t0
+        passes += 1
+    return {"value": round(nbytes * passes / elapsed / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "sample": "%d pass(es) over layer 0's 6 matrices, %.1f s" % (passes, elapsed)}
 
 
 # ---------------------------------------------------------------------------
@@ -301,7 +440,32 @@ def time_prefill(ps, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps, float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
 
-def bench_prefill(stack, dev, stream, steps=20, warmup=3):
+def prefill_per_matrix(ps, stream, reps=10):
+    """One grouped launch per matrix kind (its 26 layers), timed alone."""
+    import torch
+    from ternary_matvec_amd import qmv
+    specs = ps.stack.specs
+    out = {}
+    for mid, (name, n, k) in enumerate(ps.stack.mats):
+        idx = [i for i, sp in enumerate(specs) if sp[1] == mid]
+        sub = (qmv.qmv_problem * len(idx))(*[ps.arr[i] for i in idx])
+        ws = qmv.qmv_gemm_prefill(sub, stream=stream)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(reps):
+            qmv.qmv_gemm_prefill(sub, workspace=ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        ops = 2 * ps.m * n * k * len(idx)
+        out[name] = {"shape": "%dx%d" % (n, k), "matrices": len(idx), "us": round(ms * 1e3, 1),
+                     "TOPS": round(ops / ms / 1e9, 1)}
+    return out
+
+
+def bench_prefill(stack, dev, stream, steps=20, warmup=3, per_matrix=False):
     import torch
     ps = PrefillStack(stack, 512, dev)
     step_ms, kern_ms = time_prefill(ps, steps, warmup, stream)
@@ -311,6 +475,8 @@ def bench_prefill(stack, dev, stream, steps=20, warmup=3):
            "step_us": round(step_ms * 1e3, 1), "TOPS": round(tops, 1),
            "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
            "GB/s": round(ps.bytes() / kern_ms / 1e6, 1), "ops_per_pass": ps.ops(), "bytes_per_pass": ps.bytes()}
+    if per_matrix:
+        out["per_matrix"] = prefill_per_matrix(ps, stream)
     del ps
     torch.cuda.empty_cache()
     return out
@@ -437,6 +603,9 @@ def main():
     log("step %.2f us, gemv (events in step) %.2f us, gemv back-to-back %.2f us" %
         (step_ms * 1e3, gemv_ms * 1e3, gemv_only_ms * 1e3))
 
+    ceiling_gbs, ceiling_ms = time_read_ceiling(stack, 50, stream)
+    log("plain read of the weight copies: %.1f GB/s" % ceiling_gbs)
+
     step_bytes = stack.step_bytes()
     gemv_bytes = stack.gemv_bytes()
     value = step_bytes / step_ms / 1e6          # GB/s
@@ -463,14 +632,22 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": gemv_traffic(),
                      "bytes_per_launch": gemv_bytes, "launch_us": round(gemv_ms * 1e3, 3),
-                     "launch_us_back_to_back": round(gemv_only_ms * 1e3, 3)},
+                     "launch_us_back_to_back": round(gemv_only_ms * 1e3, 3),
+                     "measured_read_ceiling": round(ceiling_gbs, 1),
+                     "frac_of_measured_ceiling": round(achieved / ceiling_gbs, 4),
+                     "ceiling_kernel": "qmv_read_probe: one 16-byte-load read of the same weight copies "
+                                       "(%.1f MB in %.2f us)" % (stack.pool[0].numel() / 1e6, ceiling_ms * 1e3)},
     }
     log("prefill (512 tokens)")
-    result["prefill"] = bench_prefill(stack, dev, stream)
+    result["prefill"] = bench_prefill(stack, dev, stream, per_matrix=not args.no_extras)
     log("prefill %.1f us, %.1f TOPS" % (result["prefill"]["prefill_us"], result["prefill"]["TOPS"]))
     if not args.no_extras:
         extras = {}
         try:
+            log("decode variants")
+            extras["decode_copies_sweep"] = copies_sweep(stack, max(20, args.steps // 2), stream)
+            extras["decode_chained"] = chained(stack, max(5, args.steps // 20), stream)
+            extras["quantize_step"] = time_quantize(stack, max(20, args.steps // 2), stream)
             log("output layer")
             extras["lmhead"] = bench_head(dev, stream)
             torch.cuda.empty_cache()
@@ -493,6 +670,8 @@ def main():
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(stack, args.cpu_seconds, dev)
+        if not args.no_extras:
+            result.setdefault("extras", {})["cpu_oracle_1_thread"] = cpu_single_thread(stack, 3.0, dev)
     print(json.dumps(result), flush=True)
 
 

@@ -196,6 +196,17 @@ int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int
                           float* max_logit, float* logits, void* workspace, int64_t ws_bytes,
                           void* stream);
 
+/*
+ * qmv_read_probe -- a measurement aid, not part of the method: reads `bytes`
+ * of `data` once with 16-byte loads (grid-stride, the access pattern that
+ * reads fastest on this GPU) and folds them into a word written to *out only
+ * when it equals a fixed key.  Timing it beside qmv_gemv gives the achievable
+ * HBM read rate on the same buffers.
+ *   data  device, 16-byte aligned; bytes a multiple of 16 (0 = no-op).
+ *   out   device, 1 uint32 (normally left untouched).
+ */
+int32_t qmv_read_probe(const void* data, int64_t bytes, uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -589,6 +589,15 @@ int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k)
     return round_up(lmhead_partials(v) * 8, 256);
 }
 
+int32_t qmv_read_probe(const void* data, int64_t bytes, uint32_t* out, void* stream)
+{
+    if (!data || !out || bytes < 0 || !aligned(data, 16) || (bytes & 15)) return QMV_EINVAL;
+    if (bytes == 0) return QMV_OK;
+    int cus = 0;
+    device_cus(&cus);
+    return hip_status(launch_read_probe(data, bytes, out, cus, as_stream(stream)));
+}
+
 int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int64_t k, int32_t* idx,
                           float* max_logit, float* logits, void* workspace, int64_t ws_bytes, void* stream)
 {

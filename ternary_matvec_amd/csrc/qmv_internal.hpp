@@ -106,6 +106,7 @@ int64_t prefill_tiles(int64_t m, int64_t n);
 void prefill_tile_entries(int32_t slot, int64_t m, int64_t n, uint64_t* out);
 hipError_t launch_prefill(const DevProblem* probs, const uint64_t* tiles, int64_t tile_count, const int8_t* zeros,
                           hipStream_t s);
+hipError_t launch_read_probe(const void* data, int64_t bytes, uint32_t* out, int cus, hipStream_t s);
 hipError_t launch_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, int32_t* idx,
                          float* max_logit, float* logits, void* workspace, hipStream_t s);
 int64_t lmhead_partials(int64_t v);

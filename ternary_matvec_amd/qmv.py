@@ -62,6 +62,7 @@ SIGNATURES = {
     "qmv_lmhead_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
     "qmv_lmhead_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64,
                                    _c_ptr]),
+    "qmv_read_probe": (_c_i32, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
 }
 
 
@@ -243,6 +244,15 @@ def qmv_gemm_prefill(problems, workspace=None, flags=0, stream=None):
 
 def qmv_lmhead_workspace_bytes(v: int, k: int) -> int:
     return int(load().qmv_lmhead_workspace_bytes(v, k))
+
+
+def qmv_read_probe(buf, out, stream=None):
+    """Measurement aid: read a device tensor once (16-byte loads) and fold it into out[0]
+    only on a fixed key; timed beside qmv_gemv it gives the achievable HBM read rate."""
+    import torch
+    assert buf.is_cuda and out.is_cuda and out.dtype in (torch.int32, torch.uint32) and out.numel() >= 1
+    _check(load().qmv_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
+                                 _stream(stream)), "qmv_read_probe")
 
 
 def qmv_lmhead_argmax(w_bf16, x, logits=None, idx=None, max_logit=None, workspace=None, want_logits=False,

@@ -121,3 +121,16 @@ def test_gemv_validation(lib):
     # count
     assert lib.qmv_gemv(arr, 0, _fake(1 << 20), need, 0, None) == qmv.QMV_ESHAPE
     assert lib.qmv_gemv(None, 1, _fake(1 << 20), need, 0, None) == qmv.QMV_EINVAL
+
+
+def test_read_probe_rejects_bad_arguments(lib):
+    """qmv_read_probe validates on the host: null pointers, misaligned or ragged sizes."""
+    import ctypes
+    EINVAL = -1
+    out = ctypes.c_uint32(0)
+    assert lib.qmv_read_probe(None, 16, ctypes.addressof(out), None) == EINVAL
+    assert lib.qmv_read_probe(ctypes.c_void_p(16), 16, None, None) == EINVAL
+    assert lib.qmv_read_probe(ctypes.c_void_p(16), 15, ctypes.addressof(out), None) == EINVAL
+    assert lib.qmv_read_probe(ctypes.c_void_p(17), 16, ctypes.addressof(out), None) == EINVAL
+    assert lib.qmv_read_probe(ctypes.c_void_p(16), -16, ctypes.addressof(out), None) == EINVAL
+    assert lib.qmv_read_probe(ctypes.c_void_p(16), 0, ctypes.addressof(out), None) == 0
