@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--copies", type=int, default=8, help="weight copies rotated to defeat the MALL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
+    ap.add_argument("--profile-set", action="store_true",
+                    help="only the launches the kernel profiles describe: decode steps, full prefill passes and "
+                         "the output layer (no sweeps, chained, per-matrix, int8 or BitNet launches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB five times: the "
@@ -639,9 +642,13 @@ def main():
                                        "(%.1f MB in %.2f us)" % (stack.pool[0].numel() / 1e6, ceiling_ms * 1e3)},
     }
     log("prefill (512 tokens)")
-    result["prefill"] = bench_prefill(stack, dev, stream, per_matrix=not args.no_extras)
+    result["prefill"] = bench_prefill(stack, dev, stream, per_matrix=not (args.no_extras or args.profile_set))
     log("prefill %.1f us, %.1f TOPS" % (result["prefill"]["prefill_us"], result["prefill"]["TOPS"]))
-    if not args.no_extras:
+    if args.profile_set and not args.no_extras:
+        log("output layer")
+        result["extras"] = {"lmhead": bench_head(dev, stream)}
+        torch.cuda.empty_cache()
+    elif not args.no_extras:
         extras = {}
         try:
             log("decode variants")

@@ -172,7 +172,9 @@ int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64
  * qmv_gemm_prefill -- the same products for any number of tokens, computed
  * with int8 matrix cores ("Step 1": all prompt tokens go through each weight
  * matrix in one pass).  Ternary weights only.  Same arguments and results as
- * qmv_gemv, with 1 <= m <= 65536 per problem.
+ * qmv_gemv, with 1 <= m <= 65536 per problem.  The workspace also holds the
+ * kernel's tile tickets (zeroed by the table upload, left at zero by every
+ * launch), so launches that share a workspace must not overlap in time.
  */
 int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes,
                          uint32_t flags, void* stream);

@@ -8,7 +8,6 @@
 #include <cstring>
 #include <memory>
 #include <mutex>
-#include <queue>
 #include <vector>
 
 #include "qmv_internal.hpp"
@@ -365,18 +364,16 @@ int32_t check_prefill(const qmv_problem* probs, int32_t count)
     return QMV_OK;
 }
 
-constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin
 
-// Workspace of a prefill problem list: the problem table, the XCD-ordered
-// tile list (8 lists padded to the longest, bounded by 8 x all tiles) and a
-// block of zeros the kernel copies for activation columns past k.
+// Workspace of a prefill problem list: the problem table, the tile table (9
+// list offsets, every tile once, then the tickets) and a block of zeros the
+// kernel copies for activation columns past k.
 int64_t prefill_table_bytes(const qmv_problem* probs, int32_t count)
 {
     int64_t tiles = 0;
     for (int32_t i = 0; i < count; ++i) tiles += prefill_tiles(probs[i].m, probs[i].w.n);
-    // no XCD list can be longer than all tiles together
-    const int64_t bound = kXcds * tiles;
-    return round_up((int64_t)sizeof(DevProblem) * count, 256) + round_up(bound * 8, 256) + kPrefillZeroBytes;
+    return round_up((int64_t)sizeof(DevProblem) * count, 256) +
+           round_up((kXcds + 1 + tiles + kPrefillTicketWords) * 8, 256) + kPrefillZeroBytes;
 }
 
 }  // namespace
@@ -562,16 +559,28 @@ int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspac
         for (int64_t nt = 0; nt < gr.ntiles; ++nt)
             lists[x].push_back(((uint64_t)gr.slot << 48) | ((uint64_t)gr.mt << 32) | (uint64_t)nt);
     }
-    size_t longest = 0;
-    for (const auto& l : lists) longest = std::max(longest, l.size());
-    const int64_t grid = (int64_t)longest * kXcds;
-    if (pbytes + grid * 8 > need - kPrefillZeroBytes) return QMV_EWORKSPACE;  // cannot happen: need covers 8 x all tiles
-    uint64_t* te = reinterpret_cast<uint64_t*>(img.data() + pbytes);
-    for (int64_t b = 0; b < grid; ++b) {
-        const auto& l = lists[b % kXcds];
-        const size_t j = (size_t)(b / kXcds);
-        te[b] = j < l.size() ? l[j] : ~0ull;
+    // Persistent workgroups, two per compute unit: each starts on its XCD's
+    // list and takes tiles by ticket (the tickets follow the entries and start
+    // at zero; the kernel leaves them at zero).
+    int cus = 256;
+    device_cus(&cus);
+    size_t longest = 0, total = 0;
+    for (const auto& l : lists) {
+        longest = std::max(longest, l.size());
+        total += l.size();
     }
+    const int64_t per_xcd =
+        std::max<int64_t>(1, std::min<int64_t>({2 * std::max(1, cus / kXcds), kPrefillMaxGrid / kXcds, (int64_t)longest}));
+    const int64_t grid = per_xcd * kXcds;
+    if (pbytes + (kXcds + 1 + (int64_t)total + kPrefillTicketWords) * 8 > need - kPrefillZeroBytes)
+        return QMV_EWORKSPACE;  // cannot happen: need covers every tile
+    uint64_t* tt = reinterpret_cast<uint64_t*>(img.data() + pbytes);
+    uint64_t pos = 0;
+    for (int x = 0; x < kXcds; ++x) {
+        tt[x] = pos;
+        for (uint64_t e : lists[x]) tt[kXcds + 1 + pos++] = e;
+    }
+    tt[kXcds] = pos;
     const hipStream_t s = as_stream(stream);
     if (!(flags & QMV_F_TABLE_READY)) {
         hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, s);

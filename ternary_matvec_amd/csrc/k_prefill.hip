@@ -53,7 +53,10 @@ constexpr int kBBuf = 4 * 2 * 64 * 16;    // one staged weight buffer: wave x ro
 constexpr int kBNBuf = 2;                 // weight ring: read into registers one step ahead
 constexpr int kBOff = kANBuf * kABuf;
 constexpr int kEpiOff = kBOff + kBNBuf * kBBuf;
-constexpr int kPrefillLds = kEpiOff + 3 * kPBM * 4;   // + token sums (two halves) and scales: 79360 bytes
+constexpr int kNextOff = kEpiOff + 3 * kPBM * 4;      // + token sums (two halves) and scales
+constexpr int kPrefillLds = kNextOff + 16;             // + the next tile's index: 79376 bytes
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+constexpr int kBufStoreMaxN = 1 << 22;          // tile rows x n x 4 bytes stays below 2^31
 static_assert(kADma * 16 * kBlock == kABuf, "activation tile splits evenly over the copies");
 static_assert(2 * kPrefillLds <= 160 * 1024, "two workgroups per compute unit");
 
@@ -133,253 +136,417 @@ __device__ __forceinline__ uint32_t x_bytes(const QMV_GLOBAL int8_t* xr, int col
     return v;
 }
 
-__global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restrict__ probs,
-                                                       const uint64_t* __restrict__ tiles,
-                                                       const int8_t* __restrict__ zeros)
-{
-    extern __shared__ __align__(16) uint8_t smem[];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int g = lane >> 5;  // which 16 K-bytes of the MFMA operands this lane holds
-    const int l32 = lane & 31;
+// Uniform description of one tile.
+struct PTile {
+    const DevProblem* P;
+    const QMV_GLOBAL v4u32* wbase;
+    const QMV_GLOBAL int8_t* xbase;
+    int n, k, mtok, C, m0, n0, steps;
+    bool fast;               // k % 16 == 0 and 16-byte aligned rows: activation copies
+};
 
-    const uint64_t te = tiles[blockIdx.x];
-    if (te == ~0ull) return;  // padding entry of the XCD-ordered tile list
-    const DevProblem* P = probs + (int)(te >> 48);
+__device__ __forceinline__ PTile tile_of(const DevProblem* probs, uint64_t te)
+{
+    PTile T;
+    T.P = probs + (int)(te >> 48);
     const int mt = (int)((te >> 32) & 0xFFFF);
     const int nt = (int)(te & 0xFFFFFFFFu);
-    const int n = P->n, k = P->k, mtok = P->m, C = P->chunks;
-    const int m0 = mt * kPBM, n0 = nt * kPBN;
-    const int steps = (C + 1) >> 1;
+    T.n = T.P->n;
+    T.k = T.P->k;
+    T.mtok = T.P->m;
+    T.C = T.P->chunks;
+    T.m0 = mt * kPBM;
+    T.n0 = nt * kPBN;
+    T.steps = (T.C + 1) >> 1;
+    T.wbase = gload_ptr(reinterpret_cast<const v4u32*>(T.P->w));
+    T.xbase = gload_ptr(T.P->x8);
+    T.fast = ((T.k & 15) == 0) && ((reinterpret_cast<uintptr_t>(T.P->x8) & 15) == 0);
+    return T;
+}
 
-    // ---- weights: two 32-row blocks per wave, HBM -> LDS ------------------------------
-    // lane l of a row block -> 16 bytes at l * 16 of the wave's region; each
-    // lane reads its own chunk back.  Rows past n repeat row n - 1 (never stored).
-    const QMV_GLOBAL v4u32* wbase = gload_ptr(reinterpret_cast<const v4u32*>(P->w));
-    int brow[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int r = n0 + 64 * wave + 32 * nb + l32;
-        brow[nb] = r < n ? r : n - 1;
-    }
-    auto copy_b = [&](int s, int buf, int nb) {
-        const int c = min(2 * s + g, C - 1);
-        copy16_to_lds(wbase + (size_t)c * n + brow[nb], smem + kBOff + buf * kBBuf + 1024 * (2 * wave + nb));
-    };
-    auto stage_b = [&](int s, int buf) {
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) copy_b(s, buf, nb);
-    };
-    auto read_b = [&](int buf, v4u32 (&braw)[2]) {
-        const uint8_t* bbuf = smem + kBOff + buf * kBBuf;
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-            braw[nb] = *reinterpret_cast<const v4u32*>(bbuf + 1024 * (2 * wave + nb) + 16 * lane);
-    };
+// Per-lane values of the copies.  Activation copy j of wave w fills stored
+// slots 64 (5w + j) + lane, slot f = row f / 10 at stored piece f % 10.
+struct PLane {
+    int lane, g, l32;
+    int a_rp[kADma];   // tile row << 4 | source piece of each activation copy
+};
 
-    // ---- activations: 128 token rows x 10 pieces per step --------------------------------
-    // Fast path (k % 16 == 0, 16-byte aligned rows): copy j of wave w fills
-    // stored slots 64 (5w + j) + lane, slot f = row f / 10 at stored piece
-    // f % 10.  Tokens past m repeat token m - 1 (never stored).
-    const QMV_GLOBAL int8_t* xbase = gload_ptr(P->x8);
-    const QMV_GLOBAL int8_t* zsrc = gload_ptr(zeros);
-    const bool fast = ((k & 15) == 0) && ((reinterpret_cast<uintptr_t>(P->x8) & 15) == 0);
-    int a_tp[kADma];   // token << 4 | source piece of each copy
+__device__ __forceinline__ PLane lane_of(int tid, int wave)
+{
+    PLane L;
+    L.lane = tid & (kWave - 1);
+    L.g = L.lane >> 5;
+    L.l32 = L.lane & 31;
 #pragma unroll
     for (int j = 0; j < kADma; ++j) {
-        const int f = 64 * (kADma * wave + j) + lane;
+        const int f = 64 * (kADma * wave + j) + L.lane;
         const int r = f / kPieces;
         const int q = f - r * kPieces;                     // stored piece
         const int p = q - ((r >> 3) & 1);                  // source piece
-        a_tp[j] = (min(m0 + r, mtok - 1) << 4) | (p < 0 ? p + kPieces : p);
+        L.a_rp[j] = (r << 4) | (p < 0 ? p + kPieces : p);
     }
-    auto copy_a = [&](int s, int buf, int j) {
-        const int col = 160 * s + 16 * (a_tp[j] & 15);
-        const QMV_GLOBAL int8_t* src = col < k ? xbase + (size_t)(a_tp[j] >> 4) * k + col : zsrc;
-        copy16_to_lds(src, smem + buf * kABuf + 1024 * (kADma * wave + j));
-    };
-    auto stage_a = [&](int s, int buf) {
-        uint8_t* abuf = smem + buf * kABuf;
-        if (fast) {
-#pragma unroll
-            for (int j = 0; j < kADma; ++j) copy_a(s, buf, j);
-        } else {
-            // thread t writes pieces 5h .. 5h+4 of row r (h = t / 128), zero past column k
-            const int r = tid & (kPBM - 1), h = tid >> 7;
-            const int tok = m0 + r;
-            const QMV_GLOBAL int8_t* xr = xbase + (size_t)min(tok, mtok - 1) * k;
-#pragma unroll
-            for (int j = 0; j < 5; ++j) {
-                const int p = 5 * h + j;
-                uint32_t* dst = reinterpret_cast<uint32_t*>(abuf + apos(r, p));
-#pragma unroll
-                for (int d = 0; d < 4; ++d) dst[d] = tok < mtok ? x_bytes(xr, 160 * s + 16 * p + 4 * d, k) : 0u;
-            }
-        }
-    };
-    // Sum of row (tid % 128)'s staged columns, pieces 5h .. 5h+4 (h = tid / 128),
-    // one piece per plane; zero past k.
-    int rsum = 0;
-    // pieces 5h .. 5h+3 of a row are consecutive; only 5h+4 can wrap to piece 0
-    const int sbase = apos(tid & (kPBM - 1), 5 * (tid >> 7));
-    const int slast = apos(tid & (kPBM - 1), 5 * (tid >> 7) + 4);
-    auto sum_piece = [&](int buf, int j) {
-        const uint4 v = *reinterpret_cast<const uint4*>(smem + buf * kABuf + (j < 4 ? sbase + 16 * j : slast));
-        rsum = dot4(v.x, 0x01010101u, rsum);
-        rsum = dot4(v.y, 0x01010101u, rsum);
-        rsum = dot4(v.z, 0x01010101u, rsum);
-        rsum = dot4(v.w, 0x01010101u, rsum);
-    };
-    // This lane's activation operand of plane i is piece 5g + i of token row
-    // 32 tb + l32: a per-lane offset (rows of a lane share one rotation).
-    const int abase = apos(l32, 5 * g);       // pieces 5g .. 5g+3 are consecutive
-    const int alast = apos(l32, 5 * g + 4);   // piece 5g+4 can wrap to piece 0
-    auto aoff = [&](int i) { return i < 4 ? abase + 16 * i : alast; };
+    return L;
+}
 
-    v16i32 acc[4][2];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[tb][nb] = v16i32{};
+// Weights: two 32-row blocks per wave, HBM -> LDS; lane l of a row block ->
+// 16 bytes at l * 16 of the wave's region.  Rows past n repeat row n - 1
+// (never stored).
+__device__ __forceinline__ void copy_b(const PTile& T, const PLane& L, uint8_t* smem, int wave, int s, int buf, int nb)
+{
+    const int c = min(2 * s + L.g, T.C - 1);
+    const int row = min(T.n0 + 64 * wave + 32 * nb + L.l32, T.n - 1);
+    copy16_to_lds(T.wbase + (size_t)c * T.n + row, smem + kBOff + buf * kBBuf + 1024 * (2 * wave + nb));
+}
 
-    // Pipeline: at step s the MFMAs use the activations of step s (LDS ring slot
-    // s % 3) and the weights of step s (registers, read from the LDS ring during
-    // step s - 1, digits expanded one dword per plane).  Copies for step s + 2
-    // are issued during step s, weights first (plane 0), then the activations
-    // spread over planes 1..4 so that no wave stalls long on a burst of copies:
-    // "weights of s + 2 and everything older have landed" is vmcnt(activation
-    // copies of one step).
-    stage_b(0, 0);
-    stage_a(0, 0);
-    if (steps > 1) {
-        stage_b(1, 1);
-        stage_a(1, 1);
+// Activations (fast path: k % 16 == 0, 16-byte aligned rows): 128 token rows
+// x 10 pieces per step; tokens past m repeat token m - 1 (never stored),
+// columns past k come from the block of zeros.
+__device__ __forceinline__ void copy_a(const PTile& T, const PLane& L, uint8_t* smem, const QMV_GLOBAL int8_t* zsrc,
+                                       int wave, int s, int buf, int j)
+{
+    const int col = 160 * s + 16 * (L.a_rp[j] & 15);
+    const int tok = min(T.m0 + (L.a_rp[j] >> 4), T.mtok - 1);
+    const QMV_GLOBAL int8_t* src = col < T.k ? T.xbase + (size_t)tok * T.k + col : zsrc;
+    copy16_to_lds(src, smem + buf * kABuf + 1024 * (kADma * wave + j));
+}
+
+// The copies of steps 0 and 1 of a fast-path tile.
+__device__ __forceinline__ void first_copies_fast(const PTile& T, const PLane& L, uint8_t* smem,
+                                                  const QMV_GLOBAL int8_t* zsrc, int wave)
+{
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        if (s == 1 && T.steps < 2) break;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) copy_b(T, L, smem, wave, s, s, nb);
+#pragma unroll
+        for (int j = 0; j < kADma; ++j) copy_a(T, L, smem, zsrc, wave, s, s, j);
     }
-    wait_vmcnt<0>();
-    lds_barrier();
-    v4u32 braw[2];
-    read_b(0, braw);
-    uint32_t nat[2][20];   // the step's digits in natural column order, 4 per dword
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][0], &nat[nb][0]);
+}
 
-    for (int s = 0; s < steps; ++s) {
-        const int buf = s % kANBuf;
-        const bool more2 = s + 2 < steps;
-        const int abuf2 = (s + 2) % kANBuf;
-        if (more2 && !fast) stage_a(s + 2, abuf2);
-        // the next step's packed weights (after the last step: stale, expanded and
-        // never used, which keeps the MFMA block free of branches)
-        v4u32 bnext[2];
-        read_b((s + 1) & 1, bnext);
-        uint32_t nxt[2][5];
-        const uint8_t* arow = smem + buf * kABuf;   // + aoff: this lane's token row and piece
-        v4i32 aop[2][4];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) aop[0][tb] = *reinterpret_cast<const v4i32*>(arow + 32 * tb * kARow + aoff(0));
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            // copies for step s + 2: weights (into the slot of step s's weights,
-            // already in registers), then activations
-            if (more2) {
-                if (i == 0) stage_b(s + 2, s & 1);
-                else if (fast) {
-                    if (i == 1) copy_a(s + 2, abuf2, 0);
-                    copy_a(s + 2, abuf2, i);
-                }
-            }
-            sum_piece(buf, i);
-            // plane i covers columns 16i .. 16i+15 of each lane's chunk: digit
-            // dwords 4i .. 4i+3, from packed dwords i-1 and i (expanded a plane ahead)
-            if (i < 4) {
-#pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
-                    aop[(i + 1) & 1][tb] = *reinterpret_cast<const v4i32*>(arow + 32 * tb * kARow + aoff(i + 1));
-            }
-            if (i < 3) {
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][i + 1], &nat[nb][5 * (i + 1)]);
-            } else if (i == 3) {
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) natural_digits(bnext[nb][0], nxt[nb]);
-            }
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const v4i32 wop = {(int)nat[nb][4 * i], (int)nat[nb][4 * i + 1], (int)nat[nb][4 * i + 2],
-                                       (int)nat[nb][4 * i + 3]};
-                    acc[tb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[i & 1][tb], wop, acc[tb][nb], 0, 0, 0);
-                }
-            // one MFMA (its operands are ready), the next plane's LDS reads, then
-            // one MFMA per few VALU ops of the next dword's expansion
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-#pragma unroll
-            for (int q = 1; q < 8; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+// Next tile for a workgroup (one lane calls this): a ticket from list x, or
+// from the following lists once x is used up; -1 when every list is.
+__device__ __forceinline__ int take_tile(const uint64_t* table, uint32_t* tickets, int& x, int& tries)
+{
+    while (tries < kXcds) {
+        const int b = (int)table[x], e = (int)table[x + 1];
+        if (b < e) {
+            const uint32_t t = atomicAdd(tickets + x, 1u);
+            if (t < (uint32_t)(e - b)) return b + (int)t;
         }
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            braw[nb] = bnext[nb];
-#pragma unroll
-            for (int u = 0; u < 5; ++u) nat[nb][u] = nxt[nb][u];
-        }
-        if (s + 1 < steps) {
-            // activations of s + 1 and weights of s + 2 have landed once only the
-            // activation copies of s + 2 may still fly
-            if (more2 && fast) wait_vmcnt<kADma>();
-            else wait_vmcnt<0>();
-            lds_barrier();
-        }
+        x = x + 1 == kXcds ? 0 : x + 1;
+        ++tries;
     }
+    return -1;
+}
 
-    // ---- epilogue ---------------------------------------------------------------------
-    // Token sums and scales go to LDS.  Accumulator register 4q+e of lane l is
-    // token 8q + 4g + e of its 32-token block and row l % 32 of its 32-row block,
-    // so each register's half-wave holds 32 consecutive outputs of one token: a
-    // whole 128-byte line, stored straight from the registers.
-    int* tsum = reinterpret_cast<int*>(smem + kEpiOff);                 // [2][128]
-    float* tscale = reinterpret_cast<float*>(smem + kEpiOff + 2 * kPBM * 4);
-    tsum[tid] = rsum;   // half tid / 128 of row tid % 128
-    if (tid < kPBM) {
-        const int tok = m0 + tid;
-        tscale[tid] = tok < mtok ? gload_ptr(P->sx)[tok] * *gload_ptr(P->sw) : 0.0f;
+// A workgroup that found no tile left counts itself out; the last one resets
+// the tickets for the next launch on the stream.
+__device__ __forceinline__ void finish_tiles(uint32_t* tickets)
+{
+    if (atomicAdd(tickets + kXcds, 1u) == gridDim.x - 1) {
+#pragma unroll
+        for (int i = 0; i <= kXcds; ++i) __hip_atomic_store(tickets + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Persistent: the table holds 8 tile lists (offsets table[0..8], entries
+// after them), one per XCD, and then the tickets.  Workgroup b starts on the
+// list of its XCD (b % 8, round-robin dispatch) and takes tiles in list order
+// with a ticket each; when that list is used up it helps with the others.
+// The next tile is known before a tile's epilogue, so the copies that start
+// its K loop are issued before the output stores and their latency and the
+// tile set-up hide behind them.
+__global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restrict__ probs,
+                                                       const uint64_t* __restrict__ table,
+                                                       const int8_t* __restrict__ zeros)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+
+    const uint64_t* ent = table + kXcds + 1;
+    uint32_t* tickets = const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(ent + table[kXcds]));
+    int* next_lds = reinterpret_cast<int*>(smem + kNextOff);
+    const QMV_GLOBAL int8_t* zsrc = gload_ptr(zeros);
+    // ticket state, used by lane 0 of wave 0 only
+    int tx = (int)(blockIdx.x % kXcds), ttries = 0;
+    if (threadIdx.x == 0) {
+        const int first = take_tile(table, tickets, tx, ttries);
+        if (first < 0) finish_tiles(tickets);
+        next_lds[0] = first;
     }
     __syncthreads();
-    QMV_GLOBAL float* y = gstore_ptr(P->y);
-    QMV_GLOBAL int32_t* accout = P->acc ? gstore_ptr(P->acc) : nullptr;
-    const bool full = m0 + kPBM <= mtok && n0 + kPBN <= n;
-    const int rl = n0 + 64 * wave + l32;   // this lane's row in row block 0 (+32 in block 1)
-    const int loff = 4 * g * n + rl;       // + (token block base + 8q + e) * n
+    int it = __builtin_amdgcn_readfirstlane(next_lds[0]);
+    if (it < 0) return;
+
+    PTile T = tile_of(probs, ent[it]);
+    bool staged = false;   // the copies of the tile's first two steps are issued
+    for (;;) {
+        // Per-lane values come from an opaque copy of the thread index, so the
+        // compiler derives them inside the tile loop instead of hoisting dozens
+        // of them out of it into registers the K loop needs.
+        int tid = (int)threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const PLane L = lane_of(tid, wave);
+        const int lane = L.lane, g = L.g, l32 = L.l32;
+
+        auto stage_b = [&](const PTile& T, int s, int buf) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
+            for (int nb = 0; nb < 2; ++nb) copy_b(T, L, smem, wave, s, buf, nb);
+        };
+        auto read_b = [&](int buf, v4u32 (&braw)[2]) {
+            const uint8_t* bbuf = smem + kBOff + buf * kBBuf;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int t0 = 32 * tb + 8 * q + 4 * g;   // tile token of register 4q (+e)
-            const int4 ta = *reinterpret_cast<const int4*>(tsum + t0);
-            const int4 tc = *reinterpret_cast<const int4*>(tsum + kPBM + t0);
-            const float4 sc4 = *reinterpret_cast<const float4*>(tscale + t0);
-            const int tsv[4] = {ta.x + tc.x, ta.y + tc.y, ta.z + tc.z, ta.w + tc.w};
-            const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+            for (int nb = 0; nb < 2; ++nb)
+                braw[nb] = *reinterpret_cast<const v4u32*>(bbuf + 1024 * (2 * wave + nb) + 16 * lane);
+        };
+        auto stage_a = [&](const PTile& T, int s, int buf) {
+            uint8_t* abuf = smem + buf * kABuf;
+            if (T.fast) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const size_t urow = (size_t)(m0 + 32 * tb + 8 * q + e) * n;   // uniform part of the offset
+                for (int j = 0; j < kADma; ++j) copy_a(T, L, smem, zsrc, wave, s, buf, j);
+            } else {
+                // thread t writes pieces 5h .. 5h+4 of row r (h = t / 128), zero past column k
+                const int r = tid & (kPBM - 1), h = tid >> 7;
+                const int tok = T.m0 + r;
+                const QMV_GLOBAL int8_t* xr = T.xbase + (size_t)min(tok, T.mtok - 1) * T.k;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
-                    const int v = acc[tb][nb][4 * q + e] - tsv[e];
-                    if (full || (m0 + t0 + e < mtok && rl + 32 * nb < n)) {
-                        y[urow + loff + 32 * nb] = (float)v * scv[e];
-                        if (accout) accout[urow + loff + 32 * nb] = v;
+                for (int j = 0; j < 5; ++j) {
+                    const int p = 5 * h + j;
+                    uint32_t* dst = reinterpret_cast<uint32_t*>(abuf + apos(r, p));
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) dst[d] = tok < T.mtok ? x_bytes(xr, 160 * s + 16 * p + 4 * d, T.k) : 0u;
+                }
+            }
+        };
+        // the copies of steps 0 and 1 of a tile
+        auto stage_first = [&](const PTile& T) {
+            stage_b(T, 0, 0);
+            stage_a(T, 0, 0);
+            if (T.steps > 1) {
+                stage_b(T, 1, 1);
+                stage_a(T, 1, 1);
+            }
+        };
+        // Sum of row (tid % 128)'s staged columns, pieces 5h .. 5h+4 (h = tid / 128),
+        // one piece per plane; zero past k.
+        int rsum = 0;
+        // pieces 5h .. 5h+3 of a row are consecutive; only 5h+4 can wrap to piece 0
+        const int sbase = apos(tid & (kPBM - 1), 5 * (tid >> 7));
+        const int slast = apos(tid & (kPBM - 1), 5 * (tid >> 7) + 4);
+        auto sum_piece = [&](int buf, int j) {
+            const uint4 v = *reinterpret_cast<const uint4*>(smem + buf * kABuf + (j < 4 ? sbase + 16 * j : slast));
+            rsum = dot4(v.x, 0x01010101u, rsum);
+            rsum = dot4(v.y, 0x01010101u, rsum);
+            rsum = dot4(v.z, 0x01010101u, rsum);
+            rsum = dot4(v.w, 0x01010101u, rsum);
+        };
+        // This lane's activation operand of plane i is piece 5g + i of token row
+        // 32 tb + l32: a per-lane offset (rows of a lane share one rotation).
+        const int abase = apos(l32, 5 * g);       // pieces 5g .. 5g+3 are consecutive
+        const int alast = apos(l32, 5 * g + 4);   // piece 5g+4 can wrap to piece 0
+        auto aoff = [&](int i) { return i < 4 ? abase + 16 * i : alast; };
+        int* tsum = reinterpret_cast<int*>(smem + kEpiOff);                 // [2][128]
+        float* tscale = reinterpret_cast<float*>(smem + kEpiOff + 2 * kPBM * 4);
+        if (!staged) stage_first(T);
+        const int steps = T.steps;
+        v16i32 acc[4][2];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) acc[tb][nb] = v16i32{};
+        rsum = 0;
+
+        // Pipeline: at step s the MFMAs use the activations of step s (LDS ring
+        // slot s % 3) and the weights of step s (registers, read from the LDS ring
+        // during step s - 1, digits expanded one dword per plane).  Copies for step
+        // s + 2 are issued during step s, weights first (plane 0), then the
+        // activations spread over planes 1..4 so that no wave stalls long on a
+        // burst of copies: "weights of s + 2 and everything older have landed" is
+        // vmcnt(activation copies of one step).  The copies of steps 0 and 1 were
+        // issued before the previous tile's stores; waiting for them also waits
+        // for those stores.
+        wait_vmcnt<0>();
+        lds_barrier();
+        v4u32 braw[2];
+        read_b(0, braw);
+        uint32_t nat[2][20];   // the step's digits in natural column order, 4 per dword
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][0], &nat[nb][0]);
+
+        int nxt = -1;   // lane 0 of wave 0: the next tile, asked for during the last step
+        for (int s = 0; s < steps; ++s) {
+            if (s + 1 == steps && tid == 0) nxt = take_tile(table, tickets, tx, ttries);
+            const int buf = s % kANBuf;
+            const bool more2 = s + 2 < steps;
+            const int abuf2 = (s + 2) % kANBuf;
+            if (more2 && !T.fast) stage_a(T, s + 2, abuf2);
+            // the next step's packed weights (after the last step: stale, expanded and
+            // never used, which keeps the MFMA block free of branches)
+            v4u32 bnext[2];
+            read_b((s + 1) & 1, bnext);
+            uint32_t nxt[2][5];
+            const uint8_t* arow = smem + buf * kABuf;   // + aoff: this lane's token row and piece
+            v4i32 aop[2][4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) aop[0][tb] = *reinterpret_cast<const v4i32*>(arow + 32 * tb * kARow + aoff(0));
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                // copies for step s + 2: weights (into the slot of step s's weights,
+                // already in registers), then activations
+                if (more2) {
+                    if (i == 0) stage_b(T, s + 2, s & 1);
+                    else if (T.fast) {
+                        if (i == 1) copy_a(T, L, smem, zsrc, wave, s + 2, abuf2, 0);
+                        copy_a(T, L, smem, zsrc, wave, s + 2, abuf2, i);
+                    }
+                }
+                sum_piece(buf, i);
+                // plane i covers columns 16i .. 16i+15 of each lane's chunk: digit
+                // dwords 4i .. 4i+3, from packed dwords i-1 and i (expanded a plane ahead)
+                if (i < 4) {
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+                        aop[(i + 1) & 1][tb] = *reinterpret_cast<const v4i32*>(arow + 32 * tb * kARow + aoff(i + 1));
+                }
+                if (i < 3) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][i + 1], &nat[nb][5 * (i + 1)]);
+                } else if (i == 3) {
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) natural_digits(bnext[nb][0], nxt[nb]);
+                }
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) {
+                        const v4i32 wop = {(int)nat[nb][4 * i], (int)nat[nb][4 * i + 1], (int)nat[nb][4 * i + 2],
+                                           (int)nat[nb][4 * i + 3]};
+                        acc[tb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop[i & 1][tb], wop, acc[tb][nb], 0, 0, 0);
+                    }
+                // one MFMA (its operands are ready), the next plane's LDS reads, then
+                // one MFMA per few VALU ops of the next dword's expansion
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+#pragma unroll
+                for (int q = 1; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                braw[nb] = bnext[nb];
+#pragma unroll
+                for (int u = 0; u < 5; ++u) nat[nb][u] = nxt[nb][u];
+            }
+            if (s + 1 < steps) {
+                // activations of s + 1 and weights of s + 2 have landed once only the
+                // activation copies of s + 2 may still fly
+                if (more2 && T.fast) wait_vmcnt<kADma>();
+                else wait_vmcnt<0>();
+                lds_barrier();
+            }
+        }
+
+        // ---- epilogue ---------------------------------------------------------------------
+        // Token sums and scales go to LDS.  Accumulator register 4q+e of lane l is
+        // token 8q + 4g + e of its 32-token block and row l % 32 of its 32-row block,
+        // so each register's half-wave holds 32 consecutive outputs of one token: a
+        // whole 128-byte line, stored straight from the registers.
+        // Lane values rederived from a fresh opaque thread index: nothing per-lane
+        // has to stay live across the K loop for the epilogue.
+        int te = (int)threadIdx.x;
+        asm volatile("" : "+v"(te));
+        const PLane LE = lane_of(te, wave);
+        tsum[te] = rsum;   // half te / 128 of row te % 128
+        if (te < kPBM) {
+            const int tok = T.m0 + te;
+            tscale[te] = tok < T.mtok ? gload_ptr(T.P->sx)[tok] * *gload_ptr(T.P->sw) : 0.0f;
+        }
+        if (te == 0) {
+            if (nxt < 0) finish_tiles(tickets);
+            next_lds[0] = nxt;
+        }
+        // every wave is past its last read of the copy rings
+        __syncthreads();
+        // the next tile's first copies, ahead of this tile's stores (fast path;
+        // the byte-wise path stages after the stores)
+        const PTile E = T;
+        it = __builtin_amdgcn_readfirstlane(next_lds[0]);
+        const bool more = it >= 0;
+        staged = false;
+        if (more) {
+            T = tile_of(probs, ent[it]);
+            if (T.fast) {
+                first_copies_fast(T, LE, smem, zsrc, wave);
+                staged = true;
+            }
+        }
+        const bool full = E.m0 + kPBM <= E.mtok && E.n0 + kPBN <= E.n;
+        const int rl = E.n0 + 64 * wave + LE.l32;   // this lane's row in row block 0 (+32 in block 1)
+        const int loff = 4 * LE.g * E.n + rl;       // + (token block base + 8q + e) * n
+        if (full && !E.P->acc && E.n < kBufStoreMaxN) {
+            // The whole tile is in range: buffer stores over the tile's 128 token
+            // rows, the lane's offset in a VGPR fixed for the tile and the token's
+            // row offset in an SGPR, so a store costs the three VALU of its value.
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(E.P->y + (size_t)E.m0 * E.n), (short)0, kPBM * 4 * E.n, (int)kRsrcWord3);
+            const int voff = 4 * loff;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int t0 = 32 * tb + 8 * q + 4 * LE.g;
+                    const int4 ta = *reinterpret_cast<const int4*>(tsum + t0);
+                    const int4 tc = *reinterpret_cast<const int4*>(tsum + kPBM + t0);
+                    const float4 sc4 = *reinterpret_cast<const float4*>(tscale + t0);
+                    const int tsv[4] = {ta.x + tc.x, ta.y + tc.y, ta.z + tc.z, ta.w + tc.w};
+                    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int soff = 4 * (32 * tb + 8 * q + e) * E.n;
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb) {
+                            const float v = (float)(acc[tb][nb][4 * q + e] - tsv[e]) * scv[e];
+                            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, voff + 128 * nb, soff, 0);
+                        }
+                    }
+                }
+            }
+        } else {
+            QMV_GLOBAL float* y = gstore_ptr(E.P->y);
+            QMV_GLOBAL int32_t* accout = E.P->acc ? gstore_ptr(E.P->acc) : nullptr;
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int t0 = 32 * tb + 8 * q + 4 * LE.g;   // tile token of register 4q (+e)
+                    const int4 ta = *reinterpret_cast<const int4*>(tsum + t0);
+                    const int4 tc = *reinterpret_cast<const int4*>(tsum + kPBM + t0);
+                    const float4 sc4 = *reinterpret_cast<const float4*>(tscale + t0);
+                    const int tsv[4] = {ta.x + tc.x, ta.y + tc.y, ta.z + tc.z, ta.w + tc.w};
+                    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const size_t urow = (size_t)(E.m0 + 32 * tb + 8 * q + e) * E.n;   // uniform part of the offset
+#pragma unroll
+                        for (int nb = 0; nb < 2; ++nb) {
+                            const int v = acc[tb][nb][4 * q + e] - tsv[e];
+                            if (full || (E.m0 + t0 + e < E.mtok && rl + 32 * nb < E.n)) {
+                                y[urow + loff + 32 * nb] = (float)v * scv[e];
+                                if (accout) accout[urow + loff + 32 * nb] = v;
+                            }
+                        }
                     }
                 }
             }
         }
+        if (!more) break;
+        // tsum and tscale are rewritten only after the next tile's K loop, whose
+        // barriers every wave passes after its reads above
     }
 }
 
@@ -387,21 +554,13 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
 
 int64_t prefill_tiles(int64_t m, int64_t n) { return ((m + kPBM - 1) / kPBM) * ((n + kPBN - 1) / kPBN); }
 
-void prefill_tile_entries(int32_t slot, int64_t m, int64_t n, uint64_t* out)
-{
-    const int64_t mts = (m + kPBM - 1) / kPBM, nts = (n + kPBN - 1) / kPBN;
-    int64_t i = 0;
-    for (int64_t mt = 0; mt < mts; ++mt)
-        for (int64_t nt = 0; nt < nts; ++nt) out[i++] = ((uint64_t)slot << 48) | ((uint64_t)mt << 32) | (uint64_t)nt;
-}
-
-hipError_t launch_prefill(const DevProblem* probs, const uint64_t* tiles, int64_t tile_count, const int8_t* zeros,
+hipError_t launch_prefill(const DevProblem* probs, const uint64_t* table, int64_t grid, const int8_t* zeros,
                           hipStream_t s)
 {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_prefill, dim3((unsigned)tile_count), dim3(kBlock), kPrefillLds, s, probs, tiles, zeros);
+    hipLaunchKernelGGL(k_prefill, dim3((unsigned)grid), dim3(kBlock), kPrefillLds, s, probs, table, zeros);
     return hipGetLastError();
 }
 

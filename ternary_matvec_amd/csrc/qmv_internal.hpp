@@ -98,13 +98,17 @@ size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes);
 int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes);
 hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,
                               int32_t slot_bytes, hipStream_t s);
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin over them
 // Prefill (int8 matrix cores): tiles of 128 tokens x 256 rows.
 constexpr int64_t kPrefillTileM = 128;
 constexpr int64_t kPrefillTileN = 256;
 constexpr int64_t kPrefillZeroBytes = 256;   // block of zeros at the end of the prefill workspace
+constexpr int64_t kPrefillMaxGrid = 1024;     // persistent workgroups per launch, at most
+constexpr int64_t kPrefillTicketWords = 8;    // 64-bit words after the entries: 8 list tickets + 1 count (uint32)
 int64_t prefill_tiles(int64_t m, int64_t n);
-void prefill_tile_entries(int32_t slot, int64_t m, int64_t n, uint64_t* out);
-hipError_t launch_prefill(const DevProblem* probs, const uint64_t* tiles, int64_t tile_count, const int8_t* zeros,
+// table: 9 offsets (list x = entries [table[x], table[x + 1])), the entries
+// (slot << 48 | token tile << 32 | row tile), then the zeroed tickets.
+hipError_t launch_prefill(const DevProblem* probs, const uint64_t* table, int64_t grid, const int8_t* zeros,
                           hipStream_t s);
 hipError_t launch_read_probe(const void* data, int64_t bytes, uint32_t* out, int cus, hipStream_t s);
 hipError_t launch_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, int32_t* idx,
