@@ -98,6 +98,13 @@ __device__ __forceinline__ uint32_t digit2(uint32_t prev, uint32_t cur)
     return __builtin_bit_cast(uint32_t, __builtin_bit_cast(s16x2, prev) * m3 + __builtin_bit_cast(s16x2, cur));
 }
 
+// The same for 4 bytes per lane: lane i's dword lands at lds + 4 i.
+__device__ __forceinline__ void copy4_to_lds(const void QMV_GLOBAL* src, const uint8_t* lds)
+{
+    const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)lds;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(a) : "memory");
+}
+
 // One packed dword (20 trits, columns 0..19 relative) -> five dwords of
 // digits d = t + 1 in natural column order: nat[u] holds columns 4u .. 4u+3.
 __device__ __forceinline__ void natural_digits(uint32_t w, uint32_t* nat)
@@ -141,6 +148,10 @@ struct PTile {
     const DevProblem* P;
     const QMV_GLOBAL v4u32* wbase;
     const QMV_GLOBAL int8_t* xbase;
+    float* y;
+    int32_t* acc;
+    const float* sx;
+    float sw;
     int n, k, mtok, C, m0, n0, steps;
     bool fast;               // k % 16 == 0 and 16-byte aligned rows: activation copies
 };
@@ -160,6 +171,10 @@ __device__ __forceinline__ PTile tile_of(const DevProblem* probs, uint64_t te)
     T.steps = (T.C + 1) >> 1;
     T.wbase = gload_ptr(reinterpret_cast<const v4u32*>(T.P->w));
     T.xbase = gload_ptr(T.P->x8);
+    T.y = T.P->y;
+    T.acc = T.P->acc;
+    T.sx = T.P->sx;
+    T.sw = *cload_ptr(T.P->sw);
     T.fast = ((T.k & 15) == 0) && ((reinterpret_cast<uintptr_t>(T.P->x8) & 15) == 0);
     return T;
 }
@@ -224,14 +239,17 @@ __device__ __forceinline__ void first_copies_fast(const PTile& T, const PLane& L
     }
 }
 
-// Next tile for a workgroup (one lane calls this): a ticket from list x, or
-// from the following lists once x is used up; -1 when every list is.
-__device__ __forceinline__ int take_tile(const uint64_t* table, uint32_t* tickets, int& x, int& tries)
+// Next tile for a workgroup, called by all of wave 0 (lane 0 takes the
+// tickets, so x and tries stay wave-uniform): a ticket from list x, or from
+// the following lists once x is used up; -1 when every list is.
+__device__ __forceinline__ int take_tile(const uint64_t* table, uint32_t* tickets, int lane, int& x, int& tries)
 {
     while (tries < kXcds) {
         const int b = (int)table[x], e = (int)table[x + 1];
         if (b < e) {
-            const uint32_t t = atomicAdd(tickets + x, 1u);
+            uint32_t t = 0;
+            if (lane == 0) t = atomicAdd(tickets + x, 1u);
+            t = __builtin_amdgcn_readfirstlane(t);
             if (t < (uint32_t)(e - b)) return b + (int)t;
         }
         x = x + 1 == kXcds ? 0 : x + 1;
@@ -240,8 +258,8 @@ __device__ __forceinline__ int take_tile(const uint64_t* table, uint32_t* ticket
     return -1;
 }
 
-// A workgroup that found no tile left counts itself out; the last one resets
-// the tickets for the next launch on the stream.
+// A workgroup that found no tile left counts itself out (lane 0 of wave 0);
+// the last one resets the tickets for the next launch on the stream.
 __device__ __forceinline__ void finish_tiles(uint32_t* tickets)
 {
     if (atomicAdd(tickets + kXcds, 1u) == gridDim.x - 1) {
@@ -268,12 +286,14 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
     uint32_t* tickets = const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(ent + table[kXcds]));
     int* next_lds = reinterpret_cast<int*>(smem + kNextOff);
     const QMV_GLOBAL int8_t* zsrc = gload_ptr(zeros);
-    // ticket state, used by lane 0 of wave 0 only
+    // ticket state, used by wave 0 only (wave-uniform)
     int tx = (int)(blockIdx.x % kXcds), ttries = 0;
-    if (threadIdx.x == 0) {
-        const int first = take_tile(table, tickets, tx, ttries);
-        if (first < 0) finish_tiles(tickets);
-        next_lds[0] = first;
+    if (wave == 0) {
+        const int first = take_tile(table, tickets, (int)threadIdx.x, tx, ttries);
+        if (threadIdx.x == 0) {
+            if (first < 0) finish_tiles(tickets);
+            next_lds[0] = first;
+        }
     }
     __syncthreads();
     int it = __builtin_amdgcn_readfirstlane(next_lds[0]);
@@ -374,9 +394,17 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) natural_digits(braw[nb][0], &nat[nb][0]);
 
-        int nxt = -1;   // lane 0 of wave 0: the next tile, asked for during the last step
+        uint32_t tk = 0;   // lane 0 of wave 0: a ticket of list tx, taken during the last step
         for (int s = 0; s < steps; ++s) {
-            if (s + 1 == steps && tid == 0) nxt = take_tile(table, tickets, tx, ttries);
+            if (s + 1 == steps) {
+                // a step before the epilogue: the next tile's ticket, and the token
+                // scales of this tile copied into LDS (tokens past m repeat token m - 1)
+                // (the ticket is read only after the step's matrix work; the copy goes
+                // first so that no wait placed before it covers the ticket)
+                if (wave < kPBM / kWave)
+                    copy4_to_lds(gload_ptr(T.sx) + min(T.m0 + tid, T.mtok - 1), smem + kEpiOff + 2 * kPBM * 4 + 4 * kWave * wave);
+                if (wave == 0 && lane == 0 && ttries < kXcds) tk = atomicAdd(tickets + tx, 1u);
+            }
             const int buf = s % kANBuf;
             const bool more2 = s + 2 < steps;
             const int abuf2 = (s + 2) % kANBuf;
@@ -462,15 +490,27 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
         asm volatile("" : "+v"(te));
         const PLane LE = lane_of(te, wave);
         tsum[te] = rsum;   // half te / 128 of row te % 128
-        if (te < kPBM) {
-            const int tok = T.m0 + te;
-            tscale[te] = tok < T.mtok ? gload_ptr(T.P->sx)[tok] * *gload_ptr(T.P->sw) : 0.0f;
+        if (wave == 0) {
+            int nxt = -1;
+            if (ttries < kXcds) {
+                const int b = (int)table[tx], e = (int)table[tx + 1];
+                const uint32_t t = __builtin_amdgcn_readfirstlane(tk);
+                if (t < (uint32_t)(e - b)) {
+                    nxt = b + (int)t;
+                } else {
+                    tx = tx + 1 == kXcds ? 0 : tx + 1;
+                    ++ttries;
+                    nxt = take_tile(table, tickets, LE.lane, tx, ttries);
+                }
+            }
+            if (te == 0) {
+                if (nxt < 0) finish_tiles(tickets);
+                next_lds[0] = nxt;
+            }
         }
-        if (te == 0) {
-            if (nxt < 0) finish_tiles(tickets);
-            next_lds[0] = nxt;
-        }
-        // every wave is past its last read of the copy rings
+        // the token scales have landed (waves 0 and 1 copied them); every wave is
+        // past its last read of the copy rings
+        wait_vmcnt<0>();
         __syncthreads();
         // the next tile's first copies, ahead of this tile's stores (fast path;
         // the byte-wise path stages after the stores)
@@ -488,12 +528,12 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
         const bool full = E.m0 + kPBM <= E.mtok && E.n0 + kPBN <= E.n;
         const int rl = E.n0 + 64 * wave + LE.l32;   // this lane's row in row block 0 (+32 in block 1)
         const int loff = 4 * LE.g * E.n + rl;       // + (token block base + 8q + e) * n
-        if (full && !E.P->acc && E.n < kBufStoreMaxN) {
+        if (full && !E.acc && E.n < kBufStoreMaxN) {
             // The whole tile is in range: buffer stores over the tile's 128 token
             // rows, the lane's offset in a VGPR fixed for the tile and the token's
             // row offset in an SGPR, so a store costs the three VALU of its value.
             const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-                (void*)(E.P->y + (size_t)E.m0 * E.n), (short)0, kPBM * 4 * E.n, (int)kRsrcWord3);
+                (void*)(E.y + (size_t)E.m0 * E.n), (short)0, kPBM * 4 * E.n, (int)kRsrcWord3);
             const int voff = 4 * loff;
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
@@ -504,7 +544,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
                     const int4 tc = *reinterpret_cast<const int4*>(tsum + kPBM + t0);
                     const float4 sc4 = *reinterpret_cast<const float4*>(tscale + t0);
                     const int tsv[4] = {ta.x + tc.x, ta.y + tc.y, ta.z + tc.z, ta.w + tc.w};
-                    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+                    const float scv[4] = {sc4.x * E.sw, sc4.y * E.sw, sc4.z * E.sw, sc4.w * E.sw};   // sx * sw
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int soff = 4 * (32 * tb + 8 * q + e) * E.n;
@@ -517,8 +557,8 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
                 }
             }
         } else {
-            QMV_GLOBAL float* y = gstore_ptr(E.P->y);
-            QMV_GLOBAL int32_t* accout = E.P->acc ? gstore_ptr(E.P->acc) : nullptr;
+            QMV_GLOBAL float* y = gstore_ptr(E.y);
+            QMV_GLOBAL int32_t* accout = E.acc ? gstore_ptr(E.acc) : nullptr;
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
@@ -528,7 +568,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
                     const int4 tc = *reinterpret_cast<const int4*>(tsum + kPBM + t0);
                     const float4 sc4 = *reinterpret_cast<const float4*>(tscale + t0);
                     const int tsv[4] = {ta.x + tc.x, ta.y + tc.y, ta.z + tc.z, ta.w + tc.w};
-                    const float scv[4] = {sc4.x, sc4.y, sc4.z, sc4.w};
+                    const float scv[4] = {sc4.x * E.sw, sc4.y * E.sw, sc4.z * E.sw, sc4.w * E.sw};   // sx * sw
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const size_t urow = (size_t)(E.m0 + 32 * tb + 8 * q + e) * E.n;   // uniform part of the offset
