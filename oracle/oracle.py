@@ -39,6 +39,13 @@ def _load():
         lib.oracle_dequant.argtypes = [_ptr, _i64, _i64, _ptr, ctypes.c_float, _ptr]
         lib.oracle_lmhead.argtypes = [_ptr, _ptr, _i64, _i64, _ptr, _ptr, ctypes.c_int]
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_sketch_signs.argtypes = [_ptr, _i64, _i64, _ptr, ctypes.c_int]
+        lib.oracle_sketch_scale.argtypes = [_ptr, _i64, _i64, ctypes.c_int]
+        lib.oracle_sketch_scale.restype = ctypes.c_float
+        lib.oracle_sketch_plan.argtypes = [_ptr, _i64, ctypes.c_float, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]
+        lib.oracle_sketch_scores.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_float, _ptr, ctypes.c_int]
+        lib.oracle_sketch_pick.argtypes = [_ptr, _ptr, _i64, _i64, _ptr, _ptr, _ptr, _ptr]
+        lib.oracle_sketch_pick.restype = _i64
         _lib = lib
     return _lib
 
@@ -149,6 +156,71 @@ def lmhead(w_bf16, x, threads: int = 0):
     return logits, int(idx[0])
 
 
+def sketch_signs(w_bf16, threads: int = 0):
+    """Sign bits of a bf16 [v][k] table, word-major: uint32 [ceil(k/32)][v]."""
+    w, pw = _c(np.atleast_2d(w_bf16), np.uint16)
+    v, k = w.shape
+    out = np.empty(((k + 31) // 32, v), np.uint32)
+    _load().oracle_sketch_signs(pw, v, k, out.ctypes.data, threads or max_threads())
+    return out
+
+
+def sketch_scale(w_bf16, threads: int = 0):
+    """c = mean |w| of the table (fp32)."""
+    w, pw = _c(np.atleast_2d(w_bf16), np.uint16)
+    v, k = w.shape
+    return np.float32(_load().oracle_sketch_scale(pw, v, k, threads or max_threads()))
+
+
+def sketch_plan(x, c):
+    """(top_idx [T], top_x [T], group_of [k] (-1 = exact), group_n [4], group_w [4])."""
+    x, px = _c(x, np.float32)
+    k = x.size
+    top_idx = np.zeros(32, np.int32)
+    top_x = np.zeros(32, np.float32)
+    ntop = np.zeros(1, np.int32)
+    group_of = np.zeros(k, np.int32)
+    group_n = np.zeros(4, np.int32)
+    group_w = np.zeros(4, np.float32)
+    _load().oracle_sketch_plan(px, k, ctypes.c_float(float(c)), top_idx.ctypes.data, top_x.ctypes.data,
+                               ntop.ctypes.data, group_of.ctypes.data, group_n.ctypes.data, group_w.ctypes.data)
+    t = int(ntop[0])
+    return top_idx[:t], top_x[:t], group_of, group_n, group_w
+
+
+def sketch_scores(w_bf16, x, c, threads: int = 0):
+    """Approximate scores (fp32 [v]) of steps 1 and 2 of the sketch head."""
+    w, pw = _c(np.atleast_2d(w_bf16), np.uint16)
+    x, px = _c(x, np.float32)
+    v, k = w.shape
+    assert x.size == k
+    scores = np.empty(v, np.float32)
+    _load().oracle_sketch_scores(pw, px, v, k, ctypes.c_float(float(c)), scores.ctypes.data,
+                                 threads or max_threads())
+    return scores
+
+
+def sketch_pick(w_bf16, x, scores):
+    """Step 3: (candidate mask [v] bool, exact logits fp64 [v] (0 off the candidates), pick)."""
+    w, pw = _c(np.atleast_2d(w_bf16), np.uint16)
+    x, px = _c(x, np.float32)
+    scores, ps = _c(scores, np.float32)
+    v, k = w.shape
+    is_cand = np.zeros(v, np.uint8)
+    logits = np.zeros(v, np.float64)
+    idx = np.zeros(1, np.int32)
+    _load().oracle_sketch_pick(pw, px, v, k, ps, is_cand.ctypes.data, logits.ctypes.data, idx.ctypes.data)
+    return is_cand.astype(bool), logits, int(idx[0])
+
+
+def sketch_head(w_bf16, x, threads: int = 0):
+    """The whole sketch head: (pick, candidate mask, approximate scores, exact candidate logits)."""
+    c = sketch_scale(w_bf16, threads)
+    scores = sketch_scores(w_bf16, x, c, threads)
+    is_cand, logits, idx = sketch_pick(w_bf16, x, scores)
+    return idx, is_cand, scores, logits
+
+
 __all__ = ["max_threads", "quantize_rows", "quantize_tensor", "trit5_row_bytes", "trit5_row_stride",
            "int8_row_stride", "pack_trit5", "unpack_trit5", "layout_int8", "matmul_int", "dequant",
-           "lmhead"]
+           "lmhead", "sketch_signs", "sketch_scale", "sketch_plan", "sketch_scores", "sketch_pick", "sketch_head"]

@@ -260,6 +260,205 @@ void oracle_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, doub
     *idx = (int32_t)best;
 }
 
+/* ------------------------------------------------------------------------ */
+/* O7 -- the sketch head: candidates first, exact scores for those only.    */
+/*                                                                          */
+/* [T] "Step 3", the sketch head, in the page's three steps:                */
+/*  1. the 32 hidden dimensions with the largest values are scored exactly  */
+/*     for every word;                                                      */
+/*  2. the other dimensions are scored with a 1-bit (sign) copy of the      */
+/*     table, the dimensions grouped by size and each group weighted;       */
+/*  3. about 1,000 words with the best approximate scores are rescored      */
+/*     exactly; every other word scores minus infinity.                     */
+/* Readings (the page gives no more detail):                                */
+/*  - "largest values" is largest |x|; ranks are by |x| descending, ties to */
+/*    the lower dimension; T = min(32, k) dimensions are exact.             */
+/*  - a sign bit is 1 for a value below zero (so 0 and -0 count as          */
+/*    positive); a dimension adds +1 where the signs of w and x agree and   */
+/*    -1 where they differ.                                                 */
+/*  - "grouped by size": the remaining k - T dimensions in rank order are   */
+/*    cut into 4 consecutive groups, floor((k - T) / 4) each, the last      */
+/*    taking the rest.  Group weight = c * mean |x| of the group, with c    */
+/*    the mean |w| of the whole table, so a group's sign agreement is       */
+/*    turned into the size of the products it stands for.                   */
+/*  - c: each row's sum of |w| in fp32 in column order; rows summed in fp64 */
+/*    in blocks of 512 consecutive rows, the blocks summed in fp64 in       */
+/*    order, divided by v * k in fp64 and rounded to fp32.                  */
+/*  - the approximate score is a choice of candidates, so it is computed    */
+/*    in fp32 in the GPU's order (see oracle_sketch_scores) and the         */
+/*    candidate set is the same on both sides.                              */
+/*  - "about 1,000": every word whose approximate score lies in the top     */
+/*    bins holding at least min(1024, v) words, a bin being the top 12 bits */
+/*    of the score's order-preserving 32-bit key (one eighth of an octave). */
+/*  - the exact scores are O6's logits; the pick is O6's first maximum,     */
+/*    over the candidates only.                                             */
+/* ------------------------------------------------------------------------ */
+
+#define ORACLE_SKETCH_TOP 32
+#define ORACLE_SKETCH_GROUPS 4
+#define ORACLE_SKETCH_MIN_CAND 1024
+#define ORACLE_SKETCH_ROW_BLOCK 512
+
+static float oracle_bf16_to_float(uint16_t h)
+{
+    uint32_t bits = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+/* Sign bits of the table in the device layout: bit (c % 32) of word        */
+/* (c / 32) * v + r is 1 when w[r][c] < 0; bits past k are 0.                */
+void oracle_sketch_signs(const uint16_t* w, int64_t v, int64_t k, uint32_t* out, int threads)
+{
+    int64_t words = (k + 31) / 32;
+    memset(out, 0, (size_t)(words * v) * sizeof(uint32_t));
+    (void)threads;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+#endif
+    for (int64_t r = 0; r < v; ++r)
+        for (int64_t c = 0; c < k; ++c)
+            if (oracle_bf16_to_float(w[r * k + c]) < 0.0f) out[(c / 32) * v + r] |= 1u << (c % 32);
+}
+
+/* c = mean |w| of the table, in the order stated above. */
+float oracle_sketch_scale(const uint16_t* w, int64_t v, int64_t k, int threads)
+{
+    float* rows = (float*)malloc((size_t)v * sizeof(float));
+    assert(rows);
+    (void)threads;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+#endif
+    for (int64_t r = 0; r < v; ++r) {
+        float row = 0.0f;
+        for (int64_t c = 0; c < k; ++c) row += fabsf(oracle_bf16_to_float(w[r * k + c]));
+        rows[r] = row;
+    }
+    double total = 0.0;
+    for (int64_t b = 0; b * ORACLE_SKETCH_ROW_BLOCK < v; ++b) {
+        double part = 0.0;
+        for (int64_t r = b * ORACLE_SKETCH_ROW_BLOCK; r < v && r < (b + 1) * ORACLE_SKETCH_ROW_BLOCK; ++r)
+            part += (double)rows[r];
+        total += part;
+    }
+    free(rows);
+    return (float)(total / ((double)v * (double)k));
+}
+
+/* The per-token plan: the exact dimensions in rank order (top_idx, top_x,  */
+/* *ntop), the group of every dimension (-1 for an exact one), the group    */
+/* sizes and weights.                                                       */
+void oracle_sketch_plan(const float* x, int64_t k, float c, int32_t* top_idx, float* top_x, int32_t* ntop,
+                        int32_t* group_of, int32_t* group_n, float* group_w)
+{
+    /* rank by |x| descending, lower index first on ties: selection by repeated scans */
+    int64_t* order = (int64_t*)malloc((size_t)k * sizeof(int64_t));
+    uint8_t* used = (uint8_t*)calloc((size_t)k, 1);
+    assert(order && used);
+    for (int64_t r = 0; r < k; ++r) {
+        int64_t best = -1;
+        for (int64_t i = 0; i < k; ++i) {
+            if (used[i]) continue;
+            assert(isfinite(x[i]));
+            if (best < 0 || fabsf(x[i]) > fabsf(x[best])) best = i;
+        }
+        used[best] = 1;
+        order[r] = best;
+    }
+    int64_t t = k < ORACLE_SKETCH_TOP ? k : ORACLE_SKETCH_TOP;
+    *ntop = (int32_t)t;
+    for (int64_t j = 0; j < t; ++j) {
+        top_idx[j] = (int32_t)order[j];
+        top_x[j] = x[order[j]];
+        group_of[order[j]] = -1;
+    }
+    int64_t rest = k - t, base = rest / ORACLE_SKETCH_GROUPS;
+    for (int g = 0; g < ORACLE_SKETCH_GROUPS; ++g) {
+        int64_t lo = t + g * base;
+        int64_t hi = g == ORACLE_SKETCH_GROUPS - 1 ? k : lo + base;
+        group_n[g] = (int32_t)(hi - lo);
+        float sum = 0.0f;
+        for (int64_t r = lo; r < hi; ++r) {
+            group_of[order[r]] = g;
+            sum += fabsf(x[order[r]]);
+        }
+        float mean = hi > lo ? sum / (float)(hi - lo) : 0.0f;
+        group_w[g] = c * mean;
+    }
+    free(order);
+    free(used);
+}
+
+/* Approximate scores (steps 1 and 2), fp32 in this order: a = 0; for each  */
+/* exact dimension in rank order a = fma(w, x, a); then for each group g in */
+/* order a = fma(weight_g, agreement_g, a), the agreement an exact integer. */
+void oracle_sketch_scores(const uint16_t* w, const float* x, int64_t v, int64_t k, float c, float* scores,
+                          int threads)
+{
+    int32_t top_idx[ORACLE_SKETCH_TOP], ntop, group_n[ORACLE_SKETCH_GROUPS];
+    float top_x[ORACLE_SKETCH_TOP], group_w[ORACLE_SKETCH_GROUPS];
+    int32_t* group_of = (int32_t*)malloc((size_t)k * sizeof(int32_t));
+    assert(group_of);
+    oracle_sketch_plan(x, k, c, top_idx, top_x, &ntop, group_of, group_n, group_w);
+    (void)threads;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+#endif
+    for (int64_t r = 0; r < v; ++r) {
+        float a = 0.0f;
+        for (int j = 0; j < ntop; ++j) a = fmaf(oracle_bf16_to_float(w[r * k + top_idx[j]]), top_x[j], a);
+        int64_t agree[ORACLE_SKETCH_GROUPS] = {0, 0, 0, 0};
+        for (int64_t col = 0; col < k; ++col) {
+            int g = group_of[col];
+            if (g < 0) continue;
+            int sw = oracle_bf16_to_float(w[r * k + col]) < 0.0f, sx = x[col] < 0.0f;
+            agree[g] += sw == sx ? 1 : -1;
+        }
+        for (int g = 0; g < ORACLE_SKETCH_GROUPS; ++g) a = fmaf(group_w[g], (float)agree[g], a);
+        scores[r] = a;
+    }
+    free(group_of);
+}
+
+/* Order-preserving 32-bit key of an fp32 value. */
+static uint32_t oracle_order_key(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+/* Step 3: the candidates (is_cand[r] = 1) from the approximate scores, the */
+/* exact logits of the candidates (logits[r], fp64; 0 elsewhere) and the    */
+/* pick.  Returns the number of candidates.                                 */
+int64_t oracle_sketch_pick(const uint16_t* w, const float* x, int64_t v, int64_t k, const float* scores,
+                           uint8_t* is_cand, double* logits, int32_t* idx)
+{
+    int64_t hist[4096] = {0};
+    for (int64_t r = 0; r < v; ++r) ++hist[oracle_order_key(scores[r]) >> 20];
+    int64_t need = v < ORACLE_SKETCH_MIN_CAND ? v : ORACLE_SKETCH_MIN_CAND, above = 0;
+    int64_t bstar = 4095;
+    for (; bstar > 0; --bstar) {
+        above += hist[bstar];
+        if (above >= need) break;
+    }
+    int64_t count = 0, best = -1;
+    for (int64_t r = 0; r < v; ++r) {
+        logits[r] = 0.0;
+        is_cand[r] = (int64_t)(oracle_order_key(scores[r]) >> 20) >= bstar;
+        if (!is_cand[r]) continue;
+        ++count;
+        double sum = 0.0;
+        for (int64_t col = 0; col < k; ++col) sum += oracle_bf16_to_double(w[r * k + col]) * (double)x[col];
+        logits[r] = sum;
+        if (best < 0 || (float)sum > (float)logits[best]) best = r;
+    }
+    *idx = (int32_t)best;
+    return count;
+}
+
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
 int oracle_max_threads(void)
 {

@@ -314,6 +314,134 @@ def test_lmhead_one_hot_rows_read_x():
 
 
 # --------------------------------------------------------------------------
+# O7 sketch head
+# --------------------------------------------------------------------------
+
+def _bf16(a):
+    return synth.to_bf16_bits(np.asarray(a, np.float32))
+
+
+def test_sketch_signs_closed_form():
+    # row 0 all negative, row 1 negative at even columns, row 2 all positive; k = 40 spans two words
+    k = 40
+    w = np.stack([np.full(k, -0.5), np.where(np.arange(k) % 2 == 0, -0.5, 0.5), np.full(k, 0.25)])
+    bits = oracle.sketch_signs(_bf16(w))
+    assert bits.shape == (2, 3)
+    np.testing.assert_array_equal(bits[:, 0], [0xFFFFFFFF, 0xFF])
+    np.testing.assert_array_equal(bits[:, 1], [0x55555555, 0x55])
+    np.testing.assert_array_equal(bits[:, 2], [0, 0])
+    # zero and negative zero count as positive
+    z = _bf16(np.array([[0.0, -0.0, -1.0]], np.float32))
+    np.testing.assert_array_equal(oracle.sketch_signs(z)[:, 0], [0b100])
+
+
+def test_sketch_scale_closed_form():
+    w = _bf16(np.where(np.arange(600 * 40).reshape(600, 40) % 3 == 0, -0.25, 0.25))
+    assert oracle.sketch_scale(w) == np.float32(0.25)
+    w2 = _bf16(np.concatenate([np.full((300, 8), 0.5), np.full((300, 8), -1.5)]))
+    assert oracle.sketch_scale(w2) == np.float32(1.0)
+
+
+@pytest.mark.parametrize("k,sizes", [(1152, [280, 280, 280, 280]), (37, [1, 1, 1, 2]), (33, [0, 0, 0, 1]),
+                                     (20, [0, 0, 0, 0]), (100, [17, 17, 17, 17])])
+def test_sketch_plan_group_sizes(k, sizes):
+    x = synth.normal(41, (k,))
+    top_idx, top_x, group_of, group_n, group_w = oracle.sketch_plan(x, 1.0)
+    t = min(32, k)
+    assert len(top_idx) == t
+    assert list(group_n) == sizes
+    assert sorted(set(top_idx.tolist())) == sorted(top_idx.tolist())          # distinct
+    assert np.all(group_of[top_idx] == -1)
+    for g in range(4):
+        assert int((group_of == g).sum()) == sizes[g]
+    # the exact dimensions are the t largest |x|, in descending order
+    mags = np.abs(x)
+    assert np.all(np.diff(mags[top_idx]) <= 0)
+    rest = np.setdiff1d(np.arange(k), top_idx)
+    if rest.size:
+        assert mags[rest].max() <= mags[top_idx].min()
+    np.testing.assert_array_equal(top_x, x[top_idx])
+
+
+def test_sketch_plan_ties_and_group_weights_closed_form():
+    # |x| = k - i: ranks are the indices in order; ties (all equal) also rank by index
+    k = 72
+    x = np.array([(k - i) * (-1) ** i for i in range(k)], np.float32)
+    top_idx, _, group_of, group_n, group_w = oracle.sketch_plan(x, 0.5)
+    np.testing.assert_array_equal(top_idx, np.arange(32))
+    assert list(group_n) == [10, 10, 10, 10]
+    # group g holds ranks 32+10g .. 41+10g, |x| = 40-10g .. 31-10g: mean = 35.5 - 10 g
+    np.testing.assert_array_equal(group_w, np.float32(0.5) * np.array([35.5, 25.5, 15.5, 5.5], np.float32))
+    eq = np.ones(50, np.float32)
+    top_idx, _, _, _, _ = oracle.sketch_plan(eq, 1.0)
+    np.testing.assert_array_equal(top_idx, np.arange(32))
+
+
+def test_sketch_scores_equal_exact_logits_when_all_magnitudes_match():
+    # |w| = 0.5 and |x| = 1 everywhere: c = 0.5, every group weight is 0.5 and every
+    # product w*x = 0.5 * (sign agreement), so steps 1 + 2 reproduce the exact logit
+    # exactly (small multiples of 0.5); a dropped, doubled or mis-signed dimension breaks it
+    v, k = 300, 200
+    sw = np.where(synth.raw(43, v * k).reshape(v, k) % 2 == 0, 1.0, -1.0)
+    sx = np.where(synth.raw(44, k) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    w = _bf16(0.5 * sw)
+    assert oracle.sketch_scale(w) == np.float32(0.5)
+    scores = oracle.sketch_scores(w, sx, np.float32(0.5))
+    exact = (0.5 * sw) @ sx
+    np.testing.assert_array_equal(scores, exact.astype(np.float32))
+
+
+def test_sketch_scores_sign_symmetry():
+    v, k = 64, 1152
+    w = _bf16(synth.normal(45, (v, k), std=0.02))
+    x = synth.normal(46, (k,))
+    c = oracle.sketch_scale(w)
+    s1 = oracle.sketch_scores(w, x, c)
+    s2 = oracle.sketch_scores(w ^ np.uint16(0x8000), x, c)    # every weight negated
+    zero = (w & np.uint16(0x7FFF)) == 0
+    assert not zero.any()
+    np.testing.assert_array_equal(s2, -s1)
+
+
+def test_sketch_pick_all_exact_matches_full_argmax():
+    # k <= 32: every dimension is exact, so the best word always makes the candidates
+    for seed in range(5):
+        w = _bf16(synth.normal(50 + seed, (3000, 32), std=0.02))
+        x = synth.normal(60 + seed, (32,))
+        idx, cand, scores, logits = oracle.sketch_head(w, x)
+        full, fidx = oracle.lmhead(w, x)
+        assert idx == fidx
+        assert cand.sum() >= 1024
+        np.testing.assert_array_equal(logits[cand], full[cand])
+
+
+def test_sketch_pick_candidates_are_the_top_bins():
+    v, k = 5000, 256
+    w = _bf16(synth.normal(47, (v, k), std=0.02))
+    x = synth.normal(48, (k,))
+    idx, cand, scores, logits = oracle.sketch_head(w, x)
+    key = scores.view(np.uint32).astype(np.uint64)
+    key = np.where(key & 0x80000000, ~key & 0xFFFFFFFF, key | 0x80000000) >> 20
+    assert cand.sum() >= 1024
+    assert key[cand].min() > key[~cand].max()
+    above = cand & (key > key[cand].min())
+    assert above.sum() < 1024
+    assert idx == int(np.flatnonzero(cand)[np.argmax(logits[cand].astype(np.float32))])
+    # fewer words than 1024: every word is a candidate and the pick is the full argmax
+    idx2, cand2, _, _ = oracle.sketch_head(w[:700], x)
+    assert cand2.all() and idx2 == oracle.lmhead(w[:700], x)[1]
+
+
+def test_sketch_pick_planted_winner():
+    v, k = 20000, 1152
+    w = _bf16(synth.normal(49, (v, k), std=0.02))
+    wf = synth.bf16_bits_to_f32(w)
+    x = (40.0 * wf[12345] + synth.normal(51, (k,)) * 0.2).astype(np.float32)
+    idx, cand, _, _ = oracle.sketch_head(w, x)
+    assert cand[12345] and idx == 12345 == oracle.lmhead(w, x)[1]
+
+
+# --------------------------------------------------------------------------
 # The seeded generator itself (not the oracle): published splitmix64 values.
 # --------------------------------------------------------------------------
 
