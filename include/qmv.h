@@ -199,6 +199,51 @@ int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int
                           void* stream);
 
 /*
+ * The sketch head ("Step 3": candidates first, exact scores only for them).
+ * For each token:
+ *   1. the T = min(32, k) hidden dimensions with the largest |x| (ties to the
+ *      lower index) are scored exactly for every word;
+ *   2. the other dimensions are scored from the sign bits of the table: in
+ *      rank order they form 4 groups (floor((k-T)/4) each, the last takes the
+ *      rest), and group g adds c * mean|x|_g * (agreeing - disagreeing signs),
+ *      c being the mean |w| of the table (a sign bit is set for a value < 0);
+ *      the score is fp32, a = fma(w, x, a) over the exact dimensions in rank
+ *      order, then a = fma(weight_g, agreement_g, a) for g = 0..3;
+ *   3. the candidates are the words whose score falls in the top bins that
+ *      hold at least min(1024, v) words, a bin being the top 12 bits of the
+ *      score's order-preserving key; only they are scored exactly (as in
+ *      qmv_lmhead_argmax) and the first maximum among them is the choice.
+ * Limits: 8 <= k <= 8192, k % 8 == 0, 1 <= v <= QMV_MAX_N.
+ */
+int64_t qmv_sketch_bytes(int64_t v, int64_t k);            /* -1 on bad shape */
+int64_t qmv_sketch_workspace_bytes(int64_t v, int64_t k);  /* -1 on bad shape */
+
+/*
+ * qmv_sketch_build -- one-time preparation from the output layer's weights:
+ * the sign bits (word d/32 of row r at (d/32)*v + r), a dimension-major bf16
+ * copy [k][v] and c, in `sketch` (256-byte aligned, >= qmv_sketch_bytes).
+ *   w_bf16  [v][k] bf16 bit patterns, row-major, 16-byte aligned, finite.
+ * Not part of the per-token path.  EINVAL / ESHAPE / EWORKSPACE as above.
+ */
+int32_t qmv_sketch_build(const uint16_t* w_bf16, int64_t v, int64_t k, void* sketch, int64_t sketch_bytes,
+                         void* stream);
+
+/*
+ * qmv_lmhead_sketch_argmax -- the greedy choice through the sketch head.
+ *   w_bf16     the same table the sketch was built from (exact rescoring).
+ *   x          [k] fp32 hidden state, finite.
+ *   idx        1 int32: the chosen word.
+ *   max_logit  nullable, 1 fp32: its exact logit.
+ *   candidates nullable, 1 int32: how many words were rescored.
+ *   scores     nullable, [v] fp32: every word's approximate score (step 1+2).
+ *   workspace  >= qmv_sketch_workspace_bytes(v, k) bytes, 256-byte aligned;
+ *              calls that share it must not overlap.
+ */
+int32_t qmv_lmhead_sketch_argmax(const uint16_t* w_bf16, const void* sketch, const float* x, int64_t v,
+                                 int64_t k, int32_t* idx, float* max_logit, int32_t* candidates, float* scores,
+                                 void* workspace, int64_t ws_bytes, void* stream);
+
+/*
  * qmv_read_probe -- a measurement aid, not part of the method: reads `bytes`
  * of `data` once with 16-byte loads (grid-stride, the access pattern that
  * reads fastest on this GPU) and folds them into a word written to *out only

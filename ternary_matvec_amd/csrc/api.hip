@@ -617,4 +617,36 @@ int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int
     return hip_status(launch_lmhead(w_bf16, x, v, k, idx, max_logit, logits, workspace, as_stream(stream)));
 }
 
+int64_t qmv_sketch_bytes(int64_t v, int64_t k)
+{
+    if (v < 1 || v > QMV_MAX_N || k < 8 || k > kSketchMaxK || k % 8) return -1;
+    return sketch_bytes(v, k);
+}
+
+int64_t qmv_sketch_workspace_bytes(int64_t v, int64_t k)
+{
+    if (v < 1 || v > QMV_MAX_N || k < 8 || k > kSketchMaxK || k % 8) return -1;
+    return sketch_workspace_bytes(v);
+}
+
+int32_t qmv_sketch_build(const uint16_t* w_bf16, int64_t v, int64_t k, void* sketch, int64_t sketch_bytes_,
+                         void* stream)
+{
+    if (!w_bf16 || !sketch || !aligned(w_bf16, 16) || !aligned(sketch, 256)) return QMV_EINVAL;
+    if (v < 1 || v > QMV_MAX_N || k < 8 || k > kSketchMaxK || k % 8) return QMV_ESHAPE;
+    if (sketch_bytes_ < sketch_bytes(v, k)) return QMV_EWORKSPACE;
+    return hip_status(launch_sketch_build(w_bf16, v, k, sketch, as_stream(stream)));
+}
+
+int32_t qmv_lmhead_sketch_argmax(const uint16_t* w_bf16, const void* sketch, const float* x, int64_t v, int64_t k,
+                                 int32_t* idx, float* max_logit, int32_t* candidates, float* scores,
+                                 void* workspace, int64_t ws_bytes, void* stream)
+{
+    if (!w_bf16 || !sketch || !x || !idx || !aligned(w_bf16, 16) || !aligned(sketch, 256)) return QMV_EINVAL;
+    if (v < 1 || v > QMV_MAX_N || k < 8 || k > kSketchMaxK || k % 8) return QMV_ESHAPE;
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < sketch_workspace_bytes(v)) return QMV_EWORKSPACE;
+    return hip_status(launch_sketch_argmax(w_bf16, sketch, x, v, k, idx, max_logit, candidates, scores, workspace,
+                                           as_stream(stream)));
+}
+
 }  // extern "C"

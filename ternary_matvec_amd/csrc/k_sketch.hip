@@ -1,0 +1,485 @@
+// k_sketch.hip -- the sketch head: the output layer's greedy choice from
+// candidates ("Gemma 3 1B at 114 tokens per second on a laptop CPU", "Step 3:
+// the output layer became the bottleneck", the sketch head's three steps).
+//
+// Per token:
+//  1. k_sketch_plan (one workgroup): the hidden dimensions ranked by |x|
+//     (descending, ties to the lower index); the first T = min(32, k) are
+//     scored exactly, the rest are cut into 4 consecutive rank groups, each
+//     weighted by c * mean |x| (c = mean |w| of the table, computed when the
+//     sketch is built).  Group bit masks and the sign bits of x go to the
+//     workspace; the candidate histogram and the pick are cleared.
+//  2. k_sketch_score (a thread per row): a = 0; a = fma(w[r][d_j], x[d_j], a)
+//     over the exact dimensions in rank order, read from a dimension-major
+//     copy of the table; then per group a = fma(weight_g, agreement_g, a),
+//     the agreement = n_g - 2 * popcount((signs of w ^ signs of x) & mask_g)
+//     from the 1-bit table (one XOR, then AND + bit count per group, 32
+//     dimensions per word).  The fp32 score's order key goes to the
+//     workspace and into a histogram of its top 12 bits.
+//  3. k_sketch_rescore: every workgroup finds the lowest bin b* such that the
+//     bins from b* up hold at least min(1024, v) words; the words in those
+//     bins are the candidates.  A wave scores each candidate exactly (fp32,
+//     like k_lmhead) and the largest (logit, lowest index) wins through one
+//     64-bit atomic maximum; the last workgroup writes the result.
+// The score arithmetic is fixed (fp32 FMAs in the order above), so the
+// candidate set is exactly the one the oracle computes.
+#include "qmv_internal.hpp"
+
+namespace qmv {
+namespace {
+
+constexpr int kSkTop = 32;         // exactly scored dimensions
+constexpr int kSkGroups = 4;       // sign-bit groups
+constexpr int kSkMinCand = 1024;   // candidates: at least this many words (or all of them)
+constexpr int kSkBins = 4096;      // histogram over the top 12 bits of the order key
+constexpr int kSkRowBlock = 512;   // rows per fp64 partial of the table scale
+constexpr int kSkPlanThreads = 1024;
+constexpr int kSkRowsPerBlock = 1024;   // score / rescore: rows per workgroup (4 per thread)
+constexpr uint32_t kSkMagic = 0x31484b53u;   // "SKH1"
+
+// Sketch buffer: header, sign words [kw][v], dimension-major bf16 copy [k][v].
+struct SketchHeader {
+    uint32_t magic;
+    int32_t k;
+    int64_t v;
+    float c;        // mean |w| of the table
+    int32_t pad[11];
+};
+static_assert(sizeof(SketchHeader) == 64, "sketch header");
+
+// Workspace: the plan, the histogram, the pick, then the order keys [v].
+struct SketchPlan {
+    int32_t t;               // exact dimensions
+    int32_t kw;              // 32-dimension words
+    int32_t n[kSkGroups];    // group sizes
+    float wgt[kSkGroups];    // group weights
+    int32_t pad[6];
+    int32_t top_idx[kSkTop];
+    float top_x[kSkTop];
+    // then masks [kSkGroups][kw] and the sign words of x [kw]
+};
+static_assert(sizeof(SketchPlan) == 320, "sketch plan");
+constexpr int64_t kSkPlanBytes = 8192;
+constexpr int64_t kSkHistOff = kSkPlanBytes;
+constexpr int64_t kSkPickOff = kSkHistOff + kSkBins * 4;   // u64 best, u32 done, u32 candidates
+constexpr int64_t kSkKeysOff = kSkPickOff + 256;
+
+constexpr int64_t sk_round(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
+
+__device__ __forceinline__ uint32_t order_key(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// ---- build --------------------------------------------------------------------------------
+
+// A thread per row: the sign words (word w of row r at w * v + r) and the
+// row's sum of |w| in fp32, column order (into `rowsum`).
+__global__ __launch_bounds__(kBlock) void k_sketch_rows(const uint16_t* __restrict__ w, int64_t v, int k,
+                                                        uint32_t* __restrict__ signs, float* __restrict__ rowsum)
+{
+    const int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (r >= v) return;
+    const uint4* row = reinterpret_cast<const uint4*>(w + r * k);
+    float sum = 0.0f;
+    uint32_t word = 0;
+    for (int c8 = 0; c8 < k / 8; ++c8) {
+        const uint4 q = row[c8];
+        const uint32_t h[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const float f = half ? __uint_as_float(h[j] & 0xFFFF0000u) : __uint_as_float(h[j] << 16);
+                const int col = 8 * c8 + 2 * j + half;
+                sum += fabsf(f);
+                if (f < 0.0f) word |= 1u << (col & 31);
+            }
+        }
+        if ((c8 & 3) == 3 || c8 == k / 8 - 1) {
+            signs[(int64_t)(c8 >> 2) * v + r] = word;
+            word = 0;
+        }
+    }
+    rowsum[r] = sum;
+}
+
+// One workgroup: c = mean |w|.  Blocks of 512 rows are summed in fp64 in row
+// order (thread t takes blocks t, t + 256, ...), then thread 0 adds the block
+// sums in order.
+__global__ __launch_bounds__(kBlock) void k_sketch_scale(const float* __restrict__ rowsum, int64_t v, int k,
+                                                         double* __restrict__ part, SketchHeader* __restrict__ hdr)
+{
+    const int64_t nb = (v + kSkRowBlock - 1) / kSkRowBlock;
+    for (int64_t b = threadIdx.x; b < nb; b += kBlock) {
+        double s = 0.0;
+        const int64_t end = min(v, (b + 1) * kSkRowBlock);
+        for (int64_t r = b * kSkRowBlock; r < end; ++r) s += (double)rowsum[r];
+        part[b] = s;
+    }
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double total = 0.0;
+        for (int64_t b = 0; b < nb; ++b) total += part[b];
+        hdr->magic = kSkMagic;
+        hdr->k = k;
+        hdr->v = v;
+        hdr->c = (float)(total / ((double)v * (double)k));
+    }
+}
+
+// 64 x 64 tiles through LDS: wt[c][r] = w[r][c].
+__global__ __launch_bounds__(kBlock) void k_sketch_transpose(const uint16_t* __restrict__ w, int64_t v, int k,
+                                                             uint16_t* __restrict__ wt)
+{
+    __shared__ uint16_t tile[64][66];
+    const int64_t r0 = (int64_t)blockIdx.x * 64;
+    const int c0 = blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int rr = ty + 4 * i;
+        const int64_t r = r0 + rr;
+        const int c = c0 + tx;
+        tile[rr][tx] = (r < v && c < k) ? w[r * k + c] : (uint16_t)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int cc = ty + 4 * i;
+        const int c = c0 + cc;
+        const int64_t r = r0 + tx;
+        if (c < k && r < v) wt[(int64_t)c * v + r] = tile[tx][cc];
+    }
+}
+
+// ---- per token ----------------------------------------------------------------------------
+
+// One workgroup of 1024 threads; dynamic LDS: the sort keys (P = power of two
+// >= k, 8 bytes each) then the masks and x sign words (5 * kw words).
+__global__ __launch_bounds__(kSkPlanThreads) void k_sketch_plan(const float* __restrict__ x, int k, int p2,
+                                                                const SketchHeader* __restrict__ hdr,
+                                                                uint8_t* __restrict__ ws)
+{
+    extern __shared__ __align__(16) uint8_t sm[];
+    uint64_t* key = reinterpret_cast<uint64_t*>(sm);
+    const int kw = (k + 31) >> 5;
+    uint32_t* mbits = reinterpret_cast<uint32_t*>(sm + 8 * (size_t)p2);   // [5][kw]: masks, then x signs
+    const int tid = threadIdx.x;
+    // |x| ranks: key = |x| bits << 32 | (~index); padding keys are 0 and sort last
+    for (int i = tid; i < p2; i += kSkPlanThreads)
+        key[i] = i < k ? ((uint64_t)__float_as_uint(fabsf(x[i])) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
+    for (int i = tid; i < 5 * kw; i += kSkPlanThreads) mbits[i] = 0u;
+    __syncthreads();
+    // bitonic sort, descending
+    for (int size = 2; size <= p2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < p2 / 2; i += kSkPlanThreads) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a = key[lo], b = key[hi];
+                if ((a < b) == desc) {
+                    key[lo] = b;
+                    key[hi] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    SketchPlan* plan = reinterpret_cast<SketchPlan*>(ws);
+    const int t = min(k, kSkTop);
+    const int rest = k - t, base = rest / kSkGroups;
+    auto dim_of = [&](int rank) { return (int)(0xFFFFFFFFu - (uint32_t)(key[rank] & 0xFFFFFFFFu)); };
+    auto group_of_rank = [&](int rank) { return base > 0 ? min((rank - t) / base, kSkGroups - 1) : kSkGroups - 1; };
+    if (tid < t) {
+        const int d = dim_of(tid);
+        plan->top_idx[tid] = d;
+        plan->top_x[tid] = x[d];
+    }
+    for (int rank = t + tid; rank < k; rank += kSkPlanThreads) {
+        const int d = dim_of(rank);
+        atomicOr(&mbits[group_of_rank(rank) * kw + (d >> 5)], 1u << (d & 31));
+    }
+    for (int i = tid; i < k; i += kSkPlanThreads)
+        if (x[i] < 0.0f) atomicOr(&mbits[kSkGroups * kw + (i >> 5)], 1u << (i & 31));
+    if (tid < kSkGroups) {
+        // group sums of |x| in rank order, fp32
+        const int lo = t + tid * base;
+        const int hi = tid == kSkGroups - 1 ? k : lo + base;
+        float sum = 0.0f;
+        for (int rank = lo; rank < hi; ++rank) sum += fabsf(x[dim_of(rank)]);
+        const float mean = hi > lo ? sum / (float)(hi - lo) : 0.0f;
+        plan->n[tid] = hi - lo;
+        plan->wgt[tid] = hdr->c * mean;
+    }
+    if (tid == 0) {
+        plan->t = t;
+        plan->kw = kw;
+    }
+    // clear the histogram and the pick for this token
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + kSkHistOff);
+    for (int i = tid; i < kSkBins; i += kSkPlanThreads) hist[i] = 0u;
+    if (tid < 4) reinterpret_cast<uint32_t*>(ws + kSkPickOff)[tid] = 0u;
+    __syncthreads();
+    uint32_t* mout = reinterpret_cast<uint32_t*>(ws + sizeof(SketchPlan));
+    for (int i = tid; i < 5 * kw; i += kSkPlanThreads) mout[i] = mbits[i];
+}
+
+// 256 threads, 1024 rows per workgroup (rows base + tid + 256 i).
+__global__ __launch_bounds__(kBlock) void k_sketch_score(const uint32_t* __restrict__ signs,
+                                                         const uint16_t* __restrict__ wt, int64_t v,
+                                                         uint8_t* __restrict__ ws, float* __restrict__ scores)
+{
+    __shared__ uint32_t sbits[5 * 256];
+    __shared__ uint32_t shist[kSkBins];
+    __shared__ int32_t s_idx[kSkTop];
+    __shared__ float s_x[kSkTop];
+    const SketchPlan* plan = reinterpret_cast<const SketchPlan*>(ws);
+    const int tid = threadIdx.x;
+    const int t = plan->t, kw = plan->kw;
+    const uint32_t* mbits = reinterpret_cast<const uint32_t*>(ws + sizeof(SketchPlan));
+    for (int i = tid; i < 5 * kw; i += kBlock) sbits[i] = mbits[i];
+    for (int i = tid; i < kSkBins; i += kBlock) shist[i] = 0u;
+    if (tid < kSkTop) {
+        s_idx[tid] = plan->top_idx[tid];
+        s_x[tid] = plan->top_x[tid];
+    }
+    float wgt[kSkGroups];
+    int32_t ng[kSkGroups];
+#pragma unroll
+    for (int g = 0; g < kSkGroups; ++g) {
+        wgt[g] = plan->wgt[g];
+        ng[g] = plan->n[g];
+    }
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kSkRowsPerBlock + tid;
+    float a[4];
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        a[i] = 0.0f;
+        live[i] = base + 256 * i < v;
+    }
+    // step 1: the exact dimensions, in rank order
+    for (int j = 0; j < t; ++j) {
+        const uint16_t* col = wt + (int64_t)s_idx[j] * v;
+        const float xj = s_x[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (live[i]) a[i] = fmaf(bf16f(col[base + 256 * i]), xj, a[i]);
+    }
+    // step 2: sign agreement per group
+    int cnt[4][kSkGroups] = {};
+    for (int w = 0; w < kw; ++w) {
+        const uint32_t xs = sbits[kSkGroups * kw + w];
+        uint32_t m[kSkGroups];
+#pragma unroll
+        for (int g = 0; g < kSkGroups; ++g) m[g] = sbits[g * kw + w];
+        const uint32_t* srow = signs + (int64_t)w * v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (!live[i]) continue;
+            const uint32_t d = srow[base + 256 * i] ^ xs;
+#pragma unroll
+            for (int g = 0; g < kSkGroups; ++g) cnt[i][g] += __popc(d & m[g]);
+        }
+    }
+    uint32_t* keys = reinterpret_cast<uint32_t*>(ws + kSkKeysOff);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (!live[i]) continue;
+#pragma unroll
+        for (int g = 0; g < kSkGroups; ++g) a[i] = fmaf(wgt[g], (float)(ng[g] - 2 * cnt[i][g]), a[i]);
+        const uint32_t key = order_key(a[i]);
+        keys[base + 256 * i] = key;
+        if (scores) scores[base + 256 * i] = a[i];
+        atomicAdd(&shist[key >> 20], 1u);
+    }
+    __syncthreads();
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + kSkHistOff);
+    for (int i = tid; i < kSkBins; i += kBlock)
+        if (shist[i]) atomicAdd(&hist[i], shist[i]);
+}
+
+// 256 threads, 1024 rows per workgroup.  Dynamic LDS: x (k floats).
+__global__ __launch_bounds__(kBlock) void k_sketch_rescore(const uint16_t* __restrict__ w, const float* __restrict__ x,
+                                                           int64_t v, int k, uint8_t* __restrict__ ws,
+                                                           int32_t* __restrict__ idx, float* __restrict__ max_logit,
+                                                           int32_t* __restrict__ ncand)
+{
+    extern __shared__ __align__(16) float xs[];
+    __shared__ uint32_t ssum[kBlock];
+    __shared__ int32_t s_bstar;
+    __shared__ int32_t s_n;
+    __shared__ int32_t s_list[kSkRowsPerBlock];
+    __shared__ bool s_last;
+    const int tid = threadIdx.x;
+    for (int i = tid; i < k; i += kBlock) xs[i] = x[i];
+    // b*: the highest bin at which the bins from the top down first hold
+    // min(1024, v) words.  Thread t sums bins 4095 - 16t - 15 .. 4095 - 16t.
+    const uint32_t* hist = reinterpret_cast<const uint32_t*>(ws + kSkHistOff);
+    const int hi_bin = kSkBins - 1 - 16 * tid;
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) local += hist[hi_bin - j];
+    ssum[tid] = local;
+    if (tid == 0) {
+        s_n = 0;
+        s_bstar = 0;
+    }
+    __syncthreads();
+    // inclusive scan over threads (from the top bins down)
+    for (int off = 1; off < kBlock; off <<= 1) {
+        const uint32_t add = tid >= off ? ssum[tid - off] : 0u;
+        __syncthreads();
+        ssum[tid] += add;
+        __syncthreads();
+    }
+    const uint32_t need = (uint32_t)min<int64_t>(v, kSkMinCand);
+    const uint32_t before = tid ? ssum[tid - 1] : 0u;
+    if (before < need && ssum[tid] >= need) {
+        uint32_t run = before;
+        for (int j = 0; j < 16; ++j) {
+            run += hist[hi_bin - j];
+            if (run >= need) {
+                s_bstar = hi_bin - j;
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const uint32_t bstar = (uint32_t)s_bstar;
+    // this workgroup's candidates
+    const uint32_t* keys = reinterpret_cast<const uint32_t*>(ws + kSkKeysOff);
+    const int64_t base = (int64_t)blockIdx.x * kSkRowsPerBlock;
+    for (int i = tid; i < kSkRowsPerBlock; i += kBlock) {
+        const int64_t r = base + i;
+        if (r < v && (keys[r] >> 20) >= bstar) s_list[atomicAdd(&s_n, 1)] = (int32_t)r;
+    }
+    __syncthreads();
+    const int n = s_n;
+    uint32_t* pick = reinterpret_cast<uint32_t*>(ws + kSkPickOff);
+    unsigned long long* best = reinterpret_cast<unsigned long long*>(pick);
+    if (tid == 0 && n) atomicAdd(&pick[3], (uint32_t)n);
+    // exact logits: one wave per candidate, 16-byte chunks over the lanes
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    for (int c = wave; c < n; c += kBlock / kWave) {
+        const int64_t r = s_list[c];
+        const uint4* row = reinterpret_cast<const uint4*>(w + r * k);
+        float s = 0.0f;
+        for (int ch = lane; ch < k / 8; ch += kWave) {
+            const uint4 q = row[ch];
+            const float* xc = xs + 8 * ch;
+            s = fmaf(__uint_as_float(q.x << 16), xc[0], s);
+            s = fmaf(__uint_as_float(q.x & 0xFFFF0000u), xc[1], s);
+            s = fmaf(__uint_as_float(q.y << 16), xc[2], s);
+            s = fmaf(__uint_as_float(q.y & 0xFFFF0000u), xc[3], s);
+            s = fmaf(__uint_as_float(q.z << 16), xc[4], s);
+            s = fmaf(__uint_as_float(q.z & 0xFFFF0000u), xc[5], s);
+            s = fmaf(__uint_as_float(q.w << 16), xc[6], s);
+            s = fmaf(__uint_as_float(q.w & 0xFFFF0000u), xc[7], s);
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+        if (lane == 0) {
+            const unsigned long long kv =
+                ((unsigned long long)order_key(s) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)r);
+            atomicMax(best, kv);
+        }
+    }
+    // the last workgroup to finish writes the pick
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) s_last = atomicAdd(&pick[2], 1u) == gridDim.x - 1;
+    __syncthreads();
+    if (s_last && tid == 0) {
+        __threadfence();
+        const unsigned long long kv = atomicMax(best, 0ull);
+        *idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(kv & 0xFFFFFFFFu));
+        if (max_logit) *max_logit = key_value((uint32_t)(kv >> 32));
+        if (ncand) *ncand = (int32_t)atomicAdd(&pick[3], 0u);
+    }
+}
+
+}  // namespace
+
+// The copy's space also holds the build's row sums and block partials until
+// the transpose overwrites them.
+int64_t sketch_copy_bytes(int64_t v, int64_t k)
+{
+    const int64_t temp = sk_round(4 * v, 256) + sk_round(8 * ((v + kSkRowBlock - 1) / kSkRowBlock), 256);
+    return max(sk_round(2 * k * v, 256), temp);
+}
+
+int64_t sketch_bytes(int64_t v, int64_t k)
+{
+    const int64_t kw = (k + 31) / 32;
+    return 256 + sk_round(4 * kw * v, 256) + sketch_copy_bytes(v, k);
+}
+
+int64_t sketch_workspace_bytes(int64_t v) { return kSkKeysOff + sk_round(4 * v, 256); }
+
+hipError_t launch_sketch_build(const uint16_t* w, int64_t v, int64_t k, void* sketch, hipStream_t s)
+{
+    uint8_t* base = static_cast<uint8_t*>(sketch);
+    const int64_t kw = (k + 31) / 32;
+    uint32_t* signs = reinterpret_cast<uint32_t*>(base + 256);
+    uint16_t* wt = reinterpret_cast<uint16_t*>(base + 256 + sk_round(4 * kw * v, 256));
+    // the row sums and block partials live in the copy's space until the transpose
+    float* rowsum = reinterpret_cast<float*>(wt);
+    double* part = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(wt) + sk_round(4 * v, 256));
+    hipLaunchKernelGGL(k_sketch_rows, dim3((unsigned)((v + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, w, v, (int)k,
+                       signs, rowsum);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sketch_scale, dim3(1), dim3(kBlock), 0, s, rowsum, v, (int)k, part,
+                       reinterpret_cast<SketchHeader*>(base));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sketch_transpose, dim3((unsigned)((v + 63) / 64), (unsigned)((k + 63) / 64)), dim3(kBlock), 0,
+                       s, w, v, (int)k, wt);
+    return hipGetLastError();
+}
+
+hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const float* x, int64_t v, int64_t k,
+                                int32_t* idx, float* max_logit, int32_t* ncand, float* scores, void* workspace,
+                                hipStream_t s)
+{
+    const uint8_t* base = static_cast<const uint8_t*>(sketch);
+    const int64_t kw = (k + 31) / 32;
+    const uint32_t* signs = reinterpret_cast<const uint32_t*>(base + 256);
+    const uint16_t* wt = reinterpret_cast<const uint16_t*>(base + 256 + sk_round(4 * kw * v, 256));
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    int p2 = 1;
+    while (p2 < k) p2 <<= 1;
+    const size_t plan_lds = 8 * (size_t)p2 + 20 * (size_t)kw;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_plan),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sketch_plan, dim3(1), dim3(kSkPlanThreads), plan_lds, s, x, (int)k, p2,
+                       reinterpret_cast<const SketchHeader*>(base), ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned grid = (unsigned)((v + kSkRowsPerBlock - 1) / kSkRowsPerBlock);
+    hipLaunchKernelGGL(k_sketch_score, dim3(grid), dim3(kBlock), 0, s, signs, wt, v, ws, scores);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_rescore),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(4 * k));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sketch_rescore, dim3(grid), dim3(kBlock), (size_t)(4 * k), s, w, x, v, (int)k, ws, idx,
+                       max_logit, ncand);
+    return hipGetLastError();
+}
+
+}  // namespace qmv

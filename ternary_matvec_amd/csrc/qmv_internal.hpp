@@ -110,6 +110,14 @@ int64_t prefill_tiles(int64_t m, int64_t n);
 // (slot << 48 | token tile << 32 | row tile), then the zeroed tickets.
 hipError_t launch_prefill(const DevProblem* probs, const uint64_t* table, int64_t grid, const int8_t* zeros,
                           hipStream_t s);
+// Sketch head of the output layer: build tables, per-token argmax.
+constexpr int64_t kSketchMaxK = 8192;
+int64_t sketch_bytes(int64_t v, int64_t k);
+int64_t sketch_workspace_bytes(int64_t v);
+hipError_t launch_sketch_build(const uint16_t* w, int64_t v, int64_t k, void* sketch, hipStream_t s);
+hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const float* x, int64_t v, int64_t k,
+                                int32_t* idx, float* max_logit, int32_t* ncand, float* scores, void* workspace,
+                                hipStream_t s);
 hipError_t launch_read_probe(const void* data, int64_t bytes, uint32_t* out, int cus, hipStream_t s);
 hipError_t launch_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, int32_t* idx,
                          float* max_logit, float* logits, void* workspace, hipStream_t s);

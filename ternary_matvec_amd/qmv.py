@@ -63,6 +63,11 @@ SIGNATURES = {
     "qmv_lmhead_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64,
                                    _c_ptr]),
     "qmv_read_probe": (_c_i32, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
+    "qmv_sketch_bytes": (_c_i64, [_c_i64, _c_i64]),
+    "qmv_sketch_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
+    "qmv_sketch_build": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr]),
+    "qmv_lmhead_sketch_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                          _c_ptr, _c_i64, _c_ptr]),
 }
 
 
@@ -274,3 +279,50 @@ def qmv_lmhead_argmax(w_bf16, x, logits=None, idx=None, max_logit=None, workspac
     _check(load().qmv_lmhead_argmax(_ptr(w_bf16), _ptr(x), v, k, _ptr(idx), _ptr(max_logit), _ptr(logits),
                                     _ptr(workspace), workspace.numel(), _stream(stream)), "qmv_lmhead_argmax")
     return idx, max_logit, logits
+
+
+def qmv_sketch_bytes(v: int, k: int) -> int:
+    return int(load().qmv_sketch_bytes(v, k))
+
+
+def qmv_sketch_workspace_bytes(v: int, k: int) -> int:
+    return int(load().qmv_sketch_workspace_bytes(v, k))
+
+
+def qmv_sketch_build(w_bf16, sketch=None, stream=None):
+    """Builds the sketch tables of a [v][k] bf16 table; returns the uint8 sketch buffer."""
+    if w_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("w_bf16 must hold bf16 bit patterns")
+    v, k = w_bf16.shape
+    nbytes = qmv_sketch_bytes(v, k)
+    if nbytes < 0:
+        raise QmvError(-2, "qmv_sketch_bytes")
+    if sketch is None:
+        sketch = _alloc_aligned(nbytes, w_bf16.device)
+    _check(load().qmv_sketch_build(_ptr(w_bf16), v, k, _ptr(sketch), sketch.numel(), _stream(stream)),
+           "qmv_sketch_build")
+    return sketch
+
+
+def qmv_lmhead_sketch_argmax(w_bf16, sketch, x, idx=None, max_logit=None, candidates=None, scores=None,
+                             workspace=None, want_scores=False, stream=None):
+    """Returns (idx [1] int32, max_logit [1] fp32, candidates [1] int32, scores [v] fp32 or None)."""
+    if w_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("w_bf16 must hold bf16 bit patterns")
+    _dev(x, torch.float32, "x")
+    v, k = w_bf16.shape
+    dev = x.device
+    if idx is None:
+        idx = torch.empty(1, dtype=torch.int32, device=dev)
+    if max_logit is None:
+        max_logit = torch.empty(1, dtype=torch.float32, device=dev)
+    if candidates is None:
+        candidates = torch.empty(1, dtype=torch.int32, device=dev)
+    if scores is None and want_scores:
+        scores = torch.empty(v, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = _alloc_aligned(max(qmv_sketch_workspace_bytes(v, k), 256), dev)
+    _check(load().qmv_lmhead_sketch_argmax(_ptr(w_bf16), _ptr(sketch), _ptr(x), v, k, _ptr(idx), _ptr(max_logit),
+                                           _ptr(candidates), _ptr(scores), _ptr(workspace), workspace.numel(),
+                                           _stream(stream)), "qmv_lmhead_sketch_argmax")
+    return idx, max_logit, candidates, scores
