@@ -514,6 +514,78 @@ def bench_head(dev, stream, reps=50):
             "idx": int(idx.item())}
 
 
+def bench_sketch(dev, stream, reps=50, copies=6, tokens=32):
+    """The sketch head on the output layer: time per token with the tables
+    rotated over `copies` weight/sketch pairs (so they come from HBM, not the
+    256 MB last-level cache), the same on one pair (cache-resident), and how
+    often it picks the exact argmax: on random hidden states, and on peaked
+    ones (x close to one word's row, like a confident model)."""
+    import numpy as np
+    import torch
+    from ternary_matvec_amd import qmv, synth
+    v, k = synth.HEAD_V, synth.HEAD_K
+    w0 = synth.normal_torch(synth.stream_seed(3, 0, 0, synth.TAG_HEAD), (v, k), std=0.02, device=dev)
+    ws_ = [w0.to(torch.bfloat16)]
+    del w0
+    for _ in range(copies - 1):
+        ws_.append(ws_[0].clone())
+    sk = [qmv.qmv_sketch_build(w) for w in ws_]
+    torch.cuda.synchronize()
+    wsp = qmv._alloc_aligned(qmv.qmv_sketch_workspace_bytes(v, k), dev)
+    xs = [torch.from_numpy(synth.normal(synth.stream_seed(3, 1, t, synth.TAG_ACT), (k,))).to(dev)
+          for t in range(tokens)]
+    idx = torch.empty(1, dtype=torch.int32, device=dev)
+    mx = torch.empty(1, dtype=torch.float32, device=dev)
+    nc = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def timed(n_pairs):
+        for i in range(5):
+            qmv.qmv_lmhead_sketch_argmax(ws_[i % n_pairs], sk[i % n_pairs], xs[i % tokens], idx=idx, max_logit=mx,
+                                         candidates=nc, workspace=wsp, stream=stream)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(reps):
+            qmv.qmv_lmhead_sketch_argmax(ws_[i % n_pairs], sk[i % n_pairs], xs[i % tokens], idx=idx, max_logit=mx,
+                                         candidates=nc, workspace=wsp, stream=stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    ms_hbm = timed(copies)
+    ms_cached = timed(1)
+    # agreement with the exact search, and the candidate counts
+    wsl = qmv._alloc_aligned(qmv.qmv_lmhead_workspace_bytes(v, k), dev)
+    wf = ws_[0].float()
+    rng = np.random.default_rng(5)
+    agree = {"random": 0, "peaked": 0}
+    ncands = []
+    for kind in ("random", "peaked"):
+        for t in range(tokens):
+            if kind == "random":
+                x = xs[t]
+            else:
+                r = int(rng.integers(0, v))
+                x = (8.0 * wf[r] + torch.from_numpy(synth.normal(synth.stream_seed(3, 2, t, synth.TAG_ACT),
+                                                                 (k,))).to(dev) * 0.05).contiguous()
+            qmv.qmv_lmhead_sketch_argmax(ws_[0], sk[0], x, idx=idx, max_logit=mx, candidates=nc, workspace=wsp,
+                                         stream=stream)
+            ie, _, _ = qmv.qmv_lmhead_argmax(ws_[0], x, workspace=wsl, stream=stream)
+            torch.cuda.synchronize()
+            agree[kind] += int(idx.item() == ie.item())
+            ncands.append(int(nc.item()))
+    kw = (k + 31) // 32
+    cand = float(np.mean(ncands))
+    nbytes = 4 * kw * v + 2 * 32 * v + cand * 2 * k + 8 * v + 4 * k
+    return {"workload": "sketch head on the bf16 output layer 262144x1152: 32 exact dims + 1-bit groups, "
+                        ">=1024 candidates rescored",
+            "us": round(ms_hbm * 1e3, 2), "us_cache_resident": round(ms_cached * 1e3, 2),
+            "weight_copies": copies, "bytes_per_token": int(nbytes), "GB/s": round(nbytes / ms_hbm / 1e6, 1),
+            "candidates_mean": round(cand, 1),
+            "agrees_with_exact_argmax": {k_: "%d/%d" % (a, tokens) for k_, a in agree.items()}}
+
+
 def bench_int8(dev, stream, reps=2000):
     import torch
     from ternary_matvec_amd import qmv, synth
@@ -648,6 +720,9 @@ def main():
         log("output layer")
         result["extras"] = {"lmhead": bench_head(dev, stream)}
         torch.cuda.empty_cache()
+        log("sketch head")
+        result["extras"]["lmhead_sketch"] = bench_sketch(dev, stream)
+        torch.cuda.empty_cache()
     elif not args.no_extras:
         extras = {}
         try:
@@ -657,6 +732,11 @@ def main():
             extras["quantize_step"] = time_quantize(stack, max(20, args.steps // 2), stream)
             log("output layer")
             extras["lmhead"] = bench_head(dev, stream)
+            torch.cuda.empty_cache()
+            log("sketch head")
+            extras["lmhead_sketch"] = bench_sketch(dev, stream)
+            extras["lmhead_sketch"]["speedup_vs_full_head"] = round(extras["lmhead"]["us"] /
+                                                                    extras["lmhead_sketch"]["us"], 2)
             torch.cuda.empty_cache()
             log("int8 GEMV")
             extras["int8_gemv"] = bench_int8(dev, stream)

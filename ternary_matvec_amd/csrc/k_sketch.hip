@@ -59,10 +59,14 @@ struct SketchPlan {
     // then masks [kSkGroups][kw] and the sign words of x [kw]
 };
 static_assert(sizeof(SketchPlan) == 320, "sketch plan");
+constexpr int kSkHistCopies = 8;        // private histograms (workgroup b adds into copy b % 8)
+constexpr int kSkScoreThreads = 1024;   // score: a thread per row
 constexpr int64_t kSkPlanBytes = 8192;
 constexpr int64_t kSkHistOff = kSkPlanBytes;
-constexpr int64_t kSkPickOff = kSkHistOff + kSkBins * 4;   // u64 best, u32 done, u32 candidates
-constexpr int64_t kSkKeysOff = kSkPickOff + 256;
+constexpr int64_t kSkPickOff = kSkHistOff + kSkHistCopies * kSkBins * 4;   // u32 b*
+constexpr int64_t kSkWgOff = kSkPickOff + 256;   // per rescore workgroup: u64 best, then u32 counts
+constexpr int64_t kSkMaxWg = (((int64_t)1 << 24) + kSkRowsPerBlock - 1) / kSkRowsPerBlock;
+constexpr int64_t kSkKeysOff = kSkWgOff + 12 * kSkMaxWg;
 
 constexpr int64_t sk_round(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
 
@@ -164,8 +168,68 @@ __global__ __launch_bounds__(kBlock) void k_sketch_transpose(const uint16_t* __r
 
 // ---- per token ----------------------------------------------------------------------------
 
-// One workgroup of 1024 threads; dynamic LDS: the sort keys (P = power of two
-// >= k, 8 bytes each) then the masks and x sign words (5 * kw words).
+// Bitonic sort of P = 1024 M keys, descending, by the plan's 1024 threads:
+// thread t holds elements M t .. M t + M - 1 in registers.  A stage with
+// stride s pairs element e with e ^ s: inside the thread when s < M, with
+// lane t ^ (s / M) of the same wave when s / M < 64 (register shuffles, no
+// barrier), else through LDS (`key`) between two workgroup barriers.  The
+// sorted keys are left in `key`.
+template <int M>
+__device__ __forceinline__ void sort_keys_desc(uint64_t* key, int tid)
+{
+    constexpr int P = 1024 * M;
+    uint64_t kk[M];
+#pragma unroll
+    for (int j = 0; j < M; ++j) kk[j] = key[M * tid + j];
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride < M) {
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+                    if (j & stride) continue;
+                    const int e = M * tid + j;
+                    const bool desc = (e & size) == 0;
+                    const uint64_t a = kk[j], b = kk[j | stride];
+                    if ((a < b) == desc) {
+                        kk[j] = b;
+                        kk[j | stride] = a;
+                    }
+                }
+            } else if (stride / M < kWave) {
+                const int d = stride / M;
+                const bool lo = (tid & d) == 0;
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+                    const uint64_t other = __shfl_xor(kk[j], d);
+                    const bool desc = ((M * tid + j) & size) == 0;
+                    const bool keep_max = lo == desc;
+                    kk[j] = keep_max ? (kk[j] > other ? kk[j] : other) : (kk[j] < other ? kk[j] : other);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < M; ++j) key[M * tid + j] = kk[j];
+                __syncthreads();
+                const bool lo = ((M * tid) & stride) == 0;
+#pragma unroll
+                for (int j = 0; j < M; ++j) {
+                    const int e = M * tid + j;
+                    const uint64_t other = key[e ^ stride];
+                    const bool desc = (e & size) == 0;
+                    const bool keep_max = lo == desc;
+                    kk[j] = keep_max ? (kk[j] > other ? kk[j] : other) : (kk[j] < other ? kk[j] : other);
+                }
+                __syncthreads();
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < M; ++j) key[M * tid + j] = kk[j];
+    __syncthreads();
+}
+
+// One workgroup of 1024 threads; dynamic LDS: the sort keys (P = the larger
+// of 1024 and the power of two >= k, 8 bytes each) then the masks and x sign
+// words (5 * kw words).
 __global__ __launch_bounds__(kSkPlanThreads) void k_sketch_plan(const float* __restrict__ x, int k, int p2,
                                                                 const SketchHeader* __restrict__ hdr,
                                                                 uint8_t* __restrict__ ws)
@@ -180,22 +244,10 @@ __global__ __launch_bounds__(kSkPlanThreads) void k_sketch_plan(const float* __r
         key[i] = i < k ? ((uint64_t)__float_as_uint(fabsf(x[i])) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
     for (int i = tid; i < 5 * kw; i += kSkPlanThreads) mbits[i] = 0u;
     __syncthreads();
-    // bitonic sort, descending
-    for (int size = 2; size <= p2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < p2 / 2; i += kSkPlanThreads) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;
-                const uint64_t a = key[lo], b = key[hi];
-                if ((a < b) == desc) {
-                    key[lo] = b;
-                    key[hi] = a;
-                }
-            }
-            __syncthreads();
-        }
-    }
+    if (p2 == 1024) sort_keys_desc<1>(key, tid);
+    else if (p2 == 2048) sort_keys_desc<2>(key, tid);
+    else if (p2 == 4096) sort_keys_desc<4>(key, tid);
+    else sort_keys_desc<8>(key, tid);
     SketchPlan* plan = reinterpret_cast<SketchPlan*>(ws);
     const int t = min(k, kSkTop);
     const int rest = k - t, base = rest / kSkGroups;
@@ -213,11 +265,19 @@ __global__ __launch_bounds__(kSkPlanThreads) void k_sketch_plan(const float* __r
     for (int i = tid; i < k; i += kSkPlanThreads)
         if (x[i] < 0.0f) atomicOr(&mbits[kSkGroups * kw + (i >> 5)], 1u << (i & 31));
     if (tid < kSkGroups) {
-        // group sums of |x| in rank order, fp32
+        // group sums of |x| in rank order, fp32; |x| is the high word of the sorted key
         const int lo = t + tid * base;
         const int hi = tid == kSkGroups - 1 ? k : lo + base;
         float sum = 0.0f;
-        for (int rank = lo; rank < hi; ++rank) sum += fabsf(x[dim_of(rank)]);
+        int rank = lo;
+        for (; rank + 8 <= hi; rank += 8) {
+            float v8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v8[j] = __uint_as_float((uint32_t)(key[rank + j] >> 32));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sum += v8[j];
+        }
+        for (; rank < hi; ++rank) sum += __uint_as_float((uint32_t)(key[rank] >> 32));
         const float mean = hi > lo ? sum / (float)(hi - lo) : 0.0f;
         plan->n[tid] = hi - lo;
         plan->wgt[tid] = hdr->c * mean;
@@ -226,19 +286,19 @@ __global__ __launch_bounds__(kSkPlanThreads) void k_sketch_plan(const float* __r
         plan->t = t;
         plan->kw = kw;
     }
-    // clear the histogram and the pick for this token
-    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + kSkHistOff);
-    for (int i = tid; i < kSkBins; i += kSkPlanThreads) hist[i] = 0u;
-    if (tid < 4) reinterpret_cast<uint32_t*>(ws + kSkPickOff)[tid] = 0u;
+    // clear the histograms for this token
+    uint4* hist4 = reinterpret_cast<uint4*>(ws + kSkHistOff);
+    for (int i = tid; i < kSkHistCopies * kSkBins / 4; i += kSkPlanThreads) hist4[i] = make_uint4(0, 0, 0, 0);
     __syncthreads();
     uint32_t* mout = reinterpret_cast<uint32_t*>(ws + sizeof(SketchPlan));
     for (int i = tid; i < 5 * kw; i += kSkPlanThreads) mout[i] = mbits[i];
 }
 
-// 256 threads, 1024 rows per workgroup (rows base + tid + 256 i).
-__global__ __launch_bounds__(kBlock) void k_sketch_score(const uint32_t* __restrict__ signs,
-                                                         const uint16_t* __restrict__ wt, int64_t v,
-                                                         uint8_t* __restrict__ ws, float* __restrict__ scores)
+// A thread per row, 1024 rows per workgroup; the workgroup's histogram is
+// added into private copy blockIdx % 8 (a hot bin then takes few atomics).
+__global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t* __restrict__ signs,
+                                                                  const uint16_t* __restrict__ wt, int64_t v,
+                                                                  uint8_t* __restrict__ ws, float* __restrict__ scores)
 {
     __shared__ uint32_t sbits[5 * 256];
     __shared__ uint32_t shist[kSkBins];
@@ -248,8 +308,8 @@ __global__ __launch_bounds__(kBlock) void k_sketch_score(const uint32_t* __restr
     const int tid = threadIdx.x;
     const int t = plan->t, kw = plan->kw;
     const uint32_t* mbits = reinterpret_cast<const uint32_t*>(ws + sizeof(SketchPlan));
-    for (int i = tid; i < 5 * kw; i += kBlock) sbits[i] = mbits[i];
-    for (int i = tid; i < kSkBins; i += kBlock) shist[i] = 0u;
+    for (int i = tid; i < 5 * kw; i += kSkScoreThreads) sbits[i] = mbits[i];
+    for (int i = tid; i < kSkBins; i += kSkScoreThreads) shist[i] = 0u;
     if (tid < kSkTop) {
         s_idx[tid] = plan->top_idx[tid];
         s_x[tid] = plan->top_x[tid];
@@ -262,84 +322,70 @@ __global__ __launch_bounds__(kBlock) void k_sketch_score(const uint32_t* __restr
         ng[g] = plan->n[g];
     }
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kSkRowsPerBlock + tid;
-    float a[4];
-    bool live[4];
+    const int64_t r = (int64_t)blockIdx.x * kSkScoreThreads + tid;
+    const bool live = r < v;
+    const int64_t rr = live ? r : v - 1;   // a valid address for every lane; only live rows count
+    // step 1: the exact dimensions, in rank order (loads batched, FMAs in order)
+    float a = 0.0f;
+    int j = 0;
+    for (; j + 8 <= t; j += 8) {
+        uint16_t h[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a[i] = 0.0f;
-        live[i] = base + 256 * i < v;
-    }
-    // step 1: the exact dimensions, in rank order
-    for (int j = 0; j < t; ++j) {
-        const uint16_t* col = wt + (int64_t)s_idx[j] * v;
-        const float xj = s_x[j];
+        for (int u = 0; u < 8; ++u) h[u] = wt[(int64_t)s_idx[j + u] * v + rr];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (live[i]) a[i] = fmaf(bf16f(col[base + 256 * i]), xj, a[i]);
+        for (int u = 0; u < 8; ++u) a = fmaf(bf16f(h[u]), s_x[j + u], a);
     }
+    for (; j < t; ++j) a = fmaf(bf16f(wt[(int64_t)s_idx[j] * v + rr]), s_x[j], a);
     // step 2: sign agreement per group
-    int cnt[4][kSkGroups] = {};
-    for (int w = 0; w < kw; ++w) {
-        const uint32_t xs = sbits[kSkGroups * kw + w];
-        uint32_t m[kSkGroups];
+    int cnt[kSkGroups] = {0, 0, 0, 0};
+    int w = 0;
+    for (; w + 6 <= kw; w += 6) {
+        uint32_t sw6[6];
 #pragma unroll
-        for (int g = 0; g < kSkGroups; ++g) m[g] = sbits[g * kw + w];
-        const uint32_t* srow = signs + (int64_t)w * v;
+        for (int u = 0; u < 6; ++u) sw6[u] = signs[(int64_t)(w + u) * v + rr];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (!live[i]) continue;
-            const uint32_t d = srow[base + 256 * i] ^ xs;
+        for (int u = 0; u < 6; ++u) {
+            const uint32_t d = sw6[u] ^ sbits[kSkGroups * kw + w + u];
 #pragma unroll
-            for (int g = 0; g < kSkGroups; ++g) cnt[i][g] += __popc(d & m[g]);
+            for (int g = 0; g < kSkGroups; ++g) cnt[g] += __popc(d & sbits[g * kw + w + u]);
         }
     }
-    uint32_t* keys = reinterpret_cast<uint32_t*>(ws + kSkKeysOff);
+    for (; w < kw; ++w) {
+        const uint32_t d = signs[(int64_t)w * v + rr] ^ sbits[kSkGroups * kw + w];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if (!live[i]) continue;
+        for (int g = 0; g < kSkGroups; ++g) cnt[g] += __popc(d & sbits[g * kw + w]);
+    }
 #pragma unroll
-        for (int g = 0; g < kSkGroups; ++g) a[i] = fmaf(wgt[g], (float)(ng[g] - 2 * cnt[i][g]), a[i]);
-        const uint32_t key = order_key(a[i]);
-        keys[base + 256 * i] = key;
-        if (scores) scores[base + 256 * i] = a[i];
+    for (int g = 0; g < kSkGroups; ++g) a = fmaf(wgt[g], (float)(ng[g] - 2 * cnt[g]), a);
+    const uint32_t key = order_key(a);
+    if (live) {
+        reinterpret_cast<uint32_t*>(ws + kSkKeysOff)[r] = key;
+        if (scores) scores[r] = a;
         atomicAdd(&shist[key >> 20], 1u);
     }
     __syncthreads();
-    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + kSkHistOff);
-    for (int i = tid; i < kSkBins; i += kBlock)
+    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + kSkHistOff) + (blockIdx.x % kSkHistCopies) * kSkBins;
+    for (int i = tid; i < kSkBins; i += kSkScoreThreads)
         if (shist[i]) atomicAdd(&hist[i], shist[i]);
 }
 
-// 256 threads, 1024 rows per workgroup.  Dynamic LDS: x (k floats).
-__global__ __launch_bounds__(kBlock) void k_sketch_rescore(const uint16_t* __restrict__ w, const float* __restrict__ x,
-                                                           int64_t v, int k, uint8_t* __restrict__ ws,
-                                                           int32_t* __restrict__ idx, float* __restrict__ max_logit,
-                                                           int32_t* __restrict__ ncand)
+// One workgroup of 1024 threads: b*, the highest bin at which the bins from
+// the top down first hold min(1024, v) words.  Thread t owns bins
+// 4095 - 4t - 3 .. 4095 - 4t.
+__global__ __launch_bounds__(kSkPlanThreads) void k_sketch_select(int64_t v, uint8_t* __restrict__ ws)
 {
-    extern __shared__ __align__(16) float xs[];
-    __shared__ uint32_t ssum[kBlock];
-    __shared__ int32_t s_bstar;
-    __shared__ int32_t s_n;
-    __shared__ int32_t s_list[kSkRowsPerBlock];
-    __shared__ bool s_last;
+    __shared__ uint32_t ssum[kSkPlanThreads];
     const int tid = threadIdx.x;
-    for (int i = tid; i < k; i += kBlock) xs[i] = x[i];
-    // b*: the highest bin at which the bins from the top down first hold
-    // min(1024, v) words.  Thread t sums bins 4095 - 16t - 15 .. 4095 - 16t.
     const uint32_t* hist = reinterpret_cast<const uint32_t*>(ws + kSkHistOff);
-    const int hi_bin = kSkBins - 1 - 16 * tid;
-    uint32_t local = 0;
+    const int hi_bin = kSkBins - 1 - 4 * tid;
+    uint32_t hv[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int j = 0; j < 16; ++j) local += hist[hi_bin - j];
-    ssum[tid] = local;
-    if (tid == 0) {
-        s_n = 0;
-        s_bstar = 0;
-    }
+    for (int c = 0; c < kSkHistCopies; ++c)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) hv[u] += hist[c * kSkBins + hi_bin - u];
+    ssum[tid] = hv[0] + hv[1] + hv[2] + hv[3];
     __syncthreads();
-    // inclusive scan over threads (from the top bins down)
-    for (int off = 1; off < kBlock; off <<= 1) {
+    for (int off = 1; off < kSkPlanThreads; off <<= 1) {
         const uint32_t add = tid >= off ? ssum[tid - off] : 0u;
         __syncthreads();
         ssum[tid] += add;
@@ -349,65 +395,125 @@ __global__ __launch_bounds__(kBlock) void k_sketch_rescore(const uint16_t* __res
     const uint32_t before = tid ? ssum[tid - 1] : 0u;
     if (before < need && ssum[tid] >= need) {
         uint32_t run = before;
-        for (int j = 0; j < 16; ++j) {
-            run += hist[hi_bin - j];
+        for (int u = 0; u < 4; ++u) {
+            run += hv[u];
             if (run >= need) {
-                s_bstar = hi_bin - j;
+                reinterpret_cast<uint32_t*>(ws + kSkPickOff)[0] = (uint32_t)(hi_bin - u);
                 break;
             }
         }
     }
+}
+
+// 256 threads, 1024 rows per workgroup.  Dynamic LDS: x (k floats).  Each
+// workgroup writes its best (logit key << 32 | ~row) and its candidate count.
+__global__ __launch_bounds__(kBlock) void k_sketch_rescore(const uint16_t* __restrict__ w, const float* __restrict__ x,
+                                                           int64_t v, int k, uint8_t* __restrict__ ws)
+{
+    extern __shared__ __align__(16) float xs[];
+    __shared__ int32_t s_n;
+    __shared__ int32_t s_list[kSkRowsPerBlock];
+    __shared__ unsigned long long s_best[kBlock / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint32_t bstar = reinterpret_cast<const uint32_t*>(ws + kSkPickOff)[0];
+    if (tid == 0) s_n = 0;
+    if (lane == 0) s_best[wave] = 0ull;
     __syncthreads();
-    const uint32_t bstar = (uint32_t)s_bstar;
     // this workgroup's candidates
     const uint32_t* keys = reinterpret_cast<const uint32_t*>(ws + kSkKeysOff);
     const int64_t base = (int64_t)blockIdx.x * kSkRowsPerBlock;
-    for (int i = tid; i < kSkRowsPerBlock; i += kBlock) {
-        const int64_t r = base + i;
-        if (r < v && (keys[r] >> 20) >= bstar) s_list[atomicAdd(&s_n, 1)] = (int32_t)r;
+    uint32_t kv4[kSkRowsPerBlock / kBlock];
+#pragma unroll
+    for (int i = 0; i < kSkRowsPerBlock / kBlock; ++i) {
+        const int64_t r = base + tid + kBlock * i;
+        kv4[i] = r < v ? keys[r] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kSkRowsPerBlock / kBlock; ++i) {
+        const int64_t r = base + tid + kBlock * i;
+        if (r < v && (kv4[i] >> 20) >= bstar) s_list[atomicAdd(&s_n, 1)] = (int32_t)r;
     }
     __syncthreads();
     const int n = s_n;
-    uint32_t* pick = reinterpret_cast<uint32_t*>(ws + kSkPickOff);
-    unsigned long long* best = reinterpret_cast<unsigned long long*>(pick);
-    if (tid == 0 && n) atomicAdd(&pick[3], (uint32_t)n);
-    // exact logits: one wave per candidate, 16-byte chunks over the lanes
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    for (int c = wave; c < n; c += kBlock / kWave) {
-        const int64_t r = s_list[c];
-        const uint4* row = reinterpret_cast<const uint4*>(w + r * k);
-        float s = 0.0f;
-        for (int ch = lane; ch < k / 8; ch += kWave) {
-            const uint4 q = row[ch];
-            const float* xc = xs + 8 * ch;
-            s = fmaf(__uint_as_float(q.x << 16), xc[0], s);
-            s = fmaf(__uint_as_float(q.x & 0xFFFF0000u), xc[1], s);
-            s = fmaf(__uint_as_float(q.y << 16), xc[2], s);
-            s = fmaf(__uint_as_float(q.y & 0xFFFF0000u), xc[3], s);
-            s = fmaf(__uint_as_float(q.z << 16), xc[4], s);
-            s = fmaf(__uint_as_float(q.z & 0xFFFF0000u), xc[5], s);
-            s = fmaf(__uint_as_float(q.w << 16), xc[6], s);
-            s = fmaf(__uint_as_float(q.w & 0xFFFF0000u), xc[7], s);
-        }
+    if (n) {
+        for (int i = tid; i < k; i += kBlock) xs[i] = x[i];
+        __syncthreads();
+        // exact logits: one wave per candidate, 16-byte chunks over the lanes, a
+        // row's loads issued together
+        const int nch = k / 8;
+        unsigned long long mine = 0ull;
+        for (int c = wave; c < n; c += kBlock / kWave) {
+            const int64_t r = s_list[c];
+            const uint4* row = reinterpret_cast<const uint4*>(w + r * k);
+            float s = 0.0f;
+            for (int ch0 = lane; ch0 < nch; ch0 += 4 * kWave) {
+                uint4 q[4];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-        if (lane == 0) {
+                for (int u = 0; u < 4; ++u) q[u] = ch0 + u * kWave < nch ? row[ch0 + u * kWave] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int ch = ch0 + u * kWave;
+                    if (ch >= nch) break;
+                    const float* xc = xs + 8 * ch;
+                    s = fmaf(__uint_as_float(q[u].x << 16), xc[0], s);
+                    s = fmaf(__uint_as_float(q[u].x & 0xFFFF0000u), xc[1], s);
+                    s = fmaf(__uint_as_float(q[u].y << 16), xc[2], s);
+                    s = fmaf(__uint_as_float(q[u].y & 0xFFFF0000u), xc[3], s);
+                    s = fmaf(__uint_as_float(q[u].z << 16), xc[4], s);
+                    s = fmaf(__uint_as_float(q[u].z & 0xFFFF0000u), xc[5], s);
+                    s = fmaf(__uint_as_float(q[u].w << 16), xc[6], s);
+                    s = fmaf(__uint_as_float(q[u].w & 0xFFFF0000u), xc[7], s);
+                }
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
             const unsigned long long kv =
                 ((unsigned long long)order_key(s) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)r);
-            atomicMax(best, kv);
+            mine = kv > mine ? kv : mine;
         }
+        if (lane == 0) s_best[wave] = mine;
     }
-    // the last workgroup to finish writes the pick
-    __threadfence();
     __syncthreads();
-    if (tid == 0) s_last = atomicAdd(&pick[2], 1u) == gridDim.x - 1;
+    if (tid == 0) {
+        unsigned long long b = 0ull;
+#pragma unroll
+        for (int i = 0; i < kBlock / kWave; ++i) b = s_best[i] > b ? s_best[i] : b;
+        reinterpret_cast<unsigned long long*>(ws + kSkWgOff)[blockIdx.x] = b;
+        reinterpret_cast<uint32_t*>(ws + kSkWgOff + 8 * kSkMaxWg)[blockIdx.x] = (uint32_t)n;
+    }
+}
+
+// One workgroup: the overall first maximum and the candidate count.
+__global__ __launch_bounds__(kBlock) void k_sketch_final(int nwg, const uint8_t* __restrict__ ws,
+                                                         int32_t* __restrict__ idx, float* __restrict__ max_logit,
+                                                         int32_t* __restrict__ ncand)
+{
+    __shared__ unsigned long long sb[kBlock];
+    __shared__ uint32_t sn[kBlock];
+    const int tid = threadIdx.x;
+    const unsigned long long* wb = reinterpret_cast<const unsigned long long*>(ws + kSkWgOff);
+    const uint32_t* wn = reinterpret_cast<const uint32_t*>(ws + kSkWgOff + 8 * kSkMaxWg);
+    unsigned long long b = 0ull;
+    uint32_t n = 0;
+    for (int i = tid; i < nwg; i += kBlock) {
+        b = wb[i] > b ? wb[i] : b;
+        n += wn[i];
+    }
+    sb[tid] = b;
+    sn[tid] = n;
     __syncthreads();
-    if (s_last && tid == 0) {
-        __threadfence();
-        const unsigned long long kv = atomicMax(best, 0ull);
-        *idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(kv & 0xFFFFFFFFu));
-        if (max_logit) *max_logit = key_value((uint32_t)(kv >> 32));
-        if (ncand) *ncand = (int32_t)atomicAdd(&pick[3], 0u);
+    for (int off = kBlock / 2; off > 0; off >>= 1) {
+        if (tid < off) {
+            sb[tid] = sb[tid + off] > sb[tid] ? sb[tid + off] : sb[tid];
+            sn[tid] += sn[tid + off];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        *idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(sb[0] & 0xFFFFFFFFu));
+        if (max_logit) *max_logit = key_value((uint32_t)(sb[0] >> 32));
+        if (ncand) *ncand = (int32_t)sn[0];
     }
 }
 
@@ -460,7 +566,7 @@ hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const flo
     const uint32_t* signs = reinterpret_cast<const uint32_t*>(base + 256);
     const uint16_t* wt = reinterpret_cast<const uint16_t*>(base + 256 + sk_round(4 * kw * v, 256));
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    int p2 = 1;
+    int p2 = 1024;
     while (p2 < k) p2 <<= 1;
     const size_t plan_lds = 8 * (size_t)p2 + 20 * (size_t)kw;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_plan),
@@ -470,15 +576,21 @@ hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const flo
                        reinterpret_cast<const SketchHeader*>(base), ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned grid = (unsigned)((v + kSkRowsPerBlock - 1) / kSkRowsPerBlock);
-    hipLaunchKernelGGL(k_sketch_score, dim3(grid), dim3(kBlock), 0, s, signs, wt, v, ws, scores);
+    hipLaunchKernelGGL(k_sketch_score, dim3((unsigned)((v + kSkScoreThreads - 1) / kSkScoreThreads)),
+                       dim3(kSkScoreThreads), 0, s, signs, wt, v, ws, scores);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sketch_select, dim3(1), dim3(kSkPlanThreads), 0, s, v, ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_rescore),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(4 * k));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sketch_rescore, dim3(grid), dim3(kBlock), (size_t)(4 * k), s, w, x, v, (int)k, ws, idx,
-                       max_logit, ncand);
+    const int nwg = (int)((v + kSkRowsPerBlock - 1) / kSkRowsPerBlock);
+    hipLaunchKernelGGL(k_sketch_rescore, dim3((unsigned)nwg), dim3(kBlock), (size_t)(4 * k), s, w, x, v, (int)k, ws);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sketch_final, dim3(1), dim3(kBlock), 0, s, nwg, ws, idx, max_logit, ncand);
     return hipGetLastError();
 }
 
