@@ -46,6 +46,8 @@ def _load():
         lib.oracle_sketch_scores.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_float, _ptr, ctypes.c_int]
         lib.oracle_sketch_pick.argtypes = [_ptr, _ptr, _i64, _i64, _ptr, _ptr, _ptr, _ptr]
         lib.oracle_sketch_pick.restype = _i64
+        lib.oracle_rmsnorm_quantize.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_float, _ptr, _ptr, _ptr]
+        lib.oracle_glu.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_int, _ptr]
         _lib = lib
     return _lib
 
@@ -221,6 +223,35 @@ def sketch_head(w_bf16, x, threads: int = 0):
     return idx, is_cand, scores, logits
 
 
-__all__ = ["max_threads", "quantize_rows", "quantize_tensor", "trit5_row_bytes", "trit5_row_stride",
+def rmsnorm_quantize(x, weight, eps=1e-5):
+    """RMSNorm (fp32, the kernel's reduction order) then per-row int8: (int8 [m][k], fp32 [m], fp32 o [m][k])."""
+    x, px = _c(np.atleast_2d(x), np.float32)
+    w, pw = _c(weight, np.float32)
+    m, k = x.shape
+    assert w.size == k
+    q = np.empty((m, k), np.int8)
+    s = np.empty(m, np.float32)
+    o = np.empty((m, k), np.float32)
+    _load().oracle_rmsnorm_quantize(px, pw, m, k, ctypes.c_float(eps), q.ctypes.data, s.ctypes.data, o.ctypes.data)
+    return q, s, o
+
+
+GLU_GELU_TANH = 1
+GLU_SILU = 2
+
+
+def glu(gate, up, act):
+    """act(gate) * up in fp64 (act 1 = GeLU tanh form, 2 = SiLU)."""
+    g, pg = _c(np.atleast_2d(gate), np.float32)
+    u, pu = _c(np.atleast_2d(up), np.float32)
+    assert g.shape == u.shape
+    m, n = g.shape
+    h = np.empty((m, n), np.float64)
+    _load().oracle_glu(pg, pu, m, n, int(act), h.ctypes.data)
+    return h
+
+
+__all__ = ["rmsnorm_quantize", "glu", "GLU_GELU_TANH", "GLU_SILU",
+           "max_threads", "quantize_rows", "quantize_tensor", "trit5_row_bytes", "trit5_row_stride",
            "int8_row_stride", "pack_trit5", "unpack_trit5", "layout_int8", "matmul_int", "dequant",
            "lmhead", "sketch_signs", "sketch_scale", "sketch_plan", "sketch_scores", "sketch_pick", "sketch_head"]

@@ -459,6 +459,66 @@ int64_t oracle_sketch_pick(const uint16_t* w, const float* x, int64_t v, int64_t
     return count;
 }
 
+/* ------------------------------------------------------------------------ */
+/* O8 -- the steps either side of a GEMV: RMSNorm -> int8, gate -> int8.    */
+/*                                                                          */
+/* [L] "Step 1" and "Step 6": RMSNorm divides each value by the root mean   */
+/* square of the row (plus 1e-5 under the root) and multiplies by a        */
+/* per-dimension weight: o = weight * (r * x), r = 1 / sqrt(ss / k + eps).  */
+/* [L] "Step 5": the gated feed-forward multiplies act(gate) by up, act =   */
+/* SiLU(v) = v / (1 + exp(-v)); cpp20gemma and gemma.cpp use a GeLU gate   */
+/* instead (GeGLU).  [T] "Step 2": the result is then rounded to int8 per  */
+/* token (O1).                                                              */
+/* Readings:                                                                */
+/*  - RMSNorm is fp32 as in [L]'s listing.  The sum of squares is an fp32   */
+/*    sum; the listing adds sequentially, any order rounds the same RMS     */
+/*    equally well, and this one is the GPU's: 256 partial sums, partial t  */
+/*    taking x[j]^2 for j = t, t + 256, ... in order, then pairwise         */
+/*    (partial[t] += partial[t + s] for s = 128, 64, ..., 1).  The int8     */
+/*    codes are then decided from the same fp32 values on both sides.       */
+/*  - GeLU is the tanh form used by Gemma: 0.5 v (1 + tanh(sqrt(2/pi) (v +  */
+/*    0.044715 v^3))).  The gated values are computed in fp64 here; the GPU */
+/*    computes them in fp32 with its own exp/tanh, so its codes are checked */
+/*    as valid roundings of these values (see the tests).                   */
+/* ------------------------------------------------------------------------ */
+
+void oracle_rmsnorm_quantize(const float* x, const float* weight, int64_t m, int64_t k, float eps, int8_t* q,
+                             float* s, float* o_out)
+{
+    float* o = (float*)malloc((size_t)k * sizeof(float));
+    assert(o);
+    for (int64_t mi = 0; mi < m; ++mi) {
+        const float* xr = x + mi * k;
+        float part[256];
+        for (int t = 0; t < 256; ++t) {
+            float a = 0.0f;
+            for (int64_t j = t; j < k; j += 256) {
+                assert(isfinite(xr[j]));
+                a += xr[j] * xr[j];
+            }
+            part[t] = a;
+        }
+        for (int st = 128; st >= 1; st /= 2)
+            for (int t = 0; t < st; ++t) part[t] += part[t + st];
+        float r = 1.0f / sqrtf(part[0] / (float)k + eps);
+        for (int64_t j = 0; j < k; ++j) o[j] = weight[j] * (r * xr[j]);
+        if (o_out) memcpy(o_out + mi * k, o, (size_t)k * sizeof(float));
+        oracle_quantize_rows(o, 1, k, q + mi * k, s + mi);
+    }
+    free(o);
+}
+
+/* act: 1 = GeLU (tanh form), 2 = SiLU.  h = act(gate) * up in fp64. */
+void oracle_glu(const float* gate, const float* up, int64_t m, int64_t n, int act, double* h)
+{
+    const double c = sqrt(2.0 / 3.14159265358979323846);
+    for (int64_t i = 0; i < m * n; ++i) {
+        double g = gate[i];
+        double a = act == 1 ? 0.5 * g * (1.0 + tanh(c * (g + 0.044715 * g * g * g))) : g / (1.0 + exp(-g));
+        h[i] = a * (double)up[i];
+    }
+}
+
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
 int oracle_max_threads(void)
 {

@@ -442,6 +442,51 @@ def test_sketch_pick_planted_winner():
 
 
 # --------------------------------------------------------------------------
+# O8 fused RMSNorm / gated activation before quantisation
+# --------------------------------------------------------------------------
+
+def test_rmsnorm_matches_definition_and_is_scale_invariant():
+    import math
+    for m, k in [(3, 1152), (2, 257), (1, 1), (4, 6912)]:
+        x = synth.normal(81 + k, (m, k))
+        w = synth.normal(82 + k, (k,)) * 0.5 + 1.0
+        q, s, o = oracle.rmsnorm_quantize(x, w, 1e-5)
+        # the definition in exact rationals -> within a few fp32 rounding steps
+        for r in range(m):
+            ss = sum(Fraction(float(v)) ** 2 for v in x[r])
+            rms = math.sqrt(float(ss / k) + 1e-5)
+            ref = w.astype(np.float64) * x[r].astype(np.float64) / rms
+            np.testing.assert_allclose(o[r], ref, rtol=(k + 8) * 2.0 ** -24, atol=0)
+        # the codes are O1's codes of o
+        q2, s2 = oracle.quantize_rows(o)
+        np.testing.assert_array_equal(q, q2)
+        np.testing.assert_array_equal(s.view(np.uint32), s2.view(np.uint32))
+        # eps = 0: scaling x by a power of two changes nothing, bit for bit
+        _, _, o0 = oracle.rmsnorm_quantize(x, w, 0.0)
+        _, _, o1 = oracle.rmsnorm_quantize(x * np.float32(8.0), w, 0.0)
+        np.testing.assert_array_equal(o0, o1)
+    # unit weights: the output's mean square is 1 / (1 + eps / mean(x^2))
+    x = synth.normal(85, (1, 4096))
+    _, _, o = oracle.rmsnorm_quantize(x, np.ones(4096, np.float32), 1e-5)
+    ms = float(np.mean(x.astype(np.float64) ** 2))
+    assert abs(float(np.mean(o.astype(np.float64) ** 2)) - 1.0 / (1.0 + 1e-5 / ms)) < 1e-5
+
+
+def test_glu_matches_library_activations():
+    import torch
+    g = np.concatenate([synth.normal(86, (1, 500)) * 4.0, np.array([[0.0, -0.0, 30.0, -30.0, 1.0]], np.float32)], 1)
+    u = synth.normal(87, g.shape)
+    gt = torch.from_numpy(g.astype(np.float64))
+    ut = torch.from_numpy(u.astype(np.float64))
+    ref_gelu = (torch.nn.functional.gelu(gt, approximate="tanh") * ut).numpy()
+    ref_silu = (torch.nn.functional.silu(gt) * ut).numpy()
+    np.testing.assert_allclose(oracle.glu(g, u, oracle.GLU_GELU_TANH), ref_gelu, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.glu(g, u, oracle.GLU_SILU), ref_silu, rtol=1e-13, atol=1e-15)
+    h = oracle.glu(np.zeros((1, 4), np.float32), np.ones((1, 4), np.float32), oracle.GLU_GELU_TANH)
+    assert np.all(h == 0.0)
+
+
+# --------------------------------------------------------------------------
 # The seeded generator itself (not the oracle): published splitmix64 values.
 # --------------------------------------------------------------------------
 
