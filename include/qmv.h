@@ -147,6 +147,38 @@ int32_t qmv_pack_int8(const float* w, int64_t n, int64_t k, void* packed, float*
  */
 int32_t qmv_quantize_act(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, void* stream);
 
+/*
+ * qmv_rmsnorm_quantize -- RMSNorm, then the same per-token quantisation, in one
+ * pass (llama2.c tour, "Step 1" / "Step 6": o = weight * (x / rms), rms =
+ * sqrt(mean(x^2) + eps); the normalised row never goes to memory).
+ *   x      [m][k] fp32 row-major, finite.   weight [k] fp32.   eps >= 0.
+ *   x8/sx  as qmv_quantize_act, of o.
+ * fp32 throughout, in a fixed order so results are reproducible: the sum of
+ * squares is 256 partial sums (partial t over j = t, t + 256, ... in order)
+ * added pairwise (t += t + s, s = 128 .. 1); r = 1 / sqrt(ss / k + eps) with
+ * correctly rounded division and root; o = weight * (r * x); no fused
+ * multiply-adds.  EVALUE for a negative or non-finite eps.
+ */
+int32_t qmv_rmsnorm_quantize(const float* x, const float* weight, int64_t m, int64_t k, float eps, int8_t* x8,
+                             float* sx, void* stream);
+
+/* Gate activations of qmv_glu_quantize. */
+enum {
+    QMV_ACT_GELU_TANH = 1,  /* 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))), the GeGLU gate */
+    QMV_ACT_SILU = 2        /* v / (1 + exp(-v)), the SwiGLU gate */
+};
+
+/*
+ * qmv_glu_quantize -- the gated feed-forward's middle step and the
+ * quantisation for the down projection in one pass (llama2.c tour, "Step 5":
+ * act(gate) * up; Gemma uses a GeLU gate): h = act(gate) * up per element, then
+ * per-row int8 codes and scales of h as qmv_quantize_act.
+ *   gate, up [m][n] fp32, finite.   x8 [m][n].   sx [m].
+ * fp32 with the device's exp / tanh.  EINVAL for an unknown act.
+ */
+int32_t qmv_glu_quantize(const float* gate, const float* up, int64_t m, int64_t n, int32_t act, int8_t* x8, float* sx,
+                         void* stream);
+
 /* Workspace bytes qmv_gemv / qmv_gemm_prefill need for this problem list
  * (-1 on bad input).  The workspace must be 256-byte aligned. */
 int64_t qmv_gemv_workspace_bytes(const qmv_problem* probs /* host */, int32_t count);

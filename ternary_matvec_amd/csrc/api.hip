@@ -453,6 +453,24 @@ int32_t qmv_quantize_act(const float* x, int64_t m, int64_t k, int8_t* x8, float
     return hip_status(launch_quantize_rows(x, m, k, x8, sx, as_stream(stream)));
 }
 
+int32_t qmv_rmsnorm_quantize(const float* x, const float* weight, int64_t m, int64_t k, float eps, int8_t* x8,
+                             float* sx, void* stream)
+{
+    if (!x || !weight || !x8 || !sx) return QMV_EINVAL;
+    if (m < 1 || k < 1 || k > QMV_MAX_K || m > ((int64_t)1 << 31) - 1) return QMV_ESHAPE;
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return QMV_EVALUE;
+    return hip_status(launch_rmsnorm_quantize(x, weight, m, k, eps, x8, sx, as_stream(stream)));
+}
+
+int32_t qmv_glu_quantize(const float* gate, const float* up, int64_t m, int64_t n, int32_t act, int8_t* x8, float* sx,
+                         void* stream)
+{
+    if (!gate || !up || !x8 || !sx) return QMV_EINVAL;
+    if (m < 1 || n < 1 || n > QMV_MAX_K || m > ((int64_t)1 << 31) - 1) return QMV_ESHAPE;
+    if (act != QMV_ACT_GELU_TANH && act != QMV_ACT_SILU) return QMV_EINVAL;
+    return hip_status(launch_glu_quantize(gate, up, m, n, act, x8, sx, as_stream(stream)));
+}
+
 int64_t qmv_gemv_workspace_bytes(const qmv_problem* probs, int32_t count)
 {
     if (check_problems(probs, count, QMV_MAX_GEMV_M) != QMV_OK) return -1;

@@ -86,6 +86,79 @@ __global__ __launch_bounds__(kBlock) void k_quantize_rows(const float* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Fused steps either side of a GEMV (llama2.c tour, "Step 1" / "Step 6":
+// RMSNorm; "Step 5": the gated feed-forward; cpp20gemma and gemma.cpp use a
+// GeLU gate): the normalised or gated row is quantised as above without a
+// round trip through memory.  One workgroup per row.
+// ---------------------------------------------------------------------------
+
+// o = weight * (r * x), r = 1 / sqrt(ss / k + eps).  ss is an fp32 sum in a
+// fixed order: thread t adds x[j]^2 for j = t, t + 256, ... in order, then the
+// 256 partial sums meet pairwise (t += t + s for s = 128 .. 1).  Nothing is
+// contracted into fused multiply-adds, so the values (and the codes) are
+// reproducible exactly.
+__global__ __launch_bounds__(kBlock) void k_rmsnorm_quantize(const float* __restrict__ x,
+                                                            const float* __restrict__ weight, int64_t k, float eps,
+                                                            int8_t* __restrict__ x8, float* __restrict__ sx)
+{
+#pragma clang fp contract(off)
+    __shared__ float part[kBlock];
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float* xr = x + row * k;
+    int8_t* qr = x8 + row * k;
+    const int t = threadIdx.x;
+    float a = 0.0f;
+    for (int64_t j = t; j < k; j += kBlock) a += xr[j] * xr[j];
+    part[t] = a;
+    __syncthreads();
+    for (int st = kBlock / 2; st >= 1; st >>= 1) {
+        if (t < st) part[t] += part[t + st];
+        __syncthreads();
+    }
+    // correctly rounded division and root (the library is built with them)
+    const float r = 1.0f / sqrtf(part[0] / (float)k + eps);
+    float m = 0.0f;
+    for (int64_t j = t; j < k; j += kBlock) m = fmaxf(m, fabsf(weight[j] * (r * xr[j])));
+    m = block_max(m, red);
+    const float s = scale_from_max(m);
+    if (t == 0) sx[row] = s;
+    for (int64_t j = t; j < k; j += kBlock) qr[j] = quantize_one(weight[j] * (r * xr[j]), s);
+}
+
+// h = act(gate) * up, act 1 = GeLU (tanh form), 2 = SiLU, in fp32 with the
+// device's expf / tanhf.
+__device__ __forceinline__ float glu_value(float g, float u, int act)
+{
+    float a;
+    if (act == 1) {
+        const float c = 0.7978845608028654f;   // sqrt(2 / pi)
+        a = 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+    } else {
+        a = g / (1.0f + expf(-g));
+    }
+    return a * u;
+}
+
+__global__ __launch_bounds__(kBlock) void k_glu_quantize(const float* __restrict__ gate, const float* __restrict__ up,
+                                                        int64_t n, int act, int8_t* __restrict__ x8,
+                                                        float* __restrict__ sx)
+{
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const float* gr = gate + row * n;
+    const float* ur = up + row * n;
+    int8_t* qr = x8 + row * n;
+    const int t = threadIdx.x;
+    float m = 0.0f;
+    for (int64_t j = t; j < n; j += kBlock) m = fmaxf(m, fabsf(glu_value(gr[j], ur[j], act)));
+    m = block_max(m, red);
+    const float s = scale_from_max(m);
+    if (t == 0) sx[row] = s;
+    for (int64_t j = t; j < n; j += kBlock) qr[j] = quantize_one(glu_value(gr[j], ur[j], act), s);
+}
+
+// ---------------------------------------------------------------------------
 // Packing.
 // ---------------------------------------------------------------------------
 __global__ void k_fill_pack_header(float* scale_out, float scale, int32_t* bad)
@@ -177,6 +250,20 @@ int grid_for(int64_t items)
 hipError_t launch_quantize_rows(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, hipStream_t s)
 {
     hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)m), dim3(kBlock), 0, s, x, k, x8, sx);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_quantize(const float* x, const float* weight, int64_t m, int64_t k, float eps, int8_t* x8,
+                                   float* sx, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_rmsnorm_quantize, dim3((unsigned)m), dim3(kBlock), 0, s, x, weight, k, eps, x8, sx);
+    return hipGetLastError();
+}
+
+hipError_t launch_glu_quantize(const float* gate, const float* up, int64_t m, int64_t n, int act, int8_t* x8,
+                               float* sx, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_glu_quantize, dim3((unsigned)m), dim3(kBlock), 0, s, gate, up, n, act, x8, sx);
     return hipGetLastError();
 }
 

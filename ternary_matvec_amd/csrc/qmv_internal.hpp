@@ -67,6 +67,10 @@ __device__ __forceinline__ void wait_vmcnt()
 }
 
 // Launchers implemented in the kernel translation units.
+hipError_t launch_rmsnorm_quantize(const float* x, const float* weight, int64_t m, int64_t k, float eps, int8_t* x8,
+                                   float* sx, hipStream_t s);
+hipError_t launch_glu_quantize(const float* gate, const float* up, int64_t m, int64_t n, int act, int8_t* x8,
+                               float* sx, hipStream_t s);
 hipError_t launch_fill_pack_header(float* scale_out, float scale, int32_t* bad, hipStream_t s);
 hipError_t launch_pack_ternary(const int8_t* trits, int64_t n, int64_t k, int64_t chunks, uint8_t* out,
                                int32_t* bad, hipStream_t s);

@@ -63,6 +63,8 @@ SIGNATURES = {
     "qmv_lmhead_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64,
                                    _c_ptr]),
     "qmv_read_probe": (_c_i32, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
+    "qmv_rmsnorm_quantize": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr]),
+    "qmv_glu_quantize": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_i32, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_sketch_bytes": (_c_i64, [_c_i64, _c_i64]),
     "qmv_sketch_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
     "qmv_sketch_build": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr]),
@@ -326,3 +328,42 @@ def qmv_lmhead_sketch_argmax(w_bf16, sketch, x, idx=None, max_logit=None, candid
                                            _ptr(candidates), _ptr(scores), _ptr(workspace), workspace.numel(),
                                            _stream(stream)), "qmv_lmhead_sketch_argmax")
     return idx, max_logit, candidates, scores
+
+
+QMV_ACT_GELU_TANH = 1
+QMV_ACT_SILU = 2
+
+
+def qmv_rmsnorm_quantize(x, weight, eps=1e-5, x8=None, sx=None, stream=None):
+    """RMSNorm then per-row int8 of a [m][k] fp32 tensor; returns (x8, sx)."""
+    _dev(x, torch.float32, "x")
+    _dev(weight, torch.float32, "weight")
+    x2 = x if x.dim() == 2 else x.view(1, -1)
+    m, k = x2.shape
+    if weight.numel() != k:
+        raise QmvError(-2, "qmv_rmsnorm_quantize")
+    if x8 is None:
+        x8 = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check(load().qmv_rmsnorm_quantize(_ptr(x2), _ptr(weight), m, k, ctypes.c_float(eps), _ptr(x8), _ptr(sx),
+                                       _stream(stream)), "qmv_rmsnorm_quantize")
+    return x8, sx
+
+
+def qmv_glu_quantize(gate, up, act=QMV_ACT_GELU_TANH, x8=None, sx=None, stream=None):
+    """act(gate) * up then per-row int8 of [m][n] fp32 tensors; returns (x8, sx)."""
+    _dev(gate, torch.float32, "gate")
+    _dev(up, torch.float32, "up")
+    g2 = gate if gate.dim() == 2 else gate.view(1, -1)
+    u2 = up if up.dim() == 2 else up.view(1, -1)
+    if g2.shape != u2.shape:
+        raise QmvError(-2, "qmv_glu_quantize")
+    m, n = g2.shape
+    if x8 is None:
+        x8 = torch.empty((m, n), dtype=torch.int8, device=gate.device)
+    if sx is None:
+        sx = torch.empty(m, dtype=torch.float32, device=gate.device)
+    _check(load().qmv_glu_quantize(_ptr(g2), _ptr(u2), m, n, int(act), _ptr(x8), _ptr(sx), _stream(stream)),
+           "qmv_glu_quantize")
+    return x8, sx

@@ -81,6 +81,26 @@ def test_host_validation_errors(lib):
     assert lib.qmv_lmhead_argmax(_fake(4096), _fake(64), 10, 8, None, None, None, _fake(256), 4096, s) == qmv.QMV_EINVAL
     assert lib.qmv_lmhead_argmax(_fake(4096), _fake(64), 10, 8, _fake(64), None, None, None, 0, s) == qmv.QMV_EWORKSPACE
     assert qmv.qmv_lmhead_workspace_bytes(262144, 1152) > 0
+    # fused RMSNorm / gate quantisation
+    assert lib.qmv_rmsnorm_quantize(_fake(64), None, 1, 4, 1e-5, _fake(4096), _fake(8192), s) == qmv.QMV_EINVAL
+    assert lib.qmv_rmsnorm_quantize(_fake(64), _fake(64), 1, 0, 1e-5, _fake(4096), _fake(8192), s) == qmv.QMV_ESHAPE
+    assert lib.qmv_rmsnorm_quantize(_fake(64), _fake(64), 1, 4, -1.0, _fake(4096), _fake(8192), s) == qmv.QMV_EVALUE
+    assert lib.qmv_rmsnorm_quantize(_fake(64), _fake(64), 1, 4, float("nan"), _fake(4096), _fake(8192), s) == \
+        qmv.QMV_EVALUE
+    assert lib.qmv_glu_quantize(_fake(64), _fake(64), 1, 4, 3, _fake(4096), _fake(8192), s) == qmv.QMV_EINVAL
+    assert lib.qmv_glu_quantize(_fake(64), None, 1, 4, 1, _fake(4096), _fake(8192), s) == qmv.QMV_EINVAL
+    assert lib.qmv_glu_quantize(_fake(64), _fake(64), 0, 4, 1, _fake(4096), _fake(8192), s) == qmv.QMV_ESHAPE
+    # sketch head: shape limits, alignment, workspace
+    assert qmv.qmv_sketch_bytes(262144, 1152) > 0 and qmv.qmv_sketch_workspace_bytes(262144, 1152) > 0
+    for v, k in [(0, 64), (10, 7), (10, 12), (10, 8200), (10, 0)]:
+        assert qmv.qmv_sketch_bytes(v, k) == -1
+    assert lib.qmv_sketch_build(_fake(4096), 10, 64, _fake(4097), 1 << 20, s) == qmv.QMV_EINVAL
+    assert lib.qmv_sketch_build(_fake(4096), 10, 60, _fake(4096), 1 << 20, s) == qmv.QMV_ESHAPE
+    assert lib.qmv_sketch_build(_fake(4096), 10, 64, _fake(4096), 16, s) == qmv.QMV_EWORKSPACE
+    assert lib.qmv_lmhead_sketch_argmax(_fake(4096), _fake(4096), _fake(64), 10, 64, None, None, None, None,
+                                        _fake(4096), 1 << 20, s) == qmv.QMV_EINVAL
+    assert lib.qmv_lmhead_sketch_argmax(_fake(4096), _fake(4096), _fake(64), 10, 64, _fake(64), None, None, None,
+                                        _fake(4096), 16, s) == qmv.QMV_EWORKSPACE
 
 
 def _problem(wtype=qmv.QMV_W_TERNARY5, n=64, k=80, m=1, data=4096):
