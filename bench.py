@@ -586,6 +586,106 @@ def bench_sketch(dev, stream, reps=50, copies=6, tokens=32):
             "agrees_with_exact_argmax": {k_: "%d/%d" % (a, tokens) for k_, a in agree.items()}}
 
 
+def bench_ffn_chain(stack, dev, stream, tokens=50):
+    """The feed-forward half of every layer as a dependent chain per token:
+    RMSNorm -> int8 (qmv_rmsnorm_quantize), gate and up (one grouped qmv_gemv),
+    GeLU(gate) * up -> int8 (qmv_glu_quantize), down (qmv_gemv): 4 launches a
+    layer, 104 a token, on copy 0 of the decode stack's Gemma weights.  Also the
+    fused steps alone."""
+    import ctypes
+    import torch
+    from ternary_matvec_amd import qmv, synth
+    mats = [name for (name, _, _) in stack.mats]
+    gi, ui, di = mats.index("gate"), mats.index("up"), mats.index("down")
+    nm = len(mats)
+    hidden = stack.mats[gi][2]
+    inter = stack.mats[gi][1]
+    h = torch.from_numpy(synth.normal(synth.stream_seed(7, 0, 0, synth.TAG_ACT), (1, hidden))).to(dev)
+    gamma = torch.from_numpy(synth.normal(synth.stream_seed(7, 1, 0, synth.TAG_ACT), (hidden,)) * 0.1 + 1.0).to(dev)
+    x8a = torch.empty((1, hidden), dtype=torch.int8, device=dev)
+    sxa = torch.empty(1, dtype=torch.float32, device=dev)
+    yg = torch.empty((1, inter), dtype=torch.float32, device=dev)
+    yu = torch.empty((1, inter), dtype=torch.float32, device=dev)
+    x8b = torch.empty((1, inter), dtype=torch.int8, device=dev)
+    sxb = torch.empty(1, dtype=torch.float32, device=dev)
+    yd = torch.empty((1, hidden), dtype=torch.float32, device=dev)
+
+    def prob(i, x8, sx, y):
+        p = qmv.qmv_problem()
+        p.w = stack.arrays[0][i].w
+        p.x8, p.sx, p.m, p.y, p.acc = x8.data_ptr(), sx.data_ptr(), 1, y.data_ptr(), None
+        return p
+
+    layers = []
+    for layer in range(stack.layers):
+        gu = (qmv.qmv_problem * 2)(prob(layer * nm + gi, x8a, sxa, yg), prob(layer * nm + ui, x8a, sxa, yu))
+        dn = (qmv.qmv_problem * 1)(prob(layer * nm + di, x8b, sxb, yd))
+        layers.append((gu, qmv.qmv_gemv(gu, stream=stream), dn, qmv.qmv_gemv(dn, stream=stream)))
+    torch.cuda.synchronize()
+
+    def token():
+        for gu, wgu, dn, wdn in layers:
+            qmv.qmv_rmsnorm_quantize(h, gamma, 1e-6, x8=x8a, sx=sxa, stream=stream)
+            qmv.qmv_gemv(gu, workspace=wgu, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+            qmv.qmv_glu_quantize(yg, yu, qmv.QMV_ACT_GELU_TANH, x8=x8b, sx=sxb, stream=stream)
+            qmv.qmv_gemv(dn, workspace=wdn, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(reps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps * 1e3
+
+    us = timed(token, tokens)
+    # the same 104 launches captured once in a HIP graph and replayed
+    torch.cuda.synchronize()
+    yd_eager = None
+    token()
+    torch.cuda.synchronize()
+    yd_eager = yd.clone()
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            for gu, wgu, dn, wdn in layers:
+                qmv.qmv_rmsnorm_quantize(h, gamma, 1e-6, x8=x8a, sx=sxa, stream=cap)
+                qmv.qmv_gemv(gu, workspace=wgu, flags=qmv.QMV_F_TABLE_READY, stream=cap)
+                qmv.qmv_glu_quantize(yg, yu, qmv.QMV_ACT_GELU_TANH, x8=x8b, sx=sxb, stream=cap)
+                qmv.qmv_gemv(dn, workspace=wdn, flags=qmv.QMV_F_TABLE_READY, stream=cap)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    replays_match = True
+    for _ in range(3):
+        yd.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        replays_match = replays_match and bool(torch.equal(yd, yd_eager))
+    us_graph = timed(graph.replay, tokens)
+    wbytes = stack.layers * sum(n * ((k + 4) // 5) for (name, n, k) in stack.mats if name in ("gate", "up", "down"))
+    x512 = torch.from_numpy(synth.normal(synth.stream_seed(7, 2, 0, synth.TAG_ACT), (512, hidden))).to(dev)
+    g512 = torch.from_numpy(synth.normal(synth.stream_seed(7, 3, 0, synth.TAG_ACT), (512, inter))).to(dev)
+    u512 = torch.from_numpy(synth.normal(synth.stream_seed(7, 4, 0, synth.TAG_ACT), (512, inter))).to(dev)
+    r1 = timed(lambda: qmv.qmv_rmsnorm_quantize(h, gamma, 1e-6, x8=x8a, sx=sxa, stream=stream), 200)
+    r512 = timed(lambda: qmv.qmv_rmsnorm_quantize(x512, gamma, 1e-6, stream=stream), 50)
+    g1 = timed(lambda: qmv.qmv_glu_quantize(yg, yu, qmv.QMV_ACT_GELU_TANH, x8=x8b, sx=sxb, stream=stream), 200)
+    g5 = timed(lambda: qmv.qmv_glu_quantize(g512, u512, qmv.QMV_ACT_GELU_TANH, stream=stream), 50)
+    return {"workload": "Gemma-3-1B FFN half x26 layers, batch 1, dependent: rmsnorm->int8, gate+up GEMV, "
+                        "GeLU(gate)*up->int8, down GEMV (104 launches a token)",
+            "us_per_token": round(us, 1), "us_per_token_graph_replay": round(us_graph, 1),
+            "graph_replays_match_eager": replays_match,
+            "weight_bytes": wbytes, "GB/s": round(wbytes / us / 1e3, 1),
+            "rmsnorm_quantize_us": {"1x%d" % hidden: round(r1, 2), "512x%d" % hidden: round(r512, 2)},
+            "glu_quantize_us": {"1x%d" % inter: round(g1, 2), "512x%d" % inter: round(g5, 2)}}
+
+
 def bench_int8(dev, stream, reps=2000):
     import torch
     from ternary_matvec_amd import qmv, synth
@@ -730,6 +830,8 @@ def main():
             extras["decode_copies_sweep"] = copies_sweep(stack, max(20, args.steps // 2), stream)
             extras["decode_chained"] = chained(stack, max(5, args.steps // 20), stream)
             extras["quantize_step"] = time_quantize(stack, max(20, args.steps // 2), stream)
+            log("FFN chain")
+            extras["ffn_chain"] = bench_ffn_chain(stack, dev, stream)
             log("output layer")
             extras["lmhead"] = bench_head(dev, stream)
             torch.cuda.empty_cache()

@@ -140,22 +140,59 @@ __device__ __forceinline__ float glu_value(float g, float u, int act)
     return a * u;
 }
 
-__global__ __launch_bounds__(kBlock) void k_glu_quantize(const float* __restrict__ gate, const float* __restrict__ up,
-                                                        int64_t n, int act, int8_t* __restrict__ x8,
-                                                        float* __restrict__ sx)
+constexpr int kGluThreads = 1024;
+constexpr int kGluCache = 8;   // values a thread keeps between the two passes (n <= 8192)
+
+// Max over a 1024-thread block; every thread receives the result.
+__device__ __forceinline__ float block_max_1024(float v, float* red)
 {
-    __shared__ float red[4];
+    v = wave_max(v);
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < kGluThreads / kWave; ++i) r = fmaxf(r, red[i]);
+    __syncthreads();
+    return r;
+}
+
+// One workgroup of 1024 threads per row; up to 8192 columns the gated values
+// are computed once and kept in registers for the quantise pass.
+__global__ __launch_bounds__(kGluThreads) void k_glu_quantize(const float* __restrict__ gate,
+                                                             const float* __restrict__ up, int64_t n, int act,
+                                                             int8_t* __restrict__ x8, float* __restrict__ sx)
+{
+    __shared__ float red[kGluThreads / kWave];
     const int64_t row = blockIdx.x;
     const float* gr = gate + row * n;
     const float* ur = up + row * n;
     int8_t* qr = x8 + row * n;
     const int t = threadIdx.x;
     float m = 0.0f;
-    for (int64_t j = t; j < n; j += kBlock) m = fmaxf(m, fabsf(glu_value(gr[j], ur[j], act)));
-    m = block_max(m, red);
-    const float s = scale_from_max(m);
-    if (t == 0) sx[row] = s;
-    for (int64_t j = t; j < n; j += kBlock) qr[j] = quantize_one(glu_value(gr[j], ur[j], act), s);
+    if (n <= (int64_t)kGluThreads * kGluCache) {
+        float h[kGluCache];
+#pragma unroll
+        for (int i = 0; i < kGluCache; ++i) {
+            const int64_t j = t + (int64_t)kGluThreads * i;
+            h[i] = j < n ? glu_value(gr[j], ur[j], act) : 0.0f;
+            m = fmaxf(m, fabsf(h[i]));
+        }
+        m = block_max_1024(m, red);
+        const float s = scale_from_max(m);
+        if (t == 0) sx[row] = s;
+#pragma unroll
+        for (int i = 0; i < kGluCache; ++i) {
+            const int64_t j = t + (int64_t)kGluThreads * i;
+            if (j < n) qr[j] = quantize_one(h[i], s);
+        }
+    } else {
+        for (int64_t j = t; j < n; j += kGluThreads) m = fmaxf(m, fabsf(glu_value(gr[j], ur[j], act)));
+        m = block_max_1024(m, red);
+        const float s = scale_from_max(m);
+        if (t == 0) sx[row] = s;
+        for (int64_t j = t; j < n; j += kGluThreads) qr[j] = quantize_one(glu_value(gr[j], ur[j], act), s);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -263,7 +300,7 @@ hipError_t launch_rmsnorm_quantize(const float* x, const float* weight, int64_t 
 hipError_t launch_glu_quantize(const float* gate, const float* up, int64_t m, int64_t n, int act, int8_t* x8,
                                float* sx, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_glu_quantize, dim3((unsigned)m), dim3(kBlock), 0, s, gate, up, n, act, x8, sx);
+    hipLaunchKernelGGL(k_glu_quantize, dim3((unsigned)m), dim3(kGluThreads), 0, s, gate, up, n, act, x8, sx);
     return hipGetLastError();
 }
 
