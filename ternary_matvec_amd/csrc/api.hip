@@ -8,6 +8,7 @@
 #include <cstring>
 #include <memory>
 #include <mutex>
+#include <queue>
 #include <vector>
 
 #include "qmv_internal.hpp"
@@ -67,7 +68,7 @@ int32_t check_problems(const qmv_problem* probs, int32_t count, int64_t max_m)
 // streaming kernel ([nb + 1 offsets][workgroup tile entries]).  Problems are
 // grouped by weight type in the table.
 //
-// Streaming schedule: every problem gets L lanes per row (1, 2 or 4), so a
+// Streaming schedule: every problem gets L lanes per row (1, 2, 4 or 8), so a
 // workgroup tile is 4 * 64 / L rows.  Several L assignments are tried (each the
 // smallest L that brings a problem under a target number of chunk steps); each
 // is scheduled longest-processing-time-first onto the nb workgroups and the
@@ -132,7 +133,7 @@ bool schedule_stream(const std::vector<const qmv_problem*>& sp, const std::vecto
         for (size_t i = 0; i < sp.size(); ++i) {
             const int c = chunks_of(*sp[i]);
             int L = 1;
-            while (L < 4 && gemv_stream_steps(c, L) > target) L *= 2;
+            while (L < kStreamMaxLanes && gemv_stream_steps(c, L) > target) L *= 2;
             lanes[i] = L;
         }
         if (std::find(tried.begin(), tried.end(), lanes) != tried.end()) continue;
@@ -166,20 +167,10 @@ bool schedule_stream(const std::vector<const qmv_problem*>& sp, const std::vecto
         }
         std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
         const int nb = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * wg_per_cu, (int64_t)items.size()));
-        // Tiles after each workgroup's first are taken dynamically, so the
-        // finish is about the mean load plus one of the last (smallest) tiles.
-        double total = 0;
-        for (const Item& it : items) total += it.cost;
-        const double makespan = total / nb + items.back().cost;
-        if (found && makespan >= best.makespan) continue;
-        found = true;
-        best.lanes = lanes;
-        best.nb = nb;
-        best.slot_bytes = slot;
-        best.makespan = makespan;
         // The kernel deals tiles per XCD: the same items, longest first, onto
         // the 8 XCD lists (each list stays longest first).
         std::vector<std::vector<uint32_t>> xl(kStreamXcds);
+        std::vector<std::vector<double>> xc(kStreamXcds);
         std::vector<double> load(kStreamXcds, 0.0);
         std::vector<int> wgs(kStreamXcds);
         for (int x = 0; x < kStreamXcds; ++x) wgs[x] = (nb - x + kStreamXcds - 1) / kStreamXcds;
@@ -188,21 +179,46 @@ bool schedule_stream(const std::vector<const qmv_problem*>& sp, const std::vecto
             for (int x = 0; x < kStreamXcds; ++x)   // least loaded per workgroup
                 if (wgs[x] > 0 && (bx < 0 || load[x] / wgs[x] < load[bx] / wgs[bx])) bx = x;
             xl[bx].push_back(it.entry);
+            xc[bx].push_back(it.cost);
             load[bx] += it.cost;
         }
+        // Workgroup r of an XCD's w starts with list entries r and 2w - 1 - r
+        // (the longest tiles pair with the shortest of the second w), then takes
+        // the entries from 2w on by ticket, whenever it is free.  The modelled
+        // makespan replays that on each list.
+        double makespan = 0;
+        for (int x = 0; x < kStreamXcds; ++x) {
+            const size_t w = (size_t)wgs[x], sz = xc[x].size();
+            std::priority_queue<double, std::vector<double>, std::greater<double>> busy;
+            for (size_t r = 0; r < w; ++r)
+                busy.push((r < sz ? xc[x][r] : 0.0) + (2 * w - 1 - r < sz ? xc[x][2 * w - 1 - r] : 0.0));
+            for (size_t i = 2 * w; i < sz; ++i) {
+                const double t = busy.top();
+                busy.pop();
+                busy.push(t + xc[x][i]);
+            }
+            while (busy.size() > 1) busy.pop();
+            if (!busy.empty()) makespan = std::max(makespan, busy.top());
+        }
+        if (found && makespan >= best.makespan) continue;
+        found = true;
+        best.lanes = lanes;
+        best.nb = nb;
+        best.slot_bytes = slot;
+        best.makespan = makespan;
         // [counters][first two entries of each workgroup][list offsets and
         // sizes][lists]; workgroup b runs on XCD b % 8, as the XCD's workgroup
-        // r = b / 8 of w: its tiles are entries w + r and r (the shorter first:
-        // the lists are longest first, and the longer one is then staged while
-        // the shorter one streams), then the entries from 2w on as its tickets
-        // name them
+        // r = b / 8 of w: its tiles are entries 2w - 1 - r and r (the shorter
+        // first: the lists are longest first, and the longer one is then staged
+        // while the shorter one streams), then the entries from 2w on as its
+        // tickets name them
         best.words.assign(kStreamHdr + 2 * nb + 2 * kStreamXcds, 0u);
         for (int b = 0; b < nb; ++b) {
             const int x = b % kStreamXcds;
             const auto& l = xl[x];
             const size_t r = (size_t)(b / kStreamXcds), w = (size_t)wgs[x];
             const uint32_t e0 = r < l.size() ? l[r] : 0xffffffffu;
-            const uint32_t e1 = w + r < l.size() ? l[w + r] : 0xffffffffu;
+            const uint32_t e1 = 2 * w - 1 - r < l.size() ? l[2 * w - 1 - r] : 0xffffffffu;
             best.words[kStreamHdr + 2 * b] = e1 != 0xffffffffu ? e1 : e0;
             best.words[kStreamHdr + 2 * b + 1] = e1 != 0xffffffffu ? e0 : e1;
         }

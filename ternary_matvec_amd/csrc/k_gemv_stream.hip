@@ -6,7 +6,7 @@
 // README, "Architecture & implementation"), organised for streaming:
 //
 //  * Work unit = a workgroup tile: 4 * 2R rows of one problem, one 2R-row wave
-//    tile per compute wave.  R = 64 / L, L = lanes per row (1, 2 or 4, chosen
+//    tile per compute wave.  R = 64 / L, L = lanes per row (1, 2, 4 or 8, chosen
 //    by the host so tiles are of similar length).  Lane s*R + r of a wave
 //    streams chunks s, s + L, s + 2L, ... of rows r and R + r (the two rows
 //    share every activation read); for a fixed s the R rows' chunk is one
@@ -113,6 +113,19 @@ __device__ __forceinline__ void z_group(const uint32_t nat[5], uint32_t out[10],
     }
 }
 
+// One ticket from an XCD's counter (one lane).  The address is hidden from the
+// compiler's uniformity analysis: otherwise it turns the atomic into a wave-wide
+// one whose result is shared out at once, which waits for the atomic (a
+// contended counter takes microseconds) right there instead of where the
+// ticket is first used, one tile later.
+__device__ __forceinline__ uint32_t take_ticket(uint32_t* counter)
+{
+    uintptr_t a = reinterpret_cast<uintptr_t>(counter);
+    asm volatile("" : "+v"(a));
+    return __hip_atomic_fetch_add(gstore_ptr(reinterpret_cast<uint32_t*>(a)), 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // What a wave needs to know about one workgroup tile.
 struct Tile {
     const DevProblem* P;
@@ -166,7 +179,7 @@ __device__ __forceinline__ Tile tile_at(const DevProblem* probs, uint32_t te, in
     T.k = T.P->k;
     T.m = T.P->m;
     T.C = T.P->chunks;
-    T.lshift = T.P->lanes_per_row == 1 ? 0 : T.P->lanes_per_row == 2 ? 1 : 2;
+    T.lshift = 31 - __builtin_clz((uint32_t)T.P->lanes_per_row);   // lanes per row: 1, 2, 4 or 8
     tile_derive<CB>(T, wave, lane);
     return T;
 }
@@ -297,6 +310,12 @@ template <int MT, int WT, class F>
 __device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, int* corr, F after_loads)
 {
     constexpr int kD = WT == 1 ? 5 : 1;
+    // units per lane loaded before any is used: a ternary row of up to
+    // 64 * 2 * 20 = 2560 columns costs one memory round trip.  Larger batches
+    // would cover longer rows in one trip but raise the kernel's register
+    // count past what four resident workgroups per compute unit allow.
+    constexpr int kBatch = 2;
+    bool first = true;
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
         if (mi > 0 && mi >= T.m) continue;
@@ -304,27 +323,31 @@ __device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, in
         const int units = 4 * T.C;
         uint32_t sh;
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(T, mi, sh);
-        // every lane's first unit, loaded unconditionally (reads past the row
-        // return zeros)
-        uint32_t raw0[kD + 1];
-        unit_load<WT>(rs, lane, raw0);
-        if (mi == 0) after_loads();
         int s_z = 0, s_x = 0;
-        for (int g = lane; g < units; g += kWave) {
-            uint32_t raw[kD + 1];
-            if (g == lane) {
+        for (int g0 = 0; g0 < units; g0 += kWave * kBatch) {
+            uint32_t raw[kBatch][kD + 1];
+            // the batch's loads, wave-uniform conditions (reads past the row
+            // return zeros)
 #pragma unroll
-                for (int j = 0; j <= kD; ++j) raw[j] = raw0[j];
-            } else {
-                unit_load<WT>(rs, g, raw);
+            for (int b = 0; b < kBatch; ++b)
+                if (b == 0 || g0 + kWave * b < units) unit_load<WT>(rs, g0 + kWave * b + lane, raw[b]);
+            if (first) {
+                after_loads();
+                first = false;
             }
-            if (WT == 1) {
-                uint32_t nat[5], zz[10];
-                unit_of<1>(T, sh, g, raw, nat);
-                z_group(nat, zz, s_z, s_x);
-                put_z(zo, g, zz);
-            } else {
-                unit_of<2>(T, sh, g, raw, &zo[g]);
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int g = g0 + kWave * b + lane;
+                if (g < units) {
+                    if (WT == 1) {
+                        uint32_t nat[5], zz[10];
+                        unit_of<1>(T, sh, g, raw[b], nat);
+                        z_group(nat, zz, s_z, s_x);
+                        put_z(zo, g, zz);
+                    } else {
+                        unit_of<2>(T, sh, g, raw[b], &zo[g]);
+                    }
+                }
             }
         }
         if (WT == 1) {
@@ -377,8 +400,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
             T1 = tile_at<kCB>(probs, te1, 0, lane);
             d1 = desc_of(T1, te1);
         }
-        uint32_t list_size = 0;
-        const uint32_t* list = nullptr;
+        // the XCD's list, read now: these loads return with tile 0's, not behind
+        // the chip's first weight loads
+        const uint32_t list_off = cload_ptr(hdr)[2 * xcd];
+        const uint32_t list_size = cload_ptr(hdr)[2 * xcd + 1];
+        const uint32_t* const list = hdr + 2 * kStreamXcds + list_off;
         bool first = true;
         for (int par = 0; te != kEnd; par ^= 1) {
             stage<MT, WT>(T, lane, smem + (size_t)par * slot_bytes, corr_base + par * MT, [&] {
@@ -394,15 +420,10 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
                     __builtin_amdgcn_s_barrier();
                     if (lane == 0) {
                         descs[0] = d0;
-                        if (te1 != kEnd) ticket = atomicAdd(&sched[64 * xcd], 1u);
+                        if (te1 != kEnd) ticket = take_ticket(&sched[64 * xcd]);
                     }
                 }
             });
-            if (list == nullptr) {
-                const uint32_t list_off = cload_ptr(hdr)[2 * xcd];
-                list_size = cload_ptr(hdr)[2 * xcd + 1];
-                list = hdr + 2 * kStreamXcds + list_off;
-            }
             uint32_t nx = kEnd;
             if (first) {
                 nx = te1;
@@ -411,7 +432,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
                 if (lane == 0) {
                     const uint32_t i = 2 * wgs + ticket;
                     nx = i < list_size ? list[i] : kEnd;
-                    if (nx != kEnd) ticket = atomicAdd(&sched[64 * xcd], 1u);
+                    if (nx != kEnd) ticket = take_ticket(&sched[64 * xcd]);
                 }
                 nx = __builtin_amdgcn_readfirstlane(nx);
             }

@@ -27,7 +27,7 @@ struct DevProblem {
     int32_t chunks;      // 16-byte chunks per row (row stride / 16)
     int32_t tile_begin;  // first tile of this problem in the launch
     int32_t wtype;       // 1 = five trits per byte, 2 = int8
-    int32_t lanes_per_row;  // streaming kernel: lanes sharing one row (1, 2 or 4)
+    int32_t lanes_per_row;  // streaming kernel: lanes sharing one row (1, 2, 4 or 8)
     int32_t reserved;
 };
 static_assert(sizeof(DevProblem) == 80, "DevProblem layout");
@@ -94,6 +94,10 @@ constexpr int kStreamXcds = 8;
 #endif
 constexpr int kStreamRowsPerLane = QMV_STREAM_RPL;   // a workgroup tile is 4 * 64 / lanes_per_row * this rows
 constexpr int kStreamHdr = 64 * 2 * kStreamXcds;
+// At most 8 lanes per row: the smallest workgroup tile, 4 * 64 / 8 * 2 rows,
+// is no smaller than a 64-row tile, so entries and table bounds stay as sized.
+constexpr int kStreamMaxLanes = 8;
+static_assert(4 * 64 / kStreamMaxLanes * kStreamRowsPerLane >= kRowsPerTile, "stream tile rows");
 int64_t gemv_stream_steps(int chunks, int lanes);
 int64_t gemv_stream_slot_bytes(int wtype, int mt, int chunks, int lanes);
 size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes);
