@@ -48,6 +48,8 @@ def _load():
         lib.oracle_sketch_pick.restype = _i64
         lib.oracle_rmsnorm_quantize.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_float, _ptr, _ptr, _ptr]
         lib.oracle_glu.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_int, _ptr]
+        lib.oracle_quantize_groups.argtypes = [_ptr, _i64, _i64, _i64, _ptr, _ptr]
+        lib.oracle_gemv_grouped.argtypes = [_ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _ptr, _ptr, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -251,7 +253,40 @@ def glu(gate, up, act):
     return h
 
 
-__all__ = ["rmsnorm_quantize", "glu", "GLU_GELU_TANH", "GLU_SILU",
+WEIGHT_GROUP = 128
+ACT_GROUP = 32
+
+
+def quantize_groups(x, group):
+    """Group-wise int8 quantisation of the rows of a 2-D fp32 array:
+    (int8 [m][k], fp32 [m][ceil(k/group)])."""
+    x, px = _c(np.atleast_2d(x), np.float32)
+    m, k = x.shape
+    q = np.empty((m, k), np.int8)
+    s = np.empty((m, (k + group - 1) // group), np.float32)
+    _load().oracle_quantize_groups(px, m, k, int(group), q.ctypes.data, s.ctypes.data)
+    return q, s
+
+
+def gemv_grouped(w8, sw, x8, sx, threads: int = 0):
+    """y (fp64 [m][n]) with weight scales per 128 and activation scales per 32
+    columns, and sum_h |term| per output (the fp32 summation error scale)."""
+    w8, pw = _c(w8, np.int8)
+    x8, px = _c(np.atleast_2d(x8), np.int8)
+    n, k = w8.shape
+    m = x8.shape[0]
+    assert x8.shape[1] == k
+    sw, psw = _c(sw, np.float32)
+    sx, psx = _c(np.atleast_2d(sx), np.float32)
+    assert sw.shape == (n, (k + 127) // 128) and sx.shape == (m, (k + 31) // 32)
+    y = np.empty((m, n), np.float64)
+    b = np.empty((m, n), np.float64)
+    _load().oracle_gemv_grouped(pw, psw, px, psx, m, n, k, y.ctypes.data, b.ctypes.data,
+                                threads or max_threads())
+    return y, b
+
+
+__all__ = ["quantize_groups", "gemv_grouped", "WEIGHT_GROUP", "ACT_GROUP", "rmsnorm_quantize", "glu", "GLU_GELU_TANH", "GLU_SILU",
            "max_threads", "quantize_rows", "quantize_tensor", "trit5_row_bytes", "trit5_row_stride",
            "int8_row_stride", "pack_trit5", "unpack_trit5", "layout_int8", "matmul_int", "dequant",
            "lmhead", "sketch_signs", "sketch_scale", "sketch_plan", "sketch_scores", "sketch_pick", "sketch_head"]

@@ -18,6 +18,7 @@
  *   [L]  "llama2.c -- Llama-2 Inference in One C File"
  *        (sections "matmul -- the one function that eats all the FLOPs",
  *         "Sampling -- turning logits into a token", "Key ideas & tradeoffs")
+ *   [G]  the gemma.cpp tour (section "Weights, Blobs, and the .sbs Format")
  *
  * Arithmetic rules: fp32 where the pages fix fp32 (the quantisation scale and
  * the quantised value), otherwise exact integers (int64) or fp64.  Build with
@@ -517,6 +518,64 @@ void oracle_glu(const float* gate, const float* up, int64_t m, int64_t n, int ac
         double a = act == 1 ? 0.5 * g * (1.0 + tanh(c * (g + 0.044715 * g * g * g))) : g / (1.0 + exp(-g));
         h[i] = a * (double)up[i];
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* O9 -- group-wise scales.                                                 */
+/*                                                                          */
+/* [G] "Weights, Blobs, and the .sbs Format": int8 weights stored in groups */
+/* of 128 values that share one scale.  [T] "A side finding: Gemma 4 E4B in */
+/* 4-bit": one activation scale per 32 values instead of one per token.     */
+/* Readings: a group is that many consecutive columns of one row (the last  */
+/* group of a row may be shorter; groups never span rows); each group is    */
+/* quantised by O1's rule (absmax scale with the 1e-9 floor, one fp32       */
+/* division, half-to-even, clip).  Activation group h (columns 32h..32h+31) */
+/* lies inside weight group h/4, so each activation group's dot product is  */
+/* exact in integers and its two scales are applied after that exact sum:   */
+/*     y[m][n] = sum_h  sw[n][h/4] * sx[m][h] * D_h,                        */
+/*     D_h = sum over the group's columns of x8 * w8,                       */
+/* summed in fp64 (`bound` gets sum_h |term|, the scale of fp32 summation   */
+/* error).                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* Quantise every row of x [m][k] in groups of `group` columns: q [m][k],
+ * s [m][ceil(k/group)]. */
+void oracle_quantize_groups(const float* x, int64_t m, int64_t k, int64_t group, int8_t* q, float* s)
+{
+    const int64_t ng = (k + group - 1) / group;
+    for (int64_t r = 0; r < m; ++r)
+        for (int64_t g = 0; g < ng; ++g) {
+            const int64_t c0 = g * group, c1 = c0 + group < k ? c0 + group : k;
+            const float sg = oracle_scale_of(x + r * k + c0, c1 - c0);
+            s[r * ng + g] = sg;
+            for (int64_t c = c0; c < c1; ++c) q[r * k + c] = oracle_quantize_one(x[r * k + c], sg);
+        }
+}
+
+/* y and bound are [m][n] fp64; w8 [n][k] with sw [n][ceil(k/128)]; x8 [m][k]
+ * with sx [m][ceil(k/32)]. */
+void oracle_gemv_grouped(const int8_t* w8, const float* sw, const int8_t* x8, const float* sx, int64_t m,
+                         int64_t n, int64_t k, double* y, double* bound, int threads)
+{
+    const int64_t gw = (k + 127) / 128, gx = (k + 31) / 32;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+#endif
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t mi = 0; mi < m; ++mi) {
+            double sum = 0.0, abs_sum = 0.0;
+            for (int64_t h = 0; h < gx; ++h) {
+                int64_t d = 0;
+                const int64_t c1 = 32 * h + 32 < k ? 32 * h + 32 : k;
+                for (int64_t c = 32 * h; c < c1; ++c) d += (int64_t)x8[mi * k + c] * (int64_t)w8[r * k + c];
+                const double t = (double)sw[r * gw + h / 4] * (double)sx[mi * gx + h] * (double)d;
+                sum += t;
+                abs_sum += fabs(t);
+            }
+            y[mi * n + r] = sum;
+            bound[mi * n + r] = abs_sum;
+        }
+    (void)threads;
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */

@@ -500,3 +500,107 @@ def test_bf16_rounding_is_nearest_even():
     x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -9, -2.0], np.float32)
     b = synth.to_bf16_bits(x)
     np.testing.assert_array_equal(b, [0x3F80, 0x3F80, 0x3F82, 0x3F80, 0xC000])
+
+
+# --------------------------------------------------------------------------
+# O9 group-wise scales (the gemma.cpp tour, "Weights, Blobs, and the .sbs
+# Format": int8 groups of 128 sharing a scale; [T] "A side finding: Gemma 4
+# E4B in 4-bit": one activation scale per 32 values).
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", [1, 31, 32, 33, 128, 300, 1152])
+def test_groups_of_a_whole_row_are_per_row_quantisation(k):
+    x = synth.normal(91 + k, (3, k))
+    q1, s1 = oracle.quantize_rows(x)
+    for g in (k, k + 1, 4 * k):
+        q, s = oracle.quantize_groups(x, g)
+        assert s.shape == (3, 1)
+        np.testing.assert_array_equal(q, q1)
+        np.testing.assert_array_equal(s[:, 0].view(np.uint32), s1.view(np.uint32))
+
+
+def test_groups_closed_form_and_ragged_tail():
+    # k = 70 in groups of 32: [0, 32), [32, 64), [64, 70)
+    x = np.zeros((1, 70), np.float32)
+    x[0, 0], x[0, 1], x[0, 2] = 2.0, -2.0, 1.0          # group 0: absmax 2 -> codes 127, -127, 64 (63.5 -> 64)
+    x[0, 40] = -0.5                                      # group 1: absmax 0.5 -> -127
+    x[0, 69] = 3.0                                       # tail group of 6 columns
+    q, s = oracle.quantize_groups(x, 32)
+    assert s.shape == (1, 3)
+    assert s[0].tolist() == [np.float32(2.0) / np.float32(127.0), np.float32(0.5) / np.float32(127.0),
+                             np.float32(3.0) / np.float32(127.0)]
+    assert (q[0, :3] == [127, -127, 64]).all() and (q[0, 3:32] == 0).all()
+    assert q[0, 40] == -127 and q[0, 69] == 127
+    # an all-zero group takes the floor scale and zero codes
+    q0, s0 = oracle.quantize_groups(np.zeros((2, 64), np.float32), 32)
+    assert (q0 == 0).all() and (s0 == np.float32(1e-9) / np.float32(127.0)).all()
+
+
+def test_groups_are_independent_of_each_other_and_of_other_rows():
+    x = synth.normal(93, (2, 300))
+    q, s = oracle.quantize_groups(x, 128)
+    y = x.copy()
+    y[0, 130] = 1000.0            # only row 0, group 1 may change
+    q2, s2 = oracle.quantize_groups(y, 128)
+    changed = (q2 != q)
+    assert not changed[1].any() and not changed[0, :128].any() and not changed[0, 256:].any()
+    assert changed[0, 128:256].any()
+    assert (s2 != s).sum() == 1 and s2[0, 1] != s[0, 1]
+    # each group's codes equal per-row quantisation of that group alone
+    for g, (c0, c1) in enumerate([(0, 128), (128, 256), (256, 300)]):
+        qg, sg = oracle.quantize_rows(x[:, c0:c1])
+        np.testing.assert_array_equal(q[:, c0:c1], qg)
+        np.testing.assert_array_equal(s[:, g], sg)
+
+
+def _equal_absmax(seed, shape, group, amax):
+    """Values in [-amax/2, amax/2] with +-amax planted once in every group."""
+    m, k = shape
+    v = ((synth.uniform(seed, m * k).reshape(m, k) - 0.5) * amax).astype(np.float32)
+    for c0 in range(0, k, group):
+        v[:, c0] = amax if (c0 // group) % 2 == 0 else -amax
+    return v
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 5, 256), (3, 7, 300), (2, 4, 1152)])
+def test_gemv_grouped_with_equal_scales_is_the_exact_int_path(m, n, k):
+    # every weight group and every activation group has the same absmax, so all
+    # scales are equal and y must be the per-tensor result acc * sx * sw
+    w = _equal_absmax(94 + k, (n, k), 128, 0.75)
+    x = _equal_absmax(95 + k, (m, k), 32, 3.0)
+    w8, sw = oracle.quantize_groups(w, 128)
+    x8, sx = oracle.quantize_groups(x, 32)
+    assert len(set(sw.ravel().tolist())) == 1 and len(set(sx.ravel().tolist())) == 1
+    y, bound = oracle.gemv_grouped(w8, sw, x8, sx)
+    acc = oracle.matmul_int(x8, w8)
+    ref = acc.astype(np.float64) * float(sx[0, 0]) * float(sw[0, 0])
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-300)
+    assert (bound >= np.abs(y) * (1 - 1e-12)).all()
+
+
+def test_gemv_grouped_maps_activation_group_h_to_weight_group_h_div_4():
+    # x is zero outside activation group h0; weight groups have distinct scales
+    n, k = 6, 640                       # 5 weight groups, 20 activation groups
+    w = synth.normal(96, (n, k))
+    for g in range(5):
+        w[:, 128 * g:128 * g + 128] *= np.float32(1 + 3 * g)
+    w8, sw = oracle.quantize_groups(w, 128)
+    for h0 in (0, 3, 4, 5, 19):
+        x = np.zeros((1, k), np.float32)
+        x[0, 32 * h0:32 * h0 + 32] = synth.normal(97 + h0, (32,))
+        x8, sx = oracle.quantize_groups(x, 32)
+        y, _ = oracle.gemv_grouped(w8, sw, x8, sx)
+        d = oracle.matmul_int(x8[:, 32 * h0:32 * h0 + 32], w8[:, 32 * h0:32 * h0 + 32])
+        ref = d[0].astype(np.float64) * sw[:, h0 // 4].astype(np.float64) * float(sx[0, h0])
+        np.testing.assert_allclose(y[0], ref, rtol=1e-13, atol=0)
+
+
+def test_gemv_grouped_tiny_exact_rationals():
+    m, n, k = 2, 3, 70
+    w8, sw = oracle.quantize_groups(synth.normal(98, (n, k)), 128)
+    x8, sx = oracle.quantize_groups(synth.normal(99, (m, k)), 32)
+    y, _ = oracle.gemv_grouped(w8, sw, x8, sx)
+    for mi, r in itertools.product(range(m), range(n)):
+        exact = sum(Fraction(float(sw[r, c // 128])) * Fraction(float(sx[mi, c // 32])) * int(x8[mi, c]) * int(w8[r, c])
+                    for c in range(k))
+        assert abs(Fraction(y[mi, r]) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 1000)
