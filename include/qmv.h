@@ -66,8 +66,14 @@ enum {
 /* Weight types. */
 enum {
     QMV_W_TERNARY5 = 1,     /* five trits per byte, one fp32 scale per matrix */
-    QMV_W_INT8 = 2          /* int8 codes, one fp32 scale per tensor */
+    QMV_W_INT8 = 2,         /* int8 codes, one fp32 scale per tensor */
+    QMV_W_INT8_G128 = 3     /* int8 codes, one fp32 scale per QMV_WEIGHT_GROUP columns of a row */
 };
+
+/* Group sizes of the group-scaled path (QMV_W_INT8_G128 and
+ * qmv_quantize_act_grouped). */
+#define QMV_WEIGHT_GROUP 128
+#define QMV_ACT_GROUP 32
 
 /* Flags of qmv_gemv / qmv_gemm_prefill. */
 enum {
@@ -84,22 +90,26 @@ enum {
 
 /* A packed weight matrix (host struct describing device memory). */
 typedef struct qmv_weight {
-    int32_t wtype;          /* QMV_W_TERNARY5 or QMV_W_INT8 */
+    int32_t wtype;          /* QMV_W_TERNARY5, QMV_W_INT8 or QMV_W_INT8_G128 */
     int32_t reserved;       /* must be 0 */
     int64_t n;              /* output rows */
     int64_t k;              /* input columns */
     const void* data;       /* device, qmv_packed_bytes(wtype, n, k) bytes, 16-byte aligned */
-    const float* scale;     /* device, 1 fp32 */
+    const float* scale;     /* device, 1 fp32; QMV_W_INT8_G128: [n][ceil(k/128)] fp32 */
 } qmv_weight;
 
-/* One matrix-times-activations problem: y[m][n] = (x8[m][:] . W[n][:]) * sx[m] * scale. */
+/* One matrix-times-activations problem: y[m][n] = (x8[m][:] . W[n][:]) * sx[m] * scale.
+ * For QMV_W_INT8_G128 weights the activations carry one scale per 32 columns
+ * and y[m][n] = sum_h (scale[n][h/4] * sx[m][h]) * D_h, D_h the exact int32 dot
+ * of columns 32h .. 32h+31 (see qmv_pack_int8_grouped). */
 typedef struct qmv_problem {
     qmv_weight w;
     const int8_t* x8;       /* device, [m][k] int8, row-major, natural column order */
-    const float* sx;        /* device, [m] fp32 per-token scales */
+    const float* sx;        /* device, [m] fp32 per-token scales; QMV_W_INT8_G128: [m][ceil(k/32)] */
     int64_t m;              /* tokens (lanes) */
     float* y;               /* device, [m][n] fp32, row-major */
-    int32_t* acc;           /* device, [m][n] int32 exact dot products; NULL = not wanted */
+    int32_t* acc;           /* device, [m][n] int32 exact dot products; NULL = not wanted (must be NULL
+                               for QMV_W_INT8_G128) */
 } qmv_problem;
 
 /* Library version string and status names (static strings). */
@@ -107,7 +117,8 @@ const char* qmv_version(void);
 const char* qmv_status_str(int32_t status);
 
 /* Bytes of a packed matrix in the device layout: n * roundup(ceil(k/5), 16)
- * for QMV_W_TERNARY5, n * roundup(k, 16) for QMV_W_INT8; -1 on bad input. */
+ * for QMV_W_TERNARY5, n * roundup(k, 16) for QMV_W_INT8 and QMV_W_INT8_G128;
+ * -1 on bad input. */
 int64_t qmv_packed_bytes(int32_t wtype, int64_t n, int64_t k);
 
 /*
@@ -137,6 +148,40 @@ int32_t qmv_pack_ternary(const int8_t* trits, int64_t n, int64_t k, float scale,
  */
 int32_t qmv_pack_int8(const float* w, int64_t n, int64_t k, void* packed, float* scale_out,
                       qmv_weight* desc_out, void* stream);
+
+/*
+ * qmv_pack_int8_grouped -- fp32 weights -> int8 codes in groups of
+ * QMV_WEIGHT_GROUP (128) consecutive columns of a row, one fp32 scale per group
+ * (gemma.cpp tour, "Weights, Blobs, and the .sbs Format": int8 groups of 128
+ * sharing one scale).  Each group is quantised by qmv_pack_int8's rule; the
+ * last group of a row may be shorter; groups never span rows.
+ *   w       [n][k] fp32, row-major, finite.
+ *   packed  qmv_packed_bytes(QMV_W_INT8_G128, n, k) bytes, 16-byte aligned:
+ *           row-major int8, each row padded with zero bytes to roundup(k, 16)
+ *           (unlike QMV_W_INT8, rows are not chunk-interleaved).
+ *   scales  [n][ceil(k/128)] fp32, written in-stream.
+ *   desc_out nullable host struct (wtype QMV_W_INT8_G128, scale = scales).
+ * Limits: k <= 65536, n <= 2^20, n * roundup(k, 16) < 2^31 (QMV_ESHAPE).
+ * For the activations of such a matrix use qmv_quantize_act_grouped.
+ */
+int32_t qmv_pack_int8_grouped(const float* w, int64_t n, int64_t k, void* packed, float* scales,
+                              qmv_weight* desc_out, void* stream);
+
+/*
+ * qmv_quantize_act_grouped -- int8 activations with one scale per
+ * QMV_ACT_GROUP (32) consecutive columns of a row ("Gemma 3 1B at 114 tokens
+ * per second on a laptop CPU", "A side finding: Gemma 4 E4B in 4-bit": one
+ * activation scale per 32 values instead of one per token), each group by
+ * qmv_quantize_act's rule; the last group of a row may be shorter.
+ *   x [m][k] fp32 row-major, finite.   x8 [m][k] int8.   sx [m][ceil(k/32)] fp32.
+ * Pair with QMV_W_INT8_G128 weights in qmv_gemv: activation group h lies in
+ * weight group h / 4, its dot product is exact in int32 and both scales are
+ * applied after it; y is summed over h in fp32 (within (ceil(k/32) + 3) * 2^-24
+ * of sum_h |term| of the exact result).  Such problems take acc = NULL and
+ * need m * (roundup(k, 32) + 4 * ceil(k/32)) <= 160 KB (activations staged in
+ * LDS); otherwise QMV_EINVAL / QMV_ESHAPE.
+ */
+int32_t qmv_quantize_act_grouped(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, void* stream);
 
 /*
  * qmv_quantize_act -- per-token int8 activation quantisation ("Step 2": the
@@ -190,12 +235,15 @@ int64_t qmv_prefill_workspace_bytes(const qmv_problem* probs /* host */, int32_t
  * "Many users at once": one read of each byte serves every lane).
  *   probs     host array of `count` problems (1 <= count); each problem has
  *             1 <= m <= QMV_MAX_GEMV_M, its own weights, activations and
- *             outputs.  All problems run in one kernel launch.
+ *             outputs.  All problems of one weight type run in one kernel
+ *             launch (one launch per type present).
  *   workspace device, >= qmv_gemv_workspace_bytes(probs, count) bytes; holds
  *             the problem table uploaded in-stream (see QMV_F_TABLE_READY).
  *   flags     0 or QMV_F_TABLE_READY.
  * y (and acc when non-NULL) are written for every problem.  x8/acc must not
  * alias y.  Results are exact in acc and do not depend on the grouping.
+ * QMV_W_INT8_G128 problems are summed in fp32 over their activation groups
+ * (see qmv_quantize_act_grouped).
  */
 int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes,
                  uint32_t flags, void* stream);

@@ -19,13 +19,15 @@ namespace {
 
 constexpr int64_t kMaxProblems = (int64_t)1 << kTileProbBits;
 constexpr int64_t kMaxInt8K = 65536;  // keeps every int8 x int8 dot inside int32
+// group-scaled int8: row blocks of as few as 4 rows must fit a tile entry
+constexpr int64_t kMaxGroupedN = (int64_t)4 << kTileRowBits;
 
 int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 int64_t row_stride(int32_t wtype, int64_t k)
 {
     if (wtype == QMV_W_TERNARY5) return round_up((k + 4) / 5, 16);
-    if (wtype == QMV_W_INT8) return round_up(k, 16);
+    if (wtype == QMV_W_INT8 || wtype == QMV_W_INT8_G128) return round_up(k, 16);
     return -1;
 }
 
@@ -37,12 +39,15 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? QMV_OK : QMV_EHIP; }
 
 int32_t check_weight(const qmv_weight& w)
 {
-    if (w.wtype != QMV_W_TERNARY5 && w.wtype != QMV_W_INT8) return QMV_EUNSUPPORTED;
+    if (w.wtype != QMV_W_TERNARY5 && w.wtype != QMV_W_INT8 && w.wtype != QMV_W_INT8_G128) return QMV_EUNSUPPORTED;
     if (w.reserved != 0) return QMV_EINVAL;
     if (!w.data || !w.scale) return QMV_EINVAL;
     if (!aligned(w.data, 16)) return QMV_EINVAL;
     if (w.n < 1 || w.k < 1 || w.n > QMV_MAX_N || w.k > QMV_MAX_K) return QMV_ESHAPE;
     if (w.wtype == QMV_W_INT8 && w.k > kMaxInt8K) return QMV_ESHAPE;
+    if (w.wtype == QMV_W_INT8_G128 &&
+        (w.k > kMaxInt8K || w.n > kMaxGroupedN || w.n * row_stride(w.wtype, w.k) > INT32_MAX))
+        return QMV_ESHAPE;
     return QMV_OK;
 }
 
@@ -56,6 +61,10 @@ int32_t check_problems(const qmv_problem* probs, int32_t count, int64_t max_m)
         if (st != QMV_OK) return st;
         if (!p.x8 || !p.sx || !p.y) return QMV_EINVAL;
         if (p.m < 1 || p.m > max_m) return QMV_ESHAPE;
+        if (p.w.wtype == QMV_W_INT8_G128) {   // no single exact dot per output; activations staged in LDS
+            if (p.acc) return QMV_EINVAL;
+            if ((int64_t)grouped_lds_bytes(p.m, p.w.k) > kMaxLds) return QMV_ESHAPE;
+        }
     }
     return QMV_OK;
 }
@@ -83,11 +92,11 @@ constexpr int kStreamMaxM = 2;
 
 struct Table {
     std::vector<uint8_t> bytes;
-    bool stream[3] = {false, false, false};
-    int64_t region[3] = {0, 0, 0};      // byte offset of the type's tile list or schedule
-    int32_t count[3] = {0, 0, 0};       // tiles (workgroup kernel) or workgroup tiles (streaming)
-    int32_t max_m[3] = {0, 0, 0}, max_chunks[3] = {0, 0, 0};
-    int32_t nb[3] = {0, 0, 0}, slot_bytes[3] = {0, 0, 0};
+    bool stream[4] = {false, false, false, false};
+    int64_t region[4] = {0, 0, 0, 0};      // byte offset of the type's tile list or schedule
+    int32_t count[4] = {0, 0, 0, 0};       // tiles (workgroup kernels) or workgroup tiles (streaming)
+    int32_t max_m[4] = {0, 0, 0, 0}, max_chunks[4] = {0, 0, 0, 0};
+    int32_t nb[4] = {0, 0, 0, 0}, slot_bytes[4] = {0, 0, 0, 0};   // slot_bytes[3]: LDS of the grouped kernel
 };
 
 int32_t chunks_of(const qmv_problem& p) { return (int32_t)(row_stride(p.w.wtype, p.w.k) / 16); }
@@ -105,6 +114,12 @@ int64_t table_bound(const qmv_problem* probs, int32_t count, int cus)
     // rows) and the first two entries of each workgroup (no more workgroups
     // than tiles)
     for (int wt = 1; wt <= 2; ++wt) b += round_up((3 * tiles64 + kStreamHdr + 2 * kStreamXcds) * 4, 256);
+    // group-scaled int8: one entry per tile of 256 / lanes_per_row rows
+    int64_t gtiles = 0;
+    for (int32_t i = 0; i < count; ++i)
+        if (probs[i].w.wtype == QMV_W_INT8_G128)
+            gtiles += rows_tiles(probs[i].w.n, kBlock / grouped_lanes_per_row(probs[i].w.k));
+    b += round_up(gtiles * 4, 256);
     return b;
 }
 
@@ -247,7 +262,7 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
     }
     const int64_t pbytes = round_up((int64_t)sizeof(DevProblem) * count, 256);
     std::vector<int32_t> lanes(count, 1);             // per table slot
-    std::vector<uint32_t> words[3];
+    std::vector<uint32_t> words[4];
     for (int wt = 1; wt <= 2; ++wt) {
         if (t.max_m[wt] == 0) continue;
         std::vector<const qmv_problem*> sp;
@@ -275,8 +290,22 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
             t.count[wt] = (int32_t)words[wt].size();
         }
     }
+    if (t.max_m[QMV_W_INT8_G128] > 0) {   // group-scaled int8: one workgroup per tile
+        size_t lds = 0;
+        for (int32_t slot = 0; slot < count; ++slot) {
+            const qmv_problem& p = probs[order[slot]];
+            if (p.w.wtype != QMV_W_INT8_G128) continue;
+            lanes[slot] = grouped_lanes_per_row(p.w.k);
+            const int64_t nt = rows_tiles(p.w.n, kBlock / lanes[slot]);
+            for (int64_t r = 0; r < nt; ++r)
+                words[QMV_W_INT8_G128].push_back(((uint32_t)slot << kTileRowBits) | (uint32_t)r);
+            lds = std::max(lds, grouped_lds_bytes(p.m, p.w.k));
+        }
+        t.count[QMV_W_INT8_G128] = (int32_t)words[QMV_W_INT8_G128].size();
+        t.slot_bytes[QMV_W_INT8_G128] = (int32_t)lds;
+    }
     int64_t total = pbytes;
-    for (int wt = 1; wt <= 2; ++wt) {
+    for (int wt = 1; wt <= 3; ++wt) {
         t.region[wt] = total;
         total += round_up((int64_t)words[wt].size() * 4, 256);
     }
@@ -300,7 +329,7 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
         d.lanes_per_row = lanes[slot];
         d.reserved = 0;
     }
-    for (int wt = 1; wt <= 2; ++wt)
+    for (int wt = 1; wt <= 3; ++wt)
         if (!words[wt].empty())
             std::memcpy(t.bytes.data() + t.region[wt], words[wt].data(), words[wt].size() * 4);
     return QMV_OK;
@@ -462,6 +491,35 @@ int32_t qmv_pack_int8(const float* w, int64_t n, int64_t k, void* packed, float*
     return QMV_OK;
 }
 
+int32_t qmv_pack_int8_grouped(const float* w, int64_t n, int64_t k, void* packed, float* scales,
+                              qmv_weight* desc_out, void* stream)
+{
+    if (!w || !packed || !scales) return QMV_EINVAL;
+    if (n < 1 || k < 1 || n > kMaxGroupedN || k > kMaxInt8K) return QMV_ESHAPE;
+    if (n * row_stride(QMV_W_INT8_G128, k) > INT32_MAX) return QMV_ESHAPE;
+    if (!aligned(packed, 16)) return QMV_EINVAL;
+    hipError_t e = launch_quantize_groups(w, n, k, QMV_WEIGHT_GROUP, row_stride(QMV_W_INT8_G128, k),
+                                          static_cast<int8_t*>(packed), scales, as_stream(stream));
+    if (e != hipSuccess) return QMV_EHIP;
+    if (desc_out) {
+        desc_out->wtype = QMV_W_INT8_G128;
+        desc_out->reserved = 0;
+        desc_out->n = n;
+        desc_out->k = k;
+        desc_out->data = packed;
+        desc_out->scale = scales;
+    }
+    return QMV_OK;
+}
+
+int32_t qmv_quantize_act_grouped(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, void* stream)
+{
+    if (!x || !x8 || !sx) return QMV_EINVAL;
+    if (m < 1 || k < 1 || k > QMV_MAX_K || m > ((int64_t)1 << 31) - 1 || m * ((k + 31) / 32) > INT32_MAX)
+        return QMV_ESHAPE;
+    return hip_status(launch_quantize_groups(x, m, k, QMV_ACT_GROUP, k, x8, sx, as_stream(stream)));
+}
+
 int32_t qmv_quantize_act(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, void* stream)
 {
     if (!x || !x8 || !sx) return QMV_EINVAL;
@@ -517,11 +575,13 @@ int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64
     }
     uint8_t* base = static_cast<uint8_t*>(workspace);
     const DevProblem* dp = reinterpret_cast<const DevProblem*>(base);
-    for (int wt = 1; wt <= 2; ++wt) {
+    for (int wt = 1; wt <= 3; ++wt) {
         if (t.count[wt] == 0) continue;
         uint32_t* words = reinterpret_cast<uint32_t*>(base + t.region[wt]);
         hipError_t e;
-        if (t.stream[wt])
+        if (wt == QMV_W_INT8_G128)
+            e = launch_gemv_grouped(dp, words, t.count[wt], t.max_m[wt], (size_t)t.slot_bytes[wt], s);
+        else if (t.stream[wt])
             e = launch_gemv_stream(dp, words, t.nb[wt], wt, t.max_m[wt], t.slot_bytes[wt], s);
         else
             e = launch_gemv(dp, words, 0, t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);

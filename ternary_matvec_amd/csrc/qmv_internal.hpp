@@ -16,9 +16,9 @@ constexpr int kTileRowBits = 18;
 // One problem as the kernels see it (uploaded into the caller's workspace).
 struct DevProblem {
     const uint8_t* w;    // packed weights in the chunk-interleaved layout
-    const float* sw;     // 1 fp32 weight scale
+    const float* sw;     // 1 fp32 weight scale ([n][ceil(k/128)] for group-scaled int8)
     const int8_t* x8;    // [m][k] int8 activations, natural column order
-    const float* sx;     // [m] fp32 activation scales
+    const float* sx;     // [m] fp32 activation scales ([m][ceil(k/32)] for group-scaled int8)
     float* y;            // [m][n] fp32 outputs
     int32_t* acc;        // [m][n] int32 exact dots, or null
     int32_t n;           // output rows
@@ -26,8 +26,8 @@ struct DevProblem {
     int32_t m;           // tokens
     int32_t chunks;      // 16-byte chunks per row (row stride / 16)
     int32_t tile_begin;  // first tile of this problem in the launch
-    int32_t wtype;       // 1 = five trits per byte, 2 = int8
-    int32_t lanes_per_row;  // streaming kernel: lanes sharing one row (1, 2, 4 or 8)
+    int32_t wtype;       // 1 = five trits per byte, 2 = int8, 3 = int8 with group scales
+    int32_t lanes_per_row;  // lanes sharing one row (streaming kernel: 1 .. 8; group-scaled: 4 .. 64)
     int32_t reserved;
 };
 static_assert(sizeof(DevProblem) == 80, "DevProblem layout");
@@ -130,5 +130,12 @@ hipError_t launch_read_probe(const void* data, int64_t bytes, uint32_t* out, int
 hipError_t launch_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, int32_t* idx,
                          float* max_logit, float* logits, void* workspace, hipStream_t s);
 int64_t lmhead_partials(int64_t v);
+// Group-scaled int8 (weights per 128 columns, activations per 32).
+hipError_t launch_quantize_groups(const float* x, int64_t rows, int64_t k, int group, int64_t q_stride, int8_t* q,
+                                  float* s, hipStream_t st);
+int grouped_lanes_per_row(int64_t k);          // lanes sharing one row: 4 .. 64
+size_t grouped_lds_bytes(int64_t m, int64_t k);
+hipError_t launch_gemv_grouped(const DevProblem* probs, const uint32_t* tiles, int32_t count, int max_m, size_t lds,
+                               hipStream_t s);
 
 }  // namespace qmv

@@ -22,6 +22,9 @@ QMV_EWORKSPACE = -6
 
 QMV_W_TERNARY5 = 1
 QMV_W_INT8 = 2
+QMV_W_INT8_G128 = 3
+QMV_WEIGHT_GROUP = 128
+QMV_ACT_GROUP = 32
 QMV_F_TABLE_READY = 1
 QMV_MAX_GEMV_M = 16
 
@@ -55,6 +58,9 @@ SIGNATURES = {
                                   ctypes.POINTER(qmv_weight), _c_ptr]),
     "qmv_pack_int8": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.POINTER(qmv_weight), _c_ptr]),
     "qmv_quantize_act": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "qmv_pack_int8_grouped": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.POINTER(qmv_weight),
+                                       _c_ptr]),
+    "qmv_quantize_act_grouped": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_gemv_workspace_bytes": (_c_i64, [ctypes.POINTER(qmv_problem), _c_i32]),
     "qmv_prefill_workspace_bytes": (_c_i64, [ctypes.POINTER(qmv_problem), _c_i32]),
     "qmv_gemv": (_c_i32, [ctypes.POINTER(qmv_problem), _c_i32, _c_ptr, _c_i64, _c_u32, _c_ptr]),
@@ -186,6 +192,35 @@ def qmv_quantize_act(x, x8=None, sx=None, stream=None):
     if sx is None:
         sx = torch.empty(m, dtype=torch.float32, device=x.device)
     _check(load().qmv_quantize_act(_ptr(x), m, k, _ptr(x8), _ptr(sx), _stream(stream)), "qmv_quantize_act")
+    return x8, sx
+
+
+def qmv_pack_int8_grouped(w, packed=None, scales=None, stream=None) -> Weight:
+    """fp32 [n][k] -> int8 codes in groups of 128 columns, one scale per group."""
+    _dev(w, torch.float32, "w")
+    n, k = w.shape
+    nbytes = qmv_packed_bytes(QMV_W_INT8_G128, n, k)
+    if packed is None:
+        packed = _alloc_aligned(nbytes, w.device, 16)
+    if scales is None:
+        scales = torch.empty((n, (k + QMV_WEIGHT_GROUP - 1) // QMV_WEIGHT_GROUP), dtype=torch.float32,
+                             device=w.device)
+    desc = qmv_weight()
+    _check(load().qmv_pack_int8_grouped(_ptr(w), n, k, _ptr(packed), _ptr(scales), ctypes.byref(desc),
+                                        _stream(stream)), "qmv_pack_int8_grouped")
+    return Weight(desc, packed, scales)
+
+
+def qmv_quantize_act_grouped(x, x8=None, sx=None, stream=None):
+    """fp32 [m][k] -> int8 codes with one scale per 32 columns: (x8 [m][k], sx [m][ceil(k/32)])."""
+    _dev(x, torch.float32, "x")
+    m, k = x.shape
+    if x8 is None:
+        x8 = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if sx is None:
+        sx = torch.empty((m, (k + QMV_ACT_GROUP - 1) // QMV_ACT_GROUP), dtype=torch.float32, device=x.device)
+    _check(load().qmv_quantize_act_grouped(_ptr(x), m, k, _ptr(x8), _ptr(sx), _stream(stream)),
+           "qmv_quantize_act_grouped")
     return x8, sx
 
 

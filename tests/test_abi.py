@@ -55,6 +55,8 @@ def test_packed_bytes(lib):
     assert qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, 3, 81) == 3 * 32
     assert qmv.qmv_packed_bytes(qmv.QMV_W_INT8, 768, 288) == 768 * 288
     assert qmv.qmv_packed_bytes(qmv.QMV_W_INT8, 2, 17) == 64
+    assert qmv.qmv_packed_bytes(qmv.QMV_W_INT8_G128, 6912, 1152) == 6912 * 1152
+    assert qmv.qmv_packed_bytes(qmv.QMV_W_INT8_G128, 3, 300) == 3 * 304
     assert qmv.qmv_packed_bytes(7, 2, 17) == -1
     assert qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, 0, 17) == -1
 
@@ -77,6 +79,15 @@ def test_host_validation_errors(lib):
     assert lib.qmv_pack_ternary(_fake(64), 2, 4, float("inf"), _fake(4096), _fake(8192), None, None, s) == qmv.QMV_EVALUE
     # int8 K limit keeps every dot inside int32
     assert lib.qmv_pack_int8(_fake(64), 2, 70000, _fake(4096), _fake(8192), None, s) == qmv.QMV_ESHAPE
+    # group-scaled int8: nulls, shapes, alignment
+    assert lib.qmv_pack_int8_grouped(_fake(64), 2, 300, _fake(4096), None, None, s) == qmv.QMV_EINVAL
+    assert lib.qmv_pack_int8_grouped(_fake(64), 2, 70000, _fake(4096), _fake(8192), None, s) == qmv.QMV_ESHAPE
+    assert lib.qmv_pack_int8_grouped(_fake(64), (1 << 20) + 1, 64, _fake(4096), _fake(8192), None, s) == \
+        qmv.QMV_ESHAPE
+    assert lib.qmv_pack_int8_grouped(_fake(64), 1 << 20, 4096, _fake(4096), _fake(8192), None, s) == qmv.QMV_ESHAPE
+    assert lib.qmv_pack_int8_grouped(_fake(64), 2, 300, _fake(4100), _fake(8192), None, s) == qmv.QMV_EINVAL
+    assert lib.qmv_quantize_act_grouped(_fake(64), 1, 0, _fake(4096), _fake(8192), s) == qmv.QMV_ESHAPE
+    assert lib.qmv_quantize_act_grouped(None, 1, 4, _fake(4096), _fake(8192), s) == qmv.QMV_EINVAL
     # lm_head
     assert lib.qmv_lmhead_argmax(_fake(4096), _fake(64), 10, 8, None, None, None, _fake(256), 4096, s) == qmv.QMV_EINVAL
     assert lib.qmv_lmhead_argmax(_fake(4096), _fake(64), 10, 8, _fake(64), None, None, None, 0, s) == qmv.QMV_EWORKSPACE
@@ -154,3 +165,24 @@ def test_read_probe_rejects_bad_arguments(lib):
     assert lib.qmv_read_probe(ctypes.c_void_p(17), 16, ctypes.addressof(out), None) == EINVAL
     assert lib.qmv_read_probe(ctypes.c_void_p(16), -16, ctypes.addressof(out), None) == EINVAL
     assert lib.qmv_read_probe(ctypes.c_void_p(16), 0, ctypes.addressof(out), None) == 0
+
+
+def test_gemv_grouped_validation(lib):
+    g = qmv.QMV_W_INT8_G128
+    arr = (qmv.qmv_problem * 3)(_problem(wtype=g, n=6912, k=1152), _problem(n=100, k=1152, m=3),
+                                _problem(wtype=g, n=1152, k=6912, m=16))
+    need = lib.qmv_gemv_workspace_bytes(arr, 3)
+    assert need > 0 and need % 256 == 0
+    # the grouped path has no single exact dot: acc must be NULL
+    p = _problem(wtype=g)
+    p.acc = 24576
+    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EINVAL
+    # staged activations past the LDS: 16 tokens x 16384 columns
+    big = (qmv.qmv_problem * 1)(_problem(wtype=g, n=64, k=16384, m=16))
+    assert lib.qmv_gemv_workspace_bytes(big, 1) == -1
+    assert lib.qmv_gemv(big, 1, _fake(1 << 20), 1 << 30, 0, None) == qmv.QMV_ESHAPE
+    # rows past the tile-entry limit
+    big = (qmv.qmv_problem * 1)(_problem(wtype=g, n=(1 << 20) + 1, k=64))
+    assert lib.qmv_gemv_workspace_bytes(big, 1) == -1
+    # prefill takes ternary weights only
+    assert lib.qmv_prefill_workspace_bytes((qmv.qmv_problem * 1)(_problem(wtype=g)), 1) == -1
