@@ -712,6 +712,67 @@ def bench_int8(dev, stream, reps=2000):
             "GB/s": round(nbytes / us / 1e3, 2)}
 
 
+def bench_groupscale(dev, stream, copies=2, reps=50):
+    """Gemma-3-1B shapes x26 with int8 weights in groups of 128 and activation
+    scales per 32 columns, batch 1: one grouped qmv_gemv launch of 156 problems."""
+    import torch
+    from ternary_matvec_amd import qmv, synth
+    cfg = synth.CONFIG_GEMMA_DECODE
+    specs = [(layer, mid, n, k) for layer in range(synth.GEMMA_LAYERS) for mid, (_, n, k) in enumerate(synth.GEMMA_MATS)]
+    wbytes = sum(qmv.qmv_packed_bytes(qmv.QMV_W_INT8_G128, n, k) for (_, _, n, k) in specs)
+    nscale = sum(n * ((k + 127) // 128) for (_, _, n, k) in specs)
+    pools = [qmv._alloc_aligned(wbytes, dev, 256) for _ in range(copies)]
+    spool = [torch.empty(nscale, dtype=torch.float32, device=dev) for _ in range(copies)]
+    descs, off, soff = [], 0, 0
+    for (layer, mid, n, k) in specs:
+        nb = qmv.qmv_packed_bytes(qmv.QMV_W_INT8_G128, n, k)
+        ns = n * ((k + 127) // 128)
+        w = synth.normal_torch(synth.stream_seed(cfg, layer, mid, synth.TAG_WEIGHT), (n, k), std=0.02, device=dev)
+        qmv.qmv_pack_int8_grouped(w, packed=pools[0][off:off + nb], scales=spool[0][soff:soff + ns])
+        descs.append((n, k, off, nb, soff, ns))
+        off += nb
+        soff += ns
+        del w
+    torch.cuda.synchronize()
+    for c in range(1, copies):
+        pools[c].copy_(pools[0])
+        spool[c].copy_(spool[0])
+    xs = [torch.from_numpy(synth.normal(synth.stream_seed(cfg, layer, mid, synth.TAG_ACT), (1, k))).to(dev)
+          for (layer, mid, n, k) in specs]
+    acts = [qmv.qmv_quantize_act_grouped(x) for x in xs]
+    ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for (_, _, n, _) in specs]
+    arrays, workspaces = [], []
+    for c in range(copies):
+        probs = []
+        for i, (n, k, o, nb, so, ns) in enumerate(descs):
+            wc = qmv.Weight(qmv.qmv_weight(qmv.QMV_W_INT8_G128, 0, n, k, pools[c][o:].data_ptr(),
+                                           spool[c][so:].data_ptr()), pools[c][o:o + nb], spool[c][so:so + ns])
+            probs.append(qmv.Problem(wc, acts[i][0], acts[i][1], y=ys[i]))
+        arr = qmv.problem_array(probs)
+        arrays.append(arr)
+        workspaces.append(qmv.qmv_gemv(arr))
+    torch.cuda.synchronize()
+    for i in range(10):
+        qmv.qmv_gemv(arrays[i % copies], workspace=workspaces[i % copies], flags=qmv.QMV_F_TABLE_READY, stream=stream)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(reps):
+        qmv.qmv_gemv(arrays[i % copies], workspace=workspaces[i % copies], flags=qmv.QMV_F_TABLE_READY, stream=stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) / reps * 1e3
+    nbytes = wbytes + 4 * nscale + sum(k + 4 * ((k + 31) // 32) + 4 * n for (_, _, n, k) in specs)
+    out = {"workload": "int8 weights in groups of 128 columns, activation scales per 32, Gemma-3-1B shapes x26 "
+                       "(156 matrices), batch 1, one grouped launch", "weight_copies": copies,
+           "bytes_per_launch": nbytes, "us_per_launch": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
+           "frac_of_8TBps": round(nbytes / us / 8e6, 3)}
+    del pools, spool, arrays, workspaces
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_bitnet(dev, stream, steps, warmup, copies):
     import torch
     from ternary_matvec_amd import synth
@@ -842,6 +903,8 @@ def main():
             torch.cuda.empty_cache()
             log("int8 GEMV")
             extras["int8_gemv"] = bench_int8(dev, stream)
+            log("group-scaled int8 decode")
+            extras["groupscale_decode"] = bench_groupscale(dev, stream)
             log("BitNet decode")
             extras["bitnet_decode"] = bench_bitnet(dev, stream, max(20, args.steps // 4), 5, min(args.copies, 8))
         except Exception as e:  # extras never hide the headline line
