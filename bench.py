@@ -44,8 +44,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="headline workload only")
     ap.add_argument("--profile-set", action="store_true",
-                    help="only the launches the kernel profiles describe: decode steps, full prefill passes and "
-                         "the output layer (no sweeps, chained, per-matrix, int8 or BitNet launches)")
+                    help="only the launches the kernel profiles describe: decode steps, full prefill passes, "
+                         "the output layer, the sketch head and the group-scaled decode (no sweeps, chained, "
+                         "per-matrix, int8 or BitNet launches)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU-oracle time")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB five times: the "
@@ -728,15 +729,13 @@ def bench_groupscale(dev, stream, copies=2, reps=50):
         nb = qmv.qmv_packed_bytes(qmv.QMV_W_INT8_G128, n, k)
         ns = n * ((k + 127) // 128)
         w = synth.normal_torch(synth.stream_seed(cfg, layer, mid, synth.TAG_WEIGHT), (n, k), std=0.02, device=dev)
-        qmv.qmv_pack_int8_grouped(w, packed=pools[0][off:off + nb], scales=spool[0][soff:soff + ns])
+        for c in range(copies):   # packed per copy: no device copy larger than the counter calibration's
+            qmv.qmv_pack_int8_grouped(w, packed=pools[c][off:off + nb], scales=spool[c][soff:soff + ns])
         descs.append((n, k, off, nb, soff, ns))
         off += nb
         soff += ns
         del w
     torch.cuda.synchronize()
-    for c in range(1, copies):
-        pools[c].copy_(pools[0])
-        spool[c].copy_(spool[0])
     xs = [torch.from_numpy(synth.normal(synth.stream_seed(cfg, layer, mid, synth.TAG_ACT), (1, k))).to(dev)
           for (layer, mid, n, k) in specs]
     acts = [qmv.qmv_quantize_act_grouped(x) for x in xs]
@@ -884,6 +883,8 @@ def main():
         log("sketch head")
         result["extras"]["lmhead_sketch"] = bench_sketch(dev, stream)
         torch.cuda.empty_cache()
+        log("group-scaled int8 decode")
+        result["extras"]["groupscale_decode"] = bench_groupscale(dev, stream)
     elif not args.no_extras:
         extras = {}
         try:
