@@ -3,8 +3,8 @@
 Headline workload: batch-1 ternary decode over Gemma-3-1B-shaped weights,
 26 layers x {q, k, v, gate, up, down} = 156 matrices, trits iid with
 P(-1, 0, +1) = (0.3, 0.4, 0.3), one scale per matrix, x ~ N(0, 1).  One step:
-  qmv_quantize_act on the 130 activation rows of K = 1152 and the 26 rows of
-  K = 6912, then one grouped qmv_gemv over the 156 problems.
+  qmv_quantize_act_many on the 130 activation rows of K = 1152 and the 26 rows
+  of K = 6912 (one launch), then one grouped qmv_gemv over the 156 problems.
 Weights rotate over several full copies so the 256 MB Infinity Cache cannot
 hold the working set.  `value` = algorithmic bytes per step / step time.
 
@@ -86,6 +86,8 @@ class DecodeStack:
         for k in ks:
             self.x8[k] = torch.empty(self.x[k].shape, dtype=torch.int8, device=dev)
             self.sx[k] = torch.empty(self.x[k].shape[0], dtype=torch.float32, device=dev)
+        # every width's activations quantised by one launch
+        self.acts = qmv.act_array([(self.x[k], self.x8[k], self.sx[k]) for k in ks])
         total_packed = sum(qmv.qmv_packed_bytes(qmv.QMV_W_TERNARY5, n, k) for (_, _, _, n, k, _) in self.specs)
         self.packed_bytes = total_packed
         self.pool = [qmv._alloc_aligned(total_packed, dev, 256) for _ in range(copies)]
@@ -150,8 +152,7 @@ def time_decode(stack, steps, warmup, stream):
     from ternary_matvec_amd import qmv
 
     def step(i, ev=None):
-        for k in stack.x:
-            qmv.qmv_quantize_act(stack.x[k], x8=stack.x8[k], sx=stack.sx[k], stream=stream)
+        qmv.qmv_quantize_act_many(stack.acts, stream=stream)
         c = i % stack.copies
         if ev is not None:
             ev[0].record(stream)
@@ -289,23 +290,32 @@ def chained(stack, steps, stream, copies=4):
 
 
 def time_quantize(stack, steps, stream):
-    """The step's two qmv_quantize_act calls (one per K) alone."""
+    """The step's quantisation alone: the one qmv_quantize_act_many launch, and
+    for comparison one qmv_quantize_act call per width."""
     import torch
     from ternary_matvec_amd import qmv
-    for _ in range(5):
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(steps):
+            fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def per_width():
         for k in stack.x:
             qmv.qmv_quantize_act(stack.x[k], x8=stack.x8[k], sx=stack.sx[k], stream=stream)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record(stream)
-    for _ in range(steps):
-        for k in stack.x:
-            qmv.qmv_quantize_act(stack.x[k], x8=stack.x8[k], sx=stack.sx[k], stream=stream)
-    t1.record(stream)
-    torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / steps
-    return {"us": round(ms * 1e3, 2), "GB/s": round(stack.quant_bytes() / ms / 1e6, 1)}
+
+    ms = timed(lambda: qmv.qmv_quantize_act_many(stack.acts, stream=stream))
+    ms_w = timed(per_width)
+    return {"us": round(ms * 1e3, 2), "GB/s": round(stack.quant_bytes() / ms / 1e6, 1),
+            "us_one_call_per_width": round(ms_w * 1e3, 2)}
 
 
 # ---------------------------------------------------------------------------
@@ -392,6 +402,7 @@ class PrefillStack:
             self.x[k] = xk
             self.x8[k] = torch.empty(xk.shape, dtype=torch.int8, device=dev)
             self.sx[k] = torch.empty(xk.shape[0], dtype=torch.float32, device=dev)
+        self.acts = qmv.act_array([(self.x[k], self.x8[k], self.sx[k]) for k in ks])
         self.y = {}
         probs = []
         pool = stack.pool[0]
@@ -422,8 +433,7 @@ def time_prefill(ps, steps, warmup, stream):
     from ternary_matvec_amd import qmv
 
     def step(ev=None):
-        for k in ps.x:
-            qmv.qmv_quantize_act(ps.x[k], x8=ps.x8[k], sx=ps.sx[k], stream=stream)
+        qmv.qmv_quantize_act_many(ps.acts, stream=stream)
         if ev is not None:
             ev[0].record(stream)
         qmv.qmv_gemm_prefill(ps.arr, workspace=ps.ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
@@ -861,7 +871,7 @@ def main():
         "config": {"workload": "ternary batch-1 decode, Gemma-3-1B shapes x26 layers (156 matrices: q 1024x1152, "
                                "k/v 256x1152, gate/up 6912x1152, down 1152x6912), 5 trits/byte",
                    "tokens": 1, "matrices": len(stack.specs), "weight_copies": args.copies,
-                   "step": "qmv_quantize_act x2 + one grouped qmv_gemv",
+                   "step": "qmv_quantize_act_many (both widths, one launch) + one grouped qmv_gemv",
                    "step_bytes": step_bytes, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "k_gemv_stream<1,1> (grouped ternary GEMV)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

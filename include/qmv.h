@@ -192,6 +192,28 @@ int32_t qmv_quantize_act_grouped(const float* x, int64_t m, int64_t k, int8_t* x
  */
 int32_t qmv_quantize_act(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, void* stream);
 
+/* One activation set of qmv_quantize_act_many (host struct describing device memory). */
+typedef struct qmv_act {
+    const float* x;         /* device, [m][k] fp32 row-major, finite */
+    int64_t m;              /* rows (tokens) */
+    int64_t k;              /* columns */
+    int8_t* x8;             /* device, [m][k] int8 codes */
+    float* sx;              /* device, [m] fp32 scales */
+} qmv_act;
+
+#define QMV_MAX_ACT_SETS 8           /* activation sets per qmv_quantize_act_many call */
+
+/*
+ * qmv_quantize_act_many -- qmv_quantize_act over up to QMV_MAX_ACT_SETS sets of
+ * activations of different widths in one launch (a decode step's inputs of
+ * every width at once); each set's codes and scales are bit-identical to
+ * qmv_quantize_act on that set.
+ *   acts  host array of `count` sets, 1 <= count <= QMV_MAX_ACT_SETS.
+ * EINVAL for a NULL array or pointer, ESHAPE for a bad count or shape or more
+ * than 2^31 - 1 rows in all.
+ */
+int32_t qmv_quantize_act_many(const qmv_act* acts, int32_t count, void* stream);
+
 /*
  * qmv_rmsnorm_quantize -- RMSNorm, then the same per-token quantisation, in one
  * pass (llama2.c tour, "Step 1" / "Step 6": o = weight * (x / rms), rms =

@@ -520,6 +520,27 @@ int32_t qmv_quantize_act_grouped(const float* x, int64_t m, int64_t k, int8_t* x
     return hip_status(launch_quantize_groups(x, m, k, QMV_ACT_GROUP, k, x8, sx, as_stream(stream)));
 }
 
+int32_t qmv_quantize_act_many(const qmv_act* acts, int32_t count, void* stream)
+{
+    if (!acts) return QMV_EINVAL;
+    if (count < 1 || count > QMV_MAX_ACT_SETS) return QMV_ESHAPE;
+    static_assert(QMV_MAX_ACT_SETS == kMaxActSets, "activation set count");
+    ActSets sets{};
+    int64_t rows = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const qmv_act& a = acts[i];
+        if (!a.x || !a.x8 || !a.sx) return QMV_EINVAL;
+        if (a.m < 1 || a.k < 1 || a.k > QMV_MAX_K) return QMV_ESHAPE;
+        sets.set[i] = ActSet{a.x, a.x8, a.sx, a.k};
+        sets.first[i] = rows;
+        rows += a.m;
+        if (rows > ((int64_t)1 << 31) - 1) return QMV_ESHAPE;
+    }
+    sets.first[count] = rows;
+    sets.count = count;
+    return hip_status(launch_quantize_many(sets, rows, as_stream(stream)));
+}
+
 int32_t qmv_quantize_act(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, void* stream)
 {
     if (!x || !x8 || !sx) return QMV_EINVAL;

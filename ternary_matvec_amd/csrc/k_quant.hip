@@ -48,13 +48,9 @@ __device__ __forceinline__ int8_t quantize_one(float v, float s)
 // ---------------------------------------------------------------------------
 // Per-row quantisation: one workgroup per row.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_quantize_rows(const float* __restrict__ x, int64_t k,
-                                                         int8_t* __restrict__ x8, float* __restrict__ sx)
+__device__ __forceinline__ void quantize_row(const float* __restrict__ xr, int64_t k, int8_t* __restrict__ qr,
+                                             float* __restrict__ sx_out, float* red)
 {
-    __shared__ float red[4];
-    const int64_t row = blockIdx.x;
-    const float* xr = x + row * k;
-    int8_t* qr = x8 + row * k;
     float m = 0.0f;
     const bool vec = ((reinterpret_cast<uintptr_t>(xr) & 15) == 0);
     int64_t head = vec ? (k & ~int64_t(3)) : 0;
@@ -68,7 +64,7 @@ __global__ __launch_bounds__(kBlock) void k_quantize_rows(const float* __restric
     for (int64_t i = head + threadIdx.x; i < k; i += kBlock) m = fmaxf(m, fabsf(xr[i]));
     m = block_max(m, red);
     const float s = scale_from_max(m);
-    if (threadIdx.x == 0) sx[row] = s;
+    if (threadIdx.x == 0) *sx_out = s;
     const bool vec_out = vec && ((reinterpret_cast<uintptr_t>(qr) & 3) == 0);
     if (vec_out) {
         const float4* x4 = reinterpret_cast<const float4*>(xr);
@@ -83,6 +79,27 @@ __global__ __launch_bounds__(kBlock) void k_quantize_rows(const float* __restric
     } else {
         for (int64_t i = threadIdx.x; i < k; i += kBlock) qr[i] = quantize_one(xr[i], s);
     }
+}
+
+__global__ __launch_bounds__(kBlock) void k_quantize_rows(const float* __restrict__ x, int64_t k,
+                                                         int8_t* __restrict__ x8, float* __restrict__ sx)
+{
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    quantize_row(x + row * k, k, x8 + row * k, sx + row, red);
+}
+
+// Several activation sets in one launch: workgroup b quantises row
+// b - first[i] of the set i whose rows it falls in.
+__global__ __launch_bounds__(kBlock) void k_quantize_many(ActSets sets)
+{
+    __shared__ float red[4];
+    const int64_t b = blockIdx.x;
+    int i = 0;
+    while (i + 1 < sets.count && b >= sets.first[i + 1]) ++i;
+    const ActSet& a = sets.set[i];
+    const int64_t row = b - sets.first[i];
+    quantize_row(a.x + row * a.k, a.k, a.x8 + row * a.k, a.sx + row, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -287,6 +304,12 @@ int grid_for(int64_t items)
 hipError_t launch_quantize_rows(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, hipStream_t s)
 {
     hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)m), dim3(kBlock), 0, s, x, k, x8, sx);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_many(const ActSets& sets, int64_t rows, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_quantize_many, dim3((unsigned)rows), dim3(kBlock), 0, s, sets);
     return hipGetLastError();
 }
 

@@ -77,6 +77,20 @@ hipError_t launch_pack_ternary(const int8_t* trits, int64_t n, int64_t k, int64_
 hipError_t launch_pack_int8(const float* w, int64_t n, int64_t k, int64_t chunks, int8_t* out,
                             float* scale_out, hipStream_t s);
 hipError_t launch_quantize_rows(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, hipStream_t s);
+// Activation sets of one multi-set quantisation launch (a kernel argument).
+constexpr int kMaxActSets = 8;
+struct ActSet {
+    const float* x;
+    int8_t* x8;
+    float* sx;
+    int64_t k;
+};
+struct ActSets {
+    ActSet set[kMaxActSets];
+    int64_t first[kMaxActSets + 1];   // first workgroup (row) of each set; first[count] = rows
+    int32_t count;
+};
+hipError_t launch_quantize_many(const ActSets& sets, int64_t rows, hipStream_t s);
 int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks);
 constexpr int64_t kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
 hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,

@@ -41,6 +41,13 @@ class qmv_problem(ctypes.Structure):
                 ("acc", _c_ptr)]
 
 
+class qmv_act(ctypes.Structure):
+    _fields_ = [("x", _c_ptr), ("m", _c_i64), ("k", _c_i64), ("x8", _c_ptr), ("sx", _c_ptr)]
+
+
+QMV_MAX_ACT_SETS = 8
+
+
 class QmvError(RuntimeError):
     def __init__(self, status, what):
         self.status = status
@@ -58,6 +65,7 @@ SIGNATURES = {
                                   ctypes.POINTER(qmv_weight), _c_ptr]),
     "qmv_pack_int8": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.POINTER(qmv_weight), _c_ptr]),
     "qmv_quantize_act": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "qmv_quantize_act_many": (_c_i32, [ctypes.POINTER(qmv_act), _c_i32, _c_ptr]),
     "qmv_pack_int8_grouped": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.POINTER(qmv_weight),
                                        _c_ptr]),
     "qmv_quantize_act_grouped": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
@@ -222,6 +230,28 @@ def qmv_quantize_act_grouped(x, x8=None, sx=None, stream=None):
     _check(load().qmv_quantize_act_grouped(_ptr(x), m, k, _ptr(x8), _ptr(sx), _stream(stream)),
            "qmv_quantize_act_grouped")
     return x8, sx
+
+
+def act_array(sets):
+    """[(x fp32 [m][k], x8 int8 [m][k], sx fp32 [m]), ...] -> a qmv_act array (the tensors must stay alive)."""
+    arr = (qmv_act * len(sets))()
+    for i, (x, x8, sx) in enumerate(sets):
+        _dev(x, torch.float32, "x")
+        _dev(x8, torch.int8, "x8")
+        _dev(sx, torch.float32, "sx")
+        m, k = x.shape
+        if tuple(x8.shape) != (m, k) or sx.numel() != m:
+            raise QmvError(QMV_ESHAPE, "act_array")
+        arr[i] = qmv_act(x.data_ptr(), m, k, x8.data_ptr(), sx.data_ptr())
+    return arr
+
+
+def qmv_quantize_act_many(sets, stream=None):
+    """qmv_quantize_act over several activation sets in one launch; `sets` is a
+    list of (x, x8, sx) or an act_array."""
+    arr = sets if isinstance(sets, ctypes.Array) else act_array(sets)
+    _check(load().qmv_quantize_act_many(arr, len(arr), _stream(stream)), "qmv_quantize_act_many")
+    return arr
 
 
 class Problem:

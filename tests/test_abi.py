@@ -79,6 +79,19 @@ def test_host_validation_errors(lib):
     assert lib.qmv_pack_ternary(_fake(64), 2, 4, float("inf"), _fake(4096), _fake(8192), None, None, s) == qmv.QMV_EVALUE
     # int8 K limit keeps every dot inside int32
     assert lib.qmv_pack_int8(_fake(64), 2, 70000, _fake(4096), _fake(8192), None, s) == qmv.QMV_ESHAPE
+    # several activation sets in one launch
+    acts = (qmv.qmv_act * 9)()
+    for i in range(9):
+        acts[i] = qmv.qmv_act(4096, 2, 64, 8192, 12288)
+    assert lib.qmv_quantize_act_many(None, 1, s) == qmv.QMV_EINVAL
+    assert lib.qmv_quantize_act_many(acts, 0, s) == qmv.QMV_ESHAPE
+    assert lib.qmv_quantize_act_many(acts, 9, s) == qmv.QMV_ESHAPE
+    acts[1].sx = None
+    assert lib.qmv_quantize_act_many(acts, 2, s) == qmv.QMV_EINVAL
+    acts[1].sx, acts[1].k = 12288, 0
+    assert lib.qmv_quantize_act_many(acts, 2, s) == qmv.QMV_ESHAPE
+    acts[1].k, acts[1].m = 64, 1 << 31
+    assert lib.qmv_quantize_act_many(acts, 2, s) == qmv.QMV_ESHAPE
     # group-scaled int8: nulls, shapes, alignment
     assert lib.qmv_pack_int8_grouped(_fake(64), 2, 300, _fake(4096), None, None, s) == qmv.QMV_EINVAL
     assert lib.qmv_pack_int8_grouped(_fake(64), 2, 70000, _fake(4096), _fake(8192), None, s) == qmv.QMV_ESHAPE

@@ -84,8 +84,7 @@ def _check_packed(st, config_id):
 
 def _run_decode_step(st, stream):
     from ternary_matvec_amd import qmv
-    for k in st.x:
-        qmv.qmv_quantize_act(st.x[k], x8=st.x8[k], sx=st.sx[k], stream=stream)
+    qmv.qmv_quantize_act_many(st.acts, stream=stream)   # the bench's one launch for both widths
     qmv.qmv_gemv(st.arrays[0], workspace=st.workspaces[0], flags=qmv.QMV_F_TABLE_READY, stream=stream)
     torch.cuda.synchronize()
 
@@ -139,8 +138,7 @@ def test_fullsize_gemma_prefill_512(gemma_stack):
     stream = torch.cuda.current_stream()
     for y in ps.y.values():
         y.fill_(float("nan"))
-    for k in ps.x:
-        qmv.qmv_quantize_act(ps.x[k], x8=ps.x8[k], sx=ps.sx[k], stream=stream)
+    qmv.qmv_quantize_act_many(ps.acts, stream=stream)
     qmv.qmv_gemm_prefill(ps.arr, workspace=ps.ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
     torch.cuda.synchronize()
     x8, sx = {}, {}

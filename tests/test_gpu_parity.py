@@ -55,6 +55,26 @@ def test_quantize_act_bit_exact(qmv_gpu, m, k):
     np.testing.assert_array_equal(x8.cpu().numpy(), q_ref)
 
 
+def test_quantize_act_many_bit_exact_and_equal_to_single_calls(qmv_gpu):
+    from ternary_matvec_amd import qmv
+    say("quantize_act_many: 4 sets of different widths in one launch")
+    shapes = [(130, 1152), (26, 6912), (1, 7), (3, 1537)]
+    xs = [_x_for(1500 + i, m, k, std=1.5 + i) for i, (m, k) in enumerate(shapes)]
+    xs[0][5, :] = 0.0
+    xd = [_t(x) for x in xs]
+    outs = [(torch.full((m, k), 77, dtype=torch.int8, device=DEV), torch.zeros(m, dtype=torch.float32, device=DEV))
+            for (m, k) in shapes]
+    qmv.qmv_quantize_act_many([(x, o[0], o[1]) for x, o in zip(xd, outs)])
+    torch.cuda.synchronize()
+    for x, x_d, (x8, sx) in zip(xs, xd, outs):
+        q_ref, s_ref = oracle.quantize_rows(x)
+        np.testing.assert_array_equal(x8.cpu().numpy(), q_ref)
+        np.testing.assert_array_equal(sx.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+        x8s, sxs = qmv.qmv_quantize_act(x_d)
+        torch.cuda.synchronize()
+        assert torch.equal(x8s, x8) and torch.equal(sxs.view(torch.int32), sx.view(torch.int32))
+
+
 def test_quantize_act_unaligned_rows(qmv_gpu):
     from ternary_matvec_amd import qmv
     say("quantize_act unaligned")
