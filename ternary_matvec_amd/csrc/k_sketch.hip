@@ -3,12 +3,13 @@
 // the output layer became the bottleneck", the sketch head's three steps).
 //
 // Per token:
-//  1. k_sketch_plan (one workgroup): the hidden dimensions ranked by |x|
-//     (descending, ties to the lower index); the first T = min(32, k) are
-//     scored exactly, the rest are cut into 4 consecutive rank groups, each
-//     weighted by c * mean |x| (c = mean |w| of the table, computed when the
-//     sketch is built).  Group bit masks and the sign bits of x go to the
-//     workspace; the candidate histogram and the pick are cleared.
+//  1. k_sketch_rank (many workgroups) ranks the hidden dimensions by |x|
+//     (descending, ties to the lower index) by counting larger keys; then
+//     k_sketch_plan (one workgroup) takes the first T = min(32, k) as the
+//     exactly scored ones and cuts the rest into 4 consecutive rank groups,
+//     each weighted by c * mean |x| (c = mean |w| of the table, computed when
+//     the sketch is built).  Group bit masks and the sign bits of x go to the
+//     workspace; the candidate histograms are cleared.
 //  2. k_sketch_score (a thread per row): a = 0; a = fma(w[r][d_j], x[d_j], a)
 //     over the exact dimensions in rank order, read from a dimension-major
 //     copy of the table; then per group a = fma(weight_g, agreement_g, a),
@@ -16,11 +17,11 @@
 //     from the 1-bit table (one XOR, then AND + bit count per group, 32
 //     dimensions per word).  The fp32 score's order key goes to the
 //     workspace and into a histogram of its top 12 bits.
-//  3. k_sketch_rescore: every workgroup finds the lowest bin b* such that the
-//     bins from b* up hold at least min(1024, v) words; the words in those
-//     bins are the candidates.  A wave scores each candidate exactly (fp32,
-//     like k_lmhead) and the largest (logit, lowest index) wins through one
-//     64-bit atomic maximum; the last workgroup writes the result.
+//  3. k_sketch_select finds the lowest bin b* such that the bins from b* up
+//     hold at least min(1024, v) words; the words in those bins are the
+//     candidates.  k_sketch_rescore scores each candidate exactly (a wave per
+//     candidate, fp32 like k_lmhead) and keeps each workgroup's best (logit,
+//     lowest index); k_sketch_final takes the first maximum over them.
 // The score arithmetic is fixed (fp32 FMAs in the order above), so the
 // candidate set is exactly the one the oracle computes.
 #include "qmv_internal.hpp"
@@ -168,86 +169,54 @@ __global__ __launch_bounds__(kBlock) void k_sketch_transpose(const uint16_t* __r
 
 // ---- per token ----------------------------------------------------------------------------
 
-// Bitonic sort of P = 1024 M keys, descending, by the plan's 1024 threads:
-// thread t holds elements M t .. M t + M - 1 in registers.  A stage with
-// stride s pairs element e with e ^ s: inside the thread when s < M, with
-// lane t ^ (s / M) of the same wave when s / M < 64 (register shuffles, no
-// barrier), else through LDS (`key`) between two workgroup barriers.  The
-// sorted keys are left in `key`.
-template <int M>
-__device__ __forceinline__ void sort_keys_desc(uint64_t* key, int tid)
+// |x| order key of dimension i: |x| bits above the inverted index, so keys are
+// distinct, larger |x| ranks first and equal |x| go to the lower index.
+__device__ __forceinline__ uint64_t order_key_of(const float* x, int i)
 {
-    constexpr int P = 1024 * M;
-    uint64_t kk[M];
-#pragma unroll
-    for (int j = 0; j < M; ++j) kk[j] = key[M * tid + j];
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (stride < M) {
-#pragma unroll
-                for (int j = 0; j < M; ++j) {
-                    if (j & stride) continue;
-                    const int e = M * tid + j;
-                    const bool desc = (e & size) == 0;
-                    const uint64_t a = kk[j], b = kk[j | stride];
-                    if ((a < b) == desc) {
-                        kk[j] = b;
-                        kk[j | stride] = a;
-                    }
-                }
-            } else if (stride / M < kWave) {
-                const int d = stride / M;
-                const bool lo = (tid & d) == 0;
-#pragma unroll
-                for (int j = 0; j < M; ++j) {
-                    const uint64_t other = __shfl_xor(kk[j], d);
-                    const bool desc = ((M * tid + j) & size) == 0;
-                    const bool keep_max = lo == desc;
-                    kk[j] = keep_max ? (kk[j] > other ? kk[j] : other) : (kk[j] < other ? kk[j] : other);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < M; ++j) key[M * tid + j] = kk[j];
-                __syncthreads();
-                const bool lo = ((M * tid) & stride) == 0;
-#pragma unroll
-                for (int j = 0; j < M; ++j) {
-                    const int e = M * tid + j;
-                    const uint64_t other = key[e ^ stride];
-                    const bool desc = (e & size) == 0;
-                    const bool keep_max = lo == desc;
-                    kk[j] = keep_max ? (kk[j] > other ? kk[j] : other) : (kk[j] < other ? kk[j] : other);
-                }
-                __syncthreads();
-            }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < M; ++j) key[M * tid + j] = kk[j];
-    __syncthreads();
+    return ((uint64_t)__float_as_uint(fabsf(x[i])) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
 }
 
-// One workgroup of 1024 threads; dynamic LDS: the sort keys (P = the larger
-// of 1024 and the power of two >= k, 8 bytes each) then the masks and x sign
-// words (5 * kw words).
-__global__ __launch_bounds__(kSkPlanThreads) void k_sketch_plan(const float* __restrict__ x, int k, int p2,
+// Ranks by counting, spread over many compute units: workgroup b places keys
+// 16b .. 16b+15, each compared with every key by 16 threads (a sixteenth of the
+// keys each); the rank is the number of larger keys, and the key is written at
+// its rank, so `sorted` ends up in descending order.
+constexpr int kSkRankPer = 16;
+__global__ __launch_bounds__(kBlock) void k_sketch_rank(const float* __restrict__ x, int k,
+                                                        uint64_t* __restrict__ sorted)
+{
+    __shared__ uint64_t key[kSketchMaxK];
+    __shared__ uint32_t cnt[kSkRankPer];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < k; i += kBlock) key[i] = order_key_of(x, i);
+    if (tid < kSkRankPer) cnt[tid] = 0u;
+    __syncthreads();
+    const int e = blockIdx.x * kSkRankPer + (tid % kSkRankPer);
+    const int part = tid / kSkRankPer;
+    if (e < k) {
+        const uint64_t me = key[e];
+        uint32_t c = 0;
+        for (int j = part; j < k; j += kBlock / kSkRankPer) c += key[j] > me ? 1u : 0u;
+        atomicAdd(&cnt[tid % kSkRankPer], c);
+    }
+    __syncthreads();
+    if (tid < kSkRankPer && e < k) sorted[cnt[tid]] = key[e];
+}
+
+// One workgroup of 1024 threads; dynamic LDS: the k order keys in descending
+// order (from k_sketch_rank) then the masks and x sign words (5 * kw words).
+__global__ __launch_bounds__(kSkPlanThreads) void k_sketch_plan(const float* __restrict__ x, int k,
+                                                                const uint64_t* __restrict__ sorted,
                                                                 const SketchHeader* __restrict__ hdr,
                                                                 uint8_t* __restrict__ ws)
 {
     extern __shared__ __align__(16) uint8_t sm[];
     uint64_t* key = reinterpret_cast<uint64_t*>(sm);
     const int kw = (k + 31) >> 5;
-    uint32_t* mbits = reinterpret_cast<uint32_t*>(sm + 8 * (size_t)p2);   // [5][kw]: masks, then x signs
+    uint32_t* mbits = reinterpret_cast<uint32_t*>(sm + 8 * (size_t)k);   // [5][kw]: masks, then x signs
     const int tid = threadIdx.x;
-    // |x| ranks: key = |x| bits << 32 | (~index); padding keys are 0 and sort last
-    for (int i = tid; i < p2; i += kSkPlanThreads)
-        key[i] = i < k ? ((uint64_t)__float_as_uint(fabsf(x[i])) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i) : 0ull;
+    for (int i = tid; i < k; i += kSkPlanThreads) key[i] = sorted[i];
     for (int i = tid; i < 5 * kw; i += kSkPlanThreads) mbits[i] = 0u;
     __syncthreads();
-    if (p2 == 1024) sort_keys_desc<1>(key, tid);
-    else if (p2 == 2048) sort_keys_desc<2>(key, tid);
-    else if (p2 == 4096) sort_keys_desc<4>(key, tid);
-    else sort_keys_desc<8>(key, tid);
     SketchPlan* plan = reinterpret_cast<SketchPlan*>(ws);
     const int t = min(k, kSkTop);
     const int rest = k - t, base = rest / kSkGroups;
@@ -533,7 +502,9 @@ int64_t sketch_bytes(int64_t v, int64_t k)
     return 256 + sk_round(4 * kw * v, 256) + sketch_copy_bytes(v, k);
 }
 
-int64_t sketch_workspace_bytes(int64_t v) { return kSkKeysOff + sk_round(4 * v, 256); }
+// [plan][histograms][pick][per-workgroup bests][row keys: 4 v][sorted |x| keys: 8 * kSketchMaxK]
+int64_t sketch_sorted_off(int64_t v) { return kSkKeysOff + sk_round(4 * v, 256); }
+int64_t sketch_workspace_bytes(int64_t v) { return sketch_sorted_off(v) + 8 * kSketchMaxK; }
 
 hipError_t launch_sketch_build(const uint16_t* w, int64_t v, int64_t k, void* sketch, hipStream_t s)
 {
@@ -566,14 +537,17 @@ hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const flo
     const uint32_t* signs = reinterpret_cast<const uint32_t*>(base + 256);
     const uint16_t* wt = reinterpret_cast<const uint16_t*>(base + 256 + sk_round(4 * kw * v, 256));
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    int p2 = 1024;
-    while (p2 < k) p2 <<= 1;
-    const size_t plan_lds = 8 * (size_t)p2 + 20 * (size_t)kw;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_plan),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan_lds);
+    uint64_t* sorted = reinterpret_cast<uint64_t*>(ws + sketch_sorted_off(v));
+    hipLaunchKernelGGL(k_sketch_rank, dim3((unsigned)((k + kSkRankPer - 1) / kSkRankPer)), dim3(kBlock), 0, s, x,
+                       (int)k, sorted);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sketch_plan, dim3(1), dim3(kSkPlanThreads), plan_lds, s, x, (int)k, p2,
-                       reinterpret_cast<const SketchHeader*>(base), ws);
+    const size_t plan_lds = 8 * (size_t)k + 20 * (size_t)kw;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_plan), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)plan_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_sketch_plan, dim3(1), dim3(kSkPlanThreads), plan_lds, s, x, (int)k,
+                       (const uint64_t*)sorted, reinterpret_cast<const SketchHeader*>(base), ws);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_sketch_score, dim3((unsigned)((v + kSkScoreThreads - 1) / kSkScoreThreads)),
