@@ -146,8 +146,11 @@ class DecodeStack:
 
 
 def time_decode(stack, steps, warmup, stream):
-    """Whole steps (quantise + grouped GEMV) timed with events; the GEMV launch
-    of every timed step is bracketed by its own pair of events."""
+    """Whole steps (quantise + grouped GEMV): K steps timed between two events
+    with nothing else in the stream, then K more with the GEMV launch of every
+    step bracketed by its own pair of events (its duration; event records between
+    launches add a few microseconds of their own, so they stay out of the step
+    time)."""
     import torch
     from ternary_matvec_amd import qmv
 
@@ -162,19 +165,21 @@ def time_decode(stack, steps, warmup, stream):
 
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
     for i in range(steps):
-        step(i, evs[i])
+        step(i)
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     step_ms = t0.elapsed_time(t1) / steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     gemv_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     return step_ms, gemv_ms, wall
 
