@@ -48,11 +48,41 @@ __device__ __forceinline__ int8_t quantize_one(float v, float s)
 // ---------------------------------------------------------------------------
 // Per-row quantisation: one workgroup per row.
 // ---------------------------------------------------------------------------
+// Rows of up to 256 * 4 * kRegVec values that are 16-byte aligned (in) and
+// 4-byte aligned (out) are read once: the values stay in registers between
+// the maximum and the quantisation.
+constexpr int kRegVec = 8;
+
 __device__ __forceinline__ void quantize_row(const float* __restrict__ xr, int64_t k, int8_t* __restrict__ qr,
                                              float* __restrict__ sx_out, float* red)
 {
     float m = 0.0f;
     const bool vec = ((reinterpret_cast<uintptr_t>(xr) & 15) == 0);
+    if (vec && (k & 3) == 0 && k <= 4 * kBlock * kRegVec && (reinterpret_cast<uintptr_t>(qr) & 3) == 0) {
+        const float4* x4 = reinterpret_cast<const float4*>(xr);
+        const int n4 = (int)(k >> 2);
+        float4 v[kRegVec];
+#pragma unroll
+        for (int j = 0; j < kRegVec; ++j) {
+            const int i = (int)threadIdx.x + kBlock * j;
+            v[j] = i < n4 ? x4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+        }
+        m = block_max(m, red);
+        const float s = scale_from_max(m);
+        if (threadIdx.x == 0) *sx_out = s;
+        uint32_t* q4 = reinterpret_cast<uint32_t*>(qr);
+#pragma unroll
+        for (int j = 0; j < kRegVec; ++j) {
+            const int i = (int)threadIdx.x + kBlock * j;
+            if (i < n4) {
+                uint32_t b0 = (uint8_t)quantize_one(v[j].x, s), b1 = (uint8_t)quantize_one(v[j].y, s);
+                uint32_t b2 = (uint8_t)quantize_one(v[j].z, s), b3 = (uint8_t)quantize_one(v[j].w, s);
+                q4[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+            }
+        }
+        return;
+    }
     int64_t head = vec ? (k & ~int64_t(3)) : 0;
     if (vec) {
         const float4* x4 = reinterpret_cast<const float4*>(xr);
