@@ -106,8 +106,34 @@ __global__ __launch_bounds__(kBlock) void k_gemv_grouped(const DevProblem* __res
     uint8_t* xs = smem;
     float* sxs = reinterpret_cast<float*>(smem + (size_t)m * kp);
 
-    // ---- stage: x8 rows (k bytes each, any alignment) as dwords, zero past k
     const int tid = threadIdx.x;
+    const int s = tid & (pl - 1);
+    const int row = rb * (kBlock >> lshift) + (tid >> lshift);
+    const bool live = row < n;
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)P->w, (short)0, (int)((uint32_t)n * stride), (int)kRsrcWord3);
+    const float* swr = P->sw + (size_t)(live ? row : 0) * gn;
+    const uint32_t roff = (uint32_t)(live ? row : 0) * stride;
+    uint4 wlo[kGBatch], whi[kGBatch];
+    float wsc[kGBatch];
+    // one batch of the lane's groups: its weights and weight scales
+    auto load_batch = [&](int h0) {
+#pragma unroll
+        for (int b = 0; b < kGBatch; ++b) {
+            const int h = h0 + b * pl;
+            if (b == 0 || h < hn) {
+                const uint32_t o = roff + 32u * (uint32_t)h;
+                wlo[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, 0));
+                whi[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, o + 16, 0, 0));
+                wsc[b] = gload_ptr(swr)[h < hn ? h >> 2 : 0];
+            }
+        }
+    };
+    // the first batch goes out before the activations are staged, so the
+    // staging round trip overlaps the weight stream
+    if (live && s < hn) load_batch(s);
+
+    // ---- stage: x8 rows (k bytes each, any alignment) as dwords, zero past k
     for (int mi = 0; mi < m; ++mi) {
         const uintptr_t a = reinterpret_cast<uintptr_t>(x8) + (uintptr_t)mi * (uintptr_t)k;
         const uint32_t sh = (uint32_t)(a & 3);
@@ -125,30 +151,13 @@ __global__ __launch_bounds__(kBlock) void k_gemv_grouped(const DevProblem* __res
     }
     for (int i = tid; i < m * hn; i += kBlock) sxs[i] = gload_ptr(sx)[i];
     __syncthreads();
+    if (!live) return;   // no barrier follows
 
-    const int s = tid & (pl - 1);
-    const int row = rb * (kBlock >> lshift) + (tid >> lshift);
-    if (row >= n) return;   // no barrier follows
-    const __amdgpu_buffer_rsrc_t wr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)P->w, (short)0, (int)((uint32_t)n * stride), (int)kRsrcWord3);
-    const float* swr = P->sw + (size_t)row * gn;
-    const uint32_t roff = (uint32_t)row * stride;
     float acc[MT];
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) acc[mi] = 0.0f;
     for (int h0 = s; h0 < hn; h0 += kGBatch * pl) {
-        uint4 wlo[kGBatch], whi[kGBatch];
-        float wsc[kGBatch];
-#pragma unroll
-        for (int b = 0; b < kGBatch; ++b) {
-            const int h = h0 + b * pl;
-            if (b == 0 || h < hn) {
-                const uint32_t o = roff + 32u * (uint32_t)h;
-                wlo[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, 0));
-                whi[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, o + 16, 0, 0));
-                wsc[b] = gload_ptr(swr)[h >> 2];
-            }
-        }
+        if (h0 != s) load_batch(h0);
 #pragma unroll
         for (int b = 0; b < kGBatch; ++b) {
             const int h = h0 + b * pl;
