@@ -93,28 +93,44 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
         }
         __syncthreads();
     }
-    for (int q = tid; q < m * dw_per_tok; q += kBlock) {
-        const int mi = q / dw_per_tok;
-        const int d = q - mi * dw_per_tok;
-        const QMV_GLOBAL int8_t* xr = gload_ptr(P->x8) + (size_t)mi * k;
-        uint32_t v = 0;
-        if (WT == 1) {
-            const int c = d / 20;
-            const int r = d - c * 20;
-            const int i = r >> 2, wd = r & 3;
-            const int col0 = 80 * c + 20 * wd + i;
+    if (WT == 1) {
+        // one 20-column unit (packed dword w of chunk c, u = 4c + w) per step: its
+        // aligned dwords loaded with a funnel shift (rows may start anywhere),
+        // bytes past k cleared, then regrouped into the five planes
+        const int units = 4 * C;
+        for (int q = tid; q < m * units; q += kBlock) {
+            const int mi = q / units;
+            const int u = q - mi * units;
+            const uintptr_t a = reinterpret_cast<uintptr_t>(P->x8) + (uintptr_t)mi * (uintptr_t)k;
+            const uint32_t sh = (uint32_t)(a & 3);
+            const uint32_t words = (sh + (uint32_t)k + 3u) >> 2;
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)(a & ~(uintptr_t)3), (short)0, (int)(4 * words), (int)0x00020000);
+            uint32_t raw[6], nat[5], pl[5];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int col = col0 + 5 * b;
-                const uint32_t byte = (col < k) ? (uint32_t)(uint8_t)xr[col] : 0u;
-                v |= byte << (8 * b);
+            for (int j = 0; j < 6; ++j) raw[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * (5 * u + j), 0, 0);
+            int sum = 0;
+#pragma unroll
+            for (int j = 0; j < 5; ++j) {
+                const uint32_t v = __builtin_amdgcn_alignbyte(raw[j + 1], raw[j], sh);
+                const int valid = k - 4 * (5 * u + j);
+                nat[j] = valid >= 4 ? v : valid <= 0 ? 0u : v & ((1u << (8 * valid)) - 1u);
+                sum = dot4(nat[j], 0x01010101u, sum);
             }
-            const int s = dot4(v, 0x01010101u, 0);
-            if (s) {
-                atomicAdd(&s_sum[mi], s);
-                if (i == 0) atomicAdd(&s_sum0[mi], s);
-            }
-        } else {
+            reorder20(nat[0], nat[1], nat[2], nat[3], nat[4], pl);
+            const int c = u >> 2, wd = u & 3;
+#pragma unroll
+            for (int i = 0; i < 5; ++i) xs[mi * dw_per_tok + 20 * c + 4 * i + wd] = pl[i];
+            if (sum) atomicAdd(&s_sum[mi], sum);
+            const int s0 = dot4(pl[0], 0x01010101u, 0);
+            if (s0) atomicAdd(&s_sum0[mi], s0);
+        }
+    } else {
+        for (int q = tid; q < m * dw_per_tok; q += kBlock) {
+            const int mi = q / dw_per_tok;
+            const int d = q - mi * dw_per_tok;
+            const QMV_GLOBAL int8_t* xr = gload_ptr(P->x8) + (size_t)mi * k;
+            uint32_t v = 0;
             const int col0 = 4 * d;
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
@@ -122,8 +138,8 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
                 const uint32_t byte = (col < k) ? (uint32_t)(uint8_t)xr[col] : 0u;
                 v |= byte << (8 * b);
             }
+            xs[q] = v;
         }
-        xs[q] = v;
     }
     __syncthreads();
 
