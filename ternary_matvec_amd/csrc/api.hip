@@ -284,7 +284,7 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
         } else {
             if (gemv_lds_bytes(wt, t.max_m[wt], t.max_chunks[wt]) > kMaxLds) return QMV_ESHAPE;
             for (size_t i = 0; i < sp.size(); ++i) {
-                const int64_t nt = rows_tiles(sp[i]->w.n, kRowsPerTile);
+                const int64_t nt = rows_tiles(sp[i]->w.n, gemv_rows_per_tile(wt, t.max_m[wt]));
                 for (int64_t r = 0; r < nt; ++r) words[wt].push_back(((uint32_t)slots[i] << kTileRowBits) | (uint32_t)r);
             }
             t.count[wt] = (int32_t)words[wt].size();

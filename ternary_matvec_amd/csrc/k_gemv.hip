@@ -48,10 +48,20 @@ constexpr int kBatch = 4;  // chunks in flight per lane
 // faster, so the quotient form stays below 8.
 constexpr int kDigitMT = 8;
 
+// Rows per lane: from kDigitMT tokens on each lane takes two rows (64 apart),
+// so every activation read from LDS serves both; a tile is then 128 rows.
+template <int MT, int WT>
+constexpr int rows_per_lane()
+{
+    return (WT == 1 && MT >= kDigitMT) ? 2 : 1;
+}
+
 template <int MT, int WT>
 __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ probs,
                                                 const uint32_t* __restrict__ tiles, int32_t tile_base)
 {
+    constexpr int RPL = rows_per_lane<MT, WT>();
+    constexpr int kB = RPL == 1 ? kBatch : kBatch / 2;   // chunks in flight per row
     extern __shared__ __align__(16) uint8_t smem[];
     __shared__ int s_sum[MT];
     __shared__ int s_sum0[MT];
@@ -64,8 +74,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
     const DevProblem* P = probs + (te >> kTileRowBits);
     const int rb = (int)(te & ((1u << kTileRowBits) - 1));
     const int n = P->n, k = P->k, m = P->m, C = P->chunks;
-    const int row = rb * kRowsPerTile + lane;
-    const bool live = row < n;
+    const int row = rb * kRowsPerTile * RPL + lane;   // + 64 h for row h of the lane
 
     const int per = (C + 3) >> 2;
     const int c_lo = min(C, wave * per);
@@ -73,14 +82,19 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
 
     const QMV_GLOBAL v4u32* wp = gload_ptr(reinterpret_cast<const v4u32*>(P->w)) + row;
     const size_t cstride = (size_t)n;
+    bool live[RPL];
+#pragma unroll
+    for (int h = 0; h < RPL; ++h) live[h] = row + kWave * h < n;
 
     // Issue the first weight loads before staging the activations.
-    v4u32 buf[kBatch];
+    v4u32 buf[kB][RPL];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int c = c_lo + u;
-        buf[u] = (live && c < c_hi) ? wp[(size_t)c * cstride] : v4u32{0u, 0u, 0u, 0u};
-    }
+    for (int u = 0; u < kB; ++u)
+#pragma unroll
+        for (int h = 0; h < RPL; ++h) {
+            const int c = c_lo + u;
+            buf[u][h] = (live[h] && c < c_hi) ? wp[(size_t)c * cstride + kWave * h] : v4u32{0u, 0u, 0u, 0u};
+        }
 
     // ---- stage activations in LDS ------------------------------------------
     constexpr int kXBytesPerChunk = (WT == 1) ? 80 : 16;
@@ -144,68 +158,76 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
     __syncthreads();
 
     // ---- stream the wave's chunks --------------------------------------------
-    int acc_a[MT], acc_b[MT];
+    int acc_a[RPL][MT], acc_b[MT];
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
-        acc_a[mi] = 0;
+#pragma unroll
+        for (int h = 0; h < RPL; ++h) acc_a[h][mi] = 0;
         acc_b[mi] = 0;
     }
     const uint4* xs4 = reinterpret_cast<const uint4*>(smem);
     const int x4_per_tok = dw_per_tok / 4;
 
-    for (int c0 = c_lo; c0 < c_hi; c0 += kBatch) {
-        v4u32 nxt[kBatch];
+    for (int c0 = c_lo; c0 < c_hi; c0 += kB) {
+        v4u32 nxt[kB][RPL];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-            const int c = c0 + kBatch + u;
-            nxt[u] = (live && c < c_hi) ? wp[(size_t)c * cstride] : v4u32{0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < kB; ++u)
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
+            for (int h = 0; h < RPL; ++h) {
+                const int c = c0 + kB + u;
+                nxt[u][h] = (live[h] && c < c_hi) ? wp[(size_t)c * cstride + kWave * h] : v4u32{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+        for (int u = 0; u < kB; ++u) {
             const int c = c0 + u;
             if (c < c_hi) {
                 if (WT == 1 && MT >= kDigitMT) {
                     // digit planes D_i = Q_i - 3 Q_(i+1), Q_i = floor(b / 3^i) bytewise
                     // (each byte's result is 0..2 and 3 Q_(i+1) <= Q_i, so no byte borrows
                     // or carries), then 5 dot products per token
-                    uint32_t D[4][5];
+                    uint32_t D[RPL][4][5];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const uint32_t w = sel(buf[u], j);
-                        const Planes q = unpack(w);
-                        D[j][0] = w - (q.p4 + (q.p4 << 1));
-                        D[j][1] = q.p4 - (q.p3 + (q.p3 << 1));
-                        D[j][2] = q.p3 - (q.p2 + (q.p2 << 1));
-                        D[j][3] = q.p2 - (q.p1 + (q.p1 << 1));
-                        D[j][4] = q.p1;
-                    }
+                    for (int h = 0; h < RPL; ++h)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const uint32_t w = sel(buf[u][h], j);
+                            const Planes q = unpack(w);
+                            D[h][j][0] = w - (q.p4 + (q.p4 << 1));
+                            D[h][j][1] = q.p4 - (q.p3 + (q.p3 << 1));
+                            D[h][j][2] = q.p3 - (q.p2 + (q.p2 << 1));
+                            D[h][j][3] = q.p2 - (q.p1 + (q.p1 << 1));
+                            D[h][j][4] = q.p1;
+                        }
 #pragma unroll
                     for (int mi = 0; mi < MT; ++mi) {
                         if (mi < m) {
                             const uint4* xq = xs4 + mi * x4_per_tok + 5 * c;
                             const uint4 X0 = xq[0], X1 = xq[1], X2 = xq[2], X3 = xq[3], X4 = xq[4];
-                            int a = acc_a[mi];
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                                a = dot4(D[j][0], sel(X0, j), a);
-                                a = dot4(D[j][1], sel(X1, j), a);
-                                a = dot4(D[j][2], sel(X2, j), a);
-                                a = dot4(D[j][3], sel(X3, j), a);
-                                a = dot4(D[j][4], sel(X4, j), a);
+                            for (int h = 0; h < RPL; ++h) {
+                                int a = acc_a[h][mi];
+#pragma unroll
+                                for (int j = 0; j < 4; ++j) {
+                                    a = dot4(D[h][j][0], sel(X0, j), a);
+                                    a = dot4(D[h][j][1], sel(X1, j), a);
+                                    a = dot4(D[h][j][2], sel(X2, j), a);
+                                    a = dot4(D[h][j][3], sel(X3, j), a);
+                                    a = dot4(D[h][j][4], sel(X4, j), a);
+                                }
+                                acc_a[h][mi] = a;
                             }
-                            acc_a[mi] = a;
                         }
                     }
                 } else if (WT == 1) {
                     Planes pl[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) pl[j] = unpack(sel(buf[u], j));
+                    for (int j = 0; j < 4; ++j) pl[j] = unpack(sel(buf[u][0], j));
 #pragma unroll
                     for (int mi = 0; mi < MT; ++mi) {
                         if (mi < m) {
                             const uint4* xq = xs4 + mi * x4_per_tok + 5 * c;
                             const uint4 X0 = xq[0], X1 = xq[1], X2 = xq[2], X3 = xq[3], X4 = xq[4];
-                            int a = acc_a[mi], b = acc_b[mi];
+                            int a = acc_a[0][mi], b = acc_b[mi];
 #pragma unroll
                             for (int j = 0; j < 4; ++j) {
                                 const uint32_t x0 = sel(X0, j), x1 = sel(X1, j), x2 = sel(X2, j);
@@ -220,7 +242,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
                                 b = dot4(pl[j].p3, x1, b);
                                 b = dot4(pl[j].p4, x0, b);
                             }
-                            acc_a[mi] = a;
+                            acc_a[0][mi] = a;
                             acc_b[mi] = b;
                         }
                     }
@@ -229,54 +251,64 @@ __global__ __launch_bounds__(kBlock) void k_gemv(const DevProblem* __restrict__ 
                     for (int mi = 0; mi < MT; ++mi) {
                         if (mi < m) {
                             const uint4 X = xs4[mi * x4_per_tok + c];
-                            int a = acc_a[mi];
-                            a = dot4(buf[u][0], X.x, a);
-                            a = dot4(buf[u][1], X.y, a);
-                            a = dot4(buf[u][2], X.z, a);
-                            a = dot4(buf[u][3], X.w, a);
-                            acc_a[mi] = a;
+                            int a = acc_a[0][mi];
+                            a = dot4(buf[u][0][0], X.x, a);
+                            a = dot4(buf[u][0][1], X.y, a);
+                            a = dot4(buf[u][0][2], X.z, a);
+                            a = dot4(buf[u][0][3], X.w, a);
+                            acc_a[0][mi] = a;
                         }
                     }
                 }
             }
         }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) buf[u] = nxt[u];
+        for (int u = 0; u < kB; ++u)
+#pragma unroll
+            for (int h = 0; h < RPL; ++h) buf[u][h] = nxt[u][h];
     }
 
     // ---- combine the four waves and write ------------------------------------
+    // per row of the lane: the a sums of waves 1..3 (and b of the quotient form)
     int* red = reinterpret_cast<int*>(smem + (size_t)MT * dw_per_tok * 4);
+    constexpr int kParts = RPL + 1;   // a per row, then b
     if (wave > 0) {
 #pragma unroll
         for (int mi = 0; mi < MT; ++mi) {
-            red[((wave - 1) * MT + mi) * 2 * kWave + lane] = acc_a[mi];
-            red[((wave - 1) * MT + mi) * 2 * kWave + kWave + lane] = acc_b[mi];
+#pragma unroll
+            for (int h = 0; h < RPL; ++h) red[(((wave - 1) * MT + mi) * kParts + h) * kWave + lane] = acc_a[h][mi];
+            red[(((wave - 1) * MT + mi) * kParts + RPL) * kWave + lane] = acc_b[mi];
         }
     }
     __syncthreads();
-    if (wave == 0 && live) {
+    if (wave == 0) {
         const float sw = *gload_ptr(P->sw);
 #pragma unroll
-        for (int mi = 0; mi < MT; ++mi) {
-            if (mi < m) {
-                int a = acc_a[mi], b = acc_b[mi];
+        for (int h = 0; h < RPL; ++h) {
+            const int r = row + kWave * h;
+            if (!live[h]) continue;
 #pragma unroll
-                for (int w = 0; w < 3; ++w) {
-                    a += red[(w * MT + mi) * 2 * kWave + lane];
-                    b += red[(w * MT + mi) * 2 * kWave + kWave + lane];
+            for (int mi = 0; mi < MT; ++mi) {
+                if (mi < m) {
+                    int a = acc_a[h][mi], b = acc_b[mi];
+#pragma unroll
+                    for (int w = 0; w < 3; ++w) {
+                        a += red[((w * MT + mi) * kParts + h) * kWave + lane];
+                        b += red[((w * MT + mi) * kParts + RPL) * kWave + lane];
+                    }
+                    int total;
+                    if (WT == 1 && MT >= kDigitMT) {
+                        total = (int)((uint32_t)a - (uint32_t)s_sum[mi]);   // digits are t + 1
+                    } else if (WT == 1) {
+                        total = (int)((uint32_t)a + 128u * (uint32_t)s_sum0[mi] - 3u * (uint32_t)b -
+                                      (uint32_t)s_sum[mi]);
+                    } else {
+                        total = a;
+                    }
+                    const size_t o = (size_t)mi * n + r;
+                    gstore_ptr(P->y)[o] = (float)total * gload_ptr(P->sx)[mi] * sw;
+                    if (P->acc) gstore_ptr(P->acc)[o] = total;
                 }
-                int total;
-                if (WT == 1 && MT >= kDigitMT) {
-                    total = (int)((uint32_t)a - (uint32_t)s_sum[mi]);   // digits are t + 1
-                } else if (WT == 1) {
-                    total = (int)((uint32_t)a + 128u * (uint32_t)s_sum0[mi] - 3u * (uint32_t)b -
-                                  (uint32_t)s_sum[mi]);
-                } else {
-                    total = a;
-                }
-                const size_t o = (size_t)mi * n + row;
-                gstore_ptr(P->y)[o] = (float)total * gload_ptr(P->sx)[mi] * sw;
-                if (P->acc) gstore_ptr(P->acc)[o] = total;
             }
         }
     }
@@ -289,7 +321,8 @@ int mt_for(int max_m)
 
 size_t lds_bytes(int mt, int wt, int max_chunks)
 {
-    return (size_t)(wt == 1 ? 80 : 16) * max_chunks * mt + (size_t)3 * mt * 2 * kWave * 4;
+    const int rpl = (wt == 1 && mt >= kDigitMT) ? 2 : 1;
+    return (size_t)(wt == 1 ? 80 : 16) * max_chunks * mt + (size_t)3 * mt * (rpl + 1) * kWave * 4;
 }
 
 template <int MT, int WT>
@@ -319,6 +352,11 @@ hipError_t launch_wt(const DevProblem* probs, const uint32_t* tiles, int32_t til
 }
 
 }  // namespace
+
+int gemv_rows_per_tile(int wtype, int max_m)
+{
+    return kRowsPerTile * ((wtype == 1 && mt_for(max_m) >= kDigitMT) ? 2 : 1);
+}
 
 int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks)
 {
