@@ -28,7 +28,7 @@
 //    fused FMA) to 1024 + floor(v/3) for every v in 0..242, checked
 //    exhaustively.  Four chained FMAs give P_4, P_3, P_2, P_1; v_perm_b32 gathers
 //    the bytes into dot4 operands.  P_5 = b may exceed 127, so it enters as
-//    b ^ 0x80 = b - 128 and 128 * sum(X_0) is added back.  From 8 tokens on
+//    b ^ 0x80 = b - 128 and 128 * sum(X_0) is added back.  From 4 tokens on
 //    the digit planes themselves are formed once per dword instead (d_i =
 //    Q_i - 3 Q_(i+1) bytewise, Q_i = floor(b / 3^i)), so each token needs 5
 //    dot products rather than 9.  Trits are t = d - 1, so sum(x) is
@@ -41,12 +41,12 @@ namespace qmv {
 namespace {
 
 constexpr int kBatch = 4;  // chunks in flight per lane
-// From 8 tokens on, the digits of each packed dword are formed once (22 VALU)
+// From 4 tokens on, the digits of each packed dword are formed once (22 VALU)
 // and each token costs 5 dot products instead of 9 (the prefix-quotient form,
-// 15 VALU shared).  Measured on 24 BitNet-shaped layers: 5% faster at 16
-// tokens; at 4 tokens the extra registers cost a wave per SIMD and it is no
-// faster, so the quotient form stays below 8.
-constexpr int kDigitMT = 8;
+// 15 VALU shared), and each lane takes two rows (see rows_per_lane).
+// Measured on 24 BitNet-shaped layers: 4 tokens 96 -> 81 us, 16 tokens
+// 462 -> 343 us; below 4 tokens the quotient form with one row per lane stays.
+constexpr int kDigitMT = 4;
 
 // Rows per lane: from kDigitMT tokens on each lane takes two rows (64 apart),
 // so every activation read from LDS serves both; a tile is then 128 rows.

@@ -92,7 +92,7 @@ struct ActSets {
 };
 hipError_t launch_quantize_many(const ActSets& sets, int64_t rows, hipStream_t s);
 int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks);
-// Rows per tile of the workgroup GEMV (64, or 128 from 8 tokens: two rows per lane).
+// Rows per tile of the workgroup GEMV (64, or 128 from 4 tokens: two rows per lane).
 int gemv_rows_per_tile(int wtype, int max_m);
 constexpr int64_t kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
 hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
