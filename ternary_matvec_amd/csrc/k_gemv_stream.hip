@@ -58,6 +58,7 @@ constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr int kZBytes = 192;                   // staged bytes per 16-byte ternary chunk per token (4 x 12 dwords)
 constexpr int kXBytes = 16;                    // staged bytes per 16-byte int8 chunk per token
 constexpr uint32_t kEnd = 0xffffffffu;         // no tile
+constexpr int kNonTemporal = 2;                // buffer instruction cache policy: nt
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
@@ -244,7 +245,9 @@ __device__ __forceinline__ v4u32 load_step(const Tile& T, int i, uint32_t voff)
     const uint32_t nrec = (uint32_t)(T.C - c0) * T.chunk_bytes;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(T.w + (uint32_t)c0 * T.chunk_bytes), (short)0, (int)nrec, (int)kRsrcWord3);
-    return __builtin_bit_cast(v4u32, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+    // weights are read once per launch: non-temporal (aux bit 1), so they do not
+    // displace the activations and tables the caches should keep
+    return __builtin_bit_cast(v4u32, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, kNonTemporal));
 }
 
 // ---------------------------------------------------------------------------

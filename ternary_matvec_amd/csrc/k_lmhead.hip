@@ -23,6 +23,7 @@ constexpr int kIters = 4;                  // rows per group
 constexpr int kRowsPerBlock = kRowsPerIter * kIters;
 constexpr int kMaxLdsK = 16384;            // x staged in LDS up to this many columns
 constexpr int kUnroll = 8;                 // chunk loads in flight per lane
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
 
 struct Best {
     float v;
@@ -67,7 +68,10 @@ __global__ __launch_bounds__(kBlock) void k_lmhead(const uint16_t* __restrict__ 
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
                     const int c = c0 + u * kGroup;
-                    q[u] = (c < nch) ? wr[c] : make_uint4(0u, 0u, 0u, 0u);
+                    // the weights are read once: a non-temporal load
+                    q[u] = (c < nch) ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                           reinterpret_cast<const nt_u32x4*>(wr) + c))
+                                     : make_uint4(0u, 0u, 0u, 0u);
                 }
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u) {
