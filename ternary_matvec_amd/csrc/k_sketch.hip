@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
     for (; j + 8 <= t; j += 8) {
         uint16_t h[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) h[u] = wt[(int64_t)s_idx[j + u] * v + rr];
+        for (int u = 0; u < 8; ++u) h[u] = __builtin_nontemporal_load(&wt[(int64_t)s_idx[j + u] * v + rr]);   // read once per token
 #pragma unroll
         for (int u = 0; u < 8; ++u) a = fmaf(bf16f(h[u]), s_x[j + u], a);
     }
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
     for (; w + 6 <= kw; w += 6) {
         uint32_t sw6[6];
 #pragma unroll
-        for (int u = 0; u < 6; ++u) sw6[u] = signs[(int64_t)(w + u) * v + rr];
+        for (int u = 0; u < 6; ++u) sw6[u] = __builtin_nontemporal_load(&signs[(int64_t)(w + u) * v + rr]);
 #pragma unroll
         for (int u = 0; u < 6; ++u) {
             const uint32_t d = sw6[u] ^ sbits[kSkGroups * kw + w + u];
