@@ -1,7 +1,8 @@
 // k_probe.hip -- a plain read of a device buffer, the yardstick the kernels'
 // HBM rates are compared with (not part of the method: a measurement aid).
 //
-// Every byte is read once with 16-byte loads, grid-stride, two loads in flight
+// Every byte is read once with 16-byte non-temporal loads (as the weight
+// streams read), grid-stride, two loads in flight
 // per lane, 16 waves per compute unit (the configuration that read fastest on
 // this machine), and folded into one word with xor so that no load can be
 // dropped.  The result word is written only by lanes that fold to a value
@@ -24,12 +25,12 @@ __global__ __launch_bounds__(kProbeThreads) void k_read_probe(const v4u32* __res
     int64_t i = (int64_t)blockIdx.x * kProbeThreads + threadIdx.x;
     uint32_t acc = 0;
     for (; i + stride < n16; i += 2 * stride) {
-        const v4u32 a = p[i];
-        const v4u32 b = p[i + stride];
+        const v4u32 a = __builtin_nontemporal_load(p + i);
+        const v4u32 b = __builtin_nontemporal_load(p + i + stride);
         acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
     }
     if (i < n16) {
-        const v4u32 a = p[i];
+        const v4u32 a = __builtin_nontemporal_load(p + i);
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     if (acc == key) out[0] = acc;
