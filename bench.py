@@ -885,7 +885,7 @@ def main():
                      "launch_us_back_to_back": round(gemv_only_ms * 1e3, 3),
                      "measured_read_ceiling": round(ceiling_gbs, 1),
                      "frac_of_measured_ceiling": round(achieved / ceiling_gbs, 4),
-                     "ceiling_kernel": "qmv_read_probe: one 16-byte-load read of the same weight copies "
+                     "ceiling_kernel": "qmv_read_probe: one non-temporal 16-byte-load read of the same weight copies "
                                        "(%.1f MB in %.2f us)" % (stack.pool[0].numel() / 1e6, ceiling_ms * 1e3)},
     }
     log("prefill (512 tokens)")
