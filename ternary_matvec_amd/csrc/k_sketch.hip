@@ -352,14 +352,21 @@ __global__ __launch_bounds__(kSkPlanThreads) void k_sketch_select(int64_t v, uin
     for (int c = 0; c < kSkHistCopies; ++c)
 #pragma unroll
         for (int u = 0; u < 4; ++u) hv[u] += hist[c * kSkBins + hi_bin - u];
-    ssum[tid] = hv[0] + hv[1] + hv[2] + hv[3];
-    __syncthreads();
-    for (int off = 1; off < kSkPlanThreads; off <<= 1) {
-        const uint32_t add = tid >= off ? ssum[tid - off] : 0u;
-        __syncthreads();
-        ssum[tid] += add;
-        __syncthreads();
+    // inclusive scan over the threads: inside each wave by shuffles, then the
+    // wave totals (16 of them) in order
+    __shared__ uint32_t wtot[kSkPlanThreads / kWave];
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    uint32_t x = hv[0] + hv[1] + hv[2] + hv[3];
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
     }
+    if (lane == kWave - 1) wtot[wave] = x;
+    __syncthreads();
+    uint32_t base = 0;
+    for (int w = 0; w < wave; ++w) base += wtot[w];
+    ssum[tid] = x + base;
+    __syncthreads();
     const uint32_t need = (uint32_t)min<int64_t>(v, kSkMinCand);
     const uint32_t before = tid ? ssum[tid - 1] : 0u;
     if (before < need && ssum[tid] >= need) {
