@@ -41,12 +41,12 @@ def _load():
         lib.oracle_max_threads.restype = ctypes.c_int
         lib.oracle_sketch_signs.argtypes = [_ptr, _i64, _i64, _ptr, ctypes.c_int]
         lib.oracle_sketch_scale.argtypes = [_ptr, _i64, _i64, ctypes.c_int]
-        lib.oracle_sketch_scale.restype = ctypes.c_float
-        lib.oracle_sketch_plan.argtypes = [_ptr, _i64, ctypes.c_float, _ptr, _ptr, _ptr, _ptr, _ptr, _ptr]
-        lib.oracle_sketch_scores.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_float, _ptr, ctypes.c_int]
+        lib.oracle_sketch_scale.restype = ctypes.c_double
+        lib.oracle_sketch_plan.argtypes = [_ptr, _i64, ctypes.c_double, _ptr, _ptr, _ptr, _ptr, _ptr]
+        lib.oracle_sketch_scores.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_double, _ptr, _ptr, ctypes.c_int]
         lib.oracle_sketch_pick.argtypes = [_ptr, _ptr, _i64, _i64, _ptr, _ptr, _ptr, _ptr]
         lib.oracle_sketch_pick.restype = _i64
-        lib.oracle_rmsnorm_quantize.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_float, _ptr, _ptr, _ptr]
+        lib.oracle_rmsnorm.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_double, _ptr]
         lib.oracle_glu.argtypes = [_ptr, _ptr, _i64, _i64, ctypes.c_int, _ptr]
         lib.oracle_quantize_groups.argtypes = [_ptr, _i64, _i64, _i64, _ptr, _ptr]
         lib.oracle_gemv_grouped.argtypes = [_ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _ptr, _ptr, ctypes.c_int]
@@ -170,45 +170,46 @@ def sketch_signs(w_bf16, threads: int = 0):
 
 
 def sketch_scale(w_bf16, threads: int = 0):
-    """c = mean |w| of the table (fp32)."""
+    """c = mean |w| of the table (fp64)."""
     w, pw = _c(np.atleast_2d(w_bf16), np.uint16)
     v, k = w.shape
-    return np.float32(_load().oracle_sketch_scale(pw, v, k, threads or max_threads()))
+    return float(_load().oracle_sketch_scale(pw, v, k, threads or max_threads()))
 
 
 def sketch_plan(x, c):
-    """(top_idx [T], top_x [T], group_of [k] (-1 = exact), group_n [4], group_w [4])."""
+    """(top_idx [T], group_of [k] (-1 = exact), group_n [4], group_w [4] fp64)."""
     x, px = _c(x, np.float32)
     k = x.size
     top_idx = np.zeros(32, np.int32)
-    top_x = np.zeros(32, np.float32)
     ntop = np.zeros(1, np.int32)
     group_of = np.zeros(k, np.int32)
     group_n = np.zeros(4, np.int32)
-    group_w = np.zeros(4, np.float32)
-    _load().oracle_sketch_plan(px, k, ctypes.c_float(float(c)), top_idx.ctypes.data, top_x.ctypes.data,
-                               ntop.ctypes.data, group_of.ctypes.data, group_n.ctypes.data, group_w.ctypes.data)
-    t = int(ntop[0])
-    return top_idx[:t], top_x[:t], group_of, group_n, group_w
+    group_w = np.zeros(4, np.float64)
+    _load().oracle_sketch_plan(px, k, ctypes.c_double(float(c)), top_idx.ctypes.data, ntop.ctypes.data,
+                               group_of.ctypes.data, group_n.ctypes.data, group_w.ctypes.data)
+    return top_idx[:int(ntop[0])], group_of, group_n, group_w
 
 
 def sketch_scores(w_bf16, x, c, threads: int = 0):
-    """Approximate scores (fp32 [v]) of steps 1 and 2 of the sketch head."""
+    """Approximate scores (fp64 [v]) of steps 1 and 2 of the sketch head, and per word the sum of
+    the magnitudes of the score's terms (fp64 [v])."""
     w, pw = _c(np.atleast_2d(w_bf16), np.uint16)
     x, px = _c(x, np.float32)
     v, k = w.shape
     assert x.size == k
-    scores = np.empty(v, np.float32)
-    _load().oracle_sketch_scores(pw, px, v, k, ctypes.c_float(float(c)), scores.ctypes.data,
+    scores = np.empty(v, np.float64)
+    mag = np.empty(v, np.float64)
+    _load().oracle_sketch_scores(pw, px, v, k, ctypes.c_double(float(c)), scores.ctypes.data, mag.ctypes.data,
                                  threads or max_threads())
-    return scores
+    return scores, mag
 
 
 def sketch_pick(w_bf16, x, scores):
-    """Step 3: (candidate mask [v] bool, exact logits fp64 [v] (0 off the candidates), pick)."""
+    """Step 3: (candidate mask [v] bool: the min(1024, v) best scores, exact logits fp64 [v]
+    (0 off the candidates), pick)."""
     w, pw = _c(np.atleast_2d(w_bf16), np.uint16)
     x, px = _c(x, np.float32)
-    scores, ps = _c(scores, np.float32)
+    scores, ps = _c(scores, np.float64)
     v, k = w.shape
     is_cand = np.zeros(v, np.uint8)
     logits = np.zeros(v, np.float64)
@@ -220,22 +221,20 @@ def sketch_pick(w_bf16, x, scores):
 def sketch_head(w_bf16, x, threads: int = 0):
     """The whole sketch head: (pick, candidate mask, approximate scores, exact candidate logits)."""
     c = sketch_scale(w_bf16, threads)
-    scores = sketch_scores(w_bf16, x, c, threads)
+    scores, _ = sketch_scores(w_bf16, x, c, threads)
     is_cand, logits, idx = sketch_pick(w_bf16, x, scores)
     return idx, is_cand, scores, logits
 
 
-def rmsnorm_quantize(x, weight, eps=1e-5):
-    """RMSNorm (fp32, the kernel's reduction order) then per-row int8: (int8 [m][k], fp32 [m], fp32 o [m][k])."""
+def rmsnorm(x, weight, eps=1e-5):
+    """RMSNorm of every row in fp64: weight * x / sqrt(mean(x^2) + eps) -> fp64 [m][k]."""
     x, px = _c(np.atleast_2d(x), np.float32)
     w, pw = _c(weight, np.float32)
     m, k = x.shape
     assert w.size == k
-    q = np.empty((m, k), np.int8)
-    s = np.empty(m, np.float32)
-    o = np.empty((m, k), np.float32)
-    _load().oracle_rmsnorm_quantize(px, pw, m, k, ctypes.c_float(eps), q.ctypes.data, s.ctypes.data, o.ctypes.data)
-    return q, s, o
+    o = np.empty((m, k), np.float64)
+    _load().oracle_rmsnorm(px, pw, m, k, ctypes.c_double(float(eps)), o.ctypes.data)
+    return o
 
 
 GLU_GELU_TANH = 1
@@ -286,7 +285,7 @@ def gemv_grouped(w8, sw, x8, sx, threads: int = 0):
     return y, b
 
 
-__all__ = ["quantize_groups", "gemv_grouped", "WEIGHT_GROUP", "ACT_GROUP", "rmsnorm_quantize", "glu", "GLU_GELU_TANH", "GLU_SILU",
+__all__ = ["quantize_groups", "gemv_grouped", "WEIGHT_GROUP", "ACT_GROUP", "rmsnorm", "glu", "GLU_GELU_TANH", "GLU_SILU",
            "max_threads", "quantize_rows", "quantize_tensor", "trit5_row_bytes", "trit5_row_stride",
            "int8_row_stride", "pack_trit5", "unpack_trit5", "layout_int8", "matmul_int", "dequant",
            "lmhead", "sketch_signs", "sketch_scale", "sketch_plan", "sketch_scores", "sketch_pick", "sketch_head"]

@@ -282,31 +282,18 @@ void oracle_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, doub
 /*    taking the rest.  Group weight = c * mean |x| of the group, with c    */
 /*    the mean |w| of the whole table, so a group's sign agreement is       */
 /*    turned into the size of the products it stands for.                   */
-/*  - c: each row's sum of |w| in fp32 in column order; rows summed in fp64 */
-/*    in blocks of 512 consecutive rows, the blocks summed in fp64 in       */
-/*    order, divided by v * k in fp64 and rounded to fp32.                  */
-/*  - the approximate score is a choice of candidates, so it is computed    */
-/*    in fp32 in the GPU's order (see oracle_sketch_scores) and the         */
-/*    candidate set is the same on both sides.                              */
-/*  - "about 1,000": every word whose approximate score lies in the top     */
-/*    bins holding at least min(1024, v) words, a bin being the top 12 bits */
-/*    of the score's order-preserving 32-bit key (one eighth of an octave). */
+/*  - every quantity above is the plain definition, summed in fp64: c, the  */
+/*    group means, and the score                                            */
+/*        s = sum_(exact j) w_j x_j + sum_g weight_g * agreement_g.         */
+/*  - "about 1,000 words": the N = min(1024, v) best approximate scores,    */
+/*    ties to the lower word index.                                         */
 /*  - the exact scores are O6's logits; the pick is O6's first maximum,     */
 /*    over the candidates only.                                             */
 /* ------------------------------------------------------------------------ */
 
 #define ORACLE_SKETCH_TOP 32
 #define ORACLE_SKETCH_GROUPS 4
-#define ORACLE_SKETCH_MIN_CAND 1024
-#define ORACLE_SKETCH_ROW_BLOCK 512
-
-static float oracle_bf16_to_float(uint16_t h)
-{
-    uint32_t bits = (uint32_t)h << 16;
-    float f;
-    memcpy(&f, &bits, sizeof f);
-    return f;
-}
+#define ORACLE_SKETCH_CAND 1024
 
 /* Sign bits of the table in the device layout: bit (c % 32) of word        */
 /* (c / 32) * v + r is 1 when w[r][c] < 0; bits past k are 0.                */
@@ -320,39 +307,27 @@ void oracle_sketch_signs(const uint16_t* w, int64_t v, int64_t k, uint32_t* out,
 #endif
     for (int64_t r = 0; r < v; ++r)
         for (int64_t c = 0; c < k; ++c)
-            if (oracle_bf16_to_float(w[r * k + c]) < 0.0f) out[(c / 32) * v + r] |= 1u << (c % 32);
+            if (oracle_bf16_to_double(w[r * k + c]) < 0.0) out[(c / 32) * v + r] |= 1u << (c % 32);
 }
 
-/* c = mean |w| of the table, in the order stated above. */
-float oracle_sketch_scale(const uint16_t* w, int64_t v, int64_t k, int threads)
+/* c = mean |w| of the table: every |w| summed in fp64, divided by v * k. */
+double oracle_sketch_scale(const uint16_t* w, int64_t v, int64_t k, int threads)
 {
-    float* rows = (float*)malloc((size_t)v * sizeof(float));
-    assert(rows);
+    double total = 0.0;
     (void)threads;
 #ifdef _OPENMP
-#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
+#pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1) reduction(+:total)
 #endif
-    for (int64_t r = 0; r < v; ++r) {
-        float row = 0.0f;
-        for (int64_t c = 0; c < k; ++c) row += fabsf(oracle_bf16_to_float(w[r * k + c]));
-        rows[r] = row;
-    }
-    double total = 0.0;
-    for (int64_t b = 0; b * ORACLE_SKETCH_ROW_BLOCK < v; ++b) {
-        double part = 0.0;
-        for (int64_t r = b * ORACLE_SKETCH_ROW_BLOCK; r < v && r < (b + 1) * ORACLE_SKETCH_ROW_BLOCK; ++r)
-            part += (double)rows[r];
-        total += part;
-    }
-    free(rows);
-    return (float)(total / ((double)v * (double)k));
+    for (int64_t r = 0; r < v; ++r)
+        for (int64_t c = 0; c < k; ++c) total += fabs(oracle_bf16_to_double(w[r * k + c]));
+    return total / ((double)v * (double)k);
 }
 
-/* The per-token plan: the exact dimensions in rank order (top_idx, top_x,  */
-/* *ntop), the group of every dimension (-1 for an exact one), the group    */
-/* sizes and weights.                                                       */
-void oracle_sketch_plan(const float* x, int64_t k, float c, int32_t* top_idx, float* top_x, int32_t* ntop,
-                        int32_t* group_of, int32_t* group_n, float* group_w)
+/* The per-token plan: the exact dimensions in rank order (top_idx, *ntop), */
+/* the group of every dimension (-1 for an exact one), the group sizes and  */
+/* weights c * mean |x| (fp64).                                             */
+void oracle_sketch_plan(const float* x, int64_t k, double c, int32_t* top_idx, int32_t* ntop, int32_t* group_of,
+                        int32_t* group_n, double* group_w)
 {
     /* rank by |x| descending, lower index first on ties: selection by repeated scans */
     int64_t* order = (int64_t*)malloc((size_t)k * sizeof(int64_t));
@@ -372,7 +347,6 @@ void oracle_sketch_plan(const float* x, int64_t k, float c, int32_t* top_idx, fl
     *ntop = (int32_t)t;
     for (int64_t j = 0; j < t; ++j) {
         top_idx[j] = (int32_t)order[j];
-        top_x[j] = x[order[j]];
         group_of[order[j]] = -1;
     }
     int64_t rest = k - t, base = rest / ORACLE_SKETCH_GROUPS;
@@ -380,133 +354,113 @@ void oracle_sketch_plan(const float* x, int64_t k, float c, int32_t* top_idx, fl
         int64_t lo = t + g * base;
         int64_t hi = g == ORACLE_SKETCH_GROUPS - 1 ? k : lo + base;
         group_n[g] = (int32_t)(hi - lo);
-        float sum = 0.0f;
+        double sum = 0.0;
         for (int64_t r = lo; r < hi; ++r) {
             group_of[order[r]] = g;
-            sum += fabsf(x[order[r]]);
+            sum += fabs((double)x[order[r]]);
         }
-        float mean = hi > lo ? sum / (float)(hi - lo) : 0.0f;
-        group_w[g] = c * mean;
+        group_w[g] = hi > lo ? c * (sum / (double)(hi - lo)) : 0.0;
     }
     free(order);
     free(used);
 }
 
-/* Approximate scores (steps 1 and 2), fp32 in this order: a = 0; for each  */
-/* exact dimension in rank order a = fma(w, x, a); then for each group g in */
-/* order a = fma(weight_g, agreement_g, a), the agreement an exact integer. */
-void oracle_sketch_scores(const uint16_t* w, const float* x, int64_t v, int64_t k, float c, float* scores,
-                          int threads)
+/* Approximate scores (steps 1 and 2) in fp64, and for each word the sum of */
+/* the magnitudes of its terms, sum_j |w_j x_j| + sum_g weight_g |agreement_g| */
+/* (the scale any fp32 evaluation error of the score is proportional to).   */
+void oracle_sketch_scores(const uint16_t* w, const float* x, int64_t v, int64_t k, double c, double* scores,
+                          double* magnitude, int threads)
 {
     int32_t top_idx[ORACLE_SKETCH_TOP], ntop, group_n[ORACLE_SKETCH_GROUPS];
-    float top_x[ORACLE_SKETCH_TOP], group_w[ORACLE_SKETCH_GROUPS];
+    double group_w[ORACLE_SKETCH_GROUPS];
     int32_t* group_of = (int32_t*)malloc((size_t)k * sizeof(int32_t));
     assert(group_of);
-    oracle_sketch_plan(x, k, c, top_idx, top_x, &ntop, group_of, group_n, group_w);
+    oracle_sketch_plan(x, k, c, top_idx, &ntop, group_of, group_n, group_w);
     (void)threads;
 #ifdef _OPENMP
 #pragma omp parallel for schedule(static) num_threads(threads > 0 ? threads : 1)
 #endif
     for (int64_t r = 0; r < v; ++r) {
-        float a = 0.0f;
-        for (int j = 0; j < ntop; ++j) a = fmaf(oracle_bf16_to_float(w[r * k + top_idx[j]]), top_x[j], a);
+        double s = 0.0, mag = 0.0;
+        for (int j = 0; j < ntop; ++j) {
+            double p = oracle_bf16_to_double(w[r * k + top_idx[j]]) * (double)x[top_idx[j]];
+            s += p;
+            mag += fabs(p);
+        }
         int64_t agree[ORACLE_SKETCH_GROUPS] = {0, 0, 0, 0};
         for (int64_t col = 0; col < k; ++col) {
             int g = group_of[col];
             if (g < 0) continue;
-            int sw = oracle_bf16_to_float(w[r * k + col]) < 0.0f, sx = x[col] < 0.0f;
+            int sw = oracle_bf16_to_double(w[r * k + col]) < 0.0, sx = x[col] < 0.0f;
             agree[g] += sw == sx ? 1 : -1;
         }
-        for (int g = 0; g < ORACLE_SKETCH_GROUPS; ++g) a = fmaf(group_w[g], (float)agree[g], a);
-        scores[r] = a;
+        for (int g = 0; g < ORACLE_SKETCH_GROUPS; ++g) {
+            s += group_w[g] * (double)agree[g];
+            mag += group_w[g] * fabs((double)agree[g]);
+        }
+        scores[r] = s;
+        if (magnitude) magnitude[r] = mag;
     }
     free(group_of);
 }
 
-/* Order-preserving 32-bit key of an fp32 value. */
-static uint32_t oracle_order_key(float f)
-{
-    uint32_t u;
-    memcpy(&u, &f, sizeof u);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-/* Step 3: the candidates (is_cand[r] = 1) from the approximate scores, the */
+/* Step 3: the candidates (is_cand[r] = 1: the N best scores, ties to the   */
+/* lower index, found by N scans for the best word not yet taken), the      */
 /* exact logits of the candidates (logits[r], fp64; 0 elsewhere) and the    */
 /* pick.  Returns the number of candidates.                                 */
-int64_t oracle_sketch_pick(const uint16_t* w, const float* x, int64_t v, int64_t k, const float* scores,
+int64_t oracle_sketch_pick(const uint16_t* w, const float* x, int64_t v, int64_t k, const double* scores,
                            uint8_t* is_cand, double* logits, int32_t* idx)
 {
-    int64_t hist[4096] = {0};
-    for (int64_t r = 0; r < v; ++r) ++hist[oracle_order_key(scores[r]) >> 20];
-    int64_t need = v < ORACLE_SKETCH_MIN_CAND ? v : ORACLE_SKETCH_MIN_CAND, above = 0;
-    int64_t bstar = 4095;
-    for (; bstar > 0; --bstar) {
-        above += hist[bstar];
-        if (above >= need) break;
+    int64_t need = v < ORACLE_SKETCH_CAND ? v : ORACLE_SKETCH_CAND;
+    memset(is_cand, 0, (size_t)v);
+    for (int64_t n = 0; n < need; ++n) {
+        int64_t best = -1;
+        for (int64_t r = 0; r < v; ++r)
+            if (!is_cand[r] && (best < 0 || scores[r] > scores[best])) best = r;
+        is_cand[best] = 1;
     }
-    int64_t count = 0, best = -1;
+    int64_t best = -1;
     for (int64_t r = 0; r < v; ++r) {
         logits[r] = 0.0;
-        is_cand[r] = (int64_t)(oracle_order_key(scores[r]) >> 20) >= bstar;
         if (!is_cand[r]) continue;
-        ++count;
         double sum = 0.0;
         for (int64_t col = 0; col < k; ++col) sum += oracle_bf16_to_double(w[r * k + col]) * (double)x[col];
         logits[r] = sum;
         if (best < 0 || (float)sum > (float)logits[best]) best = r;
     }
     *idx = (int32_t)best;
-    return count;
+    return need;
 }
 
 /* ------------------------------------------------------------------------ */
-/* O8 -- the steps either side of a GEMV: RMSNorm -> int8, gate -> int8.    */
+/* O8 -- the steps either side of a GEMV: RMSNorm, gated activation.        */
 /*                                                                          */
 /* [L] "Step 1" and "Step 6": RMSNorm divides each value by the root mean   */
-/* square of the row (plus 1e-5 under the root) and multiplies by a        */
-/* per-dimension weight: o = weight * (r * x), r = 1 / sqrt(ss / k + eps).  */
+/* square of the row (plus eps under the root) and multiplies by a          */
+/* per-dimension weight: o = weight * x / sqrt(sum(x^2) / k + eps).         */
 /* [L] "Step 5": the gated feed-forward multiplies act(gate) by up, act =   */
 /* SiLU(v) = v / (1 + exp(-v)); cpp20gemma and gemma.cpp use a GeLU gate   */
 /* instead (GeGLU).  [T] "Step 2": the result is then rounded to int8 per  */
 /* token (O1).                                                              */
-/* Readings:                                                                */
-/*  - RMSNorm is fp32 as in [L]'s listing.  The sum of squares is an fp32   */
-/*    sum; the listing adds sequentially, any order rounds the same RMS     */
-/*    equally well, and this one is the GPU's: 256 partial sums, partial t  */
-/*    taking x[j]^2 for j = t, t + 256, ... in order, then pairwise         */
-/*    (partial[t] += partial[t + s] for s = 128, 64, ..., 1).  The int8     */
-/*    codes are then decided from the same fp32 values on both sides.       */
-/*  - GeLU is the tanh form used by Gemma: 0.5 v (1 + tanh(sqrt(2/pi) (v +  */
-/*    0.044715 v^3))).  The gated values are computed in fp64 here; the GPU */
-/*    computes them in fp32 with its own exp/tanh, so its codes are checked */
-/*    as valid roundings of these values (see the tests).                   */
+/* Readings: both are evaluated here in fp64 straight from the definition   */
+/* (the pages fix no precision for them); GeLU is the tanh form Gemma uses: */
+/* 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  The GPU evaluates them */
+/* in fp32, so its int8 codes are checked as valid roundings of these       */
+/* values (see the tests).                                                  */
 /* ------------------------------------------------------------------------ */
 
-void oracle_rmsnorm_quantize(const float* x, const float* weight, int64_t m, int64_t k, float eps, int8_t* q,
-                             float* s, float* o_out)
+void oracle_rmsnorm(const float* x, const float* weight, int64_t m, int64_t k, double eps, double* o)
 {
-    float* o = (float*)malloc((size_t)k * sizeof(float));
-    assert(o);
     for (int64_t mi = 0; mi < m; ++mi) {
         const float* xr = x + mi * k;
-        float part[256];
-        for (int t = 0; t < 256; ++t) {
-            float a = 0.0f;
-            for (int64_t j = t; j < k; j += 256) {
-                assert(isfinite(xr[j]));
-                a += xr[j] * xr[j];
-            }
-            part[t] = a;
+        double ss = 0.0;
+        for (int64_t j = 0; j < k; ++j) {
+            assert(isfinite(xr[j]));
+            ss += (double)xr[j] * (double)xr[j];
         }
-        for (int st = 128; st >= 1; st /= 2)
-            for (int t = 0; t < st; ++t) part[t] += part[t + st];
-        float r = 1.0f / sqrtf(part[0] / (float)k + eps);
-        for (int64_t j = 0; j < k; ++j) o[j] = weight[j] * (r * xr[j]);
-        if (o_out) memcpy(o_out + mi * k, o, (size_t)k * sizeof(float));
-        oracle_quantize_rows(o, 1, k, q + mi * k, s + mi);
+        double rms = sqrt(ss / (double)k + eps);
+        for (int64_t j = 0; j < k; ++j) o[mi * k + j] = (double)weight[j] * (double)xr[j] / rms;
     }
-    free(o);
 }
 
 /* act: 1 = GeLU (tanh form), 2 = SiLU.  h = act(gate) * up in fp64. */

@@ -346,7 +346,7 @@ def test_sketch_scale_closed_form():
                                      (20, [0, 0, 0, 0]), (100, [17, 17, 17, 17])])
 def test_sketch_plan_group_sizes(k, sizes):
     x = synth.normal(41, (k,))
-    top_idx, top_x, group_of, group_n, group_w = oracle.sketch_plan(x, 1.0)
+    top_idx, group_of, group_n, group_w = oracle.sketch_plan(x, 1.0)
     t = min(32, k)
     assert len(top_idx) == t
     assert list(group_n) == sizes
@@ -360,20 +360,23 @@ def test_sketch_plan_group_sizes(k, sizes):
     rest = np.setdiff1d(np.arange(k), top_idx)
     if rest.size:
         assert mags[rest].max() <= mags[top_idx].min()
-    np.testing.assert_array_equal(top_x, x[top_idx])
+    # groups follow the rank order: every |x| of group g is >= every |x| of group g + 1
+    for g in range(3):
+        if sizes[g] and sizes[g + 1]:
+            assert mags[group_of == g].min() >= mags[group_of == g + 1].max()
 
 
 def test_sketch_plan_ties_and_group_weights_closed_form():
     # |x| = k - i: ranks are the indices in order; ties (all equal) also rank by index
     k = 72
     x = np.array([(k - i) * (-1) ** i for i in range(k)], np.float32)
-    top_idx, _, group_of, group_n, group_w = oracle.sketch_plan(x, 0.5)
+    top_idx, group_of, group_n, group_w = oracle.sketch_plan(x, 0.5)
     np.testing.assert_array_equal(top_idx, np.arange(32))
     assert list(group_n) == [10, 10, 10, 10]
     # group g holds ranks 32+10g .. 41+10g, |x| = 40-10g .. 31-10g: mean = 35.5 - 10 g
-    np.testing.assert_array_equal(group_w, np.float32(0.5) * np.array([35.5, 25.5, 15.5, 5.5], np.float32))
+    np.testing.assert_array_equal(group_w, 0.5 * np.array([35.5, 25.5, 15.5, 5.5]))
     eq = np.ones(50, np.float32)
-    top_idx, _, _, _, _ = oracle.sketch_plan(eq, 1.0)
+    top_idx, _, _, _ = oracle.sketch_plan(eq, 1.0)
     np.testing.assert_array_equal(top_idx, np.arange(32))
 
 
@@ -385,10 +388,32 @@ def test_sketch_scores_equal_exact_logits_when_all_magnitudes_match():
     sw = np.where(synth.raw(43, v * k).reshape(v, k) % 2 == 0, 1.0, -1.0)
     sx = np.where(synth.raw(44, k) % 2 == 0, 1.0, -1.0).astype(np.float32)
     w = _bf16(0.5 * sw)
-    assert oracle.sketch_scale(w) == np.float32(0.5)
-    scores = oracle.sketch_scores(w, sx, np.float32(0.5))
+    assert oracle.sketch_scale(w) == 0.5
+    scores, mag = oracle.sketch_scores(w, sx, 0.5)
     exact = (0.5 * sw) @ sx
-    np.testing.assert_array_equal(scores, exact.astype(np.float32))
+    np.testing.assert_array_equal(scores, exact)
+    # the magnitude is 0.5 per exact dimension plus 0.5 |agreement| per group
+    assert np.all(mag >= np.abs(scores)) and np.all(mag <= 0.5 * k)
+    assert np.all(mag >= 0.5 * 32)
+
+
+def test_sketch_scores_brute_force_tiny():
+    # v = 3, k = 36 by hand: 32 exact dimensions, then groups of 1, 1, 1, 1 (k - T = 4)
+    k = 36
+    x = np.array([36 - i for i in range(k)], np.float32)          # ranks = indices
+    w = np.zeros((3, k), np.float32)
+    w[0, :] = 0.25                                                  # all signs agree
+    w[1, :] = -0.25                                                 # all disagree
+    w[2, :32] = 0.0
+    w[2, 32:] = [0.5, -0.5, 0.5, -0.5]
+    wb = _bf16(w)
+    c = oracle.sketch_scale(wb)
+    assert c == (0.25 * 36 * 2 + 0.5 * 4) / (3 * 36)
+    scores, _ = oracle.sketch_scores(wb, x, c)
+    exact32 = 0.25 * sum(36 - i for i in range(32))
+    tail = c * np.array([4.0, 3.0, 2.0, 1.0])                       # group weights c * |x| of ranks 32..35
+    np.testing.assert_allclose(scores, [exact32 + tail.sum(), -exact32 - tail.sum(),
+                                        tail[0] - tail[1] + tail[2] - tail[3]], rtol=1e-15)
 
 
 def test_sketch_scores_sign_symmetry():
@@ -396,11 +421,12 @@ def test_sketch_scores_sign_symmetry():
     w = _bf16(synth.normal(45, (v, k), std=0.02))
     x = synth.normal(46, (k,))
     c = oracle.sketch_scale(w)
-    s1 = oracle.sketch_scores(w, x, c)
-    s2 = oracle.sketch_scores(w ^ np.uint16(0x8000), x, c)    # every weight negated
+    s1, m1 = oracle.sketch_scores(w, x, c)
+    s2, m2 = oracle.sketch_scores(w ^ np.uint16(0x8000), x, c)    # every weight negated
     zero = (w & np.uint16(0x7FFF)) == 0
     assert not zero.any()
     np.testing.assert_array_equal(s2, -s1)
+    np.testing.assert_array_equal(m2, m1)
 
 
 def test_sketch_pick_all_exact_matches_full_argmax():
@@ -411,25 +437,41 @@ def test_sketch_pick_all_exact_matches_full_argmax():
         idx, cand, scores, logits = oracle.sketch_head(w, x)
         full, fidx = oracle.lmhead(w, x)
         assert idx == fidx
-        assert cand.sum() >= 1024
+        assert cand.sum() == 1024
         np.testing.assert_array_equal(logits[cand], full[cand])
 
 
-def test_sketch_pick_candidates_are_the_top_bins():
+def test_sketch_pick_candidates_are_the_best_scores():
     v, k = 5000, 256
     w = _bf16(synth.normal(47, (v, k), std=0.02))
     x = synth.normal(48, (k,))
     idx, cand, scores, logits = oracle.sketch_head(w, x)
-    key = scores.view(np.uint32).astype(np.uint64)
-    key = np.where(key & 0x80000000, ~key & 0xFFFFFFFF, key | 0x80000000) >> 20
-    assert cand.sum() >= 1024
-    assert key[cand].min() > key[~cand].max()
-    above = cand & (key > key[cand].min())
-    assert above.sum() < 1024
+    assert cand.sum() == 1024
+    assert scores[cand].min() >= scores[~cand].max()
     assert idx == int(np.flatnonzero(cand)[np.argmax(logits[cand].astype(np.float32))])
     # fewer words than 1024: every word is a candidate and the pick is the full argmax
     idx2, cand2, _, _ = oracle.sketch_head(w[:700], x)
     assert cand2.all() and idx2 == oracle.lmhead(w[:700], x)[1]
+
+
+def test_sketch_pick_ties_at_the_cut_go_to_the_lower_index():
+    # 150 of the 1200 words are copies of the word ranked about 1000th, so the 1024th
+    # best score is tied: exactly the copies with the lowest indices make the cut
+    v, k = 1200, 64
+    w = _bf16(synth.normal(52, (v, k), std=0.02))
+    x = synth.normal(53, (k,))
+    s, _ = oracle.sketch_scores(w, x, oracle.sketch_scale(w))
+    order = np.argsort(-s, kind="stable")
+    template = order[990]
+    w[order[1040:1190]] = w[template]
+    s, _ = oracle.sketch_scores(w, x, oracle.sketch_scale(w))
+    ties = np.flatnonzero(s == s[template])
+    above = int((s > s[template]).sum())
+    assert ties.size == 151 and above < 1024 < above + ties.size
+    cand, _, _ = oracle.sketch_pick(w, x, s)
+    assert cand.sum() == 1024
+    np.testing.assert_array_equal(np.flatnonzero(cand & (s == s[template])), ties[:1024 - above])
+    assert np.all(cand[s > s[template]]) and not np.any(cand[s < s[template]])
 
 
 def test_sketch_pick_planted_winner():
@@ -450,26 +492,30 @@ def test_rmsnorm_matches_definition_and_is_scale_invariant():
     for m, k in [(3, 1152), (2, 257), (1, 1), (4, 6912)]:
         x = synth.normal(81 + k, (m, k))
         w = synth.normal(82 + k, (k,)) * 0.5 + 1.0
-        q, s, o = oracle.rmsnorm_quantize(x, w, 1e-5)
-        # the definition in exact rationals -> within a few fp32 rounding steps
+        o = oracle.rmsnorm(x, w, 1e-5)
+        # the definition in exact rationals, then one square root: within a few fp64 roundings
         for r in range(m):
             ss = sum(Fraction(float(v)) ** 2 for v in x[r])
-            rms = math.sqrt(float(ss / k) + 1e-5)
-            ref = w.astype(np.float64) * x[r].astype(np.float64) / rms
-            np.testing.assert_allclose(o[r], ref, rtol=(k + 8) * 2.0 ** -24, atol=0)
-        # the codes are O1's codes of o
-        q2, s2 = oracle.quantize_rows(o)
-        np.testing.assert_array_equal(q, q2)
-        np.testing.assert_array_equal(s.view(np.uint32), s2.view(np.uint32))
+            ms = ss / k + Fraction(1e-5)
+            for j in (0, k // 2, k - 1):
+                ref = Fraction(float(w[j])) * Fraction(float(x[r, j]))
+                # o^2 * ms = ref^2 up to the roundings of sqrt and the divide
+                lhs = Fraction(float(o[r, j])) ** 2 * ms
+                assert abs(lhs - ref ** 2) <= Fraction(1, 10 ** 13) * ref ** 2 + Fraction(1, 10 ** 300)
+            np.testing.assert_allclose(o[r], w.astype(np.float64) * x[r].astype(np.float64) /
+                                       math.sqrt(float(ss / k) + 1e-5), rtol=1e-14, atol=0)
         # eps = 0: scaling x by a power of two changes nothing, bit for bit
-        _, _, o0 = oracle.rmsnorm_quantize(x, w, 0.0)
-        _, _, o1 = oracle.rmsnorm_quantize(x * np.float32(8.0), w, 0.0)
+        o0 = oracle.rmsnorm(x, w, 0.0)
+        o1 = oracle.rmsnorm(x * np.float32(8.0), w, 0.0)
         np.testing.assert_array_equal(o0, o1)
     # unit weights: the output's mean square is 1 / (1 + eps / mean(x^2))
     x = synth.normal(85, (1, 4096))
-    _, _, o = oracle.rmsnorm_quantize(x, np.ones(4096, np.float32), 1e-5)
+    o = oracle.rmsnorm(x, np.ones(4096, np.float32), 1e-5)
     ms = float(np.mean(x.astype(np.float64) ** 2))
-    assert abs(float(np.mean(o.astype(np.float64) ** 2)) - 1.0 / (1.0 + 1e-5 / ms)) < 1e-5
+    assert abs(float(np.mean(o ** 2)) - 1.0 / (1.0 + 1e-5 / ms)) < 1e-12
+    # a constant row of c with eps = 0 normalises to exactly +-1
+    o = oracle.rmsnorm(np.full((1, 10), -3.0, np.float32), np.ones(10, np.float32), 0.0)
+    np.testing.assert_array_equal(o, -np.ones((1, 10)))
 
 
 def test_glu_matches_library_activations():
