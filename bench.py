@@ -109,7 +109,7 @@ class DecodeStack:
             self.pool[c].copy_(self.pool[0])
         torch.cuda.synchronize()
         # one problem list (and one uploaded table) per copy
-        self.arrays, self.workspaces = [], []
+        self.arrays, self.plans = [], []
         for c in range(copies):
             probs = []
             for i, (off_i, nb, w) in enumerate(descs):
@@ -120,9 +120,8 @@ class DecodeStack:
                 probs.append(qmv.Problem(wc, self.x8[k][slot * m:(slot + 1) * m], self.sx[k][slot * m:(slot + 1) * m],
                                          y=self.y[i]))
             arr = qmv.problem_array(probs)
-            ws = qmv.qmv_gemv(arr) if m <= qmv.QMV_MAX_GEMV_M else None
             self.arrays.append(arr)
-            self.workspaces.append(ws)
+            self.plans.append(qmv.gemv_plan(arr) if m <= qmv.QMV_MAX_GEMV_M else None)
         torch.cuda.synchronize()
 
     # algorithmic bytes ---------------------------------------------------------
@@ -159,7 +158,7 @@ def time_decode(stack, steps, warmup, stream):
         c = i % stack.copies
         if ev is not None:
             ev[0].record(stream)
-        qmv.qmv_gemv(stack.arrays[c], workspace=stack.workspaces[c], flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        stack.plans[c].launch(stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -189,15 +188,13 @@ def time_gemv_only(stack, steps, warmup, stream):
     import torch
     from ternary_matvec_amd import qmv
     for i in range(warmup):
-        qmv.qmv_gemv(stack.arrays[i % stack.copies], workspace=stack.workspaces[i % stack.copies],
-                     flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        stack.plans[i % stack.copies].launch(stream)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(steps):
-        qmv.qmv_gemv(stack.arrays[i % stack.copies], workspace=stack.workspaces[i % stack.copies],
-                     flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        stack.plans[i % stack.copies].launch(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
@@ -233,15 +230,13 @@ def copies_sweep(stack, steps, stream):
         if c_count > stack.copies:
             break
         for i in range(10):
-            qmv.qmv_gemv(stack.arrays[i % c_count], workspace=stack.workspaces[i % c_count],
-                         flags=qmv.QMV_F_TABLE_READY, stream=stream)
+            stack.plans[i % c_count].launch(stream)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record(stream)
         for i in range(steps):
-            qmv.qmv_gemv(stack.arrays[i % c_count], workspace=stack.workspaces[i % c_count],
-                         flags=qmv.QMV_F_TABLE_READY, stream=stream)
+            stack.plans[i % c_count].launch(stream)
         t1.record(stream)
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / steps
@@ -265,19 +260,19 @@ def chained(stack, steps, stream, copies=4):
         one, grouped = [], []
         for i in range(len(arr)):
             sub = (qmv.qmv_problem * 1).from_address(base + i * size)
-            one.append((sub, qmv.qmv_gemv(sub, stream=stream)))
+            one.append(qmv.gemv_plan(sub, stream=stream))
         for lay in range(len(arr) // per_layer):
             for lo, hi in ((0, 3), (3, 5), (5, 6)):
                 sub = (qmv.qmv_problem * (hi - lo)).from_address(base + (lay * per_layer + lo) * size)
-                grouped.append((sub, qmv.qmv_gemv(sub, stream=stream)))
+                grouped.append(qmv.gemv_plan(sub, stream=stream))
         groups["156"].append(one)
         groups["78"].append(grouped)
     torch.cuda.synchronize()
     out = {}
     for name, per_copy in groups.items():
         def step(i):
-            for sub, ws in per_copy[i % copies]:
-                qmv.qmv_gemv(sub, workspace=ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+            for plan in per_copy[i % copies]:
+                plan.launch(stream)
         for i in range(3):
             step(i)
         t0 = torch.cuda.Event(enable_timing=True)
@@ -421,7 +416,7 @@ class PrefillStack:
             probs.append(qmv.Problem(w, self.x8[k][slot * m:(slot + 1) * m], self.sx[k][slot * m:(slot + 1) * m],
                                      y=self.y[i]))
         self.arr = qmv.problem_array(probs)
-        self.ws = qmv.qmv_gemm_prefill(self.arr)
+        self.plan = qmv.prefill_plan(self.arr)
         torch.cuda.synchronize()
 
     def ops(self):
@@ -441,7 +436,7 @@ def time_prefill(ps, steps, warmup, stream):
         qmv.qmv_quantize_act_many(ps.acts, stream=stream)
         if ev is not None:
             ev[0].record(stream)
-        qmv.qmv_gemm_prefill(ps.arr, workspace=ps.ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        ps.plan.launch(stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -468,13 +463,13 @@ def prefill_per_matrix(ps, stream, reps=10):
     for mid, (name, n, k) in enumerate(ps.stack.mats):
         idx = [i for i, sp in enumerate(specs) if sp[1] == mid]
         sub = (qmv.qmv_problem * len(idx))(*[ps.arr[i] for i in idx])
-        ws = qmv.qmv_gemm_prefill(sub, stream=stream)
+        plan = qmv.prefill_plan(sub, stream=stream)
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         t0.record(stream)
         for _ in range(reps):
-            qmv.qmv_gemm_prefill(sub, workspace=ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+            plan.launch(stream)
         t1.record(stream)
         torch.cuda.synchronize()
         ms = t0.elapsed_time(t1) / reps
@@ -636,15 +631,15 @@ def bench_ffn_chain(stack, dev, stream, tokens=50):
     for layer in range(stack.layers):
         gu = (qmv.qmv_problem * 2)(prob(layer * nm + gi, x8a, sxa, yg), prob(layer * nm + ui, x8a, sxa, yu))
         dn = (qmv.qmv_problem * 1)(prob(layer * nm + di, x8b, sxb, yd))
-        layers.append((gu, qmv.qmv_gemv(gu, stream=stream), dn, qmv.qmv_gemv(dn, stream=stream)))
+        layers.append((qmv.gemv_plan(gu, stream=stream), qmv.gemv_plan(dn, stream=stream)))
     torch.cuda.synchronize()
 
     def token():
-        for gu, wgu, dn, wdn in layers:
+        for gu, dn in layers:
             qmv.qmv_rmsnorm_quantize(h, gamma, 1e-6, x8=x8a, sx=sxa, stream=stream)
-            qmv.qmv_gemv(gu, workspace=wgu, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+            gu.launch(stream)
             qmv.qmv_glu_quantize(yg, yu, qmv.QMV_ACT_GELU_TANH, x8=x8b, sx=sxb, stream=stream)
-            qmv.qmv_gemv(dn, workspace=wdn, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+            dn.launch(stream)
 
     def timed(fn, reps):
         for _ in range(3):
@@ -671,11 +666,11 @@ def bench_ffn_chain(stack, dev, stream, tokens=50):
     cap.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(cap):
         with torch.cuda.graph(graph, stream=cap):
-            for gu, wgu, dn, wdn in layers:
+            for gu, dn in layers:
                 qmv.qmv_rmsnorm_quantize(h, gamma, 1e-6, x8=x8a, sx=sxa, stream=cap)
-                qmv.qmv_gemv(gu, workspace=wgu, flags=qmv.QMV_F_TABLE_READY, stream=cap)
+                gu.launch(cap)
                 qmv.qmv_glu_quantize(yg, yu, qmv.QMV_ACT_GELU_TANH, x8=x8b, sx=sxb, stream=cap)
-                qmv.qmv_gemv(dn, workspace=wdn, flags=qmv.QMV_F_TABLE_READY, stream=cap)
+                dn.launch(cap)
     torch.cuda.current_stream().wait_stream(cap)
     torch.cuda.synchronize()
     replays_match = True
@@ -712,14 +707,14 @@ def bench_int8(dev, stream, reps=2000):
     x8, sx = qmv.qmv_quantize_act(x)
     p = qmv.Problem(pw, x8, sx)
     arr = qmv.problem_array([p])
-    ws = qmv.qmv_gemv(arr)
+    plan = qmv.gemv_plan(arr)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for _ in range(reps):
         qmv.qmv_quantize_act(x, x8=x8, sx=sx, stream=stream)
-        qmv.qmv_gemv(arr, workspace=ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        plan.launch(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) / reps * 1e3
@@ -755,7 +750,7 @@ def bench_groupscale(dev, stream, copies=2, reps=50):
           for (layer, mid, n, k) in specs]
     acts = [qmv.qmv_quantize_act_grouped(x) for x in xs]
     ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for (_, _, n, _) in specs]
-    arrays, workspaces = [], []
+    arrays, plans = [], []
     for c in range(copies):
         probs = []
         for i, (n, k, o, nb, so, ns) in enumerate(descs):
@@ -764,16 +759,16 @@ def bench_groupscale(dev, stream, copies=2, reps=50):
             probs.append(qmv.Problem(wc, acts[i][0], acts[i][1], y=ys[i]))
         arr = qmv.problem_array(probs)
         arrays.append(arr)
-        workspaces.append(qmv.qmv_gemv(arr))
+        plans.append(qmv.gemv_plan(arr))
     torch.cuda.synchronize()
     for i in range(10):
-        qmv.qmv_gemv(arrays[i % copies], workspace=workspaces[i % copies], flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        plans[i % copies].launch(stream)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(reps):
-        qmv.qmv_gemv(arrays[i % copies], workspace=workspaces[i % copies], flags=qmv.QMV_F_TABLE_READY, stream=stream)
+        plans[i % copies].launch(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) / reps * 1e3
@@ -782,7 +777,7 @@ def bench_groupscale(dev, stream, copies=2, reps=50):
                        "(156 matrices), batch 1, one grouped launch", "weight_copies": copies,
            "bytes_per_launch": nbytes, "us_per_launch": round(us, 2), "GB/s": round(nbytes / us / 1e3, 1),
            "frac_of_8TBps": round(nbytes / us / 8e6, 3)}
-    del pools, spool, arrays, workspaces
+    del pools, spool, arrays, plans
     torch.cuda.empty_cache()
     return out
 

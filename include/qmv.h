@@ -30,8 +30,11 @@
  *   - There are no device-side error reports apart from the optional invalid
  *     trit counter of qmv_pack_ternary; read it after synchronising.
  *   - Non-finite fp32 inputs are outside the contract.
- *   - The library keeps no global mutable state: calls on different streams
- *     with different buffers may run concurrently.
+ *   - State: the library keeps one record per device, filled once on the
+ *     first call that needs it (the compute-unit count, the kernels'
+ *     dynamic-LDS limit), and nothing else between calls.  A plan (qmv_plan_*)
+ *     is host memory the caller owns through its handle.  Calls on different
+ *     streams with different buffers and workspaces may run concurrently.
  *
  * Device weight layout (both weight types): a row's bytes are cut into
  * 16-byte chunks and chunk c of every row is stored before chunk c+1 of any
@@ -74,14 +77,6 @@ enum {
  * qmv_quantize_act_grouped). */
 #define QMV_WEIGHT_GROUP 128
 #define QMV_ACT_GROUP 32
-
-/* Flags of qmv_gemv / qmv_gemm_prefill. */
-enum {
-    /* The workspace already holds the problem table written by the previous
-     * call with this workspace and an identical problem list; skip the
-     * host-to-device upload of the table. */
-    QMV_F_TABLE_READY = 1
-};
 
 /* Limits. */
 #define QMV_MAX_GEMV_M 16            /* tokens per qmv_gemv problem */
@@ -246,8 +241,11 @@ enum {
 int32_t qmv_glu_quantize(const float* gate, const float* up, int64_t m, int64_t n, int32_t act, int8_t* x8, float* sx,
                          void* stream);
 
-/* Workspace bytes qmv_gemv / qmv_gemm_prefill need for this problem list
- * (-1 on bad input).  The workspace must be 256-byte aligned. */
+/* Workspace bytes for this problem list (-1 on bad input); the workspace
+ * must be 256-byte aligned.  qmv_workspace_bytes covers both qmv_gemv and
+ * qmv_gemm_prefill (the larger need of the calls that accept the list);
+ * the other two are each call's own need. */
+int64_t qmv_workspace_bytes(const qmv_problem* probs /* host */, int32_t count);
 int64_t qmv_gemv_workspace_bytes(const qmv_problem* probs /* host */, int32_t count);
 int64_t qmv_prefill_workspace_bytes(const qmv_problem* probs /* host */, int32_t count);
 
@@ -259,27 +257,56 @@ int64_t qmv_prefill_workspace_bytes(const qmv_problem* probs /* host */, int32_t
  *             1 <= m <= QMV_MAX_GEMV_M, its own weights, activations and
  *             outputs.  All problems of one weight type run in one kernel
  *             launch (one launch per type present).
- *   workspace device, >= qmv_gemv_workspace_bytes(probs, count) bytes; holds
- *             the problem table uploaded in-stream (see QMV_F_TABLE_READY).
- *   flags     0 or QMV_F_TABLE_READY.
+ *   workspace device, >= qmv_gemv_workspace_bytes(probs, count) bytes; the
+ *             call schedules the list, uploads the schedule into the
+ *             workspace in-stream and launches.  For the same list launched
+ *             again (a decode loop) make a plan once instead (qmv_plan_*).
  * y (and acc when non-NULL) are written for every problem.  x8/acc must not
  * alias y.  Results are exact in acc and do not depend on the grouping.
  * QMV_W_INT8_G128 problems are summed in fp32 over their activation groups
- * (see qmv_quantize_act_grouped).
+ * (see qmv_quantize_act_grouped).  The upload copies from host memory that is
+ * released on return, so the call is refused (QMV_EUNSUPPORTED) while
+ * `stream` is being captured into a graph; capture qmv_plan_launch instead.
  */
-int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes,
-                 uint32_t flags, void* stream);
+int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, void* stream);
 
 /*
  * qmv_gemm_prefill -- the same products for any number of tokens, computed
  * with int8 matrix cores ("Step 1": all prompt tokens go through each weight
  * matrix in one pass).  Ternary weights only.  Same arguments and results as
  * qmv_gemv, with 1 <= m <= 65536 per problem.  The workspace also holds the
- * kernel's tile tickets (zeroed by the table upload, left at zero by every
- * launch), so launches that share a workspace must not overlap in time.
+ * kernel's tile tickets (zeroed by the upload, left at zero by every launch),
+ * so launches that share a workspace must not overlap in time.
  */
-int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes,
-                         uint32_t flags, void* stream);
+int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, void* stream);
+
+/*
+ * Plans: one problem list scheduled once and launched many times, as a decode
+ * loop with fixed buffers does (the schedule and tile tables depend only on
+ * the list and the device).  A plan is host memory owned by the caller
+ * through its handle; it is made for the device current at qmv_plan_create
+ * and must be used with streams of that device.
+ *   kind      QMV_PLAN_GEMV (the launches of qmv_gemv) or QMV_PLAN_PREFILL
+ *             (those of qmv_gemm_prefill); the list is validated as by
+ *             that call.
+ *   qmv_plan_workspace_bytes  exact workspace bytes of the plan.
+ *   qmv_plan_upload  copies the plan's tables into `workspace` (in-stream,
+ *             from the plan's host memory, which lives until
+ *             qmv_plan_destroy).  Once per workspace, before its first launch.
+ *   qmv_plan_launch  enqueues the kernels only (no copies, no allocation, no
+ *             device queries): safe to capture in a graph.  Launches that
+ *             share a workspace must not overlap in time.  The buffers named
+ *             in the list must still be valid.
+ * EINVAL for a null plan or handle pointer or an unknown kind, EWORKSPACE for
+ * a missing, misaligned or small workspace, EHIP with no usable device.
+ */
+typedef struct qmv_plan qmv_plan;
+enum { QMV_PLAN_GEMV = 1, QMV_PLAN_PREFILL = 2 };
+int32_t qmv_plan_create(int32_t kind, const qmv_problem* probs /* host */, int32_t count, qmv_plan** plan);
+int64_t qmv_plan_workspace_bytes(const qmv_plan* plan);
+int32_t qmv_plan_upload(const qmv_plan* plan, void* workspace, int64_t ws_bytes, void* stream);
+int32_t qmv_plan_launch(const qmv_plan* plan, void* workspace, int64_t ws_bytes, void* stream);
+void qmv_plan_destroy(qmv_plan* plan);
 
 /* Workspace bytes of qmv_lmhead_argmax for a v x k head. */
 int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k);

@@ -6,8 +6,8 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
-#include <memory>
 #include <mutex>
+#include <new>
 #include <queue>
 #include <vector>
 
@@ -335,67 +335,44 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
     return QMV_OK;
 }
 
-// Compute units of the current device; with no usable device the plan is made
-// for a 256-CU part (host validation still works, launches then fail).
-int device_cus(int* cus_out)
-{
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
-        *cus_out = 256;
-        return -1;
-    }
-    *cus_out = cus;
-    return dev;
-}
+// ---------------------------------------------------------------------------
+// Per-device set-up, done once per device on first use: the compute-unit
+// count and the kernels' dynamic-LDS limit raised to the whole 160 KB
+// (launches then never set attributes).
+// ---------------------------------------------------------------------------
 
-// A few recently built tables, keyed by device and the problem list's bytes,
-// so a decode loop that launches the same list again does not re-plan it.
-struct TableCache {
-    std::mutex mu;
-    struct Entry {
-        int dev, cus;
-        std::vector<uint8_t> key;
-        std::shared_ptr<const Table> table;
-    };
-    std::vector<Entry> entries;
-    size_t next = 0;
+constexpr int kMaxDevices = 64;
+
+struct DeviceSetup {
+    std::once_flag once;
+    int32_t status = QMV_EHIP;
+    int cus = 0;
 };
 
-TableCache& table_cache()
-{
-    static TableCache c;
-    return c;
-}
+DeviceSetup g_devices[kMaxDevices];
 
-int32_t get_table(const qmv_problem* probs, int32_t count, std::shared_ptr<const Table>& out)
+// The current device's record (set up on first use), or null with no usable
+// device.
+const DeviceSetup* device_setup(int* dev_out)
 {
-    int cus = 0;
-    const int dev = device_cus(&cus);
-    const uint8_t* kb = reinterpret_cast<const uint8_t*>(probs);
-    const size_t kn = sizeof(qmv_problem) * (size_t)count;
-    TableCache& c = table_cache();
-    {
-        std::lock_guard<std::mutex> g(c.mu);
-        for (const auto& e : c.entries)
-            if (e.dev == dev && e.cus == cus && e.key.size() == kn && std::memcmp(e.key.data(), kb, kn) == 0) {
-                out = e.table;
-                return QMV_OK;
-            }
-    }
-    auto t = std::make_shared<Table>();
-    const int32_t st = build_table(probs, count, cus, *t);
-    if (st != QMV_OK) return st;
-    std::lock_guard<std::mutex> g(c.mu);
-    TableCache::Entry e{dev, cus, std::vector<uint8_t>(kb, kb + kn), t};
-    if (c.entries.size() < 8) {
-        c.entries.push_back(std::move(e));
-    } else {
-        c.entries[c.next] = std::move(e);
-        c.next = (c.next + 1) % 8;
-    }
-    out = t;
-    return QMV_OK;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    DeviceSetup& d = g_devices[dev];
+    std::call_once(d.once, [&d, dev] {
+        int cus = 0;
+        hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess && cus < 1) e = hipErrorInvalidDevice;
+        if (e == hipSuccess) e = setup_workgroup_gemv_attributes();
+        if (e == hipSuccess) e = setup_stream_attributes();
+        if (e == hipSuccess) e = setup_grouped_attributes();
+        if (e == hipSuccess) e = setup_prefill_attributes();
+        if (e == hipSuccess) e = setup_sketch_attributes();
+        d.cus = cus;
+        d.status = e == hipSuccess ? QMV_OK : QMV_EHIP;
+    });
+    if (d.status != QMV_OK) return nullptr;
+    if (dev_out) *dev_out = dev;
+    return &d;
 }
 
 constexpr int64_t kMaxPrefillM = 65536;
@@ -419,6 +396,177 @@ int64_t prefill_table_bytes(const qmv_problem* probs, int32_t count)
     for (int32_t i = 0; i < count; ++i) tiles += prefill_tiles(probs[i].m, probs[i].w.n);
     return round_up((int64_t)sizeof(DevProblem) * count, 256) +
            round_up((kXcds + 1 + tiles + kPrefillTicketWords) * 8, 256) + kPrefillZeroBytes;
+}
+
+// The prefill workspace image: the problem table (longest rows first), the
+// tile table and its zeroed tickets, and the block of zeros; `grid` is the
+// persistent workgroup count.
+int32_t build_prefill_image(const qmv_problem* probs, int32_t count, int cus, std::vector<uint8_t>& img,
+                            int64_t& pbytes, int64_t& grid)
+{
+    const int64_t need = prefill_table_bytes(probs, count);
+    std::vector<int32_t> order(count);
+    for (int32_t i = 0; i < count; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return probs[a].w.k > probs[b].w.k; });
+    pbytes = round_up((int64_t)sizeof(DevProblem) * count, 256);
+    img.assign(need, 0);
+    DevProblem* dp = reinterpret_cast<DevProblem*>(img.data());
+    // Tile list, XCD-aware: workgroup b runs on XCD b % 8 (round-robin dispatch),
+    // so tiles that share an activation block (same problem and token block) go
+    // to one XCD's list and run back to back there, reusing that XCD's L2.  The
+    // token-block groups are spread over the XCDs longest first, to the least
+    // loaded one.
+    struct Group {
+        int32_t slot;
+        int64_t mt, ntiles, work;
+    };
+    std::vector<Group> groups;
+    for (int32_t slot = 0; slot < count; ++slot) {
+        const qmv_problem& p = probs[order[slot]];
+        DevProblem& d = dp[slot];
+        d.w = static_cast<const uint8_t*>(p.w.data);
+        d.sw = p.w.scale;
+        d.x8 = p.x8;
+        d.sx = p.sx;
+        d.y = p.y;
+        d.acc = p.acc;
+        d.n = (int32_t)p.w.n;
+        d.k = (int32_t)p.w.k;
+        d.m = (int32_t)p.m;
+        d.chunks = (int32_t)(row_stride(p.w.wtype, p.w.k) / 16);
+        d.tile_begin = 0;
+        d.wtype = p.w.wtype;
+        d.lanes_per_row = 1;
+        d.reserved = 0;
+        const int64_t mts = (p.m + kPrefillTileM - 1) / kPrefillTileM;
+        const int64_t nts = (p.w.n + kPrefillTileN - 1) / kPrefillTileN;
+        for (int64_t mt = 0; mt < mts; ++mt) groups.push_back({slot, mt, nts, nts * ((d.chunks + 1) / 2)});
+    }
+    std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.work > b.work; });
+    std::vector<std::vector<uint64_t>> lists(kXcds);
+    std::vector<int64_t> load(kXcds, 0);
+    for (const Group& gr : groups) {
+        int x = 0;
+        for (int i = 1; i < kXcds; ++i)
+            if (load[i] < load[x]) x = i;
+        load[x] += gr.work;
+        for (int64_t nt = 0; nt < gr.ntiles; ++nt)
+            lists[x].push_back(((uint64_t)gr.slot << 48) | ((uint64_t)gr.mt << 32) | (uint64_t)nt);
+    }
+    // Persistent workgroups, two per compute unit: each starts on its XCD's
+    // list and takes tiles by ticket (the tickets follow the entries and start
+    // at zero; the kernel leaves them at zero).
+    size_t longest = 0, total = 0;
+    for (const auto& l : lists) {
+        longest = std::max(longest, l.size());
+        total += l.size();
+    }
+    const int64_t per_xcd =
+        std::max<int64_t>(1, std::min<int64_t>({2 * std::max(1, cus / kXcds), kPrefillMaxGrid / kXcds, (int64_t)longest}));
+    grid = per_xcd * kXcds;
+    if (pbytes + (kXcds + 1 + (int64_t)total + kPrefillTicketWords) * 8 > need - kPrefillZeroBytes)
+        return QMV_EWORKSPACE;  // cannot happen: need covers every tile
+    uint64_t* tt = reinterpret_cast<uint64_t*>(img.data() + pbytes);
+    uint64_t pos = 0;
+    for (int x = 0; x < kXcds; ++x) {
+        tt[x] = pos;
+        for (uint64_t e : lists[x]) tt[kXcds + 1 + pos++] = e;
+    }
+    tt[kXcds] = pos;
+    return QMV_OK;
+}
+
+constexpr int kNoDevice = -1;
+
+}  // namespace
+
+// A launch plan: the workspace image of one problem list and the launch
+// parameters, made for one device.
+struct qmv_plan {
+    int32_t kind = 0;
+    int dev = kNoDevice;            // device the plan was made for (kNoDevice: none usable)
+    std::vector<uint8_t> image;     // uploaded into the workspace
+    Table table;                    // QMV_PLAN_GEMV: launch parameters per weight type
+    int64_t pbytes = 0, grid = 0;   // QMV_PLAN_PREFILL: tile table offset, persistent grid
+};
+
+namespace {
+
+// A plan for the current device; with no usable device it is made for a
+// 256-CU part and cannot be uploaded or launched.
+int32_t make_plan(int32_t kind, const qmv_problem* probs, int32_t count, qmv_plan& plan)
+{
+    int dev = kNoDevice;
+    const DeviceSetup* d = device_setup(&dev);
+    const int cus = d ? d->cus : 256;
+    plan.kind = kind;
+    plan.dev = d ? dev : kNoDevice;
+    if (kind == QMV_PLAN_GEMV) {
+        const int32_t st = build_table(probs, count, cus, plan.table);
+        if (st != QMV_OK) return st;
+        plan.image.swap(plan.table.bytes);
+        return QMV_OK;
+    }
+    return build_prefill_image(probs, count, cus, plan.image, plan.pbytes, plan.grid);
+}
+
+int32_t check_plan_use(const qmv_plan* plan, const void* workspace, int64_t ws_bytes)
+{
+    if (!plan) return QMV_EINVAL;
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < (int64_t)plan->image.size()) return QMV_EWORKSPACE;
+    if (plan->dev == kNoDevice) return QMV_EHIP;
+    return QMV_OK;
+}
+
+int32_t upload_plan(const qmv_plan& plan, void* workspace, hipStream_t s)
+{
+    return hip_status(hipMemcpyAsync(workspace, plan.image.data(), plan.image.size(), hipMemcpyHostToDevice, s));
+}
+
+int32_t launch_plan(const qmv_plan& plan, void* workspace, hipStream_t s)
+{
+    uint8_t* base = static_cast<uint8_t*>(workspace);
+    if (plan.kind == QMV_PLAN_PREFILL)
+        return hip_status(launch_prefill(reinterpret_cast<const DevProblem*>(base),
+                                         reinterpret_cast<const uint64_t*>(base + plan.pbytes), plan.grid,
+                                         reinterpret_cast<const int8_t*>(base + plan.image.size() - kPrefillZeroBytes),
+                                         s));
+    const Table& t = plan.table;
+    const DevProblem* dp = reinterpret_cast<const DevProblem*>(base);
+    for (int wt = 1; wt <= 3; ++wt) {
+        if (t.count[wt] == 0) continue;
+        uint32_t* words = reinterpret_cast<uint32_t*>(base + t.region[wt]);
+        hipError_t e;
+        if (wt == QMV_W_INT8_G128)
+            e = launch_gemv_grouped(dp, words, t.count[wt], t.max_m[wt], (size_t)t.slot_bytes[wt], s);
+        else if (t.stream[wt])
+            e = launch_gemv_stream(dp, words, t.nb[wt], wt, t.max_m[wt], t.slot_bytes[wt], s);
+        else
+            e = launch_gemv(dp, words, 0, t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
+        if (e != hipSuccess) return QMV_EHIP;
+    }
+    return QMV_OK;
+}
+
+// A plan made, uploaded and launched in one call (qmv_gemv, qmv_gemm_prefill).
+// The upload copies from pageable host memory that is freed on return, which
+// a stream capture would keep a pointer to: such calls are refused while the
+// stream is capturing.
+int32_t one_shot(int32_t kind, const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes,
+                 int64_t bound, void* stream)
+{
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < bound) return QMV_EWORKSPACE;
+    const hipStream_t s = as_stream(stream);
+    qmv_plan plan;
+    int32_t st = make_plan(kind, probs, count, plan);
+    if (st != QMV_OK) return st;
+    st = check_plan_use(&plan, workspace, ws_bytes);
+    if (st != QMV_OK) return st;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) return QMV_EHIP;
+    if (cap != hipStreamCaptureStatusNone) return QMV_EUNSUPPORTED;
+    st = upload_plan(plan, workspace, s);
+    return st != QMV_OK ? st : launch_plan(plan, workspace, s);
 }
 
 }  // namespace
@@ -569,46 +717,7 @@ int32_t qmv_glu_quantize(const float* gate, const float* up, int64_t m, int64_t 
 int64_t qmv_gemv_workspace_bytes(const qmv_problem* probs, int32_t count)
 {
     if (check_problems(probs, count, QMV_MAX_GEMV_M) != QMV_OK) return -1;
-    int cus = 0;
-    device_cus(&cus);
-    return table_bound(probs, count, cus);
-}
-
-int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, uint32_t flags,
-                 void* stream)
-{
-    int32_t st = check_problems(probs, count, QMV_MAX_GEMV_M);
-    if (st != QMV_OK) return st;
-    if (flags & ~(uint32_t)QMV_F_TABLE_READY) return QMV_EINVAL;
-    std::shared_ptr<const Table> tp;
-    st = get_table(probs, count, tp);
-    if (st != QMV_OK) return st;
-    const Table& t = *tp;
-    int cus = 0;
-    device_cus(&cus);
-    if (!workspace || !aligned(workspace, 256) || ws_bytes < table_bound(probs, count, cus) ||
-        ws_bytes < (int64_t)t.bytes.size())
-        return QMV_EWORKSPACE;
-    const hipStream_t s = as_stream(stream);
-    if (!(flags & QMV_F_TABLE_READY)) {
-        hipError_t e = hipMemcpyAsync(workspace, t.bytes.data(), t.bytes.size(), hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return QMV_EHIP;
-    }
-    uint8_t* base = static_cast<uint8_t*>(workspace);
-    const DevProblem* dp = reinterpret_cast<const DevProblem*>(base);
-    for (int wt = 1; wt <= 3; ++wt) {
-        if (t.count[wt] == 0) continue;
-        uint32_t* words = reinterpret_cast<uint32_t*>(base + t.region[wt]);
-        hipError_t e;
-        if (wt == QMV_W_INT8_G128)
-            e = launch_gemv_grouped(dp, words, t.count[wt], t.max_m[wt], (size_t)t.slot_bytes[wt], s);
-        else if (t.stream[wt])
-            e = launch_gemv_stream(dp, words, t.nb[wt], wt, t.max_m[wt], t.slot_bytes[wt], s);
-        else
-            e = launch_gemv(dp, words, 0, t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
-        if (e != hipSuccess) return QMV_EHIP;
-    }
-    return QMV_OK;
+    return table_bound(probs, count, 0);
 }
 
 int64_t qmv_prefill_workspace_bytes(const qmv_problem* probs, int32_t count)
@@ -617,95 +726,68 @@ int64_t qmv_prefill_workspace_bytes(const qmv_problem* probs, int32_t count)
     return prefill_table_bytes(probs, count);
 }
 
-int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, uint32_t flags,
-                         void* stream)
+int64_t qmv_workspace_bytes(const qmv_problem* probs, int32_t count)
 {
-    int32_t st = check_prefill(probs, count);
-    if (st != QMV_OK) return st;
-    if (flags & ~(uint32_t)QMV_F_TABLE_READY) return QMV_EINVAL;
-    const int64_t need = prefill_table_bytes(probs, count);
-    if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return QMV_EWORKSPACE;
-    // Problem table: longest rows first.
-    std::vector<int32_t> order(count);
-    for (int32_t i = 0; i < count; ++i) order[i] = i;
-    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return probs[a].w.k > probs[b].w.k; });
-    const int64_t pbytes = round_up((int64_t)sizeof(DevProblem) * count, 256);
-    std::vector<uint8_t> img(need, 0);
-    DevProblem* dp = reinterpret_cast<DevProblem*>(img.data());
-    // Tile list, XCD-aware: workgroup b runs on XCD b % 8 (round-robin dispatch),
-    // so tiles that share an activation block (same problem and token block) go
-    // to one XCD's list and run back to back there, reusing that XCD's L2.  The
-    // token-block groups are spread over the XCDs longest first, to the least
-    // loaded one.
-    struct Group {
-        int32_t slot;
-        int64_t mt, ntiles, work;
-    };
-    std::vector<Group> groups;
-    for (int32_t slot = 0; slot < count; ++slot) {
-        const qmv_problem& p = probs[order[slot]];
-        DevProblem& d = dp[slot];
-        d.w = static_cast<const uint8_t*>(p.w.data);
-        d.sw = p.w.scale;
-        d.x8 = p.x8;
-        d.sx = p.sx;
-        d.y = p.y;
-        d.acc = p.acc;
-        d.n = (int32_t)p.w.n;
-        d.k = (int32_t)p.w.k;
-        d.m = (int32_t)p.m;
-        d.chunks = (int32_t)(row_stride(p.w.wtype, p.w.k) / 16);
-        d.tile_begin = 0;
-        d.wtype = p.w.wtype;
-        d.lanes_per_row = 1;
-        d.reserved = 0;
-        const int64_t mts = (p.m + kPrefillTileM - 1) / kPrefillTileM;
-        const int64_t nts = (p.w.n + kPrefillTileN - 1) / kPrefillTileN;
-        for (int64_t mt = 0; mt < mts; ++mt) groups.push_back({slot, mt, nts, nts * ((d.chunks + 1) / 2)});
-    }
-    std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.work > b.work; });
-    std::vector<std::vector<uint64_t>> lists(kXcds);
-    std::vector<int64_t> load(kXcds, 0);
-    for (const Group& gr : groups) {
-        int x = 0;
-        for (int i = 1; i < kXcds; ++i)
-            if (load[i] < load[x]) x = i;
-        load[x] += gr.work;
-        for (int64_t nt = 0; nt < gr.ntiles; ++nt)
-            lists[x].push_back(((uint64_t)gr.slot << 48) | ((uint64_t)gr.mt << 32) | (uint64_t)nt);
-    }
-    // Persistent workgroups, two per compute unit: each starts on its XCD's
-    // list and takes tiles by ticket (the tickets follow the entries and start
-    // at zero; the kernel leaves them at zero).
-    int cus = 256;
-    device_cus(&cus);
-    size_t longest = 0, total = 0;
-    for (const auto& l : lists) {
-        longest = std::max(longest, l.size());
-        total += l.size();
-    }
-    const int64_t per_xcd =
-        std::max<int64_t>(1, std::min<int64_t>({2 * std::max(1, cus / kXcds), kPrefillMaxGrid / kXcds, (int64_t)longest}));
-    const int64_t grid = per_xcd * kXcds;
-    if (pbytes + (kXcds + 1 + (int64_t)total + kPrefillTicketWords) * 8 > need - kPrefillZeroBytes)
-        return QMV_EWORKSPACE;  // cannot happen: need covers every tile
-    uint64_t* tt = reinterpret_cast<uint64_t*>(img.data() + pbytes);
-    uint64_t pos = 0;
-    for (int x = 0; x < kXcds; ++x) {
-        tt[x] = pos;
-        for (uint64_t e : lists[x]) tt[kXcds + 1 + pos++] = e;
-    }
-    tt[kXcds] = pos;
-    const hipStream_t s = as_stream(stream);
-    if (!(flags & QMV_F_TABLE_READY)) {
-        hipError_t e = hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) return QMV_EHIP;
-    }
-    const uint8_t* base = static_cast<const uint8_t*>(workspace);
-    return hip_status(launch_prefill(reinterpret_cast<const DevProblem*>(base),
-                                     reinterpret_cast<const uint64_t*>(base + pbytes), grid,
-                                     reinterpret_cast<const int8_t*>(base + need - kPrefillZeroBytes), s));
+    const int64_t g = qmv_gemv_workspace_bytes(probs, count);
+    const int64_t p = qmv_prefill_workspace_bytes(probs, count);
+    return std::max(g, p);
 }
+
+int32_t qmv_gemv(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, void* stream)
+{
+    const int32_t st = check_problems(probs, count, QMV_MAX_GEMV_M);
+    if (st != QMV_OK) return st;
+    return one_shot(QMV_PLAN_GEMV, probs, count, workspace, ws_bytes, table_bound(probs, count, 0), stream);
+}
+
+int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspace, int64_t ws_bytes, void* stream)
+{
+    const int32_t st = check_prefill(probs, count);
+    if (st != QMV_OK) return st;
+    return one_shot(QMV_PLAN_PREFILL, probs, count, workspace, ws_bytes, prefill_table_bytes(probs, count), stream);
+}
+
+int32_t qmv_plan_create(int32_t kind, const qmv_problem* probs, int32_t count, qmv_plan** plan)
+{
+    if (!plan) return QMV_EINVAL;
+    *plan = nullptr;
+    int32_t st;
+    if (kind == QMV_PLAN_GEMV)
+        st = check_problems(probs, count, QMV_MAX_GEMV_M);
+    else if (kind == QMV_PLAN_PREFILL)
+        st = check_prefill(probs, count);
+    else
+        return QMV_EINVAL;
+    if (st != QMV_OK) return st;
+    qmv_plan* p = new (std::nothrow) qmv_plan;
+    if (!p) return QMV_EINVAL;
+    st = make_plan(kind, probs, count, *p);
+    if (st != QMV_OK) {
+        delete p;
+        return st;
+    }
+    *plan = p;
+    return QMV_OK;
+}
+
+int64_t qmv_plan_workspace_bytes(const qmv_plan* plan)
+{
+    return plan ? (int64_t)plan->image.size() : -1;
+}
+
+int32_t qmv_plan_upload(const qmv_plan* plan, void* workspace, int64_t ws_bytes, void* stream)
+{
+    const int32_t st = check_plan_use(plan, workspace, ws_bytes);
+    return st != QMV_OK ? st : upload_plan(*plan, workspace, as_stream(stream));
+}
+
+int32_t qmv_plan_launch(const qmv_plan* plan, void* workspace, int64_t ws_bytes, void* stream)
+{
+    const int32_t st = check_plan_use(plan, workspace, ws_bytes);
+    return st != QMV_OK ? st : launch_plan(*plan, workspace, as_stream(stream));
+}
+
+void qmv_plan_destroy(qmv_plan* plan) { delete plan; }
 
 int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k)
 {
@@ -717,9 +799,9 @@ int32_t qmv_read_probe(const void* data, int64_t bytes, uint32_t* out, void* str
 {
     if (!data || !out || bytes < 0 || !aligned(data, 16) || (bytes & 15)) return QMV_EINVAL;
     if (bytes == 0) return QMV_OK;
-    int cus = 0;
-    device_cus(&cus);
-    return hip_status(launch_read_probe(data, bytes, out, cus, as_stream(stream)));
+    const DeviceSetup* d = device_setup(nullptr);
+    if (!d) return QMV_EHIP;
+    return hip_status(launch_read_probe(data, bytes, out, d->cus, as_stream(stream)));
 }
 
 int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int64_t k, int32_t* idx,
@@ -760,6 +842,7 @@ int32_t qmv_lmhead_sketch_argmax(const uint16_t* w_bf16, const void* sketch, con
     if (!w_bf16 || !sketch || !x || !idx || !aligned(w_bf16, 16) || !aligned(sketch, 256)) return QMV_EINVAL;
     if (v < 1 || v > QMV_MAX_N || k < 8 || k > kSketchMaxK || k % 8) return QMV_ESHAPE;
     if (!workspace || !aligned(workspace, 256) || ws_bytes < sketch_workspace_bytes(v)) return QMV_EWORKSPACE;
+    if (!device_setup(nullptr)) return QMV_EHIP;
     return hip_status(launch_sketch_argmax(w_bf16, sketch, x, v, k, idx, max_logit, candidates, scores, workspace,
                                            as_stream(stream)));
 }

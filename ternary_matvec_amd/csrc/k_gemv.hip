@@ -330,11 +330,6 @@ hipError_t launch_one(const DevProblem* probs, const uint32_t* tiles, int32_t ti
                       int max_chunks, hipStream_t s)
 {
     const size_t lds = lds_bytes(MT, WT, max_chunks);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<MT, WT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL((k_gemv<MT, WT>), dim3((unsigned)tile_count), dim3(kBlock), lds, s, probs, tiles,
                        tile_begin);
     return hipGetLastError();
@@ -361,6 +356,32 @@ int gemv_rows_per_tile(int wtype, int max_m)
 int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks)
 {
     return (int64_t)lds_bytes(mt_for(max_m), wtype, max_chunks);
+}
+
+namespace {
+template <int MT, int WT>
+hipError_t lds_limit_one()
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<MT, WT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+}
+
+template <int WT>
+hipError_t lds_limit_wt()
+{
+    hipError_t e = lds_limit_one<1, WT>();
+    if (e == hipSuccess) e = lds_limit_one<2, WT>();
+    if (e == hipSuccess) e = lds_limit_one<4, WT>();
+    if (e == hipSuccess) e = lds_limit_one<8, WT>();
+    if (e == hipSuccess) e = lds_limit_one<16, WT>();
+    return e;
+}
+}  // namespace
+
+hipError_t setup_workgroup_gemv_attributes()
+{
+    hipError_t e = lds_limit_wt<1>();
+    return e == hipSuccess ? lds_limit_wt<2>() : e;
 }
 
 hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,

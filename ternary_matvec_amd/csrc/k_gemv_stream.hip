@@ -59,6 +59,7 @@ constexpr int kZBytes = 192;                   // staged bytes per 16-byte terna
 constexpr int kXBytes = 16;                    // staged bytes per 16-byte int8 chunk per token
 constexpr uint32_t kEnd = 0xffffffffu;         // no tile
 constexpr int kNonTemporal = 2;                // buffer instruction cache policy: nt
+constexpr int kDescSlots = 3;                  // tile descriptors in LDS, used round robin
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
@@ -366,7 +367,7 @@ __device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, in
 // Schedule words: [counters: 8 tile counters + 8 done counters, 64 words
 // apart][first tile entry of each workgroup][8 x (list offset, list size)]
 // [tile entries of the 8 XCD lists].
-// LDS: [2 tile slots of slot_bytes][2 tile descriptors][corr: 2 x MT]
+// LDS: [2 tile slots of slot_bytes][3 tile descriptors][corr: 2 x MT]
 template <int MT, int WT>
 __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem* __restrict__ probs,
                                                                uint32_t* __restrict__ sched, int32_t slot_bytes)
@@ -376,8 +377,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    // Tile q's descriptor is in descs[q % 3]: the staging wave writes tile q + 2's
+    // after barrier q + 1, and the compute waves last read that slot (as tile
+    // q - 1's) before barrier q.
     TileDesc* const descs = reinterpret_cast<TileDesc*>(smem + 2 * (size_t)slot_bytes);
-    int* const corr_base = reinterpret_cast<int*>(descs + 2);
+    int* const corr_base = reinterpret_cast<int*>(descs + kDescSlots);
 
     const int xcd = blockIdx.x % kStreamXcds;
     const uint32_t wgs = (gridDim.x - xcd + kStreamXcds - 1) / kStreamXcds;   // workgroups of this XCD
@@ -409,7 +413,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
         const uint32_t list_size = cload_ptr(hdr)[2 * xcd + 1];
         const uint32_t* const list = hdr + 2 * kStreamXcds + list_off;
         bool first = true;
-        for (int par = 0; te != kEnd; par ^= 1) {
+        for (int par = 0, q = 0; te != kEnd; par ^= 1, q = q == kDescSlots - 1 ? 0 : q + 1) {
+            const int qn = q == kDescSlots - 1 ? 0 : q + 1;   // the next tile's descriptor slot
             stage<MT, WT>(T, lane, smem + (size_t)par * slot_bytes, corr_base + par * MT, [&] {
                 if (first) {
                     // Tile 0: release the compute waves' weight prefetch only once
@@ -441,12 +446,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
             }
             if (nx != kEnd && par == 0 && nx == te1) {
                 T = T1;
-                if (lane == 0) descs[1] = d1;
+                if (lane == 0) descs[qn] = d1;
             } else if (nx != kEnd) {
                 T = tile_at<kCB>(probs, nx, 0, lane);
-                if (lane == 0) descs[par ^ 1] = desc_of(T, nx);
+                if (lane == 0) descs[qn] = desc_of(T, nx);
             } else if (lane == 0) {
-                descs[par ^ 1].te = kEnd;
+                descs[qn].te = kEnd;
             }
             te = nx;
             __syncthreads();
@@ -478,12 +483,12 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
 #pragma unroll
         for (int h = 0; h < kRPL; ++h) ring[r][h] = load_step(cur, r, cur.voff + h * cur.voff_r);
 
-    for (int par = 0;; par ^= 1) {
+    for (int par = 0, q = 0;; par ^= 1, q = q == kDescSlots - 1 ? 0 : q + 1) {
         __syncthreads();   // this tile is staged and the next one named; every wave is done with the last
         // The next tile (after the last one: the tile itself, with its batch loads
         // past the matrix end, so every path is the same).
-        const TileDesc cd = desc_load(descs + par);
-        const TileDesc nd = desc_load(descs + (par ^ 1));
+        const TileDesc cd = desc_load(descs + q);
+        const TileDesc nd = desc_load(descs + (q == kDescSlots - 1 ? 0 : q + 1));
         const bool has_next = nd.te != kEnd;
         const Tile nxt = tile_of<kCB>(has_next ? nd : cd, wave, lane);
         const uint8_t* zs = smem + (size_t)par * slot_bytes;
@@ -608,11 +613,6 @@ template <int MT, int WT>
 hipError_t launch_stream_one(const DevProblem* probs, uint32_t* sched, int nb, int32_t slot_bytes, hipStream_t s)
 {
     const size_t lds = gemv_stream_lds_bytes(MT, slot_bytes);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL((k_gemv_stream<MT, WT>), dim3((unsigned)nb), dim3(kStreamThreads), lds, s, probs, sched,
                        slot_bytes);
     return hipGetLastError();
@@ -632,17 +632,13 @@ int64_t gemv_stream_slot_bytes(int wtype, int mt, int chunks, int lanes)
 
 size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes)
 {
-    return (size_t)(2 * slot_bytes + 2 * (int64_t)sizeof(TileDesc) + 2 * mt * (int64_t)sizeof(int));
+    return (size_t)(2 * slot_bytes + kDescSlots * (int64_t)sizeof(TileDesc) + 2 * mt * (int64_t)sizeof(int));
 }
 
 template <int MT, int WT>
 int occupancy_one(int64_t slot_bytes)
 {
     const size_t lds = gemv_stream_lds_bytes(MT, slot_bytes);
-    if (lds > 64 * 1024 &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-        return 0;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
                                                      kStreamThreads, lds) != hipSuccess)
@@ -654,6 +650,24 @@ int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes)
 {
     if (wtype == 1) return max_m <= 1 ? occupancy_one<1, 1>(slot_bytes) : occupancy_one<2, 1>(slot_bytes);
     return max_m <= 1 ? occupancy_one<1, 2>(slot_bytes) : occupancy_one<2, 2>(slot_bytes);
+}
+
+namespace {
+template <int MT, int WT>
+hipError_t stream_lds_limit()
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+}
+}  // namespace
+
+hipError_t setup_stream_attributes()
+{
+    hipError_t e = stream_lds_limit<1, 1>();
+    if (e == hipSuccess) e = stream_lds_limit<2, 1>();
+    if (e == hipSuccess) e = stream_lds_limit<1, 2>();
+    if (e == hipSuccess) e = stream_lds_limit<2, 2>();
+    return e;
 }
 
 hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,

@@ -194,11 +194,6 @@ template <int MT>
 hipError_t launch_grouped_one(const DevProblem* probs, const uint32_t* tiles, int32_t count, size_t lds,
                               hipStream_t s)
 {
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_grouped<MT>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL((k_gemv_grouped<MT>), dim3((unsigned)count), dim3(kBlock), lds, s, probs, tiles);
     return hipGetLastError();
 }
@@ -235,6 +230,25 @@ size_t grouped_lds_bytes(int64_t m, int64_t k)
 {
     const int64_t kp = (k + 31) / 32 * 32;
     return (size_t)(m * kp + 4 * m * (kp / 32));
+}
+
+namespace {
+template <int MT>
+hipError_t grouped_lds_limit()
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_grouped<MT>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+}
+}  // namespace
+
+hipError_t setup_grouped_attributes()
+{
+    hipError_t e = grouped_lds_limit<1>();
+    if (e == hipSuccess) e = grouped_lds_limit<2>();
+    if (e == hipSuccess) e = grouped_lds_limit<4>();
+    if (e == hipSuccess) e = grouped_lds_limit<8>();
+    if (e == hipSuccess) e = grouped_lds_limit<16>();
+    return e;
 }
 
 hipError_t launch_gemv_grouped(const DevProblem* probs, const uint32_t* tiles, int32_t count, int max_m, size_t lds,

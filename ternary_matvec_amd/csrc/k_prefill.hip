@@ -594,12 +594,15 @@ __global__ __launch_bounds__(kBlock, 2) void k_prefill(const DevProblem* __restr
 
 int64_t prefill_tiles(int64_t m, int64_t n) { return ((m + kPBM - 1) / kPBM) * ((n + kPBN - 1) / kPBN); }
 
+hipError_t setup_prefill_attributes()
+{
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)kMaxLds);
+}
+
 hipError_t launch_prefill(const DevProblem* probs, const uint64_t* table, int64_t grid, const int8_t* zeros,
                           hipStream_t s)
 {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPrefillLds);
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_prefill, dim3((unsigned)grid), dim3(kBlock), kPrefillLds, s, probs, table, zeros);
     return hipGetLastError();
 }

@@ -535,6 +535,16 @@ hipError_t launch_sketch_build(const uint16_t* w, int64_t v, int64_t k, void* sk
     return hipGetLastError();
 }
 
+hipError_t setup_sketch_attributes()
+{
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_plan),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_rescore),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    return e;
+}
+
 hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const float* x, int64_t v, int64_t k,
                                 int32_t* idx, float* max_logit, int32_t* ncand, float* scores, void* workspace,
                                 hipStream_t s)
@@ -550,9 +560,6 @@ hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const flo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t plan_lds = 8 * (size_t)k + 20 * (size_t)kw;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_plan), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)plan_lds);
-    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_sketch_plan, dim3(1), dim3(kSkPlanThreads), plan_lds, s, x, (int)k,
                        (const uint64_t*)sorted, reinterpret_cast<const SketchHeader*>(base), ws);
     e = hipGetLastError();
@@ -563,9 +570,6 @@ hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const flo
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_sketch_select, dim3(1), dim3(kSkPlanThreads), 0, s, v, ws);
     e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_rescore),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(4 * k));
     if (e != hipSuccess) return e;
     const int nwg = (int)((v + kSkRowsPerBlock - 1) / kSkRowsPerBlock);
     hipLaunchKernelGGL(k_sketch_rescore, dim3((unsigned)nwg), dim3(kBlock), (size_t)(4 * k), s, w, x, v, (int)k, ws);

@@ -66,6 +66,14 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Once-per-device set-up of the kernel translation units: each raises its
+// kernels' dynamic-LDS limit to the whole kMaxLds, so launches never set
+// attributes.
+hipError_t setup_workgroup_gemv_attributes();
+hipError_t setup_stream_attributes();
+hipError_t setup_grouped_attributes();
+hipError_t setup_prefill_attributes();
+hipError_t setup_sketch_attributes();
 // Launchers implemented in the kernel translation units.
 hipError_t launch_rmsnorm_quantize(const float* x, const float* weight, int64_t m, int64_t k, float eps, int8_t* x8,
                                    float* sx, hipStream_t s);

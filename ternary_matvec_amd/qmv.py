@@ -25,8 +25,9 @@ QMV_W_INT8 = 2
 QMV_W_INT8_G128 = 3
 QMV_WEIGHT_GROUP = 128
 QMV_ACT_GROUP = 32
-QMV_F_TABLE_READY = 1
 QMV_MAX_GEMV_M = 16
+QMV_PLAN_GEMV = 1
+QMV_PLAN_PREFILL = 2
 
 _c_i32, _c_i64, _c_u32, _c_ptr, _c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
 
@@ -69,10 +70,16 @@ SIGNATURES = {
     "qmv_pack_int8_grouped": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, ctypes.POINTER(qmv_weight),
                                        _c_ptr]),
     "qmv_quantize_act_grouped": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "qmv_workspace_bytes": (_c_i64, [ctypes.POINTER(qmv_problem), _c_i32]),
     "qmv_gemv_workspace_bytes": (_c_i64, [ctypes.POINTER(qmv_problem), _c_i32]),
     "qmv_prefill_workspace_bytes": (_c_i64, [ctypes.POINTER(qmv_problem), _c_i32]),
-    "qmv_gemv": (_c_i32, [ctypes.POINTER(qmv_problem), _c_i32, _c_ptr, _c_i64, _c_u32, _c_ptr]),
-    "qmv_gemm_prefill": (_c_i32, [ctypes.POINTER(qmv_problem), _c_i32, _c_ptr, _c_i64, _c_u32, _c_ptr]),
+    "qmv_gemv": (_c_i32, [ctypes.POINTER(qmv_problem), _c_i32, _c_ptr, _c_i64, _c_ptr]),
+    "qmv_gemm_prefill": (_c_i32, [ctypes.POINTER(qmv_problem), _c_i32, _c_ptr, _c_i64, _c_ptr]),
+    "qmv_plan_create": (_c_i32, [_c_i32, ctypes.POINTER(qmv_problem), _c_i32, ctypes.POINTER(_c_ptr)]),
+    "qmv_plan_workspace_bytes": (_c_i64, [_c_ptr]),
+    "qmv_plan_upload": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_ptr]),
+    "qmv_plan_launch": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_ptr]),
+    "qmv_plan_destroy": (None, [_c_ptr]),
     "qmv_lmhead_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
     "qmv_lmhead_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64,
                                    _c_ptr]),
@@ -291,27 +298,76 @@ def qmv_prefill_workspace_bytes(arr) -> int:
     return int(load().qmv_prefill_workspace_bytes(arr, len(arr)))
 
 
-def _grouped(fn_name, ws_fn, problems, workspace, flags, stream):
-    arr = problems if isinstance(problems, ctypes.Array) else problem_array(problems)
+def qmv_workspace_bytes(arr) -> int:
+    return int(load().qmv_workspace_bytes(arr, len(arr)))
+
+
+def _as_array(problems):
+    return problems if isinstance(problems, ctypes.Array) else problem_array(problems)
+
+
+def _grouped(fn_name, ws_fn, problems, workspace, stream):
+    arr = _as_array(problems)
     need = ws_fn(arr)
     if need < 0:
         raise QmvError(QMV_ESHAPE, fn_name)
     if workspace is None:
         dev = torch.device("cuda", torch.cuda.current_device())
         workspace = _alloc_aligned(max(need, 256), dev)
-    _check(getattr(load(), fn_name)(arr, len(arr), _ptr(workspace), workspace.numel(), flags, _stream(stream)),
-           fn_name)
+    _check(getattr(load(), fn_name)(arr, len(arr), _ptr(workspace), workspace.numel(), _stream(stream)), fn_name)
     return workspace
 
 
-def qmv_gemv(problems, workspace=None, flags=0, stream=None):
-    """Grouped GEMV (1..16 tokens per problem) in one launch; returns the workspace used."""
-    return _grouped("qmv_gemv", qmv_gemv_workspace_bytes, problems, workspace, flags, stream)
+def qmv_gemv(problems, workspace=None, stream=None):
+    """Grouped GEMV (1..16 tokens per problem): schedule, upload and launch in one call;
+    returns the workspace used.  For a list launched again and again, use Plan."""
+    return _grouped("qmv_gemv", qmv_gemv_workspace_bytes, problems, workspace, stream)
 
 
-def qmv_gemm_prefill(problems, workspace=None, flags=0, stream=None):
-    """Grouped int8-MFMA GEMM for any number of tokens; returns the workspace used."""
-    return _grouped("qmv_gemm_prefill", qmv_prefill_workspace_bytes, problems, workspace, flags, stream)
+def qmv_gemm_prefill(problems, workspace=None, stream=None):
+    """Grouped int8-MFMA GEMM for any number of tokens, in one call; returns the workspace used."""
+    return _grouped("qmv_gemm_prefill", qmv_prefill_workspace_bytes, problems, workspace, stream)
+
+
+class Plan:
+    """qmv_plan_create/upload/launch/destroy: one problem list scheduled once, its
+    tables uploaded into its workspace, then launched many times (kernels only)."""
+
+    def __init__(self, kind, problems, workspace=None, stream=None):
+        lib = load()
+        self.arr = _as_array(problems)          # keeps the host structs alive with the plan
+        self._lib = lib
+        self._h = _c_ptr()
+        _check(lib.qmv_plan_create(kind, self.arr, len(self.arr), ctypes.byref(self._h)), "qmv_plan_create")
+        self.kind = kind
+        need = int(lib.qmv_plan_workspace_bytes(self._h))
+        if workspace is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+            workspace = _alloc_aligned(max(need, 256), dev)
+        self.workspace = workspace
+        self.upload(stream)
+
+    def upload(self, stream=None):
+        _check(self._lib.qmv_plan_upload(self._h, _ptr(self.workspace), self.workspace.numel(), _stream(stream)),
+               "qmv_plan_upload")
+
+    def launch(self, stream=None):
+        _check(self._lib.qmv_plan_launch(self._h, _ptr(self.workspace), self.workspace.numel(), _stream(stream)),
+               "qmv_plan_launch")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.qmv_plan_destroy(h)
+            self._h = None
+
+
+def gemv_plan(problems, workspace=None, stream=None):
+    return Plan(QMV_PLAN_GEMV, problems, workspace, stream)
+
+
+def prefill_plan(problems, workspace=None, stream=None):
+    return Plan(QMV_PLAN_PREFILL, problems, workspace, stream)
 
 
 def qmv_lmhead_workspace_bytes(v: int, k: int) -> int:

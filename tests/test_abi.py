@@ -138,33 +138,63 @@ def test_gemv_validation(lib):
     arr = (qmv.qmv_problem * 2)(_problem(), _problem(n=100, k=1152, m=3))
     need = lib.qmv_gemv_workspace_bytes(arr, 2)
     assert need > 0 and need % 256 == 0
+    assert lib.qmv_workspace_bytes(arr, 2) >= need
     # workspace missing / too small / misaligned
-    assert lib.qmv_gemv(arr, 2, None, 0, 0, None) == qmv.QMV_EWORKSPACE
-    assert lib.qmv_gemv(arr, 2, _fake(1 << 20), need - 1, 0, None) == qmv.QMV_EWORKSPACE
-    assert lib.qmv_gemv(arr, 2, _fake((1 << 20) + 64), need, 0, None) == qmv.QMV_EWORKSPACE
-    # bad flags
-    assert lib.qmv_gemv(arr, 2, _fake(1 << 20), need, 4, None) == qmv.QMV_EINVAL
+    assert lib.qmv_gemv(arr, 2, None, 0, None) == qmv.QMV_EWORKSPACE
+    assert lib.qmv_gemv(arr, 2, _fake(1 << 20), need - 1, None) == qmv.QMV_EWORKSPACE
+    assert lib.qmv_gemv(arr, 2, _fake((1 << 20) + 64), need, None) == qmv.QMV_EWORKSPACE
     # m out of range for the GEMV
     bad = (qmv.qmv_problem * 1)(_problem(m=17))
-    assert lib.qmv_gemv(bad, 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_ESHAPE
+    assert lib.qmv_gemv(bad, 1, _fake(1 << 20), 1 << 20, None) == qmv.QMV_ESHAPE
     assert lib.qmv_gemv_workspace_bytes(bad, 1) == -1
+    assert lib.qmv_workspace_bytes(bad, 1) == lib.qmv_prefill_workspace_bytes(bad, 1) > 0
     # unknown weight type, reserved field, misaligned weights, null y
     bad = (qmv.qmv_problem * 1)(_problem(wtype=9))
-    assert lib.qmv_gemv(bad, 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EUNSUPPORTED
+    assert lib.qmv_gemv(bad, 1, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EUNSUPPORTED
+    assert lib.qmv_workspace_bytes(bad, 1) == -1
     p = _problem()
     p.w.reserved = 1
-    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EINVAL
+    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EINVAL
     p = _problem(data=4100)
-    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EINVAL
+    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EINVAL
     p = _problem()
     p.y = None
-    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EINVAL
+    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EINVAL
     # activations too large to stage for 16 tokens
     big = (qmv.qmv_problem * 1)(_problem(n=64, k=1 << 20, m=16))
-    assert lib.qmv_gemv(big, 1, _fake(1 << 20), 1 << 30, 0, None) == qmv.QMV_ESHAPE
+    assert lib.qmv_gemv(big, 1, _fake(1 << 20), 1 << 30, None) == qmv.QMV_ESHAPE
     # count
-    assert lib.qmv_gemv(arr, 0, _fake(1 << 20), need, 0, None) == qmv.QMV_ESHAPE
-    assert lib.qmv_gemv(None, 1, _fake(1 << 20), need, 0, None) == qmv.QMV_EINVAL
+    assert lib.qmv_gemv(arr, 0, _fake(1 << 20), need, None) == qmv.QMV_ESHAPE
+    assert lib.qmv_gemv(None, 1, _fake(1 << 20), need, None) == qmv.QMV_EINVAL
+
+
+def test_plan_validation(lib):
+    import torch
+    arr = (qmv.qmv_problem * 2)(_problem(), _problem(n=100, k=1152, m=3))
+    h = ctypes.c_void_p()
+    assert lib.qmv_plan_create(3, arr, 2, ctypes.byref(h)) == qmv.QMV_EINVAL
+    assert lib.qmv_plan_create(qmv.QMV_PLAN_GEMV, arr, 2, None) == qmv.QMV_EINVAL
+    assert lib.qmv_plan_create(qmv.QMV_PLAN_GEMV, arr, 0, ctypes.byref(h)) == qmv.QMV_ESHAPE
+    bad = (qmv.qmv_problem * 1)(_problem(m=17))
+    assert lib.qmv_plan_create(qmv.QMV_PLAN_GEMV, bad, 1, ctypes.byref(h)) == qmv.QMV_ESHAPE and not h.value
+    g = (qmv.qmv_problem * 1)(_problem(wtype=qmv.QMV_W_INT8_G128))
+    assert lib.qmv_plan_create(qmv.QMV_PLAN_PREFILL, g, 1, ctypes.byref(h)) == qmv.QMV_EUNSUPPORTED
+    assert lib.qmv_plan_workspace_bytes(None) == -1
+    assert lib.qmv_plan_upload(None, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EINVAL
+    assert lib.qmv_plan_launch(None, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EINVAL
+    lib.qmv_plan_destroy(None)
+    for kind in (qmv.QMV_PLAN_GEMV, qmv.QMV_PLAN_PREFILL):
+        assert lib.qmv_plan_create(kind, arr, 2, ctypes.byref(h)) == qmv.QMV_OK and h.value
+        need = lib.qmv_plan_workspace_bytes(h)
+        assert need > 0
+        assert need <= (lib.qmv_gemv_workspace_bytes if kind == qmv.QMV_PLAN_GEMV
+                        else lib.qmv_prefill_workspace_bytes)(arr, 2)
+        assert lib.qmv_plan_launch(h, None, 0, None) == qmv.QMV_EWORKSPACE
+        assert lib.qmv_plan_upload(h, _fake(1 << 20), need - 1, None) == qmv.QMV_EWORKSPACE
+        assert lib.qmv_plan_launch(h, _fake((1 << 20) + 16), need, None) == qmv.QMV_EWORKSPACE
+        if not torch.cuda.is_available():      # a plan made with no usable device cannot run
+            assert lib.qmv_plan_launch(h, _fake(1 << 20), need, None) == qmv.QMV_EHIP
+        lib.qmv_plan_destroy(h)
 
 
 def test_read_probe_rejects_bad_arguments(lib):
@@ -189,11 +219,11 @@ def test_gemv_grouped_validation(lib):
     # the grouped path has no single exact dot: acc must be NULL
     p = _problem(wtype=g)
     p.acc = 24576
-    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, 0, None) == qmv.QMV_EINVAL
+    assert lib.qmv_gemv((qmv.qmv_problem * 1)(p), 1, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EINVAL
     # staged activations past the LDS: 16 tokens x 16384 columns
     big = (qmv.qmv_problem * 1)(_problem(wtype=g, n=64, k=16384, m=16))
     assert lib.qmv_gemv_workspace_bytes(big, 1) == -1
-    assert lib.qmv_gemv(big, 1, _fake(1 << 20), 1 << 30, 0, None) == qmv.QMV_ESHAPE
+    assert lib.qmv_gemv(big, 1, _fake(1 << 20), 1 << 30, None) == qmv.QMV_ESHAPE
     # rows past the tile-entry limit
     big = (qmv.qmv_problem * 1)(_problem(wtype=g, n=(1 << 20) + 1, k=64))
     assert lib.qmv_gemv_workspace_bytes(big, 1) == -1

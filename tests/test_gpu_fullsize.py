@@ -1,7 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration bench.py times.
 
 The benchmark's own stacks are built (bench.DecodeStack / bench.PrefillStack:
-the same grouped problem lists, workspaces and TABLE_READY launches), one pass
+the same grouped problem lists and plan launches), one pass
 is run, and the results are checked against the CPU oracle:
   * activations: every int8 code and scale, bit-exact;
   * packed weights: every byte, through the oracle's unpacker, against the
@@ -85,7 +85,7 @@ def _check_packed(st, config_id):
 def _run_decode_step(st, stream):
     from ternary_matvec_amd import qmv
     qmv.qmv_quantize_act_many(st.acts, stream=stream)   # the bench's one launch for both widths
-    qmv.qmv_gemv(st.arrays[0], workspace=st.workspaces[0], flags=qmv.QMV_F_TABLE_READY, stream=stream)
+    st.plans[0].launch(stream)
     torch.cuda.synchronize()
 
 
@@ -139,7 +139,7 @@ def test_fullsize_gemma_prefill_512(gemma_stack):
     for y in ps.y.values():
         y.fill_(float("nan"))
     qmv.qmv_quantize_act_many(ps.acts, stream=stream)
-    qmv.qmv_gemm_prefill(ps.arr, workspace=ps.ws, flags=qmv.QMV_F_TABLE_READY, stream=stream)
+    ps.plan.launch(stream)
     torch.cuda.synchronize()
     x8, sx = {}, {}
     for k in ps.x:
@@ -147,6 +147,8 @@ def test_fullsize_gemma_prefill_512(gemma_stack):
         np.testing.assert_array_equal(ps.x8[k].cpu().numpy(), q_ref)
         np.testing.assert_array_equal(ps.sx[k].cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
         x8[k], sx[k] = q_ref, s_ref
+    for i, y in ps.y.items():
+        assert not torch.isnan(y).any(), "prefill output %d has elements never written" % i
     _check_stack_outputs(st, x8, sx, lambda i: ps.y[i].cpu().numpy(), synth.CONFIG_GEMMA_DECODE, 512)
     del ps
     torch.cuda.empty_cache()

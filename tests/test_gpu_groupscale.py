@@ -131,12 +131,13 @@ def test_gemv_groupscale_mixed_with_other_types_and_repeated(qmv_gpu):
     probs.append(qmv.Problem(qmv.qmv_pack_int8(_t(wi)), _t(qi), _t(si),
                              acc=torch.zeros((2, 200), dtype=torch.int32, device=DEV)))
     checks.append(("i", qwi, qi))
-    ws = qmv.qmv_gemv(probs)
+    plan = qmv.gemv_plan(probs)
+    plan.launch()
     torch.cuda.synchronize()
     first = [p.y.clone() for p in probs]
     for p in probs:
         p.y.zero_()
-    qmv.qmv_gemv(probs, workspace=ws, flags=qmv.QMV_F_TABLE_READY)
+    plan.launch()
     torch.cuda.synchronize()
     for p, f in zip(probs, first):
         assert torch.equal(p.y, f)

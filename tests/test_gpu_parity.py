@@ -212,7 +212,8 @@ def test_gemv_grouped_mixed_equals_single(qmv_gpu):
             w = qmv.qmv_pack_int8(_t(wf))
             refs.append(oracle.matmul_int(q, oracle.quantize_tensor(wf)[0]))
         probs.append(qmv.Problem(w, _t(q), _t(sx), acc=torch.zeros((m, n), dtype=torch.int32, device=DEV)))
-    ws = qmv.qmv_gemv(probs)
+    plan = qmv.gemv_plan(probs)
+    plan.launch()
     torch.cuda.synchronize()
     grouped = [(p.acc.cpu().numpy().copy(), p.y.cpu().numpy().copy()) for p in probs]
     for p, ref, (acc_g, y_g) in zip(probs, refs, grouped):
@@ -223,13 +224,60 @@ def test_gemv_grouped_mixed_equals_single(qmv_gpu):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(p.acc.cpu().numpy(), acc_g)
         np.testing.assert_array_equal(p.y.cpu().numpy(), y_g)
-    # a second launch that reuses the uploaded table gives the same bits
+    # a second launch of the plan (its table uploaded once) gives the same bits
     for p in probs:
         p.y.zero_()
-    qmv.qmv_gemv(probs, workspace=ws, flags=qmv.QMV_F_TABLE_READY)
+    plan.launch()
     torch.cuda.synchronize()
     for p, (_, y_g) in zip(probs, grouped):
         np.testing.assert_array_equal(p.y.cpu().numpy(), y_g)
+
+
+def test_plan_launch_in_a_graph_and_one_shot_refused_under_capture(qmv_gpu):
+    """A plan's launch (kernels only) captured in a HIP graph and replayed,
+    with eager work between the replays, gives the eager result every time;
+    the one-shot qmv_gemv refuses a capturing stream (its upload would keep a
+    pointer to released host memory) and enqueues nothing."""
+    from ternary_matvec_amd import qmv
+    say("plan launch in a graph")
+    specs = [(1024, 1152, 1), (256, 1152, 1), (1152, 6912, 1), (6912, 1152, 1)]
+    probs, refs = [], []
+    for i, (n, k, m) in enumerate(specs):
+        t = synth.trits(8300 + i, (n, k))
+        q, sx = oracle.quantize_rows(_x_for(8400 + i, m, k))
+        w = qmv.qmv_pack_ternary(_t(t), 0.02)
+        refs.append(oracle.matmul_int(q, t))
+        probs.append(qmv.Problem(w, _t(q), _t(sx), acc=torch.zeros((m, n), dtype=torch.int32, device=DEV)))
+    plan = qmv.gemv_plan(probs)
+    plan.launch()
+    torch.cuda.synchronize()
+    eager = [p.y.clone() for p in probs]
+    for p, ref in zip(probs, refs):
+        np.testing.assert_array_equal(p.acc.cpu().numpy(), ref)
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    refused = None
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(graph, stream=cap):
+            plan.launch(cap)
+            try:
+                qmv.qmv_gemv(probs, stream=cap)
+            except qmv.QmvError as e:
+                refused = e.status
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    assert refused == qmv.QMV_EUNSUPPORTED
+    for _ in range(3):
+        for p in probs:
+            p.y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for p, e in zip(probs, eager):
+            assert torch.equal(p.y, e)
+        plan.launch()                      # eager work between the replays
+        torch.cuda.synchronize()
 
 
 def test_gemv_batch_columns_equal_single_token(qmv_gpu):
@@ -347,6 +395,33 @@ def test_prefill_parity(qmv_gpu, n, k, m):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
     _check_y(p.y.cpu().numpy(), acc_ref, sx, np.float32(sw))
+
+
+# acc = NULL: the epilogue that stores y alone (buffer stores for whole tiles),
+# the path the benchmark's prefill takes.  Full 128-token x 256-row tiles,
+# ragged edges in tokens and rows, a single K step, every element checked
+# (y starts as NaN, so an element never written fails).
+PREFILL_NOACC_CASES = [(512, 1152, 256), (1000, 1152, 300), (256, 6912, 128), (300, 161, 129), (1, 1, 1),
+                       (6912, 1152, 512), (257, 80, 5)]
+
+
+@pytest.mark.parametrize("n,k,m", PREFILL_NOACC_CASES)
+def test_prefill_parity_y_only(qmv_gpu, n, k, m):
+    from ternary_matvec_amd import qmv
+    say("prefill y only", n, k, m)
+    t = synth.trits(12500 + n + k, (n, k))
+    x = _x_for(12501 + k + m, m, k)
+    q, sx = oracle.quantize_rows(x)
+    sw = synth.ternary_scale(12502 + n)
+    acc_ref = oracle.matmul_int(q, t)
+    w = qmv.qmv_pack_ternary(_t(t), sw)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    p = qmv.Problem(w, _t(q), _t(sx), y=y)
+    qmv.qmv_gemm_prefill([p])
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert not np.isnan(got).any()
+    _check_y(got, acc_ref, sx, np.float32(sw))
 
 
 def test_prefill_grouped_equals_gemv(qmv_gpu):
