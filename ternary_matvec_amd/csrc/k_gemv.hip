@@ -362,8 +362,7 @@ namespace {
 template <int MT, int WT>
 hipError_t lds_limit_one()
 {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv<MT, WT>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    return raise_lds_limit(reinterpret_cast<const void*>(&k_gemv<MT, WT>));
 }
 
 template <int WT>

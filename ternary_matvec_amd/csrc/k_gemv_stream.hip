@@ -656,8 +656,7 @@ namespace {
 template <int MT, int WT>
 hipError_t stream_lds_limit()
 {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    return raise_lds_limit(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>));
 }
 }  // namespace
 

@@ -236,8 +236,7 @@ namespace {
 template <int MT>
 hipError_t grouped_lds_limit()
 {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_grouped<MT>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    return raise_lds_limit(reinterpret_cast<const void*>(&k_gemv_grouped<MT>));
 }
 }  // namespace
 

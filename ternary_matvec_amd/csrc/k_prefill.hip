@@ -596,8 +596,7 @@ int64_t prefill_tiles(int64_t m, int64_t n) { return ((m + kPBM - 1) / kPBM) * (
 
 hipError_t setup_prefill_attributes()
 {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(&k_prefill), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)kMaxLds);
+    return raise_lds_limit(reinterpret_cast<const void*>(&k_prefill));
 }
 
 hipError_t launch_prefill(const DevProblem* probs, const uint64_t* table, int64_t grid, const int8_t* zeros,

@@ -537,11 +537,9 @@ hipError_t launch_sketch_build(const uint16_t* w, int64_t v, int64_t k, void* sk
 
 hipError_t setup_sketch_attributes()
 {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_plan),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&k_sketch_plan));
     if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_sketch_rescore),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxLds);
+        e = raise_lds_limit(reinterpret_cast<const void*>(&k_sketch_rescore));
     return e;
 }
 

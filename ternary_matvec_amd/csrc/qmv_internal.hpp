@@ -103,6 +103,16 @@ int64_t gemv_lds_bytes(int wtype, int max_m, int max_chunks);
 // Rows per tile of the workgroup GEMV (64, or 128 from 4 tokens: two rows per lane).
 int gemv_rows_per_tile(int wtype, int max_m);
 constexpr int64_t kMaxLds = 160 * 1024;  // LDS of one gfx950 compute unit
+
+// Raise a kernel's dynamic-LDS limit to what its static LDS leaves of kMaxLds.
+inline hipError_t raise_lds_limit(const void* kernel)
+{
+    hipFuncAttributes a;
+    hipError_t e = hipFuncGetAttributes(&a, kernel);
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)(kMaxLds - (int64_t)a.sharedSizeBytes));
+}
 hipError_t launch_gemv(const DevProblem* probs, const uint32_t* tiles, int32_t tile_begin, int32_t tile_count,
                        int wtype, int max_m, int max_chunks, hipStream_t s);
 // Streaming (persistent) GEMV for 1..2 tokens.  Workgroups are 4 compute
