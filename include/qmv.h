@@ -21,7 +21,9 @@
  * Conventions (apply to every call):
  *   - Pointers are DEVICE pointers unless marked "host".  Every buffer is owned
  *     by the caller; the library never allocates or frees device memory.
- *     Scratch memory is passed in as `workspace`.
+ *     Scratch memory is passed in as `workspace` (except for
+ *     qmv_lmhead_argmax_static, whose scratch is a fixed array in the
+ *     library's code object).
  *   - Calls are asynchronous: host-side arguments are validated synchronously;
  *     on a validation failure the call returns a negative status and enqueues
  *     nothing.  Otherwise the work is enqueued on `stream` (a hipStream_t;
@@ -32,7 +34,8 @@
  *   - Non-finite fp32 inputs are outside the contract.
  *   - State: the library keeps one record per device, filled once on the
  *     first call that needs it (the compute-unit count, the kernels'
- *     dynamic-LDS limit), and nothing else between calls.  A plan (qmv_plan_*)
+ *     dynamic-LDS limit, the device address of qmv_lmhead_argmax_static's
+ *     scratch array), and nothing else between calls.  A plan (qmv_plan_*)
  *     is host memory the caller owns through its handle.  Calls on different
  *     streams with different buffers and workspaces may run concurrently.
  *
@@ -326,6 +329,19 @@ int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k);
 int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int64_t k, int32_t* idx,
                           float* max_logit, float* logits, void* workspace, int64_t ws_bytes,
                           void* stream);
+
+/*
+ * qmv_lmhead_argmax_static -- qmv_lmhead_argmax without a workspace, for
+ * callers that cannot allocate device memory (code under graph capture,
+ * serving loops that forbid allocation).  Same arguments and results; the
+ * per-workgroup maxima go to a scratch array of 256 KiB that the library
+ * holds on each device until the process ends, so v <= 2^21 rows (else
+ * QMV_ESHAPE).  Every call on one device shares that array: calls that
+ * overlap in time on one device race.  Nothing is allocated or freed; EHIP
+ * with no usable device.
+ */
+int32_t qmv_lmhead_argmax_static(const uint16_t* w_bf16, const float* x, int64_t v, int64_t k, int32_t* idx,
+                                 float* max_logit, float* logits, void* stream);
 
 /*
  * The sketch head ("Step 3": candidates first, exact scores only for them).

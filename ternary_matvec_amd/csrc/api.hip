@@ -337,16 +337,29 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
 
 // ---------------------------------------------------------------------------
 // Per-device set-up, done once per device on first use: the compute-unit
-// count and the kernels' dynamic-LDS limit raised to the whole 160 KB
-// (launches then never set attributes).
+// count, the kernels' dynamic-LDS limit raised to the whole 160 KB (launches
+// then never set attributes), and the device address of `scratch`.
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxDevices = 64;
+
+constexpr int64_t kStaticScratchBytes = 256 * 1024;
+
+}  // namespace
+
+// The scratch of qmv_lmhead_argmax_static (the output layer's per-workgroup
+// maxima): one copy per device.  Host code never uses this name as an
+// address: device_setup takes each device's address once, and the entry point
+// passes that.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
 
 struct DeviceSetup {
     std::once_flag once;
     int32_t status = QMV_EHIP;
     int cus = 0;
+    void* scratch = nullptr;   // device address of `scratch` on this device (null: not found)
 };
 
 DeviceSetup g_devices[kMaxDevices];
@@ -367,7 +380,12 @@ const DeviceSetup* device_setup(int* dev_out)
         if (e == hipSuccess) e = setup_grouped_attributes();
         if (e == hipSuccess) e = setup_prefill_attributes();
         if (e == hipSuccess) e = setup_sketch_attributes();
+        // the scratch address only serves qmv_lmhead_argmax_static, which
+        // refuses to run without it
+        void* p = nullptr;
+        if (e == hipSuccess && hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) p = nullptr;
         d.cus = cus;
+        d.scratch = p;
         d.status = e == hipSuccess ? QMV_OK : QMV_EHIP;
     });
     if (d.status != QMV_OK) return nullptr;
@@ -812,6 +830,17 @@ int32_t qmv_lmhead_argmax(const uint16_t* w_bf16, const float* x, int64_t v, int
     const int64_t need = qmv_lmhead_workspace_bytes(v, k);
     if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return QMV_EWORKSPACE;
     return hip_status(launch_lmhead(w_bf16, x, v, k, idx, max_logit, logits, workspace, as_stream(stream)));
+}
+
+int32_t qmv_lmhead_argmax_static(const uint16_t* w_bf16, const float* x, int64_t v, int64_t k, int32_t* idx,
+                                 float* max_logit, float* logits, void* stream)
+{
+    if (!w_bf16 || !x || !idx) return QMV_EINVAL;
+    if (v < 1 || k < 1 || v > QMV_MAX_N || k > QMV_MAX_K) return QMV_ESHAPE;
+    if (lmhead_partials(v) * 8 > kStaticScratchBytes) return QMV_ESHAPE;
+    const DeviceSetup* d = device_setup(nullptr);
+    if (!d || !d->scratch) return QMV_EHIP;
+    return hip_status(launch_lmhead(w_bf16, x, v, k, idx, max_logit, logits, d->scratch, as_stream(stream)));
 }
 
 int64_t qmv_sketch_bytes(int64_t v, int64_t k)

@@ -83,6 +83,7 @@ SIGNATURES = {
     "qmv_lmhead_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
     "qmv_lmhead_argmax": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64,
                                    _c_ptr]),
+    "qmv_lmhead_argmax_static": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_read_probe": (_c_i32, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "qmv_rmsnorm_quantize": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_glu_quantize": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_i32, _c_ptr, _c_ptr, _c_ptr]),
@@ -401,6 +402,25 @@ def qmv_lmhead_argmax(w_bf16, x, logits=None, idx=None, max_logit=None, workspac
         workspace = _alloc_aligned(max(qmv_lmhead_workspace_bytes(v, k), 256), dev)
     _check(load().qmv_lmhead_argmax(_ptr(w_bf16), _ptr(x), v, k, _ptr(idx), _ptr(max_logit), _ptr(logits),
                                     _ptr(workspace), workspace.numel(), _stream(stream)), "qmv_lmhead_argmax")
+    return idx, max_logit, logits
+
+
+def qmv_lmhead_argmax_static(w_bf16, x, logits=None, idx=None, max_logit=None, want_logits=False, stream=None):
+    """qmv_lmhead_argmax with the library's static scratch instead of a workspace:
+    returns (idx tensor [1] int32, max_logit tensor [1] fp32, logits or None)."""
+    if w_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("w_bf16 must hold bf16 bit patterns")
+    _dev(x, torch.float32, "x")
+    v, k = w_bf16.shape
+    dev = x.device
+    if idx is None:
+        idx = torch.empty(1, dtype=torch.int32, device=dev)
+    if max_logit is None:
+        max_logit = torch.empty(1, dtype=torch.float32, device=dev)
+    if logits is None and want_logits:
+        logits = torch.empty(v, dtype=torch.float32, device=dev)
+    _check(load().qmv_lmhead_argmax_static(_ptr(w_bf16), _ptr(x), v, k, _ptr(idx), _ptr(max_logit), _ptr(logits),
+                                           _stream(stream)), "qmv_lmhead_argmax_static")
     return idx, max_logit, logits
 
 

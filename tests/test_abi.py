@@ -197,6 +197,16 @@ def test_plan_validation(lib):
         lib.qmv_plan_destroy(h)
 
 
+def test_lmhead_static_validation(lib):
+    s = None
+    assert lib.qmv_lmhead_argmax_static(_fake(4096), _fake(64), 10, 8, None, None, None, s) == qmv.QMV_EINVAL
+    assert lib.qmv_lmhead_argmax_static(None, _fake(64), 10, 8, _fake(64), None, None, s) == qmv.QMV_EINVAL
+    assert lib.qmv_lmhead_argmax_static(_fake(4096), _fake(64), 0, 8, _fake(64), None, None, s) == qmv.QMV_ESHAPE
+    # the static scratch holds the maxima of at most 2^21 rows
+    assert lib.qmv_lmhead_argmax_static(_fake(4096), _fake(64), (1 << 21) + 64, 8, _fake(64), None, None, s) == \
+        qmv.QMV_ESHAPE
+
+
 def test_read_probe_rejects_bad_arguments(lib):
     """qmv_read_probe validates on the host: null pointers, misaligned or ragged sizes."""
     import ctypes
