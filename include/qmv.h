@@ -289,9 +289,11 @@ int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspac
  * the list and the device).  A plan is host memory owned by the caller
  * through its handle; it is made for the device current at qmv_plan_create
  * and must be used with streams of that device.
- *   kind      QMV_PLAN_GEMV (the launches of qmv_gemv) or QMV_PLAN_PREFILL
- *             (those of qmv_gemm_prefill); the list is validated as by
- *             that call.
+ *   kind      QMV_PLAN_GEMV (the launches of qmv_gemv), QMV_PLAN_PREFILL
+ *             (those of qmv_gemm_prefill), or QMV_PLAN_GEMV_DOT (qmv_gemv's
+ *             products with vector dot-product instructions only, no matrix
+ *             cores: a comparison point); the list is validated as by the
+ *             corresponding call.  Results are identical across the kinds.
  *   qmv_plan_workspace_bytes  exact workspace bytes of the plan.
  *   qmv_plan_upload  copies the plan's tables into `workspace` (in-stream,
  *             from the plan's host memory, which lives until
@@ -304,7 +306,7 @@ int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspac
  * a missing, misaligned or small workspace, EHIP with no usable device.
  */
 typedef struct qmv_plan qmv_plan;
-enum { QMV_PLAN_GEMV = 1, QMV_PLAN_PREFILL = 2 };
+enum { QMV_PLAN_GEMV = 1, QMV_PLAN_PREFILL = 2, QMV_PLAN_GEMV_DOT = 3 };
 int32_t qmv_plan_create(int32_t kind, const qmv_problem* probs /* host */, int32_t count, qmv_plan** plan);
 int64_t qmv_plan_workspace_bytes(const qmv_plan* plan);
 int32_t qmv_plan_upload(const qmv_plan* plan, void* workspace, int64_t ws_bytes, void* stream);

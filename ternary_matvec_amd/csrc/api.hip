@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <new>
 #include <queue>
@@ -89,10 +90,22 @@ int32_t check_problems(const qmv_problem* probs, int32_t count, int64_t max_m)
 #endif
 constexpr int kStreamWgPerCu = QMV_STREAM_WG_PER_CU;   // at most 16 compute waves per compute unit
 constexpr int kStreamMaxM = 2;
+// Token counts whose ternary problems go to the matrix-core kernel.  At one
+// token the streaming dot-product kernel is faster (measured on the Gemma-3-1B
+// x26 step); from two tokens the matrix cores' cost does not grow with the
+// tokens while the dot products' does.  Past four tokens the kernel's operand
+// slots leave one workgroup per compute unit on 4096-column rows, and the
+// workgroup dot-product kernel measured faster.
+constexpr int kMxMinM = 2;
+constexpr int kMxMaxM = 4;
+
+// The kernel that serves one weight type of a launch.
+enum GemvKernel { kWorkgroupDot = 0, kStreamDot = 1, kMatrixCore = 2 };
 
 struct Table {
     std::vector<uint8_t> bytes;
-    bool stream[4] = {false, false, false, false};
+    int kernel[4] = {kWorkgroupDot, kWorkgroupDot, kWorkgroupDot, kWorkgroupDot};
+    int mx_tokens = 0;                     // kMatrixCore: tokens per launch (1, 2, 4 or 8)
     int64_t region[4] = {0, 0, 0, 0};      // byte offset of the type's tile list or schedule
     int32_t count[4] = {0, 0, 0, 0};       // tiles (workgroup kernels) or workgroup tiles (streaming)
     int32_t max_m[4] = {0, 0, 0, 0}, max_chunks[4] = {0, 0, 0, 0};
@@ -123,60 +136,64 @@ int64_t table_bound(const qmv_problem* probs, int32_t count, int cus)
     return b;
 }
 
+// A persistent kernel's tile model: per problem a choice (lanes per row of the
+// streaming kernel, row groups per wave of the matrix-core kernel) made for a
+// target number of steps per tile, the rows and modelled cost of a workgroup
+// tile under that choice, and the LDS slot it needs.
+struct TileModel {
+    std::vector<int> targets;
+    std::function<int(const qmv_problem&, int target)> choose;
+    std::function<int64_t(int choice)> rows;
+    std::function<double(const qmv_problem&, int choice)> cost;
+    std::function<int64_t(const qmv_problem&, int choice)> slot_bytes;
+    std::function<size_t(int64_t slot)> lds;
+    std::function<int(int64_t slot)> wg_per_cu;   // resident workgroups per CU, 0 if unknown
+    int max_wg_per_cu;
+    int min_wg_per_cu;
+};
+
 struct StreamChoice {
-    std::vector<int32_t> lanes;        // per table slot (0 for other types)
+    std::vector<int32_t> lanes;        // per table slot: the model's choice
     std::vector<uint32_t> words;       // offsets + entries
     int nb = 0;
     int64_t slot_bytes = 0;
     double makespan = 0;
 };
 
-// Schedule the streaming problems `slots` (table slots of one weight type).
-bool schedule_stream(const std::vector<const qmv_problem*>& sp, const std::vector<int32_t>& slots, int wtype,
-                     int mt, int cus, StreamChoice& best)
+// Schedule the problems `sp` (table slots `slots`) for a persistent kernel.
+// For each distinct choice vector the tiles are dealt longest first to the 8
+// XCD lists and the makespan of the kernel's dealing is modelled; the shortest
+// is kept.
+bool schedule_persistent(const std::vector<const qmv_problem*>& sp, const std::vector<int32_t>& slots,
+                         const TileModel& model, int cus, StreamChoice& best)
 {
-    static const int kTargets[] = {4, 6, 8, 12, 16, 24, 32, 48, 64, 1 << 30};
-    for (const qmv_problem* p : sp)   // the kernel sizes its weight buffers in 32 bits
+    for (const qmv_problem* p : sp)   // the kernels size their weight buffers in 32 bits
         if ((int64_t)chunks_of(*p) * 16 * p->w.n >= ((int64_t)1 << 31)) return false;
     std::vector<std::vector<int32_t>> tried;
     bool found = false;
-    for (int target : kTargets) {
-#ifdef QMV_STREAM_TARGET
-        if (target != QMV_STREAM_TARGET) continue;
-#endif
+    for (int target : model.targets) {
         std::vector<int32_t> lanes(sp.size());
-        for (size_t i = 0; i < sp.size(); ++i) {
-            const int c = chunks_of(*sp[i]);
-            int L = 1;
-            while (L < kStreamMaxLanes && gemv_stream_steps(c, L) > target) L *= 2;
-            lanes[i] = L;
-        }
+        for (size_t i = 0; i < sp.size(); ++i) lanes[i] = model.choose(*sp[i], target);
         if (std::find(tried.begin(), tried.end(), lanes) != tried.end()) continue;
         tried.push_back(lanes);
         int64_t slot = 0;
-        for (size_t i = 0; i < sp.size(); ++i)
-            slot = std::max(slot, gemv_stream_slot_bytes(wtype, mt, chunks_of(*sp[i]), lanes[i]));
+        for (size_t i = 0; i < sp.size(); ++i) slot = std::max(slot, model.slot_bytes(*sp[i], lanes[i]));
         slot = round_up(slot, 16);
-        const size_t lds = gemv_stream_lds_bytes(mt, slot);
+        const size_t lds = model.lds(slot);
         if ((int64_t)lds > kMaxLds) continue;
         // resident workgroups per compute unit: the runtime's answer for this
         // kernel and LDS size, else (no usable device) the LDS bound
-        int wg_per_cu = gemv_stream_wg_per_cu(wtype, mt, slot);
-        if (wg_per_cu <= 0) wg_per_cu = (int)std::min<int64_t>(kStreamWgPerCu, kMaxLds / (int64_t)lds);
-        wg_per_cu = std::min(wg_per_cu, kStreamWgPerCu);
+        int wg_per_cu = model.wg_per_cu(slot);
+        if (wg_per_cu <= 0) wg_per_cu = (int)std::min<int64_t>(model.max_wg_per_cu, kMaxLds / (int64_t)lds);
+        wg_per_cu = std::min(wg_per_cu, model.max_wg_per_cu);
+        if (wg_per_cu < model.min_wg_per_cu) continue;
         // workgroup tiles, longest first
         struct Item { double cost; uint32_t entry; };
         std::vector<Item> items;
         for (size_t i = 0; i < sp.size(); ++i) {
             const qmv_problem& p = *sp[i];
-            const int c = chunks_of(p);
-            const int64_t rows = 4 * (kRowsPerTile / lanes[i]) * kStreamRowsPerLane;
-            // chunk steps (an int8 step is a quarter of a ternary one) plus the
-            // tile boundary (barrier, epilogue, ring refill), which measures at
-            // about six ternary steps
-            const double cost =
-                ((double)gemv_stream_steps(c, lanes[i]) * (wtype == 1 ? p.m : 0.3 * p.m) + 6.0) * kStreamRowsPerLane;
-            const int64_t nt = rows_tiles(p.w.n, rows);
+            const double cost = model.cost(p, lanes[i]);
+            const int64_t nt = rows_tiles(p.w.n, model.rows(lanes[i]));
             for (int64_t r = 0; r < nt; ++r)
                 items.push_back({cost, ((uint32_t)slots[i] << kTileRowBits) | (uint32_t)r});
         }
@@ -248,8 +265,64 @@ bool schedule_stream(const std::vector<const qmv_problem*>& sp, const std::vecto
     return found;
 }
 
-// Builds the table; returns QMV_OK or a status.
-int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
+// The streaming dot-product kernel (1..2 tokens): L lanes per row, a
+// workgroup tile of 4 * 64 / L * kStreamRowsPerLane rows.
+TileModel stream_model(int wtype, int mt)
+{
+    TileModel m;
+    m.targets = {4, 6, 8, 12, 16, 24, 32, 48, 64, 1 << 30};
+    m.choose = [](const qmv_problem& p, int target) {
+        const int c = chunks_of(p);
+        int L = 1;
+        while (L < kStreamMaxLanes && gemv_stream_steps(c, L) > target) L *= 2;
+        return L;
+    };
+    m.rows = [](int L) { return (int64_t)4 * (kRowsPerTile / L) * kStreamRowsPerLane; };
+    // chunk steps (an int8 step is a quarter of a ternary one) plus the tile
+    // boundary (barrier, epilogue, ring refill), which measures at about six
+    // ternary steps
+    m.cost = [wtype](const qmv_problem& p, int L) {
+        return ((double)gemv_stream_steps(chunks_of(p), L) * (wtype == 1 ? p.m : 0.3 * p.m) + 6.0) *
+               kStreamRowsPerLane;
+    };
+    m.slot_bytes = [wtype, mt](const qmv_problem& p, int L) {
+        return gemv_stream_slot_bytes(wtype, mt, chunks_of(p), L);
+    };
+    m.lds = [mt](int64_t slot) { return gemv_stream_lds_bytes(mt, slot); };
+    m.wg_per_cu = [wtype, mt](int64_t slot) { return gemv_stream_wg_per_cu(wtype, mt, slot); };
+    m.max_wg_per_cu = kStreamWgPerCu;
+    m.min_wg_per_cu = 1;
+    return m;
+}
+
+// The matrix-core kernel (ternary, 2..8 tokens): a workgroup tile of 128 rows
+// over all of K; a step is one K range (4 chunks) of one row group of 16 rows,
+// 1 KiB of weights per wave.
+TileModel mx_model(int mt)
+{
+    TileModel m;
+    m.targets = {0};
+    m.choose = [](const qmv_problem&, int) { return 2; };   // row groups per wave
+    m.rows = [](int) { return (int64_t)128; };
+    // steps (padded to a multiple of the register ring) plus about two steps
+    // of tile boundary
+    m.cost = [](const qmv_problem& p, int) {
+        const int steps = (chunks_of(p) + 3) / 4 * 2;
+        const int ring = gemv_mx_ring();
+        return (double)((steps + ring - 1) / ring * ring) + 2.0;
+    };
+    m.slot_bytes = [mt](const qmv_problem& p, int) { return gemv_mx_slot_bytes(mt, chunks_of(p)); };
+    m.lds = [mt](int64_t slot) { return gemv_mx_lds_bytes(mt, slot); };
+    m.wg_per_cu = [mt](int64_t slot) { return gemv_mx_wg_per_cu(mt, slot); };
+    m.max_wg_per_cu = kStreamWgPerCu;
+    m.min_wg_per_cu = 1;
+    return m;
+}
+
+// Builds the table; returns QMV_OK or a status.  With allow_mx, ternary
+// problems of up to 8 tokens go to the matrix-core kernel when its operand
+// slots leave at least two workgroups per compute unit.
+int32_t build_table(const qmv_problem* probs, int32_t count, int cus, bool allow_mx, Table& t)
 {
     std::vector<int32_t> order(count);
     for (int32_t i = 0; i < count; ++i) order[i] = i;
@@ -273,9 +346,19 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, Table& t)
                 slots.push_back(slot);
             }
         StreamChoice ch;
-        if (t.max_m[wt] <= kStreamMaxM &&
-            schedule_stream(sp, slots, wt, t.max_m[wt] <= 1 ? 1 : 2, cus, ch)) {
-            t.stream[wt] = true;
+        const int mxt = gemv_mx_tokens(t.max_m[wt]);
+        bool ok = false;
+        if (wt == QMV_W_TERNARY5 && allow_mx && t.max_m[wt] >= kMxMinM && t.max_m[wt] <= kMxMaxM && mxt > 0 &&
+            schedule_persistent(sp, slots, mx_model(mxt), cus, ch)) {
+            t.kernel[wt] = kMatrixCore;
+            t.mx_tokens = mxt;
+            ok = true;
+        } else if (t.max_m[wt] <= kStreamMaxM &&
+                   schedule_persistent(sp, slots, stream_model(wt, t.max_m[wt] <= 1 ? 1 : 2), cus, ch)) {
+            t.kernel[wt] = kStreamDot;
+            ok = true;
+        }
+        if (ok) {
             t.nb[wt] = ch.nb;
             t.slot_bytes[wt] = (int32_t)ch.slot_bytes;
             t.count[wt] = (int32_t)(ch.words.size() - kStreamHdr - 2 * ch.nb - 2 * kStreamXcds);
@@ -377,6 +460,7 @@ const DeviceSetup* device_setup(int* dev_out)
         if (e == hipSuccess && cus < 1) e = hipErrorInvalidDevice;
         if (e == hipSuccess) e = setup_workgroup_gemv_attributes();
         if (e == hipSuccess) e = setup_stream_attributes();
+        if (e == hipSuccess) e = setup_mx_attributes();
         if (e == hipSuccess) e = setup_grouped_attributes();
         if (e == hipSuccess) e = setup_prefill_attributes();
         if (e == hipSuccess) e = setup_sketch_attributes();
@@ -519,8 +603,8 @@ int32_t make_plan(int32_t kind, const qmv_problem* probs, int32_t count, qmv_pla
     const int cus = d ? d->cus : 256;
     plan.kind = kind;
     plan.dev = d ? dev : kNoDevice;
-    if (kind == QMV_PLAN_GEMV) {
-        const int32_t st = build_table(probs, count, cus, plan.table);
+    if (kind == QMV_PLAN_GEMV || kind == QMV_PLAN_GEMV_DOT) {
+        const int32_t st = build_table(probs, count, cus, kind == QMV_PLAN_GEMV, plan.table);
         if (st != QMV_OK) return st;
         plan.image.swap(plan.table.bytes);
         return QMV_OK;
@@ -557,7 +641,9 @@ int32_t launch_plan(const qmv_plan& plan, void* workspace, hipStream_t s)
         hipError_t e;
         if (wt == QMV_W_INT8_G128)
             e = launch_gemv_grouped(dp, words, t.count[wt], t.max_m[wt], (size_t)t.slot_bytes[wt], s);
-        else if (t.stream[wt])
+        else if (t.kernel[wt] == kMatrixCore)
+            e = launch_gemv_mx(dp, words, t.nb[wt], t.mx_tokens, t.slot_bytes[wt], s);
+        else if (t.kernel[wt] == kStreamDot)
             e = launch_gemv_stream(dp, words, t.nb[wt], wt, t.max_m[wt], t.slot_bytes[wt], s);
         else
             e = launch_gemv(dp, words, 0, t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
@@ -770,7 +856,7 @@ int32_t qmv_plan_create(int32_t kind, const qmv_problem* probs, int32_t count, q
     if (!plan) return QMV_EINVAL;
     *plan = nullptr;
     int32_t st;
-    if (kind == QMV_PLAN_GEMV)
+    if (kind == QMV_PLAN_GEMV || kind == QMV_PLAN_GEMV_DOT)
         st = check_problems(probs, count, QMV_MAX_GEMV_M);
     else if (kind == QMV_PLAN_PREFILL)
         st = check_prefill(probs, count);

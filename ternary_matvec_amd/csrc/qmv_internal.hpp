@@ -140,6 +140,18 @@ size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes);
 int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes);
 hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,
                               int32_t slot_bytes, hipStream_t s);
+// Persistent ternary GEMV on int8 matrix cores for 1..8 tokens: the same
+// schedule words as the streaming kernel; a workgroup tile is 4 * 16 * rgs rows
+// (rgs = 1 or 2 in the problem's lanes_per_row field).  Tokens per launch are
+// 1, 2, 4 or 8 (gemv_mx_tokens); LDS = two slots of slot_bytes and a few words.
+int gemv_mx_tokens(int max_m);                  // 0: more than 8 tokens
+int gemv_mx_ring();                             // steps of the kernel's weight ring (tiles pad to it)
+int64_t gemv_mx_slot_bytes(int mt, int chunks);
+size_t gemv_mx_lds_bytes(int mt, int64_t slot_bytes);
+int gemv_mx_wg_per_cu(int mt, int64_t slot_bytes);
+hipError_t setup_mx_attributes();
+hipError_t launch_gemv_mx(const DevProblem* probs, uint32_t* sched, int nb, int mt, int32_t slot_bytes,
+                          hipStream_t s);
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin over them
 // Prefill (int8 matrix cores): tiles of 128 tokens x 256 rows.
 constexpr int64_t kPrefillTileM = 128;

@@ -156,10 +156,11 @@ GEMV_CASES = [(1, 1, 1), (5, 7, 1), (64, 80, 1), (65, 81, 2), (3, 400, 1), (200,
               (64, 5, 4), (257, 333, 8), (70, 1600, 5), (17, 6912, 4)]
 
 
+@pytest.mark.parametrize("dot_only", [False, True], ids=["mfma", "dot"])
 @pytest.mark.parametrize("n,k,m", GEMV_CASES)
-def test_gemv_ternary_parity(qmv_gpu, n, k, m):
+def test_gemv_ternary_parity(qmv_gpu, n, k, m, dot_only):
     from ternary_matvec_amd import qmv
-    say("gemv ternary", n, k, m)
+    say("gemv ternary", n, k, m, "dot only" if dot_only else "matrix cores")
     t = synth.trits(4000 + n + k, (n, k))
     x = _x_for(5000 + k + m, m, k)
     q, sx = oracle.quantize_rows(x)
@@ -167,8 +168,9 @@ def test_gemv_ternary_parity(qmv_gpu, n, k, m):
     acc_ref = oracle.matmul_int(q, t)
     w = qmv.qmv_pack_ternary(_t(t), sw)
     acc = torch.full((m, n), -7, dtype=torch.int32, device=DEV)
-    p = qmv.Problem(w, _t(q), _t(sx), acc=acc)
-    qmv.qmv_gemv([p])
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    p = qmv.Problem(w, _t(q), _t(sx), y=y, acc=acc)
+    qmv.gemv_plan([p], dot_only=dot_only).launch()
     torch.cuda.synchronize()
     np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
     _check_y(p.y.cpu().numpy(), acc_ref, sx, np.float32(sw))
