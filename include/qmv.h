@@ -292,7 +292,12 @@ int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspac
  *   kind      QMV_PLAN_GEMV (the launches of qmv_gemv), QMV_PLAN_PREFILL
  *             (those of qmv_gemm_prefill), or QMV_PLAN_GEMV_DOT (qmv_gemv's
  *             products with vector dot-product instructions only, no matrix
- *             cores: a comparison point); the list is validated as by the
+ *             cores: a comparison point), or QMV_PLAN_GEMV_SKIP_ZERO
+ *             (qmv_gemv's products, with the one- and two-token ternary
+ *             kernel skipping every 20-column activation unit that is zero
+ *             for all tokens -- the work of "What is next": skipping groups
+ *             of zero inputs; exact, since such units add nothing; the
+ *             weights are still read); the list is validated as by the
  *             corresponding call.  Results are identical across the kinds.
  *   qmv_plan_workspace_bytes  exact workspace bytes of the plan.
  *   qmv_plan_upload  copies the plan's tables into `workspace` (in-stream,
@@ -306,7 +311,7 @@ int32_t qmv_gemm_prefill(const qmv_problem* probs, int32_t count, void* workspac
  * a missing, misaligned or small workspace, EHIP with no usable device.
  */
 typedef struct qmv_plan qmv_plan;
-enum { QMV_PLAN_GEMV = 1, QMV_PLAN_PREFILL = 2, QMV_PLAN_GEMV_DOT = 3 };
+enum { QMV_PLAN_GEMV = 1, QMV_PLAN_PREFILL = 2, QMV_PLAN_GEMV_DOT = 3, QMV_PLAN_GEMV_SKIP_ZERO = 4 };
 int32_t qmv_plan_create(int32_t kind, const qmv_problem* probs /* host */, int32_t count, qmv_plan** plan);
 int64_t qmv_plan_workspace_bytes(const qmv_plan* plan);
 int32_t qmv_plan_upload(const qmv_plan* plan, void* workspace, int64_t ws_bytes, void* stream);

@@ -106,6 +106,7 @@ struct Table {
     std::vector<uint8_t> bytes;
     int kernel[4] = {kWorkgroupDot, kWorkgroupDot, kWorkgroupDot, kWorkgroupDot};
     int mx_tokens = 0;                     // kMatrixCore: tokens per launch (1, 2, 4 or 8)
+    bool skip_zero = false;                // kStreamDot, ternary: skip zero activation units
     int64_t region[4] = {0, 0, 0, 0};      // byte offset of the type's tile list or schedule
     int32_t count[4] = {0, 0, 0, 0};       // tiles (workgroup kernels) or workgroup tiles (streaming)
     int32_t max_m[4] = {0, 0, 0, 0}, max_chunks[4] = {0, 0, 0, 0};
@@ -267,7 +268,7 @@ bool schedule_persistent(const std::vector<const qmv_problem*>& sp, const std::v
 
 // The streaming dot-product kernel (1..2 tokens): L lanes per row, a
 // workgroup tile of 4 * 64 / L * kStreamRowsPerLane rows.
-TileModel stream_model(int wtype, int mt)
+TileModel stream_model(int wtype, int mt, bool skip)
 {
     TileModel m;
     m.targets = {4, 6, 8, 12, 16, 24, 32, 48, 64, 1 << 30};
@@ -289,7 +290,7 @@ TileModel stream_model(int wtype, int mt)
         return gemv_stream_slot_bytes(wtype, mt, chunks_of(p), L);
     };
     m.lds = [mt](int64_t slot) { return gemv_stream_lds_bytes(mt, slot); };
-    m.wg_per_cu = [wtype, mt](int64_t slot) { return gemv_stream_wg_per_cu(wtype, mt, slot); };
+    m.wg_per_cu = [wtype, mt, skip](int64_t slot) { return gemv_stream_wg_per_cu(wtype, mt, slot, skip); };
     m.max_wg_per_cu = kStreamWgPerCu;
     m.min_wg_per_cu = 1;
     return m;
@@ -320,9 +321,10 @@ TileModel mx_model(int mt)
 }
 
 // Builds the table; returns QMV_OK or a status.  With allow_mx, ternary
-// problems of up to 8 tokens go to the matrix-core kernel when its operand
-// slots leave at least two workgroups per compute unit.
-int32_t build_table(const qmv_problem* probs, int32_t count, int cus, bool allow_mx, Table& t)
+// problems of 2..4 tokens go to the matrix-core kernel; with skip_zero,
+// ternary problems of one or two tokens go to the streaming kernel that skips
+// zero activation units.
+int32_t build_table(const qmv_problem* probs, int32_t count, int cus, bool allow_mx, bool skip_zero, Table& t)
 {
     std::vector<int32_t> order(count);
     for (int32_t i = 0; i < count; ++i) order[i] = i;
@@ -354,8 +356,11 @@ int32_t build_table(const qmv_problem* probs, int32_t count, int cus, bool allow
             t.mx_tokens = mxt;
             ok = true;
         } else if (t.max_m[wt] <= kStreamMaxM &&
-                   schedule_persistent(sp, slots, stream_model(wt, t.max_m[wt] <= 1 ? 1 : 2), cus, ch)) {
+                   schedule_persistent(sp, slots,
+                                       stream_model(wt, t.max_m[wt] <= 1 ? 1 : 2, skip_zero && wt == QMV_W_TERNARY5),
+                                       cus, ch)) {
             t.kernel[wt] = kStreamDot;
+            t.skip_zero = skip_zero && wt == QMV_W_TERNARY5;
             ok = true;
         }
         if (ok) {
@@ -603,8 +608,9 @@ int32_t make_plan(int32_t kind, const qmv_problem* probs, int32_t count, qmv_pla
     const int cus = d ? d->cus : 256;
     plan.kind = kind;
     plan.dev = d ? dev : kNoDevice;
-    if (kind == QMV_PLAN_GEMV || kind == QMV_PLAN_GEMV_DOT) {
-        const int32_t st = build_table(probs, count, cus, kind == QMV_PLAN_GEMV, plan.table);
+    if (kind == QMV_PLAN_GEMV || kind == QMV_PLAN_GEMV_DOT || kind == QMV_PLAN_GEMV_SKIP_ZERO) {
+        const int32_t st =
+            build_table(probs, count, cus, kind == QMV_PLAN_GEMV, kind == QMV_PLAN_GEMV_SKIP_ZERO, plan.table);
         if (st != QMV_OK) return st;
         plan.image.swap(plan.table.bytes);
         return QMV_OK;
@@ -644,7 +650,8 @@ int32_t launch_plan(const qmv_plan& plan, void* workspace, hipStream_t s)
         else if (t.kernel[wt] == kMatrixCore)
             e = launch_gemv_mx(dp, words, t.nb[wt], t.mx_tokens, t.slot_bytes[wt], s);
         else if (t.kernel[wt] == kStreamDot)
-            e = launch_gemv_stream(dp, words, t.nb[wt], wt, t.max_m[wt], t.slot_bytes[wt], s);
+            e = launch_gemv_stream(dp, words, t.nb[wt], wt, t.max_m[wt], t.slot_bytes[wt],
+                                   wt == QMV_W_TERNARY5 && t.skip_zero, s);
         else
             e = launch_gemv(dp, words, 0, t.count[wt], wt, t.max_m[wt], t.max_chunks[wt], s);
         if (e != hipSuccess) return QMV_EHIP;
@@ -856,7 +863,7 @@ int32_t qmv_plan_create(int32_t kind, const qmv_problem* probs, int32_t count, q
     if (!plan) return QMV_EINVAL;
     *plan = nullptr;
     int32_t st;
-    if (kind == QMV_PLAN_GEMV || kind == QMV_PLAN_GEMV_DOT)
+    if (kind == QMV_PLAN_GEMV || kind == QMV_PLAN_GEMV_DOT || kind == QMV_PLAN_GEMV_SKIP_ZERO)
         st = check_problems(probs, count, QMV_MAX_GEMV_M);
     else if (kind == QMV_PLAN_PREFILL)
         st = check_prefill(probs, count);

@@ -310,10 +310,17 @@ __device__ __forceinline__ void put_z(uint32_t* zo, int g, const uint32_t zz[10]
 // 25600 * sum Z + sum x of each token.  `after_loads` runs once, in uniform
 // control flow, right after the first activation loads of every lane are
 // issued: work placed there overlaps their latency instead of delaying them.
-template <int MT, int WT, class F>
+template <int MT, int WT, bool SKIP, class F>
 __device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, int* corr, F after_loads)
 {
     constexpr int kD = WT == 1 ? 5 : 1;
+    // Zero-unit mask (SKIP): bit j of word i is set while unit j of the chunks
+    // of step i (chunks iL .. iL+L-1) is zero for every token so far; the
+    // lanes clear the bits of units they find non-zero.  Units past k count
+    // as zero.  The words follow the tokens' staged values.
+    uint32_t* const mask = reinterpret_cast<uint32_t*>(slot + (size_t)MT * T.tok_bytes);
+    if (SKIP)
+        for (int i = lane; i < T.nsteps; i += kWave) mask[i] = 0xfu;
     // units per lane loaded before any is used: a ternary row of up to
     // 64 * 2 * 20 = 2560 columns costs one memory round trip.  Larger batches
     // would cover longer rows in one trip but raise the kernel's register
@@ -348,6 +355,9 @@ __device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, in
                         unit_of<1>(T, sh, g, raw[b], nat);
                         z_group(nat, zz, s_z, s_x);
                         put_z(zo, g, zz);
+                        if (SKIP && (nat[0] | nat[1] | nat[2] | nat[3] | nat[4]) != 0u)
+                            __hip_atomic_fetch_and(&mask[(g >> 2) >> T.lshift], ~(1u << (g & 3)), __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
                     } else {
                         unit_of<2>(T, sh, g, raw[b], &zo[g]);
                     }
@@ -368,7 +378,7 @@ __device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, in
 // apart][first tile entry of each workgroup][8 x (list offset, list size)]
 // [tile entries of the 8 XCD lists].
 // LDS: [2 tile slots of slot_bytes][3 tile descriptors][corr: 2 x MT]
-template <int MT, int WT>
+template <int MT, int WT, bool SKIP>
 __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem* __restrict__ probs,
                                                                uint32_t* __restrict__ sched, int32_t slot_bytes)
 {
@@ -415,7 +425,7 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
         bool first = true;
         for (int par = 0, q = 0; te != kEnd; par ^= 1, q = q == kDescSlots - 1 ? 0 : q + 1) {
             const int qn = q == kDescSlots - 1 ? 0 : q + 1;   // the next tile's descriptor slot
-            stage<MT, WT>(T, lane, smem + (size_t)par * slot_bytes, corr_base + par * MT, [&] {
+            stage<MT, WT, SKIP>(T, lane, smem + (size_t)par * slot_bytes, corr_base + par * MT, [&] {
                 if (first) {
                     // Tile 0: release the compute waves' weight prefetch only once
                     // these loads (and the tile's scales) are back: they gate every
@@ -507,11 +517,16 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
         const int tok_bytes = cur.tok_bytes;
         // one chunk step: the weight chunk of each of the lane's rows against the
         // staged activations of that chunk
+        const uint32_t* const zmask = reinterpret_cast<const uint32_t*>(zs + (size_t)MT * tok_bytes);
         auto run_step = [&](const v4u32* src, int i) {
             const uint8_t* zc = zlane + i * zstep;
             if (WT == 1) {
+                // SKIP: the step's units whose activations are zero for every
+                // token and every lane part add nothing; a wave-uniform skip
+                const uint32_t zm = SKIP ? __builtin_amdgcn_readfirstlane(zmask[i]) : 0u;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
+                    if (SKIP && ((zm >> j) & 1u)) continue;
                     uint4 Z[MT][3];   // the 10 Z pairs of dword j (and two pad words)
 #pragma unroll
                     for (int mi = 0; mi < MT; ++mi)
@@ -609,11 +624,11 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
     }
 }
 
-template <int MT, int WT>
+template <int MT, int WT, bool SKIP>
 hipError_t launch_stream_one(const DevProblem* probs, uint32_t* sched, int nb, int32_t slot_bytes, hipStream_t s)
 {
     const size_t lds = gemv_stream_lds_bytes(MT, slot_bytes);
-    hipLaunchKernelGGL((k_gemv_stream<MT, WT>), dim3((unsigned)nb), dim3(kStreamThreads), lds, s, probs, sched,
+    hipLaunchKernelGGL((k_gemv_stream<MT, WT, SKIP>), dim3((unsigned)nb), dim3(kStreamThreads), lds, s, probs, sched,
                        slot_bytes);
     return hipGetLastError();
 }
@@ -627,7 +642,10 @@ int64_t gemv_stream_steps(int chunks, int lanes)
 
 int64_t gemv_stream_slot_bytes(int wtype, int mt, int chunks, int lanes)
 {
-    return (int64_t)mt * gemv_stream_steps(chunks, lanes) * lanes * (wtype == 1 ? kZBytes : kXBytes);
+    // ternary slots end with the zero-unit mask of the skipping variant (one
+    // word per step)
+    const int64_t steps = gemv_stream_steps(chunks, lanes);
+    return (int64_t)mt * steps * lanes * (wtype == 1 ? kZBytes : kXBytes) + (wtype == 1 ? 4 * steps : 0);
 }
 
 size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes)
@@ -635,49 +653,58 @@ size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes)
     return (size_t)(2 * slot_bytes + kDescSlots * (int64_t)sizeof(TileDesc) + 2 * mt * (int64_t)sizeof(int));
 }
 
-template <int MT, int WT>
+template <int MT, int WT, bool SKIP>
 int occupancy_one(int64_t slot_bytes)
 {
     const size_t lds = gemv_stream_lds_bytes(MT, slot_bytes);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemv_stream<MT, WT, SKIP>),
                                                      kStreamThreads, lds) != hipSuccess)
         return 0;
     return n;
 }
 
-int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes)
+int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes, bool skip)
 {
-    if (wtype == 1) return max_m <= 1 ? occupancy_one<1, 1>(slot_bytes) : occupancy_one<2, 1>(slot_bytes);
-    return max_m <= 1 ? occupancy_one<1, 2>(slot_bytes) : occupancy_one<2, 2>(slot_bytes);
+    if (wtype == 1) {
+        if (skip) return max_m <= 1 ? occupancy_one<1, 1, true>(slot_bytes) : occupancy_one<2, 1, true>(slot_bytes);
+        return max_m <= 1 ? occupancy_one<1, 1, false>(slot_bytes) : occupancy_one<2, 1, false>(slot_bytes);
+    }
+    return max_m <= 1 ? occupancy_one<1, 2, false>(slot_bytes) : occupancy_one<2, 2, false>(slot_bytes);
 }
 
 namespace {
-template <int MT, int WT>
+template <int MT, int WT, bool SKIP>
 hipError_t stream_lds_limit()
 {
-    return raise_lds_limit(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT>));
+    return raise_lds_limit(reinterpret_cast<const void*>(&k_gemv_stream<MT, WT, SKIP>));
 }
 }  // namespace
 
 hipError_t setup_stream_attributes()
 {
-    hipError_t e = stream_lds_limit<1, 1>();
-    if (e == hipSuccess) e = stream_lds_limit<2, 1>();
-    if (e == hipSuccess) e = stream_lds_limit<1, 2>();
-    if (e == hipSuccess) e = stream_lds_limit<2, 2>();
+    hipError_t e = stream_lds_limit<1, 1, false>();
+    if (e == hipSuccess) e = stream_lds_limit<2, 1, false>();
+    if (e == hipSuccess) e = stream_lds_limit<1, 1, true>();
+    if (e == hipSuccess) e = stream_lds_limit<2, 1, true>();
+    if (e == hipSuccess) e = stream_lds_limit<1, 2, false>();
+    if (e == hipSuccess) e = stream_lds_limit<2, 2, false>();
     return e;
 }
 
 hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,
-                              int32_t slot_bytes, hipStream_t s)
+                              int32_t slot_bytes, bool skip, hipStream_t s)
 {
     if (wtype == 1) {
-        if (max_m <= 1) return launch_stream_one<1, 1>(probs, sched, nb, slot_bytes, s);
-        return launch_stream_one<2, 1>(probs, sched, nb, slot_bytes, s);
+        if (skip) {
+            if (max_m <= 1) return launch_stream_one<1, 1, true>(probs, sched, nb, slot_bytes, s);
+            return launch_stream_one<2, 1, true>(probs, sched, nb, slot_bytes, s);
+        }
+        if (max_m <= 1) return launch_stream_one<1, 1, false>(probs, sched, nb, slot_bytes, s);
+        return launch_stream_one<2, 1, false>(probs, sched, nb, slot_bytes, s);
     }
-    if (max_m <= 1) return launch_stream_one<1, 2>(probs, sched, nb, slot_bytes, s);
-    return launch_stream_one<2, 2>(probs, sched, nb, slot_bytes, s);
+    if (max_m <= 1) return launch_stream_one<1, 2, false>(probs, sched, nb, slot_bytes, s);
+    return launch_stream_one<2, 2, false>(probs, sched, nb, slot_bytes, s);
 }
 
 }  // namespace qmv

@@ -137,9 +137,11 @@ int64_t gemv_stream_slot_bytes(int wtype, int mt, int chunks, int lanes);
 size_t gemv_stream_lds_bytes(int mt, int64_t slot_bytes);
 // Workgroups of the streaming kernel resident per compute unit (registers and
 // LDS), 0 if it cannot run or no device is usable.
-int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes);
+int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes, bool skip);
+// skip (ternary only): the variant that skips 20-column units whose
+// activations are zero for every token.
 hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,
-                              int32_t slot_bytes, hipStream_t s);
+                              int32_t slot_bytes, bool skip, hipStream_t s);
 // Persistent ternary GEMV on int8 matrix cores for 1..8 tokens: the same
 // schedule words as the streaming kernel; a workgroup tile is 4 * 16 * rgs rows
 // (rgs = 1 or 2 in the problem's lanes_per_row field).  Tokens per launch are

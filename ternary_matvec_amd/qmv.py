@@ -29,6 +29,7 @@ QMV_MAX_GEMV_M = 16
 QMV_PLAN_GEMV = 1
 QMV_PLAN_PREFILL = 2
 QMV_PLAN_GEMV_DOT = 3
+QMV_PLAN_GEMV_SKIP_ZERO = 4
 
 _c_i32, _c_i64, _c_u32, _c_ptr, _c_f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_float
 
@@ -364,8 +365,9 @@ class Plan:
             self._h = None
 
 
-def gemv_plan(problems, workspace=None, stream=None, dot_only=False):
-    return Plan(QMV_PLAN_GEMV_DOT if dot_only else QMV_PLAN_GEMV, problems, workspace, stream)
+def gemv_plan(problems, workspace=None, stream=None, dot_only=False, skip_zero=False):
+    kind = QMV_PLAN_GEMV_SKIP_ZERO if skip_zero else QMV_PLAN_GEMV_DOT if dot_only else QMV_PLAN_GEMV
+    return Plan(kind, problems, workspace, stream)
 
 
 def prefill_plan(problems, workspace=None, stream=None):

@@ -93,6 +93,19 @@ def trits(seed: int, shape, start: int = 0):
     return _TRIT_OF_DECILE[r.astype(np.intp)].reshape(shape)
 
 
+def zero_groups(seed: int, shape, p_zero: float = 0.8, group: int = 4):
+    """A boolean mask of `shape` (last axis = columns) that is True on whole
+    groups of `group` consecutive columns, each group independently with
+    probability p_zero: the sparse activations of zero-group skipping (the
+    ternary page's "What is next": 80% of groups of 4 inputs zero)."""
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    k = shape[-1]
+    ng = (k + group - 1) // group
+    u = uniform(seed, rows * ng).reshape(rows, ng) < p_zero
+    mask = np.repeat(u, group, axis=1)[:, :k]
+    return mask.reshape(shape)
+
+
 def ternary_scale(seed: int) -> float:
     """One per-matrix scale, uniform in [0.01, 0.03)."""
     return float(np.float32(0.01 + 0.02 * uniform(seed, 1)[0]))

@@ -172,7 +172,7 @@ def test_plan_validation(lib):
     import torch
     arr = (qmv.qmv_problem * 2)(_problem(), _problem(n=100, k=1152, m=3))
     h = ctypes.c_void_p()
-    assert lib.qmv_plan_create(4, arr, 2, ctypes.byref(h)) == qmv.QMV_EINVAL
+    assert lib.qmv_plan_create(5, arr, 2, ctypes.byref(h)) == qmv.QMV_EINVAL
     assert lib.qmv_plan_create(qmv.QMV_PLAN_GEMV, arr, 2, None) == qmv.QMV_EINVAL
     assert lib.qmv_plan_create(qmv.QMV_PLAN_GEMV, arr, 0, ctypes.byref(h)) == qmv.QMV_ESHAPE
     bad = (qmv.qmv_problem * 1)(_problem(m=17))
@@ -183,7 +183,7 @@ def test_plan_validation(lib):
     assert lib.qmv_plan_upload(None, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EINVAL
     assert lib.qmv_plan_launch(None, _fake(1 << 20), 1 << 20, None) == qmv.QMV_EINVAL
     lib.qmv_plan_destroy(None)
-    for kind in (qmv.QMV_PLAN_GEMV, qmv.QMV_PLAN_PREFILL, qmv.QMV_PLAN_GEMV_DOT):
+    for kind in (qmv.QMV_PLAN_GEMV, qmv.QMV_PLAN_PREFILL, qmv.QMV_PLAN_GEMV_DOT, qmv.QMV_PLAN_GEMV_SKIP_ZERO):
         assert lib.qmv_plan_create(kind, arr, 2, ctypes.byref(h)) == qmv.QMV_OK and h.value
         need = lib.qmv_plan_workspace_bytes(h)
         assert need > 0

@@ -282,6 +282,71 @@ def test_plan_launch_in_a_graph_and_one_shot_refused_under_capture(qmv_gpu):
         torch.cuda.synchronize()
 
 
+# Zero-group skipping (QMV_PLAN_GEMV_SKIP_ZERO): activations with 80% of their
+# groups of 4 columns zero, all zero, or dense; one and two tokens (a unit is
+# skipped only when it is zero for both); row lengths that give every
+# lanes-per-row split (the skip must hold for all chunks of a step).  Exact:
+# acc equals the oracle's and y equals the dense plan's bit for bit.
+SKIP_CASES = [(200, 1152, 1), (1152, 6912, 1), (77, 6912, 2), (100, 2800, 1), (5, 7, 1), (64, 80, 2),
+              (300, 1536, 2), (33, 4096, 1)]
+
+
+@pytest.mark.parametrize("density", ["sparse", "zero", "dense", "mixed"])
+@pytest.mark.parametrize("n,k,m", SKIP_CASES)
+def test_gemv_skip_zero_parity(qmv_gpu, n, k, m, density):
+    from ternary_matvec_amd import qmv
+    say("gemv skip zero", n, k, m, density)
+    t = synth.trits(15000 + n + k, (n, k))
+    x = _x_for(15001 + k + m, m, k)
+    if density == "sparse":
+        x[synth.zero_groups(15002 + k, x.shape)] = 0.0
+    elif density == "zero":
+        x[:] = 0.0
+    elif density == "mixed":          # token 0 sparse, token 1 (if any) dense
+        x[0][synth.zero_groups(15003 + k, (k,))] = 0.0
+    q, sx = oracle.quantize_rows(x)
+    sw = synth.ternary_scale(15004 + n)
+    acc_ref = oracle.matmul_int(q, t)
+    w = qmv.qmv_pack_ternary(_t(t), sw)
+    acc = torch.full((m, n), -7, dtype=torch.int32, device=DEV)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=DEV)
+    p = qmv.Problem(w, _t(q), _t(sx), y=y, acc=acc)
+    qmv.gemv_plan([p], skip_zero=True).launch()
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    _check_y(y.cpu().numpy(), acc_ref, sx, np.float32(sw))
+    y_skip = y.clone()
+    y.fill_(float("nan"))
+    qmv.gemv_plan([p]).launch()
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_skip)
+
+
+def test_gemv_skip_zero_grouped_launch(qmv_gpu):
+    """One skip-plan launch over mixed shapes (every lanes-per-row split in one
+    table), launched twice, equals the oracle exactly."""
+    from ternary_matvec_amd import qmv
+    say("gemv skip zero grouped")
+    specs = [(1024, 1152, 1), (256, 1152, 1), (6912, 1152, 1), (1152, 6912, 1), (100, 333, 1)]
+    probs, refs = [], []
+    for i, (n, k, m) in enumerate(specs):
+        t = synth.trits(15100 + i, (n, k))
+        x = _x_for(15200 + i, m, k)
+        x[synth.zero_groups(15300 + i, x.shape)] = 0.0
+        q, sx = oracle.quantize_rows(x)
+        refs.append(oracle.matmul_int(q, t))
+        probs.append(qmv.Problem(qmv.qmv_pack_ternary(_t(t), 0.02), _t(q), _t(sx),
+                                 acc=torch.zeros((m, n), dtype=torch.int32, device=DEV)))
+    plan = qmv.gemv_plan(probs, skip_zero=True)
+    for _ in range(2):
+        for p in probs:
+            p.acc.fill_(-7)
+        plan.launch()
+        torch.cuda.synchronize()
+        for p, ref in zip(probs, refs):
+            np.testing.assert_array_equal(p.acc.cpu().numpy(), ref)
+
+
 def test_gemv_batch_columns_equal_single_token(qmv_gpu):
     """Exact integers: token j of a 16-token problem equals the 1-token result."""
     from ternary_matvec_amd import qmv
