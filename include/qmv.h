@@ -30,7 +30,8 @@
  *     NULL = the null stream) and the call returns QMV_OK, or QMV_EHIP if the
  *     HIP runtime reported an error when enqueuing.
  *   - There are no device-side error reports apart from the optional invalid
- *     trit counter of qmv_pack_ternary; read it after synchronising.
+ *     trit counter of qmv_pack_ternary and the status word of qmv_ffn_decode;
+ *     read them after synchronising.
  *   - Non-finite fp32 inputs are outside the contract.
  *   - State: the library keeps one record per device, filled once on the
  *     first call that needs it (the compute-unit count, the kernels'
@@ -243,6 +244,85 @@ enum {
  */
 int32_t qmv_glu_quantize(const float* gate, const float* up, int64_t m, int64_t n, int32_t act, int8_t* x8, float* sx,
                          void* stream);
+
+/* ---- The feed-forward half of a layer stack in one persistent launch ---------- */
+
+/* One layer of qmv_ffn_decode (host struct describing device memory). */
+typedef struct qmv_ffn_layer {
+    qmv_weight gate;        /* QMV_W_TERNARY5, n = inter, k = hidden */
+    qmv_weight up;          /* QMV_W_TERNARY5, n = inter, k = hidden */
+    qmv_weight down;        /* QMV_W_TERNARY5, n = hidden, k = inter */
+    const float* norm;      /* device, [hidden] fp32 RMSNorm weights */
+} qmv_ffn_layer;
+
+/* End status of a qmv_ffn_decode call (written to its status word). */
+enum {
+    QMV_FFN_OK = 0,
+    QMV_FFN_CANCELLED = 1,  /* the cancel word was nonzero at a wait */
+    QMV_FFN_TIMEOUT = 2     /* a wait ran out of polls (e.g. workgroups not all resident) */
+};
+
+#define QMV_FFN_LAUNCH_LAYERS 32     /* layers per kernel launch; more layers take more launches */
+#define QMV_FFN_TRACE_STAMPS 12      /* trace stamps per layer (qmv_ffn_decode) */
+#define QMV_FFN_MAX_HIDDEN 8192
+#define QMV_FFN_MAX_INTER 65536
+
+/* Workspace bytes of qmv_ffn_decode (-1 on bad sizes). */
+int64_t qmv_ffn_workspace_bytes(int64_t hidden, int64_t inter);
+
+/* Workgroups of one qmv_ffn_decode launch on the current device (the trace's
+ * first dimension), or a negative status. */
+int32_t qmv_ffn_grid(int32_t* grid /* host */);
+
+/*
+ * qmv_ffn_decode -- for one token, the feed-forward half of nlayers decoder
+ * layers (llama2.c tour, "forward": Step 5 and the residual connection after
+ * it; gemma.cpp tour, "The Forward Pass, Layer by Layer"), each layer being
+ *     x8, sx = qmv_rmsnorm_quantize(h, norm, eps)
+ *     g, u   = qmv_gemv of gate and up against (x8, sx)
+ *     q8, sq = qmv_glu_quantize(g, u, act)
+ *     y      = qmv_gemv of down against (q8, sq)
+ *     h      = h + y                                   (fp32 add)
+ * with results identical bit for bit to that chain of calls.  All layers run
+ * in one kernel launch (QMV_FFN_LAUNCH_LAYERS per launch) whose steps wait for
+ * each other inside the kernel: the launch needs every one of its workgroups
+ * resident at once (qmv_ffn_grid of them; the kernel shares the GPU with no
+ * other work on other streams for the duration).
+ *   layers     host, nlayers >= 1 entries, every layer of the same hidden and
+ *              inter (1 <= hidden <= QMV_FFN_MAX_HIDDEN, 1 <= inter <=
+ *              QMV_FFN_MAX_INTER); weights ternary, 16-byte aligned.
+ *   h          device, [hidden] fp32, finite: the residual stream, updated in
+ *              place.
+ *   eps        RMSNorm epsilon (>= 0, finite).   act  QMV_ACT_*.
+ *   workspace  >= qmv_ffn_workspace_bytes(hidden, inter) bytes, 256-byte
+ *              aligned, zero-filled before its first use; every launch leaves
+ *              it zero-filled again (also when it stops early), so calls on
+ *              one stream may share it; calls that overlap must not.
+ *   cancel     nullable: a device word, or host memory the device can read
+ *              (hipHostMalloc); while it is nonzero every wait stops the launch
+ *              (status QMV_FFN_CANCELLED).
+ *   spin_limit polls per wait before the launch stops with QMV_FFN_TIMEOUT
+ *              (0 = 2^20, about a second; a wait normally takes a few polls).
+ *   status     device, 1 int32, required: QMV_FFN_OK or the first QMV_FFN_*
+ *              error of the call; on an error the launches after it do
+ *              nothing and h is unspecified (its input, or the state after
+ *              some of the layers).
+ *   trace      nullable (then nlayers <= QMV_FFN_LAUNCH_LAYERS): device
+ *              uint64 [grid][1 + QMV_FFN_TRACE_STAMPS * nlayers] in ticks of the
+ *              device's 100 MHz constant clock: each workgroup's start, then
+ *              per layer: 0 layer start; for a workgroup with a gate/up task
+ *              (32 rows of both, workgroup b takes rows 32 b ..) 1 down sums of
+ *              the previous layer gathered, 2 RMSNorm's scale known, 3 codes
+ *              written, 4 their staged form ready, 5 gate/up and GLU values
+ *              written; for a workgroup with a down task (workgroup b takes task
+ *              b) 6 its GLU inputs gathered, 7 staged, 8 dots done, 9 the atomic
+ *              adds acknowledged (its completion mark follows); 10 layer end;
+ *              11 unused.  Stamps a workgroup does not reach are 0.
+ * EINVAL / ESHAPE / EUNSUPPORTED / EVALUE / EWORKSPACE on bad arguments.
+ */
+int32_t qmv_ffn_decode(const qmv_ffn_layer* layers /* host */, int32_t nlayers, float* h, float eps, int32_t act,
+                       void* workspace, int64_t ws_bytes, const int32_t* cancel, int64_t spin_limit,
+                       int32_t* status, uint64_t* trace, void* stream);
 
 /* Workspace bytes for this problem list (-1 on bad input); the workspace
  * must be 256-byte aligned.  qmv_workspace_bytes covers both qmv_gemv and

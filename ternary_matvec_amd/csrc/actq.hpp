@@ -1,0 +1,121 @@
+// actq.hpp -- per-token activation quantisation and the fused steps around
+// the matrix products, shared by the kernels that compute them, so that every
+// path that produces a code or a value does it with the same instructions.
+//
+// Quantisation (cpp20gemma README, "Architecture & implementation"; "Gemma 3
+// 1B at 114 tokens per second on a laptop CPU", "Step 2"): scale =
+// max(max|v|, 1e-9) / 127, code = clip(round(v / scale), -128, 127), IEEE fp32
+// division (the library is built with correctly rounded division and square
+// root) and round-half-to-even.  RMSNorm (llama2.c tour, "forward", Steps 1
+// and 6): o = weight * (r * x), r = 1 / sqrt(ss / k + eps).  Gated
+// feed-forward ("forward", Step 5): h = act(gate) * up.  Nothing here is
+// contracted into fused multiply-adds.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+namespace {
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Max over a 256-thread block (red: 4 floats of LDS); every thread receives it.
+__device__ __forceinline__ float block_max(float v, float* red)
+{
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x / 64;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float scale_from_max(float m)
+{
+    return fmaxf(m, 1e-9f) / 127.0f;
+}
+
+__device__ __forceinline__ int8_t quantize_one(float v, float s)
+{
+    float q = __builtin_rintf(v / s);
+    q = fminf(fmaxf(q, -128.0f), 127.0f);
+    return (int8_t)(int)q;
+}
+
+// a + x * x, rounded twice.
+__device__ __forceinline__ float add_square(float a, float x)
+{
+#pragma clang fp contract(off)
+    return a + x * x;
+}
+
+// RMSNorm's reciprocal from the 256 per-thread partial sums of squares of a
+// row of k values in part[0..255] (LDS): thread t has added x[j]^2 for j = t,
+// t + 256, ... in order; the partials meet pairwise, part[t] += part[t + s] for
+// s = 128, 64, 32, .., 1 (the last six levels inside wave 0 by lane shuffles,
+// the same additions in the same order).  Every thread of the block calls it
+// (blocks of 256 threads or more) and receives r.
+__device__ __forceinline__ float rms_tree(float* part, int64_t k, float eps)
+{
+#pragma clang fp contract(off)
+    const int t = threadIdx.x;
+    __syncthreads();
+    if (t < 128) part[t] += part[t + 128];
+    __syncthreads();
+    if (t < 64) {
+        float v = part[t] + part[t + 64];
+        for (int st = 32; st >= 1; st >>= 1) {
+            const float o = __shfl_down(v, st, 64);
+            if (t < st) v += o;
+        }
+        if (t == 0) part[0] = 1.0f / sqrtf(v / (float)k + eps);
+    }
+    __syncthreads();
+    const float r = part[0];
+    __syncthreads();
+    return r;
+}
+
+// The same from a 256-thread block whose thread t holds partial a.
+__device__ __forceinline__ float rms_reciprocal(float a, int64_t k, float eps, float* part)
+{
+    part[threadIdx.x] = a;
+    return rms_tree(part, k, eps);
+}
+
+__device__ __forceinline__ float rms_value(float weight, float r, float x)
+{
+#pragma clang fp contract(off)
+    return weight * (r * x);
+}
+
+// h = act(gate) * up, act 1 = GeLU (tanh form), 2 = SiLU, in fp32 with the
+// device's expf / tanhf.
+__device__ __forceinline__ float glu_value(float g, float u, int act)
+{
+#pragma clang fp contract(off)
+    float a;
+    if (act == 1) {
+        const float c = 0.7978845608028654f;   // sqrt(2 / pi)
+        a = 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
+    } else {
+        a = g / (1.0f + expf(-g));
+    }
+    return a * u;
+}
+
+// The dequantised output of an exact dot: (acc * sx) * sw.
+__device__ __forceinline__ float dequant(int acc, float sx, float sw)
+{
+#pragma clang fp contract(off)
+    return (float)acc * sx * sw;
+}
+
+}  // namespace
+}  // namespace qmv

@@ -448,6 +448,7 @@ struct DeviceSetup {
     int32_t status = QMV_EHIP;
     int cus = 0;
     void* scratch = nullptr;   // device address of `scratch` on this device (null: not found)
+    int ffn_grid = 0;          // workgroups of a qmv_ffn_decode launch (0: cannot run)
 };
 
 DeviceSetup g_devices[kMaxDevices];
@@ -469,6 +470,13 @@ const DeviceSetup* device_setup(int* dev_out)
         if (e == hipSuccess) e = setup_grouped_attributes();
         if (e == hipSuccess) e = setup_prefill_attributes();
         if (e == hipSuccess) e = setup_sketch_attributes();
+        if (e == hipSuccess) e = setup_ffn_attributes();
+        if (e == hipSuccess) {
+            // residency of the largest feed-forward launch decides the grid of all
+            const int64_t cg = row_stride(QMV_W_TERNARY5, QMV_FFN_MAX_HIDDEN) / 16;
+            const int occ = ffn_max_wg_per_cu(ffn_lds_bytes(QMV_FFN_MAX_HIDDEN, cg));
+            d.ffn_grid = cus * std::min(occ, kFfnWgPerCu);
+        }
         // the scratch address only serves qmv_lmhead_argmax_static, which
         // refuses to run without it
         void* p = nullptr;
@@ -480,6 +488,40 @@ const DeviceSetup* device_setup(int* dev_out)
     if (d.status != QMV_OK) return nullptr;
     if (dev_out) *dev_out = dev;
     return &d;
+}
+
+// Workspace layout of qmv_ffn_decode: sized for any grid (down tasks number
+// at most one per 4 chunks of a 64-row group).
+FfnLayout ffn_layout(int64_t hidden, int64_t inter)
+{
+    FfnLayout o;
+    const int64_t cd = row_stride(QMV_W_TERNARY5, inter) / 16;
+    const int64_t dn_cap = ((hidden + 63) / 64) * ((cd + 3) / 4);
+    const int64_t gu = (inter + 31) / 32;
+    o.hp = round_up(hidden, 64);
+    o.done = kFfnCtrlBytes;
+    o.pmax = o.done + round_up(4 * dn_cap, 256);
+    o.glu = o.pmax + round_up(2 * 8 * round_up(gu, 2), 256);
+    o.acc = o.glu + round_up(8 * inter, 256);
+    o.bytes = o.acc + 2 * 4 * o.hp;
+    return o;
+}
+
+int64_t ffn_workspace(int64_t hidden, int64_t inter) { return ffn_layout(hidden, inter).bytes; }
+
+int32_t check_ffn_layer(const qmv_ffn_layer& y, int64_t hidden, int64_t inter)
+{
+    const qmv_weight* ws[3] = {&y.gate, &y.up, &y.down};
+    for (const qmv_weight* w : ws) {
+        const int32_t st = check_weight(*w);
+        if (st != QMV_OK) return st;
+        if (w->wtype != QMV_W_TERNARY5) return QMV_EUNSUPPORTED;
+    }
+    if (y.gate.n != inter || y.gate.k != hidden || y.up.n != inter || y.up.k != hidden || y.down.n != hidden ||
+        y.down.k != inter)
+        return QMV_ESHAPE;
+    if (!y.norm) return QMV_EINVAL;
+    return QMV_OK;
 }
 
 constexpr int64_t kMaxPrefillM = 65536;
@@ -823,6 +865,78 @@ int32_t qmv_glu_quantize(const float* gate, const float* up, int64_t m, int64_t 
     if (m < 1 || n < 1 || n > QMV_MAX_K || m > ((int64_t)1 << 31) - 1) return QMV_ESHAPE;
     if (act != QMV_ACT_GELU_TANH && act != QMV_ACT_SILU) return QMV_EINVAL;
     return hip_status(launch_glu_quantize(gate, up, m, n, act, x8, sx, as_stream(stream)));
+}
+
+int64_t qmv_ffn_workspace_bytes(int64_t hidden, int64_t inter)
+{
+    if (hidden < 1 || hidden > QMV_FFN_MAX_HIDDEN || inter < 1 || inter > QMV_FFN_MAX_INTER) return -1;
+    return ffn_workspace(hidden, inter);
+}
+
+int32_t qmv_ffn_grid(int32_t* grid)
+{
+    if (!grid) return QMV_EINVAL;
+    const DeviceSetup* d = device_setup(nullptr);
+    if (!d) return QMV_EHIP;
+    if (d->ffn_grid < 1) return QMV_EUNSUPPORTED;
+    *grid = d->ffn_grid;
+    return QMV_OK;
+}
+
+int32_t qmv_ffn_decode(const qmv_ffn_layer* layers, int32_t nlayers, float* h, float eps, int32_t act,
+                       void* workspace, int64_t ws_bytes, const int32_t* cancel, int64_t spin_limit,
+                       int32_t* status, uint64_t* trace, void* stream)
+{
+    if (!layers || !h || !status) return QMV_EINVAL;
+    if (nlayers < 1) return QMV_ESHAPE;
+    const int64_t hidden = layers[0].gate.k, inter = layers[0].gate.n;
+    if (hidden < 1 || hidden > QMV_FFN_MAX_HIDDEN || inter < 1 || inter > QMV_FFN_MAX_INTER) return QMV_ESHAPE;
+    for (int32_t l = 0; l < nlayers; ++l) {
+        const int32_t st = check_ffn_layer(layers[l], hidden, inter);
+        if (st != QMV_OK) return st;
+    }
+    if (!(eps >= 0.0f) || !std::isfinite(eps)) return QMV_EVALUE;
+    if (act != QMV_ACT_GELU_TANH && act != QMV_ACT_SILU) return QMV_EINVAL;
+    if (spin_limit < 0) return QMV_EVALUE;
+    if (trace && nlayers > QMV_FFN_LAUNCH_LAYERS) return QMV_EINVAL;
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < ffn_workspace(hidden, inter)) return QMV_EWORKSPACE;
+    const DeviceSetup* d = device_setup(nullptr);
+    if (!d) return QMV_EHIP;
+    if (d->ffn_grid < 1) return QMV_EUNSUPPORTED;
+    FfnLaunch f{};
+    f.h = h;
+    f.hidden = hidden;
+    f.inter = inter;
+    f.cg = row_stride(QMV_W_TERNARY5, hidden) / 16;
+    f.cd = row_stride(QMV_W_TERNARY5, inter) / 16;
+    // every workgroup takes gate/up tasks (32 rows of both) and down tasks (64
+    // rows x runs of 4 * dcs chunks, dcs <= 4), one of each where the grid allows
+    const int64_t grid = d->ffn_grid;
+    f.gu_tasks = (int32_t)((inter + 31) / 32);
+    const int64_t groups = (hidden + 63) / 64;
+    const int64_t dcs = std::min<int64_t>(4, std::max<int64_t>(1, (groups * f.cd + 4 * grid - 1) / (4 * grid)));
+    f.dcs = (int32_t)dcs;
+    f.dparts = (int32_t)((f.cd + 4 * dcs - 1) / (4 * dcs));
+    f.dn_tasks = (int32_t)(groups * f.dparts);
+    f.layout = ffn_layout(hidden, inter);
+    f.act = act;
+    f.eps = eps;
+    f.workspace = workspace;
+    f.cancel = cancel;
+    f.status = status;
+    f.trace = trace;
+    f.spin_limit = spin_limit;
+    f.grid = (int32_t)grid;
+    f.lds = ffn_lds_bytes(hidden, f.cg);
+    const hipStream_t s = as_stream(stream);
+    for (int32_t l0 = 0; l0 < nlayers; l0 += QMV_FFN_LAUNCH_LAYERS) {
+        f.layers = layers + l0;
+        f.nlayers = std::min<int32_t>(QMV_FFN_LAUNCH_LAYERS, nlayers - l0);
+        f.first_launch = l0 == 0;
+        const hipError_t e = launch_ffn(f, s);
+        if (e != hipSuccess) return QMV_EHIP;
+    }
+    return QMV_OK;
 }
 
 int64_t qmv_gemv_workspace_bytes(const qmv_problem* probs, int32_t count)

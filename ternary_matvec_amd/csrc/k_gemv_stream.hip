@@ -24,24 +24,18 @@
 //    compute waves stream the current one, so activation loads never sit in
 //    the compute waves' in-order memory counters.  For ternary weights what is
 //    staged is not x itself but, per packed byte, the five int16 combinations
-//    Z_1..Z_5 described below, in the order the weight registers come out of
+//    Z_1..Z_5 of zform.hpp, in the order the weight registers come out of
 //    the unpacker: the page's once-per-token input reorder.
 //  * Weight loads are raw buffer loads into a register ring (kRing - 1 chunk
 //    loads in flight while one is consumed): past the end of the matrix they
 //    return zeros instead of faulting, so no lane clamps or branches; loads past
 //    a tile's last chunk fetch the next tile's first chunks.
 //
-// Ternary arithmetic.  For a packed byte b with base-3 digits d_1..d_5 (d_1 the
-// most significant, digit d = trit + 1) meeting activations X_1..X_5, let
-// P_j = floor(b / 3^(5-j)), so d_j = P_j - 3 P_(j-1) and
-//     sum_j d_j X_j = sum_j P_j Z_j,   Z_j = X_j - 3 X_(j+1) (j < 5),  Z_5 = X_5.
-// The unpacker holds P_j of two bytes as the fp16 pair 1024 + P_j, whose int16
-// bit pattern is 25600 + P_j, so one v_dot2_i32_i16 with the int16 pair of Z
-// values adds P.Z plus 25600 * (Z sum); that constant and sum x (trit = d - 1)
-// are taken off once per row.  Sums are modulo 2^32, exact whenever the true
-// dot fits int32.
+// Ternary arithmetic: the Z form of zform.hpp (P_j . Z_j sums on v_dot2_i32_i16,
+// one correction per row).
 #include "qmv_internal.hpp"
 #include "unpack.hpp"
+#include "zform.hpp"
 
 namespace qmv {
 namespace {
@@ -61,13 +55,6 @@ constexpr uint32_t kEnd = 0xffffffffu;         // no tile
 constexpr int kNonTemporal = 2;                // buffer instruction cache policy: nt
 constexpr int kDescSlots = 3;                  // tile descriptors in LDS, used round robin
 
-typedef short s16x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ int dot2(uint32_t a, uint32_t b, int c)
-{
-    return __builtin_amdgcn_sdot2(__builtin_bit_cast(s16x2, a), __builtin_bit_cast(s16x2, b), c, false);
-}
-
 // Sum over a wave, exact in int32 arithmetic: prefix sums inside each row of
 // 16 lanes by DPP row shifts (lanes shifted in from outside the row add 0),
 // then the four row totals through lane reads.
@@ -79,40 +66,6 @@ __device__ __forceinline__ int wave_total(int v)
     v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
     return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) + __builtin_amdgcn_readlane(v, 47) +
            __builtin_amdgcn_readlane(v, 63);
-}
-
-// Z values of one 20-column group (natural dwords nat[0..4]; packed byte q of
-// the group covers columns 5q .. 5q+4, column 5q+e meeting the digit of 3^e,
-// so X_j = x[5q + 5 - j]).  out[2i + r] is the int16 pair of Z_(i+1) for bytes
-// r (low half) and r + 2 (high half): the same byte pairs the unpacker puts
-// into one fp16 register.  Adds the group's Z sum and x sum to sum_z, sum_x.
-__device__ __forceinline__ void z_group(const uint32_t nat[5], uint32_t out[10], int& sum_z, int& sum_x)
-{
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        int za[5], zb[5];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int q = r + 2 * h;
-            int x[5];
-#pragma unroll
-            for (int e = 0; e < 5; ++e) {
-                const int b = 5 * q + e;
-                x[e] = (int)(int8_t)(uint8_t)(nat[b >> 2] >> (8 * (b & 3)));
-                sum_x += x[e];
-            }
-            int* z = h ? zb : za;
-            z[0] = x[4] - 3 * x[3];
-            z[1] = x[3] - 3 * x[2];
-            z[2] = x[2] - 3 * x[1];
-            z[3] = x[1] - 3 * x[0];
-            z[4] = x[0];
-            // Z_1 + .. + Z_5 = x4 - 2 (x3 + x2 + x1 + x0)
-            sum_z += x[4] - 2 * (x[3] + x[2] + x[1] + x[0]);
-        }
-#pragma unroll
-        for (int i = 0; i < 5; ++i) out[2 * i + r] = __builtin_amdgcn_perm((uint32_t)zb[i], (uint32_t)za[i], 0x05040100u);
-    }
 }
 
 // One ticket from an XCD's counter (one lane).  The address is hidden from the
@@ -366,7 +319,7 @@ __device__ __forceinline__ void stage(const Tile& T, int lane, uint8_t* slot, in
         }
         if (WT == 1) {
             for (int d = 48 * T.C + lane; d < 48 * T.cpad; d += kWave) zo[d] = 0u;
-            const int cw = wave_total((int)(25600u * (uint32_t)s_z + (uint32_t)s_x));
+            const int cw = wave_total(z_correction(s_z, s_x));
             if (lane == 0) corr[mi] = cw;
         } else {
             for (int d = units + lane; d < 4 * T.cpad; d += kWave) zo[d] = 0u;

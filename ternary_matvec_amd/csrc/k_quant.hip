@@ -11,39 +11,10 @@
 // Five trits per byte ("Step 1": 3^5 = 243 codes fit in a byte): byte j of a
 // row is sum_i (t[5j+i] + 1) * 3^i; columns past k count as trit 0.
 #include "qmv_internal.hpp"
+#include "actq.hpp"
 
 namespace qmv {
 namespace {
-
-__device__ __forceinline__ float wave_max(float v)
-{
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
-}
-
-// Max over a 256-thread block; every thread receives the result.
-__device__ __forceinline__ float block_max(float v, float* red)
-{
-    v = wave_max(v);
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    if (lane == 0) red[wave] = v;
-    __syncthreads();
-    float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ float scale_from_max(float m)
-{
-    return fmaxf(m, 1e-9f) / 127.0f;
-}
-
-__device__ __forceinline__ int8_t quantize_one(float v, float s)
-{
-    float q = __builtin_rintf(v / s);
-    q = fminf(fmaxf(q, -128.0f), 127.0f);
-    return (int8_t)(int)q;
-}
 
 // ---------------------------------------------------------------------------
 // Per-row quantisation: one workgroup per row.
@@ -139,16 +110,13 @@ __global__ __launch_bounds__(kBlock) void k_quantize_many(ActSets sets)
 // round trip through memory.  One workgroup per row.
 // ---------------------------------------------------------------------------
 
-// o = weight * (r * x), r = 1 / sqrt(ss / k + eps).  ss is an fp32 sum in a
-// fixed order: thread t adds x[j]^2 for j = t, t + 256, ... in order, then the
-// 256 partial sums meet pairwise (t += t + s for s = 128 .. 1).  Nothing is
-// contracted into fused multiply-adds, so the values (and the codes) are
-// reproducible exactly.
+// RMSNorm with the sum-of-squares order of rms_reciprocal (actq.hpp), then
+// the per-token quantisation; the values and the codes are reproducible
+// exactly.
 __global__ __launch_bounds__(kBlock) void k_rmsnorm_quantize(const float* __restrict__ x,
                                                             const float* __restrict__ weight, int64_t k, float eps,
                                                             int8_t* __restrict__ x8, float* __restrict__ sx)
 {
-#pragma clang fp contract(off)
     __shared__ float part[kBlock];
     __shared__ float red[4];
     const int64_t row = blockIdx.x;
@@ -156,35 +124,14 @@ __global__ __launch_bounds__(kBlock) void k_rmsnorm_quantize(const float* __rest
     int8_t* qr = x8 + row * k;
     const int t = threadIdx.x;
     float a = 0.0f;
-    for (int64_t j = t; j < k; j += kBlock) a += xr[j] * xr[j];
-    part[t] = a;
-    __syncthreads();
-    for (int st = kBlock / 2; st >= 1; st >>= 1) {
-        if (t < st) part[t] += part[t + st];
-        __syncthreads();
-    }
-    // correctly rounded division and root (the library is built with them)
-    const float r = 1.0f / sqrtf(part[0] / (float)k + eps);
+    for (int64_t j = t; j < k; j += kBlock) a = add_square(a, xr[j]);
+    const float r = rms_reciprocal(a, k, eps, part);
     float m = 0.0f;
-    for (int64_t j = t; j < k; j += kBlock) m = fmaxf(m, fabsf(weight[j] * (r * xr[j])));
+    for (int64_t j = t; j < k; j += kBlock) m = fmaxf(m, fabsf(rms_value(weight[j], r, xr[j])));
     m = block_max(m, red);
     const float s = scale_from_max(m);
     if (t == 0) sx[row] = s;
-    for (int64_t j = t; j < k; j += kBlock) qr[j] = quantize_one(weight[j] * (r * xr[j]), s);
-}
-
-// h = act(gate) * up, act 1 = GeLU (tanh form), 2 = SiLU, in fp32 with the
-// device's expf / tanhf.
-__device__ __forceinline__ float glu_value(float g, float u, int act)
-{
-    float a;
-    if (act == 1) {
-        const float c = 0.7978845608028654f;   // sqrt(2 / pi)
-        a = 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g)));
-    } else {
-        a = g / (1.0f + expf(-g));
-    }
-    return a * u;
+    for (int64_t j = t; j < k; j += kBlock) qr[j] = quantize_one(rms_value(weight[j], r, xr[j]), s);
 }
 
 constexpr int kGluThreads = 1024;

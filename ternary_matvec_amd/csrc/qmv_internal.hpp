@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <qmv.h>
+
 namespace qmv {
 
 constexpr int kWave = 64;         // CDNA wavefront width
@@ -185,5 +187,40 @@ int grouped_lanes_per_row(int64_t k);          // lanes sharing one row: 4 .. 64
 size_t grouped_lds_bytes(int64_t m, int64_t k);
 hipError_t launch_gemv_grouped(const DevProblem* probs, const uint32_t* tiles, int32_t count, int max_m, size_t lds,
                                hipStream_t s);
+
+// Feed-forward half of a layer stack, one token, one persistent launch
+// (k_ffn.hip).  Workspace: control words, then the down tasks' tags, the
+// per-task GLU maxima (two layer parities), the GLU value records and two
+// int32 accumulators; byte offsets in FfnLayout.
+constexpr int64_t kFfnCtrlBytes = 4096;
+constexpr int kFfnWgPerCu = 1;          // workgroups per compute unit, if occupancy allows
+struct FfnLayout {
+    int64_t hp;                         // accumulator words per parity (hidden rounded up to 64)
+    int64_t done, pmax, glu, acc, bytes;
+};
+struct FfnLaunch {
+    const qmv_ffn_layer* layers;        // host, nlayers entries (this launch's)
+    int32_t nlayers;
+    float* h;
+    int64_t hidden, inter;
+    int64_t cg, cd;                     // 16-byte chunks per gate/up row, per down row
+    int32_t dcs, dparts;                // down chunks per wave, chunk runs per 64-row group
+    int32_t gu_tasks, dn_tasks;
+    int32_t act;
+    float eps;
+    void* workspace;
+    FfnLayout layout;
+    const int32_t* cancel;
+    int32_t* status;
+    uint64_t* trace;
+    int64_t spin_limit;
+    int32_t first_launch;
+    int32_t grid;
+    size_t lds;
+};
+size_t ffn_lds_bytes(int64_t hidden, int64_t cg);
+int ffn_max_wg_per_cu(size_t lds);
+hipError_t setup_ffn_attributes();
+hipError_t launch_ffn(const FfnLaunch& f, hipStream_t s);
 
 }  // namespace qmv

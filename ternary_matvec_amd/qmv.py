@@ -44,6 +44,10 @@ class qmv_problem(ctypes.Structure):
                 ("acc", _c_ptr)]
 
 
+class qmv_ffn_layer(ctypes.Structure):
+    _fields_ = [("gate", qmv_weight), ("up", qmv_weight), ("down", qmv_weight), ("norm", _c_ptr)]
+
+
 class qmv_act(ctypes.Structure):
     _fields_ = [("x", _c_ptr), ("m", _c_i64), ("k", _c_i64), ("x8", _c_ptr), ("sx", _c_ptr)]
 
@@ -89,6 +93,10 @@ SIGNATURES = {
     "qmv_read_probe": (_c_i32, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "qmv_rmsnorm_quantize": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_glu_quantize": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_i32, _c_ptr, _c_ptr, _c_ptr]),
+    "qmv_ffn_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
+    "qmv_ffn_grid": (_c_i32, [ctypes.POINTER(_c_i32)]),
+    "qmv_ffn_decode": (_c_i32, [ctypes.POINTER(qmv_ffn_layer), _c_i32, _c_ptr, ctypes.c_float, _c_i32, _c_ptr,
+                                _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_sketch_bytes": (_c_i64, [_c_i64, _c_i64]),
     "qmv_sketch_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
     "qmv_sketch_build": (_c_i32, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_i64, _c_ptr]),
@@ -511,3 +519,60 @@ def qmv_glu_quantize(gate, up, act=QMV_ACT_GELU_TANH, x8=None, sx=None, stream=N
     _check(load().qmv_glu_quantize(_ptr(g2), _ptr(u2), m, n, int(act), _ptr(x8), _ptr(sx), _stream(stream)),
            "qmv_glu_quantize")
     return x8, sx
+
+
+QMV_FFN_OK = 0
+QMV_FFN_CANCELLED = 1
+QMV_FFN_TIMEOUT = 2
+QMV_FFN_LAUNCH_LAYERS = 32
+QMV_FFN_TRACE_STAMPS = 12
+QMV_FFN_MAX_HIDDEN = 8192
+QMV_FFN_MAX_INTER = 65536
+
+
+def qmv_ffn_workspace_bytes(hidden: int, inter: int) -> int:
+    return int(load().qmv_ffn_workspace_bytes(hidden, inter))
+
+
+def qmv_ffn_grid() -> int:
+    g = _c_i32(0)
+    _check(load().qmv_ffn_grid(ctypes.byref(g)), "qmv_ffn_grid")
+    return int(g.value)
+
+
+def ffn_layer_array(layers):
+    """layers: sequence of (gate Weight, up Weight, down Weight, norm tensor)."""
+    arr = (qmv_ffn_layer * len(layers))()
+    for i, (g, u, d, norm) in enumerate(layers):
+        _dev(norm, torch.float32, "norm")
+        arr[i].gate, arr[i].up, arr[i].down = g.desc, u.desc, d.desc
+        arr[i].norm = norm.data_ptr()
+    return arr
+
+
+def ffn_workspace(hidden: int, inter: int, device):
+    """A zero-filled, 256-byte aligned workspace for qmv_ffn_decode."""
+    n = qmv_ffn_workspace_bytes(hidden, inter)
+    if n < 0:
+        raise QmvError(QMV_ESHAPE, "qmv_ffn_workspace_bytes")
+    ws = _alloc_aligned(n, device)
+    ws.zero_()
+    return ws
+
+
+def qmv_ffn_decode(layers, h, eps=1e-6, act=QMV_ACT_GELU_TANH, workspace=None, status=None, cancel=None,
+                   spin_limit=0, trace=None, stream=None):
+    """The feed-forward half of len(layers) layers for one token, h updated in
+    place.  layers: a ctypes qmv_ffn_layer array (ffn_layer_array).  Returns the
+    status tensor (1 int32, device; read it after synchronising)."""
+    _dev(h, torch.float32, "h")
+    if not isinstance(layers, ctypes.Array):
+        layers = ffn_layer_array(layers)
+    if workspace is None:
+        workspace = ffn_workspace(int(layers[0].gate.k), int(layers[0].gate.n), h.device)
+    if status is None:
+        status = torch.zeros(1, dtype=torch.int32, device=h.device)
+    _check(load().qmv_ffn_decode(layers, len(layers), _ptr(h), ctypes.c_float(eps), int(act), _ptr(workspace),
+                                 workspace.numel(), None if cancel is None else ctypes.c_void_p(cancel.data_ptr()),
+                                 int(spin_limit), _ptr(status), _ptr(trace), _stream(stream)), "qmv_ffn_decode")
+    return status

@@ -239,3 +239,81 @@ def test_gemv_grouped_validation(lib):
     assert lib.qmv_gemv_workspace_bytes(big, 1) == -1
     # prefill takes ternary weights only
     assert lib.qmv_prefill_workspace_bytes((qmv.qmv_problem * 1)(_problem(wtype=g)), 1) == -1
+
+
+def _ffn_layers(n, hidden=1152, inter=6912):
+    arr = (qmv.qmv_ffn_layer * n)()
+    for i in range(n):
+        for name, (rows, cols) in (("gate", (inter, hidden)), ("up", (inter, hidden)), ("down", (hidden, inter))):
+            w = getattr(arr[i], name)
+            w.wtype, w.n, w.k, w.data, w.scale = qmv.QMV_W_TERNARY5, rows, cols, 4096 * (i + 1), 64
+        arr[i].norm = 128
+    return arr
+
+
+def test_ffn_workspace_bytes(lib):
+    # control words; a tag per down task (at most one per 4 chunks of a 64-row group); two
+    # parities of the GLU maxima of the 32-row gate/up tasks (8-byte records, an even count);
+    # inter 8-byte GLU records;
+    # two int32 accumulators of round_up(hidden, 64) -- each region 256-byte rounded
+    assert qmv.qmv_ffn_workspace_bytes(1152, 6912) == 4096 + 1792 + 3584 + 8 * 6912 + 2 * 4 * 1152
+    assert qmv.qmv_ffn_workspace_bytes(5, 3) == 4096 + 256 + 256 + 256 + 2 * 4 * 64
+    assert qmv.qmv_ffn_workspace_bytes(0, 8) == -1
+    assert qmv.qmv_ffn_workspace_bytes(8, 0) == -1
+    assert qmv.qmv_ffn_workspace_bytes(qmv.QMV_FFN_MAX_HIDDEN + 1, 8) == -1
+    assert qmv.qmv_ffn_workspace_bytes(8, qmv.QMV_FFN_MAX_INTER + 1) == -1
+
+
+def test_ffn_decode_validation(lib):
+    """qmv_ffn_decode refuses bad arguments on the host, before any device work."""
+    ws_need = qmv.qmv_ffn_workspace_bytes(1152, 6912)
+    ws, st, h, s = _fake(1 << 20), _fake(64), _fake(8192), None
+
+    def call(arr, n=None, h_=h, eps=1e-6, act=qmv.QMV_ACT_GELU_TANH, ws_=ws, wsb=ws_need, spin=0, st_=st,
+             trace=None):
+        return lib.qmv_ffn_decode(arr, len(arr) if n is None else n, h_, ctypes.c_float(eps), act, ws_, wsb, None,
+                                  spin, st_, trace, s)
+
+    arr = _ffn_layers(3)
+    assert lib.qmv_ffn_decode(None, 3, h, ctypes.c_float(1e-6), 1, ws, ws_need, None, 0, st, None, s) == \
+        qmv.QMV_EINVAL
+    assert call(arr, h_=None) == qmv.QMV_EINVAL
+    assert call(arr, st_=None) == qmv.QMV_EINVAL                 # the status word is required
+    assert call(arr, n=0) == qmv.QMV_ESHAPE
+    assert call(arr, eps=-1.0) == qmv.QMV_EVALUE
+    assert call(arr, eps=float("inf")) == qmv.QMV_EVALUE
+    assert call(arr, act=3) == qmv.QMV_EINVAL
+    assert call(arr, spin=-1) == qmv.QMV_EVALUE
+    assert call(arr, ws_=None) == qmv.QMV_EWORKSPACE
+    assert call(arr, ws_=_fake((1 << 20) + 16)) == qmv.QMV_EWORKSPACE   # not 256-byte aligned
+    assert call(arr, wsb=ws_need - 1) == qmv.QMV_EWORKSPACE
+    # a trace covers one launch
+    assert call(_ffn_layers(qmv.QMV_FFN_LAUNCH_LAYERS + 1), trace=_fake(64)) == qmv.QMV_EINVAL
+    # shapes: every layer the same hidden / inter, down the transpose of gate / up
+    bad = _ffn_layers(2)
+    bad[1].up.n = 6911
+    assert call(bad) == qmv.QMV_ESHAPE
+    bad = _ffn_layers(2)
+    bad[0].down.k = 1152
+    assert call(bad) == qmv.QMV_ESHAPE
+    assert call(_ffn_layers(1, hidden=qmv.QMV_FFN_MAX_HIDDEN + 1, inter=64)) == qmv.QMV_ESHAPE
+    assert call(_ffn_layers(1, hidden=64, inter=qmv.QMV_FFN_MAX_INTER + 1)) == qmv.QMV_ESHAPE
+    # ternary weights only, aligned, with scales and RMSNorm weights
+    bad = _ffn_layers(2)
+    bad[1].down.wtype = qmv.QMV_W_INT8
+    assert call(bad) == qmv.QMV_EUNSUPPORTED
+    bad = _ffn_layers(2)
+    bad[0].gate.data = 4096 + 8
+    assert call(bad) == qmv.QMV_EINVAL
+    bad = _ffn_layers(2)
+    bad[0].up.scale = None
+    assert call(bad) == qmv.QMV_EINVAL
+    bad = _ffn_layers(2)
+    bad[1].norm = None
+    assert call(bad) == qmv.QMV_EINVAL
+    import torch
+    if not torch.cuda.is_available():   # valid arguments and no usable device
+        assert call(arr) == qmv.QMV_EHIP
+        g = ctypes.c_int32(0)
+        assert lib.qmv_ffn_grid(ctypes.byref(g)) == qmv.QMV_EHIP
+    assert lib.qmv_ffn_grid(None) == qmv.QMV_EINVAL
