@@ -317,7 +317,8 @@ int32_t qmv_ffn_grid(int32_t* grid /* host */);
  *              written; for a workgroup with a down task (workgroup b takes task
  *              b) 6 its GLU inputs gathered, 7 staged, 8 dots done, 9 the atomic
  *              adds acknowledged (its completion mark follows); 10 layer end;
- *              11 unused.  Stamps a workgroup does not reach are 0.
+ *              11 (a count, not a time) the poll rounds of the layer's waits.
+ *              Stamps a workgroup does not reach are 0.
  * EINVAL / ESHAPE / EUNSUPPORTED / EVALUE / EWORKSPACE on bad arguments.
  */
 int32_t qmv_ffn_decode(const qmv_ffn_layer* layers /* host */, int32_t nlayers, float* h, float eps, int32_t act,

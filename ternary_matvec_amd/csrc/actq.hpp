@@ -58,8 +58,9 @@ __device__ __forceinline__ float add_square(float a, float x)
 // RMSNorm's reciprocal from the 256 per-thread partial sums of squares of a
 // row of k values in part[0..255] (LDS): thread t has added x[j]^2 for j = t,
 // t + 256, ... in order; the partials meet pairwise, part[t] += part[t + s] for
-// s = 128, 64, 32, .., 1 (the last six levels inside wave 0 by lane shuffles,
-// the same additions in the same order).  Every thread of the block calls it
+// s = 128, 64, 32, .., 1 (the last six levels inside wave 0 by lane shuffles and
+// DPP moves: the same additions in the same order; lanes t >= s compute values
+// nobody reads).  Every thread of the block calls it
 // (blocks of 256 threads or more) and receives r.
 __device__ __forceinline__ float rms_tree(float* part, int64_t k, float eps)
 {
@@ -70,10 +71,16 @@ __device__ __forceinline__ float rms_tree(float* part, int64_t k, float eps)
     __syncthreads();
     if (t < 64) {
         float v = part[t] + part[t + 64];
-        for (int st = 32; st >= 1; st >>= 1) {
+        for (int st = 32; st >= 16; st >>= 1) {
             const float o = __shfl_down(v, st, 64);
             if (t < st) v += o;
         }
+        // s = 8 .. 1 stay inside a row of 16 lanes: DPP row_shl:s hands lane t
+        // the value of lane t + s
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x108, 0xf, 0xf, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x104, 0xf, 0xf, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x102, 0xf, 0xf, true));
+        v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x101, 0xf, 0xf, true));
         if (t == 0) part[0] = 1.0f / sqrtf(v / (float)k + eps);
     }
     __syncthreads();

@@ -491,17 +491,19 @@ const DeviceSetup* device_setup(int* dev_out)
 }
 
 // Workspace layout of qmv_ffn_decode: sized for any grid (down tasks number
-// at most one per 4 chunks of a 64-row group).
+// at most one per kFfnComputeWaves chunks of a 64-row group).
 FfnLayout ffn_layout(int64_t hidden, int64_t inter)
 {
     FfnLayout o;
     const int64_t cd = row_stride(QMV_W_TERNARY5, inter) / 16;
-    const int64_t dn_cap = ((hidden + 63) / 64) * ((cd + 3) / 4);
+    const int64_t dn_cap = ((hidden + 63) / 64) * ((cd + kFfnComputeWaves - 1) / kFfnComputeWaves);
     const int64_t gu = (inter + 31) / 32;
     o.hp = round_up(hidden, 64);
+    o.done_rep = round_up(4 * dn_cap, 4096);
+    o.pmax_rep = round_up(2 * 8 * round_up(gu, 2), 4096);
     o.done = kFfnCtrlBytes;
-    o.pmax = o.done + round_up(4 * dn_cap, 256);
-    o.glu = o.pmax + round_up(2 * 8 * round_up(gu, 2), 256);
+    o.pmax = o.done + kFfnReplicas * o.done_rep;
+    o.glu = o.pmax + kFfnReplicas * o.pmax_rep;
     o.acc = o.glu + round_up(8 * inter, 256);
     o.bytes = o.acc + 2 * 4 * o.hp;
     return o;
@@ -910,13 +912,15 @@ int32_t qmv_ffn_decode(const qmv_ffn_layer* layers, int32_t nlayers, float* h, f
     f.cg = row_stride(QMV_W_TERNARY5, hidden) / 16;
     f.cd = row_stride(QMV_W_TERNARY5, inter) / 16;
     // every workgroup takes gate/up tasks (32 rows of both) and down tasks (64
-    // rows x runs of 4 * dcs chunks, dcs <= 4), one of each where the grid allows
+    // rows x runs of W * dcs chunks, W compute waves, dcs <= kFfnDownChunks), one
+    // of each where the grid allows
     const int64_t grid = d->ffn_grid;
+    const int64_t W = kFfnComputeWaves;
     f.gu_tasks = (int32_t)((inter + 31) / 32);
     const int64_t groups = (hidden + 63) / 64;
-    const int64_t dcs = std::min<int64_t>(4, std::max<int64_t>(1, (groups * f.cd + 4 * grid - 1) / (4 * grid)));
+    const int64_t dcs = std::min<int64_t>(kFfnDownChunks, std::max<int64_t>(1, (groups * f.cd + W * grid - 1) / (W * grid)));
     f.dcs = (int32_t)dcs;
-    f.dparts = (int32_t)((f.cd + 4 * dcs - 1) / (4 * dcs));
+    f.dparts = (int32_t)((f.cd + W * dcs - 1) / (W * dcs));
     f.dn_tasks = (int32_t)(groups * f.dparts);
     f.layout = ffn_layout(hidden, inter);
     f.act = act;

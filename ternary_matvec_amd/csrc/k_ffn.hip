@@ -50,12 +50,13 @@
 namespace qmv {
 namespace {
 
-constexpr int kCompute = 4;                       // compute waves
+constexpr int kCompute = kFfnComputeWaves;        // compute waves (two per SIMD)
 constexpr int kThreads = (kCompute + 1) * kWave;  // + the io wave
 constexpr int kCT = kCompute * kWave;             // compute threads
-constexpr int kGuRegs = 8;      // gate/up chunks a wave holds in registers
-constexpr int kDnRegs = 4;      // down chunks per wave (the largest run)
-constexpr int kNormRegs = 8;    // RMSNorm values per thread kept in registers (h of up to 2048)
+constexpr int kRmsThreads = 256;                  // RMSNorm's partial sums (the order of qmv_rmsnorm_quantize)
+constexpr int kGuRegs = 4;      // gate/up chunks a lane holds in registers
+constexpr int kDnRegs = kFfnDownChunks;   // down chunks per wave (the largest run)
+constexpr int kNormRegs = 4;    // RMSNorm weights per thread kept in registers (h of up to 2048)
 constexpr int64_t kDefaultSpin = 1 << 20;
 constexpr int kFfnStamps = QMV_FFN_TRACE_STAMPS;   // trace stamps per layer
 constexpr int kSc1 = 16;        // buffer instruction cache policy: sc1 (device-coherent)
@@ -130,10 +131,31 @@ __device__ __forceinline__ uint32_t z_of_group(const int8_t* x, int g, uint32_t*
     return (uint32_t)z_correction(s_z, s_x);
 }
 
+// Wave reductions by DPP row shifts (lanes shifted in from outside a row of 16
+// bring 0) and reads of the four row totals; every lane receives the result.
+// Call with every lane of the wave active.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v)
 {
-    for (int off = 32; off >= 1; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, kWave);
-    return v;
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 15) + (uint32_t)__builtin_amdgcn_readlane((int)v, 31) +
+           (uint32_t)__builtin_amdgcn_readlane((int)v, 47) + (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+// Max over a wave of non-negative values (float bit patterns order as uint).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
+}
+__device__ __forceinline__ float wave_fmax(float v)   // v >= 0
+{
+    return __uint_as_float(wave_umax(__float_as_uint(v)));
 }
 
 __device__ __forceinline__ v4u32 load_chunk(const uint8_t* base, int64_t n, int c, int64_t row)
@@ -156,8 +178,11 @@ struct FfnArgs {
     FfnLayerDev layer[QMV_FFN_LAUNCH_LAYERS];
     float* h;               // [hidden] in/out
     uint32_t* ctrl;         // control words
-    uint32_t* done;         // [dn_tasks] tag of each down task's finished layer
-    uint64_t* pmax;         // [2][even(gu_tasks)] records: max |GLU| of a gate/up task (by layer parity)
+    uint32_t* done;         // [kFfnReplicas][done_rep] tag of each down task's finished layer
+    uint64_t* pmax;         // [kFfnReplicas][pmax_rep] x [2][even(gu_tasks)] records: max |GLU| of a
+                            // gate/up task (by layer parity)
+    int32_t done_rep;       // words between tag replicas
+    int32_t pmax_rep;       // records between max replicas
     uint64_t* glu;          // [inter] records: GLU values
     int32_t* acc;           // [2][hp] int32 down sums (by layer parity)
     const int32_t* cancel;  // nonzero: stop (device or host-mapped memory), or null
@@ -186,9 +211,9 @@ namespace {
 __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    __shared__ float part[kCT];
+    __shared__ float part[kRmsThreads];
     __shared__ float red[kCompute];
-    __shared__ int tot[3][kWave];
+    __shared__ int tot[kCompute - 1][kWave];
     __shared__ uint32_t ired[kCompute];
     __shared__ float sxb_s;
     __shared__ int stop_s;
@@ -228,8 +253,10 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
     };
     // io wave: poll until ready() holds on every lane (true), or stop (false).
     // ready() issues the round's loads; the error and cancel words ride along.
+    uint32_t polls = 0;   // io wave: poll rounds of this layer (trace slot 11)
     auto io_wait = [&](auto ready) -> bool {
         for (int64_t i = 0;; ++i) {
+            ++polls;
             uint32_t e = 0, c = 0;
             if (lane == 0) e = load_agent(&ctrl[kErr]);
             if (lane == 1 && a.cancel)
@@ -254,7 +281,10 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
     // io wave: the max |GLU| of layer l over every gate/up task, if all are in
     // (m: the bits of the max, on every lane)
     const int gp = (a.gu_tasks + 1) & ~1;   // records per parity (even: 16-byte aligned halves)
-    const __amdgpu_buffer_rsrc_t rpmax = rsrc(a.pmax, (int64_t)16 * gp);
+    // polled words are read from this workgroup's XCD's replica (workgroups are
+    // dealt round robin over the XCDs)
+    const int rep = b % kFfnReplicas;
+    const __amdgpu_buffer_rsrc_t rpmax = rsrc(a.pmax + (size_t)rep * a.pmax_rep, (int64_t)16 * gp);
     auto pmax_ready = [&](int l, uint32_t& m) -> bool {
         bool ok = true;
         uint32_t mx = 0;
@@ -279,16 +309,18 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
                 }
             }
         }
-        for (int off = 32; off >= 1; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, kWave));
+        mx = wave_umax(mx);
         m = mx;
         return ok;
     };
     // Max over the compute threads (io wave: 0); every thread receives it.
     auto cmax = [&](float v) -> float {
-        v = wave_max(v);
+        v = wave_fmax(v);
         if (lane == 0 && !io) red[w] = v;
         __syncthreads();
-        const float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        float r = red[0];
+#pragma unroll
+        for (int i = 1; i < kCompute; ++i) r = fmaxf(r, red[i]);
         __syncthreads();
         return r;
     };
@@ -305,14 +337,15 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
     int8_t* const xd = reinterpret_cast<int8_t*>(dsm + 4 * kCompute * kDnRegs * 80 + 4 * kCompute * kDnRegs * 48) +
                        w * kDnRegs * 80;
 
-    // ---- gate/up tasks: 32 rows of both matrices; wave w takes matrix w / 2 and
-    // half w % 2 of the chunks, lanes 32..63 the odd chunks of that half ----------------
+    // ---- gate/up tasks: 32 rows of both matrices; wave w takes matrix w / 4 and
+    // quarter w % 4 of the chunks, lanes 32..63 the odd chunks of that quarter ----------
     const bool has_gu = b < a.gu_tasks;
-    const int cgh = (a.cg + 1) >> 1;
-    const int gmat = w >> 1;
+    const int cgq = (a.cg + 3) >> 2;
+    const int gmat = w >> 2;
     const int gpar = lane >> 5;
-    const int gc0 = (w & 1) * cgh + gpar;                                           // first chunk of the lane
-    const int gn = io ? 0 : (max(0, min(a.cg, (w & 1) * cgh + cgh) - (w & 1) * cgh) - gpar + 1) / 2;
+    const int gq0 = (w & 3) * cgq;
+    const int gc0 = gq0 + gpar;                                                     // first chunk of the lane
+    const int gn = io ? 0 : (max(0, min(a.cg, gq0 + cgq) - gq0) - gpar + 1) / 2;
     // ---- down tasks: 64 rows x 4 * dcs chunks; wave w takes dcs of them ----------------
     const bool has_dn = b < a.dn_tasks;
     auto task_chunks = [&](int task, int& c0, int& nch, int64_t& row) {
@@ -355,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
 
     // io wave: wait for layer l's down sums, then gather them and the layer's GLU
     // scale into LDS
-    const __amdgpu_buffer_rsrc_t rdone = rsrc(a.done, (int64_t)4 * a.dn_tasks);
+    const __amdgpu_buffer_rsrc_t rdone = rsrc(a.done + (size_t)rep * a.done_rep, (int64_t)4 * a.dn_tasks);
     const __amdgpu_buffer_rsrc_t racc = rsrc(a.acc, (int64_t)8 * a.hp);
     const __amdgpu_buffer_rsrc_t rglu = rsrc(a.glu, (int64_t)8 * I);
     auto gather_sums = [&](int l) -> bool {
@@ -417,17 +450,17 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
                 __syncthreads();
                 if (stop_s) break;
                 const float sxb = sxb_s;
-                if (!io)
-                    for (int j = t; j < H; j += kCT) {
+                if (t < kRmsThreads)
+                    for (int j = t; j < H; j += kRmsThreads) {
                         const float v = hs[j] + dequant(accs[j], sxb, sd_prev);
                         hs[j] = v;
                         ss = add_square(ss, v);
                     }
-            } else if (!io) {
-                for (int j = t; j < H; j += kCT) ss = add_square(ss, hs[j]);
+            } else if (t < kRmsThreads) {
+                for (int j = t; j < H; j += kRmsThreads) ss = add_square(ss, hs[j]);
             }
             stamp(l, 1);
-            if (!io) part[t] = ss;
+            if (t < kRmsThreads) part[t] = ss;
             const float r = rms_tree(part, H, a.eps);
             stamp(l, 2);
             float o[kNormRegs];
@@ -460,7 +493,9 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
             cpart = wave_sum(cpart);
             if (lane == 0 && !io) ired[w] = cpart;
             __syncthreads();
-            const uint32_t corr = ired[0] + ired[1] + ired[2] + ired[3];
+            uint32_t corr = 0;
+#pragma unroll
+            for (int i = 0; i < kCompute; ++i) corr += ired[i];
             stamp(l, 4);
             for (int task = b, first = 1; task < a.gu_tasks; task += G, first = 0) {
                 const int64_t row = (int64_t)32 * task + (lane & 31);
@@ -484,16 +519,22 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
                 if (w == 0) {
                     float mv = 0.0f;
                     if (lane < 32) {
-                        const int tg = (int)((uint32_t)total + (uint32_t)tot[0][lane] - corr);
-                        const int tu = (int)((uint32_t)tot[1][lane] + (uint32_t)tot[2][lane] - corr);
+                        uint32_t g = (uint32_t)total - corr, u = 0u - corr;
+#pragma unroll
+                        for (int i = 0; i < kCompute / 2 - 1; ++i) g += (uint32_t)tot[i][lane];
+#pragma unroll
+                        for (int i = kCompute / 2 - 1; i < kCompute - 1; ++i) u += (uint32_t)tot[i][lane];
+                        const int tg = (int)g, tu = (int)u;
                         const float v = glu_value(dequant(tg, sxa, sg), dequant(tu, sxa, su), a.act);
                         if (row < I) {
                             store_record(a.glu + row, __float_as_uint(v), tag(l));
                             mv = fabsf(v);
                         }
                     }
-                    mv = wave_max(mv);
-                    if (lane == 0) store_record(a.pmax + (size_t)gp * (l & 1) + task, __float_as_uint(mv), tag(l));
+                    mv = wave_fmax(mv);
+                    if (lane < kFfnReplicas)
+                        store_record(a.pmax + (size_t)lane * a.pmax_rep + (size_t)gp * (l & 1) + task, __float_as_uint(mv),
+                                     tag(l));
                 }
                 __syncthreads();
             }
@@ -570,27 +611,29 @@ __global__ __launch_bounds__(kThreads) void k_ffn(FfnArgs a)
                 __syncthreads();
                 stamp(l, 8);
                 if (w == 0 && row < H) {
-                    const int s = (int)((uint32_t)total + (uint32_t)tot[0][lane] + (uint32_t)tot[1][lane] +
-                                        (uint32_t)tot[2][lane]);
-                    __hip_atomic_fetch_add(&accl[row], s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-                // The accumulator of layer l - 1: every gate/up task read it before
-                // it wrote this layer's GLU values, which this task has seen; it is
-                // next added to in layer l + 1, which no task reaches before seeing
-                // this task's tag.
-                if (task == 0 && l > 0 && !io) {
-                    uint32_t* prev = reinterpret_cast<uint32_t*>(a.acc + (size_t)a.hp * ((l - 1) & 1));
-                    for (int j = t; j < H; j += kCT) store_agent(&prev[j], 0u);
+                    uint32_t sum = (uint32_t)total;
+#pragma unroll
+                    for (int i = 0; i < kCompute - 1; ++i) sum += (uint32_t)tot[i][lane];
+                    __hip_atomic_fetch_add(&accl[row], (int)sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    // The first task of a row group clears the group's rows of the
+                    // accumulator of layer l - 1: every gate/up task read them before
+                    // it wrote its max record of this layer, all of which this task
+                    // has seen; they are next added to in layer l + 1, which no task
+                    // reaches before seeing this task's tag.
+                    if (p == 0 && l > 0)
+                        store_agent(reinterpret_cast<uint32_t*>(a.acc + (size_t)a.hp * ((l - 1) & 1)) + row, 0u);
                 }
                 __builtin_amdgcn_s_waitcnt(0);   // the adds (and clears) are done
                 stamp(l, 9);
                 __syncthreads();
-                if (io && lane == 0) store_agent(&a.done[task], tag(l));
+                if (io && lane < kFfnReplicas) store_agent(&a.done[(size_t)lane * a.done_rep + task], tag(l));
             }
             if (stop) break;
             if (l + 1 < a.nlayers && !io) load_dn(l + 1, b);
         }
         stamp(l, 10);
+        if (a.trace && io && lane == 0) stamps[1 + kFfnStamps * l + 11] = polls;
+        polls = 0;
     }
     // ---- the last residual update, written out by workgroup 0 ----------------------------
     if (run && l == a.nlayers && b == 0) {
@@ -670,6 +713,8 @@ hipError_t launch_ffn(const FfnLaunch& f, hipStream_t s)
     a.ctrl = reinterpret_cast<uint32_t*>(ws);
     a.done = reinterpret_cast<uint32_t*>(ws + o.done);
     a.pmax = reinterpret_cast<uint64_t*>(ws + o.pmax);
+    a.done_rep = (int32_t)(o.done_rep / 4);
+    a.pmax_rep = (int32_t)(o.pmax_rep / 8);
     a.glu = reinterpret_cast<uint64_t*>(ws + o.glu);
     a.acc = reinterpret_cast<int32_t*>(ws + o.acc);
     a.cancel = f.cancel;

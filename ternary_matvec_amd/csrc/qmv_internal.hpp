@@ -189,14 +189,18 @@ hipError_t launch_gemv_grouped(const DevProblem* probs, const uint32_t* tiles, i
                                hipStream_t s);
 
 // Feed-forward half of a layer stack, one token, one persistent launch
-// (k_ffn.hip).  Workspace: control words, then the down tasks' tags, the
-// per-task GLU maxima (two layer parities), the GLU value records and two
-// int32 accumulators; byte offsets in FfnLayout.
+// (k_ffn.hip).  Workspace: control words, then kFfnReplicas copies of the down
+// tasks' tags and of the per-task GLU maxima (two layer parities), the GLU
+// value records and two int32 accumulators; byte offsets in FfnLayout.
 constexpr int64_t kFfnCtrlBytes = 4096;
 constexpr int kFfnWgPerCu = 1;          // workgroups per compute unit, if occupancy allows
+constexpr int kFfnComputeWaves = 8;     // compute waves of a workgroup (plus one io wave)
+constexpr int kFfnDownChunks = 2;       // down chunks per wave, at most
+constexpr int kFfnReplicas = 8;         // copies of the polled tags and maxima (one per XCD)
 struct FfnLayout {
     int64_t hp;                         // accumulator words per parity (hidden rounded up to 64)
     int64_t done, pmax, glu, acc, bytes;
+    int64_t done_rep, pmax_rep;         // bytes between the replicas of the tags, of the maxima
 };
 struct FfnLaunch {
     const qmv_ffn_layer* layers;        // host, nlayers entries (this launch's)

@@ -252,12 +252,12 @@ def _ffn_layers(n, hidden=1152, inter=6912):
 
 
 def test_ffn_workspace_bytes(lib):
-    # control words; a tag per down task (at most one per 4 chunks of a 64-row group); two
-    # parities of the GLU maxima of the 32-row gate/up tasks (8-byte records, an even count);
-    # inter 8-byte GLU records;
-    # two int32 accumulators of round_up(hidden, 64) -- each region 256-byte rounded
-    assert qmv.qmv_ffn_workspace_bytes(1152, 6912) == 4096 + 1792 + 3584 + 8 * 6912 + 2 * 4 * 1152
-    assert qmv.qmv_ffn_workspace_bytes(5, 3) == 4096 + 256 + 256 + 256 + 2 * 4 * 64
+    # control words; 8 replicas (4 KiB-rounded) of a tag per down task (at most one per 8
+    # chunks of a 64-row group) and of two parities of the GLU maxima of the 32-row gate/up
+    # tasks (8-byte records, an even count); inter 8-byte GLU records (256-byte rounded); two
+    # int32 accumulators of round_up(hidden, 64)
+    assert qmv.qmv_ffn_workspace_bytes(1152, 6912) == 4096 + 8 * 4096 + 8 * 4096 + 8 * 6912 + 2 * 4 * 1152
+    assert qmv.qmv_ffn_workspace_bytes(5, 3) == 4096 + 8 * 4096 + 8 * 4096 + 256 + 2 * 4 * 64
     assert qmv.qmv_ffn_workspace_bytes(0, 8) == -1
     assert qmv.qmv_ffn_workspace_bytes(8, 0) == -1
     assert qmv.qmv_ffn_workspace_bytes(qmv.QMV_FFN_MAX_HIDDEN + 1, 8) == -1

@@ -265,7 +265,8 @@ def test_ffn_trace(qmv_gpu):
     gu_tasks = (I + 31) // 32
     gu = t[:min(grid, gu_tasks)]
     assert np.all(t[:, 0] > 0)
-    for row in t:
+    times = t[:, 1:].reshape(grid, L, S)[:, :, :S - 1]          # slot S-1 counts poll rounds
+    for row in np.concatenate([t[:, :1], times.reshape(grid, -1)], axis=1):
         nz = row[row > 0]
         assert np.all(np.diff(nz) >= 0)
     st_gu = gu[:, 1:].reshape(len(gu), L, S)
