@@ -14,12 +14,12 @@
 //  * Every workgroup takes both kinds of task, so each step of a layer has the
 //    whole chip.  Gate/up: workgroup b keeps its own copy of h in LDS; per layer
 //    it applies the previous layer's residual update, RMSNorm and the int8
-//    codes, then computes 32 rows of gate and up (four waves = gate/up x two
-//    halves of the chunks, lanes 32..63 taking the odd chunks of a half) and
-//    the GLU value of each row.  Down: workgroup b's task is 64 rows x a run of
-//    chunks, split over the four waves; it quantises the GLU values of its own
-//    columns and adds int32 partial sums into one of two accumulators with
-//    atomic adds.
+//    codes, then computes 32 rows of gate and up (eight waves = gate/up x four
+//    quarters of the chunks, lanes 32..63 taking the odd chunks of a quarter)
+//    and the GLU value of each row.  Down: workgroup b's task is 64 rows x a
+//    run of chunks, split over the eight waves; it quantises the GLU values of
+//    its own columns and adds int32 partial sums into one of two accumulators
+//    with atomic adds.
 //  * No device-wide barrier.  What crosses workgroups travels as 64-bit
 //    records (value, tag), tag = launch generation << 8 | layer + 1, written
 //    with device-coherent stores: the GLU values, the per-task max |GLU|, and
@@ -27,7 +27,7 @@
 //    polls exactly the records it needs until every tag is the one it waits
 //    for.  Records of other layers or launches carry other tags, so nothing is
 //    cleared between layers.
-//  * A fifth wave per workgroup (the io wave) does all polling and gathers the
+//  * A ninth wave per workgroup (the io wave) does all polling and gathers the
 //    values into LDS, so the compute waves' weight loads, which are issued a
 //    layer ahead as soon as their registers are free, never hold up a poll.
 //  * Waits are bounded: a poll also reads the error word and the caller's
