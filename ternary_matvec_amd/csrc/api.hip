@@ -93,11 +93,9 @@ constexpr int kStreamMaxM = 2;
 // Token counts whose ternary problems go to the matrix-core kernel.  At one
 // token the streaming dot-product kernel is faster (measured on the Gemma-3-1B
 // x26 step); from two tokens the matrix cores' cost does not grow with the
-// tokens while the dot products' does.  Past four tokens the kernel's operand
-// slots leave one workgroup per compute unit on 4096-column rows, and the
-// workgroup dot-product kernel measured faster.
+// tokens while the dot products' does.
 constexpr int kMxMinM = 2;
-constexpr int kMxMaxM = 4;
+constexpr int kMxMaxM = 16;
 
 // The kernel that serves one weight type of a launch.
 enum GemvKernel { kWorkgroupDot = 0, kStreamDot = 1, kMatrixCore = 2 };

@@ -1,16 +1,18 @@
-// k_gemv_mx.hip -- persistent grouped ternary GEMV for 1..8 tokens whose
+// k_gemv_mx.hip -- persistent grouped ternary GEMV for 1..16 tokens whose
 // multiply-adds run on the int8 matrix cores (gfx950).
 //
 // Same results as the other GEMV kernels: the exact int32 dot product of int8
 // activations with five-trits-per-byte weights, the two scales applied once
 // after the sum ("Gemma 3 1B at 114 tokens per second on a laptop CPU",
-// "Step 1"; cpp20gemma README, "Architecture & implementation").
+// "Step 1" and "Many users at once"; cpp20gemma README, "Architecture &
+// implementation").
 //
 // Why matrix cores for a product that streams its weights once.  Decoding a
-// packed byte and multiplying its five trits costs vector instructions; with
-// dot2 instructions a packed dword takes 20 of them, about as long as HBM takes
-// to deliver the dword.  Here the vector units only decode (11 instructions per
-// dword) and the matrix cores, otherwise idle, do every multiply-add.
+// packed byte and multiplying its five trits costs vector instructions, and
+// with dot-product instructions the multiplies grow with the token count.
+// Here the vector units only decode (15 instructions per packed dword,
+// whatever the token count) and the matrix cores, otherwise idle, do every
+// multiply-add.
 //
 // Arithmetic.  A packed byte b has base-3 digits d_1..d_5 (d_1 the most
 // significant, digit = trit + 1); byte q of a chunk covers columns 5q..5q+4 and
@@ -23,32 +25,34 @@
 // holds P_j, column B holds X_(j+1) (nothing for P_5).  The integer result is
 // A - 3 B + 128 sum X_5 - sum x: P_5 enters as b XOR 0x80 = b - 128, and
 // trit = digit - 1.
-//   * P_4..P_1 come from the packed-fp16 floor-by-3 chain (unpack.hpp): a
-//     register [P(b0), 0x64, P(b2), 0x64] of fp16 pairs 1024 + P is an operand
-//     as it stands; the activation bytes that face the 0x64 bytes are zero.
-//   * Per packed dword: 1 XOR, 2 byte permutes, 8 packed-fp16 FMAs; the nine
-//     operand dwords feed the matrix cores.
+//   * P_4..P_1 come from the packed-fp16 floor-by-3 chain (unpack.hpp) on the
+//     pairs 1024 + P of the even and of the odd bytes; one byte permute per
+//     level puts the four quotient bytes of a packed dword back in byte order.
+//   * Per packed dword: 1 XOR, 2 byte permutes, 8 packed-fp16 FMAs and 4 byte
+//     permutes; per level one operand of 16 quotient bytes.
 //
 // Matrix instruction: v_mfma_i32_16x16x64_i8 with the activations as the
-// first operand (16 columns: token t's A and B are columns 2t and 2t + 1) and
-// the weights as the second (16 rows).  Lane l supplies column / row l % 16 and
-// K group l / 16.  A wave step is 16 rows x 4 chunks (lane group g takes chunk
-// 4kr + g of its row, one 16-byte load) = 1 KiB of packed weights, 9 MFMAs.
+// first operand (16 columns: token t's A and B are columns 2t and 2t + 1 of
+// its column set; tokens 8..15 form a second set) and the weights as the
+// second (16 rows).  Lane l supplies column / row l % 16 and K group l / 16.
+// A wave step is 16 rows x 4 chunks (lane group g takes chunk 4kr + g of its
+// row, one 16-byte load) = 1 KiB of packed weights: five matrix instructions
+// per column set (P_5, P_4, .., P_1), each weight operand serving both sets.
 // Accumulator register i of lane l holds column 4 (l / 16) + i of row l % 16,
-// so lane group g finishes tokens 2g and 2g + 1 of its row without any
-// cross-lane reduction.
+// so lane group g finishes tokens 2g and 2g + 1 of its set and row without
+// any cross-lane reduction.
 //
 // Work and schedule (as the streaming VALU kernel): a workgroup is four
 // compute waves and one staging wave; a workgroup tile is 4 x 32 rows of one
 // problem over all of K (each wave two row groups of 16, which share every
-// activation operand read from LDS).  Tiles are dealt to the 8 XCD lists by the host; each workgroup's
-// first two tiles are fixed, later ones come from a per-XCD ticket.  The
-// staging wave writes the next tile's activation operands into LDS (two slots)
-// while the compute waves stream the current one:
-//     per chunk and token, 176 bytes: [X_5 of bytes 0..15] then, for
-//     j = 5..1, [X_j of bytes 0,2 | 4,6 | 8,10 | 12,14] and [the same for the
-//     odd bytes], each X in the low byte of a 16-bit lane (the high byte 0).
-// Column A of MFMA i >= 1 reads the block at 16 (i + 2), column B at 16 i.
+// activation operand read from LDS).  Tiles are dealt to the 8 XCD lists by
+// the host; each workgroup's first two tiles are fixed, later ones come from a
+// per-XCD ticket.  The staging wave writes the next tile's activation
+// operands into LDS (two slots) while the compute waves stream the current
+// one: per chunk and token 80 bytes, the page's input reorder ("Step 1": plane
+// v = the x values that meet digit v of each packed byte), plane v holding
+// X_(5-v) of bytes 0..15.  Column A of level j reads plane 5 - j, column B
+// plane 4 - j (16 bytes lower; zeros for P_5).
 #include <type_traits>
 
 #include "qmv_internal.hpp"
@@ -68,7 +72,8 @@ constexpr int kThreads = (kComputeWaves + 1) * kWave;   // + the staging wave
 #define QMV_MX_WAVES 5
 #endif
 constexpr int kRing = QMV_MX_RING;             // weight steps in the register ring: kRing - 1 loads ahead
-constexpr int kOps = 9;                        // matrix instructions per step
+constexpr int kOps = 5;                        // matrix instructions per step and column set
+constexpr int kPlaneBytes = 80;                // staged bytes per chunk and token (5 planes of 16)
 constexpr int kRowGroups = 2;                  // row groups of 16 per wave: a K range's operands serve both
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr uint32_t kEnd = 0xffffffffu;         // no tile
@@ -226,31 +231,19 @@ __device__ __forceinline__ void unit_of(int k, uint32_t sh, int u, const uint32_
     }
 }
 
-// The 11 operand dwords of one 20-column group (natural bytes B0..B19 in
-// dwords n0..n4, packed byte q covering B(5q)..B(5q+4), X_j(q) = B(5q + 5 - j))
-// written into the chunk's 176-byte block; adds the group's sum X_5 and sum x.
-// A byte permute takes two source dwords: byte selector 0..3 picks from the
-// second, 4..7 from the first, 12 gives zero.
-__device__ __forceinline__ uint32_t pick2(const uint32_t nat[5], int p0, int p1)
-{
-    // bytes p0 (low half) and p1 (high half) of the group, zero-extended
-    const int d0 = p0 >> 2, d1 = p1 >> 2;
-    const uint32_t sel = (uint32_t)(p0 & 3) | (12u << 8) | ((uint32_t)(4 + (p1 & 3)) << 16) | (12u << 24);
-    return __builtin_amdgcn_perm(nat[d1], nat[d0], sel);
-}
-
+// The five plane dwords of one 20-column group (natural bytes B0..B19 in
+// dwords nat[0..4]; packed byte q covers B(5q)..B(5q+4)) written into dword d
+// of the chunk's five 16-byte planes (plane v = [B(v), B(5+v), B(10+v),
+// B(15+v)], the x values that meet digit v); adds the group's sum X_5 (plane
+// 0) and sum x.
 __device__ __forceinline__ void put_group(uint8_t* blk, int d, const uint32_t nat[5], int& s5, int& s)
 {
     uint32_t* o = reinterpret_cast<uint32_t*>(blk);
-    // X_5 of the four bytes: B0, B5, B10, B15
-    const uint32_t x5c = __builtin_amdgcn_perm(__builtin_amdgcn_perm(nat[3], nat[2], 0x0c0c0702u),
-                                               __builtin_amdgcn_perm(nat[1], nat[0], 0x0c0c0500u), 0x05040100u);
-    o[d] = x5c;
+    uint32_t pl[5];
+    reorder20(nat[0], nat[1], nat[2], nat[3], nat[4], pl);
 #pragma unroll
-    for (int j = 5; j >= 1; --j)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) o[4 + 4 * (2 * (5 - j) + h) + d] = pick2(nat, 5 * h + 5 - j, 5 * h + 15 - j);
-    s5 = dot4(x5c, 0x01010101u, s5);
+    for (int v = 0; v < 5; ++v) o[4 * v + d] = pl[v];
+    s5 = dot4(pl[0], 0x01010101u, s5);
 #pragma unroll
     for (int i = 0; i < 5; ++i) s = dot4(nat[i], 0x01010101u, s);
 }
@@ -272,7 +265,7 @@ __device__ __forceinline__ void stage(const DevProblem* P, int lane, uint8_t* sl
         if (t > 0 && t >= m) continue;
         uint32_t sh;
         const __amdgpu_buffer_rsrc_t rs = row_rsrc(x8 + (size_t)t * k, k, sh);
-        uint8_t* base = slot + (size_t)t * cpad * 176;
+        uint8_t* base = slot + (size_t)t * cpad * kPlaneBytes;
         int s5 = 0, s = 0;
         for (int u0 = 0; u0 < units; u0 += kWave * kBatch) {
             uint32_t raw[kBatch][6];
@@ -289,7 +282,7 @@ __device__ __forceinline__ void stage(const DevProblem* P, int lane, uint8_t* sl
                 if (u < units) {
                     uint32_t nat[5];
                     unit_of(k, sh, u, raw[b], nat);
-                    put_group(base + (size_t)(u >> 2) * 176, u & 3, nat, s5, s);
+                    put_group(base + (size_t)(u >> 2) * kPlaneBytes, u & 3, nat, s5, s);
                 }
             }
         }
@@ -306,10 +299,11 @@ __device__ __forceinline__ void stage(const DevProblem* P, int lane, uint8_t* sl
 // [8 x (list offset, list size)][tile entries of the 8 XCD lists].
 // LDS: [2 slots of slot_bytes][3 descriptors][2 x MT token data][zeros].
 template <int MT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMV_MX_WAVES))) void k_gemv_mx(const DevProblem* __restrict__ probs,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT > 8 ? 2 : QMV_MX_WAVES))) void k_gemv_mx(const DevProblem* __restrict__ probs,
                                                       uint32_t* __restrict__ sched, int32_t slot_bytes)
 {
     extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int kSets = (2 * MT + 15) / 16;   // column sets of 8 tokens
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -414,38 +408,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMV_MX
         const uint8_t* const slot = smem + (size_t)par * slot_bytes;
         const TokenData* const tok = tokd + par * MT;
         const int m = cd.m;
-        // This lane's activation blocks (chunk 4kr + g of its token): column B
-        // reads 32 bytes lower than column A, and its P_5 operand is zero.
-        // Columns of tokens past m read token 0's blocks: every output column
-        // is independent of the others, and those columns are never stored.
-        const int lt = tcol < m ? tcol : 0;
-        const uint8_t* const blk = slot + (size_t)(lt * cur.cpad + g) * 176;
-        const uint8_t* const opbase = blk + (colb ? 0 : 32);
+        // This lane's activation planes (chunk 4kr + g of its token, in each
+        // column set): column A of level j reads plane 5 - j, column B plane
+        // 4 - j, 16 bytes lower, and zeros for P_5.  Columns of tokens past m
+        // read token 0's planes: every output column is independent of the
+        // others, and those columns are never stored.
+        const uint8_t* blk[kSets];
+#pragma unroll
+        for (int cs = 0; cs < kSets; ++cs) {
+            const int tt = 8 * cs + tcol;
+            blk[cs] = slot + (size_t)((tt < m ? tt : 0) * cur.cpad + g) * kPlaneBytes;
+        }
 
-        v4i32 accA[kRowGroups] = {};
-        v4i32 bop[kOps];
+        v4i32 acc[kRowGroups][kSets] = {};
+        v4i32 bop[kSets][kOps];
         // one step: the lane's 16 weight bytes against the K range's operands
-        auto run_step = [&](const v4u32& w, v4i32& ea) {
+        auto run_step = [&](const v4u32& w, v4i32 (&ea)[kSets]) {
             constexpr uint32_t mag = 0x64646464u;
-            v4u32 p5, lo, hi;
+            v4u32 p5, lo, hi, pq;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 p5[d] = w[d] ^ 0x80808080u;
                 lo[d] = __builtin_amdgcn_perm(mag, w[d], 0x04020400u);   // [b0 64 b2 64] = fp16 1024 + b
                 hi[d] = __builtin_amdgcn_perm(mag, w[d], 0x04030401u);   // [b1 64 b3 64]
             }
-            ea = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop[0], __builtin_bit_cast(v4i32, p5), ea, 0, 0, 0);
+#pragma unroll
+            for (int cs = 0; cs < kSets; ++cs)
+                ea[cs] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop[cs][0], __builtin_bit_cast(v4i32, p5), ea[cs], 0, 0, 0);
 #pragma unroll
             for (int lvl = 0; lvl < 4; ++lvl) {   // P_4 .. P_1
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     lo[d] = third2(lo[d]);
                     hi[d] = third2(hi[d]);
+                    pq[d] = __builtin_amdgcn_perm(hi[d], lo[d], 0x06020400u);   // the four quotients in byte order
                 }
-                ea = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop[1 + 2 * lvl], __builtin_bit_cast(v4i32, lo), ea, 0, 0,
-                                                            0);
-                ea = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop[2 + 2 * lvl], __builtin_bit_cast(v4i32, hi), ea, 0, 0,
-                                                            0);
+#pragma unroll
+                for (int cs = 0; cs < kSets; ++cs)
+                    ea[cs] = __builtin_amdgcn_mfma_i32_16x16x64_i8(bop[cs][1 + lvl], __builtin_bit_cast(v4i32, pq),
+                                                                   ea[cs], 0, 0, 0);
             }
         };
         // Register ring: while step s is consumed, steps s+1 .. s+kRing-1 are in
@@ -472,13 +473,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMV_MX
                     if (s < S) {
                         const int rg = u % RGS;   // a constant once the loop is unrolled
                         if (rg == 0) {   // a new K range: its operands from LDS
-                            const int off = (s / RGS) * 4 * 176;
+                            const int off = (s / RGS) * 4 * kPlaneBytes;
 #pragma unroll
-                            for (int i = 1; i < kOps; ++i)
-                                bop[i] = *reinterpret_cast<const v4i32*>(opbase + off + 16 * i);
-                            bop[0] = *reinterpret_cast<const v4i32*>(colb ? zeros : blk + off);
+                            for (int cs = 0; cs < kSets; ++cs) {
+#pragma unroll
+                                for (int i = 1; i < kOps; ++i)
+                                    bop[cs][i] = *reinterpret_cast<const v4i32*>(blk[cs] + off + 16 * (i - colb));
+                                bop[cs][0] = *reinterpret_cast<const v4i32*>(colb ? zeros : blk[cs] + off);
+                            }
                         }
-                        run_step(ring[u], accA[rg]);
+                        run_step(ring[u], acc[rg]);
                     }
                 }
             };
@@ -488,20 +492,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QMV_MX
         static_assert(kRing % kRowGroups == 0, "a ring group holds whole K ranges");
         groups(std::integral_constant<int, kRowGroups>{});
 
-        // ---- epilogue: lane group g holds tokens 2g and 2g + 1 of its row -------
+        // ---- epilogue: lane group g holds tokens 2g and 2g + 1 of each column
+        // set, for its row ---------------------------------------------------------
 #pragma unroll
         for (int rg = 0; rg < kRowGroups; ++rg) {
-            const v4i32 a = accA[rg];
             const int row = cur.row0 + 16 * rg + (lane & 15);
             if (row < cur.n) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int t = 2 * g + h;
-                    if (t < MT && t < m) {
-                        const int tot = (int)((uint32_t)a[2 * h] - 3u * (uint32_t)a[2 * h + 1] + (uint32_t)tok[t].corr);
-                        const size_t o = (size_t)t * cur.n + row;
-                        gstore_ptr(cd.y)[o] = (float)tot * tok[t].sx * cd.sw;
-                        if (cd.acc) gstore_ptr(cd.acc)[o] = tot;
+                for (int cs = 0; cs < kSets; ++cs) {
+                    const v4i32 a = acc[rg][cs];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int t = 8 * cs + 2 * g + h;
+                        if (t < MT && t < m) {
+                            const int tot =
+                                (int)((uint32_t)a[2 * h] - 3u * (uint32_t)a[2 * h + 1] + (uint32_t)tok[t].corr);
+                            const size_t o = (size_t)t * cur.n + row;
+                            gstore_ptr(cd.y)[o] = (float)tot * tok[t].sx * cd.sw;
+                            if (cd.acc) gstore_ptr(cd.acc)[o] = tot;
+                        }
                     }
                 }
             }
@@ -535,12 +544,12 @@ int gemv_mx_ring() { return kRing; }
 
 int gemv_mx_tokens(int max_m)
 {
-    return max_m <= 1 ? 1 : max_m <= 2 ? 2 : max_m <= 4 ? 4 : max_m <= 8 ? 8 : 0;
+    return max_m <= 1 ? 1 : max_m <= 2 ? 2 : max_m <= 4 ? 4 : max_m <= 8 ? 8 : max_m <= 16 ? 16 : 0;
 }
 
 int64_t gemv_mx_slot_bytes(int mt, int chunks)
 {
-    return (int64_t)mt * 4 * ((chunks + 3) / 4) * 176;
+    return (int64_t)mt * 4 * ((chunks + 3) / 4) * kPlaneBytes;
 }
 
 size_t gemv_mx_lds_bytes(int mt, int64_t slot_bytes)
@@ -556,6 +565,7 @@ int gemv_mx_wg_per_cu(int mt, int64_t slot_bytes)
         case 2: return mx_occupancy_one<2>(slot_bytes);
         case 4: return mx_occupancy_one<4>(slot_bytes);
         case 8: return mx_occupancy_one<8>(slot_bytes);
+        case 16: return mx_occupancy_one<16>(slot_bytes);
         default: return 0;
     }
 }
@@ -566,6 +576,7 @@ hipError_t setup_mx_attributes()
     if (e == hipSuccess) e = raise_lds_limit(reinterpret_cast<const void*>(&k_gemv_mx<2>));
     if (e == hipSuccess) e = raise_lds_limit(reinterpret_cast<const void*>(&k_gemv_mx<4>));
     if (e == hipSuccess) e = raise_lds_limit(reinterpret_cast<const void*>(&k_gemv_mx<8>));
+    if (e == hipSuccess) e = raise_lds_limit(reinterpret_cast<const void*>(&k_gemv_mx<16>));
     return e;
 }
 
@@ -576,6 +587,7 @@ hipError_t launch_gemv_mx(const DevProblem* probs, uint32_t* sched, int nb, int 
         case 2: return launch_mx_one<2>(probs, sched, nb, slot_bytes, s);
         case 4: return launch_mx_one<4>(probs, sched, nb, slot_bytes, s);
         case 8: return launch_mx_one<8>(probs, sched, nb, slot_bytes, s);
+        case 16: return launch_mx_one<16>(probs, sched, nb, slot_bytes, s);
         default: return hipErrorInvalidValue;
     }
 }
