@@ -294,20 +294,21 @@ TileModel stream_model(int wtype, int mt, bool skip)
     return m;
 }
 
-// The matrix-core kernel (ternary, 2..8 tokens): a workgroup tile of 128 rows
-// over all of K; a step is one K range (4 chunks) of one row group of 16 rows,
-// 1 KiB of weights per wave.
+// The matrix-core kernel (ternary, 2..16 tokens): a workgroup tile of compute
+// waves x rgs row groups of 16 rows over all of K; a step is one K range (4
+// chunks) of one row group, 1 KiB of weights per wave.
 TileModel mx_model(int mt)
 {
     TileModel m;
+    const int rgs = gemv_mx_row_groups(mt);
     m.targets = {0};
-    m.choose = [](const qmv_problem&, int) { return 2; };   // row groups per wave
-    m.rows = [](int) { return (int64_t)128; };
+    m.choose = [rgs](const qmv_problem&, int) { return rgs; };
+    m.rows = [mt](int) { return gemv_mx_tile_rows(mt); };
     // steps (padded to a multiple of the register ring) plus about two steps
     // of tile boundary
-    m.cost = [](const qmv_problem& p, int) {
-        const int steps = (chunks_of(p) + 3) / 4 * 2;
-        const int ring = gemv_mx_ring();
+    m.cost = [mt, rgs](const qmv_problem& p, int) {
+        const int steps = (chunks_of(p) + 3) / 4 * rgs;
+        const int ring = gemv_mx_ring(mt);
         return (double)((steps + ring - 1) / ring * ring) + 2.0;
     };
     m.slot_bytes = [mt](const qmv_problem& p, int) { return gemv_mx_slot_bytes(mt, chunks_of(p)); };

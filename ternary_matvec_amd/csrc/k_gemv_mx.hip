@@ -43,16 +43,18 @@
 // any cross-lane reduction.
 //
 // Work and schedule (as the streaming VALU kernel): a workgroup is four
-// compute waves and one staging wave; a workgroup tile is 4 x 32 rows of one
-// problem over all of K (each wave two row groups of 16, which share every
-// activation operand read from LDS).  Tiles are dealt to the 8 XCD lists by
-// the host; each workgroup's first two tiles are fixed, later ones come from a
-// per-XCD ticket.  The staging wave writes the next tile's activation
-// operands into LDS (two slots) while the compute waves stream the current
-// one: per chunk and token 80 bytes, the page's input reorder ("Step 1": plane
-// v = the x values that meet digit v of each packed byte), plane v holding
-// X_(5-v) of bytes 0..15.  Column A of level j reads plane 5 - j, column B
-// plane 4 - j (16 bytes lower; zeros for P_5).
+// compute waves and one staging wave; a workgroup tile is 4 x 16 x rgs rows of
+// one problem over all of K (each wave rgs row groups of 16, which share every
+// activation operand read from LDS; rgs = 2, 4, 4 for up to 4, 8, 16 tokens).
+// Tiles are dealt to the 8 XCD lists by the host; each workgroup's first two
+// tiles are fixed, later ones come from a per-XCD ticket.  The staging wave
+// writes the next tile's activation operands into LDS (two slots) while the
+// compute waves stream the current one: per chunk and token 80 bytes, the
+// page's input reorder ("Step 1": plane v = the x values that meet digit v of
+// each packed byte), plane v holding X_(5-v) of bytes 0..15.  Column A of
+// level j reads plane 5 - j, column B plane 4 - j (16 bytes lower; zeros for
+// P_5).  The staging wave takes one (token, chunk) per lane over all tokens
+// at once, so a tile's staging is a few rounds of loads, not one per token.
 #include <type_traits>
 
 #include "qmv_internal.hpp"
@@ -63,18 +65,62 @@ namespace {
 
 typedef int v4i32 __attribute__((ext_vector_type(4)));
 
-constexpr int kComputeWaves = 4;
-constexpr int kThreads = (kComputeWaves + 1) * kWave;   // + the staging wave
+// Shapes per token count (1..4 / 5..8 / 9..16 tokens): register-ring steps,
+// row groups of 16 per wave, compute waves, and the waves per SIMD the
+// registers are budgeted for.  Build-time knobs; the defaults are the fastest
+// measured on the BitNet-large x24 decode (16 tokens: 16-row-group tiles
+// 187.6 us, 256-row tiles 56.7 us, once the activations are staged a
+// (token, chunk) per lane).
 #ifndef QMV_MX_RING
 #define QMV_MX_RING 4
+#endif
+#ifndef QMV_MX_RGS
+#define QMV_MX_RGS 2
 #endif
 #ifndef QMV_MX_WAVES
 #define QMV_MX_WAVES 5
 #endif
-constexpr int kRing = QMV_MX_RING;             // weight steps in the register ring: kRing - 1 loads ahead
+#ifndef QMV_MX8_RING
+#define QMV_MX8_RING 4
+#endif
+#ifndef QMV_MX8_RGS
+#define QMV_MX8_RGS 4
+#endif
+#ifndef QMV_MX8_CWAVES
+#define QMV_MX8_CWAVES 4
+#endif
+#ifndef QMV_MX8_WAVES
+#define QMV_MX8_WAVES 3
+#endif
+#ifndef QMV_MX16_RING
+#define QMV_MX16_RING 8
+#endif
+#ifndef QMV_MX16_RGS
+#define QMV_MX16_RGS 4
+#endif
+#ifndef QMV_MX16_CWAVES
+#define QMV_MX16_CWAVES 4
+#endif
+#ifndef QMV_MX16_WAVES
+#define QMV_MX16_WAVES 2
+#endif
 constexpr int kOps = 5;                        // matrix instructions per step and column set
 constexpr int kPlaneBytes = 80;                // staged bytes per chunk and token (5 planes of 16)
-constexpr int kRowGroups = 2;                  // row groups of 16 per wave: a K range's operands serve both
+
+// Per token count: weight steps in the register ring (kRing - 1 loads ahead),
+// row groups of 16 per wave (a K range's operands serve all of them), compute
+// waves per workgroup (plus one staging wave) and the waves per SIMD the
+// register budget is made for.
+template <int MT>
+struct MxShape {
+    static constexpr int kRing = MT > 8 ? QMV_MX16_RING : MT > 4 ? QMV_MX8_RING : QMV_MX_RING;
+    static constexpr int kRowGroups = MT > 8 ? QMV_MX16_RGS : MT > 4 ? QMV_MX8_RGS : QMV_MX_RGS;
+    static constexpr int kComputeWaves = MT > 8 ? QMV_MX16_CWAVES : MT > 4 ? QMV_MX8_CWAVES : 4;
+    static constexpr int kThreads = (kComputeWaves + 1) * kWave;
+    static constexpr int kWavesPerEu = MT > 8 ? QMV_MX16_WAVES : MT > 4 ? QMV_MX8_WAVES : QMV_MX_WAVES;
+    static constexpr int kTileRows = 16 * kRowGroups * kComputeWaves;
+    static_assert(kRing % kRowGroups == 0, "a ring group holds whole K ranges");
+};
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr uint32_t kEnd = 0xffffffffu;         // no tile
 constexpr uint32_t kOob = 0xfffffff0u;         // a byte offset past any matrix: the load returns zeros
@@ -160,6 +206,7 @@ struct MTile {
     int n, nkr, S, Spad, cpad, row0;
 };
 
+template <int RGS, int RING, int WAVES>
 __device__ __forceinline__ MTile mtile_of(const MDesc& d, int wave, int lane)
 {
     MTile T;
@@ -170,9 +217,9 @@ __device__ __forceinline__ MTile mtile_of(const MDesc& d, int wave, int lane)
     T.nrec = (uint32_t)d.C * cstride;
     T.nkr = (d.C + 3) >> 2;
     T.cpad = 4 * T.nkr;
-    T.S = T.nkr * kRowGroups;
-    T.Spad = (T.S + kRing - 1) / kRing * kRing;
-    T.row0 = (d.wb * kComputeWaves + wave) * 16 * kRowGroups;
+    T.S = T.nkr * RGS;
+    T.Spad = (T.S + RING - 1) / RING * RING;
+    T.row0 = (d.wb * WAVES + wave) * 16 * RGS;
     T.lane_base = (uint32_t)(lane >> 4) * cstride + (uint32_t)(T.row0 + (lane & 15)) * 16u;
     return T;
 }
@@ -185,11 +232,12 @@ __device__ __forceinline__ v4u32 load_at(const uint8_t* w, uint32_t nrec, uint32
 }
 
 // The 16 weight bytes of this lane for step s of tile `a` (when `first`) or of
-// tile `b`: K range s / 2, row group s % 2; steps past the tile's
+// tile `b`: K range s / RGS, row group s % RGS; steps past the tile's
 // last are loads that return zeros.  One load instruction whatever the tile,
 // with the tile's fields chosen by wave-uniform selects: two load
 // instructions on two paths would make the compiler wait for every
 // outstanding load before each use.
+template <int RGS>
 __device__ __forceinline__ v4u32 load_step(const MTile& a, const MTile& b, bool first, int s)
 {
     const uint8_t* w = first ? a.w : b.w;
@@ -197,7 +245,7 @@ __device__ __forceinline__ v4u32 load_step(const MTile& a, const MTile& b, bool 
     const uint32_t kstride = first ? a.kstride : b.kstride;
     const uint32_t base = first ? a.lane_base : b.lane_base;
     const int S = first ? a.S : b.S;
-    const uint32_t step_off = (uint32_t)(s / kRowGroups) * kstride + (uint32_t)(s % kRowGroups) * 256u;
+    const uint32_t step_off = (uint32_t)(s / RGS) * kstride + (uint32_t)(s % RGS) * 256u;
     return load_at(w, nrec, s < S ? base + step_off : kOob);
 }
 
@@ -251,22 +299,99 @@ __device__ __forceinline__ void put_group(uint8_t* blk, int d, const uint32_t na
 // Stage tile P / te into an LDS slot: the operand blocks of chunks 0 .. cpad-1
 // for every token (zeros past k) and the tokens' corrections and scales.
 // `after_loads` runs once, right after the first activation loads are issued.
+// Chunk c of token t (rows 16-byte aligned, k a multiple of 16): the 80
+// columns as five 16-byte loads through one buffer over the staged tokens'
+// rows (pieces past the row read as zeros), then the four groups' planes,
+// plane v of the chunk written as one 16-byte block.
+__device__ __forceinline__ void chunk_load(__amdgpu_buffer_rsrc_t rs, int k, int t, int c, v4u32 raw[5])
+{
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int o = 80 * c + 16 * i;
+        const uint32_t voff = o < k ? (uint32_t)(t * k + o) : kOob;
+        raw[i] = __builtin_bit_cast(v4u32, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+    }
+}
+
+__device__ __forceinline__ int put_chunk(const v4u32 raw[5], uint8_t* blk)
+{
+    uint32_t nat[20];
+#pragma unroll
+    for (int i = 0; i < 5; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nat[4 * i + j] = raw[i][j];
+    uint32_t pl[4][5];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) reorder20(nat[5 * d], nat[5 * d + 1], nat[5 * d + 2], nat[5 * d + 3], nat[5 * d + 4], pl[d]);
+#pragma unroll
+    for (int v = 0; v < 5; ++v)
+        *reinterpret_cast<v4u32*>(blk + 16 * v) = v4u32{pl[0][v], pl[1][v], pl[2][v], pl[3][v]};
+    int s5 = 0, s = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) s5 = dot4(pl[d][0], 0x01010101u, s5);
+#pragma unroll
+    for (int i = 0; i < 20; ++i) s = dot4(nat[i], 0x01010101u, s);
+    return (int)(128u * (uint32_t)s5 - (uint32_t)s);   // the chunk's share of the token's correction
+}
+
+// Stage tile P / te into an LDS slot: the operand planes of chunks 0 .. cpad-1
+// for every token (zeros past k) and the tokens' corrections and scales.
+// Rows that start on 16 bytes with k a multiple of 16 go a (token, chunk) per
+// lane, all tokens together; others a 20-column group per lane, token by
+// token.  `after_loads` runs once, right after the first activation loads
+// are issued (in wave-uniform control flow: it may hold a barrier).
 template <int MT, class F>
 __device__ __forceinline__ void stage(const DevProblem* P, int lane, uint8_t* slot, TokenData* tok, F after_loads)
 {
-    constexpr int kBatch = 2;   // units per lane loaded before any is used
+    constexpr int kBatch = 2;   // units or chunks per lane loaded before any is used
     const int k = P->k, m = P->m;
     const int cpad = 4 * ((P->chunks + 3) >> 2);
     const int units = 4 * cpad;
     const int8_t* x8 = P->x8;
+    const bool whole = ((reinterpret_cast<uintptr_t>(x8) | (uintptr_t)k) & 15) == 0;
     bool first = true;
+    if (whole) {
+        const int mm = m < MT ? m : MT;   // tokens staged
+        const int total = mm * cpad;
+        // t = i / cpad as (i * inv) >> 22, exact for i * cpad < 2^22 (here
+        // i < MT * cpad, which the LDS bounds to about a thousand)
+        const uint32_t inv = ((1u << 22) + (uint32_t)cpad - 1) / (uint32_t)cpad;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)x8, (short)0, mm * k, (int)kRsrcWord3);
+        if (lane < mm) tok[lane].corr = 0;
+        for (int i0 = 0; i0 < total; i0 += kBatch * kWave) {   // uniform: after_loads may hold a barrier
+            v4u32 raw[kBatch][5];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int i = i0 + b * kWave + lane;
+                if (i < total) {
+                    const int t = (int)(((uint32_t)i * inv) >> 22);
+                    chunk_load(rs, k, t, i - t * cpad, raw[b]);
+                }
+            }
+            if (first) {
+                after_loads();
+                first = false;
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int i = i0 + b * kWave + lane;
+                if (i < total) {
+                    const int t = (int)(((uint32_t)i * inv) >> 22);
+                    const int corr = put_chunk(raw[b], slot + (size_t)i * kPlaneBytes);   // token t, chunk i - t cpad
+                    atomicAdd(&tok[t].corr, corr);
+                }
+            }
+        }
+        if (lane < mm) tok[lane].sx = cload_ptr(P->sx)[lane];
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
         if (t > 0 && t >= m) continue;
-        uint32_t sh;
-        const __amdgpu_buffer_rsrc_t rs = row_rsrc(x8 + (size_t)t * k, k, sh);
         uint8_t* base = slot + (size_t)t * cpad * kPlaneBytes;
         int s5 = 0, s = 0;
+        uint32_t sh;
+        const __amdgpu_buffer_rsrc_t rs = row_rsrc(x8 + (size_t)t * k, k, sh);
         for (int u0 = 0; u0 < units; u0 += kWave * kBatch) {
             uint32_t raw[kBatch][6];
 #pragma unroll
@@ -299,11 +424,14 @@ __device__ __forceinline__ void stage(const DevProblem* P, int lane, uint8_t* sl
 // [8 x (list offset, list size)][tile entries of the 8 XCD lists].
 // LDS: [2 slots of slot_bytes][3 descriptors][2 x MT token data][zeros].
 template <int MT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT > 8 ? 2 : QMV_MX_WAVES))) void k_gemv_mx(const DevProblem* __restrict__ probs,
+__global__ __launch_bounds__(MxShape<MT>::kThreads) __attribute__((amdgpu_waves_per_eu(MxShape<MT>::kWavesPerEu))) void k_gemv_mx(const DevProblem* __restrict__ probs,
                                                       uint32_t* __restrict__ sched, int32_t slot_bytes)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int kSets = (2 * MT + 15) / 16;   // column sets of 8 tokens
+    constexpr int kRing = MxShape<MT>::kRing;
+    constexpr int kRowGroups = MxShape<MT>::kRowGroups;
+    constexpr int kComputeWaves = MxShape<MT>::kComputeWaves;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -393,18 +521,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT > 8
     const int g = lane >> 4;          // K group: chunk 4kr + g
     const int tcol = col >> 1;        // token of that column
     const int colb = col & 1;         // 0: column A, 1: column B
-    MTile cur = mtile_of(desc_of(probs + (te0 >> kTileRowBits), te0), wave, lane);
+    MTile cur = mtile_of<kRowGroups, kRing, kComputeWaves>(desc_of(probs + (te0 >> kTileRowBits), te0), wave, lane);
     __builtin_amdgcn_s_barrier();     // the staging wave has issued tile 0's activation loads
     v4u32 ring[kRing];
 #pragma unroll
-    for (int r = 0; r + 1 < kRing; ++r) ring[r] = load_step(cur, cur, true, r);
+    for (int r = 0; r + 1 < kRing; ++r) ring[r] = load_step<kRowGroups>(cur, cur, true, r);
 
     for (int par = 0, q = 0;; par ^= 1, q = q == kDescSlots - 1 ? 0 : q + 1) {
         __syncthreads();   // this tile is staged and the next one named; every wave is done with the last
         const MDesc cd = desc_load(descs + q);
         const MDesc nd = desc_load(descs + (q == kDescSlots - 1 ? 0 : q + 1));
         const bool has_next = nd.te != kEnd;
-        const MTile nxt = mtile_of(has_next ? nd : cd, wave, lane);
+        const MTile nxt = mtile_of<kRowGroups, kRing, kComputeWaves>(has_next ? nd : cd, wave, lane);
         const uint8_t* const slot = smem + (size_t)par * slot_bytes;
         const TokenData* const tok = tokd + par * MT;
         const int m = cd.m;
@@ -467,7 +595,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT > 8
                         const uint32_t off = (uint32_t)(b / RGS) * cur.kstride + (uint32_t)(b % RGS) * 256u;
                         ring[(u + kRing - 1) % kRing] = load_at(cur.w, cur.nrec, b < S ? cur.lane_base + off : kOob);
                     } else {
-                        ring[(u + kRing - 1) % kRing] = load_step(nxt, nxt, true, has_next ? b - Spad : nxt.Spad);
+                        ring[(u + kRing - 1) % kRing] =
+                            load_step<kRowGroups>(nxt, nxt, true, has_next ? b - Spad : nxt.Spad);
                     }
                     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the step they overlap
                     if (s < S) {
@@ -489,7 +618,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT > 8
             for (int s0 = 0; s0 < Spad - kRing; s0 += kRing) group(s0, std::false_type{});
             group(Spad - kRing, std::true_type{});
         };
-        static_assert(kRing % kRowGroups == 0, "a ring group holds whole K ranges");
         groups(std::integral_constant<int, kRowGroups>{});
 
         // ---- epilogue: lane group g holds tokens 2g and 2g + 1 of each column
@@ -523,7 +651,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MT > 8
 template <int MT>
 hipError_t launch_mx_one(const DevProblem* probs, uint32_t* sched, int nb, int32_t slot_bytes, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_gemv_mx<MT>), dim3((unsigned)nb), dim3(kThreads), gemv_mx_lds_bytes(MT, slot_bytes), s,
+    hipLaunchKernelGGL((k_gemv_mx<MT>), dim3((unsigned)nb), dim3(MxShape<MT>::kThreads), gemv_mx_lds_bytes(MT, slot_bytes), s,
                        probs, sched, slot_bytes);
     return hipGetLastError();
 }
@@ -532,7 +660,7 @@ template <int MT>
 int mx_occupancy_one(int64_t slot_bytes)
 {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemv_mx<MT>), kThreads,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_gemv_mx<MT>), MxShape<MT>::kThreads,
                                                      gemv_mx_lds_bytes(MT, slot_bytes)) != hipSuccess)
         return 0;
     return n;
@@ -540,7 +668,17 @@ int mx_occupancy_one(int64_t slot_bytes)
 
 }  // namespace
 
-int gemv_mx_ring() { return kRing; }
+int gemv_mx_ring(int mt) { return mt > 8 ? MxShape<16>::kRing : mt > 4 ? MxShape<8>::kRing : MxShape<4>::kRing; }
+
+int gemv_mx_row_groups(int mt)
+{
+    return mt > 8 ? MxShape<16>::kRowGroups : mt > 4 ? MxShape<8>::kRowGroups : MxShape<4>::kRowGroups;
+}
+
+int64_t gemv_mx_tile_rows(int mt)
+{
+    return mt > 8 ? MxShape<16>::kTileRows : mt > 4 ? MxShape<8>::kTileRows : MxShape<4>::kTileRows;
+}
 
 int gemv_mx_tokens(int max_m)
 {

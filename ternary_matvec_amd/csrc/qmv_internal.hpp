@@ -145,11 +145,14 @@ int gemv_stream_wg_per_cu(int wtype, int max_m, int64_t slot_bytes, bool skip);
 hipError_t launch_gemv_stream(const DevProblem* probs, uint32_t* sched, int nb, int wtype, int max_m,
                               int32_t slot_bytes, bool skip, hipStream_t s);
 // Persistent ternary GEMV on int8 matrix cores for 1..16 tokens: the same
-// schedule words as the streaming kernel; a workgroup tile is 4 * 16 * 2 rows.
-// Tokens per launch are 1, 2, 4, 8 or 16 (gemv_mx_tokens); LDS = two slots of
-// slot_bytes and a few words.
+// schedule words as the streaming kernel; a workgroup tile is
+// gemv_mx_tile_rows rows (compute waves x row groups x 16).  Tokens per launch
+// are 1, 2, 4, 8 or 16 (gemv_mx_tokens); LDS = two slots of slot_bytes and a
+// few words.
 int gemv_mx_tokens(int max_m);                  // 0: more than 16 tokens
-int gemv_mx_ring();                             // steps of the kernel's weight ring (tiles pad to it)
+int gemv_mx_ring(int mt);                       // steps of the kernel's weight ring (tiles pad to it)
+int gemv_mx_row_groups(int mt);                 // row groups of 16 per wave
+int64_t gemv_mx_tile_rows(int mt);              // rows of a workgroup tile
 int64_t gemv_mx_slot_bytes(int mt, int chunks);
 size_t gemv_mx_lds_bytes(int mt, int64_t slot_bytes);
 int gemv_mx_wg_per_cu(int mt, int64_t slot_bytes);
