@@ -17,16 +17,19 @@ longer than the step it belongs to; its rocprofv3 kernel-trace median agrees
 with it (the profiles' command is `--profile-set`, which runs only the launches
 the profiles describe).
 
-Also reported by default: the 512-token prefill through one prefill plan launch
-(int8 TOPS against the published int8 matrix-core peak), and the CPU oracle
-timed on the host's cores on bounded samples of each configuration.
+Also reported by default: the "+o_proj" decode step (182 matrices), the
+BitNet-b1.58-large-shaped decode (168 matrices) at 1, 4 and 16 tokens with the
+kernel that served each and the dot-product plan beside it, the 512-token
+prefill through one prefill plan launch (int8 TOPS against the published int8
+matrix-core peak), and the CPU oracle timed on the host's cores on bounded
+samples of each configuration.
 
 Opt-in (--extras NAME,... or all; never part of the default run): the weight-copy
 sweep, chained per-matrix launches, the quantiser alone, host overhead per
 launch, the feed-forward half as a launch-per-step chain and as one persistent
-launch, the "+o_proj" decode row, zero-group skipping, the 262144 x 1152 bf16
-output layer with greedy argmax, the sketch head, the 768 x 288 int8 GEMV, the
-group-scaled int8 decode and BitNet-b1.58-large-shaped decode at 1..16 tokens.
+launch, zero-group skipping, the 262144 x 1152 bf16 output layer with greedy
+argmax, the sketch head, the 768 x 288 int8 GEMV, the group-scaled int8 decode
+and the BitNet decode at 1..16 tokens.
 Each extra prints its name before it starts.
 """
 import argparse
@@ -47,8 +50,8 @@ INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, datasheet
 GEMV_SOURCES = ("k_gemv_stream.hip", "unpack.hpp", "zform.hpp", "qmv_internal.hpp")
 GEMV_COUNTERS = os.path.join(ROOT, "profiles", "k_gemv_stream_counters.json")
 N_REP = 5
-EXTRAS = ("decode_copies_sweep", "decode_chained", "quantize_step", "host_overhead", "ffn", "decode_o_proj",
-          "zero_skip", "lmhead", "lmhead_sketch", "int8_gemv", "groupscale_decode", "bitnet_decode")
+EXTRAS = ("decode_copies_sweep", "decode_chained", "quantize_step", "host_overhead", "ffn", "zero_skip", "lmhead",
+          "lmhead_sketch", "int8_gemv", "groupscale_decode", "bitnet_decode_all")
 
 
 def log(*a):
@@ -67,9 +70,9 @@ def parse():
                          + ", ".join(EXTRAS))
     ap.add_argument("--profile-set", action="store_true",
                     help="only the launches the kernel profiles describe, each kernel name from one workload: "
-                         "decode steps, prefill passes, the output layer, the sketch head, the group-scaled "
-                         "decode, BitNet decode at 4 and 16 tokens, the 768x288 int8 GEMV, the persistent "
-                         "feed-forward launch and the zero-skip plan (no CPU baselines of the other configurations)")
+                         "decode steps, BitNet decode at 4 and 16 tokens, prefill passes, and the extras named "
+                         "with --extras in their profiled form (the persistent feed-forward launch alone, the "
+                         "zero-skip plan alone); no CPU baselines of the other configurations")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target CPU-oracle time for the headline")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB five times: the "
@@ -211,11 +214,13 @@ class DecodeStack:
 
 
 def route_of(m):
-    """The kernel a one-token-per-problem-row qmv_gemv plan runs (the library's routing rule)."""
+    """The kernel a qmv_gemv plan runs for ternary problems of m tokens whose
+    staged activations fit the matrix-core kernel's LDS (the library's routing)."""
     if m == 1:
-        return "k_gemv_stream (v_dot2 on staged Z operands)"
-    if m <= 4:
-        return "k_gemv_mx (v_mfma_i32_16x16x64_i8, %d token columns)" % (2 if m <= 2 else 4)
+        return "k_gemv_stream<1,1> (v_dot2 on staged Z operands)"
+    if m <= 16:
+        mt = 2 if m <= 2 else 4 if m <= 4 else 8 if m <= 8 else 16
+        return "k_gemv_mx<%d> (v_mfma_i32_16x16x64_i8 on prefix-quotient bytes)" % mt
     return "k_gemv (workgroup tiles, v_dot4 on reordered planes)"
 
 
@@ -469,10 +474,10 @@ def bench_zero_skip(dev, stream, reps, copies, dense=True):
     return out
 
 
-def bench_bitnet(dev, stream, reps, copies, ms_list=(1, 2, 4, 8, 16), dot_compare=(2, 4), prefill_compare=(4, 16)):
+def bench_bitnet(dev, stream, reps, copies, ms_list=(1, 2, 4, 8, 16), dot_compare=(2, 4)):
     """BitNet-b1.58-large shapes x24 (168 matrices) at several tokens per step:
-    the default plan's kernel, the dot-product plan beside the matrix-core one,
-    and the prefill GEMM on the same problems."""
+    the default plan's kernel, and the dot-product plan beside the matrix-core
+    one."""
     import torch
     from ternary_matvec_amd import qmv, synth
     out = {}
@@ -489,11 +494,6 @@ def bench_bitnet(dev, stream, reps, copies, ms_list=(1, 2, 4, 8, 16), dot_compar
             dms, _ = median_time(lambda i: dot[i % copies].launch(stream), reps, stream)
             row["dot_plan_us"] = us(dms)
             del dot
-        if m in prefill_compare:
-            pf = [qmv.prefill_plan(st.arrays[c]) for c in range(copies)]
-            pms, _ = median_time(lambda i: pf[i % copies].launch(stream), reps, stream)
-            row["prefill_gemm_us"] = us(pms)
-            del pf
         out["m%d" % m] = row
         del st
         torch.cuda.empty_cache()
@@ -970,44 +970,48 @@ def main():
                      "ceiling_kernel": "qmv_read_probe: one non-temporal 16-byte-load read of the same weight copies "
                                        "(%.1f MB in %.2f us)" % (stack.pool[0].numel() / 1e6, ceiling_ms * 1e3)},
     }
+    # the decode rows beside the headline: the same plan launches as the
+    # headline's, on the "+o_proj" stack and on the BitNet-large shapes (in the
+    # profile set only the matrix-core rows, so that every kernel name in a
+    # profile comes from one workload)
+    rows = ((("bitnet_decode", lambda: bench_bitnet(dev, stream, reps, min(args.copies, 8), ms_list=(4, 16),
+                                                    dot_compare=())),) if args.profile_set else
+            (("decode_o_proj", lambda: bench_o_proj(dev, stream, reps, args.copies)),
+             ("bitnet_decode", lambda: bench_bitnet(dev, stream, reps, min(args.copies, 8), ms_list=(1, 4, 16),
+                                                    dot_compare=(4, 16)))))
+    for name, fn in rows:
+        log(name)
+        result[name] = fn()
+        torch.cuda.synchronize()
+    for key, r in result["bitnet_decode"].items():
+        log("bitnet %s: %.1f us (%s)" % (key, r["gemv_us"], r["kernel"]))
     log("prefill (512 tokens)")
     result["prefill"] = bench_prefill(stack, dev, stream)
     log("prefill %.1f us, %.1f TOPS" % (result["prefill"]["prefill_us"], result["prefill"]["TOPS"]))
+    # opt-in extras (in the profile set, the forms the profiles describe)
+    ps = args.profile_set
+    runs = {"decode_copies_sweep": lambda: copies_sweep(stack, reps, stream),
+            "decode_chained": lambda: chained(stack, 20, stream),
+            "quantize_step": lambda: {"us": us(median_time(lambda i: qmv.qmv_quantize_act_many(
+                stack.acts, stream=stream), reps, stream)[0]), "bytes": stack.quant_bytes()},
+            "host_overhead": lambda: host_overhead(stack, stream),
+            "ffn": lambda: bench_ffn(stack, dev, stream, chain=not ps),
+            "zero_skip": lambda: bench_zero_skip(dev, stream, reps, min(args.copies, 4), dense=not ps),
+            "lmhead": lambda: bench_head(dev, stream),
+            "lmhead_sketch": lambda: bench_sketch(dev, stream),
+            "int8_gemv": lambda: bench_int8(dev, stream),
+            "groupscale_decode": lambda: bench_groupscale(dev, stream),
+            "bitnet_decode_all": lambda: bench_bitnet(dev, stream, reps, min(args.copies, 8),
+                                                      ms_list=(1, 2, 4, 8, 16), dot_compare=(2, 4, 8, 16))}
     extras = {}
-    if args.profile_set:
-        log("profile set: output layer, sketch head, group-scaled decode, FFN, zero skip, int8, BitNet 4/16")
-        extras["lmhead"] = bench_head(dev, stream)
+    for name in args.extras:
+        log(name)
+        extras[name] = runs[name]()   # an error ends the run: nothing is reported past a failed launch
+        torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        extras["lmhead_sketch"] = bench_sketch(dev, stream)
-        torch.cuda.empty_cache()
-        extras["groupscale_decode"] = bench_groupscale(dev, stream)
-        extras["ffn"] = bench_ffn(stack, dev, stream, chain=False)
-        extras["zero_skip"] = bench_zero_skip(dev, stream, reps, min(args.copies, 4), dense=False)
-        extras["int8_gemv"] = bench_int8(dev, stream)
-        extras["bitnet_decode"] = bench_bitnet(dev, stream, reps, min(args.copies, 8), ms_list=(4, 16),
-                                               dot_compare=(), prefill_compare=())
-    else:
-        runs = {"decode_copies_sweep": lambda: copies_sweep(stack, reps, stream),
-                "decode_chained": lambda: chained(stack, 20, stream),
-                "quantize_step": lambda: {"us": us(median_time(lambda i: qmv.qmv_quantize_act_many(
-                    stack.acts, stream=stream), reps, stream)[0]), "bytes": stack.quant_bytes()},
-                "host_overhead": lambda: host_overhead(stack, stream),
-                "ffn": lambda: bench_ffn(stack, dev, stream),
-                "decode_o_proj": lambda: bench_o_proj(dev, stream, reps, args.copies),
-                "zero_skip": lambda: bench_zero_skip(dev, stream, reps, min(args.copies, 4)),
-                "lmhead": lambda: bench_head(dev, stream),
-                "lmhead_sketch": lambda: bench_sketch(dev, stream),
-                "int8_gemv": lambda: bench_int8(dev, stream),
-                "groupscale_decode": lambda: bench_groupscale(dev, stream),
-                "bitnet_decode": lambda: bench_bitnet(dev, stream, reps, min(args.copies, 8))}
-        for name in args.extras:
-            log(name)
-            extras[name] = runs[name]()   # an error ends the run: nothing is reported past a failed launch
-            torch.cuda.synchronize()
-            torch.cuda.empty_cache()
-        if "us" in extras.get("lmhead", {}) and "us" in extras.get("lmhead_sketch", {}):
-            extras["lmhead_sketch"]["speedup_vs_full_head"] = round(extras["lmhead"]["us"] /
-                                                                    extras["lmhead_sketch"]["us"], 2)
+    if "us" in extras.get("lmhead", {}) and "us" in extras.get("lmhead_sketch", {}):
+        extras["lmhead_sketch"]["speedup_vs_full_head"] = round(extras["lmhead"]["us"] /
+                                                                extras["lmhead_sketch"]["us"], 2)
     if extras:
         result["extras"] = extras
     if args.copy_probe_mb:
@@ -1021,7 +1025,10 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         log("CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(stack, args.cpu_seconds, dev)
+        try:
+            result["cpu_baseline"] = cpu_baseline(stack, args.cpu_seconds, dev)
+        except Exception as e:
+            result["cpu_baseline"] = {"error": repr(e)}
         if not args.profile_set:
             log("CPU oracle on the other configurations")
             try:
