@@ -718,7 +718,9 @@ def bench_int8(dev, stream, reps=2000):
     x = torch.from_numpy(synth.normal(synth.stream_seed(synth.CONFIG_INT8, 0, 0, synth.TAG_ACT), (1, k))).to(dev)
     pw = qmv.qmv_pack_int8(w)
     x8, sx = qmv.qmv_quantize_act(x)
-    plan = qmv.gemv_plan(qmv.problem_array([qmv.Problem(pw, x8, sx)]))
+    y = torch.empty((1, n), dtype=torch.float32, device=dev)   # owned here for as long as the plan runs
+    prob = qmv.Problem(pw, x8, sx, y=y)
+    plan = qmv.gemv_plan([prob])
     torch.cuda.synchronize()
 
     def both(i):

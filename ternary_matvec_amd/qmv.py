@@ -251,8 +251,10 @@ def qmv_quantize_act_grouped(x, x8=None, sx=None, stream=None):
 
 
 def act_array(sets):
-    """[(x fp32 [m][k], x8 int8 [m][k], sx fp32 [m]), ...] -> a qmv_act array (the tensors must stay alive)."""
+    """[(x fp32 [m][k], x8 int8 [m][k], sx fp32 [m]), ...] -> a qmv_act array.  The array
+    holds references to the tensors, so they live as long as it does."""
     arr = (qmv_act * len(sets))()
+    arr._tensors = [tuple(s) for s in sets]
     for i, (x, x8, sx) in enumerate(sets):
         _dev(x, torch.float32, "x")
         _dev(x8, torch.int8, "x8")
@@ -295,9 +297,14 @@ class Problem:
 
 
 def problem_array(problems):
+    """Problems -> a qmv_problem array.  The array holds references to the
+    Problem objects (and so to their weights, activations and outputs): a plan
+    launched after the caller dropped its Problems still writes into live
+    tensors, never into memory the allocator has handed to someone else."""
     arr = (qmv_problem * len(problems))()
     for i, p in enumerate(problems):
         arr[i] = p.struct()
+    arr._problems = list(problems)
     return arr
 
 
@@ -346,7 +353,7 @@ class Plan:
 
     def __init__(self, kind, problems, workspace=None, stream=None):
         lib = load()
-        self.arr = _as_array(problems)          # keeps the host structs alive with the plan
+        self.arr = _as_array(problems)          # the host structs, and (through them) the tensors they name
         self._lib = lib
         self._h = _c_ptr()
         _check(lib.qmv_plan_create(kind, self.arr, len(self.arr), ctypes.byref(self._h)), "qmv_plan_create")
@@ -541,8 +548,10 @@ def qmv_ffn_grid() -> int:
 
 
 def ffn_layer_array(layers):
-    """layers: sequence of (gate Weight, up Weight, down Weight, norm tensor)."""
+    """layers: sequence of (gate Weight, up Weight, down Weight, norm tensor).  The
+    array holds references to them, so they live as long as it does."""
     arr = (qmv_ffn_layer * len(layers))()
+    arr._layers = [tuple(l) for l in layers]
     for i, (g, u, d, norm) in enumerate(layers):
         _dev(norm, torch.float32, "norm")
         arr[i].gate, arr[i].up, arr[i].down = g.desc, u.desc, d.desc
