@@ -500,7 +500,8 @@ __global__ __launch_bounds__(MxShape<MT>::kThreads) __attribute__((amdgpu_waves_
                 descs[qn].te = kEnd;
             }
             te = nx;
-            __syncthreads();
+            // the tile's LDS writes are done; the ticket taken above stays in flight
+            lds_barrier();
         }
         // Every workgroup of the XCD counts itself done once; the last one resets
         // both counters for the next launch (relaxed order suffices: every ticket
@@ -528,7 +529,9 @@ __global__ __launch_bounds__(MxShape<MT>::kThreads) __attribute__((amdgpu_waves_
     for (int r = 0; r + 1 < kRing; ++r) ring[r] = load_step<kRowGroups>(cur, cur, true, r);
 
     for (int par = 0, q = 0;; par ^= 1, q = q == kDescSlots - 1 ? 0 : q + 1) {
-        __syncthreads();   // this tile is staged and the next one named; every wave is done with the last
+        // this tile is staged and the next one named; every wave is done with the
+        // last; the ring's loads of this tile's first steps stay in flight
+        lds_barrier();
         const MDesc cd = desc_load(descs + q);
         const MDesc nd = desc_load(descs + (q == kDescSlots - 1 ? 0 : q + 1));
         const bool has_next = nd.te != kEnd;

@@ -417,7 +417,8 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
                 descs[qn].te = kEnd;
             }
             te = nx;
-            __syncthreads();
+            // the tile's LDS writes are done; the ticket taken above stays in flight
+            lds_barrier();
         }
         // Every workgroup of the XCD counts itself done once; the last one resets
         // both counters.  Relaxed order suffices: a workgroup reaches this point
@@ -447,7 +448,9 @@ __global__ __launch_bounds__(kStreamThreads) void k_gemv_stream(const DevProblem
         for (int h = 0; h < kRPL; ++h) ring[r][h] = load_step(cur, r, cur.voff + h * cur.voff_r);
 
     for (int par = 0, q = 0;; par ^= 1, q = q == kDescSlots - 1 ? 0 : q + 1) {
-        __syncthreads();   // this tile is staged and the next one named; every wave is done with the last
+        // this tile is staged and the next one named; every wave is done with the
+        // last; the ring's loads of this tile's first steps stay in flight
+        lds_barrier();
         // The next tile (after the last one: the tile itself, with its batch loads
         // past the matrix end, so every path is the same).
         const TileDesc cd = desc_load(descs + q);

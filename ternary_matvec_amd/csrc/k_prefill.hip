@@ -69,15 +69,6 @@ __device__ __forceinline__ int apos(int r, int p)
     return r * kARow + 16 * (q >= kPieces ? q - kPieces : q);
 }
 
-// Workgroup barrier for LDS hand-offs that leaves this wave's copies into LDS
-// in flight: it waits only for the wave's own LDS (and scalar) accesses; the
-// copies a hand-off depends on are waited for explicitly (wait_vmcnt) before
-// it.  The memory clobber keeps the compiler from moving LDS accesses across.
-__device__ __forceinline__ void lds_barrier()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // HBM -> LDS copy of 16 bytes per lane: lane i's bytes land at lds + 16 i (lds
 // wave-uniform).  Issued as inline assembly so that the compiler's wait-count
 // pass does not track it: it would wait for every copy in flight before each

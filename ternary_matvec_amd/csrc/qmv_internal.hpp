@@ -68,6 +68,17 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier for LDS hand-offs that leaves the wave's global memory
+// operations in flight (loads into registers or LDS, atomics): it waits only
+// for the wave's own LDS (and scalar) accesses, so what was written to LDS
+// before it is visible to every wave after it.  Anything else a hand-off
+// depends on is waited for explicitly before it.  The memory clobber keeps the
+// compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Once-per-device set-up of the kernel translation units: each raises its
 // kernels' dynamic-LDS limit to the whole kMaxLds, so launches never set
 // attributes.
