@@ -320,7 +320,7 @@ TileModel mx_model(int mt)
 }
 
 // Builds the table; returns QMV_OK or a status.  With allow_mx, ternary
-// problems of 2..4 tokens go to the matrix-core kernel; with skip_zero,
+// problems of 2..16 tokens go to the matrix-core kernel (when its LDS slots fit); with skip_zero,
 // ternary problems of one or two tokens go to the streaming kernel that skips
 // zero activation units.
 int32_t build_table(const qmv_problem* probs, int32_t count, int cus, bool allow_mx, bool skip_zero, Table& t)
