@@ -21,7 +21,8 @@ Also reported by default: the "+o_proj" decode step (182 matrices), the
 BitNet-b1.58-large-shaped decode (168 matrices) at 1, 4 and 16 tokens with the
 kernel that served each and the dot-product plan beside it, the 512-token
 prefill through one prefill plan launch (int8 TOPS against the published int8
-matrix-core peak), and the CPU oracle timed on the host's cores on bounded
+matrix-core peak and against a register-only matrix-instruction ceiling
+measured in the same run), and the CPU oracle timed on the host's cores on bounded
 samples of each configuration.
 
 Opt-in (--extras NAME,... or all; never part of the default run): the weight-copy
@@ -336,18 +337,36 @@ class PrefillStack:
         return sum(5 * v.numel() + 4 * v.shape[0] for v in self.x.values())
 
 
+def mfma_ceiling(dev, stream):
+    """The int8 matrix-instruction rate of this GPU with no memory traffic
+    (qmv_mfma_probe), for both instruction shapes; TOPS."""
+    import torch
+    from ternary_matvec_amd import qmv
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {}
+    for kind, name in ((0, "v_mfma_i32_16x16x64_i8"), (1, "v_mfma_i32_32x32x32_i8")):
+        iters = 2048 if kind == 0 else 1024
+        ops = qmv.qmv_mfma_probe(kind, iters, out, stream=stream)
+        ms, _ = median_time(lambda i: qmv.qmv_mfma_probe(kind, iters, out, stream=stream), 10, stream)
+        res[name] = round(ops / ms / 1e9, 1)
+    return res
+
+
 def bench_prefill(stack, dev, stream, reps=20):
     import torch
     from ternary_matvec_amd import qmv
     ps = PrefillStack(stack, 512, dev)
     kern_ms, kern_all = median_time(lambda i: ps.plan.launch(stream), reps, stream)
     quant_ms, _ = median_time(lambda i: qmv.qmv_quantize_act_many(ps.acts, stream=stream), reps, stream)
+    ceil = mfma_ceiling(dev, stream)
     tops = ps.ops() / kern_ms / 1e9
     out = {"workload": "ternary prefill, 512 tokens x Gemma-3-1B shapes x26 layers (156 matrices)",
            "kernel": "k_prefill (v_mfma_i32_32x32x32_i8)", "prefill_us": us(kern_ms),
            "prefill_us_reps": [us(v) for v in kern_all],
            "quantize_us": us(quant_ms), "quantize_GB/s": round(ps.quant_bytes() / quant_ms / 1e6, 1),
            "TOPS": round(tops, 1), "frac_int8_mfma_peak": round(tops / INT8_PEAK_TOPS, 4),
+           "measured_mfma_ceiling_TOPS": ceil,
+           "frac_of_measured_ceiling": round(tops / ceil["v_mfma_i32_32x32x32_i8"], 4),
            "GB/s": round(ps.bytes() / kern_ms / 1e6, 1), "ops_per_pass": ps.ops(), "bytes_per_pass": ps.bytes()}
     del ps
     torch.cuda.empty_cache()

@@ -487,6 +487,19 @@ int32_t qmv_lmhead_sketch_argmax(const uint16_t* w_bf16, const void* sketch, con
  */
 int32_t qmv_read_probe(const void* data, int64_t bytes, uint32_t* out, void* stream);
 
+/*
+ * qmv_mfma_probe -- a measurement aid, not part of the method: every wave of
+ * four workgroups per compute unit issues iters x 6 (kind 0:
+ * v_mfma_i32_16x16x64_i8) or iters x 8 (kind 1: v_mfma_i32_32x32x32_i8)
+ * independent int8 matrix instructions on register operands and folds the
+ * results into a word written to *out only when it equals a fixed key.  *ops
+ * (host) receives the int8 operations of the launch (2 per multiply-add);
+ * ops / time is the matrix cores' rate on this machine, the yardstick of
+ * qmv_gemm_prefill.
+ *   1 <= iters <= 2^20.   EINVAL otherwise.
+ */
+int32_t qmv_mfma_probe(int32_t kind, int32_t iters, uint32_t* out, int64_t* ops /* host */, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1023,6 +1023,14 @@ int64_t qmv_lmhead_workspace_bytes(int64_t v, int64_t k)
     return round_up(lmhead_partials(v) * 8, 256);
 }
 
+int32_t qmv_mfma_probe(int32_t kind, int32_t iters, uint32_t* out, int64_t* ops, void* stream)
+{
+    if (!out || !ops || (kind != 0 && kind != 1) || iters < 1 || iters > (1 << 20)) return QMV_EINVAL;
+    const DeviceSetup* d = device_setup(nullptr);
+    if (!d) return QMV_EHIP;
+    return hip_status(launch_mfma_probe(kind, iters, out, d->cus, ops, as_stream(stream)));
+}
+
 int32_t qmv_read_probe(const void* data, int64_t bytes, uint32_t* out, void* stream)
 {
     if (!data || !out || bytes < 0 || !aligned(data, 16) || (bytes & 15)) return QMV_EINVAL;

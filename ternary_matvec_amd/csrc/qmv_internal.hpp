@@ -191,6 +191,7 @@ hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const flo
                                 int32_t* idx, float* max_logit, int32_t* ncand, float* scores, void* workspace,
                                 hipStream_t s);
 hipError_t launch_read_probe(const void* data, int64_t bytes, uint32_t* out, int cus, hipStream_t s);
+hipError_t launch_mfma_probe(int kind, int iters, uint32_t* out, int cus, int64_t* ops, hipStream_t s);
 hipError_t launch_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, int32_t* idx,
                          float* max_logit, float* logits, void* workspace, hipStream_t s);
 int64_t lmhead_partials(int64_t v);

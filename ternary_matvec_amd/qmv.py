@@ -91,6 +91,7 @@ SIGNATURES = {
                                    _c_ptr]),
     "qmv_lmhead_argmax_static": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_read_probe": (_c_i32, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
+    "qmv_mfma_probe": (_c_i32, [_c_i32, _c_i32, _c_ptr, ctypes.POINTER(_c_i64), _c_ptr]),
     "qmv_rmsnorm_quantize": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_float, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_glu_quantize": (_c_i32, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_i32, _c_ptr, _c_ptr, _c_ptr]),
     "qmv_ffn_workspace_bytes": (_c_i64, [_c_i64, _c_i64]),
@@ -400,6 +401,14 @@ def qmv_read_probe(buf, out, stream=None):
     assert buf.is_cuda and out.is_cuda and out.dtype in (torch.int32, torch.uint32) and out.numel() >= 1
     _check(load().qmv_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
                                  _stream(stream)), "qmv_read_probe")
+
+
+def qmv_mfma_probe(kind, iters, out, stream=None) -> int:
+    """Launch the matrix-instruction yardstick; returns the launch's int8 operations."""
+    ops = _c_i64(0)
+    _check(load().qmv_mfma_probe(int(kind), int(iters), _ptr(out), ctypes.byref(ops), _stream(stream)),
+           "qmv_mfma_probe")
+    return int(ops.value)
 
 
 def qmv_lmhead_argmax(w_bf16, x, logits=None, idx=None, max_logit=None, workspace=None, want_logits=False,

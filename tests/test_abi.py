@@ -317,3 +317,13 @@ def test_ffn_decode_validation(lib):
         g = ctypes.c_int32(0)
         assert lib.qmv_ffn_grid(ctypes.byref(g)) == qmv.QMV_EHIP
     assert lib.qmv_ffn_grid(None) == qmv.QMV_EINVAL
+
+
+def test_mfma_probe_validation(lib):
+    ops = ctypes.c_int64(0)
+    out = _fake(64)
+    assert lib.qmv_mfma_probe(0, 10, None, ctypes.byref(ops), None) == qmv.QMV_EINVAL
+    assert lib.qmv_mfma_probe(0, 10, out, None, None) == qmv.QMV_EINVAL
+    assert lib.qmv_mfma_probe(2, 10, out, ctypes.byref(ops), None) == qmv.QMV_EINVAL
+    assert lib.qmv_mfma_probe(1, 0, out, ctypes.byref(ops), None) == qmv.QMV_EINVAL
+    assert lib.qmv_mfma_probe(1, (1 << 20) + 1, out, ctypes.byref(ops), None) == qmv.QMV_EINVAL

@@ -15,7 +15,7 @@ import pytest
 
 from ternary_matvec_amd import build
 
-MFMA_SOURCES = ("k_gemv_mx.hip", "k_prefill.hip")
+MFMA_SOURCES = ("k_gemv_mx.hip", "k_prefill.hip", "k_probe.hip")
 REG = re.compile(r"^([av])\[(\d+):(\d+)\]$|^([av])(\d+)$")
 
 
