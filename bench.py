@@ -555,7 +555,7 @@ def bench_sketch(dev, stream, reps=50, copies=6, tokens=32):
         ws_.append(ws_[0].clone())
     sk = [qmv.qmv_sketch_build(w) for w in ws_]
     torch.cuda.synchronize()
-    wsp = qmv._alloc_aligned(qmv.qmv_sketch_workspace_bytes(v, k), dev)
+    wsp = qmv.sketch_workspace(v, k, dev)
     xs = [torch.from_numpy(synth.normal(synth.stream_seed(synth.CONFIG_HEAD, 1, t, synth.TAG_ACT), (k,))).to(dev)
           for t in range(tokens)]
     idx = torch.empty(1, dtype=torch.int32, device=dev)

@@ -440,12 +440,16 @@ int32_t qmv_lmhead_argmax_static(const uint16_t* w_bf16, const float* x, int64_t
  *      rank order they form 4 groups (floor((k-T)/4) each, the last takes the
  *      rest), and group g adds c * mean|x|_g * (agreeing - disagreeing signs),
  *      c being the mean |w| of the table (a sign bit is set for a value < 0);
- *      the score is fp32, a = fma(w, x, a) over the exact dimensions in rank
+ *      the score is fp32: a = fma(w, x, a) over the exact dimensions in index
  *      order, then a = fma(weight_g, agreement_g, a) for g = 0..3;
  *   3. the candidates are the words whose score falls in the top bins that
- *      hold at least min(1024, v) words, a bin being the top 12 bits of the
- *      score's order-preserving key; only they are scored exactly (as in
- *      qmv_lmhead_argmax) and the first maximum among them is the choice.
+ *      hold at least min(1024, v) words, a bin being the top 13 bits of the
+ *      score's order-preserving key (a sixteenth of an octave), the bins
+ *      searched being the 256 below the highest non-empty one (16 octaves;
+ *      if they hold fewer words, every word is a candidate); only they are
+ *      scored exactly (as in qmv_lmhead_argmax) and the first maximum among
+ *      them is the choice.
+ * Two launches per token (scores; cut, rescoring and choice).
  * Limits: 8 <= k <= 8192, k % 8 == 0, 1 <= v <= QMV_MAX_N.
  */
 int64_t qmv_sketch_bytes(int64_t v, int64_t k);            /* -1 on bad shape */
@@ -453,8 +457,9 @@ int64_t qmv_sketch_workspace_bytes(int64_t v, int64_t k);  /* -1 on bad shape */
 
 /*
  * qmv_sketch_build -- one-time preparation from the output layer's weights:
- * the sign bits (word d/32 of row r at (d/32)*v + r), a dimension-major bf16
- * copy [k][v] and c, in `sketch` (256-byte aligned, >= qmv_sketch_bytes).
+ * the sign bits (word d/32 of row r at (d/32)*vp + r), a dimension-major bf16
+ * copy [k][vp] and c, in `sketch` (256-byte aligned, >= qmv_sketch_bytes);
+ * vp = v rounded up to a multiple of 1024, rows v..vp-1 zero in both tables.
  *   w_bf16  [v][k] bf16 bit patterns, row-major, 16-byte aligned, finite.
  * Not part of the per-token path.  EINVAL / ESHAPE / EWORKSPACE as above.
  */
@@ -464,13 +469,16 @@ int32_t qmv_sketch_build(const uint16_t* w_bf16, int64_t v, int64_t k, void* ske
 /*
  * qmv_lmhead_sketch_argmax -- the greedy choice through the sketch head.
  *   w_bf16     the same table the sketch was built from (exact rescoring).
- *   x          [k] fp32 hidden state, finite.
+ *   x          [k] fp32 hidden state, finite, 16-byte aligned.
  *   idx        1 int32: the chosen word.
  *   max_logit  nullable, 1 fp32: its exact logit.
  *   candidates nullable, 1 int32: how many words were rescored.
  *   scores     nullable, [v] fp32: every word's approximate score (step 1+2).
- *   workspace  >= qmv_sketch_workspace_bytes(v, k) bytes, 256-byte aligned;
- *              calls that share it must not overlap.
+ *   workspace  >= qmv_sketch_workspace_bytes(v, k) bytes, 256-byte aligned,
+ *              zero-filled before its first use; it carries state from one
+ *              call to the next and every call leaves it ready for the next
+ *              (also for other shapes).  Calls that share it must not
+ *              overlap; if a launch fails (QMV_EHIP), zero it again.
  */
 int32_t qmv_lmhead_sketch_argmax(const uint16_t* w_bf16, const void* sketch, const float* x, int64_t v,
                                  int64_t k, int32_t* idx, float* max_logit, int32_t* candidates, float* scores,

@@ -1086,7 +1086,8 @@ int32_t qmv_lmhead_sketch_argmax(const uint16_t* w_bf16, const void* sketch, con
                                  int32_t* idx, float* max_logit, int32_t* candidates, float* scores,
                                  void* workspace, int64_t ws_bytes, void* stream)
 {
-    if (!w_bf16 || !sketch || !x || !idx || !aligned(w_bf16, 16) || !aligned(sketch, 256)) return QMV_EINVAL;
+    if (!w_bf16 || !sketch || !x || !idx || !aligned(w_bf16, 16) || !aligned(sketch, 256) || !aligned(x, 16))
+        return QMV_EINVAL;
     if (v < 1 || v > QMV_MAX_N || k < 8 || k > kSketchMaxK || k % 8) return QMV_ESHAPE;
     if (!workspace || !aligned(workspace, 256) || ws_bytes < sketch_workspace_bytes(v)) return QMV_EWORKSPACE;
     if (!device_setup(nullptr)) return QMV_EHIP;

@@ -2,43 +2,75 @@
 // candidates ("Gemma 3 1B at 114 tokens per second on a laptop CPU", "Step 3:
 // the output layer became the bottleneck", the sketch head's three steps).
 //
-// Per token:
-//  1. k_sketch_rank (many workgroups) ranks the hidden dimensions by |x|
-//     (descending, ties to the lower index) by counting larger keys; then
-//     k_sketch_plan (one workgroup) takes the first T = min(32, k) as the
-//     exactly scored ones and cuts the rest into 4 consecutive rank groups,
-//     each weighted by c * mean |x| (c = mean |w| of the table, computed when
-//     the sketch is built).  Group bit masks and the sign bits of x go to the
-//     workspace; the candidate histograms are cleared.
-//  2. k_sketch_score (a thread per row): a = 0; a = fma(w[r][d_j], x[d_j], a)
-//     over the exact dimensions in rank order, read from a dimension-major
-//     copy of the table; then per group a = fma(weight_g, agreement_g, a),
-//     the agreement = n_g - 2 * popcount((signs of w ^ signs of x) & mask_g)
-//     from the 1-bit table (one XOR, then AND + bit count per group, 32
-//     dimensions per word).  The fp32 score's order key goes to the
-//     workspace and into a histogram of its top 12 bits.
-//  3. k_sketch_select finds the lowest bin b* such that the bins from b* up
-//     hold at least min(1024, v) words; the words in those bins are the
-//     candidates.  k_sketch_rescore scores each candidate exactly (a wave per
-//     candidate, fp32 like k_lmhead) and keeps each workgroup's best (logit,
-//     lowest index); k_sketch_final takes the first maximum over them.
-// The score arithmetic is fixed (fp32 FMAs in the order above), so the
-// candidate set is exactly the one the oracle computes.
+// Per token, two launches:
+//  1. k_sketch_score, a workgroup per 1024 rows (two per lane).  Each
+//     workgroup reads x, asks for its rows' sign words (they do not depend on
+//     the token's plan) and makes the plan itself in LDS while they are in
+//     flight: the T = min(32, k) dimensions with the largest |x| (ties to the
+//     lower index) are scored exactly, the other k - T form 4 consecutive rank
+//     groups, each weighted by c * mean |x| of the group (c = mean |w| of the
+//     table, computed when the sketch is built).  Ranks are never sorted out:
+//     the order key at each of the 4 group boundaries is selected by a shared
+//     histogram of the top 11 bits of |x|, then (for a bin of more than 64
+//     dimensions) further 10-bit digits, and the at most 64 dimensions left in
+//     the boundary's bin are ranked against each other (by |x|, then index);
+//     a dimension's class is then three compares.  The approximate score of a
+//     row is the exact products over the T dimensions (from the
+//     dimension-major copy of the table) plus, per group, weight * (n_g - 2 *
+//     popcount((signs of w ^ signs of x) & mask_g)) from the 1-bit table.
+//     Each row's fp32 score order key goes to the workspace and into a
+//     histogram of its top 13 bits; the 256 bins below the workgroup's highest
+//     non-empty one are added into one of 8 device copies.
+//  2. k_sketch_pick, a workgroup per 1024 rows (one per lane).  Every
+//     workgroup finds the cut b*, the highest bin at which the bins from the
+//     top down hold min(1024, v) words, among the 256 bins below the highest
+//     non-empty one (every workgroup of launch 1 added all of those); if they
+//     hold fewer, every word is a candidate.  It scores its own candidates
+//     exactly (a wave per word, fp32 like k_lmhead) and leaves its best (logit
+//     key, lowest row) and count in its slot; the last workgroup out (counted
+//     in 8 groups, then over the groups) takes the first maximum over the
+//     slots and writes the choice.
+// Every workgroup makes the same plan from the same x in the same order, so
+// the scores of one token are consistent over workgroups and calls.
+//
+// The workspace carries the state between launches and tokens: zero-filled
+// before its first use, each token leaves it ready for the next (the score
+// launch clears the pick's counters, the pick launch clears the histogram set
+// the next token will use; the two sets alternate on a parity word).  Values
+// shared between workgroups of one launch go through device-scope atomics:
+// the compute dies' L2 caches are not coherent with each other for plain
+// accesses.  Atomics on one address are few (at most a group's workgroups),
+// since the memory side serialises them.
 #include "qmv_internal.hpp"
 
 namespace qmv {
 namespace {
 
-constexpr int kSkTop = 32;         // exactly scored dimensions
-constexpr int kSkGroups = 4;       // sign-bit groups
-constexpr int kSkMinCand = 1024;   // candidates: at least this many words (or all of them)
-constexpr int kSkBins = 4096;      // histogram over the top 12 bits of the order key
-constexpr int kSkRowBlock = 512;   // rows per fp64 partial of the table scale
-constexpr int kSkPlanThreads = 1024;
-constexpr int kSkRowsPerBlock = 1024;   // score / rescore: rows per workgroup (4 per thread)
-constexpr uint32_t kSkMagic = 0x31484b53u;   // "SKH1"
+constexpr int kSkTop = 32;            // exactly scored dimensions
+constexpr int kSkGroups = 4;          // sign-bit groups
+constexpr int kSkMinCand = 1024;      // candidates: at least this many words (or all of them)
+constexpr int kSkBinBits = 13;        // histogram over the top 13 bits of the score's order key
+constexpr int kSkBins = 1 << kSkBinBits;
+constexpr int kSkWindow = 256;        // bins searched below the highest non-empty one
+constexpr int kSkCopies = 8;          // device histograms: score workgroup b adds into copy b % 8
+constexpr int kSkSets = 8;            // max-bin words and exit counters: workgroup b in set b % 8
+constexpr int kSkRowBlock = 512;      // build: rows per fp64 partial of the table scale
+constexpr int kSkRows = 1024;         // rows per workgroup in both per-token launches (the table pitch)
+constexpr int kSkScoreThreads = 512;  // score: two rows per lane
+constexpr int kSkScoreWaves = kSkScoreThreads / kWave;
+constexpr int kSkPickThreads = 1024;  // pick: one row per lane
+constexpr int kSkWords = kSketchMaxK / 32;
+constexpr int kSkChunks = kSketchMaxK / 64;
+constexpr int kSkList = 64;           // dimensions of a boundary's bin ranked against each other
+constexpr int kSkPre = 36;            // sign words per lane asked for before the plan (all of them for k <= 1152)
+constexpr int kSkBatch = 12;          // sign words per batch after those
+constexpr int kSkXLoads = kSketchMaxK / (4 * kSkScoreThreads);   // 16-byte loads of x per lane
+constexpr uint32_t kSkMagic = 0x32484b53u;   // "SKH2"
 
-// Sketch buffer: header, sign words [kw][v], dimension-major bf16 copy [k][v].
+typedef uint32_t sk_u32x2 __attribute__((ext_vector_type(2)));
+
+// Sketch buffer: header, sign words [kw][vp], dimension-major bf16 copy [k][vp],
+// vp = v rounded up to a multiple of kSkRows (rows v..vp-1 hold zeros).
 struct SketchHeader {
     uint32_t magic;
     int32_t k;
@@ -48,28 +80,21 @@ struct SketchHeader {
 };
 static_assert(sizeof(SketchHeader) == 64, "sketch header");
 
-// Workspace: the plan, the histogram, the pick, then the order keys [v].
-struct SketchPlan {
-    int32_t t;               // exact dimensions
-    int32_t kw;              // 32-dimension words
-    int32_t n[kSkGroups];    // group sizes
-    float wgt[kSkGroups];    // group weights
-    int32_t pad[6];
-    int32_t top_idx[kSkTop];
-    float top_x[kSkTop];
-    // then masks [kSkGroups][kw] and the sign words of x [kw]
-};
-static_assert(sizeof(SketchPlan) == 320, "sketch plan");
-constexpr int kSkHistCopies = 8;        // private histograms (workgroup b adds into copy b % 8)
-constexpr int kSkScoreThreads = 1024;   // score: a thread per row
-constexpr int64_t kSkPlanBytes = 8192;
-constexpr int64_t kSkHistOff = kSkPlanBytes;
-constexpr int64_t kSkPickOff = kSkHistOff + kSkHistCopies * kSkBins * 4;   // u32 b*
-constexpr int64_t kSkWgOff = kSkPickOff + 256;   // per rescore workgroup: u64 best, then u32 counts
-constexpr int64_t kSkMaxWg = (((int64_t)1 << 24) + kSkRowsPerBlock - 1) / kSkRowsPerBlock;
-constexpr int64_t kSkKeysOff = kSkWgOff + 12 * kSkMaxWg;
+// Workspace: control words, two histogram sets, a slot per pick workgroup, the
+// row keys [vp].  Each control word has a 64-byte line of its own.
+constexpr int kCtlParity = 0;                    // histogram set of the next token
+constexpr int kCtlMaxBin = 16;                   // [kSkSets]: highest non-empty bin (score; reset by pick)
+constexpr int kCtlOut = 16 * (1 + kSkSets);      // [kSkSets]: pick workgroups out; then [kSkSets]: sets out
+constexpr int kCtlOutAll = kCtlOut + 16 * kSkSets;
+constexpr int64_t kSkCtlBytes = 2048;
+static_assert(4 * (kCtlOutAll + 16) <= kSkCtlBytes, "sketch control words");
+constexpr int64_t kSkHistOff = kSkCtlBytes;
+constexpr int64_t kSkHistSet = (int64_t)kSkCopies * kSkBins;   // words per set
+constexpr int64_t kSkSlotOff = kSkHistOff + 2 * 4 * kSkHistSet;   // 16 bytes per pick workgroup
 
 constexpr int64_t sk_round(int64_t n, int64_t a) { return (n + a - 1) / a * a; }
+constexpr int64_t sk_pitch(int64_t v) { return sk_round(v, kSkRows); }
+constexpr int64_t sk_keys_off(int64_t vp) { return kSkSlotOff + sk_round(16 * (vp / kSkRows), 256); }
 
 __device__ __forceinline__ uint32_t order_key(float f)
 {
@@ -82,17 +107,20 @@ __device__ __forceinline__ float key_value(uint32_t key)
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
-
 // ---- build --------------------------------------------------------------------------------
 
-// A thread per row: the sign words (word w of row r at w * v + r) and the
-// row's sum of |w| in fp32, column order (into `rowsum`).
-__global__ __launch_bounds__(kBlock) void k_sketch_rows(const uint16_t* __restrict__ w, int64_t v, int k,
+// A thread per row of the padded table: the sign words (word w of row r at
+// w * vp + r) and the row's sum of |w| in fp32, column order (into `rowsum`);
+// padding rows get zero words.
+__global__ __launch_bounds__(kBlock) void k_sketch_rows(const uint16_t* __restrict__ w, int64_t v, int64_t vp, int k,
                                                         uint32_t* __restrict__ signs, float* __restrict__ rowsum)
 {
     const int64_t r = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (r >= v) return;
+    if (r >= vp) return;
+    if (r >= v) {
+        for (int wd = 0; wd < (k + 31) / 32; ++wd) signs[(int64_t)wd * vp + r] = 0u;
+        return;
+    }
     const uint4* row = reinterpret_cast<const uint4*>(w + r * k);
     float sum = 0.0f;
     uint32_t word = 0;
@@ -110,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void k_sketch_rows(const uint16_t* __restri
             }
         }
         if ((c8 & 3) == 3 || c8 == k / 8 - 1) {
-            signs[(int64_t)(c8 >> 2) * v + r] = word;
+            signs[(int64_t)(c8 >> 2) * vp + r] = word;
             word = 0;
         }
     }
@@ -142,9 +170,9 @@ __global__ __launch_bounds__(kBlock) void k_sketch_scale(const float* __restrict
     }
 }
 
-// 64 x 64 tiles through LDS: wt[c][r] = w[r][c].
-__global__ __launch_bounds__(kBlock) void k_sketch_transpose(const uint16_t* __restrict__ w, int64_t v, int k,
-                                                             uint16_t* __restrict__ wt)
+// 64 x 64 tiles through LDS: wt[c][r] = w[r][c], zero for the padding rows.
+__global__ __launch_bounds__(kBlock) void k_sketch_transpose(const uint16_t* __restrict__ w, int64_t v, int64_t vp,
+                                                             int k, uint16_t* __restrict__ wt)
 {
     __shared__ uint16_t tile[64][66];
     const int64_t r0 = (int64_t)blockIdx.x * 64;
@@ -163,333 +191,684 @@ __global__ __launch_bounds__(kBlock) void k_sketch_transpose(const uint16_t* __r
         const int cc = ty + 4 * i;
         const int c = c0 + cc;
         const int64_t r = r0 + tx;
-        if (c < k && r < v) wt[(int64_t)c * v + r] = tile[tx][cc];
+        if (c < k && r < vp) wt[(int64_t)c * vp + r] = tile[tx][cc];
     }
 }
 
-// ---- per token ----------------------------------------------------------------------------
+// ---- per token: plan and approximate scores ------------------------------------------------
 
-// |x| order key of dimension i: |x| bits above the inverted index, so keys are
-// distinct, larger |x| ranks first and equal |x| go to the lower index.
-__device__ __forceinline__ uint64_t order_key_of(const float* x, int i)
-{
-    return ((uint64_t)__float_as_uint(fabsf(x[i])) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-}
-
-// Ranks by counting, spread over many compute units: workgroup b places keys
-// 16b .. 16b+15, each compared with every key by 16 threads (a sixteenth of the
-// keys each); the rank is the number of larger keys, and the key is written at
-// its rank, so `sorted` ends up in descending order.
-constexpr int kSkRankPer = 16;
-__global__ __launch_bounds__(kBlock) void k_sketch_rank(const float* __restrict__ x, int k,
-                                                        uint64_t* __restrict__ sorted)
-{
-    __shared__ uint64_t key[kSketchMaxK];
-    __shared__ uint32_t cnt[kSkRankPer];
-    const int tid = threadIdx.x;
-    for (int i = tid; i < k; i += kBlock) key[i] = order_key_of(x, i);
-    if (tid < kSkRankPer) cnt[tid] = 0u;
-    __syncthreads();
-    const int e = blockIdx.x * kSkRankPer + (tid % kSkRankPer);
-    const int part = tid / kSkRankPer;
-    if (e < k) {
-        const uint64_t me = key[e];
-        uint32_t c = 0;
-        for (int j = part; j < k; j += kBlock / kSkRankPer) c += key[j] > me ? 1u : 0u;
-        atomicAdd(&cnt[tid % kSkRankPer], c);
-    }
-    __syncthreads();
-    if (tid < kSkRankPer && e < k) sorted[cnt[tid]] = key[e];
-}
-
-// One workgroup of 1024 threads; dynamic LDS: the k order keys in descending
-// order (from k_sketch_rank) then the masks and x sign words (5 * kw words).
-__global__ __launch_bounds__(kSkPlanThreads) void k_sketch_plan(const float* __restrict__ x, int k,
-                                                                const uint64_t* __restrict__ sorted,
-                                                                const SketchHeader* __restrict__ hdr,
-                                                                uint8_t* __restrict__ ws)
-{
-    extern __shared__ __align__(16) uint8_t sm[];
-    uint64_t* key = reinterpret_cast<uint64_t*>(sm);
-    const int kw = (k + 31) >> 5;
-    uint32_t* mbits = reinterpret_cast<uint32_t*>(sm + 8 * (size_t)k);   // [5][kw]: masks, then x signs
-    const int tid = threadIdx.x;
-    for (int i = tid; i < k; i += kSkPlanThreads) key[i] = sorted[i];
-    for (int i = tid; i < 5 * kw; i += kSkPlanThreads) mbits[i] = 0u;
-    __syncthreads();
-    SketchPlan* plan = reinterpret_cast<SketchPlan*>(ws);
-    const int t = min(k, kSkTop);
-    const int rest = k - t, base = rest / kSkGroups;
-    auto dim_of = [&](int rank) { return (int)(0xFFFFFFFFu - (uint32_t)(key[rank] & 0xFFFFFFFFu)); };
-    auto group_of_rank = [&](int rank) { return base > 0 ? min((rank - t) / base, kSkGroups - 1) : kSkGroups - 1; };
-    if (tid < t) {
-        const int d = dim_of(tid);
-        plan->top_idx[tid] = d;
-        plan->top_x[tid] = x[d];
-    }
-    for (int rank = t + tid; rank < k; rank += kSkPlanThreads) {
-        const int d = dim_of(rank);
-        atomicOr(&mbits[group_of_rank(rank) * kw + (d >> 5)], 1u << (d & 31));
-    }
-    for (int i = tid; i < k; i += kSkPlanThreads)
-        if (x[i] < 0.0f) atomicOr(&mbits[kSkGroups * kw + (i >> 5)], 1u << (i & 31));
-    if (tid < kSkGroups) {
-        // group sums of |x| in rank order, fp32; |x| is the high word of the sorted key
-        const int lo = t + tid * base;
-        const int hi = tid == kSkGroups - 1 ? k : lo + base;
-        float sum = 0.0f;
-        int rank = lo;
-        for (; rank + 8 <= hi; rank += 8) {
-            float v8[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v8[j] = __uint_as_float((uint32_t)(key[rank + j] >> 32));
-#pragma unroll
-            for (int j = 0; j < 8; ++j) sum += v8[j];
-        }
-        for (; rank < hi; ++rank) sum += __uint_as_float((uint32_t)(key[rank] >> 32));
-        const float mean = hi > lo ? sum / (float)(hi - lo) : 0.0f;
-        plan->n[tid] = hi - lo;
-        plan->wgt[tid] = hdr->c * mean;
-    }
-    if (tid == 0) {
-        plan->t = t;
-        plan->kw = kw;
-    }
-    // clear the histograms for this token
-    uint4* hist4 = reinterpret_cast<uint4*>(ws + kSkHistOff);
-    for (int i = tid; i < kSkHistCopies * kSkBins / 4; i += kSkPlanThreads) hist4[i] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
-    uint32_t* mout = reinterpret_cast<uint32_t*>(ws + sizeof(SketchPlan));
-    for (int i = tid; i < 5 * kw; i += kSkPlanThreads) mout[i] = mbits[i];
-}
-
-// A thread per row, 1024 rows per workgroup; the workgroup's histogram is
-// added into private copy blockIdx % 8 (a hot bin then takes few atomics).
-__global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t* __restrict__ signs,
-                                                                  const uint16_t* __restrict__ wt, int64_t v,
-                                                                  uint8_t* __restrict__ ws, float* __restrict__ scores)
-{
-    __shared__ uint32_t sbits[5 * 256];
-    __shared__ uint32_t shist[kSkBins];
-    __shared__ int32_t s_idx[kSkTop];
-    __shared__ float s_x[kSkTop];
-    const SketchPlan* plan = reinterpret_cast<const SketchPlan*>(ws);
-    const int tid = threadIdx.x;
-    const int t = plan->t, kw = plan->kw;
-    const uint32_t* mbits = reinterpret_cast<const uint32_t*>(ws + sizeof(SketchPlan));
-    for (int i = tid; i < 5 * kw; i += kSkScoreThreads) sbits[i] = mbits[i];
-    for (int i = tid; i < kSkBins; i += kSkScoreThreads) shist[i] = 0u;
-    if (tid < kSkTop) {
-        s_idx[tid] = plan->top_idx[tid];
-        s_x[tid] = plan->top_x[tid];
-    }
+struct ScoreLds {
+    uint32_t xb[kSketchMaxK];                    // x's bit patterns
+    alignas(16) uint32_t rh0[2048];                          // top 11 bits of |x|, shared by the boundaries
+    alignas(16) uint32_t rh[kSkGroups][1024];                // further 10-bit digits, one histogram per boundary
+    uint64_t lst[kSkGroups][kSkList];            // order keys of the dimensions in a boundary's bin
+    alignas(16) uint32_t word[6][kSkWords + kSkBatch];       // masks: [0] exact, [1..4] groups, [5] signs of x
+    uint32_t tcnt[kSkChunks], tpre[kSkChunks];   // exact dimensions per 64 and their prefix
+    float gpart[kSkScoreWaves][kSkGroups];       // the groups' sums of |x| per wave
+    uint64_t kb[kSkGroups];                      // order key at each boundary rank (0: none)
+    uint32_t pre[kSkGroups], res[kSkGroups], cnt[kSkGroups], sh[kSkGroups], lcnt[kSkGroups];
+    int32_t top_idx[kSkTop];
+    float top_x[kSkTop];
     float wgt[kSkGroups];
     int32_t ng[kSkGroups];
-#pragma unroll
-    for (int g = 0; g < kSkGroups; ++g) {
-        wgt[g] = plan->wgt[g];
-        ng[g] = plan->n[g];
-    }
-    __syncthreads();
-    const int64_t r = (int64_t)blockIdx.x * kSkScoreThreads + tid;
-    const bool live = r < v;
-    const int64_t rr = live ? r : v - 1;   // a valid address for every lane; only live rows count
-    // step 1: the exact dimensions, in rank order (loads batched, FMAs in order)
-    float a = 0.0f;
-    int j = 0;
-    for (; j + 8 <= t; j += 8) {
-        uint16_t h[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) h[u] = __builtin_nontemporal_load(&wt[(int64_t)s_idx[j + u] * v + rr]);   // read once per token
-#pragma unroll
-        for (int u = 0; u < 8; ++u) a = fmaf(bf16f(h[u]), s_x[j + u], a);
-    }
-    for (; j < t; ++j) a = fmaf(bf16f(wt[(int64_t)s_idx[j] * v + rr]), s_x[j], a);
-    // step 2: sign agreement per group
-    int cnt[kSkGroups] = {0, 0, 0, 0};
-    int w = 0;
-    for (; w + 6 <= kw; w += 6) {
-        uint32_t sw6[6];
-#pragma unroll
-        for (int u = 0; u < 6; ++u) sw6[u] = __builtin_nontemporal_load(&signs[(int64_t)(w + u) * v + rr]);
-#pragma unroll
-        for (int u = 0; u < 6; ++u) {
-            const uint32_t d = sw6[u] ^ sbits[kSkGroups * kw + w + u];
-#pragma unroll
-            for (int g = 0; g < kSkGroups; ++g) cnt[g] += __popc(d & sbits[g * kw + w + u]);
-        }
-    }
-    for (; w < kw; ++w) {
-        const uint32_t d = signs[(int64_t)w * v + rr] ^ sbits[kSkGroups * kw + w];
-#pragma unroll
-        for (int g = 0; g < kSkGroups; ++g) cnt[g] += __popc(d & sbits[g * kw + w]);
-    }
-#pragma unroll
-    for (int g = 0; g < kSkGroups; ++g) a = fmaf(wgt[g], (float)(ng[g] - 2 * cnt[g]), a);
-    const uint32_t key = order_key(a);
-    if (live) {
-        reinterpret_cast<uint32_t*>(ws + kSkKeysOff)[r] = key;
-        if (scores) scores[r] = a;
-        atomicAdd(&shist[key >> 20], 1u);
-    }
-    __syncthreads();
-    uint32_t* hist = reinterpret_cast<uint32_t*>(ws + kSkHistOff) + (blockIdx.x % kSkHistCopies) * kSkBins;
-    for (int i = tid; i < kSkBins; i += kSkScoreThreads)
-        if (shist[i]) atomicAdd(&hist[i], shist[i]);
+    uint32_t wmax[kSkScoreWaves];
+    alignas(16) uint32_t hist[kSkBins];
+};
+
+// Lane l + the lanes up to l - 1, 2, 4, 8 back within its row of 16 (DPP row shifts; a lane
+// past the row's start adds 0): an inclusive prefix within each row.
+__device__ __forceinline__ uint32_t row_scan_u32(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);   // row_shr:8
+    return v;
 }
 
-// One workgroup of 1024 threads: b*, the highest bin at which the bins from
-// the top down first hold min(1024, v) words.  Thread t owns bins
-// 4095 - 4t - 3 .. 4095 - 4t.
-__global__ __launch_bounds__(kSkPlanThreads) void k_sketch_select(int64_t v, uint8_t* __restrict__ ws)
+__device__ __forceinline__ float row_scan_f(float a)
 {
-    __shared__ uint32_t ssum[kSkPlanThreads];
-    const int tid = threadIdx.x;
-    const uint32_t* hist = reinterpret_cast<const uint32_t*>(ws + kSkHistOff);
-    const int hi_bin = kSkBins - 1 - 4 * tid;
-    uint32_t hv[4] = {0, 0, 0, 0};
+    a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x111, 0xf, 0xf, false));
+    a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x112, 0xf, 0xf, false));
+    a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x114, 0xf, 0xf, false));
+    a += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x118, 0xf, 0xf, false));
+    return a;
+}
+
+// Sum over the wave in a fixed order (each row's prefix tree, then the four rows in order),
+// the same in every lane.
+__device__ __forceinline__ float wave_sum_f(float a)
+{
+    a = row_scan_f(a);
+    return ((__int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 15)) +
+             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 31))) +
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 47))) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 63));
+}
+
+// Maximum over the wave (every lane gets it): DPP row shifts (a lane past the row's
+// start takes 0), then the four rows' last lanes.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)v, 15), (uint32_t)__builtin_amdgcn_readlane((int)v, 31)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)v, 47), (uint32_t)__builtin_amdgcn_readlane((int)v, 63)));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
 #pragma unroll
-    for (int c = 0; c < kSkHistCopies; ++c)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) hv[u] += hist[c * kSkBins + hi_bin - u];
-    // inclusive scan over the threads: inside each wave by shuffles, then the
-    // wave totals (16 of them) in order
-    __shared__ uint32_t wtot[kSkPlanThreads / kWave];
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    uint32_t x = hv[0] + hv[1] + hv[2] + hv[3];
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
+    for (int step = 0; step < 4; ++step) {
+        uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32), slo, shi;
+        switch (step) {   // row_shr:1, 2, 4, 8
+        case 0:
+            slo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0x111, 0xf, 0xf, false);
+            shi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x111, 0xf, 0xf, false);
+            break;
+        case 1:
+            slo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0x112, 0xf, 0xf, false);
+            shi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x112, 0xf, 0xf, false);
+            break;
+        case 2:
+            slo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0x114, 0xf, 0xf, false);
+            shi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x114, 0xf, 0xf, false);
+            break;
+        default:
+            slo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0x118, 0xf, 0xf, false);
+            shi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x118, 0xf, 0xf, false);
+            break;
+        }
+        const uint64_t o = ((uint64_t)shi << 32) | slo;
+        v = o > v ? o : v;
     }
-    if (lane == kWave - 1) wtot[wave] = x;
-    __syncthreads();
-    uint32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += wtot[w];
-    ssum[tid] = x + base;
-    __syncthreads();
-    const uint32_t need = (uint32_t)min<int64_t>(v, kSkMinCand);
-    const uint32_t before = tid ? ssum[tid - 1] : 0u;
-    if (before < need && ssum[tid] >= need) {
-        uint32_t run = before;
-        for (int u = 0; u < 4; ++u) {
-            run += hv[u];
-            if (run >= need) {
-                reinterpret_cast<uint32_t*>(ws + kSkPickOff)[0] = (uint32_t)(hi_bin - u);
-                break;
+    uint64_t m = 0ull;
+#pragma unroll
+    for (int r = 15; r < kWave; r += 16) {
+        const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, r);
+        m = o > m ? o : m;
+    }
+    return m;
+}
+
+// Inclusive prefix sum over the wave's lanes.
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v, int lane)
+{
+    v = row_scan_u32(v);
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const int row = lane >> 4;
+    return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask)
+{
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// |x| order key of dimension d: |x| bits above the inverted index, so keys are
+// distinct, larger |x| ranks first and equal |x| go to the lower index.
+__device__ __forceinline__ uint64_t dim_key(uint32_t ubits, int d)
+{
+    return ((uint64_t)ubits << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)d);
+}
+
+// Rank of the first dimension of group b (b = 0: of the first non-exact one).
+__device__ __forceinline__ int boundary_rank(int b, int t, int base)
+{
+    return b == 0 || base == 0 ? t : t + b * base;
+}
+
+// One wave: in the histogram h of 64 * PER bins, the bin D holding rank r
+// counted from the top bin down, r's rank within D and D's count (in every
+// lane).  Lane l sums bins 64 PER - 1 - PER l down to 64 PER - PER (l + 1).
+template <int PER>
+__device__ __forceinline__ void find_digit(const uint32_t* h, uint32_t r, int lane, uint32_t& digit, uint32_t& rin,
+                                           uint32_t& cnt)
+{
+    constexpr int kNb = kWave * PER;
+    const int lo = kNb - PER * (lane + 1);
+    uint32_t q[PER];
+#pragma unroll
+    for (int j = 0; j < PER; j += 4) {
+        const uint4 v4 = *reinterpret_cast<const uint4*>(h + lo + j);
+        q[j] = v4.x;
+        q[j + 1] = v4.y;
+        q[j + 2] = v4.z;
+        q[j + 3] = v4.w;
+    }
+    uint32_t sum = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) sum += q[j];
+    const uint32_t incl = wave_scan_incl(sum, lane);
+    const uint32_t excl = incl - sum;
+    const bool mine = excl <= r && r < incl;
+    uint32_t dg = 0u, ri = 0u, c = 0u, run = excl;
+    bool done = false;
+#pragma unroll
+    for (int j = PER - 1; j >= 0; --j) {   // highest bin first, without branches
+        const bool hit = !done && r < run + q[j];
+        dg = hit ? (uint32_t)(lo + j) : dg;
+        ri = hit ? r - run : ri;
+        c = hit ? q[j] : c;
+        done = done || hit;
+        run += q[j];
+    }
+    const int src = (int)__builtin_ctzll(__ballot(mine) | (1ull << 63));
+    digit = (uint32_t)__builtin_amdgcn_readlane((int)dg, src);
+    rin = (uint32_t)__builtin_amdgcn_readlane((int)ri, src);
+    cnt = (uint32_t)__builtin_amdgcn_readlane((int)c, src);
+}
+
+__global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t* __restrict__ signs,
+                                                                  const uint16_t* __restrict__ wt,
+                                                                  const float* __restrict__ x,
+                                                                  const SketchHeader* __restrict__ hdr, int64_t v,
+                                                                  int64_t vp, int k, uint8_t* __restrict__ ws,
+                                                                  float* __restrict__ scores)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    ScoreLds& s = *reinterpret_cast<ScoreLds*>(smem);
+    uint32_t* ctlw = reinterpret_cast<uint32_t*>(ws);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const float ctab = hdr->c;
+    const uint32_t parity = ctlw[kCtlParity] & 1u;
+    const int kw = (k + 31) >> 5, k4 = k >> 2;
+    const int64_t col = ((int64_t)blockIdx.x * kSkRows >> 1) + tid;   // this lane's row pair: rows 2 col, 2 col + 1
+    const int64_t vp2 = vp >> 1;
+
+    // x first (its few loads would otherwise wait behind the sign words) ...
+    float4 xv[kSkXLoads];
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+#pragma unroll
+    for (int i = 0; i < kSkXLoads; ++i) xv[i] = x4[min(tid + kSkScoreThreads * i, k4 - 1)];
+    uint32_t ux[kSkXLoads][4];   // |x| bits of dimensions 4 q .. 4 q + 3, q = tid + 512 i (all ones: none)
+#pragma unroll
+    for (int i = 0; i < kSkXLoads; ++i) {
+        const int q = tid + kSkScoreThreads * i;
+        const uint32_t b4[4] = {__float_as_uint(xv[i].x), __float_as_uint(xv[i].y), __float_as_uint(xv[i].z),
+                                __float_as_uint(xv[i].w)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ux[i][j] = q < k4 ? (b4[j] & 0x7FFFFFFFu) : 0xFFFFFFFFu;
+        if (q < k4) reinterpret_cast<float4*>(s.xb)[q] = xv[i];
+    }
+    asm volatile("" ::: "memory");
+    // ... then the sign words, which stay in flight while the plan is made
+    const sk_u32x2* sg = reinterpret_cast<const sk_u32x2*>(signs);
+    sk_u32x2 sw[kSkPre];
+#pragma unroll
+    for (int u = 0; u < kSkPre; ++u) sw[u] = __builtin_nontemporal_load(&sg[(int64_t)min(u, kw - 1) * vp2 + col]);
+
+    // ---- the plan ----
+    for (int i = tid; i < 6 * (kSkWords + kSkBatch) / 4; i += kSkScoreThreads)
+        reinterpret_cast<uint4*>(&s.word[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < kSkBins / 4; i += kSkScoreThreads)
+        reinterpret_cast<uint4*>(s.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < 2048 / 4; i += kSkScoreThreads)
+        reinterpret_cast<uint4*>(s.rh0)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < kSkGroups * 1024 / 4; i += kSkScoreThreads)
+        reinterpret_cast<uint4*>(&s.rh[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    const int t = min(k, kSkTop), rest = k - t, base = rest / kSkGroups;
+    bool act[kSkGroups];
+#pragma unroll
+    for (int b = 0; b < kSkGroups; ++b) act[b] = boundary_rank(b, t, base) < k;
+    if (tid < kSkGroups) s.lcnt[tid] = 0u;
+    const int nq = (k4 + kSkScoreThreads - 1) / kSkScoreThreads;
+    lds_barrier();
+    // the boundaries' bins of the top 11 bits of |x|
+#pragma unroll
+    for (int i = 0; i < kSkXLoads; ++i) {
+        if (i >= nq) break;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (ux[i][j] != 0xFFFFFFFFu) atomicAdd(&s.rh0[ux[i][j] >> 20], 1u);
+    }
+    lds_barrier();
+    if (wave < kSkGroups && act[wave]) {
+        uint32_t dg, rin, c;
+        find_digit<32>(s.rh0, (uint32_t)boundary_rank(wave, t, base), lane, dg, rin, c);
+        if (lane == 0) {
+            s.pre[wave] = dg;
+            s.res[wave] = rin;
+            s.cnt[wave] = c;
+            s.sh[wave] = 20u;
+        }
+    }
+    lds_barrier();
+    // a bin of more than kSkList dimensions: the next 10 bits (then the last 10)
+#pragma unroll
+    for (int p = 1; p <= 2; ++p) {
+        const int sh = 20 - 10 * p;
+        bool more[kSkGroups];
+        bool any_more = false;
+        uint32_t pre[kSkGroups];
+#pragma unroll
+        for (int b = 0; b < kSkGroups; ++b) {
+            more[b] = act[b] && s.cnt[b] > (uint32_t)kSkList;
+            any_more = any_more || more[b];
+            pre[b] = s.pre[b];
+        }
+        if (!any_more) break;
+#pragma unroll
+        for (int i = 0; i < kSkXLoads; ++i) {
+            if (i >= nq) break;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t u = ux[i][j];
+#pragma unroll
+                for (int b = 0; b < kSkGroups; ++b)
+                    if (more[b] && (u >> (sh + 10)) == pre[b]) atomicAdd(&s.rh[b][(u >> sh) & 1023u], 1u);
             }
         }
+        lds_barrier();
+        if (wave < kSkGroups && more[wave]) {
+            uint32_t dg, rin, c;
+            find_digit<16>(s.rh[wave], s.res[wave], lane, dg, rin, c);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) s.rh[wave][16 * lane + j] = 0u;   // only this wave reads it
+            if (lane == 0) {
+                s.pre[wave] = (pre[wave] << 10) | dg;
+                s.res[wave] = rin;
+                s.cnt[wave] = c;
+                s.sh[wave] = (uint32_t)sh;
+            }
+        }
+        lds_barrier();
     }
-}
-
-// 256 threads, 1024 rows per workgroup.  Dynamic LDS: x (k floats).  Each
-// workgroup writes its best (logit key << 32 | ~row) and its candidate count.
-__global__ __launch_bounds__(kBlock) void k_sketch_rescore(const uint16_t* __restrict__ w, const float* __restrict__ x,
-                                                           int64_t v, int k, uint8_t* __restrict__ ws)
-{
-    extern __shared__ __align__(16) float xs[];
-    __shared__ int32_t s_n;
-    __shared__ int32_t s_list[kSkRowsPerBlock];
-    __shared__ unsigned long long s_best[kBlock / kWave];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    const uint32_t bstar = reinterpret_cast<const uint32_t*>(ws + kSkPickOff)[0];
-    if (tid == 0) s_n = 0;
-    if (lane == 0) s_best[wave] = 0ull;
-    __syncthreads();
-    // this workgroup's candidates
-    const uint32_t* keys = reinterpret_cast<const uint32_t*>(ws + kSkKeysOff);
-    const int64_t base = (int64_t)blockIdx.x * kSkRowsPerBlock;
-    uint32_t kv4[kSkRowsPerBlock / kBlock];
+    // the dimensions left in each boundary's bin
+    {
+        bool in_list[kSkGroups];
+        uint32_t pre[kSkGroups], shb[kSkGroups];
 #pragma unroll
-    for (int i = 0; i < kSkRowsPerBlock / kBlock; ++i) {
-        const int64_t r = base + tid + kBlock * i;
-        kv4[i] = r < v ? keys[r] : 0u;
-    }
+        for (int b = 0; b < kSkGroups; ++b) {
+            in_list[b] = act[b] && s.cnt[b] <= (uint32_t)kSkList;
+            pre[b] = s.pre[b];
+            shb[b] = s.sh[b];
+        }
 #pragma unroll
-    for (int i = 0; i < kSkRowsPerBlock / kBlock; ++i) {
-        const int64_t r = base + tid + kBlock * i;
-        if (r < v && (kv4[i] >> 20) >= bstar) s_list[atomicAdd(&s_n, 1)] = (int32_t)r;
-    }
-    __syncthreads();
-    const int n = s_n;
-    if (n) {
-        for (int i = tid; i < k; i += kBlock) xs[i] = x[i];
-        __syncthreads();
-        // exact logits: one wave per candidate, 16-byte chunks over the lanes, a
-        // row's loads issued together
-        const int nch = k / 8;
-        unsigned long long mine = 0ull;
-        for (int c = wave; c < n; c += kBlock / kWave) {
-            const int64_t r = s_list[c];
-            const uint4* row = reinterpret_cast<const uint4*>(w + r * k);
-            float s = 0.0f;
-            for (int ch0 = lane; ch0 < nch; ch0 += 4 * kWave) {
-                uint4 q[4];
+        for (int i = 0; i < kSkXLoads; ++i) {
+            if (i >= nq) break;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) q[u] = ch0 + u * kWave < nch ? row[ch0 + u * kWave] : make_uint4(0, 0, 0, 0);
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t u = ux[i][j];
+                const int d = 4 * (tid + kSkScoreThreads * i) + j;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int ch = ch0 + u * kWave;
-                    if (ch >= nch) break;
-                    const float* xc = xs + 8 * ch;
-                    s = fmaf(__uint_as_float(q[u].x << 16), xc[0], s);
-                    s = fmaf(__uint_as_float(q[u].x & 0xFFFF0000u), xc[1], s);
-                    s = fmaf(__uint_as_float(q[u].y << 16), xc[2], s);
-                    s = fmaf(__uint_as_float(q[u].y & 0xFFFF0000u), xc[3], s);
-                    s = fmaf(__uint_as_float(q[u].z << 16), xc[4], s);
-                    s = fmaf(__uint_as_float(q[u].z & 0xFFFF0000u), xc[5], s);
-                    s = fmaf(__uint_as_float(q[u].w << 16), xc[6], s);
-                    s = fmaf(__uint_as_float(q[u].w & 0xFFFF0000u), xc[7], s);
+                for (int b = 0; b < kSkGroups; ++b) {
+                    if (in_list[b] && (u >> shb[b]) == pre[b]) {
+                        const uint32_t slot = atomicAdd(&s.lcnt[b], 1u);
+                        if (slot < (uint32_t)kSkList) s.lst[b][slot] = dim_key(u, d);
+                    }
                 }
             }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
-            const unsigned long long kv =
-                ((unsigned long long)order_key(s) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)r);
-            mine = kv > mine ? kv : mine;
         }
-        if (lane == 0) s_best[wave] = mine;
     }
+    lds_barrier();
+    const int nch = (k + 63) >> 6;
+    if (wave < kSkGroups) {
+        const int b = wave;
+        if (!act[b]) {
+            if (lane == 0) s.kb[b] = 0ull;   // no such rank: every key is above
+        } else if (s.cnt[b] <= (uint32_t)kSkList) {
+            // rank the bin's dimensions against each other
+            const uint32_t c = s.cnt[b], r = s.res[b];
+            const uint64_t my = lane < (int)c ? s.lst[b][lane] : 0ull;
+            uint32_t above = 0u;
+            for (uint32_t j = 0; j < c; j += 8) {   // entries past c are ignored below
+                uint64_t e[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) e[u] = s.lst[b][(j + u) & (kSkList - 1)];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) above += (j + u < c && e[u] > my) ? 1u : 0u;
+            }
+            if (lane < (int)c && above == r) s.kb[b] = my;
+        } else {
+            // more than kSkList dimensions with exactly the boundary's |x|: by index
+            const uint32_t ub = s.pre[b];
+            uint32_t r = s.res[b];
+            for (int c = 0; c < nch; ++c) {
+                const int d = 64 * c + lane;
+                const bool m = d < k && (s.xb[min(d, k - 1)] & 0x7FFFFFFFu) == ub;
+                const uint64_t mask = __ballot(m);
+                const uint32_t n = (uint32_t)__popcll(mask);
+                if (r < n) {
+                    if (m && lanes_below(mask) == r) s.kb[b] = dim_key(ub, d);
+                    break;
+                }
+                r -= n;
+            }
+        }
+    }
+    lds_barrier();
+    // classes, 64 dimensions per wave step: mask words, exact dimensions per step, group sums of |x|
+    const uint64_t k0 = s.kb[0], k1 = s.kb[1], k2 = s.kb[2], k3 = s.kb[3];
+    {
+        float gp[kSkGroups] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int c = wave; c < nch; c += kSkScoreWaves) {
+            const int d = 64 * c + lane;
+            const bool valid = d < k;
+            const uint32_t xbits = valid ? s.xb[d] : 0u;
+            const uint64_t key = dim_key(xbits & 0x7FFFFFFFu, d);
+            const bool top = valid && key > k0;
+            const bool rst = valid && !top;
+            const int g = (key <= k1 ? 1 : 0) + (key <= k2 ? 1 : 0) + (key <= k3 ? 1 : 0);
+            const float ax = __uint_as_float(xbits & 0x7FFFFFFFu);
+            uint64_t m[6];
+            m[0] = __ballot(top);
+#pragma unroll
+            for (int gi = 0; gi < kSkGroups; ++gi) {
+                m[1 + gi] = __ballot(rst && g == gi);
+                gp[gi] += rst && g == gi ? ax : 0.0f;
+            }
+            m[5] = __ballot(valid && __uint_as_float(xbits) < 0.0f);
+            if (lane == 0) {
+#pragma unroll
+                for (int q = 0; q < 6; ++q) {
+                    s.word[q][2 * c] = (uint32_t)m[q];
+                    s.word[q][2 * c + 1] = (uint32_t)(m[q] >> 32);
+                }
+                s.tcnt[c] = (uint32_t)__popcll(m[0]);
+            }
+        }
+#pragma unroll
+        for (int gi = 0; gi < kSkGroups; ++gi) {
+            const float a = wave_sum_f(gp[gi]);
+            if (lane == 0) s.gpart[wave][gi] = a;
+        }
+    }
+    lds_barrier();
+    if (wave == 0) {   // where each step's exact dimensions go in the list (index order)
+        const uint32_t a = 2 * lane < nch ? s.tcnt[2 * lane] : 0u;
+        const uint32_t b = 2 * lane + 1 < nch ? s.tcnt[2 * lane + 1] : 0u;
+        const uint32_t excl = wave_scan_incl(a + b, lane) - (a + b);
+        if (2 * lane < nch) s.tpre[2 * lane] = excl;
+        if (2 * lane + 1 < nch) s.tpre[2 * lane + 1] = excl + a;
+    }
+    if (tid >= kWave && tid < kWave + kSkGroups) {   // group weights
+        const int g = tid - kWave;
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kSkScoreWaves; ++w) sum += s.gpart[w][g];
+        const int n = g < kSkGroups - 1 ? base : rest - (kSkGroups - 1) * base;
+        s.ng[g] = n;
+        s.wgt[g] = n > 0 ? ctab * (sum / (float)n) : 0.0f;
+    }
+    lds_barrier();
+    for (int c = wave; c < nch; c += kSkScoreWaves) {
+        const int d = 64 * c + lane;
+        const bool valid = d < k;
+        const uint32_t xbits = valid ? s.xb[d] : 0u;
+        const bool top = valid && dim_key(xbits & 0x7FFFFFFFu, d) > k0;
+        const uint64_t mt = __ballot(top);
+        const uint32_t pos = s.tpre[c] + lanes_below(mt);
+        if (top && pos < (uint32_t)kSkTop) {
+            s.top_idx[pos] = d;
+            s.top_x[pos] = __uint_as_float(xbits);
+        }
+    }
+    lds_barrier();
+
+    // ---- scores of rows 2 col and 2 col + 1 ----
+    const uint32_t* wt2 = reinterpret_cast<const uint32_t*>(wt);
+    uint32_t hx[kSkTop];
+#pragma unroll
+    for (int j = 0; j < kSkTop; ++j) {
+        const uint32_t d = min((uint32_t)s.top_idx[min(j, t - 1)], (uint32_t)(k - 1));
+        hx[j] = __builtin_nontemporal_load(&wt2[(int64_t)d * vp2 + col]);
+    }
+    int c0[kSkGroups] = {0, 0, 0, 0}, c1[kSkGroups] = {0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < kSkPre; ++u) {
+        const uint32_t xs = s.word[5][u];
+        const uint32_t d0 = sw[u].x ^ xs, d1 = sw[u].y ^ xs;
+#pragma unroll
+        for (int g = 0; g < kSkGroups; ++g) {
+            const uint32_t m = s.word[1 + g][u];
+            c0[g] += __popc(d0 & m);
+            c1[g] += __popc(d1 & m);
+        }
+    }
+    for (int w0 = kSkPre; w0 < kw; w0 += kSkBatch) {
+        sk_u32x2 bw[kSkBatch];
+#pragma unroll
+        for (int u = 0; u < kSkBatch; ++u)
+            bw[u] = __builtin_nontemporal_load(&sg[(int64_t)min(w0 + u, kw - 1) * vp2 + col]);
+#pragma unroll
+        for (int u = 0; u < kSkBatch; ++u) {
+            const uint32_t xs = s.word[5][w0 + u];
+            const uint32_t d0 = bw[u].x ^ xs, d1 = bw[u].y ^ xs;
+#pragma unroll
+            for (int g = 0; g < kSkGroups; ++g) {
+                const uint32_t m = s.word[1 + g][w0 + u];
+                c0[g] += __popc(d0 & m);
+                c1[g] += __popc(d1 & m);
+            }
+        }
+    }
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSkTop; ++j) {
+        if (j < t) {
+            const float xj = s.top_x[j];
+            a0 = fmaf(__uint_as_float(hx[j] << 16), xj, a0);
+            a1 = fmaf(__uint_as_float(hx[j] & 0xFFFF0000u), xj, a1);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < kSkGroups; ++g) {
+        const float wg = s.wgt[g];
+        const int n = s.ng[g];
+        a0 = fmaf(wg, (float)(n - 2 * c0[g]), a0);
+        a1 = fmaf(wg, (float)(n - 2 * c1[g]), a1);
+    }
+    const uint32_t key0 = order_key(a0), key1 = order_key(a1);
+    reinterpret_cast<sk_u32x2*>(ws + sk_keys_off(vp))[col] = sk_u32x2{key0, key1};
+    const int64_t r0 = 2 * col;
+    const bool live0 = r0 < v, live1 = r0 + 1 < v;
+    if (scores) {
+        if (live0) scores[r0] = a0;
+        if (live1) scores[r0 + 1] = a1;
+    }
+    if (live0) atomicAdd(&s.hist[key0 >> (32 - kSkBinBits)], 1u);
+    if (live1) atomicAdd(&s.hist[key1 >> (32 - kSkBinBits)], 1u);
+    lds_barrier();
+    {
+        uint32_t top1 = 0u;   // highest non-empty bin of this thread's, plus one
+#pragma unroll
+        for (int i = 0; i < kSkBins / kSkScoreThreads; ++i) {
+            const int bin = tid + kSkScoreThreads * i;
+            top1 = s.hist[bin] ? (uint32_t)bin + 1u : top1;
+        }
+        top1 = wave_max_u32(top1);
+        if (lane == 0) s.wmax[wave] = top1;
+    }
+    lds_barrier();
+    // the kSkWindow bins below the highest non-empty one, two bins per 64-bit add (each
+    // 32-bit half holds a bin's count, which never carries over)
+    uint32_t top1 = 0u;
+#pragma unroll
+    for (int w = 0; w < kSkScoreWaves; ++w) top1 = max(top1, s.wmax[w]);
+    const int lmax = (int)top1 - 1;   // every workgroup has a live row
+    uint64_t* hist64 = reinterpret_cast<uint64_t*>(ws + kSkHistOff) +
+                       (parity * kSkHistSet + (int64_t)(blockIdx.x % kSkCopies) * kSkBins) / 2;
+    for (int pr = max(lmax - (kSkWindow - 1), 0) / 2 + tid; pr <= lmax / 2; pr += kSkScoreThreads) {
+        const uint32_t h0 = s.hist[2 * pr], h1 = s.hist[2 * pr + 1];
+        if (h0 | h1)
+            __hip_atomic_fetch_add(&hist64[pr], (uint64_t)h0 | ((uint64_t)h1 << 32), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0)
+        __hip_atomic_fetch_max(&ctlw[kCtlMaxBin + 16 * (blockIdx.x % kSkSets)], (uint32_t)lmax, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    if (blockIdx.x == 0 && tid < 2 * kSkSets)   // the pick launch's exit counters, used only after this launch
+        ctlw[kCtlOut + 16 * tid] = 0u;
+}
+
+// ---- per token: the cut, exact scores of the candidates, the choice ------------------------
+
+__global__ __launch_bounds__(kSkPickThreads) void k_sketch_pick(const uint16_t* __restrict__ w,
+                                                                const float* __restrict__ x, int64_t v, int64_t vp,
+                                                                int k, uint8_t* __restrict__ ws,
+                                                                int32_t* __restrict__ idx,
+                                                                float* __restrict__ max_logit,
+                                                                int32_t* __restrict__ ncand)
+{
+    __shared__ __align__(16) float xs[kSketchMaxK];
+    __shared__ int32_t s_list[kSkRows];
+    __shared__ uint32_t s_part[kSkCopies][kSkWindow];
+    __shared__ unsigned long long s_best[kSkPickThreads / kWave];
+    __shared__ uint32_t s_cnt[kSkPickThreads / kWave];
+    __shared__ uint32_t s_n, s_bstar;
+    __shared__ int32_t s_found, s_last;
+    uint32_t* ctlw = reinterpret_cast<uint32_t*>(ws);
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const uint32_t parity = ctlw[kCtlParity] & 1u;
+    uint32_t mb = 0u;
+#pragma unroll
+    for (int g = 0; g < kSkSets; ++g) mb = max(mb, ctlw[kCtlMaxBin + 16 * g]);
+    const int max_bin = (int)min(mb, (uint32_t)(kSkBins - 1));
+    const int64_t r = (int64_t)blockIdx.x * kSkRows + tid;
+    const uint32_t key = reinterpret_cast<const uint32_t*>(ws + sk_keys_off(vp))[r];
+    for (int q = tid; q < (k >> 2); q += kSkPickThreads)
+        reinterpret_cast<float4*>(xs)[q] = reinterpret_cast<const float4*>(x)[q];
+    if (tid == 0) {
+        s_n = 0u;
+        s_found = 0;
+    }
+    // this workgroup's share of clearing the other histogram set (the next token's)
+    uint4* other = reinterpret_cast<uint4*>(ws + kSkHistOff) + (int64_t)(1u - parity) * (kSkHistSet / 4);
+    for (int64_t i = (int64_t)blockIdx.x * kSkPickThreads + tid; i < kSkHistSet / 4;
+         i += (int64_t)gridDim.x * kSkPickThreads)
+        other[i] = make_uint4(0u, 0u, 0u, 0u);
+    // the cut, among the kSkWindow bins below the highest non-empty one
+    const uint32_t need = (uint32_t)min<int64_t>(v, kSkMinCand);
+    uint32_t bstar = 0u;
+    if ((int64_t)need < v) {
+        const uint32_t* hist = reinterpret_cast<const uint32_t*>(ws + kSkHistOff) + parity * kSkHistSet;
+        {
+            const int c = tid / (kSkWindow / 2), jj = 2 * (tid % (kSkWindow / 2));   // bins max_bin - jj, - jj - 1
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int bin = max_bin - jj - e;
+                s_part[c][jj + e] = bin >= 0 ? hist[c * kSkBins + bin] : 0u;
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            uint32_t h4[4], sum = 0u;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h4[e] = 0u;
+#pragma unroll
+                for (int c = 0; c < kSkCopies; ++c) h4[e] += s_part[c][4 * lane + e];
+                sum += h4[e];
+            }
+            const uint32_t incl = wave_scan_incl(sum, lane);
+            const uint32_t excl = incl - sum;
+            if (excl < need && incl >= need) {
+                uint32_t run = excl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    run += h4[e];
+                    if (run >= need) {
+                        s_bstar = (uint32_t)(max_bin - (4 * lane + e));
+                        s_found = 1;
+                        break;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        bstar = s_found ? s_bstar : 0u;   // fewer than need words in the window: every word
+    }
+    // this workgroup's candidates, scored exactly: a wave per word
+    if (r < v && (key >> (32 - kSkBinBits)) >= bstar) s_list[atomicAdd(&s_n, 1u)] = (int32_t)r;
     __syncthreads();
+    const int n = (int)s_n;
+    const int nch = k / 8;
+    unsigned long long mine = 0ull;
+    for (int c = wave; c < n; c += kSkPickThreads / kWave) {
+        const int64_t row_i = s_list[c];
+        const uint4* row = reinterpret_cast<const uint4*>(w + row_i * k);
+        float sum = 0.0f;
+        for (int ch0 = lane; ch0 < nch; ch0 += 4 * kWave) {
+            uint4 q[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = ch0 + u * kWave < nch ? row[ch0 + u * kWave] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int ch = ch0 + u * kWave;
+                if (ch >= nch) break;
+                const float* xc = xs + 8 * ch;
+                sum = fmaf(__uint_as_float(q[u].x << 16), xc[0], sum);
+                sum = fmaf(__uint_as_float(q[u].x & 0xFFFF0000u), xc[1], sum);
+                sum = fmaf(__uint_as_float(q[u].y << 16), xc[2], sum);
+                sum = fmaf(__uint_as_float(q[u].y & 0xFFFF0000u), xc[3], sum);
+                sum = fmaf(__uint_as_float(q[u].z << 16), xc[4], sum);
+                sum = fmaf(__uint_as_float(q[u].z & 0xFFFF0000u), xc[5], sum);
+                sum = fmaf(__uint_as_float(q[u].w << 16), xc[6], sum);
+                sum = fmaf(__uint_as_float(q[u].w & 0xFFFF0000u), xc[7], sum);
+            }
+        }
+        sum = wave_sum_f(sum);
+        const unsigned long long kv =
+            ((unsigned long long)order_key(sum) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)row_i);
+        mine = kv > mine ? kv : mine;
+    }
+    if (lane == 0) s_best[wave] = mine;
+    __syncthreads();
+    // this workgroup's slot, then count it out (per set of workgroups, then over the sets)
+    uint64_t* slots = reinterpret_cast<uint64_t*>(ws + kSkSlotOff);
     if (tid == 0) {
         unsigned long long b = 0ull;
 #pragma unroll
-        for (int i = 0; i < kBlock / kWave; ++i) b = s_best[i] > b ? s_best[i] : b;
-        reinterpret_cast<unsigned long long*>(ws + kSkWgOff)[blockIdx.x] = b;
-        reinterpret_cast<uint32_t*>(ws + kSkWgOff + 8 * kSkMaxWg)[blockIdx.x] = (uint32_t)n;
+        for (int i = 0; i < kSkPickThreads / kWave; ++i) b = s_best[i] > b ? s_best[i] : b;
+        __hip_atomic_store(&slots[2 * blockIdx.x], (uint64_t)b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&slots[2 * blockIdx.x + 1], (uint64_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);   // the slot is written before this workgroup counts itself out
+        const uint32_t set = blockIdx.x % kSkSets;
+        const uint32_t in_set = (gridDim.x - set + kSkSets - 1) / kSkSets;
+        int last = 0;
+        if (__hip_atomic_fetch_add(&ctlw[kCtlOut + 16 * set], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            in_set - 1)
+            last = __hip_atomic_fetch_add(&ctlw[kCtlOutAll], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   min(gridDim.x, (uint32_t)kSkSets) - 1;
+        s_last = last;
     }
-}
-
-// One workgroup: the overall first maximum and the candidate count.
-__global__ __launch_bounds__(kBlock) void k_sketch_final(int nwg, const uint8_t* __restrict__ ws,
-                                                         int32_t* __restrict__ idx, float* __restrict__ max_logit,
-                                                         int32_t* __restrict__ ncand)
-{
-    __shared__ unsigned long long sb[kBlock];
-    __shared__ uint32_t sn[kBlock];
-    const int tid = threadIdx.x;
-    const unsigned long long* wb = reinterpret_cast<const unsigned long long*>(ws + kSkWgOff);
-    const uint32_t* wn = reinterpret_cast<const uint32_t*>(ws + kSkWgOff + 8 * kSkMaxWg);
-    unsigned long long b = 0ull;
-    uint32_t n = 0;
-    for (int i = tid; i < nwg; i += kBlock) {
-        b = wb[i] > b ? wb[i] : b;
-        n += wn[i];
-    }
-    sb[tid] = b;
-    sn[tid] = n;
     __syncthreads();
-    for (int off = kBlock / 2; off > 0; off >>= 1) {
-        if (tid < off) {
-            sb[tid] = sb[tid + off] > sb[tid] ? sb[tid + off] : sb[tid];
-            sn[tid] += sn[tid + off];
+    if (s_last) {
+        unsigned long long b = 0ull;
+        uint32_t cnt = 0u;
+        for (uint32_t i = tid; i < gridDim.x; i += kSkPickThreads) {
+            const unsigned long long bi = __hip_atomic_load(&slots[2 * i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            b = bi > b ? bi : b;
+            cnt += (uint32_t)__hip_atomic_load(&slots[2 * i + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        b = wave_max_u64(b);
+        cnt = wave_scan_incl(cnt, lane);
+        if (lane == kWave - 1) {
+            s_best[wave] = b;
+            s_cnt[wave] = cnt;
         }
         __syncthreads();
-    }
-    if (tid == 0) {
-        *idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(sb[0] & 0xFFFFFFFFu));
-        if (max_logit) *max_logit = key_value((uint32_t)(sb[0] >> 32));
-        if (ncand) *ncand = (int32_t)sn[0];
+        if (tid == 0) {
+            unsigned long long fb = 0ull;
+            uint32_t fc = 0u;
+#pragma unroll
+            for (int i = 0; i < kSkPickThreads / kWave; ++i) {
+                fb = s_best[i] > fb ? s_best[i] : fb;
+                fc += s_cnt[i];
+            }
+            *idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(fb & 0xFFFFFFFFu));
+            if (max_logit) *max_logit = key_value((uint32_t)(fb >> 32));
+            if (ncand) *ncand = (int32_t)fc;
+        }
+        if (tid < kSkSets)
+            __hip_atomic_store(&ctlw[kCtlMaxBin + 16 * tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(&ctlw[kCtlParity], 1u - parity, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -500,80 +879,58 @@ __global__ __launch_bounds__(kBlock) void k_sketch_final(int nwg, const uint8_t*
 int64_t sketch_copy_bytes(int64_t v, int64_t k)
 {
     const int64_t temp = sk_round(4 * v, 256) + sk_round(8 * ((v + kSkRowBlock - 1) / kSkRowBlock), 256);
-    return max(sk_round(2 * k * v, 256), temp);
+    return max(sk_round(2 * k * sk_pitch(v), 256), temp);
 }
 
 int64_t sketch_bytes(int64_t v, int64_t k)
 {
     const int64_t kw = (k + 31) / 32;
-    return 256 + sk_round(4 * kw * v, 256) + sketch_copy_bytes(v, k);
+    return 256 + sk_round(4 * kw * sk_pitch(v), 256) + sketch_copy_bytes(v, k);
 }
 
-// [plan][histograms][pick][per-workgroup bests][row keys: 4 v][sorted |x| keys: 8 * kSketchMaxK]
-int64_t sketch_sorted_off(int64_t v) { return kSkKeysOff + sk_round(4 * v, 256); }
-int64_t sketch_workspace_bytes(int64_t v) { return sketch_sorted_off(v) + 8 * kSketchMaxK; }
+// [control][2 histogram sets][a slot per pick workgroup][row keys: 4 vp]
+int64_t sketch_workspace_bytes(int64_t v) { return sk_keys_off(sk_pitch(v)) + 4 * sk_pitch(v); }
 
 hipError_t launch_sketch_build(const uint16_t* w, int64_t v, int64_t k, void* sketch, hipStream_t s)
 {
     uint8_t* base = static_cast<uint8_t*>(sketch);
-    const int64_t kw = (k + 31) / 32;
+    const int64_t kw = (k + 31) / 32, vp = sk_pitch(v);
     uint32_t* signs = reinterpret_cast<uint32_t*>(base + 256);
-    uint16_t* wt = reinterpret_cast<uint16_t*>(base + 256 + sk_round(4 * kw * v, 256));
+    uint16_t* wt = reinterpret_cast<uint16_t*>(base + 256 + sk_round(4 * kw * vp, 256));
     // the row sums and block partials live in the copy's space until the transpose
     float* rowsum = reinterpret_cast<float*>(wt);
     double* part = reinterpret_cast<double*>(reinterpret_cast<uint8_t*>(wt) + sk_round(4 * v, 256));
-    hipLaunchKernelGGL(k_sketch_rows, dim3((unsigned)((v + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, w, v, (int)k,
-                       signs, rowsum);
+    hipLaunchKernelGGL(k_sketch_rows, dim3((unsigned)((vp + kBlock - 1) / kBlock)), dim3(kBlock), 0, s, w, v, vp,
+                       (int)k, signs, rowsum);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_sketch_scale, dim3(1), dim3(kBlock), 0, s, rowsum, v, (int)k, part,
                        reinterpret_cast<SketchHeader*>(base));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sketch_transpose, dim3((unsigned)((v + 63) / 64), (unsigned)((k + 63) / 64)), dim3(kBlock), 0,
-                       s, w, v, (int)k, wt);
+    hipLaunchKernelGGL(k_sketch_transpose, dim3((unsigned)(vp / 64), (unsigned)((k + 63) / 64)), dim3(kBlock), 0, s,
+                       w, v, vp, (int)k, wt);
     return hipGetLastError();
 }
 
-hipError_t setup_sketch_attributes()
-{
-    hipError_t e = raise_lds_limit(reinterpret_cast<const void*>(&k_sketch_plan));
-    if (e == hipSuccess)
-        e = raise_lds_limit(reinterpret_cast<const void*>(&k_sketch_rescore));
-    return e;
-}
+hipError_t setup_sketch_attributes() { return raise_lds_limit(reinterpret_cast<const void*>(&k_sketch_score)); }
 
 hipError_t launch_sketch_argmax(const uint16_t* w, const void* sketch, const float* x, int64_t v, int64_t k,
                                 int32_t* idx, float* max_logit, int32_t* ncand, float* scores, void* workspace,
                                 hipStream_t s)
 {
     const uint8_t* base = static_cast<const uint8_t*>(sketch);
-    const int64_t kw = (k + 31) / 32;
+    const int64_t kw = (k + 31) / 32, vp = sk_pitch(v);
     const uint32_t* signs = reinterpret_cast<const uint32_t*>(base + 256);
-    const uint16_t* wt = reinterpret_cast<const uint16_t*>(base + 256 + sk_round(4 * kw * v, 256));
+    const uint16_t* wt = reinterpret_cast<const uint16_t*>(base + 256 + sk_round(4 * kw * vp, 256));
     uint8_t* ws = static_cast<uint8_t*>(workspace);
-    uint64_t* sorted = reinterpret_cast<uint64_t*>(ws + sketch_sorted_off(v));
-    hipLaunchKernelGGL(k_sketch_rank, dim3((unsigned)((k + kSkRankPer - 1) / kSkRankPer)), dim3(kBlock), 0, s, x,
-                       (int)k, sorted);
+    const unsigned nwg = (unsigned)(vp / kSkRows);
+    hipLaunchKernelGGL(k_sketch_score, dim3(nwg), dim3(kSkScoreThreads), sizeof(ScoreLds), s, signs, wt, x,
+                       reinterpret_cast<const SketchHeader*>(base), v, vp, (int)k, ws, scores);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t plan_lds = 8 * (size_t)k + 20 * (size_t)kw;
-    hipLaunchKernelGGL(k_sketch_plan, dim3(1), dim3(kSkPlanThreads), plan_lds, s, x, (int)k,
-                       (const uint64_t*)sorted, reinterpret_cast<const SketchHeader*>(base), ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sketch_score, dim3((unsigned)((v + kSkScoreThreads - 1) / kSkScoreThreads)),
-                       dim3(kSkScoreThreads), 0, s, signs, wt, v, ws, scores);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sketch_select, dim3(1), dim3(kSkPlanThreads), 0, s, v, ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int nwg = (int)((v + kSkRowsPerBlock - 1) / kSkRowsPerBlock);
-    hipLaunchKernelGGL(k_sketch_rescore, dim3((unsigned)nwg), dim3(kBlock), (size_t)(4 * k), s, w, x, v, (int)k, ws);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_sketch_final, dim3(1), dim3(kBlock), 0, s, nwg, ws, idx, max_logit, ncand);
+    hipLaunchKernelGGL(k_sketch_pick, dim3(nwg), dim3(kSkPickThreads), 0, s, w, x, v, vp, (int)k, ws, idx, max_logit,
+                       ncand);
     return hipGetLastError();
 }
 

@@ -474,6 +474,17 @@ def qmv_sketch_build(w_bf16, sketch=None, stream=None):
     return sketch
 
 
+def sketch_workspace(v: int, k: int, device):
+    """A zero-filled, 256-byte aligned sketch workspace (the state it carries
+    between tokens starts at zero; every call leaves it ready for the next)."""
+    nbytes = qmv_sketch_workspace_bytes(v, k)
+    if nbytes < 0:
+        raise QmvError(-2, "qmv_sketch_workspace_bytes")
+    ws = _alloc_aligned(nbytes, device)
+    ws.zero_()
+    return ws
+
+
 def qmv_lmhead_sketch_argmax(w_bf16, sketch, x, idx=None, max_logit=None, candidates=None, scores=None,
                              workspace=None, want_scores=False, stream=None):
     """Returns (idx [1] int32, max_logit [1] fp32, candidates [1] int32, scores [v] fp32 or None)."""
@@ -491,7 +502,7 @@ def qmv_lmhead_sketch_argmax(w_bf16, sketch, x, idx=None, max_logit=None, candid
     if scores is None and want_scores:
         scores = torch.empty(v, dtype=torch.float32, device=dev)
     if workspace is None:
-        workspace = _alloc_aligned(max(qmv_sketch_workspace_bytes(v, k), 256), dev)
+        workspace = sketch_workspace(v, k, dev)
     _check(load().qmv_lmhead_sketch_argmax(_ptr(w_bf16), _ptr(sketch), _ptr(x), v, k, _ptr(idx), _ptr(max_logit),
                                            _ptr(candidates), _ptr(scores), _ptr(workspace), workspace.numel(),
                                            _stream(stream)), "qmv_lmhead_sketch_argmax")

@@ -125,6 +125,8 @@ def test_host_validation_errors(lib):
                                         _fake(4096), 1 << 20, s) == qmv.QMV_EINVAL
     assert lib.qmv_lmhead_sketch_argmax(_fake(4096), _fake(4096), _fake(64), 10, 64, _fake(64), None, None, None,
                                         _fake(4096), 16, s) == qmv.QMV_EWORKSPACE
+    assert lib.qmv_lmhead_sketch_argmax(_fake(4096), _fake(4096), _fake(68), 10, 64, _fake(64), None, None, None,
+                                        _fake(4096), 1 << 20, s) == qmv.QMV_EINVAL   # x not 16-byte aligned
 
 
 def _problem(wtype=qmv.QMV_W_TERNARY5, n=64, k=80, m=1, data=4096):

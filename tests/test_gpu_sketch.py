@@ -10,7 +10,8 @@ the plain N = min(1024, v) best approximate scores as its candidates.
     of the group weights ((k + n_g + 2) roundings), times the sum of the
     magnitudes of the score's terms;
   * the GPU's candidates, rebuilt from its own scores by its documented rule
-    (the top bins of 12-bit order keys that hold at least N words), number
+    (the top bins of 13-bit order keys that hold at least N words, among the
+    256 bins below the highest non-empty one, else every word), number
     what the kernel reports, and contain every word whose oracle score clears
     the N-th best upper bound by more than its own error bound
     (containment: such a word is in the GPU's top N whatever the rounding);
@@ -19,7 +20,8 @@ the plain N = min(1024, v) best approximate scores as its candidates.
     of the oracle's pick whenever that word is surely a GPU candidate;
     max_logit within that bound of the pick's exact logit.
 Shapes: small and ragged cases, fewer words than 1024, k <= 32 (all exact),
-ties, and the output layer's full 262144 x 1152.
+ties, and the output layer's full 262144 x 1152.  The workspace carries state
+from call to call: one workspace is also reused over several shapes in a row.
 """
 import sys
 
@@ -43,13 +45,19 @@ def _round(n, a):
     return (n + a - 1) // a * a
 
 
+BIN_BITS = 13      # the candidate rule's bins: top 13 bits of the score's order key
+WINDOW = 256       # bins searched below the highest non-empty one
+
+
 def _tables(sketch, v, k):
+    """The header's c, the sign words [kw][vp] and the copy [k][vp], vp = v rounded up to 1024."""
     raw = sketch.cpu().numpy()
     kw = (k + 31) // 32
+    vp = _round(v, 1024)
     c = raw[16:20].view(np.float32)[0]
-    signs = raw[256:256 + 4 * kw * v].view(np.uint32).reshape(kw, v)
-    off = 256 + _round(4 * kw * v, 256)
-    wt = raw[off:off + 2 * k * v].view(np.uint16).reshape(k, v)
+    signs = raw[256:256 + 4 * kw * vp].view(np.uint32).reshape(kw, vp)
+    off = 256 + _round(4 * kw * vp, 256)
+    wt = raw[off:off + 2 * k * vp].view(np.uint16).reshape(k, vp)
     return c, signs, wt
 
 
@@ -71,19 +79,24 @@ def _score_bound(k, group_n, mag):
 
 def _bins(scores32):
     u = scores32.view(np.uint32).astype(np.uint64)
-    return (np.where(u & 0x80000000, ~u & 0xFFFFFFFF, u | 0x80000000) >> 20).astype(np.int64)
+    return (np.where(u & 0x80000000, ~u & 0xFFFFFFFF, u | 0x80000000) >> (32 - BIN_BITS)).astype(np.int64)
 
 
 def _gpu_candidates(scores32, n_need):
-    """The documented rule: the top bins (12-bit order keys) holding at least n_need words."""
+    """The documented rule: the top bins (13-bit order keys) holding at least n_need words,
+    searched over the WINDOW bins below the highest non-empty one; every word if those hold fewer."""
+    nb = 1 << BIN_BITS
     b = _bins(scores32)
-    hist = np.bincount(b, minlength=4096)
+    in_window = b >= b.max() - (WINDOW - 1)
+    hist = np.bincount(b[in_window], minlength=nb)
     above = np.cumsum(hist[::-1])
-    bstar = 4095 - int(np.argmax(above >= n_need))
+    if above[-1] < n_need:
+        return np.ones(b.shape, dtype=bool)
+    bstar = nb - 1 - int(np.argmax(above >= n_need))
     return b >= bstar
 
 
-def _run(w_bits, x, build_check=True, calls=1):
+def _run(w_bits, x, build_check=True, calls=1, ws=None):
     from ternary_matvec_amd import qmv
     v, k = w_bits.shape
     w = torch.from_numpy(w_bits.view(np.int16)).to(DEV)
@@ -93,10 +106,12 @@ def _run(w_bits, x, build_check=True, calls=1):
     c, signs, wt = _tables(sketch, v, k)
     assert abs(float(c) - c_ref) <= (k + 1) * U * 1.01 * c_ref, (c, c_ref)
     if build_check:
-        np.testing.assert_array_equal(signs, oracle.sketch_signs(w_bits))
-        np.testing.assert_array_equal(wt, w_bits.T)
+        np.testing.assert_array_equal(signs[:, :v], oracle.sketch_signs(w_bits))
+        np.testing.assert_array_equal(wt[:, :v], w_bits.T)
+        assert not signs[:, v:].any() and not wt[:, v:].any()
     xd = torch.from_numpy(x).to(DEV)
-    ws = qmv._alloc_aligned(qmv.qmv_sketch_workspace_bytes(v, k), xd.device)
+    if ws is None:
+        ws = qmv.sketch_workspace(v, k, xd.device)
     for _ in range(calls):
         idx, mx, ncand, scores = qmv.qmv_lmhead_sketch_argmax(w, sketch, xd, workspace=ws, want_scores=True)
     torch.cuda.synchronize()
@@ -184,3 +199,16 @@ def test_sketch_fullsize_output_layer(qmv_gpu):
     for t in range(3):
         x = synth.normal(synth.stream_seed(synth.CONFIG_HEAD, 1, t, synth.TAG_ACT), (k,))
         _run(w_bits, x, build_check=(t == 0))
+
+
+def test_sketch_workspace_reused_over_shapes(qmv_gpu):
+    """One zero-filled workspace, sized for the largest shape, through tokens of
+    different shapes in a row (the state each call leaves must suit any next one)."""
+    from ternary_matvec_amd import qmv
+    shapes = [(5000, 256), (1500, 64), (20000, 1152), (900, 96), (5000, 256)]
+    ws = qmv.sketch_workspace(max(v for v, _ in shapes), max(k for _, k in shapes), DEV)
+    for i, (v, k) in enumerate(shapes):
+        say("sketch %d x %d on a shared workspace (call %d)" % (v, k, i))
+        w = synth.to_bf16_bits(synth.normal(3000 + i, (v, k), std=0.02))
+        x = synth.normal(4000 + i, (k,))
+        _run(w, x, build_check=False, calls=2, ws=ws)
