@@ -60,7 +60,6 @@ constexpr int kSkScoreThreads = 512;  // score: two rows per lane
 constexpr int kSkScoreWaves = kSkScoreThreads / kWave;
 constexpr int kSkPickThreads = 1024;  // pick: one row per lane
 constexpr int kSkWords = kSketchMaxK / 32;
-constexpr int kSkChunks = kSketchMaxK / 64;
 constexpr int kSkList = 64;           // dimensions of a boundary's bin ranked against each other
 constexpr int kSkPre = 36;            // sign words per lane asked for before the plan (all of them for k <= 1152)
 constexpr int kSkBatch = 12;          // sign words per batch after those
@@ -199,14 +198,14 @@ __global__ __launch_bounds__(kBlock) void k_sketch_transpose(const uint16_t* __r
 
 struct ScoreLds {
     uint32_t xb[kSketchMaxK];                    // x's bit patterns
-    alignas(16) uint32_t rh0[2048];                          // top 11 bits of |x|, shared by the boundaries
-    alignas(16) uint32_t rh[kSkGroups][1024];                // further 10-bit digits, one histogram per boundary
+    alignas(16) uint32_t rh0[2048];              // top 11 bits of |x|, shared by the boundaries
+    alignas(16) uint32_t rh[2][kSkGroups][1024]; // the next 10-bit digits, then the last (per boundary)
     uint64_t lst[kSkGroups][kSkList];            // order keys of the dimensions in a boundary's bin
-    alignas(16) uint32_t word[6][kSkWords + kSkBatch];       // masks: [0] exact, [1..4] groups, [5] signs of x
-    uint32_t tcnt[kSkChunks], tpre[kSkChunks];   // exact dimensions per 64 and their prefix
+    uint64_t toplist[kSkTop];                    // order keys of the exact dimensions
+    alignas(16) uint32_t word[6][kSkWords + kSkBatch];   // masks: [0] exact, [1..4] groups, [5] signs of x
     float gpart[kSkScoreWaves][kSkGroups];       // the groups' sums of |x| per wave
     uint64_t kb[kSkGroups];                      // order key at each boundary rank (0: none)
-    uint32_t pre[kSkGroups], res[kSkGroups], cnt[kSkGroups], sh[kSkGroups], lcnt[kSkGroups];
+    uint32_t lcnt[kSkGroups], tcount;
     int32_t top_idx[kSkTop];
     float top_x[kSkTop];
     float wgt[kSkGroups];
@@ -364,6 +363,196 @@ __device__ __forceinline__ void find_digit(const uint32_t* h, uint32_t r, int la
     cnt = (uint32_t)__builtin_amdgcn_readlane((int)c, src);
 }
 
+// One wave, the shared histogram of the top 11 bits (2048 bins): for each active
+// boundary b, the bin holding rank B[b] from the top, the rank within it and the
+// bin's count (the same in every lane).  Lane l first sums bins 2047 - 32 l down to
+// 2016 - 32 l; the lane whose range holds the rank then has its 32 bins spread
+// over lanes 0..31 and scanned again.
+__device__ __forceinline__ void find_digits4(const uint32_t* h, const int* B, const bool* act, int lane,
+                                             uint32_t* pre, uint32_t* res, uint32_t* cnt)
+{
+    constexpr int kPer = 32;
+    const int lo = 2048 - kPer * (lane + 1);
+    uint32_t sum = 0u;
+#pragma unroll
+    for (int j = 0; j < kPer; j += 4) {
+        const uint4 v4 = *reinterpret_cast<const uint4*>(h + lo + j);
+        sum += (v4.x + v4.y) + (v4.z + v4.w);
+    }
+    const uint32_t incl = wave_scan_incl(sum, lane);
+    const uint32_t excl = incl - sum;
+#pragma unroll
+    for (int b = 0; b < kSkGroups; ++b) {
+        pre[b] = res[b] = cnt[b] = 0u;
+        if (!act[b]) continue;
+        const uint32_t r = (uint32_t)B[b];
+        const int src = (int)__builtin_ctzll(__ballot(excl <= r && r < incl) | (1ull << 63));
+        const uint32_t e_src = (uint32_t)__builtin_amdgcn_readlane((int)excl, src);
+        const int lo_src = 2048 - kPer * (src + 1);
+        const uint32_t hv = lane < kPer ? h[lo_src + kPer - 1 - lane] : 0u;   // its bins, highest first
+        const uint32_t ci = wave_scan_incl(hv, lane);
+        const int j = (int)__builtin_ctzll(__ballot(lane < kPer && e_src + ci > r) | (1ull << 63));
+        pre[b] = (uint32_t)(lo_src + kPer - 1 - j);
+        cnt[b] = (uint32_t)__builtin_amdgcn_readlane((int)hv, j);
+        res[b] = r - e_src - ((uint32_t)__builtin_amdgcn_readlane((int)ci, j) - cnt[b]);
+    }
+}
+
+__device__ __forceinline__ void store_agent(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The cut b*: the highest bin at which the bins from the top down hold `need`
+// words, among the kSkWindow bins below the highest non-empty one (0 when they
+// hold fewer, or when every word is needed).  The same in every thread.  The
+// histogram and the maxima come from the previous launch: plain loads see them.
+template <int THREADS>
+__device__ __forceinline__ uint32_t find_cut(const uint32_t* ctlw, const uint32_t* hist, uint32_t need, int64_t v,
+                                             uint32_t (*part)[kSkWindow], uint32_t& s_bstar, int32_t& s_found,
+                                             int tid, int lane, int wave)
+{
+    if ((int64_t)need >= v) return 0u;
+    uint32_t mb = 0u;
+#pragma unroll
+    for (int g = 0; g < kSkSets; ++g) mb = max(mb, ctlw[kCtlMaxBin + 16 * g]);
+    const int max_bin = (int)min(mb, (uint32_t)(kSkBins - 1));
+    if (tid == 0) s_found = 0;
+    for (int i = tid; i < kSkCopies * kSkWindow; i += THREADS) {
+        const int c = i / kSkWindow, j = i % kSkWindow, bin = max_bin - j;
+        part[c][j] = bin >= 0 ? hist[c * kSkBins + bin] : 0u;
+    }
+    __syncthreads();
+    if (wave == 0) {   // lane l: bins max_bin - 4 l .. max_bin - 4 l - 3
+        uint32_t h4[4], sum = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            h4[e] = 0u;
+#pragma unroll
+            for (int c = 0; c < kSkCopies; ++c) h4[e] += part[c][4 * lane + e];
+            sum += h4[e];
+        }
+        const uint32_t incl = wave_scan_incl(sum, lane);
+        const uint32_t excl = incl - sum;
+        if (excl < need && incl >= need) {
+            uint32_t run = excl;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                run += h4[e];
+                if (run >= need) {
+                    s_bstar = (uint32_t)(max_bin - (4 * lane + e));
+                    s_found = 1;
+                    break;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    return s_found ? s_bstar : 0u;   // fewer than need words in the window: every word
+}
+
+// Exact logits of the workgroup's candidates, a wave per word (x in LDS); the
+// wave's best (logit order key << 32 | ~row).
+template <int WAVES>
+__device__ __forceinline__ unsigned long long rescore(const uint16_t* __restrict__ w, const float* xs, int k,
+                                                      const int32_t* list, int n, int lane, int wave)
+{
+    const int nch = k / 8;
+    unsigned long long mine = 0ull;
+    for (int c = wave; c < n; c += WAVES) {
+        const int64_t row_i = list[c];
+        const uint4* row = reinterpret_cast<const uint4*>(w + row_i * k);
+        float sum = 0.0f;
+        for (int ch0 = lane; ch0 < nch; ch0 += 4 * kWave) {
+            uint4 q[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) q[u] = ch0 + u * kWave < nch ? row[ch0 + u * kWave] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int ch = ch0 + u * kWave;
+                if (ch >= nch) break;
+                const float* xc = xs + 8 * ch;
+                sum = fmaf(__uint_as_float(q[u].x << 16), xc[0], sum);
+                sum = fmaf(__uint_as_float(q[u].x & 0xFFFF0000u), xc[1], sum);
+                sum = fmaf(__uint_as_float(q[u].y << 16), xc[2], sum);
+                sum = fmaf(__uint_as_float(q[u].y & 0xFFFF0000u), xc[3], sum);
+                sum = fmaf(__uint_as_float(q[u].z << 16), xc[4], sum);
+                sum = fmaf(__uint_as_float(q[u].z & 0xFFFF0000u), xc[5], sum);
+                sum = fmaf(__uint_as_float(q[u].w << 16), xc[6], sum);
+                sum = fmaf(__uint_as_float(q[u].w & 0xFFFF0000u), xc[7], sum);
+            }
+        }
+        sum = wave_sum_f(sum);
+        const unsigned long long kv =
+            ((unsigned long long)order_key(sum) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)row_i);
+        mine = kv > mine ? kv : mine;
+    }
+    return mine;
+}
+
+// The workgroup's best and count go to its slot; it counts itself out (per set
+// of workgroups, then over the sets), and the last one out takes the first
+// maximum over the slots, writes the choice and readies the control words for
+// the next token.
+template <int THREADS>
+__device__ __forceinline__ void finish(uint8_t* ws, uint32_t* ctlw, unsigned long long mine, uint32_t n,
+                                       uint32_t parity, int32_t* idx, float* max_logit, int32_t* ncand,
+                                       unsigned long long* s_best, uint32_t* s_cnt, int32_t& s_last, int tid,
+                                       int lane, int wave)
+{
+    constexpr int kWaves = THREADS / kWave;
+    uint64_t* slots = reinterpret_cast<uint64_t*>(ws + kSkSlotOff);
+    if (lane == 0) s_best[wave] = mine;
+    __syncthreads();
+    if (tid == 0) {
+        unsigned long long b = 0ull;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) b = s_best[i] > b ? s_best[i] : b;
+        __hip_atomic_store(&slots[2 * blockIdx.x], (uint64_t)b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&slots[2 * blockIdx.x + 1], (uint64_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);   // the slot is written before this workgroup counts itself out
+        const uint32_t set = blockIdx.x % kSkSets;
+        const uint32_t in_set = (gridDim.x - set + kSkSets - 1) / kSkSets;
+        int last = 0;
+        if (__hip_atomic_fetch_add(&ctlw[kCtlOut + 16 * set], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            in_set - 1)
+            last = __hip_atomic_fetch_add(&ctlw[kCtlOutAll], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   min(gridDim.x, (uint32_t)kSkSets) - 1;
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    unsigned long long b = 0ull;
+    uint32_t cnt = 0u;
+    for (uint32_t i = tid; i < gridDim.x; i += THREADS) {
+        const unsigned long long bi = __hip_atomic_load(&slots[2 * i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        b = bi > b ? bi : b;
+        cnt += (uint32_t)__hip_atomic_load(&slots[2 * i + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    b = wave_max_u64(b);
+    cnt = wave_scan_incl(cnt, lane);
+    if (lane == kWave - 1) {
+        s_best[wave] = b;
+        s_cnt[wave] = cnt;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        unsigned long long fb = 0ull;
+        uint32_t fc = 0u;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) {
+            fb = s_best[i] > fb ? s_best[i] : fb;
+            fc += s_cnt[i];
+        }
+        *idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(fb & 0xFFFFFFFFu));
+        if (max_logit) *max_logit = key_value((uint32_t)(fb >> 32));
+        if (ncand) *ncand = (int32_t)fc;
+        store_agent(&ctlw[kCtlParity], 1u - parity);
+    }
+    if (tid < kSkSets) store_agent(&ctlw[kCtlMaxBin + 16 * tid], 0u);
+    if (tid < 2 * kSkSets) store_agent(&ctlw[kCtlOut + 16 * tid], 0u);
+}
+
 __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t* __restrict__ signs,
                                                                   const uint16_t* __restrict__ wt,
                                                                   const float* __restrict__ x,
@@ -410,16 +599,21 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         reinterpret_cast<uint4*>(s.hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     for (int i = tid; i < 2048 / 4; i += kSkScoreThreads)
         reinterpret_cast<uint4*>(s.rh0)[i] = make_uint4(0u, 0u, 0u, 0u);
-    for (int i = tid; i < kSkGroups * 1024 / 4; i += kSkScoreThreads)
-        reinterpret_cast<uint4*>(&s.rh[0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < 2 * kSkGroups * 1024 / 4; i += kSkScoreThreads)
+        reinterpret_cast<uint4*>(&s.rh[0][0][0])[i] = make_uint4(0u, 0u, 0u, 0u);
     const int t = min(k, kSkTop), rest = k - t, base = rest / kSkGroups;
+    int B[kSkGroups];
     bool act[kSkGroups];
 #pragma unroll
-    for (int b = 0; b < kSkGroups; ++b) act[b] = boundary_rank(b, t, base) < k;
+    for (int b = 0; b < kSkGroups; ++b) {
+        B[b] = boundary_rank(b, t, base);
+        act[b] = B[b] < k;
+    }
     if (tid < kSkGroups) s.lcnt[tid] = 0u;
+    if (tid == 0) s.tcount = 0u;
     const int nq = (k4 + kSkScoreThreads - 1) / kSkScoreThreads;
     lds_barrier();
-    // the boundaries' bins of the top 11 bits of |x|
+    // the boundaries' bins of the top 11 bits of |x| (every wave finds them; the state stays in registers)
 #pragma unroll
     for (int i = 0; i < kSkXLoads; ++i) {
         if (i >= nq) break;
@@ -428,80 +622,56 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
             if (ux[i][j] != 0xFFFFFFFFu) atomicAdd(&s.rh0[ux[i][j] >> 20], 1u);
     }
     lds_barrier();
-    if (wave < kSkGroups && act[wave]) {
-        uint32_t dg, rin, c;
-        find_digit<32>(s.rh0, (uint32_t)boundary_rank(wave, t, base), lane, dg, rin, c);
-        if (lane == 0) {
-            s.pre[wave] = dg;
-            s.res[wave] = rin;
-            s.cnt[wave] = c;
-            s.sh[wave] = 20u;
-        }
-    }
-    lds_barrier();
+    uint32_t pre[kSkGroups], res[kSkGroups], cnt[kSkGroups], shv[kSkGroups];
+    find_digits4(s.rh0, B, act, lane, pre, res, cnt);
+#pragma unroll
+    for (int b = 0; b < kSkGroups; ++b) shv[b] = 20u;
     // a bin of more than kSkList dimensions: the next 10 bits (then the last 10)
 #pragma unroll
     for (int p = 1; p <= 2; ++p) {
         const int sh = 20 - 10 * p;
         bool more[kSkGroups];
         bool any_more = false;
-        uint32_t pre[kSkGroups];
 #pragma unroll
         for (int b = 0; b < kSkGroups; ++b) {
-            more[b] = act[b] && s.cnt[b] > (uint32_t)kSkList;
+            more[b] = act[b] && cnt[b] > (uint32_t)kSkList;
             any_more = any_more || more[b];
-            pre[b] = s.pre[b];
         }
         if (!any_more) break;
-#pragma unroll
-        for (int i = 0; i < kSkXLoads; ++i) {
-            if (i >= nq) break;
+#pragma unroll 1
+        for (int i = 0; i < nq; ++i) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const uint32_t u = ux[i][j];
 #pragma unroll
                 for (int b = 0; b < kSkGroups; ++b)
-                    if (more[b] && (u >> (sh + 10)) == pre[b]) atomicAdd(&s.rh[b][(u >> sh) & 1023u], 1u);
+                    if (more[b] && (u >> (sh + 10)) == pre[b]) atomicAdd(&s.rh[p - 1][b][(u >> sh) & 1023u], 1u);
             }
         }
         lds_barrier();
-        if (wave < kSkGroups && more[wave]) {
-            uint32_t dg, rin, c;
-            find_digit<16>(s.rh[wave], s.res[wave], lane, dg, rin, c);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) s.rh[wave][16 * lane + j] = 0u;   // only this wave reads it
-            if (lane == 0) {
-                s.pre[wave] = (pre[wave] << 10) | dg;
-                s.res[wave] = rin;
-                s.cnt[wave] = c;
-                s.sh[wave] = (uint32_t)sh;
-            }
-        }
-        lds_barrier();
-    }
-    // the dimensions left in each boundary's bin
-    {
-        bool in_list[kSkGroups];
-        uint32_t pre[kSkGroups], shb[kSkGroups];
 #pragma unroll
         for (int b = 0; b < kSkGroups; ++b) {
-            in_list[b] = act[b] && s.cnt[b] <= (uint32_t)kSkList;
-            pre[b] = s.pre[b];
-            shb[b] = s.sh[b];
+            if (!more[b]) continue;
+            uint32_t dg, rin, c;
+            find_digit<16>(s.rh[p - 1][b], res[b], lane, dg, rin, c);
+            pre[b] = (pre[b] << 10) | dg;
+            res[b] = rin;
+            cnt[b] = c;
+            shv[b] = (uint32_t)sh;
         }
+    }
+    // the dimensions left in each boundary's bin
+#pragma unroll 1
+    for (int i = 0; i < nq; ++i) {
 #pragma unroll
-        for (int i = 0; i < kSkXLoads; ++i) {
-            if (i >= nq) break;
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t u = ux[i][j];
+            const int d = 4 * (tid + kSkScoreThreads * i) + j;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t u = ux[i][j];
-                const int d = 4 * (tid + kSkScoreThreads * i) + j;
-#pragma unroll
-                for (int b = 0; b < kSkGroups; ++b) {
-                    if (in_list[b] && (u >> shb[b]) == pre[b]) {
-                        const uint32_t slot = atomicAdd(&s.lcnt[b], 1u);
-                        if (slot < (uint32_t)kSkList) s.lst[b][slot] = dim_key(u, d);
-                    }
+            for (int b = 0; b < kSkGroups; ++b) {
+                if (act[b] && cnt[b] <= (uint32_t)kSkList && (u >> shv[b]) == pre[b]) {
+                    const uint32_t slot = atomicAdd(&s.lcnt[b], 1u);
+                    if (slot < (uint32_t)kSkList) s.lst[b][slot] = dim_key(u, d);
                 }
             }
         }
@@ -512,9 +682,9 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         const int b = wave;
         if (!act[b]) {
             if (lane == 0) s.kb[b] = 0ull;   // no such rank: every key is above
-        } else if (s.cnt[b] <= (uint32_t)kSkList) {
+        } else if (cnt[b] <= (uint32_t)kSkList) {
             // rank the bin's dimensions against each other
-            const uint32_t c = s.cnt[b], r = s.res[b];
+            const uint32_t c = cnt[b], r = res[b];
             const uint64_t my = lane < (int)c ? s.lst[b][lane] : 0ull;
             uint32_t above = 0u;
             for (uint32_t j = 0; j < c; j += 8) {   // entries past c are ignored below
@@ -527,8 +697,8 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
             if (lane < (int)c && above == r) s.kb[b] = my;
         } else {
             // more than kSkList dimensions with exactly the boundary's |x|: by index
-            const uint32_t ub = s.pre[b];
-            uint32_t r = s.res[b];
+            const uint32_t ub = pre[b];
+            uint32_t r = res[b];
             for (int c = 0; c < nch; ++c) {
                 const int d = 64 * c + lane;
                 const bool m = d < k && (s.xb[min(d, k - 1)] & 0x7FFFFFFFu) == ub;
@@ -543,7 +713,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         }
     }
     lds_barrier();
-    // classes, 64 dimensions per wave step: mask words, exact dimensions per step, group sums of |x|
+    // classes, 64 dimensions per wave step: mask words, the exact dimensions, group sums of |x|
     const uint64_t k0 = s.kb[0], k1 = s.kb[1], k2 = s.kb[2], k3 = s.kb[3];
     {
         float gp[kSkGroups] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -570,7 +740,10 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
                     s.word[q][2 * c] = (uint32_t)m[q];
                     s.word[q][2 * c + 1] = (uint32_t)(m[q] >> 32);
                 }
-                s.tcnt[c] = (uint32_t)__popcll(m[0]);
+            }
+            if (top) {
+                const uint32_t slot = atomicAdd(&s.tcount, 1u);
+                if (slot < (uint32_t)kSkTop) s.toplist[slot] = key;
             }
         }
 #pragma unroll
@@ -580,12 +753,16 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         }
     }
     lds_barrier();
-    if (wave == 0) {   // where each step's exact dimensions go in the list (index order)
-        const uint32_t a = 2 * lane < nch ? s.tcnt[2 * lane] : 0u;
-        const uint32_t b = 2 * lane + 1 < nch ? s.tcnt[2 * lane + 1] : 0u;
-        const uint32_t excl = wave_scan_incl(a + b, lane) - (a + b);
-        if (2 * lane < nch) s.tpre[2 * lane] = excl;
-        if (2 * lane + 1 < nch) s.tpre[2 * lane + 1] = excl + a;
+    if (wave == 0) {   // the exact dimensions in rank order (largest |x| first)
+        const uint64_t my = lane < t ? s.toplist[lane] : 0ull;
+        uint32_t above = 0u;
+#pragma unroll 8
+        for (int j = 0; j < t; ++j) above += s.toplist[j] > my ? 1u : 0u;
+        if (lane < t && above < (uint32_t)kSkTop) {
+            const int d = (int)(0xFFFFFFFFu - (uint32_t)my);
+            s.top_idx[above] = d;
+            s.top_x[above] = __uint_as_float(s.xb[min(d, k - 1)]);
+        }
     }
     if (tid >= kWave && tid < kWave + kSkGroups) {   // group weights
         const int g = tid - kWave;
@@ -595,19 +772,6 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         const int n = g < kSkGroups - 1 ? base : rest - (kSkGroups - 1) * base;
         s.ng[g] = n;
         s.wgt[g] = n > 0 ? ctab * (sum / (float)n) : 0.0f;
-    }
-    lds_barrier();
-    for (int c = wave; c < nch; c += kSkScoreWaves) {
-        const int d = 64 * c + lane;
-        const bool valid = d < k;
-        const uint32_t xbits = valid ? s.xb[d] : 0u;
-        const bool top = valid && dim_key(xbits & 0x7FFFFFFFu, d) > k0;
-        const uint64_t mt = __ballot(top);
-        const uint32_t pos = s.tpre[c] + lanes_below(mt);
-        if (top && pos < (uint32_t)kSkTop) {
-            s.top_idx[pos] = d;
-            s.top_x[pos] = __uint_as_float(xbits);
-        }
     }
     lds_barrier();
 
@@ -707,7 +871,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         ctlw[kCtlOut + 16 * tid] = 0u;
 }
 
-// ---- per token: the cut, exact scores of the candidates, the choice ------------------------
+// ---- per token, second launch: the cut, exact scores of the candidates, the choice ----------
 
 __global__ __launch_bounds__(kSkPickThreads) void k_sketch_pick(const uint16_t* __restrict__ w,
                                                                 const float* __restrict__ x, int64_t v, int64_t vp,
@@ -726,150 +890,25 @@ __global__ __launch_bounds__(kSkPickThreads) void k_sketch_pick(const uint16_t* 
     uint32_t* ctlw = reinterpret_cast<uint32_t*>(ws);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const uint32_t parity = ctlw[kCtlParity] & 1u;
-    uint32_t mb = 0u;
-#pragma unroll
-    for (int g = 0; g < kSkSets; ++g) mb = max(mb, ctlw[kCtlMaxBin + 16 * g]);
-    const int max_bin = (int)min(mb, (uint32_t)(kSkBins - 1));
     const int64_t r = (int64_t)blockIdx.x * kSkRows + tid;
     const uint32_t key = reinterpret_cast<const uint32_t*>(ws + sk_keys_off(vp))[r];
     for (int q = tid; q < (k >> 2); q += kSkPickThreads)
         reinterpret_cast<float4*>(xs)[q] = reinterpret_cast<const float4*>(x)[q];
-    if (tid == 0) {
-        s_n = 0u;
-        s_found = 0;
-    }
+    if (tid == 0) s_n = 0u;
     // this workgroup's share of clearing the other histogram set (the next token's)
     uint4* other = reinterpret_cast<uint4*>(ws + kSkHistOff) + (int64_t)(1u - parity) * (kSkHistSet / 4);
     for (int64_t i = (int64_t)blockIdx.x * kSkPickThreads + tid; i < kSkHistSet / 4;
          i += (int64_t)gridDim.x * kSkPickThreads)
         other[i] = make_uint4(0u, 0u, 0u, 0u);
-    // the cut, among the kSkWindow bins below the highest non-empty one
     const uint32_t need = (uint32_t)min<int64_t>(v, kSkMinCand);
-    uint32_t bstar = 0u;
-    if ((int64_t)need < v) {
-        const uint32_t* hist = reinterpret_cast<const uint32_t*>(ws + kSkHistOff) + parity * kSkHistSet;
-        {
-            const int c = tid / (kSkWindow / 2), jj = 2 * (tid % (kSkWindow / 2));   // bins max_bin - jj, - jj - 1
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int bin = max_bin - jj - e;
-                s_part[c][jj + e] = bin >= 0 ? hist[c * kSkBins + bin] : 0u;
-            }
-        }
-        __syncthreads();
-        if (wave == 0) {
-            uint32_t h4[4], sum = 0u;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                h4[e] = 0u;
-#pragma unroll
-                for (int c = 0; c < kSkCopies; ++c) h4[e] += s_part[c][4 * lane + e];
-                sum += h4[e];
-            }
-            const uint32_t incl = wave_scan_incl(sum, lane);
-            const uint32_t excl = incl - sum;
-            if (excl < need && incl >= need) {
-                uint32_t run = excl;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    run += h4[e];
-                    if (run >= need) {
-                        s_bstar = (uint32_t)(max_bin - (4 * lane + e));
-                        s_found = 1;
-                        break;
-                    }
-                }
-            }
-        }
-        __syncthreads();
-        bstar = s_found ? s_bstar : 0u;   // fewer than need words in the window: every word
-    }
-    // this workgroup's candidates, scored exactly: a wave per word
+    const uint32_t bstar = find_cut<kSkPickThreads>(
+        ctlw, reinterpret_cast<const uint32_t*>(ws + kSkHistOff) + parity * kSkHistSet, need, v, s_part, s_bstar,
+        s_found, tid, lane, wave);
     if (r < v && (key >> (32 - kSkBinBits)) >= bstar) s_list[atomicAdd(&s_n, 1u)] = (int32_t)r;
     __syncthreads();
-    const int n = (int)s_n;
-    const int nch = k / 8;
-    unsigned long long mine = 0ull;
-    for (int c = wave; c < n; c += kSkPickThreads / kWave) {
-        const int64_t row_i = s_list[c];
-        const uint4* row = reinterpret_cast<const uint4*>(w + row_i * k);
-        float sum = 0.0f;
-        for (int ch0 = lane; ch0 < nch; ch0 += 4 * kWave) {
-            uint4 q[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) q[u] = ch0 + u * kWave < nch ? row[ch0 + u * kWave] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int ch = ch0 + u * kWave;
-                if (ch >= nch) break;
-                const float* xc = xs + 8 * ch;
-                sum = fmaf(__uint_as_float(q[u].x << 16), xc[0], sum);
-                sum = fmaf(__uint_as_float(q[u].x & 0xFFFF0000u), xc[1], sum);
-                sum = fmaf(__uint_as_float(q[u].y << 16), xc[2], sum);
-                sum = fmaf(__uint_as_float(q[u].y & 0xFFFF0000u), xc[3], sum);
-                sum = fmaf(__uint_as_float(q[u].z << 16), xc[4], sum);
-                sum = fmaf(__uint_as_float(q[u].z & 0xFFFF0000u), xc[5], sum);
-                sum = fmaf(__uint_as_float(q[u].w << 16), xc[6], sum);
-                sum = fmaf(__uint_as_float(q[u].w & 0xFFFF0000u), xc[7], sum);
-            }
-        }
-        sum = wave_sum_f(sum);
-        const unsigned long long kv =
-            ((unsigned long long)order_key(sum) << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)row_i);
-        mine = kv > mine ? kv : mine;
-    }
-    if (lane == 0) s_best[wave] = mine;
-    __syncthreads();
-    // this workgroup's slot, then count it out (per set of workgroups, then over the sets)
-    uint64_t* slots = reinterpret_cast<uint64_t*>(ws + kSkSlotOff);
-    if (tid == 0) {
-        unsigned long long b = 0ull;
-#pragma unroll
-        for (int i = 0; i < kSkPickThreads / kWave; ++i) b = s_best[i] > b ? s_best[i] : b;
-        __hip_atomic_store(&slots[2 * blockIdx.x], (uint64_t)b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&slots[2 * blockIdx.x + 1], (uint64_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);   // the slot is written before this workgroup counts itself out
-        const uint32_t set = blockIdx.x % kSkSets;
-        const uint32_t in_set = (gridDim.x - set + kSkSets - 1) / kSkSets;
-        int last = 0;
-        if (__hip_atomic_fetch_add(&ctlw[kCtlOut + 16 * set], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-            in_set - 1)
-            last = __hip_atomic_fetch_add(&ctlw[kCtlOutAll], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                   min(gridDim.x, (uint32_t)kSkSets) - 1;
-        s_last = last;
-    }
-    __syncthreads();
-    if (s_last) {
-        unsigned long long b = 0ull;
-        uint32_t cnt = 0u;
-        for (uint32_t i = tid; i < gridDim.x; i += kSkPickThreads) {
-            const unsigned long long bi = __hip_atomic_load(&slots[2 * i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            b = bi > b ? bi : b;
-            cnt += (uint32_t)__hip_atomic_load(&slots[2 * i + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        b = wave_max_u64(b);
-        cnt = wave_scan_incl(cnt, lane);
-        if (lane == kWave - 1) {
-            s_best[wave] = b;
-            s_cnt[wave] = cnt;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            unsigned long long fb = 0ull;
-            uint32_t fc = 0u;
-#pragma unroll
-            for (int i = 0; i < kSkPickThreads / kWave; ++i) {
-                fb = s_best[i] > fb ? s_best[i] : fb;
-                fc += s_cnt[i];
-            }
-            *idx = (int32_t)(0xFFFFFFFFu - (uint32_t)(fb & 0xFFFFFFFFu));
-            if (max_logit) *max_logit = key_value((uint32_t)(fb >> 32));
-            if (ncand) *ncand = (int32_t)fc;
-        }
-        if (tid < kSkSets)
-            __hip_atomic_store(&ctlw[kCtlMaxBin + 16 * tid], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (tid == 0) __hip_atomic_store(&ctlw[kCtlParity], 1u - parity, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const uint32_t n = s_n;
+    const unsigned long long mine = rescore<kSkPickThreads / kWave>(w, xs, k, s_list, (int)n, lane, wave);
+    finish<kSkPickThreads>(ws, ctlw, mine, n, parity, idx, max_logit, ncand, s_best, s_cnt, s_last, tid, lane, wave);
 }
 
 }  // namespace

@@ -20,7 +20,8 @@ the plain N = min(1024, v) best approximate scores as its candidates.
     of the oracle's pick whenever that word is surely a GPU candidate;
     max_logit within that bound of the pick's exact logit.
 Shapes: small and ragged cases, fewer words than 1024, k <= 32 (all exact),
-ties, and the output layer's full 262144 x 1152.  The workspace carries state
+ties, the output layer's full 262144 x 1152, and 300000 rows (more workgroups
+than compute units).  The workspace carries state
 from call to call: one workspace is also reused over several shapes in a row.
 """
 import sys
@@ -212,3 +213,13 @@ def test_sketch_workspace_reused_over_shapes(qmv_gpu):
         w = synth.to_bf16_bits(synth.normal(3000 + i, (v, k), std=0.02))
         x = synth.normal(4000 + i, (k,))
         _run(w, x, build_check=False, calls=2, ws=ws)
+
+
+def test_sketch_more_workgroups_than_compute_units(qmv_gpu):
+    """300000 rows = 293 workgroups of 1024 rows, more than the 256 compute units
+    (several workgroups per histogram copy and exit set beyond one round); twice, so
+    the state the first call leaves is used again."""
+    say("sketch 300000 x 64, two calls")
+    w = synth.to_bf16_bits(synth.normal(91, (300000, 64), std=0.02))
+    x = synth.normal(92, (64,))
+    _run(w, x, calls=2)
