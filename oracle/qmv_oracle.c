@@ -295,8 +295,8 @@ void oracle_lmhead(const uint16_t* w, const float* x, int64_t v, int64_t k, doub
 #define ORACLE_SKETCH_GROUPS 4
 #define ORACLE_SKETCH_CAND 1024
 
-/* Sign bits of the table in the device layout: bit (c % 32) of word        */
-/* (c / 32) * v + r is 1 when w[r][c] < 0; bits past k are 0.                */
+/* Sign bits of the table, word-major: bit (c % 32) of word (c / 32) * v + r */
+/* is 1 when w[r][c] < 0; bits past k are 0.                                 */
 void oracle_sketch_signs(const uint16_t* w, int64_t v, int64_t k, uint32_t* out, int threads)
 {
     int64_t words = (k + 31) / 32;
