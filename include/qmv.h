@@ -440,7 +440,7 @@ int32_t qmv_lmhead_argmax_static(const uint16_t* w_bf16, const float* x, int64_t
  *      rank order they form 4 groups (floor((k-T)/4) each, the last takes the
  *      rest), and group g adds c * mean|x|_g * (agreeing - disagreeing signs),
  *      c being the mean |w| of the table (a sign bit is set for a value < 0);
- *      the score is fp32: a = fma(w, x, a) over the exact dimensions in rank
+ *      the score is fp32: a = fma(w, x, a) over the exact dimensions in index
  *      order, then a = fma(weight_g, agreement_g, a) for g = 0..3;
  *   3. the candidates are the words whose score falls in the top bins that
  *      hold at least min(1024, v) words, a bin being the top 13 bits of the

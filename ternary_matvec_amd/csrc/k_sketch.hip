@@ -201,15 +201,12 @@ struct ScoreLds {
     alignas(16) uint32_t rh0[2048];              // top 11 bits of |x|, shared by the boundaries
     alignas(16) uint32_t rh[2][kSkGroups][1024]; // the next 10-bit digits, then the last (per boundary)
     uint64_t lst[kSkGroups][kSkList];            // order keys of the dimensions in a boundary's bin
-    uint64_t toplist[kSkTop];                    // order keys of the exact dimensions
     alignas(16) uint32_t word[6][kSkWords + kSkBatch];   // masks: [0] exact, [1..4] groups, [5] signs of x
     float gpart[kSkScoreWaves][kSkGroups];       // the groups' sums of |x| per wave
     uint64_t kb[kSkGroups];                      // order key at each boundary rank (0: none)
-    uint32_t lcnt[kSkGroups], tcount;
-    int32_t top_idx[kSkTop];
-    float top_x[kSkTop];
-    float wgt[kSkGroups];
-    int32_t ng[kSkGroups];
+    uint32_t lcnt[kSkGroups];
+    int32_t top_idx[kSkScoreWaves][kSkTop];      // each wave's copy of the exact dimensions (index order)
+    float top_x[kSkScoreWaves][kSkTop];
     uint32_t wmax[kSkScoreWaves];
     alignas(16) uint32_t hist[kSkBins];
 };
@@ -610,7 +607,6 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         act[b] = B[b] < k;
     }
     if (tid < kSkGroups) s.lcnt[tid] = 0u;
-    if (tid == 0) s.tcount = 0u;
     const int nq = (k4 + kSkScoreThreads - 1) / kSkScoreThreads;
     lds_barrier();
     // the boundaries' bins of the top 11 bits of |x| (every wave finds them; the state stays in registers)
@@ -741,10 +737,6 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
                     s.word[q][2 * c + 1] = (uint32_t)(m[q] >> 32);
                 }
             }
-            if (top) {
-                const uint32_t slot = atomicAdd(&s.tcount, 1u);
-                if (slot < (uint32_t)kSkTop) s.toplist[slot] = key;
-            }
         }
 #pragma unroll
         for (int gi = 0; gi < kSkGroups; ++gi) {
@@ -753,34 +745,45 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         }
     }
     lds_barrier();
-    if (wave == 0) {   // the exact dimensions in rank order (largest |x| first)
-        const uint64_t my = lane < t ? s.toplist[lane] : 0ull;
-        uint32_t above = 0u;
-#pragma unroll 8
-        for (int j = 0; j < t; ++j) above += s.toplist[j] > my ? 1u : 0u;
-        if (lane < t && above < (uint32_t)kSkTop) {
-            const int d = (int)(0xFFFFFFFFu - (uint32_t)my);
-            s.top_idx[above] = d;
-            s.top_x[above] = __uint_as_float(s.xb[min(d, k - 1)]);
-        }
-    }
-    if (tid >= kWave && tid < kWave + kSkGroups) {   // group weights
-        const int g = tid - kWave;
+    // every wave on its own from here: the group weights (the partial sums in wave order) and the
+    // exact dimensions in index order (a scan of the exact-mask words over the 64-dimension steps)
+    float wgt[kSkGroups];
+    int ng[kSkGroups];
+#pragma unroll
+    for (int g = 0; g < kSkGroups; ++g) {
         float sum = 0.0f;
 #pragma unroll
         for (int w = 0; w < kSkScoreWaves; ++w) sum += s.gpart[w][g];
-        const int n = g < kSkGroups - 1 ? base : rest - (kSkGroups - 1) * base;
-        s.ng[g] = n;
-        s.wgt[g] = n > 0 ? ctab * (sum / (float)n) : 0.0f;
+        ng[g] = g < kSkGroups - 1 ? base : rest - (kSkGroups - 1) * base;
+        wgt[g] = ng[g] > 0 ? ctab * (sum / (float)ng[g]) : 0.0f;
     }
-    lds_barrier();
+    {
+        uint32_t before = 0u;
+        for (int c0 = 0; c0 < nch; c0 += kWave) {
+            const int c = c0 + lane;
+            uint64_t m = 0ull;
+            if (c < nch) m = ((uint64_t)s.word[0][2 * c + 1] << 32) | s.word[0][2 * c];
+            const uint32_t n = (uint32_t)__popcll(m);
+            const uint32_t incl = wave_scan_incl(n, lane);
+            uint32_t pos = before + incl - n;
+            while (m && pos < (uint32_t)kSkTop) {
+                const int d = 64 * c + (int)__builtin_ctzll(m);
+                m &= m - 1;
+                s.top_idx[wave][pos] = d;
+                s.top_x[wave][pos] = __uint_as_float(s.xb[d]);
+                ++pos;
+            }
+            before += (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's list is written before it is read
 
     // ---- scores of rows 2 col and 2 col + 1 ----
     const uint32_t* wt2 = reinterpret_cast<const uint32_t*>(wt);
     uint32_t hx[kSkTop];
 #pragma unroll
     for (int j = 0; j < kSkTop; ++j) {
-        const uint32_t d = min((uint32_t)s.top_idx[min(j, t - 1)], (uint32_t)(k - 1));
+        const uint32_t d = min((uint32_t)s.top_idx[wave][min(j, t - 1)], (uint32_t)(k - 1));
         hx[j] = __builtin_nontemporal_load(&wt2[(int64_t)d * vp2 + col]);
     }
     int c0[kSkGroups] = {0, 0, 0, 0}, c1[kSkGroups] = {0, 0, 0, 0};
@@ -816,17 +819,15 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
 #pragma unroll
     for (int j = 0; j < kSkTop; ++j) {
         if (j < t) {
-            const float xj = s.top_x[j];
+            const float xj = s.top_x[wave][j];
             a0 = fmaf(__uint_as_float(hx[j] << 16), xj, a0);
             a1 = fmaf(__uint_as_float(hx[j] & 0xFFFF0000u), xj, a1);
         }
     }
 #pragma unroll
     for (int g = 0; g < kSkGroups; ++g) {
-        const float wg = s.wgt[g];
-        const int n = s.ng[g];
-        a0 = fmaf(wg, (float)(n - 2 * c0[g]), a0);
-        a1 = fmaf(wg, (float)(n - 2 * c1[g]), a1);
+        a0 = fmaf(wgt[g], (float)(ng[g] - 2 * c0[g]), a0);
+        a1 = fmaf(wgt[g], (float)(ng[g] - 2 * c1[g]), a1);
     }
     const uint32_t key0 = order_key(a0), key1 = order_key(a1);
     reinterpret_cast<sk_u32x2*>(ws + sk_keys_off(vp))[col] = sk_u32x2{key0, key1};
