@@ -223,3 +223,25 @@ def test_sketch_more_workgroups_than_compute_units(qmv_gpu):
     w = synth.to_bf16_bits(synth.normal(91, (300000, 64), std=0.02))
     x = synth.normal(92, (64,))
     _run(w, x, calls=2)
+
+
+def test_sketch_widest_rows(qmv_gpu):
+    """k = 8192, the largest supported: the bins of the top 11 bits of |x| hold more than
+    64 dimensions, so the further 10-bit digits are taken, and the sign words run past
+    the ones loaded before the plan."""
+    say("sketch 3000 x 8192")
+    w = synth.to_bf16_bits(synth.normal(95, (3000, 8192), std=0.02))
+    x = synth.normal(96, (8192,))
+    _run(w, x)
+
+
+def test_sketch_zero_heavy_hidden_state(qmv_gpu):
+    """60% of x exactly zero (some of them -0.0): the group boundaries fall among equal |x|,
+    which are ranked by index."""
+    say("sketch 20000 x 1152, 60% zero x")
+    w = synth.to_bf16_bits(synth.normal(97, (20000, 1152), std=0.02))
+    x = synth.normal(98, (1152,))
+    r = synth.raw(99, 1152) % 10
+    x[r < 6] = 0.0
+    x[r == 0] = -0.0
+    _run(w, x.astype(np.float32))
