@@ -51,6 +51,7 @@ INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, datasheet
 GEMV_SOURCES = ("k_gemv_stream.hip", "unpack.hpp", "zform.hpp", "qmv_internal.hpp")
 GEMV_COUNTERS = os.path.join(ROOT, "profiles", "k_gemv_stream_counters.json")
 N_REP = 5
+WARM_MS = 200.0   # GPU time of back-to-back calls before a timed row's repetitions
 EXTRAS = ("decode_copies_sweep", "decode_chained", "quantize_step", "host_overhead", "ffn", "zero_skip", "lmhead",
           "lmhead_sketch", "int8_gemv", "groupscale_decode", "bitnet_decode_all")
 
@@ -86,12 +87,25 @@ def parse():
     return args
 
 
-def median_time(fn, reps, stream, warm=3, n_rep=N_REP):
+def median_time(fn, reps, stream, warm=3, n_rep=N_REP, warm_ms=WARM_MS):
     """Median (over n_rep repetitions) of the time per call of `reps`
-    back-to-back calls fn(i), in ms, with every repetition's value."""
+    back-to-back calls fn(i), in ms, with every repetition's value.  Before
+    the repetitions: `warm` calls, then blocks of `reps` calls until warm_ms of
+    GPU time has passed (back-to-back times keep falling for tens of ms after a
+    pause: clocks and caches settle), so the repetitions see steady state."""
     import torch
     for i in range(warm):
         fn(i)
+    spent = 0.0
+    while spent < warm_ms:
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(reps):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        spent += t0.elapsed_time(t1)
     vals = []
     for r in range(n_rep):
         t0 = torch.cuda.Event(enable_timing=True)
