@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200, help="back-to-back steps per repetition (at least 100)")
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="GPU time of back-to-back calls before each timed row's repetitions (0: none; counter "
+                         "runs, whose figures do not depend on it, use 0)")
     ap.add_argument("--copies", type=int, default=8, help="weight copies rotated to defeat the MALL")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extras", default="",
@@ -87,7 +90,7 @@ def parse():
     return args
 
 
-def median_time(fn, reps, stream, warm=3, n_rep=N_REP, warm_ms=WARM_MS):
+def median_time(fn, reps, stream, warm=3, n_rep=N_REP, warm_ms=None):
     """Median (over n_rep repetitions) of the time per call of `reps`
     back-to-back calls fn(i), in ms, with every repetition's value.  Before
     the repetitions: `warm` calls, then blocks of `reps` calls until warm_ms of
@@ -96,6 +99,7 @@ def median_time(fn, reps, stream, warm=3, n_rep=N_REP, warm_ms=WARM_MS):
     import torch
     for i in range(warm):
         fn(i)
+    warm_ms = WARM_MS if warm_ms is None else warm_ms
     spent = 0.0
     while spent < warm_ms:
         t0 = torch.cuda.Event(enable_timing=True)
@@ -943,7 +947,9 @@ def cpu_baselines(stack, dev):
 # ---------------------------------------------------------------------------
 
 def main():
+    global WARM_MS
     args = parse()
+    WARM_MS = max(0.0, args.warm_ms)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
