@@ -14,7 +14,7 @@
 //     histogram of the top 11 bits of |x|, then (for a bin of more than 64
 //     dimensions) further 10-bit digits, and the at most 64 dimensions left in
 //     the boundary's bin are ranked against each other (by |x|, then index);
-//     a dimension's class is then three compares.  The approximate score of a
+//     a dimension's class is then four compares.  The approximate score of a
 //     row is the exact products over the T dimensions (from the
 //     dimension-major copy of the table) plus, per group, weight * (n_g - 2 *
 //     popcount((signs of w ^ signs of x) & mask_g)) from the 1-bit table.
