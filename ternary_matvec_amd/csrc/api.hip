@@ -561,16 +561,17 @@ int32_t build_prefill_image(const qmv_problem* probs, int32_t count, int cus, st
     pbytes = round_up((int64_t)sizeof(DevProblem) * count, 256);
     img.assign(need, 0);
     DevProblem* dp = reinterpret_cast<DevProblem*>(img.data());
-    // Tile list, XCD-aware: workgroup b runs on XCD b % 8 (round-robin dispatch),
-    // so tiles that share an activation block (same problem and token block) go
-    // to one XCD's list and run back to back there, reusing that XCD's L2.  The
-    // token-block groups are spread over the XCDs longest first, to the least
-    // loaded one.
-    struct Group {
+    // Tile list, XCD-aware: workgroup b runs on XCD b % 8 (round-robin dispatch).
+    // All tiles of a problem go to one XCD's list, row block major (its token
+    // blocks side by side), so the tiles in flight on an XCD share both their
+    // weight row blocks and their activation blocks in that XCD's L2: a weight
+    // row block is fetched once per pass instead of once per token block.  The
+    // problems are spread over the XCDs longest first, to the least loaded one.
+    struct Prob {
         int32_t slot;
-        int64_t mt, ntiles, work;
+        int64_t mts, nts, work;
     };
-    std::vector<Group> groups;
+    std::vector<Prob> pr;
     for (int32_t slot = 0; slot < count; ++slot) {
         const qmv_problem& p = probs[order[slot]];
         DevProblem& d = dp[slot];
@@ -590,18 +591,19 @@ int32_t build_prefill_image(const qmv_problem* probs, int32_t count, int cus, st
         d.reserved = 0;
         const int64_t mts = (p.m + kPrefillTileM - 1) / kPrefillTileM;
         const int64_t nts = (p.w.n + kPrefillTileN - 1) / kPrefillTileN;
-        for (int64_t mt = 0; mt < mts; ++mt) groups.push_back({slot, mt, nts, nts * ((d.chunks + 1) / 2)});
+        pr.push_back({slot, mts, nts, mts * nts * ((d.chunks + 1) / 2)});
     }
-    std::stable_sort(groups.begin(), groups.end(), [](const Group& a, const Group& b) { return a.work > b.work; });
+    std::stable_sort(pr.begin(), pr.end(), [](const Prob& a, const Prob& b) { return a.work > b.work; });
     std::vector<std::vector<uint64_t>> lists(kXcds);
     std::vector<int64_t> load(kXcds, 0);
-    for (const Group& gr : groups) {
+    for (const Prob& q : pr) {
         int x = 0;
         for (int i = 1; i < kXcds; ++i)
             if (load[i] < load[x]) x = i;
-        load[x] += gr.work;
-        for (int64_t nt = 0; nt < gr.ntiles; ++nt)
-            lists[x].push_back(((uint64_t)gr.slot << 48) | ((uint64_t)gr.mt << 32) | (uint64_t)nt);
+        load[x] += q.work;
+        for (int64_t nt = 0; nt < q.nts; ++nt)
+            for (int64_t mt = 0; mt < q.mts; ++mt)
+                lists[x].push_back(((uint64_t)q.slot << 48) | ((uint64_t)mt << 32) | (uint64_t)nt);
     }
     // Persistent workgroups, two per compute unit: each starts on its XCD's
     // list and takes tiles by ticket (the tickets follow the entries and start
