@@ -18,20 +18,35 @@
 namespace qmv {
 namespace {
 
+// Max over a wave of values >= 0 (every lane receives it): DPP row shifts
+// within each row of 16 lanes (a lane shifted in from outside the row brings
+// 0, which changes no such maximum), then the four rows' last lanes.  fmaxf,
+// so a NaN never wins.
 __device__ __forceinline__ float wave_max(float v)
 {
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, false)));
+    const float a = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15)),
+                          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31)));
+    const float b = fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47)),
+                          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63)));
+    return fmaxf(a, b);
 }
 
-// Max over a 256-thread block (red: 4 floats of LDS); every thread receives it.
+// Max over a block of BS threads of values >= 0 (red: BS / 64 floats of
+// LDS); every thread receives it.
+template <int BS = 256>
 __device__ __forceinline__ float block_max(float v, float* red)
 {
     v = wave_max(v);
     const int lane = threadIdx.x & 63, wave = threadIdx.x / 64;
     if (lane == 0) red[wave] = v;
     __syncthreads();
-    float r = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < BS / 64; ++i) r = fmaxf(r, red[i]);
     __syncthreads();
     return r;
 }
@@ -44,6 +59,23 @@ __device__ __forceinline__ float scale_from_max(float m)
 __device__ __forceinline__ int8_t quantize_one(float v, float s)
 {
     float q = __builtin_rintf(v / s);
+    q = fminf(fmaxf(q, -128.0f), 127.0f);
+    return (int8_t)(int)q;
+}
+
+// quantize_one(v, s) for a row whose scale s = scale_from_max(m) has |v| <= m,
+// given r = 1 / s (IEEE), with one multiply in place of the division.  Each of
+// r, y = v * r and the quotient v / s is within a relative 2^-24 of its exact
+// value and |v / s| <= 127 (1 + 2^-23), so y lies within 2^-15 of the rounded
+// quotient: both round to the same integer unless y is within 2^-14 of a
+// half-integer (or is NaN), and there the division decides.  The same code for
+// every such input.
+__device__ __forceinline__ int8_t quantize_one_r(float v, float s, float r)
+{
+#pragma clang fp contract(off)
+    const float y = v * r;
+    const float n = __builtin_rintf(y);
+    float q = fabsf(y - n) < 0.5f - 0x1p-14f ? n : __builtin_rintf(v / s);
     q = fminf(fmaxf(q, -128.0f), 127.0f);
     return (int8_t)(int)q;
 }

@@ -19,36 +19,40 @@ namespace {
 // ---------------------------------------------------------------------------
 // Per-row quantisation: one workgroup per row.
 // ---------------------------------------------------------------------------
-// Rows of up to 256 * 4 * kRegVec values that are 16-byte aligned (in) and
-// 4-byte aligned (out) are read once: the values stay in registers between
-// the maximum and the quantisation.
-constexpr int kRegVec = 8;
+// A workgroup of kQuantThreads per row.  Rows of up to 8192 values that are
+// 16-byte aligned (in) and 4-byte aligned (out) are read once: the values stay
+// in registers between the maximum and the quantisation.  The codes come from
+// quantize_one_r, the division's codes with one multiply per value.
+constexpr int kQuantThreads = 512;
+constexpr int kRegVec = 8192 / (4 * kQuantThreads);
 
 __device__ __forceinline__ void quantize_row(const float* __restrict__ xr, int64_t k, int8_t* __restrict__ qr,
                                              float* __restrict__ sx_out, float* red)
 {
+    constexpr int BS = kQuantThreads;
     float m = 0.0f;
     const bool vec = ((reinterpret_cast<uintptr_t>(xr) & 15) == 0);
-    if (vec && (k & 3) == 0 && k <= 4 * kBlock * kRegVec && (reinterpret_cast<uintptr_t>(qr) & 3) == 0) {
+    if (vec && (k & 3) == 0 && k <= 4 * BS * kRegVec && (reinterpret_cast<uintptr_t>(qr) & 3) == 0) {
         const float4* x4 = reinterpret_cast<const float4*>(xr);
         const int n4 = (int)(k >> 2);
         float4 v[kRegVec];
 #pragma unroll
         for (int j = 0; j < kRegVec; ++j) {
-            const int i = (int)threadIdx.x + kBlock * j;
+            const int i = (int)threadIdx.x + BS * j;
             v[j] = i < n4 ? x4[i] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)), fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
         }
-        m = block_max(m, red);
+        m = block_max<BS>(m, red);
         const float s = scale_from_max(m);
+        const float r = 1.0f / s;
         if (threadIdx.x == 0) *sx_out = s;
         uint32_t* q4 = reinterpret_cast<uint32_t*>(qr);
 #pragma unroll
         for (int j = 0; j < kRegVec; ++j) {
-            const int i = (int)threadIdx.x + kBlock * j;
+            const int i = (int)threadIdx.x + BS * j;
             if (i < n4) {
-                uint32_t b0 = (uint8_t)quantize_one(v[j].x, s), b1 = (uint8_t)quantize_one(v[j].y, s);
-                uint32_t b2 = (uint8_t)quantize_one(v[j].z, s), b3 = (uint8_t)quantize_one(v[j].w, s);
+                uint32_t b0 = (uint8_t)quantize_one_r(v[j].x, s, r), b1 = (uint8_t)quantize_one_r(v[j].y, s, r);
+                uint32_t b2 = (uint8_t)quantize_one_r(v[j].z, s, r), b3 = (uint8_t)quantize_one_r(v[j].w, s, r);
                 q4[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
             }
         }
@@ -57,44 +61,45 @@ __device__ __forceinline__ void quantize_row(const float* __restrict__ xr, int64
     int64_t head = vec ? (k & ~int64_t(3)) : 0;
     if (vec) {
         const float4* x4 = reinterpret_cast<const float4*>(xr);
-        for (int64_t i = threadIdx.x; i < head / 4; i += kBlock) {
+        for (int64_t i = threadIdx.x; i < head / 4; i += BS) {
             float4 v = x4[i];
             m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
         }
     }
-    for (int64_t i = head + threadIdx.x; i < k; i += kBlock) m = fmaxf(m, fabsf(xr[i]));
-    m = block_max(m, red);
+    for (int64_t i = head + threadIdx.x; i < k; i += BS) m = fmaxf(m, fabsf(xr[i]));
+    m = block_max<BS>(m, red);
     const float s = scale_from_max(m);
+    const float r = 1.0f / s;
     if (threadIdx.x == 0) *sx_out = s;
     const bool vec_out = vec && ((reinterpret_cast<uintptr_t>(qr) & 3) == 0);
     if (vec_out) {
         const float4* x4 = reinterpret_cast<const float4*>(xr);
         uint32_t* q4 = reinterpret_cast<uint32_t*>(qr);
-        for (int64_t i = threadIdx.x; i < head / 4; i += kBlock) {
+        for (int64_t i = threadIdx.x; i < head / 4; i += BS) {
             float4 v = x4[i];
-            uint32_t b0 = (uint8_t)quantize_one(v.x, s), b1 = (uint8_t)quantize_one(v.y, s);
-            uint32_t b2 = (uint8_t)quantize_one(v.z, s), b3 = (uint8_t)quantize_one(v.w, s);
+            uint32_t b0 = (uint8_t)quantize_one_r(v.x, s, r), b1 = (uint8_t)quantize_one_r(v.y, s, r);
+            uint32_t b2 = (uint8_t)quantize_one_r(v.z, s, r), b3 = (uint8_t)quantize_one_r(v.w, s, r);
             q4[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
         }
-        for (int64_t i = head + threadIdx.x; i < k; i += kBlock) qr[i] = quantize_one(xr[i], s);
+        for (int64_t i = head + threadIdx.x; i < k; i += BS) qr[i] = quantize_one_r(xr[i], s, r);
     } else {
-        for (int64_t i = threadIdx.x; i < k; i += kBlock) qr[i] = quantize_one(xr[i], s);
+        for (int64_t i = threadIdx.x; i < k; i += BS) qr[i] = quantize_one_r(xr[i], s, r);
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_quantize_rows(const float* __restrict__ x, int64_t k,
-                                                         int8_t* __restrict__ x8, float* __restrict__ sx)
+__global__ __launch_bounds__(kQuantThreads) void k_quantize_rows(const float* __restrict__ x, int64_t k,
+                                                                int8_t* __restrict__ x8, float* __restrict__ sx)
 {
-    __shared__ float red[4];
+    __shared__ float red[kQuantThreads / 64];
     const int64_t row = blockIdx.x;
     quantize_row(x + row * k, k, x8 + row * k, sx + row, red);
 }
 
 // Several activation sets in one launch: workgroup b quantises row
 // b - first[i] of the set i whose rows it falls in.
-__global__ __launch_bounds__(kBlock) void k_quantize_many(ActSets sets)
+__global__ __launch_bounds__(kQuantThreads) void k_quantize_many(ActSets sets)
 {
-    __shared__ float red[4];
+    __shared__ float red[kQuantThreads / 64];
     const int64_t b = blockIdx.x;
     int i = 0;
     while (i + 1 < sets.count && b >= sets.first[i + 1]) ++i;
@@ -280,13 +285,13 @@ int grid_for(int64_t items)
 
 hipError_t launch_quantize_rows(const float* x, int64_t m, int64_t k, int8_t* x8, float* sx, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)m), dim3(kBlock), 0, s, x, k, x8, sx);
+    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)m), dim3(kQuantThreads), 0, s, x, k, x8, sx);
     return hipGetLastError();
 }
 
 hipError_t launch_quantize_many(const ActSets& sets, int64_t rows, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_quantize_many, dim3((unsigned)rows), dim3(kBlock), 0, s, sets);
+    hipLaunchKernelGGL(k_quantize_many, dim3((unsigned)rows), dim3(kQuantThreads), 0, s, sets);
     return hipGetLastError();
 }
 
