@@ -4,9 +4,10 @@
 // scale = max(max|v|, 1e-9) / 127, code = clip(round(v / scale), -128, 127),
 // with one scale per token for activations ("Gemma 3 1B at 114 tokens per
 // second on a laptop CPU", "Step 2": every layer's inputs are rounded to int8)
-// and one per tensor for int8 weights.  Division is IEEE fp32 (the library is
-// built with correctly rounded division) and rounding is half-to-even
-// (v_rndne_f32), the IEEE default.
+// and one per tensor for int8 weights.  The code is that of an IEEE fp32
+// division (the library is built with correctly rounded division) rounded
+// half-to-even (v_rndne_f32), the IEEE default; the per-row activation kernels
+// reach it with one multiply per value (actq.hpp, quantize_one_r).
 //
 // Five trits per byte ("Step 1": 3^5 = 243 codes fit in a byte): byte j of a
 // row is sum_i (t[5j+i] + 1) * 3^i; columns past k count as trit 0.
