@@ -436,7 +436,23 @@ def chained(stack, reps, stream, copies=4):
             for plan in per_copy[i % copies]:
                 plan.launch(stream)
         ms, _ = median_time(step, reps, stream)
-        out["launches_%s" % name] = {"step_us": us(ms), "GB/s": round(stack.gemv_bytes() / ms / 1e6, 1)}
+        # the same launches replayed from a graph per weight copy: the GPU's own cost
+        # of the dependent chain, without the host's per-call time
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cap = torch.cuda.current_stream()
+                for plan in per_copy[c]:
+                    plan.launch(cap)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        gms, _ = median_time(lambda i: graphs[i % copies].replay(), reps, stream)
+        out["launches_%s" % name] = {"step_us": us(ms), "GB/s": round(stack.gemv_bytes() / ms / 1e6, 1),
+                                     "graph_step_us": us(gms),
+                                     "graph_GB/s": round(stack.gemv_bytes() / gms / 1e6, 1)}
+        del graphs
+        torch.cuda.synchronize()
     return out
 
 
