@@ -5,8 +5,8 @@
 // Per token, two launches:
 //  1. k_sketch_score, a workgroup per 1024 rows (two per lane).  Each
 //     workgroup reads x, asks for its rows' sign words (they do not depend on
-//     the token's plan) and makes the plan itself in LDS while they are in
-//     flight: the T = min(32, k) dimensions with the largest |x| (ties to the
+//     the token's plan; issued in batches between the plan's steps) and makes
+//     the plan itself in LDS while they are in flight: the T = min(32, k) dimensions with the largest |x| (ties to the
 //     lower index) are scored exactly, the other k - T form 4 consecutive rank
 //     groups, each weighted by c * mean |x| of the group (c = mean |w| of the
 //     table, computed when the sketch is built).  Ranks are never sorted out:
@@ -583,11 +583,21 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         if (q < k4) reinterpret_cast<float4*>(s.xb)[q] = xv[i];
     }
     asm volatile("" ::: "memory");
-    // ... then the sign words, which stay in flight while the plan is made
+    // ... then the sign words, which stay in flight while the plan is made.  They go out in six
+    // batches, one before the plan and one after each of its first five LDS steps: asked for at
+    // once, the whole chip's requests fill the memory queues and issuing them holds the wave for
+    // microseconds before the plan can start; spread out, the plan runs while the queues drain.
     const sk_u32x2* sg = reinterpret_cast<const sk_u32x2*>(signs);
     sk_u32x2 sw[kSkPre];
+    constexpr int kSkPreBatch = kSkPre / 6;
+    static_assert(kSkPre % 6 == 0, "six batches of sign words");
+    auto issue = [&](int b) {
 #pragma unroll
-    for (int u = 0; u < kSkPre; ++u) sw[u] = __builtin_nontemporal_load(&sg[(int64_t)min(u, kw - 1) * vp2 + col]);
+        for (int u = b * kSkPreBatch; u < (b + 1) * kSkPreBatch; ++u)
+            sw[u] = __builtin_nontemporal_load(&sg[(int64_t)min(u, kw - 1) * vp2 + col]);
+        asm volatile("" ::: "memory");
+    };
+    issue(0);
 
     // ---- the plan ----
     for (int i = tid; i < 6 * (kSkWords + kSkBatch) / 4; i += kSkScoreThreads)
@@ -609,6 +619,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
     if (tid < kSkGroups) s.lcnt[tid] = 0u;
     const int nq = (k4 + kSkScoreThreads - 1) / kSkScoreThreads;
     lds_barrier();
+    issue(1);
     // the boundaries' bins of the top 11 bits of |x| (every wave finds them; the state stays in registers)
 #pragma unroll
     for (int i = 0; i < kSkXLoads; ++i) {
@@ -618,6 +629,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
             if (ux[i][j] != 0xFFFFFFFFu) atomicAdd(&s.rh0[ux[i][j] >> 20], 1u);
     }
     lds_barrier();
+    issue(2);
     uint32_t pre[kSkGroups], res[kSkGroups], cnt[kSkGroups], shv[kSkGroups];
     find_digits4(s.rh0, B, act, lane, pre, res, cnt);
 #pragma unroll
@@ -673,6 +685,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         }
     }
     lds_barrier();
+    issue(3);
     const int nch = (k + 63) >> 6;
     if (wave < kSkGroups) {
         const int b = wave;
@@ -709,6 +722,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         }
     }
     lds_barrier();
+    issue(4);
     // classes, 64 dimensions per wave step: mask words, the exact dimensions, group sums of |x|
     const uint64_t k0 = s.kb[0], k1 = s.kb[1], k2 = s.kb[2], k3 = s.kb[3];
     {
@@ -745,6 +759,7 @@ __global__ __launch_bounds__(kSkScoreThreads) void k_sketch_score(const uint32_t
         }
     }
     lds_barrier();
+    issue(5);
     // every wave on its own from here: the group weights (the partial sums in wave order) and the
     // exact dimensions in index order (a scan of the exact-mask words over the 64-dimension steps)
     float wgt[kSkGroups];
