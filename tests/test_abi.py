@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
     assert sorted(qmv.SIGNATURES) == names
 
 
-def test_north_star_entry_points_present(lib):
+def test_core_entry_points_present(lib):
     for name in ("qmv_pack_ternary", "qmv_pack_int8", "qmv_quantize_act", "qmv_gemv", "qmv_gemm_prefill",
                  "qmv_lmhead_argmax"):
         assert hasattr(lib, name)
